@@ -1,0 +1,186 @@
+/*
+ * oracle.c -- plain float64 CPU reference of the matrix-state affine scan.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark load this library.  It
+ * shares no source, header, table or helper with the GPU library.
+ *
+ * What it computes (one head; rows of S are value channels i, columns are key
+ * channels j; S has d_v rows and d_k columns):
+ *
+ *   S_t = S_{t-1} E_t + f_t,     o_t = S_t q_t            (inclusive read-out)
+ *
+ * gated delta rule (mode 0):  E_t = alpha_t (I - beta_t k_t k_t^T),
+ *                             f_t = beta_t v_t k_t^T
+ * gated linear attention (mode 1):  E_t = alpha_t I,  f_t = v_t k_t^T
+ *
+ * Sources:
+ *  - "Sequential Parallel Duality in Prefix Scannable Models" (papernotes.org
+ *    ICLR 2026 notes), key design 2: an efficient layer is an affine state
+ *    update s_t = E_t |> s_{t-1} + f_t whose coefficients depend only on the
+ *    current token; the second component of the running monoid product is the
+ *    recurrent state, so the left-to-right fold below IS the scan's result.
+ *    Key design 1: inference is one state update per token.
+ *  - "PRISM: Parallel Residual Iterative Sequence Model" (gist.science
+ *    explainer), Resume Technique 2.1: the state update is written
+ *    S_t = S_{t-1} A_t + B_t with the forget operator A_t a structured rank-1
+ *    form identical to Gated DeltaNet, and 2.2: S_{t-1} k_t is the value the
+ *    state currently recalls for key k_t (so S maps keys to values and E acts
+ *    on the key index).
+ *  - PRISM article (banbantang.com), section 1(4): a global scalar gate decays
+ *    the whole state, a rank-1 term forgets selectively along k, and each token
+ *    writes one rank-1 outer product.  The page's formula itself was lost in
+ *    extraction; E_t and f_t above are the reading those three statements fix.
+ *    Gated linear attention is the scalar-gate member of the family listed in
+ *    key design 2 of the first page (Katharopoulos et al. for the ungated case).
+ *
+ * Arithmetic: each token is applied exactly as written above, per row i:
+ *   a_i   = sum_j S_ij k_j                       (row of S_{t-1} k_t)
+ *   S_ij <- alpha (S_ij - beta a_i k_j) + beta v_i k_j      [gdn]
+ *   S_ij <- alpha S_ij + v_i k_j                            [gla]
+ *   o_i   = sum_j S_ij q_j                       (row of S_t q_t)
+ * Inputs arrive as float32 (bfloat16 inputs are exact in float32) and are
+ * widened exactly to float64.  Rows of S are independent, so work is split over
+ * (head, block of rows) across threads; every row sees the same sequence of
+ * operations whatever the split, so results do not depend on thread count.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fPIC -shared -pthread
+ */
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_GDN = 0, ORACLE_GLA = 1 };
+
+typedef struct {
+    int mode;
+    int64_t BH, T;
+    int dk, dv;
+    const float *q, *k, *v, *alpha, *beta;
+    const double *S0;
+    double *o, *ST;
+    int row_blocks;
+    int64_t n_items;
+    int64_t next;        /* shared work counter */
+    int failed;
+} job_t;
+
+/* Apply tokens 0..T-1 of head h to rows [r0, r1) of its state. */
+static int run_rows(const job_t *J, int64_t h, int r0, int r1)
+{
+    const int dk = J->dk, dv = J->dv;
+    const int64_t T = J->T;
+    const int nrows = r1 - r0;
+    double *S = (double *)malloc(sizeof(double) * (size_t)nrows * (size_t)dk);
+    if (!S) return -1;
+    for (int r = 0; r < nrows; ++r)
+        for (int j = 0; j < dk; ++j)
+            S[(size_t)r * dk + j] = J->S0 ? J->S0[((size_t)h * dv + r0 + r) * dk + j] : 0.0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        const size_t tok = (size_t)(h * T + t);
+        const float *qt = J->q + tok * dk;
+        const float *kt = J->k + tok * dk;
+        const float *vt = J->v + tok * dv;
+        const double al = (double)J->alpha[tok];
+        const double be = J->mode == ORACLE_GDN ? (double)J->beta[tok] : 0.0;
+        for (int r = 0; r < nrows; ++r) {
+            double *Si = S + (size_t)r * dk;
+            const double vi = (double)vt[r0 + r];
+            if (J->mode == ORACLE_GDN) {
+                double a = 0.0;
+                for (int j = 0; j < dk; ++j) a += Si[j] * (double)kt[j];
+                for (int j = 0; j < dk; ++j)
+                    Si[j] = al * (Si[j] - be * a * (double)kt[j]) + be * vi * (double)kt[j];
+            } else {
+                for (int j = 0; j < dk; ++j) Si[j] = al * Si[j] + vi * (double)kt[j];
+            }
+            double oi = 0.0;
+            for (int j = 0; j < dk; ++j) oi += Si[j] * (double)qt[j];
+            if (J->o) J->o[tok * dv + r0 + r] = oi;
+        }
+    }
+    if (J->ST)
+        memcpy(J->ST + ((size_t)h * dv + r0) * dk, S, sizeof(double) * (size_t)nrows * dk);
+    free(S);
+    return 0;
+}
+
+static void *worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    for (;;) {
+        int64_t it = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+        if (it >= J->n_items) break;
+        const int64_t h = it / J->row_blocks;
+        const int b = (int)(it % J->row_blocks);
+        const int per = (J->dv + J->row_blocks - 1) / J->row_blocks;
+        const int r0 = b * per;
+        const int r1 = r0 + per < J->dv ? r0 + per : J->dv;
+        if (r0 < r1 && run_rows(J, h, r0, r1) != 0) __atomic_store_n(&J->failed, 1, __ATOMIC_RELAXED);
+    }
+    return NULL;
+}
+
+/*
+ * Full-sequence scan of BH independent heads.
+ *   q, k: [BH, T, dk] float32     v: [BH, T, dv] float32
+ *   alpha, beta: [BH, T] float32 (beta ignored, may be NULL, in mode 1)
+ *   S0: [BH, dv, dk] float64 or NULL (zero state)
+ *   o:  [BH, T, dv] float64 or NULL (not stored; still computed)
+ *   ST: [BH, dv, dk] float64 or NULL
+ * Returns the number of threads used (>= 1), or -1 on bad arguments or
+ * allocation failure.
+ */
+int oracle_scan_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
+                    const float *q, const float *k, const float *v,
+                    const float *alpha, const float *beta, const double *S0,
+                    double *o, double *ST, int nthreads)
+{
+    if ((mode != ORACLE_GDN && mode != ORACLE_GLA) || BH < 0 || T < 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (mode == ORACLE_GDN && !beta && BH * T > 0) return -1;
+    if (BH * T > 0 && (!q || !k || !v || !alpha)) return -1;
+    if (nthreads < 1) nthreads = 1;
+
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.mode = mode; J.BH = BH; J.T = T; J.dk = dk; J.dv = dv;
+    J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.S0 = S0;
+    J.o = o; J.ST = ST;
+    /* enough (head, row-block) items to keep every thread busy */
+    int rb = 1;
+    while (BH * rb < 2 * (int64_t)nthreads && rb < dv) rb *= 2;
+    J.row_blocks = rb;
+    J.n_items = BH * rb;
+    if (J.n_items == 0) return 1;
+    if ((int64_t)nthreads > J.n_items) nthreads = (int)J.n_items;
+
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) return -1;
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, worker, &J) != 0) break;
+        ++started;
+    }
+    worker(&J);
+    for (int i = 1; i <= started; ++i) pthread_join(tid[i], NULL);
+    free(tid);
+    return J.failed ? -1 : started + 1;
+}
+
+/*
+ * One token for each of N independent states, state updated in place:
+ *   q, k: [N, dk]   v: [N, dv]   alpha, beta: [N]   S: [N, dv, dk] float64
+ *   o: [N, dv] float64 = S_new q
+ * Same arithmetic as oracle_scan_f64 with T = 1 (the per-token update of the
+ * sequential view, key design 1 of the prefix-scan notes).
+ */
+int oracle_decode_f64(int mode, int64_t N, int dk, int dv,
+                      const float *q, const float *k, const float *v,
+                      const float *alpha, const float *beta,
+                      double *S, double *o, int nthreads)
+{
+    return oracle_scan_f64(mode, N, 1, dk, dv, q, k, v, alpha, beta, S, o, S, nthreads);
+}
