@@ -1,0 +1,142 @@
+/*
+ * gdscan.h -- C ABI of the gfx950 (MI355X) matrix-state affine scan library.
+ *
+ * The library computes, per head, the prefix scan of the affine monoid
+ * (E_t, f_t) acting on a matrix state S (d_v rows = value channels, d_k
+ * columns = key channels):
+ *
+ *     S_t = S_{t-1} E_t + f_t,          o_t = S_t q_t   (inclusive read-out)
+ *
+ *   SCAN_GDN (gated delta rule):       E_t = alpha_t (I - beta_t k_t k_t^T),
+ *                                      f_t = beta_t v_t k_t^T
+ *   SCAN_GLA (gated linear attention): E_t = alpha_t I,  f_t = v_t k_t^T
+ *
+ * Sources: "Sequential Parallel Duality in Prefix Scannable Models"
+ * (papernotes.org ICLR 2026 notes), key design 2 (affine update
+ * s_t = E_t |> s_{t-1} + f_t, monoid combine (E2,f2)+(E1,f1) = (E2 E1, E2 f1 + f2),
+ * identity (I,0); gated linear attention is the scalar-gate member) and key
+ * design 1 (a parallel training circuit over all positions, plus a per-token
+ * state update for inference); "PRISM: Parallel Residual Iterative Sequence
+ * Model" (gist.science explainer, technical summary 2.1: S_t = S_{t-1} A_t + B_t
+ * with a Gated-DeltaNet rank-1 forget operator; 2.2: S_{t-1} k_t is the value
+ * recalled for key k_t) and the PRISM article (banbantang.com, section 1(4):
+ * global scalar decay, rank-1 forgetting along k, rank-1 write).  In the
+ * right-action form used here E acts on the key index; since every E_t is
+ * symmetric this is the left action E_t S^T_{t-1} + f_t^T on the transposed
+ * (d_k x d_v) storage.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *    allocates nothing and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Buffers must stay alive until the stream has completed.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    non-zero status means nothing was enqueued and nothing was written, and
+ *    scan_last_error() (per host thread) describes the problem.
+ *  - Data preconditions are documented, not checked on the device: finite
+ *    inputs, 0 < alpha <= 1, and for SCAN_GDN 0 <= beta <= 1 with unit-norm keys
+ *    recommended (then every E_t has spectral norm <= 1).
+ *  - Layouts are dense and row-major.  q, k, v, o, S0, ST and S must be 16-byte
+ *    aligned; alpha and beta 4-byte aligned.
+ */
+#ifndef GDSCAN_H_
+#define GDSCAN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* mode */
+#define SCAN_GDN 0
+#define SCAN_GLA 1
+
+/* element type of q, k, v and o (alpha, beta and all states are float32) */
+#define SCAN_F32 0
+#define SCAN_BF16 1
+
+/* status codes */
+#define SCAN_OK 0
+#define SCAN_EINVAL 1        /* null required pointer, bad enum, bad size, overlap */
+#define SCAN_EUNSUPPORTED 2  /* shape/chunk/dtype combination not built */
+#define SCAN_EWORKSPACE 3    /* workspace missing or smaller than required */
+#define SCAN_EALIGN 4        /* pointer not aligned as documented above */
+#define SCAN_EHIP 5          /* HIP launch/runtime failure (message has the HIP error) */
+
+/* scan_opts.path */
+#define SCAN_PATH_AUTO 0
+#define SCAN_PATH_SEQUENTIAL 1  /* one pass over the chunks of each head */
+#define SCAN_PATH_BLELLOCH 2    /* leaf aggregates + fixed Blelloch tree + output pass */
+
+typedef struct scan_opts {
+    int path;         /* SCAN_PATH_*; AUTO picks BLELLOCH when B*H is too small to fill the GPU */
+    int leaf_chunks;  /* Blelloch path: chunks per leaf (power of two); 0 = library default */
+} scan_opts;
+
+/*
+ * Bytes of device workspace scan_fwd needs for these arguments (0 if none).
+ * Returns (size_t)-1 if the arguments are invalid or unsupported
+ * (scan_last_error() says why).  opts may be NULL (defaults).
+ */
+size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk, int dv,
+                               int chunk, const scan_opts *opts);
+
+/*
+ * Full-sequence forward scan (the parallel training view of key design 1 in
+ * the prefix-scan notes; chunked as in their overall framework: every chunk is
+ * encoded, chunk states are combined in a fixed order, then each chunk is read
+ * out from its exclusive prefix state).
+ *
+ *   q, k : [B, H, T, dk]  dtype          v, o : [B, H, T, dv]  dtype
+ *   alpha: [B, H, T] float32 in (0, 1]
+ *   beta : [B, H, T] float32 for SCAN_GDN; must be NULL for SCAN_GLA
+ *   S0   : [B, H, dv, dk] float32 initial state, or NULL for the zero state
+ *   ST   : [B, H, dv, dk] float32 final state, or NULL to skip writing it.
+ *          ST may be the same pointer as S0 (in-place carry); any other overlap
+ *          with an input is invalid.
+ *   o    : written for every token, o_t = S_t q_t; must not overlap any input.
+ *   chunk: tokens per chunk, 16, 32 or 64.  A ragged last chunk behaves as if
+ *          padded with identity tokens (alpha = 1, beta = 0, q = k = v = 0);
+ *          padded outputs are not written.
+ *   workspace / workspace_bytes: device scratch of at least
+ *          scan_fwd_workspace_size(...) bytes (may be NULL when that is 0).
+ *          Reusable across calls that are ordered on one stream.
+ * Supported: dtype SCAN_BF16 with dk = dv = 128 (chunk 64 on the fast path;
+ * chunk 16/32 and other sizes take the float32 kernel); dtype SCAN_F32 with
+ * dk, dv in {16, 32, 64, 128}.  T >= 1; B, H >= 1.
+ * Returns SCAN_OK or an error status (see above).
+ */
+int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+             const void *q, const void *k, const void *v, const float *alpha,
+             const float *beta, const float *S0, void *o, float *ST,
+             void *workspace, size_t workspace_bytes, const scan_opts *opts, void *stream);
+
+/*
+ * One token for each of N independent states (the sequential view: state
+ * update U and read-out F of key design 1 in the prefix-scan notes); exactly
+ * scan_fwd with T = 1 applied to each state, state updated in place:
+ *
+ *   S <- S E + f,   o = S q   (with the updated S)
+ *
+ *   q, k : [N, dk] dtype     v, o : [N, dv] dtype
+ *   alpha: [N] float32       beta : [N] float32 (SCAN_GDN) or NULL (SCAN_GLA)
+ *   S    : [N, dv, dk] float32, read and written in place
+ * Supported: dk in {16, 32, 64, 128}, dv >= 1, either dtype.
+ * o must not overlap any input or S.  Returns SCAN_OK or an error status.
+ */
+int decode_step(int mode, int dtype, int N, int dk, int dv, const void *q, const void *k,
+                const void *v, const float *alpha, const float *beta, float *S, void *o,
+                void *stream);
+
+/* Message describing the last non-zero status returned on this host thread. */
+const char *scan_last_error(void);
+
+/* Library name, version and the GPU architecture it was built for. */
+const char *scan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDSCAN_H_ */

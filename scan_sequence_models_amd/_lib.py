@@ -1,0 +1,194 @@
+"""ctypes binding of ``libgdscan.so`` (include/gdscan.h).
+
+Argument marshalling only: shapes and dtypes are checked, outputs are
+allocated with torch when the caller does not pass them, and the C entry points
+of the same names are called on torch's current HIP stream.  Every step of the
+scan runs in the library's kernels; there is no other implementation to fall
+back on, so a missing or unloadable library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdscan.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "gdscan.h")
+
+SCAN_GDN, SCAN_GLA = 0, 1
+SCAN_F32, SCAN_BF16 = 0, 1
+SCAN_OK, SCAN_EINVAL, SCAN_EUNSUPPORTED, SCAN_EWORKSPACE, SCAN_EALIGN, SCAN_EHIP = range(6)
+PATHS = {"auto": 0, "sequential": 1, "blelloch": 2}
+STATUS_NAMES = {0: "SCAN_OK", 1: "SCAN_EINVAL", 2: "SCAN_EUNSUPPORTED", 3: "SCAN_EWORKSPACE",
+                4: "SCAN_EALIGN", 5: "SCAN_EHIP"}
+
+
+class ScanOpts(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("leaf_chunks", ctypes.c_int)]
+
+
+class ScanError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m scan_sequence_models_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.scan_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ScanOpts)]
+        L.scan_fwd_workspace_size.restype = sz
+        L.scan_fwd.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p, sz,
+                               ctypes.POINTER(ScanOpts), p]
+        L.scan_fwd.restype = i
+        L.decode_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
+        L.decode_step.restype = i
+        L.scan_last_error.restype = ctypes.c_char_p
+        L.scan_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gdscan.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def last_error() -> str:
+    return lib().scan_last_error().decode()
+
+
+def version() -> str:
+    return lib().scan_version().decode()
+
+
+def _check(status: int):
+    if status != SCAN_OK:
+        raise ScanError(status, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SCAN_F32
+    if t.dtype == torch.bfloat16:
+        return SCAN_BF16
+    raise TypeError(f"q, k, v must be float32 or bfloat16 (got {t.dtype})")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def scan_fwd_workspace_size(mode: int, dtype: int, B: int, H: int, T: int, dk: int, dv: int,
+                            chunk: int, path: str = "auto", leaf_chunks: int = 0) -> int:
+    opts = ScanOpts(PATHS[path], leaf_chunks)
+    n = lib().scan_fwd_workspace_size(mode, dtype, B, H, T, dk, dv, chunk, ctypes.byref(opts))
+    if n == ctypes.c_size_t(-1).value:
+        raise ScanError(SCAN_EINVAL, last_error())
+    return n
+
+
+def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str = "auto",
+             leaf_chunks: int = 0, o=None, ST=None, workspace=None, write_state: bool = True):
+    """Forward scan over [B, H, T, d] tensors; returns (o, ST).
+
+    ``beta is None`` selects gated linear attention (E = alpha I, f = v k^T),
+    otherwise the gated delta rule.  ``S0=None`` is the zero state.  ``ST`` may
+    be ``S0`` itself (in-place carry).  ``write_state=False`` skips S_T.
+    """
+    _need(q, "q")
+    dev = q.device
+    dt = q.dtype
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", dt, (B, H, T, dk), dev)
+    _need(v, "v", dt, (B, H, T, dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    mode = SCAN_GLA if beta is None else SCAN_GDN
+    if beta is not None:
+        _need(beta, "beta", torch.float32, (B, H, T), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _need(o, "o", dt, (B, H, T, dv), dev)
+    if ST is None and write_state:
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if ST is not None:
+        _need(ST, "ST", torch.float32, (B, H, dv, dk), dev)
+    dcode = _dtype_code(q)
+    ws_bytes = scan_fwd_workspace_size(mode, dcode, B, H, T, dk, dv, chunk, path, leaf_chunks)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, dev)
+    opts = ScanOpts(PATHS[path], leaf_chunks)
+    with torch.cuda.device(dev):
+        st = lib().scan_fwd(mode, dcode, B, H, T, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), ctypes.byref(opts),
+                            _stream(dev))
+    _check(st)
+    return o, ST
+
+
+def decode_step(q, k, v, alpha, beta, S, o=None):
+    """One token per state: S [N, dv, dk] float32 updated in place; returns o [N, dv].
+
+    ``beta is None`` selects gated linear attention.
+    """
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    if q.dim() != 2:
+        raise ValueError("q must be [N, dk]")
+    N, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", dt, (N, dk), dev)
+    _need(v, "v", dt, (N, dv), dev)
+    _need(alpha, "alpha", torch.float32, (N,), dev)
+    mode = SCAN_GLA if beta is None else SCAN_GDN
+    if beta is not None:
+        _need(beta, "beta", torch.float32, (N,), dev)
+    _need(S, "S", torch.float32, (N, dv, dk), dev)
+    if o is None:
+        o = torch.empty((N, dv), dtype=dt, device=dev)
+    _need(o, "o", dt, (N, dv), dev)
+    with torch.cuda.device(dev):
+        st = lib().decode_step(mode, _dtype_code(q), N, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(alpha), _ptr(beta), _ptr(S), _ptr(o), _stream(dev))
+    _check(st)
+    return o

@@ -1,0 +1,203 @@
+// api.hip -- the C ABI declared in include/gdscan.h: argument validation,
+// workspace sizing, path selection and error reporting.  No device code here.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdscan.h"
+#include "kernels.hpp"
+#include "blelloch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const char* name, const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SCAN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Number of compute units of the current device (cached per device).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+struct Plan {
+    int path;          // SCAN_PATH_SEQUENTIAL or SCAN_PATH_BLELLOCH
+    bool mfma;         // bf16 MFMA kernel (else float32 kernel)
+    int leaf_chunks;   // Blelloch leaf size in chunks
+    size_t workspace;  // bytes
+};
+
+// Validates the sizes/enums of a scan_fwd call and picks the kernels.
+int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+              const scan_opts* opts, Plan* plan) {
+    if (mode != SCAN_GDN && mode != SCAN_GLA) return fail(SCAN_EINVAL, "mode must be SCAN_GDN or SCAN_GLA (got %d)", mode);
+    if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
+    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
+        return fail(SCAN_EINVAL, "B, H, T, dk, dv must be >= 1 (got %d, %d, %d, %d, %d)", B, H, T, dk, dv);
+    if ((int64_t)B * H > INT32_MAX / 64) return fail(SCAN_EINVAL, "B*H too large");
+    if (chunk != 16 && chunk != 32 && chunk != 64) return fail(SCAN_EUNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
+    const int path = opts ? opts->path : SCAN_PATH_AUTO;
+    if (path != SCAN_PATH_AUTO && path != SCAN_PATH_SEQUENTIAL && path != SCAN_PATH_BLELLOCH)
+        return fail(SCAN_EINVAL, "opts->path must be SCAN_PATH_AUTO, _SEQUENTIAL or _BLELLOCH (got %d)", path);
+    int leaf = opts ? opts->leaf_chunks : 0;
+    if (leaf < 0 || (leaf & (leaf - 1)) != 0) return fail(SCAN_EINVAL, "opts->leaf_chunks must be 0 or a power of two (got %d)", leaf);
+
+    Plan p{};
+    p.mfma = dtype == SCAN_BF16 && gds::chunk_mfma_supported(mode, dk, dv, chunk);
+    if (!p.mfma && !gds::chunk_f32_supported(mode, dk, dv, chunk))
+        return fail(SCAN_EUNSUPPORTED, "unsupported size: dk=%d dv=%d chunk=%d (dk in {16,32,64,128}, dv a multiple of 16)", dk, dv, chunk);
+
+    const int64_t nchunks = (T + chunk - 1) / chunk;
+    const int64_t heads = (int64_t)B * H;
+    p.path = SCAN_PATH_SEQUENTIAL;
+    if (path == SCAN_PATH_BLELLOCH) {
+        p.path = SCAN_PATH_BLELLOCH;
+    } else if (path == SCAN_PATH_AUTO) {
+        // The sequential pass runs one workgroup per (head, value slice); when
+        // that cannot fill the GPU and the sequence is long, split it into
+        // leaves and combine their aggregates with the Blelloch tree.
+        const int64_t wgs = heads * gds::sequential_workgroups_per_head(p.mfma, dv);
+        if (wgs * 2 <= device_cus() && nchunks >= 256) p.path = SCAN_PATH_BLELLOCH;
+    }
+    if (p.path == SCAN_PATH_BLELLOCH) {
+        if (!gds::blelloch_supported(mode, dtype, dk, dv, chunk))
+            return fail(SCAN_EUNSUPPORTED, "the Blelloch path supports dk = dv = 128 only (got dk=%d dv=%d)", dk, dv);
+        if (leaf == 0) leaf = gds::blelloch_default_leaf_chunks(nchunks, heads, device_cus());
+        p.leaf_chunks = leaf;
+        p.workspace = gds::blelloch_workspace_bytes(heads, nchunks, leaf, dk, dv);
+    }
+    *plan = p;
+    return SCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* scan_last_error(void) { return g_err; }
+
+const char* scan_version(void) { return "gdscan 0.1.0 (gfx950, HIP)"; }
+
+size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+                               const scan_opts* opts) {
+    Plan p;
+    if (plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p) != SCAN_OK) return (size_t)-1;
+    return p.workspace;
+}
+
+int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk, const void* q,
+             const void* k, const void* v, const float* alpha, const float* beta, const float* S0,
+             void* o, float* ST, void* workspace, size_t workspace_bytes, const scan_opts* opts,
+             void* stream) {
+    Plan p;
+    int st = plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p);
+    if (st != SCAN_OK) return st;
+    if (!q || !k || !v || !alpha || !o) return fail(SCAN_EINVAL, "q, k, v, alpha and o must be non-null");
+    if (mode == SCAN_GDN && !beta) return fail(SCAN_EINVAL, "SCAN_GDN needs beta");
+    if (mode == SCAN_GLA && beta) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta (pass NULL)");
+    const void* a16[] = {q, k, v, o, S0, ST};
+    const char* n16[] = {"q", "k", "v", "o", "S0", "ST"};
+    for (int i = 0; i < 6; ++i)
+        if (a16[i] && !aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
+    if (!aligned(alpha, 4) || (beta && !aligned(beta, 4))) return fail(SCAN_EALIGN, "alpha/beta not 4-byte aligned");
+    if (p.workspace > 0) {
+        if (!workspace || workspace_bytes < p.workspace)
+            return fail(SCAN_EWORKSPACE, "workspace of %zu bytes required (got %zu)", p.workspace, workspace_bytes);
+        if (!aligned(workspace, 256)) return fail(SCAN_EALIGN, "workspace is not 256-byte aligned");
+    }
+    const size_t es = dtype == SCAN_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H;
+    const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
+                        range("v", v, BH * T * dv * es), range("alpha", alpha, BH * T * 4),
+                        range("beta", beta, BH * T * 4), range("S0", S0, BH * dv * dk * 4),
+                        range("workspace", workspace, p.workspace)};
+    const Range ro = range("o", o, BH * T * dv * es);
+    const Range rs = range("ST", ST, BH * dv * dk * 4);
+    for (const Range& r : in) {
+        if (overlaps(ro, r)) return fail(SCAN_EINVAL, "o overlaps %s", r.name);
+        if (overlaps(rs, r) && !(r.name[0] == 'S' && ST == S0))
+            return fail(SCAN_EINVAL, "ST overlaps %s (only ST == S0 is allowed)", r.name);
+    }
+    if (overlaps(ro, rs)) return fail(SCAN_EINVAL, "o overlaps ST");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p.path == SCAN_PATH_BLELLOCH) {
+        e = gds::launch_blelloch(mode, (int)BH, T, dk, dv, chunk, p.leaf_chunks, q, k, v, alpha, beta,
+                                 S0, o, ST, workspace, s);
+    } else if (p.mfma) {
+        e = gds::launch_chunk_mfma(mode, (int)BH, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST, s);
+    } else {
+        e = gds::launch_chunk_f32(mode, dtype, (int)BH, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "scan_fwd launch");
+    return SCAN_OK;
+}
+
+int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const void* k,
+                const void* v, const float* alpha, const float* beta, float* S, void* o,
+                void* stream) {
+    if (mode != SCAN_GDN && mode != SCAN_GLA) return fail(SCAN_EINVAL, "mode must be SCAN_GDN or SCAN_GLA (got %d)", mode);
+    if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
+    if (N < 1 || dk < 1 || dv < 1) return fail(SCAN_EINVAL, "N, dk, dv must be >= 1 (got %d, %d, %d)", N, dk, dv);
+    if (!gds::decode_supported(dk)) return fail(SCAN_EUNSUPPORTED, "decode_step supports dk in {16,32,64,128} (got %d)", dk);
+    if ((int64_t)N * ((dv + 127) / 128) > INT32_MAX) return fail(SCAN_EINVAL, "N*dv too large");
+    if (!q || !k || !v || !alpha || !S || !o) return fail(SCAN_EINVAL, "q, k, v, alpha, S and o must be non-null");
+    if (mode == SCAN_GDN && !beta) return fail(SCAN_EINVAL, "SCAN_GDN needs beta");
+    if (mode == SCAN_GLA && beta) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta (pass NULL)");
+    const void* a16[] = {q, k, v, o, S};
+    const char* n16[] = {"q", "k", "v", "o", "S"};
+    for (int i = 0; i < 5; ++i)
+        if (!aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
+    if (!aligned(alpha, 4) || (beta && !aligned(beta, 4))) return fail(SCAN_EALIGN, "alpha/beta not 4-byte aligned");
+    const size_t es = dtype == SCAN_BF16 ? 2 : 4;
+    const Range in[] = {range("q", q, (size_t)N * dk * es), range("k", k, (size_t)N * dk * es),
+                        range("v", v, (size_t)N * dv * es), range("alpha", alpha, (size_t)N * 4),
+                        range("beta", beta, (size_t)N * 4), range("S", S, (size_t)N * dv * dk * 4)};
+    const Range ro = range("o", o, (size_t)N * dv * es);
+    for (const Range& r : in)
+        if (overlaps(ro, r)) return fail(SCAN_EINVAL, "o overlaps %s", r.name);
+    const Range rS = in[5];
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(rS, in[i])) return fail(SCAN_EINVAL, "S overlaps %s", in[i].name);
+    hipError_t e = gds::launch_decode(mode, dtype, N, dk, dv, q, k, v, alpha, beta, S, o,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode_step launch");
+    return SCAN_OK;
+}
+
+}  // extern "C"

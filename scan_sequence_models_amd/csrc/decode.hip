@@ -1,0 +1,127 @@
+// decode.hip -- single-token state update, one streaming pass over each state.
+//
+// Sequential (inference) view of the affine scan: one update of the fixed-size
+// state per token ("Sequential Parallel Duality in Prefix Scannable Models",
+// papernotes.org notes, key design 1; constant-size state, key design 2).  Per
+// state S (dv x dk, fp32, in place) and token (q, k, v, alpha, beta):
+//
+//   a = S k,  b = S q                         (row dot products of the old S)
+//   gdn: u = beta (v - alpha a)      gla: u = v
+//   S  <- alpha S + u k^T                     (= S E + f for this token)
+//   o   = S_new q = alpha b + (k . q) u
+//
+// The work is HBM-bound (64 KB read + 64 KB written per 128x128 state, ~7 d^2
+// flop), so the kernel is organised around the stream: rows of S are
+// independent, a row of dk floats is covered by dk/4 lanes with one 16-byte
+// load each, and every thread issues all of its row loads before the first
+// reduction so that each wave keeps 16 loads in flight.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gds {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = 128;
+
+template <int DK, int MODE, typename E>
+__global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks,
+                                                          const E* __restrict__ q,
+                                                          const E* __restrict__ k,
+                                                          const E* __restrict__ v,
+                                                          const float* __restrict__ alpha,
+                                                          const float* __restrict__ beta,
+                                                          float* __restrict__ S,
+                                                          E* __restrict__ o) {
+    constexpr int L = DK / 4;                       // lanes per row
+    constexpr int kRowsPerWavePass = kWave / L;
+    constexpr int kRowsPerPass = kRowsPerWavePass * (kThreads / kWave);
+    constexpr int kPasses = kRowsPerBlock / kRowsPerPass;
+
+    const int n = blockIdx.x / row_blocks;
+    const int rb = blockIdx.x - n * row_blocks;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int sub = lane % L;
+    const int rsub = lane / L;
+
+    const float4 k4 = io<E>::load4(k, (size_t)n * DK + sub * 4);
+    const float4 q4 = io<E>::load4(q, (size_t)n * DK + sub * 4);
+    const float kq = group_sum<L>(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
+    const float al = alpha[n];
+    const float be = MODE == 0 ? beta[n] : 0.f;
+
+    float* Sn = S + (size_t)n * dv * DK;
+    int rows[kPasses];
+    float4 s[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        rows[p] = rb * kRowsPerBlock + p * kRowsPerPass + wave * kRowsPerWavePass + rsub;
+        s[p] = rows[p] < dv ? *reinterpret_cast<const float4*>(Sn + (size_t)rows[p] * DK + sub * 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        float a = s[p].x * k4.x + s[p].y * k4.y + s[p].z * k4.z + s[p].w * k4.w;
+        float b = s[p].x * q4.x + s[p].y * q4.y + s[p].z * q4.z + s[p].w * q4.w;
+        a = group_sum<L>(a);
+        b = group_sum<L>(b);
+        if (rows[p] < dv) {
+            const float vi = io<E>::load(v, (size_t)n * dv + rows[p]);
+            const float u = MODE == 0 ? be * (vi - al * a) : vi;
+            float4 r;
+            r.x = al * s[p].x + u * k4.x;
+            r.y = al * s[p].y + u * k4.y;
+            r.z = al * s[p].z + u * k4.z;
+            r.w = al * s[p].w + u * k4.w;
+            *reinterpret_cast<float4*>(Sn + (size_t)rows[p] * DK + sub * 4) = r;
+            if (sub == 0) io<E>::store(o, (size_t)n * dv + rows[p], al * b + kq * u);
+        }
+    }
+}
+
+template <int DK, typename E>
+hipError_t launch_typed(int mode, int N, int dv, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, float* S, void* o,
+                        hipStream_t stream) {
+    const int rb = (dv + kRowsPerBlock - 1) / kRowsPerBlock;
+    const dim3 grid((unsigned)((size_t)N * rb));
+    const E* qq = static_cast<const E*>(q);
+    const E* kk = static_cast<const E*>(k);
+    const E* vv = static_cast<const E*>(v);
+    E* oo = static_cast<E*>(o);
+    if (mode == 0)
+        hipLaunchKernelGGL((decode_kernel<DK, 0, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
+                           kk, vv, alpha, beta, S, oo);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, 1, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
+                           kk, vv, alpha, beta, S, oo);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_dk(int mode, int N, int dk, int dv, const void* q, const void* k,
+                     const void* v, const float* alpha, const float* beta, float* S, void* o,
+                     hipStream_t stream) {
+    switch (dk) {
+        case 16: return launch_typed<16, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
+        case 32: return launch_typed<32, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
+        case 64: return launch_typed<64, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
+        case 128: return launch_typed<128, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decode_supported(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk == 128; }
+
+hipError_t launch_decode(int mode, int dtype, int N, int dk, int dv, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         float* S, void* o, hipStream_t stream) {
+    if (dtype == 0)
+        return launch_dk<float>(mode, N, dk, dv, q, k, v, alpha, beta, S, o, stream);
+    return launch_dk<uint16_t>(mode, N, dk, dv, q, k, v, alpha, beta, S, o, stream);
+}
+
+}  // namespace gds
