@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the forward gated-delta scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one scan_fwd call over one batch of synthetic inputs that are
+already resident in HBM: B=8 sequences x H=16 heads x T=8192 tokens, d=128,
+bf16 q/k/v, fp32 state, chunk 64 (the gated-delta training-shape forward).
+Prints one JSON line with tokens/s, the roofline of the dominant kernel and the
+float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s fwd gated-delta scan (H=16,d=128,T=8192); % MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def scan_bytes(w) -> int:
+    """Algorithmic HBM bytes of one scan_fwd call: q, k, v read and o written
+    once (dtype), alpha (+ beta) read once (fp32), S0 read and S_T written once
+    (fp32).  Intermediates stay on chip."""
+    es = 2 if w.dtype == "bf16" else 4
+    ht = w.B * w.H * w.T
+    b = ht * (2 * w.dk + 2 * w.dv) * es
+    b += ht * 4 * (2 if w.mode == "gdn" else 1)
+    b += w.B * w.H * w.dv * w.dk * 4 * (2 if w.s0_var is not None else 1)
+    return b
+
+
+def scan_flops(w) -> float:
+    """Executed MFMA flops of the chunk algorithm per call (dense tiles):
+    gdn: 5 C^2-sized products (K K^T, Q K^T, W, U~, P U) = 10 C d per
+    head-token, 3 state products (W S^T, Q S^T, U^T D K) = 6 d^2, UT solve C^2/3;
+    gla: 2 C^2 products (Q K^T, P V) and 2 state products."""
+    C, d = w.chunk, w.dk
+    per = (10 * C * d + 6 * d * d + C * C / 3) if w.mode == "gdn" else (4 * C * d + 4 * d * d)
+    return per * w.B * w.H * w.T
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_src: str, summary: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_sha(kernel_src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, heads: int):
+    """The float64 oracle, as it stands, on the first ``heads`` heads of ``w``
+    (full length each), using every host core it is given."""
+    import numpy as np
+
+    import oracle
+    from scan_sequence_models_amd import inputs as I
+
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
+    hs = [I.head_inputs(w, b, h) for b, h in sel]
+    st = lambda f: None if getattr(hs[0], f) is None else np.stack([getattr(x, f) for x in hs])  # noqa: E731
+    q, k, v, a, be, S0 = st("q"), st("k"), st("v"), st("alpha"), st("beta"), st("S0")
+    S0 = None if S0 is None else S0.astype(np.float64)
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    _, _, threads = oracle.scan(w.mode, q, k, v, a, be, S0, return_threads=True)
+    sec = time.perf_counter() - t0
+    head_tokens = len(sel) * w.T
+    return {
+        "value": head_tokens / w.H / sec,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(sel)} of {w.B * w.H} heads x {w.T} tokens ({head_tokens} head-tokens, "
+                  f"= {head_tokens // w.H} tokens of all {w.H} heads), float64 token recurrence, "
+                  f"{sec:.2f} s",
+        "head_tokens_per_s": head_tokens / sec,
+        "seconds": sec,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gdn-b8h16t8192")
+    ap.add_argument("--path", default="auto", choices=["auto", "sequential", "blelloch"])
+    ap.add_argument("--leaf-chunks", type=int, default=0)
+    ap.add_argument("--cpu-heads", type=int, default=128,
+                    help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and sequences shard with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import scan_sequence_models_amd as gds
+    from scan_sequence_models_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    if w.path == "decode":
+        raise SystemExit("decode workloads are timed by their own tests, not by bench.py")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"bench: generating {w.name} (B={w.B} H={w.H} T={w.T} d={w.dk})")
+    b = I.batch_inputs(w, threads=16)
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    bf = w.dtype == "bf16"
+    q, k, v = up(b.q, bf), up(b.k, bf), up(b.v, bf)
+    alpha = up(b.alpha)
+    beta = up(b.beta) if b.beta is not None else None
+    S0 = up(b.S0) if b.S0 is not None else None
+    del b
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=q.dtype, device=dev)
+    ST = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    mode = gds.SCAN_GDN if w.mode == "gdn" else gds.SCAN_GLA
+    dcode = gds.SCAN_BF16 if bf else gds.SCAN_F32
+    path = args.path if args.path != "auto" else w.path if w.path == "blelloch" else "auto"
+    ws_bytes = gds.scan_fwd_workspace_size(mode, dcode, w.B, w.H, w.T, w.dk, w.dv, w.chunk, path,
+                                           args.leaf_chunks)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+
+    def step():
+        gds.scan_fwd(q, k, v, alpha, beta, S0, chunk=w.chunk, path=path,
+                     leaf_chunks=args.leaf_chunks, o=o, ST=ST, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    span_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = span_ms / args.steps
+    kern_ms = float(np.mean(per_launch_ms))
+    tokens = w.B * w.T
+    value = tokens / (ms_per_step / 1e3)
+    log(f"bench: {args.steps} steps, span {span_ms:.3f} ms, per launch mean {kern_ms:.4f} ms "
+        f"(min {min(per_launch_ms):.4f}, max {max(per_launch_ms):.4f}), wall {wall * 1e3:.1f} ms")
+
+    alg_bytes = scan_bytes(w)
+    flops = scan_flops(w)
+    achieved_gbs = alg_bytes / (kern_ms / 1e3) / 1e9
+    achieved_tfs = flops / (kern_ms / 1e3) / 1e12
+    kernel_src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_bf16.hip")
+    traffic = None
+    if path != "blelloch" and w.dk == 128 and w.chunk == 64 and bf:
+        traffic = measured_traffic(kernel_src, f"chunk_mfma_{w.name}_traffic.txt")
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "T": w.T,
+                   "dk": w.dk, "dv": w.dv, "chunk": w.chunk, "path": path,
+                   "io_dtype": w.dtype, "state_dtype": "f32"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "chunk_mfma_kernel" if path != "blelloch" else "blelloch path (all kernels)",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel_ms": kern_ms,
+        },
+        "mfma": {
+            "achieved_tflops": achieved_tfs,
+            "peak_tflops": BF16_MFMA_PEAK_TFS,
+            "frac": achieved_tfs / BF16_MFMA_PEAK_TFS,
+            "flops_per_launch": flops,
+            "count": "executed dense-tile flops of the chunk algorithm",
+        },
+        "head_tokens_per_s": w.B * w.H * w.T / (ms_per_step / 1e3),
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle on {args.cpu_heads} heads")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
