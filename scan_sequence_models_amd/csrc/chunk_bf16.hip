@@ -71,6 +71,7 @@ struct Smem {
     float A[C * LA];        // strict-lower A (fp32)
     float Tm[C * LA];       // T = (I + A)^-1 (fp32, lower blocks)
     float X[2][16 * LX];    // solve scratch
+    uint16_t O[C * LT];     // output tile of the slice, [token][value] (bf16)
     float g[C], gam[C], dec[C], bet[C];
 };
 
@@ -114,6 +115,14 @@ __device__ __forceinline__ float quad_sum(float x) {
     return x;
 }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits
+// for every outstanding global load and store of the wave (vmcnt), which would
+// stall on the next chunk's prefetch and on the o stores at every barrier.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Registers holding the next chunk while the current one is computed.
 struct Prefetch {
     uint4 q[4], k[4], v[2];
@@ -126,7 +135,7 @@ __device__ __forceinline__ void load_chunk(Prefetch& p, int n, int T, size_t qk_
                                            const uint16_t* __restrict__ k,
                                            const uint16_t* __restrict__ v,
                                            const float* __restrict__ alpha,
-                                           const float* __restrict__ beta, int tid) {
+                                           const float* __restrict__ beta, int tid, bool vzero) {
     const int c0 = n * C;
     const int jc = tid & 15, tg = tid >> 4;  // q/k: rows 4tg..4tg+3, keys 8jc..8jc+7
 #pragma unroll
@@ -140,8 +149,9 @@ __device__ __forceinline__ void load_chunk(Prefetch& p, int n, int T, size_t qk_
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const int tok = c0 + 2 * vt + m;
-        p.v[m] = tok < T ? *reinterpret_cast<const uint4*>(v + v_base + (size_t)tok * DV + 8 * vc)
-                         : make_uint4(0, 0, 0, 0);
+        p.v[m] = tok < T && !vzero
+                     ? *reinterpret_cast<const uint4*>(v + v_base + (size_t)tok * DV + 8 * vc)
+                     : make_uint4(0, 0, 0, 0);
     }
     const int tok = c0 + (tid & 63);
     if (tid < 64) p.ab = tok < T ? alpha[a_base + tok] : 1.f;
@@ -201,57 +211,99 @@ __device__ __forceinline__ void store_chunk(Smem& sm, const Prefetch& p, int tid
 constexpr uint64_t kTileI = 0x3333222110ull;
 constexpr uint64_t kTileJ = 0x3210210100ull;
 
-template <int MODE>
-__global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
-    int BH, int T, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ alpha,
-    const float* __restrict__ beta, const float* __restrict__ S0, uint16_t* __restrict__ o,
-    float* __restrict__ ST) {
-    constexpr bool GDN = MODE == 0;
-    __shared__ Smem sm;
-
-    // both value slices of a head on one XCD when the grid allows it
-    int bh, sl;
-    const int x = blockIdx.x;
-    if ((BH & 7) == 0) {
-        const int xcd = x & 7, j = x >> 3;
-        bh = (j >> 1) * 8 + xcd;
-        sl = j & 1;
-    } else {
-        bh = x >> 1;
-        sl = x & 1;
+// Writes the staged output tile of chunk n (64 tokens x 64 values of this
+// slice) with 16-byte stores: 128 contiguous bytes per token row.
+__device__ __forceinline__ void flush_o(const Smem& sm, uint16_t* __restrict__ o, size_t o_base,
+                                       int n, int T, int tid) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int e = tid + m * NT;           // 512 pieces of 8 values
+        const int t = e >> 3, c = (e & 7) * 8;
+        if (n * C + t < T)
+            *reinterpret_cast<uint4*>(o + o_base + (size_t)(n * C + t) * DV + c) =
+                *reinterpret_cast<const uint4*>(&sm.O[t * LT + c]);
     }
-    const int r0 = sl * DVS;
+}
+
+// Work unit = (head, leaf): a run of consecutive chunks of one head, walked in
+// order by 2 (or 4) workgroups, one per 64-row slice of the state.
+//  kSequential:    one leaf per head (all chunks); S_in = S0 [heads][DV][DK] or
+//                  null (zero); S_out = S_T or null; o written.
+//  kLeafAggregate: 4 slices; slices 0-1 carry the value rows of f starting
+//                  from 0, slices 2-3 carry the rows of E starting from the
+//                  identity with v = 0, so that after the leaf S_in E + f is
+//                  the leaf's action.  S_out = [units][f rows; E rows][DK].
+//  kLeafOutput:    S_in = state entering each leaf [units][DV][DK]; o written;
+//                  the leaf job.last_leaf writes S_T to S_out (if not null).
+template <int MODE, int ROLE>
+__global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(const ChunkJob job) {
+    constexpr bool GDN = MODE == 0;
+    constexpr int NS = ROLE == kLeafAggregate ? 4 : 2;  // 64-row slices per unit
+    __shared__ Smem sm;
+    const uint16_t* __restrict__ q = job.q;
+    const uint16_t* __restrict__ k = job.k;
+    const uint16_t* __restrict__ v = job.v;
+    const float* __restrict__ alpha = job.alpha;
+    const float* __restrict__ beta = job.beta;
+    uint16_t* __restrict__ o = job.o;
+    const int T = job.T;
+
+    // all slices of a unit on one XCD when the grid allows it (blocks are dealt
+    // round-robin over the 8 XCDs), so their repeated q/k reads share an L2
+    const int units = job.heads * job.leaves;
+    int u, sl;
+    const int x = blockIdx.x;
+    if ((units & 7) == 0) {
+        const int xcd = x & 7, j = x >> 3;
+        u = (j / NS) * 8 + xcd;
+        sl = j % NS;
+    } else {
+        u = x / NS;
+        sl = x % NS;
+    }
+    const int head = u / job.leaves, leaf = u - head * job.leaves;
+    const int nb = leaf * job.leaf_chunks;
+    const int ne = min(nb + job.leaf_chunks, job.nchunks);
+    const bool erows = ROLE == kLeafAggregate && sl >= 2;
+    const int r0 = (sl & 1) * DVS;  // first value row (or E row) of the slice
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n16 = lane & 15, g4 = lane >> 4;
-    const size_t qk_base = (size_t)bh * T * DK;
-    const size_t v_base = (size_t)bh * T * DV + r0;
-    const size_t a_base = (size_t)bh * T;
-    const size_t s_base = ((size_t)bh * DV + r0 + 16 * w + n16) * DK;
+    const int row = r0 + 16 * w + n16;  // state row held by this lane
+    const size_t qk_base = (size_t)head * T * DK;
+    const size_t v_base = (size_t)head * T * DV + r0;
+    const size_t a_base = (size_t)head * T;
 
-    // state: lane (n, g) of tile jb holds S^T[16 jb + 4g + r][16 w + n] = S[r0+16w+n][16jb+4g+r]
+    // state: lane (n, g) of tile jb holds S^T[16 jb + 4g + r][16 w + n] = S[row][16jb+4g+r]
     f32x4 sacc[8];
+    if (ROLE == kLeafAggregate) {
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb)
-        sacc[jb] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_base + 16 * jb + 4 * g4)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[jb][r] = erows && 16 * jb + 4 * g4 + r == row ? 1.f : 0.f;
+    } else {
+        const size_t sb = ((size_t)(ROLE == kSequential ? head : u) * DV + row) * DK;
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+            sacc[jb] = job.S_in ? *reinterpret_cast<const f32x4*>(job.S_in + sb + 16 * jb + 4 * g4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     Prefetch pf;
-    load_chunk<MODE>(pf, 0, T, qk_base, v_base, a_base, q, k, v, alpha, beta, tid);
-    const int nchunks = (T + C - 1) / C;
-    for (int n = 0; n < nchunks; ++n) {
-        const int c0 = n * C;
-        __syncthreads();  // every wave is done with the previous chunk's tiles
+    if (nb < ne)
+        load_chunk<MODE>(pf, nb, T, qk_base, v_base, a_base, q, k, v, alpha, beta, tid, erows);
+    for (int n = nb; n < ne; ++n) {
+        lds_barrier();  // every wave is done with the previous chunk's tiles
+        if (o && n > nb) flush_o(sm, o, v_base, n - 1, T, tid);
         store_chunk<MODE>(sm, pf, tid);
-        if (n + 1 < nchunks)
-            load_chunk<MODE>(pf, n + 1, T, qk_base, v_base, a_base, q, k, v, alpha, beta, tid);
+        if (n + 1 < ne)
+            load_chunk<MODE>(pf, n + 1, T, qk_base, v_base, a_base, q, k, v, alpha, beta, tid, erows);
         // upper blocks of P inside the used contraction ranges must read as zero
         for (int e = tid; e < 2 * 16 * 16; e += NT) {
             const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
             const int t = 32 * blk + rr, s = 32 * blk + 16 + cc;
             sm.P[t * LT + s] = 0;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- k-Gram (A) and masked decayed scores (P), lower 16x16 blocks ----
         const int njobs = GDN ? 20 : 10;
@@ -280,7 +332,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
         }
 
         if constexpr (GDN) {
-            __syncthreads();
+            lds_barrier();
             // ---- UT solve: diagonal 16x16 blocks, wave w inverts block w ----
             {
                 const int c = lane >> 2, sub = lane & 3;
@@ -301,7 +353,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int m = 0; m < 4; ++m) sm.Tm[(base + 4 * m + sub) * LA + base + c] = xs[m];
             }
-            __syncthreads();
+            lds_barrier();
             // ---- off-diagonal blocks: T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ ----
             // product helpers (fp32 MFMA, 16x16x4): lane (n, g)
             auto mul_lds = [&](const float* X, int ldx, const float* Y, int ldy, f32x4 acc) {
@@ -338,7 +390,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
             } else {              // X_31 = A_31 T_11
                 keep = mul_lds(blkA(3, 1), LA, blkT(1, 1), LA, z);
             }
-            __syncthreads();
+            lds_barrier();
             if (w == 0) {         // X_20 = A_20 T_00 + A_21 T_10
                 keep = mul_lds(blkA(2, 1), LA, blkT(1, 0), LA, mul_lds(blkA(2, 0), LA, blkT(0, 0), LA, z));
                 put(sm.X[1], LX, keep, 1.f);
@@ -350,14 +402,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
                 const f32x4 t = mul_lds(blkT(3, 2), LA, sm.X[0], LX, z);
                 put(blkT(3, 1), LA, mul_acc(blkT(3, 3), LA, keep, t), -1.f);
             }
-            __syncthreads();
+            lds_barrier();
             if (w == 0) {         // T_20 = -T_22 X_20
                 put(blkT(2, 0), LA, mul_acc(blkT(2, 2), LA, keep, z), -1.f);
             } else if (w == 1) {  // T_30 = -(T_32 X_20 + T_33 X_30)
                 const f32x4 t = mul_lds(blkT(3, 2), LA, sm.X[1], LX, z);
                 put(blkT(3, 0), LA, mul_acc(blkT(3, 3), LA, keep, t), -1.f);
             }
-            __syncthreads();
+            lds_barrier();
             // ---- bf16 right-hand-side factors: T diag(beta), T diag(beta gamma) ----
             for (int e = tid; e < C * C; e += NT) {
                 const int t = e >> 6, s = e & 63;
@@ -366,7 +418,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
                 sm.Tb[t * LT + s] = f32_to_bf16(tv * b);
                 sm.Tbg[t * LT + s] = f32_to_bf16(tv * b * sm.gam[s]);
             }
-            __syncthreads();
+            lds_barrier();
             // ---- W^T = K^T (T diag(beta gamma))^T; stored as -W [token][key] ----
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -385,7 +437,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- state-dependent part; wave w owns value columns [16w, 16w+16) ----
         bf16x8 sb[4];  // S^T as B operands, contraction over keys (permuted)
@@ -437,9 +489,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tb + 4 * g4 + r;
-                if (c0 + t < T)
-                    o[((size_t)bh * T + c0 + t) * DV + r0 + 16 * w + n16] =
-                        f32_to_bf16(sm.gam[t] * qs[r] + pu[r]);
+                sm.O[t * LT + 16 * w + n16] = f32_to_bf16(sm.gam[t] * qs[r] + pu[r]);
             }
         }
 
@@ -468,10 +518,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(
         }
     }
 
-    if (ST) {
+    if (o && ne > nb) {
+        lds_barrier();
+        flush_o(sm, o, v_base, ne - 1, T, tid);
+    }
+    float* dst = nullptr;
+    if (ROLE == kSequential && job.S_out) dst = job.S_out + ((size_t)head * DV + row) * DK;
+    if (ROLE == kLeafAggregate) dst = job.S_out + ((size_t)u * (DV + DK) + sl * DVS + 16 * w + n16) * DK;
+    if (ROLE == kLeafOutput && job.S_out && leaf == job.last_leaf)
+        dst = job.S_out + ((size_t)head * DV + row) * DK;
+    if (dst) {
 #pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-            *reinterpret_cast<f32x4*>(ST + s_base + 16 * jb + 4 * g4) = sacc[jb];
+        for (int jb = 0; jb < 8; ++jb) *reinterpret_cast<f32x4*>(dst + 16 * jb + 4 * g4) = sacc[jb];
     }
 }
 
@@ -482,22 +540,43 @@ bool chunk_mfma_supported(int mode, int dk, int dv, int chunk) {
     return dk == DK && dv == DV && chunk == C;
 }
 
+template <int MODE>
+static hipError_t launch_role(int role, const ChunkJob& job, hipStream_t stream) {
+    const int units = job.heads * job.leaves;
+    const dim3 block(NT);
+    if (role == kSequential)
+        hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kSequential>), dim3(2 * units), block, 0, stream, job);
+    else if (role == kLeafAggregate)
+        hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kLeafAggregate>), dim3(4 * units), block, 0, stream, job);
+    else
+        hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kLeafOutput>), dim3(2 * units), block, 0, stream, job);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_job(int mode, int role, const ChunkJob& job, hipStream_t stream) {
+    return mode == 0 ? launch_role<0>(role, job, stream) : launch_role<1>(role, job, stream);
+}
+
 hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk, const void* q,
                              const void* k, const void* v, const float* alpha, const float* beta,
                              const float* S0, void* o, float* ST, hipStream_t stream) {
     (void)dk; (void)dv; (void)chunk;
-    const dim3 grid((unsigned)(2 * BH)), block(NT);
-    const uint16_t* qq = static_cast<const uint16_t*>(q);
-    const uint16_t* kk = static_cast<const uint16_t*>(k);
-    const uint16_t* vv = static_cast<const uint16_t*>(v);
-    uint16_t* oo = static_cast<uint16_t*>(o);
-    if (mode == 0)
-        hipLaunchKernelGGL(chunk_mfma_kernel<0>, grid, block, 0, stream, BH, T, qq, kk, vv, alpha,
-                           beta, S0, oo, ST);
-    else
-        hipLaunchKernelGGL(chunk_mfma_kernel<1>, grid, block, 0, stream, BH, T, qq, kk, vv, alpha,
-                           beta, S0, oo, ST);
-    return hipGetLastError();
+    ChunkJob job{};
+    job.q = static_cast<const uint16_t*>(q);
+    job.k = static_cast<const uint16_t*>(k);
+    job.v = static_cast<const uint16_t*>(v);
+    job.alpha = alpha;
+    job.beta = beta;
+    job.o = static_cast<uint16_t*>(o);
+    job.S_in = S0;
+    job.S_out = ST;
+    job.heads = BH;
+    job.T = T;
+    job.nchunks = (T + C - 1) / C;
+    job.leaves = 1;
+    job.leaf_chunks = job.nchunks;
+    job.last_leaf = 0;
+    return launch_chunk_job(mode, kSequential, job, stream);
 }
 
 }  // namespace gds
