@@ -119,6 +119,10 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=128,
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB before the timed "
+                         "steps (a known-size kernel that calibrates rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -166,6 +170,14 @@ def main():
         gds.scan_fwd(q, k, v, alpha, beta, S0, chunk=w.chunk, path=path,
                      leaf_chunks=args.leaf_chunks, o=o, ST=ST, workspace=ws)
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
