@@ -58,6 +58,17 @@ def source_sha(path: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
+def decode_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode_step over all states: the fp32 state
+    read and written once, q, k, v read and o written once, alpha (+ beta)."""
+    es = 2 if w.dtype == "bf16" else 4
+    N = w.B * w.H
+    b = N * w.dv * w.dk * 4 * 2
+    b += N * (2 * w.dk + 2 * w.dv) * es
+    b += N * 4 * (2 if w.mode == "gdn" else 1)
+    return b
+
+
 def measured_traffic(kernel_src: str, summary: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when there is none or the kernel source changed since it was taken."""
@@ -108,16 +119,160 @@ def cpu_baseline(w, heads: int):
     }
 
 
+def cpu_baseline_decode(w, states: int):
+    """The float64 oracle's decode step on the first ``states`` states of ``w``,
+    all of the workload's steps each."""
+    import numpy as np
+
+    import oracle
+    from scan_sequence_models_amd import inputs as I
+
+    S0, q, k, v, a, be = I.decode_inputs(w, N=states, threads=16)
+    S = S0.astype(np.float64)
+    oracle.build(force=False)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    for t in range(w.steps):
+        oracle.decode_step(w.mode, q[t], k[t], v[t], a[t], None if be is None else be[t], S,
+                           threads=threads)
+    sec = time.perf_counter() - t0
+    state_steps = states * w.steps
+    return {
+        "value": state_steps / w.H / sec,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{states} of {w.B * w.H} states x {w.steps} steps ({state_steps} state-steps "
+                  f"= {state_steps // w.H} tokens of all {w.H} heads), float64, {sec:.2f} s",
+        "seconds": sec,
+    }
+
+
+def timed(step, K: int, dev):
+    """Run step(0..K-1) back to back on the current stream between two HIP
+    events (after a device synchronize); returns (event span in ms, wall s)."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), time.perf_counter() - t0
+
+
+def copy_probe(mib: int, dev):
+    """One plain device copy of ``mib`` MiB (a kernel of known traffic that
+    calibrates the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)."""
+    if not mib:
+        return
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_decode(args, w):
+    """decode_step over all B*H states, ``steps`` launches back to back on the
+    same states (in place), each with its own token."""
+    import numpy as np
+    import torch
+
+    import scan_sequence_models_amd as gds
+    from scan_sequence_models_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N = w.B * w.H
+    nsteps = w.steps
+    log(f"bench: generating {w.name} (N={N} states, d={w.dk}, {nsteps} tokens each)")
+    S0, q, k, v, a, be = I.decode_inputs(w, threads=16)
+    bf = w.dtype == "bf16"
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    S = up(S0)
+    q, k, v, a = up(q, bf), up(k, bf), up(v, bf), up(a)
+    be = up(be) if be is not None else None
+    o = torch.empty((N, w.dv), dtype=q.dtype, device=dev)
+
+    def step(t):
+        gds.decode_step(q[t], k[t], v[t], a[t], None if be is None else be[t], S, o=o)
+
+    copy_probe(args.copy_probe_mib, dev)
+
+    for i in range(args.warmup):
+        step(i % nsteps)
+    torch.cuda.synchronize()
+    K = args.steps if args.steps else nsteps
+    span_ms, wall = timed(lambda i: step(i % nsteps), K, dev)
+    ms_per_step = span_ms / K
+    kern_ms = ms_per_step  # one kernel launch per step
+    log(f"bench: {K} decode steps back to back, span {span_ms:.3f} ms "
+        f"({kern_ms * 1e3:.2f} us per launch), wall {wall * 1e3:.1f} ms")
+    alg = decode_bytes(w)
+    gbs = alg / (kern_ms / 1e3) / 1e9
+    src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "decode.hip")
+    result = {
+        "metric": "tokens/s decode_step (256 sequences x 16 heads, d=128); % HBM roofline",
+        "value": w.B * 1 / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "states": N, "sequences": w.B, "H": w.H,
+                   "dk": w.dk, "dv": w.dv, "io_dtype": w.dtype, "state_dtype": "f32"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": measured_traffic(src, f"decode_{w.name}_traffic.txt"),
+            "kernel": "decode_kernel",
+            "algorithmic_bytes_per_launch": alg,
+            "kernel_ms": kern_ms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle on {args.cpu_states} states")
+        result["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_states)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; decode workloads: the workload's token count)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gdn-b8h16t8192")
     ap.add_argument("--path", default="auto", choices=["auto", "sequential", "blelloch"])
     ap.add_argument("--leaf-chunks", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=128,
                     help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-states", type=int, default=4096,
+                    help="decode workloads: states the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB before the timed "
@@ -140,7 +295,9 @@ def main():
 
     w = I.WORKLOADS[args.workload]
     if w.path == "decode":
-        raise SystemExit("decode workloads are timed by their own tests, not by bench.py")
+        return bench_decode(args, w)
+    if args.steps is None:
+        args.steps = 20
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -170,37 +327,20 @@ def main():
         gds.scan_fwd(q, k, v, alpha, beta, S0, chunk=w.chunk, path=path,
                      leaf_chunks=args.leaf_chunks, o=o, ST=ST, workspace=ws)
 
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(args.copy_probe_mib, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    span_ms = starts[0].elapsed_time(ends[-1])
+    span_ms, wall = timed(lambda i: step(), args.steps, dev)
     ms_per_step = span_ms / args.steps
-    kern_ms = float(np.mean(per_launch_ms))
+    # the sequential path is one kernel launch per step; the long path's
+    # figure covers all of its kernels
+    kern_ms = ms_per_step
     tokens = w.B * w.T
     value = tokens / (ms_per_step / 1e3)
-    log(f"bench: {args.steps} steps, span {span_ms:.3f} ms, per launch mean {kern_ms:.4f} ms "
-        f"(min {min(per_launch_ms):.4f}, max {max(per_launch_ms):.4f}), wall {wall * 1e3:.1f} ms")
+    log(f"bench: {args.steps} steps back to back, span {span_ms:.3f} ms "
+        f"({kern_ms:.4f} ms per step), wall {wall * 1e3:.1f} ms")
 
     alg_bytes = scan_bytes(w)
     flops = scan_flops(w)

@@ -42,12 +42,26 @@ template <> struct io<uint16_t> {
     }
 };
 
-// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
-// every lane of the group receives the group's sum.
+// The value of the lane that DPP control word CTRL selects (all rows and banks).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float y) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G consecutive lanes (G in {4, 8, 16, 32, 64});
+// every lane of the group receives the group's sum.  Within a 16-lane row the
+// partners come from DPP (quad permutes, then the half-row and row mirrors);
+// across rows from a 32-lane swizzle and a 64-lane shuffle.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+    x += dpp_move<0xB1>(x);                          // lane ^ 1
+    x += dpp_move<0x4E>(x);                          // lane ^ 2
+    if constexpr (G >= 8) x += dpp_move<0x141>(x);   // row half mirror: the other quad of the 8
+    if constexpr (G >= 16) x += dpp_move<0x140>(x);  // row mirror: the other 8 of the row
+    if constexpr (G >= 32)                      // lane ^ 16 within 32 (bit-mode swizzle)
+        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    if constexpr (G >= 64) x += __shfl_xor(x, 32, kWave);
     return x;
 }
 

@@ -13,8 +13,11 @@
 // The work is HBM-bound (64 KB read + 64 KB written per 128x128 state, ~7 d^2
 // flop), so the kernel is organised around the stream: rows of S are
 // independent, a row of dk floats is covered by dk/4 lanes with one 16-byte
-// load each, and every thread issues all of its row loads before the first
-// reduction so that each wave keeps 16 loads in flight.
+// load each, and every thread issues all of its row loads before anything
+// else, so that each wave keeps 16 loads in flight; the token's v entries are
+// fetched up front too, the row reductions run on DPP lane permutes, and the
+// new state is written with non-temporal stores (it is not read again within
+// the step).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,36 +48,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
     const int sub = lane % L;
     const int rsub = lane / L;
 
-    const float4 k4 = io<E>::load4(k, (size_t)n * DK + sub * 4);
-    const float4 q4 = io<E>::load4(q, (size_t)n * DK + sub * 4);
-    const float kq = group_sum<L>(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
-    const float al = alpha[n];
-    const float be = MODE == 0 ? beta[n] : 0.f;
-
-    float* Sn = S + (size_t)n * dv * DK;
+    // The state rows first: every load of the block is in flight before any
+    // other memory operation.  Rows past dv (dv not a multiple of the block)
+    // are clamped to a valid row; their results are not stored.
+    f32x4* Sn = reinterpret_cast<f32x4*>(S + (size_t)n * dv * DK);
     int rows[kPasses];
-    float4 s[kPasses];
+    f32x4 s[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         rows[p] = rb * kRowsPerBlock + p * kRowsPerPass + wave * kRowsPerWavePass + rsub;
-        s[p] = rows[p] < dv ? *reinterpret_cast<const float4*>(Sn + (size_t)rows[p] * DK + sub * 4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int rc = rows[p] < dv ? rows[p] : dv - 1;
+        s[p] = Sn[(size_t)rc * (DK / 4) + sub];
     }
+    const float4 k4 = io<E>::load4(k, (size_t)n * DK + sub * 4);
+    const float4 q4 = io<E>::load4(q, (size_t)n * DK + sub * 4);
+    const float al = alpha[n];
+    const float be = MODE == 0 ? beta[n] : 0.f;
+    float vr[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+        vr[p] = io<E>::load(v, (size_t)n * dv + (rows[p] < dv ? rows[p] : dv - 1));
+    const float kq = group_sum<L>(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
+
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         float a = s[p].x * k4.x + s[p].y * k4.y + s[p].z * k4.z + s[p].w * k4.w;
         float b = s[p].x * q4.x + s[p].y * q4.y + s[p].z * q4.z + s[p].w * q4.w;
         a = group_sum<L>(a);
         b = group_sum<L>(b);
+        const float u = MODE == 0 ? be * (vr[p] - al * a) : vr[p];
+        f32x4 r;
+        r.x = al * s[p].x + u * k4.x;
+        r.y = al * s[p].y + u * k4.y;
+        r.z = al * s[p].z + u * k4.z;
+        r.w = al * s[p].w + u * k4.w;
         if (rows[p] < dv) {
-            const float vi = io<E>::load(v, (size_t)n * dv + rows[p]);
-            const float u = MODE == 0 ? be * (vi - al * a) : vi;
-            float4 r;
-            r.x = al * s[p].x + u * k4.x;
-            r.y = al * s[p].y + u * k4.y;
-            r.z = al * s[p].z + u * k4.z;
-            r.w = al * s[p].w + u * k4.w;
-            *reinterpret_cast<float4*>(Sn + (size_t)rows[p] * DK + sub * 4) = r;
+            __builtin_nontemporal_store(r, Sn + (size_t)rows[p] * (DK / 4) + sub);
             if (sub == 0) io<E>::store(o, (size_t)n * dv + rows[p], al * b + kq * u);
         }
     }
