@@ -13,9 +13,9 @@
 //
 //   A    = strict_lower(diag(beta) (Gamma * K K^T))        k-Gram      (MFMA)
 //   T    = (I + A)^-1                                       UT solve    (fp32)
-//   W    = T diag(beta gamma) K,   U~ = T diag(beta) V      WY factors  (MFMA)
+//   W    = T diag(beta gamma) K                             WY factor   (MFMA)
 //   P    = (Q K^T) * Gamma * M_incl                         scores      (MFMA)
-//   U    = U~ - W S^T                                       (MFMA, needs S)
+//   U    = T diag(beta) V - W S^T                           (MFMA, needs S)
 //   O    = diag(gamma) Q S^T + P U                          (MFMA, needs S)
 //   S   <- gamma_C S + U^T diag(dec) K                      (MFMA, fp32 state)
 //
@@ -24,29 +24,33 @@
 // Mapping onto gfx950.  A workgroup of 8 waves owns one head and a 64-row slice
 // of its value channels (B*H*2 workgroups on the sequential path); all slices of
 // a head go to one XCD (blocks are dealt round-robin over the 8 XCDs) so their
-// repeated q/k reads share that XCD's L2.  The waves specialise:
+// repeated q/k reads share that XCD's L2.  The waves specialise and work on
+// three chunks at once:
 //   waves 0-1      state waves: wave w keeps the 32 value columns [32w, 32w+32)
 //                  of S^T (128 keys, fp32) in four 32x32 MFMA accumulator tiles
-//                  for the whole sequence and runs the S-dependent products of
-//                  chunk n;
-//   waves 2,3,6,7  k-Gram and scores, the off-diagonal UT-solve blocks and W
-//                  for chunk n+1;
-//   waves 4-5      q tile, transposed k/v tiles, the diagonal UT-solve blocks
-//                  and U~ for chunk n+1.
-// Chunk n+1's factors are built while chunk n's state pass runs; they meet
-// through LDS (double-buffered where the phase order needs it).  All waves
-// pass the same seven barriers per chunk.  Every product is
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation, bf16 operands) except the UT
-// solve: its 16x16 diagonal blocks run in fp32 on the VALU and its off-diagonal
-// blocks on the fp32 MFMA (16x16x4).
+//                  for the whole sequence and runs chunk n's S-dependent
+//                  products (U, O, the state update);
+//   waves 2,3,6,7  chunk n+1's k-Gram tiles and UT solve: the two diagonal
+//                  32x32 blocks of T are inverted inside one wave each (no
+//                  barrier), the off-diagonal block by two waves, then W;
+//   waves 4-5      load chunk n+2 (coalesced 16-byte rows), stage it in LDS
+//                  (q, k row-major; k^T, v^T transposed), build its gates, and
+//                  compute two of chunk n+1's score tiles.
+// Everything meets through LDS and all waves pass the same three barriers per
+// chunk.  Products are v_mfma_f32_32x32x16_bf16 (fp32 accumulation, bf16
+// operands) except the UT solve, which stays in fp32: diagonal 16x16 blocks by
+// forward substitution on the VALU, off-diagonal blocks on the fp32 MFMA
+// (16x16x4).
 //
 // Operand trick: a 32x32 accumulator tile holds, in lane (n, h), rows
 // 8b + 4h + r (b, r < 4) of column n.  Elements 8s..8s+7 of a lane are then the
 // 8 rows {16s + 8b' + 4h + r}: a B operand whose contraction index is the
-// tile's row.  The state and U tiles are laid out with bits 2 and 3 of the row
-// index swapped (row rho holds key/token perm5(rho)), so those 8 rows are the 8
-// consecutive keys/tokens 16s + 8h .. 16s + 8h + 7, and the matching A operand
-// is one natural 16-byte LDS or global read.
+// tile's row.  Rows are therefore numbered with bits 2 and 3 swapped (perm5):
+// accumulator row rho holds key/token perm5(rho), and elements 8s..8s+7 are the
+// consecutive keys/tokens 16s + 8h .. 16s + 8h + 7.  Every LDS array whose
+// rows are read as an A operand stores logical row r at physical row perm5(r),
+// so that all operand reads are natural 16-byte row reads (conflict-free with
+// the padded strides below).
 //
 // Tokens past T in the last chunk are identity tokens (alpha = 1, beta = 0,
 // q = k = v = 0), which leave S unchanged; their outputs are not written.
@@ -61,36 +65,33 @@ constexpr int DK = 128;      // key channels
 constexpr int DV = 128;      // value channels
 constexpr int DVS = 64;      // value channels per workgroup
 constexpr int NT = 512;      // 8 waves
-constexpr int LW = DK + 8;   // row stride (elements) of -W [token][key]
-constexpr int LT = C + 8;    // row stride of [*][token] bf16 tiles
-constexpr int LA = C + 4;    // row stride of fp32 64x64 tiles
-constexpr int LU = DVS + 4;  // row stride of U~ [token][value] (fp32)
-constexpr int LX = 16 + 4;   // row stride of fp32 16x16 scratch tiles
+constexpr int LW = DK + 8;   // row stride (elements) of [token][key] bf16 arrays
+constexpr int LT = C + 8;    // row stride of [*][token] bf16 arrays
+constexpr int LS = 32 + 4;   // row stride of fp32 32x32 solve tiles
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Gates of one chunk: g = in-chunk cumulative ln alpha, gamma = e^g,
+// dec = e^(g_C - g), beta; gl = g log2(e) and gb = gl + log2(beta) feed the
+// masks as exp2(gl_t - gl_s) = Gamma_ts and exp2(gb_t - gl_s) = beta_t Gamma_ts.
 struct Gates {
-    float g[C], gam[C], dec[C], bet[C];
+    float g[C], gam[C], dec[C], bet[C], gl[C], gb[C];
 };
 
+// Shared memory of one workgroup (158 KB).  Chunk c's gates live in gate[c % 3],
+// its q in Q[c % 2], its k^T in KT[c % 2]; the other arrays are single.
 struct Smem {
-    uint16_t Q[C * LW];       // q of the chunk the state waves consume next [token][key]
-    uint16_t W[C * LW];       // -W of the chunk the state waves consume next
-    uint16_t KT[2][DK * LT];  // k transposed [key][token] (token granules swizzled)
-    uint16_t P[2][C * LT];    // scores [token][token]
-    float Ut[C * LU];         // U~ [token][value]
-    Gates gate[2];
-    union {
-        float A[C * LA];      // strict-lower A (fp32), solve phases
-        struct {
-            uint16_t Tb[C * LT];   // T diag(beta)
-            uint16_t Tbg[C * LT];  // T diag(beta gamma)
-        } t;
-    } a;
-    float Tm[C * LA];         // T = (I + A)^-1 (fp32, lower blocks)
-    uint16_t VT[DVS * LT];    // v slice transposed [value][token] (swizzled)
-    float X[2][16 * LX];      // solve scratch
-    float gs[4][2][C];        // per Gram wave: g and beta of its chunk
+    uint16_t Q[2][C * LW];    // q [token][key]                        (rows perm5)
+    uint16_t K[C * LW];       // k [token][key]                        (rows perm5)
+    uint16_t W[C * LW];       // -W [token][key]                       (rows perm5)
+    uint16_t KT[2][DK * LT];  // k^T [key][token]     (rows perm5, token granules swizzled)
+    uint16_t VT[DVS * LT];    // v slice^T [value][token]              (token granules swizzled)
+    uint16_t P[C * LT];       // scores [token][token]                 (rows perm5)
+    uint16_t Tb[C * LT];      // T diag(beta) [token][token]           (rows perm5)
+    uint16_t Tbg[C * LT];     // T diag(beta gamma)                    (rows perm5)
+    float Tm[2][32 * LS];     // diagonal 32x32 blocks of A, then of T (fp32, natural)
+    float Abl[32 * LS];       // A rows 32..63, columns 0..31 (fp32, natural)
+    Gates gate[3];
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -102,7 +103,6 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 template <int OFF>
 __device__ __forceinline__ bf16x8 half8(const f32x16& x) {
     bf16x8 r;
@@ -120,12 +120,6 @@ __device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) { return (a >
 __device__ __forceinline__ uint32_t word(const uint4& u, int i) {
     return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
-// sum over the 4 lanes of a quad (DPP quad permutes)
-__device__ __forceinline__ float quad_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-    return x;
-}
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits
 // for every outstanding global load and store of the wave (vmcnt), which would
 // stall on prefetches and output stores at every barrier.  The memory clobber
@@ -133,24 +127,23 @@ __device__ __forceinline__ float quad_sum(float x) {
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value,
 // so that role and tile choices compile to scalar branches.
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// Row permutation of the state and U tiles: swap bits 2 and 3.
+// Row permutation: swap bits 2 and 3 (an involution that keeps 32-row blocks).
 __device__ __forceinline__ int perm5(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 // Key (state tile) or token (U / O tile) held by accumulator element e of a
-// lane in half h of the wave.
+// lane in half h of the wave: perm5 of the accumulator row.
 __device__ __forceinline__ int elem_index(int tile, int e, int h) {
     return 32 * tile + 16 * (e >> 3) + 8 * h + 4 * ((e >> 2) & 1) + (e & 3);
 }
-// [row][token] tiles with 8-token granules XOR-swizzled by row, so that the
-// transposed 8-byte stores spread over all LDS banks.
-__device__ __forceinline__ int tsw(int row, int tok) {
-    return row * LT + ((((tok >> 3) ^ (row >> 3)) & 7) << 3) + (tok & 7);
+// [row][token] arrays with 8-token granules XOR-swizzled by row, so that the
+// transposed 8-byte stores spread over the LDS banks (prow: physical row).
+__device__ __forceinline__ int tsw(int prow, int tok) {
+    return prow * LT + ((((tok >> 3) ^ (prow >> 3)) & 7) << 3) + (tok & 7);
 }
 
 // Rows of chunk m of one head's [T][ld] bf16 tensor, read through a buffer
@@ -170,13 +163,14 @@ struct Rows {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * ld + col) * 2, 0, 0));
     }
 };
-// Per-token float of chunk m (alpha or beta); tokens past T read as `pad`.
-__device__ __forceinline__ float ldtok(const float* head, int m, int i, int T, float pad) {
+// Per-token float of chunk m (alpha or beta); tokens past T read as 0.  The
+// caller substitutes any other pad value where it uses the result, so that the
+// load stays in flight until then.
+__device__ __forceinline__ float ldtok(const float* head, int m, int i, int T) {
     const int valid = __builtin_amdgcn_readfirstlane(min(max(T - m * C, 0), C));
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(head + (size_t)m * C), (short)0, valid * 4, 0x00020000);
-    const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
-    return v + (i < valid ? 0.f : pad);  // the hardware returns 0 past the end
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
 }
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
 // row broadcasts of lanes 15 and 31).
@@ -190,37 +184,141 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x;
 }
 
-// 16x16 block products of the UT solve (fp32 MFMA, 16x16x4); lane (n16, g4).
+// 16x16 block products of the UT solve (fp32 MFMA 16x16x4); lane (n16, g4)
+// holds rows 4 g4 .. 4 g4 + 3 of column n16 of a result.
 struct Solve {
-    Smem& sm;
     int n16, g4;
-    // acc += X * Y, both 16x16 in LDS (natural k order)
-    __device__ f32x4 mul_lds(const float* X, int ldx, const float* Y, int ldy, f32x4 acc) const {
+    // acc += X Y, both 16x16 blocks of fp32 tiles with row stride LS
+    __device__ __forceinline__ f32x4 mul_lds(const float* X, const float* Y, f32x4 acc) const {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            acc = mfma4(X[n16 * ldx + 4 * kk + g4], Y[(4 * kk + g4) * ldy + n16], acc);
+            acc = mfma4(X[n16 * LS + 4 * kk + g4], Y[(4 * kk + g4) * LS + n16], acc);
         return acc;
     }
-    // acc += X * Y, X in LDS, Y an accumulator tile (k = 4 g4 + kk)
-    __device__ f32x4 mul_acc(const float* X, int ldx, f32x4 Yacc, f32x4 acc) const {
-        const f32x4 xr = *reinterpret_cast<const f32x4*>(&X[n16 * ldx + 4 * g4]);
+    // acc += X Y, X a block in LDS, Y an accumulator block (k = 4 g4 + kk)
+    __device__ __forceinline__ f32x4 mul_acc(const float* X, f32x4 Yacc, f32x4 acc) const {
+        const f32x4 xr = *reinterpret_cast<const f32x4*>(&X[n16 * LS + 4 * g4]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) acc = mfma4(xr[kk], Yacc[kk], acc);
         return acc;
     }
-    __device__ float* blkA(int I, int J) const { return &sm.a.A[16 * I * LA + 16 * J]; }
-    __device__ float* blkT(int I, int J) const { return &sm.Tm[16 * I * LA + 16 * J]; }
-    __device__ void put(float* dst, int ld, f32x4 acc, float sign) const {
+    __device__ __forceinline__ void put(float* dst, f32x4 acc, float sign) const {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * ld + n16] = sign * acc[r];
+        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * LS + n16] = sign * acc[r];
     }
 };
+
+// sum over the 4 lanes of a quad (DPP quad permutes)
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+    return x;
+}
+// In place: the two 16x16 diagonal blocks of the fp32 32x32 tile X (unit lower
+// triangular I + A_bb, strictly lower part stored) are replaced by their
+// inverses, by forward substitution in fp32.  Lane (c, sub) owns column c of
+// both inverses and sums the terms j = sub (mod 4) of each row; a quad
+// reduction completes the row.  The two blocks are interleaved for ILP.
+__device__ __forceinline__ void diag_inverse2(float* X, int lane) {
+    const int c = lane >> 2, sub = lane & 3;
+    float a[2][16][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) a[b][r][mm] = X[(16 * b + r) * LS + 16 * b + 4 * mm + sub];
+    float xs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float p = a[b][r][0] * xs[b][0] + a[b][r][1] * xs[b][1] + a[b][r][2] * xs[b][2] +
+                      a[b][r][3] * xs[b][3];
+            p = quad_sum(p);
+            const float xr = (r == c ? 1.f : 0.f) - p;
+            if ((r & 3) == sub) xs[b][r >> 2] = xr;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) X[(16 * b + 4 * mm + sub) * LS + 16 * b + c] = xs[b][mm];
+}
 
 // B operand for contraction step kk (16 rows) from accumulator tiles:
 // tile kk/2, elements 8(kk%2) .. 8(kk%2)+7, rounded to bf16.
 template <int N>
 __device__ __forceinline__ bf16x8 sop(const f32x16 (&t)[N], int kk) {
     return (kk & 1) ? half8<8>(t[kk >> 1]) : half8<0>(t[kk >> 1]);
+}
+
+// One 32x32 k-Gram or score tile of chunk-local tokens, computed transposed:
+// acc[s][t] = sum_key Y[s][key] X[t][key] with s = 32J + row, t = 32I + column.
+// X and Y are [token][key] LDS arrays with rows perm5, read at natural rows, so
+// lane l32 holds column t = 32I + perm5(l32) and element e row
+// s = 32J + elem_index(0, e, h).
+__device__ __forceinline__ f32x16 gram_tile(const uint16_t* X, int I, const uint16_t* Y, int J,
+                                            int l32, int h) {
+    f32x16 acc = {};
+    const uint16_t* xr = X + (32 * I + l32) * LW + 8 * h;
+    const uint16_t* yr = Y + (32 * J + l32) * LW + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(yr + 16 * kk), lds8(xr + 16 * kk), acc);
+    return acc;
+}
+
+// Decay mask of tile (I, J): element e of lane (l32, h) is scaled by
+// e^(g_t - g_s) (times beta_t for A) where t >= s (t > s for A), else zeroed;
+// tiles below the diagonal (I > J) need no comparison.  Results in the same
+// layout, 4 consecutive s per element group.
+template <bool IS_A>
+__device__ __forceinline__ f32x16 mask_tile(const f32x16& acc, const Gates& G, int I, int J,
+                                            int l32, int h) {
+    const int t = 32 * I + perm5(l32);
+    const float et = IS_A ? G.gb[t] : G.gl[t];
+    f32x16 r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int s0 = 32 * J + elem_index(0, 4 * b, h);
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(&G.gl[s0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float d = __builtin_amdgcn_exp2f(et - gs[i]) * acc[4 * b + i];
+            if (I > J) r[4 * b + i] = d;
+            else r[4 * b + i] = (IS_A ? t > s0 + i : t >= s0 + i) ? d : 0.f;
+        }
+    }
+    return r;
+}
+
+// Scores tile (I, J) of chunk m, masked, packed to bf16 (lane's row of P:
+// physical row 32I + l32, columns 32J + elem_index(0, 4b, h) .. +3).
+__device__ __forceinline__ void score_tile(const Smem& sm, int qbuf, const Gates& G, int I, int J,
+                                           int l32, int h, uint2 (&out)[4]) {
+    const f32x16 acc = gram_tile(sm.Q[qbuf], I, sm.K, J, l32, h);
+    const f32x16 p = mask_tile<false>(acc, G, I, J, l32, h);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) out[b] = pack4(p[4 * b], p[4 * b + 1], p[4 * b + 2], p[4 * b + 3]);
+}
+__device__ __forceinline__ void store_score_tile(Smem& sm, int I, int J, int l32, int h,
+                                                 const uint2 (&p)[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<uint2*>(&sm.P[(32 * I + l32) * LT + 32 * J + elem_index(0, 4 * b, h)]) = p[b];
+}
+
+// k-Gram tile (I, J) of chunk m masked into A (fp32, natural indices, local to
+// the 32x32 destination tile `dst`).
+__device__ __forceinline__ void a_tile(const Smem& sm, const Gates& G, int I, int J, float* dst,
+                                       int l32, int h) {
+    const f32x16 acc = gram_tile(sm.K, I, sm.K, J, l32, h);
+    const f32x16 a = mask_tile<true>(acc, G, I, J, l32, h);
+    const int tl = perm5(l32);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<f32x4*>(&dst[tl * LS + elem_index(0, 4 * b, h)]) =
+            f32x4{a[4 * b], a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]};
 }
 
 struct Unit {
@@ -262,7 +360,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
     const int tid = threadIdx.x, lane = tid & 63, ib = wave_id();
     const int l32 = lane & 31, h = lane >> 5;
     const int T = job.T;
-    const int vcol = un.r0 + 32 * ib + l32;  // state row (value channel) of this lane
+    const int vl = 32 * ib + l32;   // value channel of this lane within the slice
+    const int vcol = un.r0 + vl;    // state row (value channel) of this lane
 
     // sacc[jt] element e = S[vcol][elem_index(jt, e, h)]
     f32x16 sacc[4];
@@ -290,45 +389,76 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             }
     }
 
+    // qacc[tt] = Q S^T of the chunk the next iteration reads out (old state)
+    f32x16 qacc[2];
+    auto q_state = [&](int c) {
+        const uint16_t* Q = sm.Q[c & 1];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            f32x16 acc = {};
+            const uint16_t* qr = &Q[(32 * tt + l32) * LW + 8 * h];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(qr + 16 * kk), sop(sacc, kk), acc);
+            qacc[tt] = acc;
+        }
+    };
+
+    lds_barrier();  // prologue: chunk nb staged
     for (int it = un.nb - 1; it < un.ne; ++it) {
         const bool act = it >= un.nb;
-        const int n = it, buf = n & 1;
-        const Gates& G = sm.gate[buf];
+        const int n = it;
+        const Gates& G = sm.gate[(n + 3) % 3];
         f32x16 uacc[2];
-        // ---- phase 1: U = U~ - W S^T ----
+        // ---- phase A: U = T diag(beta) V - W S^T ----
         if (act) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    uacc[tt][e] = sm.Ut[elem_index(tt, e, h) * LU + 32 * ib + l32];
                 if (GDN) {
-                    const uint16_t* wr = &sm.W[(32 * tt + perm5(l32)) * LW + 8 * h];
+                    f32x16 acc = {};
+                    const uint16_t* tr = &sm.Tb[(32 * tt + l32) * LT + 8 * h];
 #pragma unroll
-                    for (int kk = 0; kk < 8; ++kk)
-                        uacc[tt] = mfma32(lds8(wr + 16 * kk), sop(sacc, kk), uacc[tt]);
+                    for (int kk = 0; kk < 4; ++kk) {
+                        if (tt == 0 && kk >= 2) continue;  // T is lower triangular
+                        acc = mfma32(lds8(tr + 16 * kk), lds8(&sm.VT[tsw(vl, 16 * kk + 8 * h)]), acc);
+                    }
+                    const uint16_t* wr = &sm.W[(32 * tt + l32) * LW + 8 * h];
+#pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(wr + 16 * kk), sop(sacc, kk), acc);
+                    uacc[tt] = acc;
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const bf16x8 v8 = lds8(&sm.VT[tsw(vl, 32 * tt + 16 * s + 8 * h)]);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) uacc[tt][8 * s + i] = static_cast<float>(v8[i]);
+                    }
                 }
             }
         }
-        lds_barrier();  // 1
-        // ---- phases 2-3: O = diag(gamma) Q S^T + P U for token tile tt = phase - 2, write o ----
+        lds_barrier();  // A
+        // ---- phase B: O = diag(gamma) Q S^T + P U, written out; S^T <- gamma_C S^T + K^T diag(dec) U ----
+        if (act) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            if (act) {
-                f32x16 acc = {};
-                const uint16_t* qr = &sm.Q[(32 * tt + perm5(l32)) * LW + 8 * h];
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x16 acc = qacc[tt];
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(qr + 16 * kk), sop(sacc, kk), acc);
+                for (int b = 0; b < 2; ++b) {
+                    const f32x4 g0 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h]);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h + 4]);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[e] *= G.gam[elem_index(tt, e, h)];
-                const uint16_t* pr = &sm.P[buf][(32 * tt + perm5(l32)) * LT + 8 * h];
+                    for (int i = 0; i < 4; ++i) {
+                        acc[8 * b + i] *= g0[i];
+                        acc[8 * b + 4 + i] *= g1[i];
+                    }
+                }
+                const uint16_t* pr = &sm.P[(32 * tt + l32) * LT + 8 * h];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     if (tt == 0 && ks >= 2) continue;  // P is lower triangular
                     acc = mfma32(lds8(pr + 16 * ks), sop(uacc, ks), acc);
                 }
                 if (job.o) {
-                    uint16_t* orow = job.o + ((size_t)un.head * T + (size_t)n * C) * DV + un.r0 + 32 * ib + l32;
+                    uint16_t* orow = job.o + ((size_t)un.head * T + (size_t)n * C) * DV + vcol;
                     if ((n + 1) * C <= T) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e)
@@ -342,41 +472,40 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                     }
                 }
             }
-            lds_barrier();  // 2, 3
-        }
-        // ---- phase 4: S^T <- gamma_C S^T + K^T diag(dec) U ----
-        if (act) {
             bf16x8 db[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                f32x16 x = uacc[ks >> 1];
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(&G.dec[16 * ks + 8 * h]);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(&G.dec[16 * ks + 8 * h + 4]);
+                const f32x16& u = uacc[ks >> 1];
                 const int off = 8 * (ks & 1);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[off + i] *= G.dec[16 * ks + 8 * h + i];
-                db[ks] = (ks & 1) ? half8<8>(x) : half8<0>(x);
+                for (int i = 0; i < 4; ++i) {
+                    db[ks][i] = static_cast<__bf16>(u[off + i] * d0[i]);
+                    db[ks][4 + i] = static_cast<__bf16>(u[off + 4 + i] * d1[i]);
+                }
             }
             const float gC = G.gam[C - 1];
-            const uint16_t* KT = sm.KT[buf];
+            const uint16_t* KT = sm.KT[n & 1];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 f32x16 acc = sacc[jt] * gC;
-                const int row = 32 * jt + perm5(l32);
+                const int prow = 32 * jt + l32;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma32(lds8(&KT[tsw(row, 16 * ks + 8 * h)]), db[ks], acc);
+                for (int ks = 0; ks < 4; ++ks) acc = mfma32(lds8(&KT[tsw(prow, 16 * ks + 8 * h)]), db[ks], acc);
                 sacc[jt] = acc;
             }
         }
-        lds_barrier();  // 4
-        lds_barrier();  // 5
-        lds_barrier();  // 6
-        lds_barrier();  // 7
+        lds_barrier();  // B
+        // ---- phase C: Q S^T of chunk n+1 with the state entering it ----
+        if (n + 1 < un.ne) q_state(n + 1);
+        lds_barrier();  // C
     }
 
     float* dst = nullptr;
     if (ROLE == kSequential && job.S_out) dst = job.S_out + ((size_t)un.head * DV + vcol) * DK;
     if (ROLE == kLeafAggregate)
-        dst = job.S_out + ((size_t)(un.head * job.leaves + un.leaf) * (DV + DK) + un.sl * DVS +
-                           32 * ib + l32) * DK;
+        dst = job.S_out + ((size_t)(un.head * job.leaves + un.leaf) * (DV + DK) + un.sl * DVS + vl) * DK;
     if (ROLE == kLeafOutput && job.S_out && un.leaf == job.last_leaf)
         dst = job.S_out + ((size_t)un.head * DV + vcol) * DK;
     if (dst) {
@@ -394,338 +523,254 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
     }
 }
 
-// Inverse of the unit lower-triangular 16x16 diagonal block I + A_bb, by
-// forward substitution in fp32: lane (c, sub) owns column c of the inverse and
-// sums the terms s = sub (mod 4) of each row; a quad reduction completes it.
-__device__ __forceinline__ void diag_inverse(Smem& sm, int blk, int lane) {
-    const int c = lane >> 2, sub = lane & 3;
-    const int base = 16 * blk;
-    float a[16][4];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) a[r][mm] = sm.a.A[(base + r) * LA + base + 4 * mm + sub];
-    float xs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float p = a[r][0] * xs[0] + a[r][1] * xs[1] + a[r][2] * xs[2] + a[r][3] * xs[3];
-        p = quad_sum(p);
-        const float xr = (r == c ? 1.f : 0.f) - p;
-        if ((r & 3) == sub) xs[r >> 2] = xr;
-    }
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) sm.Tm[(base + 4 * mm + sub) * LA + base + c] = xs[mm];
-}
-
-// Tb / Tbg: T diag(beta) and T diag(beta gamma) in bf16, upper part zero.
-// Shared by the six prep waves (prep thread index p in 0..383).
-__device__ __forceinline__ void build_tb(Smem& sm, const Gates& G, int p) {
-    for (int piece = p; piece < C * C / 8; piece += 384) {
-        const int t = piece >> 3, s0 = (piece & 7) * 8;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sm.Tm[t * LA + s0]);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&sm.Tm[t * LA + s0 + 4]);
-        float tv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            tv[i] = s0 + i <= t ? x0[i] : 0.f;
-            tv[4 + i] = s0 + 4 + i <= t ? x1[i] : 0.f;
-        }
-        uint32_t b[4], bg[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = s0 + 2 * i;
-            const float e0 = tv[2 * i] * G.bet[s], e1 = tv[2 * i + 1] * G.bet[s + 1];
-            b[i] = f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
-            bg[i] = f32_to_bf16(e0 * G.gam[s]) | ((uint32_t)f32_to_bf16(e1 * G.gam[s + 1]) << 16);
-        }
-        *reinterpret_cast<uint4*>(&sm.a.t.Tb[t * LT + s0]) = make_uint4(b[0], b[1], b[2], b[3]);
-        *reinterpret_cast<uint4*>(&sm.a.t.Tbg[t * LT + s0]) = make_uint4(bg[0], bg[1], bg[2], bg[3]);
-    }
-}
-
 // ----------------------------------------------------------------------------
-// k-Gram / scores / UT solve / W waves (2, 3, 6, 7): chunk n+1
+// k-Gram / UT solve / W waves (2, 3, 6, 7 -> gi 0..3): chunk n+1
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int lane = threadIdx.x & 63, w = wave_id();
     const int gi = w == 2 ? 0 : w == 3 ? 1 : w == 6 ? 2 : 3;
     const int l32 = lane & 31, h = lane >> 5;
-    const int n16 = lane & 15, g4 = lane >> 4;
-    const int T = job.T;
-    const size_t qk_base = (size_t)un.head * T * DK;
-    const size_t a_base = (size_t)un.head * T;
+    const Solve sv{lane & 15, lane >> 4};
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    uint2 preg[4];  // gi 3: chunk m's score tile (1, 0), stored in phase C
 
-    // Operand rows of the wave's tiles: op0 = k rows [row0, row0+32),
-    // op1 = (gi == 0 ? k : q) rows [row1, row1+32).
-    //   gdn: gi 0: A00 (op0 op0), A10 (op1 op0);  gi 1: A11 (op0 op0), P11 (op1 op0);
-    //        gi 2: P00 (op1 op0);  gi 3: P10 (op1 op0).   gla: gi 1..3 as gdn's P tiles.
-    const uint16_t* src1 = gi == 0 ? job.k : job.q;
-    const int row0 = gi == 1 ? 32 : 0, row1 = gi == 2 ? 0 : 32;
-    uint4 op0[8], op1[8];
-    float pa = 1.f, pb = 0.f;  // alpha and beta of token `lane`
-    auto load_ops = [&](int m) {
-        const Rows r0(job.k + qk_base, m, T, DK), r1(src1 + qk_base, m, T, DK);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            op0[kk] = r0.at(row0 + l32, 16 * kk + 8 * h);
-            op1[kk] = r1.at(row1 + l32, 16 * kk + 8 * h);
-        }
-        pa = ldtok(job.alpha + a_base, m, lane, T, 1.f);
-        pb = GDN ? ldtok(job.beta + a_base, m, lane, T, 0.f) : 0.f;
-    };
-    if (un.nb < un.ne) load_ops(un.nb);
-    const Solve sv{sm, n16, g4};
-
+    lds_barrier();  // prologue
     for (int it = un.nb - 1; it < un.ne; ++it) {
         const int m = it + 1;
         const bool act = m < un.ne;
-        const int buf = m & 1;
-        Gates& G = sm.gate[buf];
-        // ---- phase 1: gates, k-Gram A and scores P of chunk m ----
+        const Gates& G = sm.gate[m % 3];
+        // ---- phase A: k-Gram tiles; diagonal 32x32 blocks of T in-wave ----
         if (act) {
-            const float x = wave_inclusive_sum(__logf(pa));
-            float* gsl = sm.gs[gi][0];
-            float* bsl = sm.gs[gi][1];
-            gsl[lane] = x;
-            bsl[lane] = pb;
-            if (gi == 0) {
-                const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-                G.g[lane] = x;
-                G.gam[lane] = __expf(x);
-                G.dec[lane] = __expf(last - x);
-                G.bet[lane] = pb;
+            if (GDN && gi <= 1) {
+                float* X = sm.Tm[gi];
+                a_tile(sm, G, gi, gi, X, l32, h);
+                diag_inverse2(X, lane);
+                // T_10 = -D_1 A_10 D_0 within the 32x32 block
+                const f32x4 mm = sv.mul_lds(X + 16 * LS, X, z);
+                sv.put(X + 16 * LS, sv.mul_acc(X + 16 * LS + 16, mm, z), -1.f);
+            } else if (GDN && gi == 2) {
+                a_tile(sm, G, 1, 0, sm.Abl, l32, h);
+            } else if (gi == 3) {
+                score_tile(sm, m & 1, G, 1, 0, l32, h, preg);
             }
-            // tiles (isP, I, J, A operand = op1?):
-            //   gdn: gi 0: A00, A10;  gi 1: A11, P11;  gi 2: P00;  gi 3: P10.
-            //   gla: gi 1: P11;  gi 2: P00;  gi 3: P10.
-            const int ntiles = GDN ? (gi <= 1 ? 2 : 1) : (gi == 0 ? 0 : 1);
-            bool isP[2], a1[2];
-            int I[2], J[2];
+        }
+        lds_barrier();  // A
+        // ---- phase B: off-diagonal 32x32 block of T; bf16 Tb, Tbg ----
+        if (GDN && act) {
+            if (gi <= 1) {
+                // rows 32gi + tl of the diagonal block, 16 columns from c0
+                const float* X = sm.Tm[gi];
+                const int tl = lane >> 1, c0 = 16 * (lane & 1);
+                const int prow = 32 * gi + perm5(tl);
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                if (gi == 0) { isP[ti] = false; I[ti] = ti; J[ti] = 0; a1[ti] = ti == 1; }
-                else if (gi == 1) { isP[ti] = !GDN || ti == 1; I[ti] = 1; J[ti] = 1; a1[ti] = isP[ti]; }
-                else if (gi == 2) { isP[ti] = true; I[ti] = 0; J[ti] = 0; a1[ti] = true; }
-                else { isP[ti] = true; I[ti] = 1; J[ti] = 0; a1[ti] = true; }
-            }
-            // every gate value the masks need, read before any mask is written
-            float grow[2][16], brow[2][16], gcol[2];
+                for (int hh = 0; hh < 2; ++hh) {
+                    uint32_t b[4], bg[4];
+                    const int s0 = 32 * gi + c0 + 8 * hh;
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&X[tl * LS + c0 + 8 * hh]);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&X[tl * LS + c0 + 8 * hh + 4]);
+                    const f32x4 be0 = *reinterpret_cast<const f32x4*>(&G.bet[s0]);
+                    const f32x4 be1 = *reinterpret_cast<const f32x4*>(&G.bet[s0 + 4]);
+                    const f32x4 ga0 = *reinterpret_cast<const f32x4*>(&G.gam[s0]);
+                    const f32x4 ga1 = *reinterpret_cast<const f32x4*>(&G.gam[s0 + 4]);
+                    float tv[8], bv[8], gv[8];
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                gcol[ti] = gsl[32 * J[ti] + l32];
+                    for (int i = 0; i < 4; ++i) {
+                        tv[i] = x0[i]; tv[4 + i] = x1[i];
+                        bv[i] = be0[i]; bv[4 + i] = be1[i];
+                        gv[i] = ga0[i]; gv[4 + i] = ga1[i];
+                    }
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = 32 * I[ti] + 8 * (e >> 2) + 4 * h + (e & 3);
-                    grow[ti][e] = gsl[t];
-                    brow[ti][e] = bsl[t];
+                    for (int i = 0; i < 4; ++i) {
+                        const int sa = c0 + 8 * hh + 2 * i;  // local column of element 2i
+                        const float e0 = sa <= tl ? tv[2 * i] * bv[2 * i] : 0.f;
+                        const float e1 = sa + 1 <= tl ? tv[2 * i + 1] * bv[2 * i + 1] : 0.f;
+                        b[i] = f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
+                        bg[i] = f32_to_bf16(e0 * gv[2 * i]) | ((uint32_t)f32_to_bf16(e1 * gv[2 * i + 1]) << 16);
+                    }
+                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + s0]) = make_uint4(b[0], b[1], b[2], b[3]);
+                    *reinterpret_cast<uint4*>(&sm.Tbg[prow * LT + s0]) = make_uint4(bg[0], bg[1], bg[2], bg[3]);
+                }
+            } else {
+                // columns 16J .. 16J+15 of T rows 32..63:
+                //   Y_iJ = sum_K A_bl(i, K) T_0(K, J),  T_bl(i, J) = -sum_K T_1(i, K) Y_KJ
+                const int J = gi - 2;
+                const float* T0 = sm.Tm[0];
+                const float* T1 = sm.Tm[1];
+                f32x4 y0, y1;
+                if (J == 0) {
+                    y0 = sv.mul_lds(sm.Abl + 16, T0 + 16 * LS, sv.mul_lds(sm.Abl, T0, z));
+                    y1 = sv.mul_lds(sm.Abl + 16 * LS + 16, T0 + 16 * LS, sv.mul_lds(sm.Abl + 16 * LS, T0, z));
+                } else {
+                    y0 = sv.mul_lds(sm.Abl + 16, T0 + 16 * LS + 16, z);
+                    y1 = sv.mul_lds(sm.Abl + 16 * LS + 16, T0 + 16 * LS + 16, z);
+                }
+                const f32x4 t0 = sv.mul_acc(T1, y0, z);
+                const f32x4 t1 = sv.mul_acc(T1 + 16 * LS + 16, y1, sv.mul_acc(T1 + 16 * LS, y0, z));
+                const int s = 16 * J + sv.n16;
+                const float bs = G.bet[s], bgs = G.bet[s] * G.gam[s];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p0 = 32 + perm5(4 * sv.g4 + r), p1 = 32 + perm5(16 + 4 * sv.g4 + r);
+                    sm.Tb[p0 * LT + s] = f32_to_bf16(-t0[r] * bs);
+                    sm.Tbg[p0 * LT + s] = f32_to_bf16(-t0[r] * bgs);
+                    sm.Tb[p1 * LT + s] = f32_to_bf16(-t1[r] * bs);
+                    sm.Tbg[p1 * LT + s] = f32_to_bf16(-t1[r] * bgs);
                 }
             }
+        }
+        lds_barrier();  // B
+        // ---- phase C: W = T diag(beta gamma) K (stored -W) for key tile gi; scores ----
+        if (act) {
+            if (GDN) {
+                const uint16_t* KT = sm.KT[m & 1];
+                const int jt = gi;
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                if (ti >= ntiles) break;
-                f32x16 acc = {};
+                for (int tt = 0; tt < 2; ++tt) {
+                    f32x16 acc = {};
+                    const uint16_t* tr = &sm.Tbg[(32 * tt + l32) * LT + 8 * h];
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-                    acc = mfma32(as_bf16x8(a1[ti] ? op1[kk] : op0[kk]), as_bf16x8(op0[kk]), acc);
-                const int s = 32 * J[ti] + l32;
-                float val[16];
+                    for (int kk = 0; kk < 4; ++kk) {
+                        if (tt == 0 && kk >= 2) continue;  // T is lower triangular
+                        acc = mfma32(lds8(&KT[tsw(32 * jt + l32, 16 * kk + 8 * h)]), lds8(tr + 16 * kk), acc);
+                    }
+                    uint16_t* wrow = &sm.W[(32 * tt + l32) * LW + 32 * jt];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = 32 * I[ti] + 8 * (e >> 2) + 4 * h + (e & 3);
-                    const float decay = __expf(grow[ti][e] - gcol[ti]);
-                    val[e] = isP[ti] ? (t >= s ? decay * acc[e] : 0.f)
-                                     : (t > s ? brow[ti][e] * decay * acc[e] : 0.f);
+                    for (int b = 0; b < 4; ++b)
+                        *reinterpret_cast<uint2*>(wrow + elem_index(0, 4 * b, h)) =
+                            pack4(-acc[4 * b], -acc[4 * b + 1], -acc[4 * b + 2], -acc[4 * b + 3]);
                 }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = 32 * I[ti] + 8 * (e >> 2) + 4 * h + (e & 3);
-                    if (isP[ti]) sm.P[buf][t * LT + s] = f32_to_bf16(val[e]);
-                    else sm.a.A[t * LA + s] = val[e];
-                }
             }
+            if (gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
         }
-        lds_barrier();  // 1
-        // ---- phase 2: next chunk's operands in flight (the diagonal inverses run on waves 4-5) ----
-        if (act && m + 1 < un.ne) load_ops(m + 1);
-        lds_barrier();  // 2
-        // ---- phases 3-5: off-diagonal blocks T_IJ = -T_II sum_K A_IK T_KJ ----
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 keep = z;
-        if (GDN && act) {
-            if (gi == 0) {         // T_10
-                const f32x4 mm = sv.mul_lds(sv.blkA(1, 0), LA, sv.blkT(0, 0), LA, z);
-                sv.put(sv.blkT(1, 0), LA, sv.mul_acc(sv.blkT(1, 1), LA, mm, z), -1.f);
-            } else if (gi == 1) {  // T_32
-                const f32x4 mm = sv.mul_lds(sv.blkA(3, 2), LA, sv.blkT(2, 2), LA, z);
-                sv.put(sv.blkT(3, 2), LA, sv.mul_acc(sv.blkT(3, 3), LA, mm, z), -1.f);
-            } else if (gi == 2) {  // X_21 = A_21 T_11
-                keep = sv.mul_lds(sv.blkA(2, 1), LA, sv.blkT(1, 1), LA, z);
-                sv.put(sm.X[0], LX, keep, 1.f);
-            } else {               // X_31 = A_31 T_11
-                keep = sv.mul_lds(sv.blkA(3, 1), LA, sv.blkT(1, 1), LA, z);
-            }
-        }
-        lds_barrier();  // 3
-        if (GDN && act) {
-            if (gi == 0) {         // X_20 = A_20 T_00 + A_21 T_10
-                keep = sv.mul_lds(sv.blkA(2, 1), LA, sv.blkT(1, 0), LA,
-                                  sv.mul_lds(sv.blkA(2, 0), LA, sv.blkT(0, 0), LA, z));
-                sv.put(sm.X[1], LX, keep, 1.f);
-            } else if (gi == 1) {  // X_30 = A_30 T_00 + A_31 T_10
-                keep = sv.mul_lds(sv.blkA(3, 1), LA, sv.blkT(1, 0), LA,
-                                  sv.mul_lds(sv.blkA(3, 0), LA, sv.blkT(0, 0), LA, z));
-            } else if (gi == 2) {  // T_21 = -T_22 X_21
-                sv.put(sv.blkT(2, 1), LA, sv.mul_acc(sv.blkT(2, 2), LA, keep, z), -1.f);
-            } else {               // T_31 = -(T_32 X_21 + T_33 X_31)
-                const f32x4 t = sv.mul_lds(sv.blkT(3, 2), LA, sm.X[0], LX, z);
-                sv.put(sv.blkT(3, 1), LA, sv.mul_acc(sv.blkT(3, 3), LA, keep, t), -1.f);
-            }
-        }
-        lds_barrier();  // 4
-        if (GDN && act) {
-            if (gi == 0) {         // T_20 = -T_22 X_20
-                sv.put(sv.blkT(2, 0), LA, sv.mul_acc(sv.blkT(2, 2), LA, keep, z), -1.f);
-            } else if (gi == 1) {  // T_30 = -(T_32 X_20 + T_33 X_30)
-                const f32x4 t = sv.mul_lds(sv.blkT(3, 2), LA, sm.X[1], LX, z);
-                sv.put(sv.blkT(3, 0), LA, sv.mul_acc(sv.blkT(3, 3), LA, keep, t), -1.f);
-            }
-        }
-        lds_barrier();  // 5
-        // ---- phase 6: bf16 right-hand-side factors ----
-        if (GDN && act) build_tb(sm, G, tid - 128);
-        lds_barrier();  // 6
-        // ---- phase 7: W^T = K^T (T diag(beta gamma))^T for key tile jt = gi; stored as -W ----
-        if (GDN && act) {
-            const uint16_t* KT = sm.KT[buf];
-            const int jt = gi;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x16 acc = {};
-                const uint16_t* tr = &sm.a.t.Tbg[(32 * tt + l32) * LT + 8 * h];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    if (tt == 0 && kk >= 2) continue;  // T is lower triangular
-                    acc = mfma32(lds8(&KT[tsw(32 * jt + l32, 16 * kk + 8 * h)]), lds8(tr + 16 * kk), acc);
-                }
-                uint16_t* wrow = &sm.W[(32 * tt + l32) * LW + 32 * jt + 4 * h];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    *reinterpret_cast<uint2*>(wrow + 8 * b) =
-                        pack4(-acc[4 * b], -acc[4 * b + 1], -acc[4 * b + 2], -acc[4 * b + 3]);
-            }
-        }
-        lds_barrier();  // 7
+        lds_barrier();  // C
     }
 }
 
 // ----------------------------------------------------------------------------
-// transpose / U~ waves (4, 5): chunk n+1
+// load / transpose waves (4, 5): stage chunk n+2; score tiles (0,0), (1,1) of n+1
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int ti = w - 4;     // value tile of U~ (0 or 1)
+    const int ti = w - 4;     // score tile (ti, ti)
     const int x = tid - 256;  // 0..127
     const int l32 = lane & 31, h = lane >> 5;
     const int T = job.T;
     const size_t qk_base = (size_t)un.head * T * DK;
     const size_t v_base = (size_t)un.head * T * DV + un.r0;
-    // k: keys 8jc..8jc+7 of tokens 4tg..4tg+3 and 32+4tg..32+4tg+3;
-    // v: values 8vc..8vc+7 of tokens 4vt..4vt+3
+    const size_t a_base = (size_t)un.head * T;
+    // q, k: keys 8jc..8jc+7 of tokens 32(i>>2) + 4tg + (i&3), i < 8;
+    // v: values 8vc..8vc+7 of tokens 4vt + i, i < 4
     const int jc = x & 15, tg = x >> 4;
     const int vc = x & 7, vt = x >> 3;
-    uint4 kr[8], vr[4], qr[8];
-    auto load_q = [&](int m) {
-        const Rows rq(job.q + qk_base, m, T, DK);
+    uint4 qr[8], kc[8], kn[8], vcur[4], vnx[4];
+    float pa = 1.f, pb = 0.f;  // alpha, beta of token `lane` (wave 4; 0 past T)
+    auto load = [&](int c, uint4 (&kk)[8], uint4 (&vv)[4]) {
+        const Rows rq(job.q + qk_base, c, T, DK), rk(job.k + qk_base, c, T, DK), rv(job.v + v_base, c, T, DV);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qr[i] = rq.at(32 * (i >> 2) + 4 * tg + (i & 3), 8 * jc);
+        for (int i = 0; i < 8; ++i) {
+            const int row = 32 * (i >> 2) + 4 * tg + (i & 3);
+            kk[i] = rk.at(row, 8 * jc);
+            qr[i] = rq.at(row, 8 * jc);
+        }
+        if (un.erows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vv[i] = make_uint4(0, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vv[i] = rv.at(4 * vt + i, 8 * vc);
+        }
+        if (ti == 0) {
+            pa = ldtok(job.alpha + a_base, c, lane, T);
+            if (GDN) pb = ldtok(job.beta + a_base, c, lane, T);
+        }
     };
-    auto load_raw = [&](int m) {
-        const Rows rk(job.k + qk_base, m, T, DK), rv(job.v + v_base, m, T, DV);
+    // k, q rows of chunk c (from kk, qr) and its gates into LDS
+    auto stage = [&](int c, const uint4 (&kk)[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kr[i] = rk.at(32 * (i >> 2) + 4 * tg + (i & 3), 8 * jc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = un.erows ? make_uint4(0, 0, 0, 0) : rv.at(4 * vt + i, 8 * vc);
+        for (int i = 0; i < 8; ++i) {
+            const int prow = perm5(32 * (i >> 2) + 4 * tg + (i & 3));
+            *reinterpret_cast<uint4*>(&sm.K[prow * LW + 8 * jc]) = kk[i];
+            *reinterpret_cast<uint4*>(&sm.Q[c & 1][prow * LW + 8 * jc]) = qr[i];
+        }
+        if (ti == 0) {
+            Gates& G = sm.gate[c % 3];
+            // identity tokens past T: alpha = 1 (beta is already 0)
+            const float x = wave_inclusive_sum(c * C + lane < T ? __logf(pa) : 0.f);
+            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+            const float xl = x * 1.4426950408889634f;  // log2(e)
+            G.g[lane] = x;
+            G.gam[lane] = __expf(x);
+            G.dec[lane] = __expf(last - x);
+            G.bet[lane] = pb;
+            G.gl[lane] = xl;
+            G.gb[lane] = xl + __builtin_amdgcn_logf(pb);  // log2; -inf where beta = 0
+        }
     };
-    if (un.nb < un.ne) {
-        load_raw(un.nb);
-        load_q(un.nb);
-    }
-
-    for (int it = un.nb - 1; it < un.ne; ++it) {
-        const int m = it + 1;
-        const bool act = m < un.ne;
-        const int buf = m & 1;
-        // ---- phase 1: k^T and v^T tiles of chunk m ----
-        if (act) {
-            uint16_t* KT = sm.KT[buf];
+    // k^T of chunk c (from kk) into KT[c % 2]: keys 8jc + e, tokens 32half + 4tg .. +3
+    auto stage_kt = [&](int c, const uint4 (&kk)[8]) {
+        uint16_t* KT = sm.KT[c & 1];
 #pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int wi = e >> 1;
-                    const uint4* kk = &kr[4 * half];
-                    uint2 u;
-                    u.x = (e & 1) ? hi16x2(word(kk[0], wi), word(kk[1], wi)) : lo16x2(word(kk[0], wi), word(kk[1], wi));
-                    u.y = (e & 1) ? hi16x2(word(kk[2], wi), word(kk[3], wi)) : lo16x2(word(kk[2], wi), word(kk[3], wi));
-                    *reinterpret_cast<uint2*>(&KT[tsw(8 * jc + e, 32 * half + 4 * tg)]) = u;
-                }
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int wi = e >> 1;
+                const uint4* k4 = &kk[4 * half];
                 uint2 u;
-                u.x = (e & 1) ? hi16x2(word(vr[0], wi), word(vr[1], wi)) : lo16x2(word(vr[0], wi), word(vr[1], wi));
-                u.y = (e & 1) ? hi16x2(word(vr[2], wi), word(vr[3], wi)) : lo16x2(word(vr[2], wi), word(vr[3], wi));
-                *reinterpret_cast<uint2*>(&sm.VT[tsw(8 * vc + e, 4 * vt)]) = u;
+                u.x = (e & 1) ? hi16x2(word(k4[0], wi), word(k4[1], wi)) : lo16x2(word(k4[0], wi), word(k4[1], wi));
+                u.y = (e & 1) ? hi16x2(word(k4[2], wi), word(k4[3], wi)) : lo16x2(word(k4[2], wi), word(k4[3], wi));
+                *reinterpret_cast<uint2*>(&KT[tsw(perm5(8 * jc + e), 32 * half + 4 * tg)]) = u;
+            }
+    };
+    // v^T of the chunk (from vv) into VT: values 8vc + e, tokens 4vt .. 4vt+3
+    auto stage_vt = [&](const uint4 (&vv)[4]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int wi = e >> 1;
+            uint2 u;
+            u.x = (e & 1) ? hi16x2(word(vv[0], wi), word(vv[1], wi)) : lo16x2(word(vv[0], wi), word(vv[1], wi));
+            u.y = (e & 1) ? hi16x2(word(vv[2], wi), word(vv[3], wi)) : lo16x2(word(vv[2], wi), word(vv[3], wi));
+            *reinterpret_cast<uint2*>(&sm.VT[tsw(8 * vc + e, 4 * vt)]) = u;
+        }
+    };
+
+    // prologue: chunk nb's k, q, gates in LDS; its k, v kept for k^T / v^T
+    if (un.nb < un.ne) {
+        load(un.nb, kc, vcur);
+        stage(un.nb, kc);
+    }
+    lds_barrier();  // prologue
+    uint2 preg[4];
+    for (int it = un.nb - 1; it < un.ne; ++it) {
+        const int m = it + 1;
+        const bool act = m < un.ne;
+        const bool nxt = m + 1 < un.ne;
+        const Gates& G = sm.gate[m % 3];
+        // ---- phase A: chunk m+1 in flight; k^T of chunk m; score tile (ti, ti) of m ----
+        if (act) {
+            if (nxt) load(m + 1, kn, vnx);
+            stage_kt(m, kc);
+            score_tile(sm, m & 1, G, ti, ti, l32, h, preg);
+        }
+        lds_barrier();  // A
+        // ---- phase B: v^T of chunk m ----
+        if (act) stage_vt(vcur);
+        lds_barrier();  // B
+        // ---- phase C: scores of m; k, q, gates of chunk m+1 ----
+        if (act) {
+            store_score_tile(sm, ti, ti, l32, h, preg);
+            if (nxt) {
+                stage(m + 1, kn);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kc[i] = kn[i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vcur[i] = vnx[i];
             }
         }
-        lds_barrier();  // 1
-        // ---- phase 2: next chunk's k, v in flight; diagonal 16x16 inverses 2ti, 2ti+1 ----
-        if (act && m + 1 < un.ne) load_raw(m + 1);
-        if (GDN && act) {
-            diag_inverse(sm, 2 * ti, lane);
-            diag_inverse(sm, 2 * ti + 1, lane);
-        }
-        lds_barrier();  // 2
-        lds_barrier();  // 3
-        // ---- phase 4: q tile of chunk m (the state waves read chunk n's in phases 2-3) ----
-        if (act) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint4*>(&sm.Q[(32 * (i >> 2) + 4 * tg + (i & 3)) * LW + 8 * jc]) = qr[i];
-            if (m + 1 < un.ne) load_q(m + 1);
-        }
-        lds_barrier();  // 4
-        lds_barrier();  // 5
-        if (GDN && act) build_tb(sm, sm.gate[buf], tid - 128);
-        lds_barrier();  // 6
-        // ---- phase 7: U~ = T diag(beta) V for value tile ti (gla: U~ = V) ----
-        if (act) {
-            if (GDN) {
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    f32x16 acc = {};
-                    const uint16_t* tr = &sm.a.t.Tb[(32 * tt + l32) * LT + 8 * h];
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        if (tt == 0 && kk >= 2) continue;
-                        acc = mfma32(lds8(tr + 16 * kk), lds8(&sm.VT[tsw(32 * ti + l32, 16 * kk + 8 * h)]), acc);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        sm.Ut[(32 * tt + 8 * (e >> 2) + 4 * h + (e & 3)) * LU + 32 * ti + l32] = acc[e];
-                }
-            } else {
-                for (int e = x; e < C * DVS; e += 128) {
-                    const int t = e >> 6, i = e & 63;
-                    sm.Ut[t * LU + i] = bf16_to_f32(sm.VT[tsw(i, t)]);
-                }
-            }
-        }
-        lds_barrier();  // 7
+        lds_barrier();  // C
     }
 }
 
