@@ -208,42 +208,71 @@ struct Solve {
     }
 };
 
-// sum over the 4 lanes of a quad (DPP quad permutes)
-__device__ __forceinline__ float quad_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-    return x;
-}
 // In place: the two 16x16 diagonal blocks of the fp32 32x32 tile X (unit lower
 // triangular I + A_bb, strictly lower part stored) are replaced by their
-// inverses, by forward substitution in fp32.  Lane (c, sub) owns column c of
-// both inverses and sums the terms j = sub (mod 4) of each row; a quad
-// reduction completes the row.  The two blocks are interleaved for ILP.
+// inverses, by forward substitution in fp32.  Lane (b, c) (lanes 0..31; lanes
+// 32..63 repeat them and store nothing) owns column c of block b's inverse:
+// x_r = [r == c] - sum_{j<r} A_rj x_j, with row r read as broadcast 16-byte
+// loads (left-looking).
 __device__ __forceinline__ void diag_inverse2(float* X, int lane) {
-    const int c = lane >> 2, sub = lane & 3;
-    float a[2][16][4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-#pragma unroll
-            for (int mm = 0; mm < 4; ++mm) a[b][r][mm] = X[(16 * b + r) * LS + 16 * b + 4 * mm + sub];
-    float xs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int b = (lane >> 4) & 1, c = lane & 15;
+    const float* A = X + 16 * b * LS + 16 * b;
+    float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            float p = a[b][r][0] * xs[b][0] + a[b][r][1] * xs[b][1] + a[b][r][2] * xs[b][2] +
-                      a[b][r][3] * xs[b][3];
-            p = quad_sum(p);
-            const float xr = (r == c ? 1.f : 0.f) - p;
-            if ((r & 3) == sub) xs[b][r >> 2] = xr;
+        for (int q = 0; q < (r + 3) / 4; ++q) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&A[r * LS + 4 * q]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * q + i;
+                if (j < r) {
+                    if (i & 1) s1 += a[i] * x[j];
+                    else s0 += a[i] * x[j];
+                }
+            }
         }
+        x[r] = (r == c ? 1.f : 0.f) - (s0 + s1);
     }
+    if (lane < 32) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+        for (int r = 0; r < 16; ++r) X[(16 * b + r) * LS + 16 * b + c] = x[r];
+    }
+}
+
+// acc += sum_{k < N} A(k) B(k) with the LDS operand A(k) loaded two steps
+// ahead of its MFMA; the order is pinned so that each MFMA waits only for its
+// own operand while the next two loads are in flight.
+template <int N, typename LA, typename GB>
+__device__ __forceinline__ f32x16 mfma_chain(LA load_a, GB get_b, f32x16 acc) {
+    bf16x8 a0 = load_a(0), a1 = N > 1 ? load_a(1) : a0;
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) X[(16 * b + 4 * mm + sub) * LS + 16 * b + c] = xs[b][mm];
+    for (int k = 0; k < N; ++k) {
+        const bf16x8 a2 = k + 2 < N ? load_a(k + 2) : a0;
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(a0, get_b(k), acc);
+        a0 = a1;
+        a1 = a2;
+    }
+    return acc;
+}
+
+// As mfma_chain, with both operands loaded from LDS two steps ahead.
+template <int N, typename LA, typename LB>
+__device__ __forceinline__ f32x16 mfma_chain2(LA load_a, LB load_b, f32x16 acc) {
+    bf16x8 a0 = load_a(0), b0 = load_b(0);
+    bf16x8 a1 = N > 1 ? load_a(1) : a0, b1 = N > 1 ? load_b(1) : b0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const bf16x8 a2 = k + 2 < N ? load_a(k + 2) : a0;
+        const bf16x8 b2 = k + 2 < N ? load_b(k + 2) : b0;
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(a0, b0, acc);
+        a0 = a1; b0 = b1;
+        a1 = a2; b1 = b2;
+    }
+    return acc;
 }
 
 // B operand for contraction step kk (16 rows) from accumulator tiles:
@@ -260,12 +289,10 @@ __device__ __forceinline__ bf16x8 sop(const f32x16 (&t)[N], int kk) {
 // s = 32J + elem_index(0, e, h).
 __device__ __forceinline__ f32x16 gram_tile(const uint16_t* X, int I, const uint16_t* Y, int J,
                                             int l32, int h) {
-    f32x16 acc = {};
     const uint16_t* xr = X + (32 * I + l32) * LW + 8 * h;
     const uint16_t* yr = Y + (32 * J + l32) * LW + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(yr + 16 * kk), lds8(xr + 16 * kk), acc);
-    return acc;
+    return mfma_chain2<8>([&](int k) { return lds8(yr + 16 * k); },
+                          [&](int k) { return lds8(xr + 16 * k); }, f32x16{});
 }
 
 // Decay mask of tile (I, J): element e of lane (l32, h) is scaled by
@@ -389,19 +416,24 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             }
     }
 
+    // sbf[kk]: the state rounded to bf16 as B operands (contraction step kk);
     // qacc[tt] = Q S^T of the chunk the next iteration reads out (old state)
+    bf16x8 sbf[8];
+    auto round_state = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) sbf[kk] = sop(sacc, kk);
+    };
     f32x16 qacc[2];
     auto q_state = [&](int c) {
         const uint16_t* Q = sm.Q[c & 1];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            f32x16 acc = {};
             const uint16_t* qr = &Q[(32 * tt + l32) * LW + 8 * h];
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(qr + 16 * kk), sop(sacc, kk), acc);
-            qacc[tt] = acc;
+            qacc[tt] = mfma_chain<8>([&](int k) { return lds8(qr + 16 * k); },
+                                     [&](int k) { return sbf[k]; }, f32x16{});
         }
     };
+    round_state();
 
     lds_barrier();  // prologue: chunk nb staged
     for (int it = un.nb - 1; it < un.ne; ++it) {
@@ -422,9 +454,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                         acc = mfma32(lds8(tr + 16 * kk), lds8(&sm.VT[tsw(vl, 16 * kk + 8 * h)]), acc);
                     }
                     const uint16_t* wr = &sm.W[(32 * tt + l32) * LW + 8 * h];
-#pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) acc = mfma32(lds8(wr + 16 * kk), sop(sacc, kk), acc);
-                    uacc[tt] = acc;
+                    uacc[tt] = mfma_chain<8>([&](int k) { return lds8(wr + 16 * k); },
+                                             [&](int k) { return sbf[k]; }, acc);
                 } else {
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
@@ -458,18 +489,16 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                     acc = mfma32(lds8(pr + 16 * ks), sop(uacc, ks), acc);
                 }
                 if (job.o) {
-                    uint16_t* orow = job.o + ((size_t)un.head * T + (size_t)n * C) * DV + vcol;
-                    if ((n + 1) * C <= T) {
+                    // rows past T fall outside the resource and are dropped
+                    const int valid = __builtin_amdgcn_readfirstlane(min(T - n * C, C));
+                    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                        job.o + ((size_t)un.head * T + (size_t)n * C) * DV + un.r0, (short)0,
+                        valid * DV * 2 - un.r0 * 2, 0x00020000);
+                    const int voff = (8 * h * DV + vl) * 2;
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            orow[(size_t)elem_index(tt, e, h) * DV] = f32_to_bf16(acc[e]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int t = elem_index(tt, e, h);
-                            if (n * C + t < T) orow[(size_t)t * DV] = f32_to_bf16(acc[e]);
-                        }
-                    }
+                    for (int e = 0; e < 16; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), orsrc, voff,
+                                                              (elem_index(tt, e, 0)) * DV * 2, 0);
                 }
             }
             bf16x8 db[4];
@@ -489,12 +518,11 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             const uint16_t* KT = sm.KT[n & 1];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
-                f32x16 acc = sacc[jt] * gC;
                 const int prow = 32 * jt + l32;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma32(lds8(&KT[tsw(prow, 16 * ks + 8 * h)]), db[ks], acc);
-                sacc[jt] = acc;
+                sacc[jt] = mfma_chain<4>([&](int k) { return lds8(&KT[tsw(prow, 16 * k + 8 * h)]); },
+                                         [&](int k) { return db[k]; }, sacc[jt] * gC);
             }
+            round_state();
         }
         lds_barrier();  // B
         // ---- phase C: Q S^T of chunk n+1 with the state entering it ----
@@ -628,13 +656,11 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 const int jt = gi;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    f32x16 acc = {};
                     const uint16_t* tr = &sm.Tbg[(32 * tt + l32) * LT + 8 * h];
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        if (tt == 0 && kk >= 2) continue;  // T is lower triangular
-                        acc = mfma32(lds8(&KT[tsw(32 * jt + l32, 16 * kk + 8 * h)]), lds8(tr + 16 * kk), acc);
-                    }
+                    auto lk = [&](int k) { return lds8(&KT[tsw(32 * jt + l32, 16 * k + 8 * h)]); };
+                    auto lt = [&](int k) { return lds8(tr + 16 * k); };
+                    // T is lower triangular: token tile 0 needs columns 0..31 only
+                    const f32x16 acc = tt == 0 ? mfma_chain2<2>(lk, lt, f32x16{}) : mfma_chain2<4>(lk, lt, f32x16{});
                     uint16_t* wrow = &sm.W[(32 * tt + l32) * LW + 32 * jt];
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
