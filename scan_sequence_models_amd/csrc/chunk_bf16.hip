@@ -70,6 +70,7 @@ constexpr int LT = C + 8;    // row stride of [*][token] bf16 arrays
 constexpr int LS = 32 + 4;   // row stride of fp32 32x32 solve tiles
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // Gates of one chunk: g = in-chunk cumulative ln alpha, gamma = e^g,
 // dec = e^(g_C - g), beta; gl = g log2(e) and gb = gl + log2(beta) feed the
@@ -103,20 +104,24 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
+// bf16 rounding of float vectors (packed conversions, two values per instruction)
 template <int OFF>
 __device__ __forceinline__ bf16x8 half8(const f32x16& x) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(x[OFF + i]);
-    return r;
+    const f32x8 v = __builtin_shufflevector(x, x, OFF, OFF + 1, OFF + 2, OFF + 3, OFF + 4, OFF + 5,
+                                            OFF + 6, OFF + 7);
+    return __builtin_convertvector(v, bf16x8);
 }
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-    const uint32_t x0 = f32_to_bf16(a), x1 = f32_to_bf16(b);
-    const uint32_t x2 = f32_to_bf16(c), x3 = f32_to_bf16(d);
-    return make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+    return __builtin_bit_cast(uint2, __builtin_convertvector((f32x4{a, b, c, d}), bf16x4));
 }
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+// low (high) 16-bit halves of a and b, a's in the low half of the result
+__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 __device__ __forceinline__ uint32_t word(const uint4& u, int i) {
     return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
@@ -508,11 +513,13 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                 const f32x4 d1 = *reinterpret_cast<const f32x4*>(&G.dec[16 * ks + 8 * h + 4]);
                 const f32x16& u = uacc[ks >> 1];
                 const int off = 8 * (ks & 1);
+                f32x8 x;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    db[ks][i] = static_cast<__bf16>(u[off + i] * d0[i]);
-                    db[ks][4 + i] = static_cast<__bf16>(u[off + 4 + i] * d1[i]);
+                    x[i] = u[off + i] * d0[i];
+                    x[4 + i] = u[off + 4 + i] * d1[i];
                 }
+                db[ks] = __builtin_convertvector(x, bf16x8);
             }
             const float gC = G.gam[C - 1];
             const uint16_t* KT = sm.KT[n & 1];
@@ -614,8 +621,8 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                         const int sa = c0 + 8 * hh + 2 * i;  // local column of element 2i
                         const float e0 = sa <= tl ? tv[2 * i] * bv[2 * i] : 0.f;
                         const float e1 = sa + 1 <= tl ? tv[2 * i + 1] * bv[2 * i + 1] : 0.f;
-                        b[i] = f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
-                        bg[i] = f32_to_bf16(e0 * gv[2 * i]) | ((uint32_t)f32_to_bf16(e1 * gv[2 * i + 1]) << 16);
+                        b[i] = pack2(e0, e1);
+                        bg[i] = pack2(e0 * gv[2 * i], e1 * gv[2 * i + 1]);
                     }
                     *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + s0]) = make_uint4(b[0], b[1], b[2], b[3]);
                     *reinterpret_cast<uint4*>(&sm.Tbg[prow * LT + s0]) = make_uint4(bg[0], bg[1], bg[2], bg[3]);
@@ -770,33 +777,34 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
     }
     lds_barrier();  // prologue
     uint2 preg[4];
-    for (int it = un.nb - 1; it < un.ne; ++it) {
+    // one chunk step; kc/vcur hold chunk m's k and v, kn/vnx receive chunk m+1's
+    auto step = [&](int it, uint4 (&kcur)[8], uint4 (&knext)[8], uint4 (&vcu)[4], uint4 (&vne)[4]) {
         const int m = it + 1;
         const bool act = m < un.ne;
         const bool nxt = m + 1 < un.ne;
         const Gates& G = sm.gate[m % 3];
         // ---- phase A: chunk m+1 in flight; k^T of chunk m; score tile (ti, ti) of m ----
         if (act) {
-            if (nxt) load(m + 1, kn, vnx);
-            stage_kt(m, kc);
+            if (nxt) load(m + 1, knext, vne);
+            stage_kt(m, kcur);
             score_tile(sm, m & 1, G, ti, ti, l32, h, preg);
         }
         lds_barrier();  // A
         // ---- phase B: v^T of chunk m ----
-        if (act) stage_vt(vcur);
+        if (act) stage_vt(vcu);
         lds_barrier();  // B
         // ---- phase C: scores of m; k, q, gates of chunk m+1 ----
         if (act) {
             store_score_tile(sm, ti, ti, l32, h, preg);
-            if (nxt) {
-                stage(m + 1, kn);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) kc[i] = kn[i];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vcur[i] = vnx[i];
-            }
+            if (nxt) stage(m + 1, knext);
         }
         lds_barrier();  // C
+    };
+    // two steps per trip so that the current / next register sets alternate
+    // without copies
+    for (int it = un.nb - 1; it < un.ne; it += 2) {
+        step(it, kc, kn, vcur, vnx);
+        if (it + 1 < un.ne) step(it + 1, kn, kc, vnx, vcur);
     }
 }
 
