@@ -193,11 +193,16 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 // holds rows 4 g4 .. 4 g4 + 3 of column n16 of a result.
 struct Solve {
     int n16, g4;
-    // acc += X Y, both 16x16 blocks of fp32 tiles with row stride LS
+    // acc += X Y, both 16x16 blocks of fp32 tiles with row stride LS; lane
+    // (n16, g4) supplies the contraction indices 4 g4 .. 4 g4 + 3, so its X
+    // operands are one 16-byte row read
     __device__ __forceinline__ f32x4 mul_lds(const float* X, const float* Y, f32x4 acc) const {
+        const f32x4 xr = *reinterpret_cast<const f32x4*>(&X[n16 * LS + 4 * g4]);
+        float yc[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            acc = mfma4(X[n16 * LS + 4 * kk + g4], Y[(4 * kk + g4) * LS + n16], acc);
+        for (int kk = 0; kk < 4; ++kk) yc[kk] = Y[(4 * g4 + kk) * LS + n16];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma4(xr[kk], yc[kk], acc);
         return acc;
     }
     // acc += X Y, X a block in LDS, Y an accumulator block (k = 4 g4 + kk)
@@ -217,27 +222,34 @@ struct Solve {
 // triangular I + A_bb, strictly lower part stored) are replaced by their
 // inverses, by forward substitution in fp32.  Lane (b, c) (lanes 0..31; lanes
 // 32..63 repeat them and store nothing) owns column c of block b's inverse:
-// x_r = [r == c] - sum_{j<r} A_rj x_j, with row r read as broadcast 16-byte
-// loads (left-looking).
+// x_r = [r == c] - sum_{j<r} A_rj x_j (left-looking), with row r read as
+// broadcast 16-byte loads issued two rows ahead.
 __device__ __forceinline__ void diag_inverse2(float* X, int lane) {
     const int b = (lane >> 4) & 1, c = lane & 15;
     const float* A = X + 16 * b * LS + 16 * b;
     float x[16];
+    f32x4 row[3][4];  // rows r, r+1, r+2 in flight (columns 0 .. 4*ceil(r/4)-1)
+    auto load_row = [&](int r, f32x4 (&dst)[4]) {
+#pragma unroll
+        for (int q = 0; q < (r + 3) / 4; ++q) dst[q] = *reinterpret_cast<const f32x4*>(&A[r * LS + 4 * q]);
+    };
+    load_row(1, row[1]);
+    load_row(2, row[2]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+        if (r + 2 < 16) load_row(r + 2, row[(r + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int q = 0; q < (r + 3) / 4; ++q) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&A[r * LS + 4 * q]);
+        for (int q = 0; q < (r + 3) / 4; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 4 * q + i;
                 if (j < r) {
-                    if (i & 1) s1 += a[i] * x[j];
-                    else s0 += a[i] * x[j];
+                    if (i & 1) s1 += row[r % 3][q][i] * x[j];
+                    else s0 += row[r % 3][q][i] * x[j];
                 }
             }
-        }
         x[r] = (r == c ? 1.f : 0.f) - (s0 + s1);
     }
     if (lane < 32) {
@@ -259,6 +271,21 @@ __device__ __forceinline__ f32x16 mfma_chain(LA load_a, GB get_b, f32x16 acc) {
         acc = mfma32(a0, get_b(k), acc);
         a0 = a1;
         a1 = a2;
+    }
+    return acc;
+}
+
+// As mfma_chain with the roles swapped: A(k) from registers, B(k) from LDS.
+template <int N, typename GA, typename LB>
+__device__ __forceinline__ f32x16 mfma_chain_b(GA get_a, LB load_b, f32x16 acc) {
+    bf16x8 b0 = load_b(0), b1 = N > 1 ? load_b(1) : b0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const bf16x8 b2 = k + 2 < N ? load_b(k + 2) : b0;
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(get_a(k), b0, acc);
+        b0 = b1;
+        b1 = b2;
     }
     return acc;
 }
@@ -421,8 +448,10 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             }
     }
 
-    // sbf[kk]: the state rounded to bf16 as B operands (contraction step kk);
-    // qacc[tt] = Q S^T of the chunk the next iteration reads out (old state)
+    // sbf[kk]: the state rounded to bf16 as MFMA operands (contraction step kk);
+    // qacc[tt] = (Q S^T)^T of the chunk the next iteration reads out (old
+    // state), transposed: lane column = token 32 tt + perm5(l32), element row =
+    // value channel 32 ib + 8 (e/4) + 4 h + e % 4 of the wave's slice.
     bf16x8 sbf[8];
     auto round_state = [&]() {
 #pragma unroll
@@ -434,8 +463,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const uint16_t* qr = &Q[(32 * tt + l32) * LW + 8 * h];
-            qacc[tt] = mfma_chain<8>([&](int k) { return lds8(qr + 16 * k); },
-                                     [&](int k) { return sbf[k]; }, f32x16{});
+            qacc[tt] = mfma_chain_b<8>([&](int k) { return sbf[k]; },
+                                       [&](int k) { return lds8(qr + 16 * k); }, f32x16{});
         }
     };
     round_state();
@@ -476,34 +505,29 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
         if (act) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                f32x16 acc = qacc[tt];
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const f32x4 g0 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h]);
-                    const f32x4 g1 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h + 4]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[8 * b + i] *= g0[i];
-                        acc[8 * b + 4 + i] *= g1[i];
-                    }
-                }
+                // O^T = diag(gamma) (Q S^T)^T + U^T P^T for token tile tt
+                const int tl = 32 * tt + perm5(l32);  // this lane's token
+                f32x16 acc = qacc[tt] * G.gam[tl];
                 const uint16_t* pr = &sm.P[(32 * tt + l32) * LT + 8 * h];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    if (tt == 0 && ks >= 2) continue;  // P is lower triangular
-                    acc = mfma32(lds8(pr + 16 * ks), sop(uacc, ks), acc);
-                }
+                auto au = [&](int k) { return sop(uacc, k); };
+                auto lp = [&](int k) { return lds8(pr + 16 * k); };
+                // P is lower triangular: token tile 0 needs columns 0..31 only
+                acc = tt == 0 ? mfma_chain_b<2>(au, lp, acc) : mfma_chain_b<4>(au, lp, acc);
                 if (job.o) {
                     // rows past T fall outside the resource and are dropped
                     const int valid = __builtin_amdgcn_readfirstlane(min(T - n * C, C));
                     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                         job.o + ((size_t)un.head * T + (size_t)n * C) * DV + un.r0, (short)0,
                         valid * DV * 2 - un.r0 * 2, 0x00020000);
-                    const int voff = (8 * h * DV + vl) * 2;
+                    const int voff = (tl * DV + 32 * ib + 4 * h) * 2;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), orsrc, voff,
-                                                              (elem_index(tt, e, 0)) * DV * 2, 0);
+                    for (int b = 0; b < 4; ++b)
+                    {
+                        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(u32x2, pack4(acc[4 * b], acc[4 * b + 1], acc[4 * b + 2], acc[4 * b + 3])),
+                            orsrc, voff, 16 * b, 0);
+                    }
                 }
             }
             bf16x8 db[4];
