@@ -380,6 +380,20 @@ __device__ __forceinline__ void a_tile(const Smem& sm, const Gates& G, int I, in
             f32x4{a[4 * b], a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]};
 }
 
+// Gates of chunk c from alpha, beta of token `lane` (0 past T; identity tokens
+// there: alpha = 1, beta = 0): an inclusive wave scan of ln alpha.
+__device__ __forceinline__ void stage_gates(Gates& G, int c, float pa, float pb, int T, int lane) {
+    const float x = wave_inclusive_sum(c * C + lane < T ? __logf(pa) : 0.f);
+    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    const float xl = x * 1.4426950408889634f;  // log2(e)
+    G.g[lane] = x;
+    G.gam[lane] = __expf(x);
+    G.dec[lane] = __expf(last - x);
+    G.bet[lane] = pb;
+    G.gl[lane] = xl;
+    G.gb[lane] = xl + __builtin_amdgcn_logf(pb);  // log2; -inf where beta = 0
+}
+
 struct Unit {
     int head, leaf, sl, nb, ne, r0;
     bool erows;
@@ -594,6 +608,18 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     const Solve sv{lane & 15, lane >> 4};
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     uint2 preg[4];  // gi 3: chunk m's score tile (1, 0), stored in phase C
+    // gi 0: alpha, beta of chunk m+1's token `lane` (0 past T); its gates
+    const int T = job.T;
+    const size_t a_base = (size_t)un.head * T;
+    float pa = 1.f, pb = 0.f;
+    auto load_ab = [&](int c) {
+        pa = ldtok(job.alpha + a_base, c, lane, T);
+        if (GDN) pb = ldtok(job.beta + a_base, c, lane, T);
+    };
+    if (gi == 0 && un.nb < un.ne) {
+        load_ab(un.nb);
+        stage_gates(sm.gate[un.nb % 3], un.nb, pa, pb, T, lane);
+    }
 
     lds_barrier();  // prologue
     for (int it = un.nb - 1; it < un.ne; ++it) {
@@ -601,6 +627,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
         const bool act = m < un.ne;
         const Gates& G = sm.gate[m % 3];
         // ---- phase A: k-Gram tiles; diagonal 32x32 blocks of T in-wave ----
+        if (gi == 0 && m + 1 < un.ne) load_ab(m + 1);
         if (act) {
             if (GDN && gi <= 1) {
                 float* X = sm.Tm[gi];
@@ -701,6 +728,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
             }
             if (gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
         }
+        if (gi == 0 && m + 1 < un.ne) stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, T, lane);
         lds_barrier();  // C
     }
 }
@@ -718,13 +746,11 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
     const int T = job.T;
     const size_t qk_base = (size_t)un.head * T * DK;
     const size_t v_base = (size_t)un.head * T * DV + un.r0;
-    const size_t a_base = (size_t)un.head * T;
     // q, k: keys 8jc..8jc+7 of tokens 32(i>>2) + 4tg + (i&3), i < 8;
     // v: values 8vc..8vc+7 of tokens 4vt + i, i < 4
     const int jc = x & 15, tg = x >> 4;
     const int vc = x & 7, vt = x >> 3;
     uint4 qr[8], kc[8], kn[8], vcur[4], vnx[4];
-    float pa = 1.f, pb = 0.f;  // alpha, beta of token `lane` (wave 4; 0 past T)
     auto load = [&](int c, uint4 (&kk)[8], uint4 (&vv)[4]) {
         const Rows rq(job.q + qk_base, c, T, DK), rk(job.k + qk_base, c, T, DK), rv(job.v + v_base, c, T, DV);
 #pragma unroll
@@ -740,10 +766,6 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
 #pragma unroll
             for (int i = 0; i < 4; ++i) vv[i] = rv.at(4 * vt + i, 8 * vc);
         }
-        if (ti == 0) {
-            pa = ldtok(job.alpha + a_base, c, lane, T);
-            if (GDN) pb = ldtok(job.beta + a_base, c, lane, T);
-        }
     };
     // k, q rows of chunk c (from kk, qr) and its gates into LDS
     auto stage = [&](int c, const uint4 (&kk)[8]) {
@@ -752,19 +774,6 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
             const int prow = perm5(32 * (i >> 2) + 4 * tg + (i & 3));
             *reinterpret_cast<uint4*>(&sm.K[prow * LW + 8 * jc]) = kk[i];
             *reinterpret_cast<uint4*>(&sm.Q[c & 1][prow * LW + 8 * jc]) = qr[i];
-        }
-        if (ti == 0) {
-            Gates& G = sm.gate[c % 3];
-            // identity tokens past T: alpha = 1 (beta is already 0)
-            const float x = wave_inclusive_sum(c * C + lane < T ? __logf(pa) : 0.f);
-            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-            const float xl = x * 1.4426950408889634f;  // log2(e)
-            G.g[lane] = x;
-            G.gam[lane] = __expf(x);
-            G.dec[lane] = __expf(last - x);
-            G.bet[lane] = pb;
-            G.gl[lane] = xl;
-            G.gb[lane] = xl + __builtin_amdgcn_logf(pb);  // log2; -inf where beta = 0
         }
     };
     // k^T of chunk c (from kk) into KT[c % 2]: keys 8jc + e, tokens 32half + 4tg .. +3
