@@ -494,16 +494,27 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 if (GDN) {
-                    f32x16 acc = {};
+                    // T diag(beta) V operands read first (T is lower triangular:
+                    // tile 0 contracts over tokens 0..31 only); they arrive while
+                    // the W S^T chain runs
                     const uint16_t* tr = &sm.Tb[(32 * tt + l32) * LT + 8 * h];
+                    bf16x8 ta[4], va[4];
+                    const int nk = tt == 0 ? 2 : 4;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        if (tt == 0 && kk >= 2) continue;  // T is lower triangular
-                        acc = mfma32(lds8(tr + 16 * kk), lds8(&sm.VT[tsw(vl, 16 * kk + 8 * h)]), acc);
+                        if (kk >= nk) continue;
+                        ta[kk] = lds8(tr + 16 * kk);
+                        va[kk] = lds8(&sm.VT[tsw(vl, 16 * kk + 8 * h)]);
                     }
                     const uint16_t* wr = &sm.W[(32 * tt + l32) * LW + 8 * h];
-                    uacc[tt] = mfma_chain<8>([&](int k) { return lds8(wr + 16 * k); },
-                                             [&](int k) { return sbf[k]; }, acc);
+                    f32x16 acc = mfma_chain<8>([&](int k) { return lds8(wr + 16 * k); },
+                                               [&](int k) { return sbf[k]; }, f32x16{});
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        if (kk >= nk) continue;
+                        acc = mfma32(ta[kk], va[kk], acc);
+                    }
+                    uacc[tt] = acc;
                 } else {
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
@@ -738,7 +749,6 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Unit& un) {
-    constexpr bool GDN = MODE == 0;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int ti = w - 4;     // score tile (ti, ti)
     const int x = tid - 256;  // 0..127
