@@ -430,6 +430,7 @@ __device__ __forceinline__ Unit unit_of(const ChunkJob& job) {
 template <int MODE, int ROLE>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
+    constexpr bool OUT = ROLE != kLeafAggregate;  // o is read out (not for leaf aggregates)
     const int tid = threadIdx.x, lane = tid & 63, ib = wave_id();
     const int l32 = lane & 31, h = lane >> 5;
     const int T = job.T;
@@ -499,7 +500,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                     // the W S^T chain runs
                     const uint16_t* tr = &sm.Tb[(32 * tt + l32) * LT + 8 * h];
                     bf16x8 ta[4], va[4];
-                    const int nk = tt == 0 ? 2 : 4;
+                    const int nk = un.erows ? 0 : tt == 0 ? 2 : 4;  // rows of E: v = 0
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
                         if (kk >= nk) continue;
@@ -527,7 +528,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
         }
         lds_barrier();  // A
         // ---- phase B: O = diag(gamma) Q S^T + P U, written out; S^T <- gamma_C S^T + K^T diag(dec) U ----
-        if (act) {
+        if (OUT && act) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 // O^T = diag(gamma) (Q S^T)^T + U^T P^T for token tile tt
@@ -555,6 +556,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                     }
                 }
             }
+        }
+        if (act) {
             bf16x8 db[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -582,7 +585,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
         }
         lds_barrier();  // B
         // ---- phase C: Q S^T of chunk n+1 with the state entering it ----
-        if (n + 1 < un.ne) q_state(n + 1);
+        if (OUT && n + 1 < un.ne) q_state(n + 1);
         lds_barrier();  // C
     }
 
@@ -613,6 +616,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 template <int MODE, int ROLE>
 __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
+    constexpr bool OUT = ROLE != kLeafAggregate;  // scores needed only where o is read out
     const int lane = threadIdx.x & 63, w = wave_id();
     const int gi = w == 2 ? 0 : w == 3 ? 1 : w == 6 ? 2 : 3;
     const int l32 = lane & 31, h = lane >> 5;
@@ -649,7 +653,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 sv.put(X + 16 * LS, sv.mul_acc(X + 16 * LS + 16, mm, z), -1.f);
             } else if (GDN && gi == 2) {
                 a_tile(sm, G, 1, 0, sm.Abl, l32, h);
-            } else if (gi == 3) {
+            } else if (OUT && gi == 3) {
                 score_tile(sm, m & 1, G, 1, 0, l32, h, preg);
             }
         }
@@ -737,7 +741,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                             pack4(-acc[4 * b], -acc[4 * b + 1], -acc[4 * b + 2], -acc[4 * b + 3]);
                 }
             }
-            if (gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
+            if (OUT && gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
         }
         if (gi == 0 && m + 1 < un.ne) stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, T, lane);
         lds_barrier();  // C
@@ -749,6 +753,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Unit& un) {
+    constexpr bool OUT = ROLE != kLeafAggregate;  // q and scores needed only where o is read out
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int ti = w - 4;     // score tile (ti, ti)
     const int x = tid - 256;  // 0..127
@@ -767,7 +772,7 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
         for (int i = 0; i < 8; ++i) {
             const int row = 32 * (i >> 2) + 4 * tg + (i & 3);
             kk[i] = rk.at(row, 8 * jc);
-            qr[i] = rq.at(row, 8 * jc);
+            if (OUT) qr[i] = rq.at(row, 8 * jc);
         }
         if (un.erows) {
 #pragma unroll
@@ -783,7 +788,7 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
         for (int i = 0; i < 8; ++i) {
             const int prow = perm5(32 * (i >> 2) + 4 * tg + (i & 3));
             *reinterpret_cast<uint4*>(&sm.K[prow * LW + 8 * jc]) = kk[i];
-            *reinterpret_cast<uint4*>(&sm.Q[c & 1][prow * LW + 8 * jc]) = qr[i];
+            if (OUT) *reinterpret_cast<uint4*>(&sm.Q[c & 1][prow * LW + 8 * jc]) = qr[i];
         }
     };
     // k^T of chunk c (from kk) into KT[c % 2]: keys 8jc + e, tokens 32half + 4tg .. +3
@@ -830,7 +835,7 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
         if (act) {
             if (nxt) load(m + 1, knext, vne);
             stage_kt(m, kcur);
-            score_tile(sm, m & 1, G, ti, ti, l32, h, preg);
+            if (OUT) score_tile(sm, m & 1, G, ti, ti, l32, h, preg);
         }
         lds_barrier();  // A
         // ---- phase B: v^T of chunk m ----
@@ -838,7 +843,7 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
         lds_barrier();  // B
         // ---- phase C: scores of m; k, q, gates of chunk m+1 ----
         if (act) {
-            store_score_tile(sm, ti, ti, l32, h, preg);
+            if (OUT) store_score_tile(sm, ti, ti, l32, h, preg);
             if (nxt) stage(m + 1, knext);
         }
         lds_barrier();  // C
