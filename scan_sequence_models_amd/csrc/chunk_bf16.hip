@@ -275,21 +275,6 @@ __device__ __forceinline__ f32x16 mfma_chain(LA load_a, GB get_b, f32x16 acc) {
     return acc;
 }
 
-// As mfma_chain with the roles swapped: A(k) from registers, B(k) from LDS.
-template <int N, typename GA, typename LB>
-__device__ __forceinline__ f32x16 mfma_chain_b(GA get_a, LB load_b, f32x16 acc) {
-    bf16x8 b0 = load_b(0), b1 = N > 1 ? load_b(1) : b0;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        const bf16x8 b2 = k + 2 < N ? load_b(k + 2) : b0;
-        __builtin_amdgcn_sched_barrier(0);
-        acc = mfma32(get_a(k), b0, acc);
-        b0 = b1;
-        b1 = b2;
-    }
-    return acc;
-}
-
 // As mfma_chain, with both operands loaded from LDS two steps ahead.
 template <int N, typename LA, typename LB>
 __device__ __forceinline__ f32x16 mfma_chain2(LA load_a, LB load_b, f32x16 acc) {
@@ -463,10 +448,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             }
     }
 
-    // sbf[kk]: the state rounded to bf16 as MFMA operands (contraction step kk);
-    // qacc[tt] = (Q S^T)^T of the chunk the next iteration reads out (old
-    // state), transposed: lane column = token 32 tt + perm5(l32), element row =
-    // value channel 32 ib + 8 (e/4) + 4 h + e % 4 of the wave's slice.
+    // sbf[kk]: the state rounded to bf16 as B operands (contraction step kk);
+    // qacc[tt] = Q S^T of the chunk the next iteration reads out (old state)
     bf16x8 sbf[8];
     auto round_state = [&]() {
 #pragma unroll
@@ -478,8 +461,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const uint16_t* qr = &Q[(32 * tt + l32) * LW + 8 * h];
-            qacc[tt] = mfma_chain_b<8>([&](int k) { return sbf[k]; },
-                                       [&](int k) { return lds8(qr + 16 * k); }, f32x16{});
+            qacc[tt] = mfma_chain<8>([&](int k) { return lds8(qr + 16 * k); },
+                                     [&](int k) { return sbf[k]; }, f32x16{});
         }
     };
     round_state();
@@ -531,29 +514,34 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
         if (OUT && act) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                // O^T = diag(gamma) (Q S^T)^T + U^T P^T for token tile tt
-                const int tl = 32 * tt + perm5(l32);  // this lane's token
-                f32x16 acc = qacc[tt] * G.gam[tl];
+                f32x16 acc = qacc[tt];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const f32x4 g0 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h]);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h + 4]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[8 * b + i] *= g0[i];
+                        acc[8 * b + 4 + i] *= g1[i];
+                    }
+                }
                 const uint16_t* pr = &sm.P[(32 * tt + l32) * LT + 8 * h];
-                auto au = [&](int k) { return sop(uacc, k); };
-                auto lp = [&](int k) { return lds8(pr + 16 * k); };
-                // P is lower triangular: token tile 0 needs columns 0..31 only
-                acc = tt == 0 ? mfma_chain_b<2>(au, lp, acc) : mfma_chain_b<4>(au, lp, acc);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (tt == 0 && ks >= 2) continue;  // P is lower triangular
+                    acc = mfma32(lds8(pr + 16 * ks), sop(uacc, ks), acc);
+                }
                 if (job.o) {
                     // rows past T fall outside the resource and are dropped
                     const int valid = __builtin_amdgcn_readfirstlane(min(T - n * C, C));
                     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                         job.o + ((size_t)un.head * T + (size_t)n * C) * DV + un.r0, (short)0,
                         valid * DV * 2 - un.r0 * 2, 0x00020000);
-                    const int voff = (tl * DV + 32 * ib + 4 * h) * 2;
+                    const int voff = (8 * h * DV + vl) * 2;
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                    {
-                        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            __builtin_bit_cast(u32x2, pack4(acc[4 * b], acc[4 * b + 1], acc[4 * b + 2], acc[4 * b + 3])),
-                            orsrc, voff, 16 * b, 0);
-                    }
+                    for (int e = 0; e < 16; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), orsrc, voff,
+                                                              (elem_index(tt, e, 0)) * DV * 2, 0);
                 }
             }
         }
