@@ -8,6 +8,12 @@ already resident in HBM: B=8 sequences x H=16 heads x T=8192 tokens, d=128,
 bf16 q/k/v, fp32 state, chunk 64 (the gated-delta training-shape forward).
 Prints one JSON line with tokens/s, the roofline of the dominant kernel and the
 float64 CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads: --workload gla-b4h8t4096 (gated linear attention),
+long-b2h8t262144 (the long-sequence path) and decode-4096x100 (decode_step over
+4096 states, one timed step per token).  Timing: W untimed steps (by default
+enough to cover the GPU's clock ramp), then two HIP events around K back-to-back
+steps on the launch stream.
 """
 from __future__ import annotations
 
@@ -264,8 +270,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; decode workloads: the workload's token count)")
-    ap.add_argument("--warmup", type=int, default=3)
+                    help="timed steps (default 50; decode workloads: the workload's token count)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: enough to cover the GPU's clock ramp, "
+                         "~15 ms: 30 scan calls or 300 decode steps)")
     ap.add_argument("--workload", default="gdn-b8h16t8192")
     ap.add_argument("--path", default="auto", choices=["auto", "sequential", "blelloch"])
     ap.add_argument("--leaf-chunks", type=int, default=0)
@@ -295,9 +303,13 @@ def main():
 
     w = I.WORKLOADS[args.workload]
     if w.path == "decode":
+        if args.warmup is None:
+            args.warmup = 300
         return bench_decode(args, w)
     if args.steps is None:
-        args.steps = 20
+        args.steps = 50
+    if args.warmup is None:
+        args.warmup = 30
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
