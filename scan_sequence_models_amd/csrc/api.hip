@@ -88,10 +88,16 @@ int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chun
         p.path = SCAN_PATH_BLELLOCH;
     } else if (path == SCAN_PATH_AUTO) {
         // The sequential pass runs one workgroup per (head, value slice); when
-        // that cannot fill the GPU and the sequence is long, split it into
-        // leaves and combine their aggregates with the Blelloch tree.
+        // that cannot fill the GPU, split the sequence into leaves and combine
+        // their aggregates with the Blelloch tree.  The tree pass costs about
+        // three times the chunk work, so it pays when the sequential grid
+        // fills at most a quarter of the CUs (at least two leaves of 16
+        // chunks), or half of them on long sequences.
         const int64_t wgs = heads * gds::sequential_workgroups_per_head(p.mfma, dv);
-        if (wgs * 2 <= device_cus() && nchunks >= 256) p.path = SCAN_PATH_BLELLOCH;
+        const int cus = device_cus();
+        if (gds::blelloch_supported(mode, dtype, dk, dv, chunk) &&
+            ((wgs * 4 <= cus && nchunks >= 32) || (wgs * 2 <= cus && nchunks >= 256)))
+            p.path = SCAN_PATH_BLELLOCH;
     }
     if (p.path == SCAN_PATH_BLELLOCH) {
         if (!gds::blelloch_supported(mode, dtype, dk, dv, chunk))

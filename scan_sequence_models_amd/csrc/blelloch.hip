@@ -170,10 +170,13 @@ bool blelloch_supported(int mode, int dtype, int dk, int dv, int chunk) {
 }
 
 int blelloch_default_leaf_chunks(int64_t nchunks, int64_t heads, int cus) {
-    // enough leaves that the two passes over the leaves (2 or 4 workgroups per
-    // leaf) keep every CU busy several times over
-    const int64_t want_leaves = next_pow2(ceil_div(4 * (int64_t)cus, 2 * heads));
-    int64_t g = next_pow2(ceil_div(nchunks, want_leaves));
+    // enough leaves that the output pass (2 workgroups per leaf) fills every CU
+    // about once (the leaf pass, 4 workgroups per leaf, twice), and at least 16
+    // chunks per leaf; measured best for 16 heads x 4096 chunks and 32 heads x
+    // 64 chunks on 256 CUs (fewer, longer leaves also shorten the tree)
+    int64_t leaves = next_pow2(ceil_div((int64_t)cus, 2 * heads));
+    while (leaves > 1 && nchunks / leaves < 16) leaves >>= 1;
+    int64_t g = next_pow2(ceil_div(nchunks, leaves));
     if (g < 1) g = 1;
     if (g > (1 << 20)) g = 1 << 20;
     return (int)g;
