@@ -59,6 +59,16 @@ def scan_flops(w) -> float:
     return per * w.B * w.H * w.T
 
 
+def scan_flops_alg(w) -> float:
+    """Algorithmic flops per call: the triangular products counted at their
+    useful size (half of each C x C-sized product), state products in full and
+    the UT solve C^2/3 per head-token; gla: Q K^T and P V at half size plus the
+    two state products."""
+    C, d = w.chunk, w.dk
+    per = (5 * C * d + 6 * d * d + C * C / 3) if w.mode == "gdn" else (2 * C * d + 4 * d * d)
+    return per * w.B * w.H * w.T
+
+
 def source_sha(path: str) -> str:
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
@@ -356,6 +366,7 @@ def main():
 
     alg_bytes = scan_bytes(w)
     flops = scan_flops(w)
+    flops_alg = scan_flops_alg(w)
     achieved_gbs = alg_bytes / (kern_ms / 1e3) / 1e9
     achieved_tfs = flops / (kern_ms / 1e3) / 1e12
     kernel_src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_bf16.hip")
@@ -395,6 +406,9 @@ def main():
             "frac": achieved_tfs / BF16_MFMA_PEAK_TFS,
             "flops_per_launch": flops,
             "count": "executed dense-tile flops of the chunk algorithm",
+            "alg_tflops": flops_alg / (kern_ms / 1e3) / 1e12,
+            "alg_frac": flops_alg / (kern_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
+            "alg_flops_per_launch": flops_alg,
         },
         "head_tokens_per_s": w.B * w.H * w.T / (ms_per_step / 1e3),
     }
