@@ -25,7 +25,7 @@ _CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-p
            "-std=c11", "-Wall", "-Wextra"]
 _lib = None
 
-GDN, GLA = 0, 1
+GDN, GLA, GDN_EW = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -74,6 +74,8 @@ def _mode(mode) -> int:
         return GDN
     if mode in (GLA, "gla"):
         return GLA
+    if mode in (GDN_EW, "gdn_ew"):
+        return GDN_EW
     raise ValueError(f"unknown mode {mode!r}")
 
 
@@ -81,9 +83,11 @@ def scan(mode, q, k, v, alpha, beta=None, S0=None, threads: int | None = None,
          store_o: bool = True, return_threads: bool = False):
     """Token-by-token scan in float64.
 
-    q, k: [..., T, dk]; v: [..., T, dv]; alpha, beta: [..., T]; S0: [..., dv, dk]
-    or None (zero).  Leading dimensions are independent heads.  Inputs are taken
-    as float32 (exact for bfloat16 values), S0 as float64.
+    q, k: [..., T, dk]; v: [..., T, dv]; alpha: [..., T]; beta: [..., T] for
+    "gdn", None for "gla", [2, ..., T] (erase strengths, then write strengths)
+    for "gdn_ew"; S0: [..., dv, dk] or None (zero).  Leading dimensions are
+    independent heads.  Inputs are taken as float32 (exact for bfloat16
+    values), S0 as float64.
     Returns (o [..., T, dv] float64 or None, ST [..., dv, dk] float64).
     """
     m = _mode(mode)
@@ -94,11 +98,11 @@ def scan(mode, q, k, v, alpha, beta=None, S0=None, threads: int | None = None,
     BH = int(np.prod(lead)) if lead else 1
     if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or alpha.shape != q.shape[:-1]:
         raise ValueError("shape mismatch among q, k, v, alpha")
-    if m == GDN:
+    if m != GLA:
         if beta is None:
-            raise ValueError("gdn mode needs beta")
+            raise ValueError("gdn modes need beta")
         beta = _f32(beta)
-        if beta.shape != alpha.shape:
+        if beta.shape != ((2, *alpha.shape) if m == GDN_EW else alpha.shape):
             raise ValueError("beta shape mismatch")
     else:
         beta = None
@@ -119,6 +123,7 @@ def scan(mode, q, k, v, alpha, beta=None, S0=None, threads: int | None = None,
 def decode_step(mode, q, k, v, alpha, beta, S, threads: int | None = None):
     """One token per state, S ([N, dv, dk] float64, C-contiguous) updated in place.
 
+    beta: [N] ("gdn"), None ("gla") or [2, N] ("gdn_ew": erase, write).
     Returns o [N, dv] float64 = S_new q.
     """
     m = _mode(mode)
@@ -129,8 +134,10 @@ def decode_step(mode, q, k, v, alpha, beta, S, threads: int | None = None):
     dv = v.shape[1]
     if S.shape != (N, dv, dk):
         raise ValueError("S shape mismatch")
-    if m == GDN:
+    if m != GLA:
         beta = _f32(beta)
+        if beta.shape != ((2, N) if m == GDN_EW else (N,)):
+            raise ValueError("beta shape mismatch")
     else:
         beta = None
     o = np.empty((N, dv), np.float64)

@@ -13,6 +13,13 @@
  * gated delta rule (mode 0):  E_t = alpha_t (I - beta_t k_t k_t^T),
  *                             f_t = beta_t v_t k_t^T
  * gated linear attention (mode 1):  E_t = alpha_t I,  f_t = v_t k_t^T
+ * gated delta rule with separate erase and write strengths (mode 2):
+ *                             E_t = alpha_t (I - be_t k_t k_t^T),
+ *                             f_t = bw_t v_t k_t^T
+ *   (PRISM's write-forget decoupling, gist.science explainer 2.1: the forget
+ *   operator stays the Gated-DeltaNet rank-1 form while the write is free; a
+ *   token with alpha = 1, be = 0 is a pure write, which is how PRISM's rank-L
+ *   corrections enter the scan)
  *
  * Sources:
  *  - "Sequential Parallel Duality in Prefix Scannable Models" (papernotes.org
@@ -38,6 +45,7 @@
  *   a_i   = sum_j S_ij k_j                       (row of S_{t-1} k_t)
  *   S_ij <- alpha (S_ij - beta a_i k_j) + beta v_i k_j      [gdn]
  *   S_ij <- alpha S_ij + v_i k_j                            [gla]
+ *   S_ij <- alpha (S_ij - be a_i k_j) + bw v_i k_j          [gdn, split strengths]
  *   o_i   = sum_j S_ij q_j                       (row of S_t q_t)
  * Inputs arrive as float32 (bfloat16 inputs are exact in float32) and are
  * widened exactly to float64.  Rows of S are independent, so work is split over
@@ -51,7 +59,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_GDN = 0, ORACLE_GLA = 1 };
+enum { ORACLE_GDN = 0, ORACLE_GLA = 1, ORACLE_GDN_EW = 2 };
 
 typedef struct {
     int mode;
@@ -84,15 +92,17 @@ static int run_rows(const job_t *J, int64_t h, int r0, int r1)
         const float *kt = J->k + tok * dk;
         const float *vt = J->v + tok * dv;
         const double al = (double)J->alpha[tok];
-        const double be = J->mode == ORACLE_GDN ? (double)J->beta[tok] : 0.0;
+        /* erase and write strengths; mode 2 reads them from two planes of BH*T */
+        const double be = J->mode != ORACLE_GLA ? (double)J->beta[tok] : 0.0;
+        const double bw = J->mode == ORACLE_GDN_EW ? (double)J->beta[(size_t)(J->BH * T) + tok] : be;
         for (int r = 0; r < nrows; ++r) {
             double *Si = S + (size_t)r * dk;
             const double vi = (double)vt[r0 + r];
-            if (J->mode == ORACLE_GDN) {
+            if (J->mode != ORACLE_GLA) {
                 double a = 0.0;
                 for (int j = 0; j < dk; ++j) a += Si[j] * (double)kt[j];
                 for (int j = 0; j < dk; ++j)
-                    Si[j] = al * (Si[j] - be * a * (double)kt[j]) + be * vi * (double)kt[j];
+                    Si[j] = al * (Si[j] - be * a * (double)kt[j]) + bw * vi * (double)kt[j];
             } else {
                 for (int j = 0; j < dk; ++j) Si[j] = al * Si[j] + vi * (double)kt[j];
             }
@@ -126,7 +136,9 @@ static void *worker(void *arg)
 /*
  * Full-sequence scan of BH independent heads.
  *   q, k: [BH, T, dk] float32     v: [BH, T, dv] float32
- *   alpha, beta: [BH, T] float32 (beta ignored, may be NULL, in mode 1)
+ *   alpha: [BH, T] float32
+ *   beta: [BH, T] float32 (mode 0); ignored, may be NULL (mode 1); [2, BH, T]
+ *         float32 (mode 2: erase strengths, then write strengths)
  *   S0: [BH, dv, dk] float64 or NULL (zero state)
  *   o:  [BH, T, dv] float64 or NULL (not stored; still computed)
  *   ST: [BH, dv, dk] float64 or NULL
@@ -138,9 +150,10 @@ int oracle_scan_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
                     const float *alpha, const float *beta, const double *S0,
                     double *o, double *ST, int nthreads)
 {
-    if ((mode != ORACLE_GDN && mode != ORACLE_GLA) || BH < 0 || T < 0 || dk <= 0 || dv <= 0)
+    if ((mode != ORACLE_GDN && mode != ORACLE_GLA && mode != ORACLE_GDN_EW) || BH < 0 || T < 0 ||
+        dk <= 0 || dv <= 0)
         return -1;
-    if (mode == ORACLE_GDN && !beta && BH * T > 0) return -1;
+    if (mode != ORACLE_GLA && !beta && BH * T > 0) return -1;
     if (BH * T > 0 && (!q || !k || !v || !alpha)) return -1;
     if (nthreads < 1) nthreads = 1;
 
@@ -172,7 +185,8 @@ int oracle_scan_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
 
 /*
  * One token for each of N independent states, state updated in place:
- *   q, k: [N, dk]   v: [N, dv]   alpha, beta: [N]   S: [N, dv, dk] float64
+ *   q, k: [N, dk]   v: [N, dv]   alpha: [N]   beta: [N] ([2, N] in mode 2)
+ *   S: [N, dv, dk] float64
  *   o: [N, dv] float64 = S_new q
  * Same arithmetic as oracle_scan_f64 with T = 1 (the per-token update of the
  * sequential view, key design 1 of the prefix-scan notes).
