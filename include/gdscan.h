@@ -10,6 +10,15 @@
  *   SCAN_GDN (gated delta rule):       E_t = alpha_t (I - beta_t k_t k_t^T),
  *                                      f_t = beta_t v_t k_t^T
  *   SCAN_GLA (gated linear attention): E_t = alpha_t I,  f_t = v_t k_t^T
+ *   SCAN_GDN_EW (gated delta rule, separate erase and write strengths):
+ *                                      E_t = alpha_t (I - be_t k_t k_t^T),
+ *                                      f_t = bw_t v_t k_t^T
+ *
+ * SCAN_GDN_EW is PRISM's write-forget decoupling ("PRISM: Parallel Residual
+ * Iterative Sequence Model", gist.science explainer, technical summary 2.1:
+ * the forget operator stays the Gated-DeltaNet rank-1 form, the write is
+ * free).  An element with alpha = 1, be = 0 is a pure write, so a token's
+ * rank-L write becomes L + 1 consecutive elements (see prism_expand below).
  *
  * Sources: "Sequential Parallel Duality in Prefix Scannable Models"
  * (papernotes.org ICLR 2026 notes), key design 2 (affine update
@@ -35,7 +44,8 @@
  *    scan_last_error() (per host thread) describes the problem.
  *  - Data preconditions are documented, not checked on the device: finite
  *    inputs, 0 < alpha <= 1, and for SCAN_GDN 0 <= beta <= 1 with unit-norm keys
- *    recommended (then every E_t has spectral norm <= 1).
+ *    recommended (then every E_t has spectral norm <= 1; the same holds for
+ *    the erase strengths of SCAN_GDN_EW, whose write strengths are free).
  *  - Layouts are dense and row-major.  q, k, v, o, S0, ST and S must be 16-byte
  *    aligned; alpha and beta 4-byte aligned.
  */
@@ -51,6 +61,7 @@ extern "C" {
 /* mode */
 #define SCAN_GDN 0
 #define SCAN_GLA 1
+#define SCAN_GDN_EW 2
 
 /* element type of q, k, v and o (alpha, beta and all states are float32) */
 #define SCAN_F32 0
@@ -90,7 +101,9 @@ size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk,
  *
  *   q, k : [B, H, T, dk]  dtype          v, o : [B, H, T, dv]  dtype
  *   alpha: [B, H, T] float32 in (0, 1]
- *   beta : [B, H, T] float32 for SCAN_GDN; must be NULL for SCAN_GLA
+ *   beta : [B, H, T] float32 for SCAN_GDN; must be NULL for SCAN_GLA;
+ *          [2, B, H, T] float32 for SCAN_GDN_EW (plane 0: erase strengths be,
+ *          plane 1: write strengths bw)
  *   S0   : [B, H, dv, dk] float32 initial state, or NULL for the zero state
  *   ST   : [B, H, dv, dk] float32 final state, or NULL to skip writing it.
  *          ST may be the same pointer as S0 (in-place carry); any other overlap
@@ -120,7 +133,8 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
  *   S <- S E + f,   o = S q   (with the updated S)
  *
  *   q, k : [N, dk] dtype     v, o : [N, dv] dtype
- *   alpha: [N] float32       beta : [N] float32 (SCAN_GDN) or NULL (SCAN_GLA)
+ *   alpha: [N] float32       beta : [N] float32 (SCAN_GDN), NULL (SCAN_GLA) or
+ *                            [2, N] float32 (SCAN_GDN_EW: erase, then write)
  *   S    : [N, dv, dk] float32, read and written in place
  * Supported: dk in {16, 32, 64, 128}, dv >= 1, either dtype.
  * o must not overlap any input or S.  Returns SCAN_OK or an error status.
@@ -128,6 +142,48 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
 int decode_step(int mode, int dtype, int N, int dk, int dv, const void *q, const void *k,
                 const void *v, const float *alpha, const float *beta, float *S, void *o,
                 void *stream);
+
+/* Limits of prism_expand */
+#define PRISM_MAX_STEPS 8   /* L: refinement steps (rank-1 corrections) per token */
+#define PRISM_MAX_WINDOW 8  /* W: taps of the anchor's short convolution */
+
+/*
+ * PRISM's rank-L write ("PRISM: Parallel Residual Iterative Sequence Model",
+ * gist.science explainer, technical summary 2.2; PRISM article,
+ * banbantang.com, section 3(2)-(4)) expanded into a SCAN_GDN_EW element
+ * stream.  Per head and token t, from the input only:
+ *
+ *   u_t       = sum_{j<W} conv[j] * x_{t-j}          (0 before the start)
+ *   r^(1)     = v_t - u_t
+ *   k^(l)     = Wk[l] u_t,   p^(l) = Wp[l] u_t       (l = 1..L)
+ *   delta^(l) = GELU(p^(l) * r^(l)),  r^(l+1) = r^(l) - delta^(l)
+ *
+ * and the write B_t = beta_t v_t k_t^T + sum_l beta_l[t,l] delta^(l) k^(l)T.
+ * Token t becomes elements t(L+1) .. t(L+1)+L of the output stream:
+ *   element t(L+1)    : q = 0 (q_t if L = 0), k_t, v_t, alpha_t, erase beta_t, write beta_t
+ *   element t(L+1)+l  : q = 0 (q_t for l = L), k^(l), delta^(l), alpha 1, erase 0,
+ *                       write beta_l[t, l-1]
+ * so scan_fwd(SCAN_GDN_EW, ..., T (L+1), q2, k2, v2, alpha2, beta2, ...) gives
+ * o2 with the layer's output o_t = o2[t (L+1) + L] and the same final state.
+ * GELU is x (1 + erf(x / sqrt 2)) / 2; the factors are computed in float32
+ * (bfloat16 data: the anchor is split into two bfloat16 parts for the MFMA
+ * projections) and stored in dtype.
+ *
+ *   q, k : [B, H, T, dk] dtype      v, x : [B, H, T, dv] dtype (x: the anchor's source)
+ *   alpha, beta : [B, H, T] float32  beta_l : [B, H, T, L] float32
+ *   conv : [H, W, dv] float32        Wk : [H, L, dk, dv] dtype   Wp : [H, L, dv, dv] dtype
+ *   q2, k2 : [B, H, T (L+1), dk] dtype      v2 : [B, H, T (L+1), dv] dtype
+ *   alpha2 : [B, H, T (L+1)] float32        beta2 : [2, B, H, T (L+1)] float32
+ * x, beta_l, conv, Wk and Wp may be NULL when L = 0.  Outputs must not overlap
+ * inputs or each other.  Supported: dk, dv in {16, 32, 64, 128}, either dtype
+ * (bfloat16 with dk = dv = 128 projects on the MFMA units).  0 <= L <= 8,
+ * 1 <= W <= 8.  Returns SCAN_OK or an error status.
+ */
+int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
+                 const void *q, const void *k, const void *v, const void *x,
+                 const float *alpha, const float *beta, const float *beta_l,
+                 const float *conv, const void *Wk, const void *Wp,
+                 void *q2, void *k2, void *v2, float *alpha2, float *beta2, void *stream);
 
 /* Message describing the last non-zero status returned on this host thread. */
 const char *scan_last_error(void);

@@ -1,11 +1,12 @@
-"""gfx950 (MI355X) matrix-state affine prefix scan: gated delta rule and gated
-linear attention.
+"""gfx950 (MI355X) matrix-state affine prefix scan: gated delta rule (with
+optionally split erase/write strengths), gated linear attention, and PRISM's
+rank-L write expanded onto the same scan.
 
 The compute path is the C-ABI library ``libgdscan.so`` (``include/gdscan.h``,
 sources in ``csrc/``); this package is its Python binding.  The library is
 loaded on first use.
 """
 from ._lib import (  # noqa: F401
-    PATHS, SCAN_BF16, SCAN_F32, SCAN_GDN, SCAN_GLA, ScanError, decode_step, last_error, lib,
-    scan_fwd, scan_fwd_workspace_size, version,
+    PATHS, SCAN_BF16, SCAN_F32, SCAN_GDN, SCAN_GDN_EW, SCAN_GLA, ScanError, decode_step,
+    last_error, lib, prism_expand, prism_scan_fwd, scan_fwd, scan_fwd_workspace_size, version,
 )

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdscan.s
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "gdscan.h")
 
-SCAN_GDN, SCAN_GLA = 0, 1
+SCAN_GDN, SCAN_GLA, SCAN_GDN_EW = 0, 1, 2
 SCAN_F32, SCAN_BF16 = 0, 1
 SCAN_OK, SCAN_EINVAL, SCAN_EUNSUPPORTED, SCAN_EWORKSPACE, SCAN_EALIGN, SCAN_EHIP = range(6)
 PATHS = {"auto": 0, "sequential": 1, "blelloch": 2}
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.scan_fwd.restype = i
         L.decode_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
         L.decode_step.restype = i
+        L.prism_expand.argtypes = [i] * 8 + [p] * 15 + [p]
+        L.prism_expand.restype = i
         L.scan_last_error.restype = ctypes.c_char_p
         L.scan_version.restype = ctypes.c_char_p
         _lib = L
@@ -125,7 +127,9 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
     """Forward scan over [B, H, T, d] tensors; returns (o, ST).
 
     ``beta is None`` selects gated linear attention (E = alpha I, f = v k^T),
-    otherwise the gated delta rule.  ``S0=None`` is the zero state.  ``ST`` may
+    a [B, H, T] ``beta`` the gated delta rule, and a [2, B, H, T] ``beta``
+    (erase strengths, then write strengths) the gated delta rule with split
+    strengths (SCAN_GDN_EW).  ``S0=None`` is the zero state.  ``ST`` may
     be ``S0`` itself (in-place carry).  ``write_state=False`` skips S_T.
     """
     _need(q, "q")
@@ -138,9 +142,9 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
     _need(k, "k", dt, (B, H, T, dk), dev)
     _need(v, "v", dt, (B, H, T, dv), dev)
     _need(alpha, "alpha", torch.float32, (B, H, T), dev)
-    mode = SCAN_GLA if beta is None else SCAN_GDN
+    mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 4 else SCAN_GDN
     if beta is not None:
-        _need(beta, "beta", torch.float32, (B, H, T), dev)
+        _need(beta, "beta", torch.float32, (2, B, H, T) if mode == SCAN_GDN_EW else (B, H, T), dev)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, dv, dk), dev)
     if o is None:
@@ -169,7 +173,8 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
 def decode_step(q, k, v, alpha, beta, S, o=None):
     """One token per state: S [N, dv, dk] float32 updated in place; returns o [N, dv].
 
-    ``beta is None`` selects gated linear attention.
+    ``beta is None`` selects gated linear attention; a [2, N] ``beta`` (erase,
+    write) the split-strength mode.
     """
     _need(q, "q")
     dev, dt = q.device, q.dtype
@@ -180,9 +185,9 @@ def decode_step(q, k, v, alpha, beta, S, o=None):
     _need(k, "k", dt, (N, dk), dev)
     _need(v, "v", dt, (N, dv), dev)
     _need(alpha, "alpha", torch.float32, (N,), dev)
-    mode = SCAN_GLA if beta is None else SCAN_GDN
+    mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 2 else SCAN_GDN
     if beta is not None:
-        _need(beta, "beta", torch.float32, (N,), dev)
+        _need(beta, "beta", torch.float32, (2, N) if mode == SCAN_GDN_EW else (N,), dev)
     _need(S, "S", torch.float32, (N, dv, dk), dev)
     if o is None:
         o = torch.empty((N, dv), dtype=dt, device=dev)
@@ -192,3 +197,65 @@ def decode_step(q, k, v, alpha, beta, S, o=None):
                                _ptr(alpha), _ptr(beta), _ptr(S), _ptr(o), _stream(dev))
     _check(st)
     return o
+
+
+def prism_expand(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, Wp=None):
+    """PRISM write factors expanded into a split-strength scan stream.
+
+    q, k [B, H, T, dk] and v, x [B, H, T, dv] (float32 or bfloat16); alpha, beta
+    [B, H, T] float32; beta_l [B, H, T, L] float32; conv [H, W, dv] float32; Wk
+    [H, L, dk, dv] and Wp [H, L, dv, dv] in the data type.  ``beta_l=None``
+    means L = 0.  Returns (q2, k2, v2, alpha2, beta2) with T (L+1) elements per
+    head; beta2 is [2, B, H, T (L+1)] (erase, write), ready for ``scan_fwd``.
+    """
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", dt, (B, H, T, dk), dev)
+    _need(v, "v", dt, (B, H, T, dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    _need(beta, "beta", torch.float32, (B, H, T), dev)
+    L = 0 if beta_l is None else beta_l.shape[-1]
+    W = 1
+    if L > 0:
+        _need(x, "x", dt, (B, H, T, dv), dev)
+        _need(beta_l, "beta_l", torch.float32, (B, H, T, L), dev)
+        _need(conv, "conv", torch.float32, None, dev)
+        if conv.dim() != 3 or conv.shape[0] != H or conv.shape[2] != dv:
+            raise ValueError(f"conv must be [H, W, dv] = [{H}, W, {dv}]")
+        W = conv.shape[1]
+        _need(Wk, "Wk", dt, (H, L, dk, dv), dev)
+        _need(Wp, "Wp", dt, (H, L, dv, dv), dev)
+    T2 = T * (L + 1)
+    q2 = torch.empty((B, H, T2, dk), dtype=dt, device=dev)
+    k2 = torch.empty((B, H, T2, dk), dtype=dt, device=dev)
+    v2 = torch.empty((B, H, T2, dv), dtype=dt, device=dev)
+    a2 = torch.empty((B, H, T2), dtype=torch.float32, device=dev)
+    b2 = torch.empty((2, B, H, T2), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().prism_expand(_dtype_code(q), B, H, T, dk, dv, L, W, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(x) if L else None, _ptr(alpha), _ptr(beta),
+                                _ptr(beta_l) if L else None, _ptr(conv) if L else None,
+                                _ptr(Wk) if L else None, _ptr(Wp) if L else None, _ptr(q2),
+                                _ptr(k2), _ptr(v2), _ptr(a2), _ptr(b2), _stream(dev))
+    _check(st)
+    return q2, k2, v2, a2, b2
+
+
+def prism_scan_fwd(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, Wp=None,
+                   S0=None, *, chunk: int = 64, path: str = "auto", leaf_chunks: int = 0,
+                   write_state: bool = True):
+    """PRISM layer forward: ``prism_expand`` then the split-strength ``scan_fwd``.
+
+    Returns (o, ST) with o [B, H, T, dv] a view of the expanded output (every
+    (L+1)-th element, the last of each token's group).
+    """
+    q2, k2, v2, a2, b2 = prism_expand(q, k, v, alpha, beta, x, beta_l, conv, Wk, Wp)
+    o2, ST = scan_fwd(q2, k2, v2, a2, b2, S0, chunk=chunk, path=path, leaf_chunks=leaf_chunks,
+                      write_state=write_state)
+    B, H, T, _ = q.shape
+    G = q2.shape[2] // T
+    return o2.view(B, H, T, G, o2.shape[-1])[:, :, :, G - 1], ST

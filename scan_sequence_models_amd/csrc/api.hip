@@ -61,10 +61,17 @@ struct Plan {
     size_t workspace;  // bytes
 };
 
+bool valid_mode(int mode) { return mode == SCAN_GDN || mode == SCAN_GLA || mode == SCAN_GDN_EW; }
+// Kernel mode: 0 = gated delta rule (erase and write strengths may differ), 1 = GLA.
+int kernel_mode(int mode) { return mode == SCAN_GLA ? 1 : 0; }
+// Elements of the beta argument per token: 1, none (GLA), or 2 planes (split strengths).
+int beta_planes(int mode) { return mode == SCAN_GLA ? 0 : mode == SCAN_GDN_EW ? 2 : 1; }
+
 // Validates the sizes/enums of a scan_fwd call and picks the kernels.
 int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
               const scan_opts* opts, Plan* plan) {
-    if (mode != SCAN_GDN && mode != SCAN_GLA) return fail(SCAN_EINVAL, "mode must be SCAN_GDN or SCAN_GLA (got %d)", mode);
+    if (!valid_mode(mode)) return fail(SCAN_EINVAL, "mode must be SCAN_GDN, SCAN_GLA or SCAN_GDN_EW (got %d)", mode);
+    const int km = kernel_mode(mode);
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
     if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
         return fail(SCAN_EINVAL, "B, H, T, dk, dv must be >= 1 (got %d, %d, %d, %d, %d)", B, H, T, dk, dv);
@@ -77,8 +84,8 @@ int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chun
     if (leaf < 0 || (leaf & (leaf - 1)) != 0) return fail(SCAN_EINVAL, "opts->leaf_chunks must be 0 or a power of two (got %d)", leaf);
 
     Plan p{};
-    p.mfma = dtype == SCAN_BF16 && gds::chunk_mfma_supported(mode, dk, dv, chunk);
-    if (!p.mfma && !gds::chunk_f32_supported(mode, dk, dv, chunk))
+    p.mfma = dtype == SCAN_BF16 && gds::chunk_mfma_supported(km, dk, dv, chunk);
+    if (!p.mfma && !gds::chunk_f32_supported(km, dk, dv, chunk))
         return fail(SCAN_EUNSUPPORTED, "unsupported size: dk=%d dv=%d chunk=%d (dk in {16,32,64,128}, dv a multiple of 16)", dk, dv, chunk);
 
     const int64_t nchunks = (T + chunk - 1) / chunk;
@@ -95,12 +102,12 @@ int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chun
         // chunks), or half of them on long sequences.
         const int64_t wgs = heads * gds::sequential_workgroups_per_head(p.mfma, dv);
         const int cus = device_cus();
-        if (gds::blelloch_supported(mode, dtype, dk, dv, chunk) &&
+        if (gds::blelloch_supported(km, dtype, dk, dv, chunk) &&
             ((wgs * 4 <= cus && nchunks >= 32) || (wgs * 2 <= cus && nchunks >= 256)))
             p.path = SCAN_PATH_BLELLOCH;
     }
     if (p.path == SCAN_PATH_BLELLOCH) {
-        if (!gds::blelloch_supported(mode, dtype, dk, dv, chunk))
+        if (!gds::blelloch_supported(km, dtype, dk, dv, chunk))
             return fail(SCAN_EUNSUPPORTED, "the Blelloch path supports dk = dv = 128 only (got dk=%d dv=%d)", dk, dv);
         if (leaf == 0) leaf = gds::blelloch_default_leaf_chunks(nchunks, heads, device_cus());
         p.leaf_chunks = leaf;
@@ -133,7 +140,7 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     int st = plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p);
     if (st != SCAN_OK) return st;
     if (!q || !k || !v || !alpha || !o) return fail(SCAN_EINVAL, "q, k, v, alpha and o must be non-null");
-    if (mode == SCAN_GDN && !beta) return fail(SCAN_EINVAL, "SCAN_GDN needs beta");
+    if (mode != SCAN_GLA && !beta) return fail(SCAN_EINVAL, "SCAN_GDN and SCAN_GDN_EW need beta");
     if (mode == SCAN_GLA && beta) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta (pass NULL)");
     const void* a16[] = {q, k, v, o, S0, ST};
     const char* n16[] = {"q", "k", "v", "o", "S0", "ST"};
@@ -149,7 +156,8 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     const size_t BH = (size_t)B * H;
     const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
                         range("v", v, BH * T * dv * es), range("alpha", alpha, BH * T * 4),
-                        range("beta", beta, BH * T * 4), range("S0", S0, BH * dv * dk * 4),
+                        range("beta", beta, BH * T * 4 * beta_planes(mode)),
+                        range("S0", S0, BH * dv * dk * 4),
                         range("workspace", workspace, p.workspace)};
     const Range ro = range("o", o, BH * T * dv * es);
     const Range rs = range("ST", ST, BH * dv * dk * 4);
@@ -161,14 +169,19 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     if (overlaps(ro, rs)) return fail(SCAN_EINVAL, "o overlaps ST");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int km = kernel_mode(mode);
+    // split strengths: the write plane follows the erase plane
+    const float* beta_w = mode == SCAN_GDN_EW ? beta + BH * T : beta;
     hipError_t e;
     if (p.path == SCAN_PATH_BLELLOCH) {
-        e = gds::launch_blelloch(mode, (int)BH, T, dk, dv, chunk, p.leaf_chunks, q, k, v, alpha, beta,
-                                 S0, o, ST, workspace, s);
+        e = gds::launch_blelloch(km, (int)BH, T, dk, dv, chunk, p.leaf_chunks, q, k, v, alpha, beta,
+                                 beta_w, S0, o, ST, workspace, s);
     } else if (p.mfma) {
-        e = gds::launch_chunk_mfma(mode, (int)BH, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST, s);
+        e = gds::launch_chunk_mfma(km, (int)BH, T, dk, dv, chunk, q, k, v, alpha, beta, beta_w, S0, o,
+                                   ST, s);
     } else {
-        e = gds::launch_chunk_f32(mode, dtype, (int)BH, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST, s);
+        e = gds::launch_chunk_f32(km, dtype, (int)BH, T, dk, dv, chunk, q, k, v, alpha, beta, beta_w,
+                                  S0, o, ST, s);
     }
     if (e != hipSuccess) return hip_fail(e, "scan_fwd launch");
     return SCAN_OK;
@@ -177,13 +190,13 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
 int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const void* k,
                 const void* v, const float* alpha, const float* beta, float* S, void* o,
                 void* stream) {
-    if (mode != SCAN_GDN && mode != SCAN_GLA) return fail(SCAN_EINVAL, "mode must be SCAN_GDN or SCAN_GLA (got %d)", mode);
+    if (!valid_mode(mode)) return fail(SCAN_EINVAL, "mode must be SCAN_GDN, SCAN_GLA or SCAN_GDN_EW (got %d)", mode);
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
     if (N < 1 || dk < 1 || dv < 1) return fail(SCAN_EINVAL, "N, dk, dv must be >= 1 (got %d, %d, %d)", N, dk, dv);
     if (!gds::decode_supported(dk)) return fail(SCAN_EUNSUPPORTED, "decode_step supports dk in {16,32,64,128} (got %d)", dk);
     if ((int64_t)N * ((dv + 127) / 128) > INT32_MAX) return fail(SCAN_EINVAL, "N*dv too large");
     if (!q || !k || !v || !alpha || !S || !o) return fail(SCAN_EINVAL, "q, k, v, alpha, S and o must be non-null");
-    if (mode == SCAN_GDN && !beta) return fail(SCAN_EINVAL, "SCAN_GDN needs beta");
+    if (mode != SCAN_GLA && !beta) return fail(SCAN_EINVAL, "SCAN_GDN and SCAN_GDN_EW need beta");
     if (mode == SCAN_GLA && beta) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta (pass NULL)");
     const void* a16[] = {q, k, v, o, S};
     const char* n16[] = {"q", "k", "v", "o", "S"};
@@ -193,16 +206,73 @@ int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const
     const size_t es = dtype == SCAN_BF16 ? 2 : 4;
     const Range in[] = {range("q", q, (size_t)N * dk * es), range("k", k, (size_t)N * dk * es),
                         range("v", v, (size_t)N * dv * es), range("alpha", alpha, (size_t)N * 4),
-                        range("beta", beta, (size_t)N * 4), range("S", S, (size_t)N * dv * dk * 4)};
+                        range("beta", beta, (size_t)N * 4 * beta_planes(mode)),
+                        range("S", S, (size_t)N * dv * dk * 4)};
     const Range ro = range("o", o, (size_t)N * dv * es);
     for (const Range& r : in)
         if (overlaps(ro, r)) return fail(SCAN_EINVAL, "o overlaps %s", r.name);
     const Range rS = in[5];
     for (int i = 0; i < 5; ++i)
         if (overlaps(rS, in[i])) return fail(SCAN_EINVAL, "S overlaps %s", in[i].name);
-    hipError_t e = gds::launch_decode(mode, dtype, N, dk, dv, q, k, v, alpha, beta, S, o,
-                                      static_cast<hipStream_t>(stream));
+    const float* beta_w = mode == SCAN_GDN_EW ? beta + N : beta;
+    hipError_t e = gds::launch_decode(kernel_mode(mode), dtype, N, dk, dv, q, k, v, alpha, beta, beta_w,
+                                      S, o, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode_step launch");
+    return SCAN_OK;
+}
+
+int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W, const void* q,
+                 const void* k, const void* v, const void* x, const float* alpha, const float* beta,
+                 const float* beta_l, const float* conv, const void* Wk, const void* Wp, void* q2,
+                 void* k2, void* v2, float* alpha2, float* beta2, void* stream) {
+    if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
+    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
+        return fail(SCAN_EINVAL, "B, H, T, dk, dv must be >= 1 (got %d, %d, %d, %d, %d)", B, H, T, dk, dv);
+    if (L < 0 || L > PRISM_MAX_STEPS) return fail(SCAN_EINVAL, "L must be in [0, %d] (got %d)", PRISM_MAX_STEPS, L);
+    if (W < 1 || W > PRISM_MAX_WINDOW) return fail(SCAN_EINVAL, "W must be in [1, %d] (got %d)", PRISM_MAX_WINDOW, W);
+    if (!gds::prism_supported(dtype, dk, dv))
+        return fail(SCAN_EUNSUPPORTED, "prism_expand supports dk, dv in {16, 32, 64, 128} (got %d, %d)", dk, dv);
+    const int64_t G = L + 1;
+    if ((int64_t)T * G > INT32_MAX / 2 || (int64_t)B * H > INT32_MAX / 64 ||
+        (int64_t)B * H * ((T + 15) / 16) > INT32_MAX)
+        return fail(SCAN_EINVAL, "B*H and T*(L+1) too large");
+    if (!q || !k || !v || !alpha || !beta || !q2 || !k2 || !v2 || !alpha2 || !beta2)
+        return fail(SCAN_EINVAL, "q, k, v, alpha, beta and the five outputs must be non-null");
+    if (L > 0 && (!x || !beta_l || !conv || !Wk || !Wp))
+        return fail(SCAN_EINVAL, "L > 0 needs x, beta_l, conv, Wk and Wp");
+    const void* a16[] = {q, k, v, x, conv, Wk, Wp, q2, k2, v2};
+    const char* n16[] = {"q", "k", "v", "x", "conv", "Wk", "Wp", "q2", "k2", "v2"};
+    for (int i = 0; i < 10; ++i)
+        if (a16[i] && !aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
+    const void* a4[] = {alpha, beta, beta_l, alpha2, beta2};
+    for (const void* p : a4)
+        if (p && !aligned(p, 4)) return fail(SCAN_EALIGN, "gate arrays must be 4-byte aligned");
+    const size_t es = dtype == SCAN_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H, T2 = (size_t)T * G;
+    const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
+                        range("v", v, BH * T * dv * es), range("x", x, L ? BH * T * dv * es : 0),
+                        range("alpha", alpha, BH * T * 4), range("beta", beta, BH * T * 4),
+                        range("beta_l", beta_l, BH * T * L * 4),
+                        range("conv", conv, L ? (size_t)H * W * dv * 4 : 0),
+                        range("Wk", Wk, (size_t)H * L * dk * dv * es),
+                        range("Wp", Wp, (size_t)H * L * dv * dv * es)};
+    const Range out[] = {range("q2", q2, BH * T2 * dk * es), range("k2", k2, BH * T2 * dk * es),
+                         range("v2", v2, BH * T2 * dv * es), range("alpha2", alpha2, BH * T2 * 4),
+                         range("beta2", beta2, 2 * BH * T2 * 4)};
+    for (int a = 0; a < 5; ++a) {
+        for (const Range& r : in)
+            if (overlaps(out[a], r)) return fail(SCAN_EINVAL, "%s overlaps %s", out[a].name, r.name);
+        for (int b = a + 1; b < 5; ++b)
+            if (overlaps(out[a], out[b])) return fail(SCAN_EINVAL, "%s overlaps %s", out[a].name, out[b].name);
+    }
+    gds::PrismJob j{};
+    j.q = q; j.k = k; j.v = v; j.x = x;
+    j.alpha = alpha; j.beta = beta; j.beta_l = beta_l; j.conv = conv;
+    j.Wk = Wk; j.Wp = Wp;
+    j.q2 = q2; j.k2 = k2; j.v2 = v2; j.alpha2 = alpha2; j.beta2 = beta2;
+    j.BH = (int)BH; j.H = H; j.T = T; j.dk = dk; j.dv = dv; j.L = L; j.W = W;
+    hipError_t e = gds::launch_prism_expand(dtype, j, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prism_expand launch");
     return SCAN_OK;
 }
 

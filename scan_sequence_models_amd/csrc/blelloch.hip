@@ -190,12 +190,13 @@ size_t blelloch_workspace_bytes(int64_t heads, int64_t nchunks, int leaf_chunks,
 
 hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, int leaf_chunks,
                            const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* S0, void* o, float* ST,
-                           void* workspace, hipStream_t stream) {
+                           const float* beta, const float* beta_w, const float* S0, void* o,
+                           float* ST, void* workspace, hipStream_t stream) {
     const int nchunks = (T + kChunk - 1) / kChunk;
     const Layout L = layout(BH, nchunks, leaf_chunks);
     if (L.m == 1)  // one leaf: the tree is empty
-        return launch_chunk_mfma(mode, BH, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST, stream);
+        return launch_chunk_mfma(mode, BH, T, dk, dv, chunk, q, k, v, alpha, beta, beta_w, S0, o, ST,
+                                 stream);
     float* ws = static_cast<float*>(workspace);
 
     ChunkJob job{};
@@ -204,6 +205,7 @@ hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, i
     job.v = static_cast<const uint16_t*>(v);
     job.alpha = alpha;
     job.beta = beta;
+    job.beta_w = beta_w;
     job.heads = BH;
     job.T = T;
     job.nchunks = nchunks;

@@ -15,7 +15,7 @@ int blelloch_default_leaf_chunks(int64_t nchunks, int64_t heads, int cus);
 size_t blelloch_workspace_bytes(int64_t heads, int64_t nchunks, int leaf_chunks, int dk, int dv);
 hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, int leaf_chunks,
                            const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* S0, void* o, float* ST,
-                           void* workspace, hipStream_t stream);
+                           const float* beta, const float* beta_w, const float* S0, void* o,
+                           float* ST, void* workspace, hipStream_t stream);
 
 }  // namespace gds

@@ -1,7 +1,8 @@
 // chunk_bf16.hip -- fused bfloat16 MFMA chunk kernel (dk = dv = 128, C = 64).
 //
 // What it computes: the chunkwise form of the affine scan S_t = S_{t-1} E_t + f_t
-// (gated delta rule: E_t = alpha_t (I - beta_t k_t k_t^T), f_t = beta_t v_t k_t^T;
+// (gated delta rule: E_t = alpha_t (I - beta_t k_t k_t^T), f_t = bw_t v_t k_t^T
+// with the write strength bw_t = beta_t unless erase and write are split;
 // gated linear attention: E_t = alpha_t I, f_t = v_t k_t^T), o_t = S_t q_t.
 // The sequence is cut into chunks; each chunk is encoded independently of the
 // state, chunk states are carried in order and every chunk is read out from its
@@ -15,7 +16,7 @@
 //   T    = (I + A)^-1                                       UT solve    (fp32)
 //   W    = T diag(beta gamma) K                             WY factor   (MFMA)
 //   P    = (Q K^T) * Gamma * M_incl                         scores      (MFMA)
-//   U    = T diag(beta) V - W S^T                           (MFMA, needs S)
+//   U    = T diag(bw) V - W S^T                             (MFMA, needs S)
 //   O    = diag(gamma) Q S^T + P U                          (MFMA, needs S)
 //   S   <- gamma_C S + U^T diag(dec) K                      (MFMA, fp32 state)
 //
@@ -73,13 +74,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // Gates of one chunk: g = in-chunk cumulative ln alpha, gamma = e^g,
-// dec = e^(g_C - g), beta; gl = g log2(e) and gb = gl + log2(beta) feed the
-// masks as exp2(gl_t - gl_s) = Gamma_ts and exp2(gb_t - gl_s) = beta_t Gamma_ts.
+// dec = e^(g_C - g), beta (erase) and bw (write strength); gl = g log2(e) and
+// gb = gl + log2(beta) feed the masks as exp2(gl_t - gl_s) = Gamma_ts and
+// exp2(gb_t - gl_s) = beta_t Gamma_ts.
 struct Gates {
-    float g[C], gam[C], dec[C], bet[C], gl[C], gb[C];
+    float g[C], gam[C], dec[C], bet[C], bw[C], gl[C], gb[C];
 };
 
-// Shared memory of one workgroup (158 KB).  Chunk c's gates live in gate[c % 3],
+// Shared memory of one workgroup (159 KB).  Chunk c's gates live in gate[c % 3],
 // its q in Q[c % 2], its k^T in KT[c % 2]; the other arrays are single.
 struct Smem {
     uint16_t Q[2][C * LW];    // q [token][key]                        (rows perm5)
@@ -88,7 +90,7 @@ struct Smem {
     uint16_t KT[2][DK * LT];  // k^T [key][token]     (rows perm5, token granules swizzled)
     uint16_t VT[DVS * LT];    // v slice^T [value][token]              (token granules swizzled)
     uint16_t P[C * LT];       // scores [token][token]                 (rows perm5)
-    uint16_t Tb[C * LT];      // T diag(beta) [token][token]           (rows perm5)
+    uint16_t Tb[C * LT];      // T diag(bw) [token][token]             (rows perm5)
     uint16_t Tbg[C * LT];     // T diag(beta gamma)                    (rows perm5)
     float Tm[2][32 * LS];     // diagonal 32x32 blocks of A, then of T (fp32, natural)
     float Abl[32 * LS];       // A rows 32..63, columns 0..31 (fp32, natural)
@@ -365,9 +367,10 @@ __device__ __forceinline__ void a_tile(const Smem& sm, const Gates& G, int I, in
             f32x4{a[4 * b], a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]};
 }
 
-// Gates of chunk c from alpha, beta of token `lane` (0 past T; identity tokens
-// there: alpha = 1, beta = 0): an inclusive wave scan of ln alpha.
-__device__ __forceinline__ void stage_gates(Gates& G, int c, float pa, float pb, int T, int lane) {
+// Gates of chunk c from alpha, beta, bw of token `lane` (0 past T; identity
+// tokens there: alpha = 1, beta = bw = 0): an inclusive wave scan of ln alpha.
+__device__ __forceinline__ void stage_gates(Gates& G, int c, float pa, float pb, float pw, int T,
+                                            int lane) {
     const float x = wave_inclusive_sum(c * C + lane < T ? __logf(pa) : 0.f);
     const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
     const float xl = x * 1.4426950408889634f;  // log2(e)
@@ -375,6 +378,7 @@ __device__ __forceinline__ void stage_gates(Gates& G, int c, float pa, float pb,
     G.gam[lane] = __expf(x);
     G.dec[lane] = __expf(last - x);
     G.bet[lane] = pb;
+    G.bw[lane] = pw;
     G.gl[lane] = xl;
     G.gb[lane] = xl + __builtin_amdgcn_logf(pb);  // log2; -inf where beta = 0
 }
@@ -614,14 +618,18 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     // gi 0: alpha, beta of chunk m+1's token `lane` (0 past T); its gates
     const int T = job.T;
     const size_t a_base = (size_t)un.head * T;
-    float pa = 1.f, pb = 0.f;
+    float pa = 1.f, pb = 0.f, pw = 0.f;
+    const bool split = job.beta_w != job.beta;  // separate write strengths
     auto load_ab = [&](int c) {
         pa = ldtok(job.alpha + a_base, c, lane, T);
-        if (GDN) pb = ldtok(job.beta + a_base, c, lane, T);
+        if (GDN) {
+            pb = ldtok(job.beta + a_base, c, lane, T);
+            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
+        }
     };
     if (gi == 0 && un.nb < un.ne) {
         load_ab(un.nb);
-        stage_gates(sm.gate[un.nb % 3], un.nb, pa, pb, T, lane);
+        stage_gates(sm.gate[un.nb % 3], un.nb, pa, pb, split ? pw : pb, T, lane);
     }
 
     lds_barrier();  // prologue
@@ -646,7 +654,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
             }
         }
         lds_barrier();  // A
-        // ---- phase B: off-diagonal 32x32 block of T; bf16 Tb, Tbg ----
+        // ---- phase B: off-diagonal 32x32 block of T; bf16 Tb = T diag(bw), Tbg = T diag(beta gamma) ----
         if (GDN && act) {
             if (gi <= 1) {
                 // rows 32gi + tl of the diagonal block, 16 columns from c0
@@ -661,22 +669,25 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                     const f32x4 x1 = *reinterpret_cast<const f32x4*>(&X[tl * LS + c0 + 8 * hh + 4]);
                     const f32x4 be0 = *reinterpret_cast<const f32x4*>(&G.bet[s0]);
                     const f32x4 be1 = *reinterpret_cast<const f32x4*>(&G.bet[s0 + 4]);
+                    const f32x4 bw0 = *reinterpret_cast<const f32x4*>(&G.bw[s0]);
+                    const f32x4 bw1 = *reinterpret_cast<const f32x4*>(&G.bw[s0 + 4]);
                     const f32x4 ga0 = *reinterpret_cast<const f32x4*>(&G.gam[s0]);
                     const f32x4 ga1 = *reinterpret_cast<const f32x4*>(&G.gam[s0 + 4]);
-                    float tv[8], bv[8], gv[8];
+                    float tv[8], bv[8], wv[8], gv[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         tv[i] = x0[i]; tv[4 + i] = x1[i];
                         bv[i] = be0[i]; bv[4 + i] = be1[i];
+                        wv[i] = bw0[i]; wv[4 + i] = bw1[i];
                         gv[i] = ga0[i]; gv[4 + i] = ga1[i];
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int sa = c0 + 8 * hh + 2 * i;  // local column of element 2i
-                        const float e0 = sa <= tl ? tv[2 * i] * bv[2 * i] : 0.f;
-                        const float e1 = sa + 1 <= tl ? tv[2 * i + 1] * bv[2 * i + 1] : 0.f;
-                        b[i] = pack2(e0, e1);
-                        bg[i] = pack2(e0 * gv[2 * i], e1 * gv[2 * i + 1]);
+                        const float t0 = sa <= tl ? tv[2 * i] : 0.f;
+                        const float t1 = sa + 1 <= tl ? tv[2 * i + 1] : 0.f;
+                        b[i] = pack2(t0 * wv[2 * i], t1 * wv[2 * i + 1]);
+                        bg[i] = pack2(t0 * bv[2 * i] * gv[2 * i], t1 * bv[2 * i + 1] * gv[2 * i + 1]);
                     }
                     *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + s0]) = make_uint4(b[0], b[1], b[2], b[3]);
                     *reinterpret_cast<uint4*>(&sm.Tbg[prow * LT + s0]) = make_uint4(bg[0], bg[1], bg[2], bg[3]);
@@ -698,7 +709,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 const f32x4 t0 = sv.mul_acc(T1, y0, z);
                 const f32x4 t1 = sv.mul_acc(T1 + 16 * LS + 16, y1, sv.mul_acc(T1 + 16 * LS, y0, z));
                 const int s = 16 * J + sv.n16;
-                const float bs = G.bet[s], bgs = G.bet[s] * G.gam[s];
+                const float bs = G.bw[s], bgs = G.bet[s] * G.gam[s];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int p0 = 32 + perm5(4 * sv.g4 + r), p1 = 32 + perm5(16 + 4 * sv.g4 + r);
@@ -731,7 +742,8 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
             }
             if (OUT && gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
         }
-        if (gi == 0 && m + 1 < un.ne) stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, T, lane);
+        if (gi == 0 && m + 1 < un.ne)
+            stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, split ? pw : pb, T, lane);
         lds_barrier();  // C
     }
 }
@@ -883,7 +895,8 @@ hipError_t launch_chunk_job(int mode, int role, const ChunkJob& job, hipStream_t
 
 hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk, const void* q,
                              const void* k, const void* v, const float* alpha, const float* beta,
-                             const float* S0, void* o, float* ST, hipStream_t stream) {
+                             const float* beta_w, const float* S0, void* o, float* ST,
+                             hipStream_t stream) {
     (void)dk; (void)dv; (void)chunk;
     ChunkJob job{};
     job.q = static_cast<const uint16_t*>(q);
@@ -891,6 +904,7 @@ hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk,
     job.v = static_cast<const uint16_t*>(v);
     job.alpha = alpha;
     job.beta = beta;
+    job.beta_w = beta_w;
     job.o = static_cast<uint16_t*>(o);
     job.S_in = S0;
     job.S_out = ST;

@@ -8,14 +8,15 @@
 // log-decay, gamma = exp(g)) obeys, with S the state entering the chunk:
 //
 //   A  = strict_lower( diag(beta) (Gamma * K K^T) ),  Gamma_ij = exp(g_i - g_j)
-//   (I + A) [W | U~] = [diag(beta gamma) K | diag(beta) V]   (forward substitution)
+//   (I + A) [W | U~] = [diag(beta gamma) K | diag(beta_w) V]  (forward substitution)
 //   U  = U~ - W S^T
 //   O  = diag(gamma) Q S^T + (Q K^T * Gamma * M) U            (M: inclusive causal)
 //   S <- gamma_C S + U^T diag(exp(g_C - g)) K
 //
 // and for gated linear attention U = V (no A, no W).  These follow from
 // unrolling the token recurrence S_t = alpha_t S_{t-1} + u_t k_t^T with
-// u_t = beta_t (v_t - alpha_t S_{t-1} k_t) inside one chunk.  Decay ratios are
+// u_t = beta_w,t v_t - beta_t alpha_t S_{t-1} k_t inside one chunk (beta_w, the
+// write strength, equals beta except where erase and write are split).  Decay ratios are
 // always exp(g_i - g_j) with i >= j (never quotients of products), so they stay
 // in (0, 1].
 //
@@ -36,7 +37,8 @@ template <int MODE, int DK, int C, typename E>
 __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     int T, int dv, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
-    const float* __restrict__ S0, E* __restrict__ o, float* __restrict__ ST) {
+    const float* __restrict__ beta_w, const float* __restrict__ S0, E* __restrict__ o,
+    float* __restrict__ ST) {
     constexpr bool GDN = MODE == 0;
     __shared__ float Qs[C * DK];
     __shared__ float Ks[C * DK];
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     __shared__ float Us[C * kSlice];
     __shared__ float AP[C * C];
     __shared__ float Ss[kSlice * DK];
-    __shared__ float g[C], gam[C], bet[C], dec[C];
+    __shared__ float g[C], gam[C], bet[C], bw[C], dec[C];
 
     const int slices = dv / kSlice;
     const int bh = blockIdx.x / slices;
@@ -76,6 +78,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
             const bool in = c0 + tid < T;  // padded tokens: alpha = 1, beta = 0
             g[tid] = in ? logf(alpha[a_base + c0 + tid]) : 0.f;
             bet[tid] = (GDN && in) ? beta[a_base + c0 + tid] : 0.f;
+            bw[tid] = (GDN && in) ? beta_w[a_base + c0 + tid] : 0.f;
         }
         __syncthreads();
         if (tid == 0) {
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
             }
             for (int x = tid; x < C * kSlice; x += kThreads) {
                 const int t = x / kSlice;
-                Us[x] = bet[t] * Vs[x];
+                Us[x] = bw[t] * Vs[x];
             }
             __syncthreads();
             // forward substitution: row i of [W | U~] -= sum_{j<i} A_ij row j
@@ -173,36 +176,36 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
 
 template <int MODE, int DK, int C, typename E>
 hipError_t launch3(int BH, int T, int dv, const void* q, const void* k, const void* v,
-                   const float* alpha, const float* beta, const float* S0, void* o, float* ST,
+                   const float* alpha, const float* beta, const float* bw, const float* S0, void* o, float* ST,
                    hipStream_t stream) {
     const dim3 grid((unsigned)((size_t)BH * (dv / kSlice)));
     hipLaunchKernelGGL((chunk_f32_kernel<MODE, DK, C, E>), grid, dim3(kThreads), 0, stream, T, dv,
                        static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(v), alpha, beta, S0, static_cast<E*>(o), ST);
+                       static_cast<const E*>(v), alpha, beta, bw, S0, static_cast<E*>(o), ST);
     return hipGetLastError();
 }
 
 template <int MODE, int DK, typename E>
 hipError_t launch2(int chunk, int BH, int T, int dv, const void* q, const void* k, const void* v,
-                   const float* alpha, const float* beta, const float* S0, void* o, float* ST,
+                   const float* alpha, const float* beta, const float* bw, const float* S0, void* o, float* ST,
                    hipStream_t s) {
     switch (chunk) {
-        case 16: return launch3<MODE, DK, 16, E>(BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-        case 32: return launch3<MODE, DK, 32, E>(BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-        case 64: return launch3<MODE, DK, 64, E>(BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
+        case 16: return launch3<MODE, DK, 16, E>(BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+        case 32: return launch3<MODE, DK, 32, E>(BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+        case 64: return launch3<MODE, DK, 64, E>(BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int MODE, typename E>
 hipError_t launch1(int dk, int chunk, int BH, int T, int dv, const void* q, const void* k,
-                   const void* v, const float* alpha, const float* beta, const float* S0,
+                   const void* v, const float* alpha, const float* beta, const float* bw, const float* S0,
                    void* o, float* ST, hipStream_t s) {
     switch (dk) {
-        case 16: return launch2<MODE, 16, E>(chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-        case 32: return launch2<MODE, 32, E>(chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-        case 64: return launch2<MODE, 64, E>(chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-        case 128: return launch2<MODE, 128, E>(chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
+        case 16: return launch2<MODE, 16, E>(chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+        case 32: return launch2<MODE, 32, E>(chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+        case 64: return launch2<MODE, 64, E>(chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+        case 128: return launch2<MODE, 128, E>(chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -218,14 +221,14 @@ bool chunk_f32_supported(int mode, int dk, int dv, int chunk) {
 
 hipError_t launch_chunk_f32(int mode, int dtype, int BH, int T, int dk, int dv, int chunk,
                             const void* q, const void* k, const void* v, const float* alpha,
-                            const float* beta, const float* S0, void* o, float* ST,
+                            const float* beta, const float* bw, const float* S0, void* o, float* ST,
                             hipStream_t s) {
     if (dtype == 0) {
-        if (mode == 0) return launch1<0, float>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-        return launch1<1, float>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
+        if (mode == 0) return launch1<0, float>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+        return launch1<1, float>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
     }
-    if (mode == 0) return launch1<0, uint16_t>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
-    return launch1<1, uint16_t>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, S0, o, ST, s);
+    if (mode == 0) return launch1<0, uint16_t>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
+    return launch1<1, uint16_t>(dk, chunk, BH, T, dv, q, k, v, alpha, beta, bw, S0, o, ST, s);
 }
 
 }  // namespace gds

@@ -6,7 +6,8 @@
 // state S (dv x dk, fp32, in place) and token (q, k, v, alpha, beta):
 //
 //   a = S k,  b = S q                         (row dot products of the old S)
-//   gdn: u = beta (v - alpha a)      gla: u = v
+//   gdn: u = beta_w v - beta alpha a      gla: u = v
+//   (beta_w, the write strength, is beta unless erase and write are split)
 //   S  <- alpha S + u k^T                     (= S E + f for this token)
 //   o   = S_new q = alpha b + (k . q) u
 //
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
                                                           const E* __restrict__ v,
                                                           const float* __restrict__ alpha,
                                                           const float* __restrict__ beta,
+                                                          const float* __restrict__ beta_w,
                                                           float* __restrict__ S,
                                                           E* __restrict__ o) {
     constexpr int L = DK / 4;                       // lanes per row
@@ -64,6 +66,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
     const float4 q4 = io<E>::load4(q, (size_t)n * DK + sub * 4);
     const float al = alpha[n];
     const float be = MODE == 0 ? beta[n] : 0.f;
+    const float bw = MODE == 0 ? beta_w[n] : 0.f;
     float vr[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
         float b = s[p].x * q4.x + s[p].y * q4.y + s[p].z * q4.z + s[p].w * q4.w;
         a = group_sum<L>(a);
         b = group_sum<L>(b);
-        const float u = MODE == 0 ? be * (vr[p] - al * a) : vr[p];
+        const float u = MODE == 0 ? bw * vr[p] - be * (al * a) : vr[p];
         f32x4 r;
         r.x = al * s[p].x + u * k4.x;
         r.y = al * s[p].y + u * k4.y;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
 
 template <int DK, typename E>
 hipError_t launch_typed(int mode, int N, int dv, const void* q, const void* k, const void* v,
-                        const float* alpha, const float* beta, float* S, void* o,
+                        const float* alpha, const float* beta, const float* beta_w, float* S, void* o,
                         hipStream_t stream) {
     const int rb = (dv + kRowsPerBlock - 1) / kRowsPerBlock;
     const dim3 grid((unsigned)((size_t)N * rb));
@@ -101,22 +104,22 @@ hipError_t launch_typed(int mode, int N, int dv, const void* q, const void* k, c
     E* oo = static_cast<E*>(o);
     if (mode == 0)
         hipLaunchKernelGGL((decode_kernel<DK, 0, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
-                           kk, vv, alpha, beta, S, oo);
+                           kk, vv, alpha, beta, beta_w, S, oo);
     else
         hipLaunchKernelGGL((decode_kernel<DK, 1, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
-                           kk, vv, alpha, beta, S, oo);
+                           kk, vv, alpha, beta, beta_w, S, oo);
     return hipGetLastError();
 }
 
 template <typename E>
 hipError_t launch_dk(int mode, int N, int dk, int dv, const void* q, const void* k,
-                     const void* v, const float* alpha, const float* beta, float* S, void* o,
+                     const void* v, const float* alpha, const float* beta, const float* beta_w, float* S, void* o,
                      hipStream_t stream) {
     switch (dk) {
-        case 16: return launch_typed<16, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
-        case 32: return launch_typed<32, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
-        case 64: return launch_typed<64, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
-        case 128: return launch_typed<128, E>(mode, N, dv, q, k, v, alpha, beta, S, o, stream);
+        case 16: return launch_typed<16, E>(mode, N, dv, q, k, v, alpha, beta, beta_w, S, o, stream);
+        case 32: return launch_typed<32, E>(mode, N, dv, q, k, v, alpha, beta, beta_w, S, o, stream);
+        case 64: return launch_typed<64, E>(mode, N, dv, q, k, v, alpha, beta, beta_w, S, o, stream);
+        case 128: return launch_typed<128, E>(mode, N, dv, q, k, v, alpha, beta, beta_w, S, o, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -127,10 +130,10 @@ bool decode_supported(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk ==
 
 hipError_t launch_decode(int mode, int dtype, int N, int dk, int dv, const void* q,
                          const void* k, const void* v, const float* alpha, const float* beta,
-                         float* S, void* o, hipStream_t stream) {
+                         const float* beta_w, float* S, void* o, hipStream_t stream) {
     if (dtype == 0)
-        return launch_dk<float>(mode, N, dk, dv, q, k, v, alpha, beta, S, o, stream);
-    return launch_dk<uint16_t>(mode, N, dk, dv, q, k, v, alpha, beta, S, o, stream);
+        return launch_dk<float>(mode, N, dk, dv, q, k, v, alpha, beta, beta_w, S, o, stream);
+    return launch_dk<uint16_t>(mode, N, dk, dv, q, k, v, alpha, beta, beta_w, S, o, stream);
 }
 
 }  // namespace gds

@@ -13,16 +13,18 @@ namespace gds {
 
 // decode.hip -------------------------------------------------------------
 bool decode_supported(int dk);
+// beta_w: write strengths (the gated delta rule's f_t = beta_w v k^T); equal to
+// beta except for split erase/write strengths.  Ignored in mode 1.
 hipError_t launch_decode(int mode, int dtype, int N, int dk, int dv, const void* q,
                          const void* k, const void* v, const float* alpha, const float* beta,
-                         float* S, void* o, hipStream_t stream);
+                         const float* beta_w, float* S, void* o, hipStream_t stream);
 
 // chunk_f32.hip -- plain float32 chunkwise kernel (any supported size) -------
 bool chunk_f32_supported(int mode, int dk, int dv, int chunk);
 hipError_t launch_chunk_f32(int mode, int dtype, int BH, int T, int dk, int dv, int chunk,
                             const void* q, const void* k, const void* v, const float* alpha,
-                            const float* beta, const float* S0, void* o, float* ST,
-                            hipStream_t stream);
+                            const float* beta, const float* beta_w, const float* S0, void* o,
+                            float* ST, hipStream_t stream);
 
 // chunk_bf16.hip -- bfloat16 MFMA chunkwise kernel ---------------------------
 // (dk = dv = 128, chunk 64; q, k, v, o bfloat16; states float32)
@@ -33,7 +35,8 @@ struct ChunkJob {
     const uint16_t* k;
     const uint16_t* v;
     const float* alpha;
-    const float* beta;
+    const float* beta;   // erase strengths (E_t)
+    const float* beta_w; // write strengths (f_t); == beta unless split
     uint16_t* o;         // outputs, or null (not written)
     const float* S_in;   // role-dependent, see chunk_bf16.hip
     float* S_out;        // role-dependent, see chunk_bf16.hip
@@ -47,7 +50,20 @@ bool chunk_mfma_supported(int mode, int dk, int dv, int chunk);
 hipError_t launch_chunk_job(int mode, int role, const ChunkJob& job, hipStream_t stream);
 hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk,
                              const void* q, const void* k, const void* v, const float* alpha,
-                             const float* beta, const float* S0, void* o, float* ST,
-                             hipStream_t stream);
+                             const float* beta, const float* beta_w, const float* S0, void* o,
+                             float* ST, hipStream_t stream);
+
+// prism.hip -- PRISM write factors expanded into a split-strength scan stream ---
+struct PrismJob {
+    const void *q, *k, *v, *x;           // [BH, T, dk] / [BH, T, dv], element type of dtype
+    const float *alpha, *beta, *beta_l;  // [BH, T], [BH, T], [BH, T, L]
+    const float* conv;                   // [H, W, dv]
+    const void *Wk, *Wp;                 // [H, L, dk, dv], [H, L, dv, dv]
+    void *q2, *k2, *v2;                  // [BH, T (L+1), d]
+    float *alpha2, *beta2;               // [BH, T (L+1)], [2, BH, T (L+1)]
+    int BH, H, T, dk, dv, L, W;
+};
+bool prism_supported(int dtype, int dk, int dv);
+hipError_t launch_prism_expand(int dtype, const PrismJob& job, hipStream_t stream);
 
 }  // namespace gds

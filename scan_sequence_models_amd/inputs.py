@@ -16,6 +16,14 @@ Recipe (one independent stream per head):
 Decode workloads draw each state ``n`` from ``SeedSequence([seed, n])``: the
 initial state first, then all steps' q, k, v, alpha and beta (see
 ``decode_state_inputs``).
+
+PRISM workloads (``prism_steps`` L > 0) add, per head (b, h), from
+``SeedSequence([seed, b, h, 1])``: the anchor source x ~ N(0, 1) (T x dv) and
+the step gates beta^(l) = sigmoid(N(0, 1)) (T x L); and per head index h,
+shared over the batch, from ``SeedSequence([seed, 2**31, h])``: conv taps
+~ N(0, 1/W) (W x dv, float32), W_k^(l) ~ N(0, 1/dv) (L x dk x dv) and
+W_p^(l) ~ N(0, 1/dv) (L x dv x dv), cast like the data.  Split erase/write
+strength tests draw a write plane ~ U(0, 1.5) from ``SeedSequence([seed, b, h, 2])``.
 """
 from __future__ import annotations
 
@@ -109,6 +117,8 @@ class Workload:
     seed: int
     path: str = "sequential"   # "sequential" or "blelloch"
     steps: int = 0       # decode workloads only: number of consecutive tokens
+    prism_steps: int = 0   # PRISM workloads: L rank-1 corrections per token
+    prism_window: int = 4  # PRISM workloads: taps W of the anchor convolution
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -131,6 +141,13 @@ WORKLOADS = {
     "long-b2h8t262144": Workload("long-b2h8t262144", "gdn", 2, 8, 262144, 128, 128, "bf16", 64,
                                  ("uniform", 0.97, 1.0), ("sigmoid_normal", 0.0, 1.0), 0.01,
                                  seed=5, path="blelloch"),
+    # PRISM: the training-shape gated delta rule with L = 2 corrections per token
+    "prism-b8h16t8192-l2": Workload("prism-b8h16t8192-l2", "gdn", 8, 16, 8192, 128, 128, "bf16",
+                                    64, ("sigmoid_normal", 3.0, 1.0), ("sigmoid_normal", 0.0, 1.0),
+                                    0.01, seed=6, prism_steps=2, prism_window=4),
+    "tiny-prism": Workload("tiny-prism", "gdn", 1, 2, 64, 16, 16, "f32", 16,
+                           ("uniform", 0.9, 1.0), ("uniform", 0.0, 1.0), None, seed=7,
+                           prism_steps=2, prism_window=4),
 }
 
 
@@ -245,3 +262,42 @@ def decode_inputs(w: Workload, N: int | None = None, steps: int | None = None,
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(fill, range(N)))
     return S0, q, k, v, alpha, beta
+
+
+# ---------------------------------------------------------------------------
+# split erase / write strengths and PRISM write inputs
+# ---------------------------------------------------------------------------
+
+
+def write_strengths(w: Workload, b: int, h: int, T: int | None = None) -> np.ndarray:
+    """A write-strength plane for head (b, h): U(0, 1.5), float32."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 2]))
+    return cast(rng.uniform(0.0, 1.5, T), "f32")
+
+
+@dataclasses.dataclass
+class PrismWeights:
+    conv: np.ndarray  # [W, dv] float32
+    Wk: np.ndarray    # [L, dk, dv] float32 (values of the data type)
+    Wp: np.ndarray    # [L, dv, dv]
+
+
+def prism_weights(w: Workload, h: int) -> PrismWeights:
+    """Anchor taps and projections of head index h (shared by every batch row)."""
+    L, W = w.prism_steps, w.prism_window
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 2**31, h]))
+    conv = cast(rng.normal(0.0, np.sqrt(1.0 / W), size=(W, w.dv)), "f32")
+    Wk = cast(rng.normal(0.0, np.sqrt(1.0 / w.dv), size=(L, w.dk, w.dv)), w.dtype)
+    Wp = cast(rng.normal(0.0, np.sqrt(1.0 / w.dv), size=(L, w.dv, w.dv)), w.dtype)
+    return PrismWeights(conv, Wk, Wp)
+
+
+def prism_token_inputs(w: Workload, b: int, h: int, T: int | None = None):
+    """Anchor source x [T, dv] (data type) and step gates beta^(l) [T, L] of head (b, h)."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 1]))
+    x = cast(rng.standard_normal((T, w.dv)), w.dtype)
+    z = rng.normal(0.0, 1.0, size=(T, w.prism_steps))
+    beta_l = cast(1.0 / (1.0 + np.exp(-z)), "f32")
+    return x, beta_l

@@ -20,7 +20,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = L.header_functions()
-    assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "decode_step",
+    assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "decode_step", "prism_expand",
                           "scan_last_error", "scan_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -60,6 +60,11 @@ def _scan(lib, mode=0, dtype=1, B=1, H=2, T=64, dk=128, dv=128, chunk=64, q=FAKE
     (dict(S0=FAKE + 5 * STEP, ST=FAKE + 5 * STEP + 256), L.SCAN_EINVAL),  # partial alias
     (dict(opts=_opts(path=9)), L.SCAN_EINVAL),
     (dict(opts=_opts(path=1, leaf=3)), L.SCAN_EINVAL),
+    (dict(mode=2, beta=None), L.SCAN_EINVAL),         # split strengths need beta
+    # split strengths: beta holds two planes (2 x B*H*T floats = 1 KB here), so
+    # an output starting 768 bytes after beta overlaps its write plane (with
+    # one plane counted it would not)
+    (dict(mode=2, o=FAKE + 4 * STEP + 768), L.SCAN_EINVAL),
 ])
 def test_scan_fwd_rejects(lib, kw, code):
     assert _scan(lib, **kw) == code
@@ -83,7 +88,9 @@ def _decode(lib, mode=0, dtype=1, N=4, dk=128, dv=128, q=FAKE, k=FAKE + STEP, v=
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(mode=2), L.SCAN_EINVAL),
+    (dict(mode=3), L.SCAN_EINVAL),
+    (dict(mode=2, beta=None), L.SCAN_EINVAL),
+    (dict(mode=2, o=FAKE + 4 * STEP + 16), L.SCAN_EINVAL),  # o inside beta's write plane
     (dict(N=0), L.SCAN_EINVAL),
     (dict(dk=96), L.SCAN_EUNSUPPORTED),
     (dict(S=None), L.SCAN_EINVAL),
@@ -95,3 +102,39 @@ def _decode(lib, mode=0, dtype=1, N=4, dk=128, dv=128, q=FAKE, k=FAKE + STEP, v=
 ])
 def test_decode_step_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def _prism(lib, dtype=1, B=1, H=2, T=64, dk=128, dv=128, Lsteps=2, W=4, q=FAKE, k=FAKE + STEP,
+           v=FAKE + 2 * STEP, x=FAKE + 3 * STEP, alpha=FAKE + 4 * STEP, beta=FAKE + 5 * STEP,
+           beta_l=FAKE + 6 * STEP, conv=FAKE + 7 * STEP, Wk=FAKE + 8 * STEP, Wp=FAKE + 9 * STEP,
+           q2=FAKE + 10 * STEP, k2=FAKE + 11 * STEP, v2=FAKE + 12 * STEP, a2=FAKE + 13 * STEP,
+           b2=FAKE + 14 * STEP):
+    # a valid argument set would launch with fake pointers: only invalid ones are passed
+    return lib.prism_expand(dtype, B, H, T, dk, dv, Lsteps, W, q, k, v, x, alpha, beta, beta_l,
+                            conv, Wk, Wp, q2, k2, v2, a2, b2, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), L.SCAN_EINVAL),
+    (dict(T=0), L.SCAN_EINVAL),
+    (dict(Lsteps=-1), L.SCAN_EINVAL),
+    (dict(Lsteps=9), L.SCAN_EINVAL),
+    (dict(W=0), L.SCAN_EINVAL),
+    (dict(W=9), L.SCAN_EINVAL),
+    (dict(dk=96), L.SCAN_EUNSUPPORTED),
+    (dict(dv=48), L.SCAN_EUNSUPPORTED),
+    (dict(q=None), L.SCAN_EINVAL),
+    (dict(beta=None), L.SCAN_EINVAL),
+    (dict(b2=None), L.SCAN_EINVAL),
+    (dict(Wk=None), L.SCAN_EINVAL),                   # L > 0 needs the weights
+    (dict(x=None), L.SCAN_EINVAL),
+    (dict(conv=FAKE + 7 * STEP + 8), L.SCAN_EALIGN),
+    (dict(Wp=FAKE + 9 * STEP + 2), L.SCAN_EALIGN),
+    (dict(beta_l=FAKE + 6 * STEP + 2), L.SCAN_EALIGN),
+    (dict(q2=FAKE + 512), L.SCAN_EINVAL),             # q2 overlaps q
+    (dict(v2=FAKE + 11 * STEP + 4096), L.SCAN_EINVAL),  # v2 overlaps k2
+    (dict(b2=FAKE + 5 * STEP + 256), L.SCAN_EINVAL),  # beta2 overlaps beta
+])
+def test_prism_expand_rejects(lib, kw, code):
+    assert _prism(lib, **kw) == code
+    assert len(L.last_error()) > 0
