@@ -10,8 +10,9 @@ Prints one JSON line with tokens/s, the roofline of the dominant kernel and the
 float64 CPU oracle timed on a bounded sample of the same workload.
 
 Other workloads: --workload gla-b4h8t4096 (gated linear attention),
-long-b2h8t262144 (the long-sequence path) and decode-4096x100 (decode_step over
-4096 states, one timed step per token).  Timing: W untimed steps (by default
+long-b2h8t262144 (the long-sequence path), decode-4096x100 (decode_step over
+4096 states, one timed step per token) and prism-b8h16t8192-l2 (the PRISM layer:
+prism_expand, then the split-strength scan of the 3x longer element stream).  Timing: W untimed steps (by default
 enough to cover the GPU's clock ramp), then two HIP events around K back-to-back
 steps on the launch stream.
 """
@@ -44,7 +45,7 @@ def scan_bytes(w) -> int:
     es = 2 if w.dtype == "bf16" else 4
     ht = w.B * w.H * w.T
     b = ht * (2 * w.dk + 2 * w.dv) * es
-    b += ht * 4 * (2 if w.mode == "gdn" else 1)
+    b += ht * 4 * {"gdn": 2, "gla": 1, "gdn_ew": 3}[w.mode]  # alpha and strength planes
     b += w.B * w.H * w.dv * w.dk * 4 * (2 if w.s0_var is not None else 1)
     return b
 
@@ -276,6 +277,178 @@ def bench_decode(args, w):
     print(json.dumps(result), flush=True)
 
 
+def prism_expand_bytes(w) -> int:
+    """Algorithmic HBM bytes of one prism_expand call: q, k, v, x read once and
+    the G = L+1 element stream (q2, k2, v2 in the data type; alpha2 and the two
+    strength planes in fp32) written once; alpha, beta, beta^(l) read once; the
+    per-head weights (L (dk + dv) dv elements, conv W dv fp32) read once."""
+    es = 2 if w.dtype == "bf16" else 4
+    L, G = w.prism_steps, w.prism_steps + 1
+    ht = w.B * w.H * w.T
+    b = ht * (2 * w.dk + 2 * w.dv) * es + ht * 4 * (2 + L)
+    b += ht * G * ((2 * w.dk + w.dv) * es + 3 * 4)
+    b += w.H * (L * (w.dk + w.dv) * w.dv * es + w.prism_window * w.dv * 4)
+    return b
+
+
+def cpu_baseline_prism(w, heads: int):
+    """The float64 PRISM oracle (write factors, expansion, token recurrence) on
+    the first ``heads`` heads of ``w``, full length each."""
+    import numpy as np
+
+    import oracle
+    from oracle import prism as oprism
+    from scan_sequence_models_amd import inputs as I
+
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
+    hs = [I.head_inputs(w, b, h) for b, h in sel]
+    tok = [I.prism_token_inputs(w, b, h) for b, h in sel]
+    wts = [I.prism_weights(w, h) for _, h in sel]
+    rnd = (lambda z: I.cast(z, "bf16").astype(np.float64)) if w.dtype == "bf16" else None
+    oracle.build(force=False)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    for x, (xs, bl), p in zip(hs, tok, wts):
+        oprism.prism_scan(x.q, x.k, x.v, x.alpha, x.beta, xs, p.conv, p.Wk, p.Wp, bl,
+                          None if x.S0 is None else x.S0.astype(np.float64), factor_round=rnd,
+                          threads=threads)
+    sec = time.perf_counter() - t0
+    head_tokens = len(sel) * w.T
+    return {
+        "value": head_tokens / w.H / sec,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(sel)} of {w.B * w.H} heads x {w.T} tokens ({head_tokens} head-tokens), "
+                  f"float64 write factors + token recurrence over {w.prism_steps + 1} elements "
+                  f"per token, {sec:.2f} s",
+        "seconds": sec,
+    }
+
+
+def bench_prism(args, w):
+    """The PRISM layer: prism_expand then scan_fwd over the expanded stream."""
+    import numpy as np
+    import torch
+
+    import scan_sequence_models_amd as gds
+    from scan_sequence_models_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, T, L = w.B, w.H, w.T, w.prism_steps
+    G = L + 1
+    log(f"bench: generating {w.name} (B={B} H={H} T={T} d={w.dk} L={L})")
+    b = I.batch_inputs(w, threads=16)
+    bf = w.dtype == "bf16"
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    q, k, v = up(b.q, bf), up(b.k, bf), up(b.v, bf)
+    alpha, beta, S0 = up(b.alpha), up(b.beta), up(b.S0)
+    del b
+    xs = np.empty((B, H, T, w.dv), np.float32)
+    bl = np.empty((B, H, T, L), np.float32)
+    for bb in range(B):
+        for hh in range(H):
+            xs[bb, hh], bl[bb, hh] = I.prism_token_inputs(w, bb, hh)
+    x, beta_l = up(xs, bf), up(bl)
+    del xs, bl
+    wts = [I.prism_weights(w, hh) for hh in range(H)]
+    conv = up(np.stack([p.conv for p in wts]))
+    Wk = up(np.stack([p.Wk for p in wts]), bf)
+    Wp = up(np.stack([p.Wp for p in wts]), bf)
+    T2 = T * G
+    dt = q.dtype
+    stream_bufs = (torch.empty((B, H, T2, w.dk), dtype=dt, device=dev),
+                   torch.empty((B, H, T2, w.dk), dtype=dt, device=dev),
+                   torch.empty((B, H, T2, w.dv), dtype=dt, device=dev),
+                   torch.empty((B, H, T2), dtype=torch.float32, device=dev),
+                   torch.empty((2, B, H, T2), dtype=torch.float32, device=dev))
+    o2 = torch.empty((B, H, T2, w.dv), dtype=dt, device=dev)
+    ST = torch.empty((B, H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    q2, k2, v2, a2, b2 = stream_bufs
+
+    def expand():
+        gds.prism_expand(q, k, v, alpha, beta, x, beta_l, conv, Wk, Wp, out=stream_bufs)
+
+    def scan():
+        gds.scan_fwd(q2, k2, v2, a2, b2, S0, chunk=w.chunk, o=o2, ST=ST)
+
+    def step():
+        expand()
+        scan()
+
+    copy_probe(args.copy_probe_mib, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    span_ms, wall = timed(lambda i: step(), args.steps, dev)
+    ms_per_step = span_ms / args.steps
+    # each kernel alone, back to back, for the per-kernel rooflines
+    exp_ms = timed(lambda i: expand(), args.steps, dev)[0] / args.steps
+    scan_ms = timed(lambda i: scan(), args.steps, dev)[0] / args.steps
+    log(f"bench: {args.steps} layer steps, {ms_per_step:.4f} ms per step "
+        f"(prism_expand {exp_ms:.4f} ms, scan {scan_ms:.4f} ms alone), wall {wall * 1e3:.1f} ms")
+    ws = w.replace(T=T2, mode="gdn_ew")
+    scan_alg = scan_bytes(ws)
+    scan_flops_alg_ = scan_flops_alg(w.replace(T=T2))
+    exp_alg = prism_expand_bytes(w)
+    src_scan = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_bf16.hip")
+    src_exp = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "prism.hip")
+    result = {
+        "metric": "tokens/s PRISM layer fwd (rank-L write, L=2; H=16, d=128, T=8192); "
+                  "% MFMA / HBM roofline",
+        "value": B * T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": "gdn_ew (PRISM)", "B": B, "H": H, "T": T,
+                   "elements_per_token": G, "L": L, "W": w.prism_window, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "io_dtype": w.dtype, "state_dtype": "f32"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": scan_alg / (scan_ms / 1e3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": scan_alg / (scan_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic(src_scan, f"chunk_mfma_{w.name}_traffic.txt"),
+            "kernel": "chunk_mfma_kernel (expanded stream)",
+            "algorithmic_bytes_per_launch": scan_alg,
+            "kernel_ms": scan_ms,
+            "alg_tflops": scan_flops_alg_ / (scan_ms / 1e3) / 1e12,
+            "alg_mfma_frac": scan_flops_alg_ / (scan_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
+        },
+        "expand_roofline": {
+            "bound": "hbm",
+            "achieved": exp_alg / (exp_ms / 1e3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": exp_alg / (exp_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic(src_exp, f"prism_expand_{w.name}_traffic.txt"),
+            "kernel": "prism_mfma_kernel",
+            "algorithmic_bytes_per_launch": exp_alg,
+            "kernel_ms": exp_ms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        heads = min(args.cpu_heads, 16)
+        log(f"bench: timing the CPU PRISM oracle on {heads} heads")
+        result["cpu_baseline"] = cpu_baseline_prism(w, heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +493,8 @@ def main():
         args.steps = 50
     if args.warmup is None:
         args.warmup = 30
+    if w.prism_steps:
+        return bench_prism(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

@@ -199,7 +199,8 @@ def decode_step(q, k, v, alpha, beta, S, o=None):
     return o
 
 
-def prism_expand(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, Wp=None):
+def prism_expand(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, Wp=None, *,
+                 out=None):
     """PRISM write factors expanded into a split-strength scan stream.
 
     q, k [B, H, T, dk] and v, x [B, H, T, dv] (float32 or bfloat16); alpha, beta
@@ -207,6 +208,7 @@ def prism_expand(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, 
     [H, L, dk, dv] and Wp [H, L, dv, dv] in the data type.  ``beta_l=None``
     means L = 0.  Returns (q2, k2, v2, alpha2, beta2) with T (L+1) elements per
     head; beta2 is [2, B, H, T (L+1)] (erase, write), ready for ``scan_fwd``.
+    ``out`` may pass those five tensors preallocated.
     """
     _need(q, "q")
     dev, dt = q.device, q.dtype
@@ -230,11 +232,18 @@ def prism_expand(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, 
         _need(Wk, "Wk", dt, (H, L, dk, dv), dev)
         _need(Wp, "Wp", dt, (H, L, dv, dv), dev)
     T2 = T * (L + 1)
-    q2 = torch.empty((B, H, T2, dk), dtype=dt, device=dev)
-    k2 = torch.empty((B, H, T2, dk), dtype=dt, device=dev)
-    v2 = torch.empty((B, H, T2, dv), dtype=dt, device=dev)
-    a2 = torch.empty((B, H, T2), dtype=torch.float32, device=dev)
-    b2 = torch.empty((2, B, H, T2), dtype=torch.float32, device=dev)
+    if out is None:
+        out = (torch.empty((B, H, T2, dk), dtype=dt, device=dev),
+               torch.empty((B, H, T2, dk), dtype=dt, device=dev),
+               torch.empty((B, H, T2, dv), dtype=dt, device=dev),
+               torch.empty((B, H, T2), dtype=torch.float32, device=dev),
+               torch.empty((2, B, H, T2), dtype=torch.float32, device=dev))
+    q2, k2, v2, a2, b2 = out
+    _need(q2, "q2", dt, (B, H, T2, dk), dev)
+    _need(k2, "k2", dt, (B, H, T2, dk), dev)
+    _need(v2, "v2", dt, (B, H, T2, dv), dev)
+    _need(a2, "alpha2", torch.float32, (B, H, T2), dev)
+    _need(b2, "beta2", torch.float32, (2, B, H, T2), dev)
     with torch.cuda.device(dev):
         st = lib().prism_expand(_dtype_code(q), B, H, T, dk, dv, L, W, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(x) if L else None, _ptr(alpha), _ptr(beta),

@@ -26,9 +26,13 @@
 //     bfloat16 parts, ~16 significant bits); each projection is two
 //     v_mfma_f32_32x32x16_bf16 passes (u_hi W + u_lo W) with float32
 //     accumulation, so the factors carry float32-level accuracy until they are
-//     rounded to bfloat16 on output.  Wave w owns output channels
-//     [32w, 32w + 32) for all 64 tokens; its weight rows are read straight into
-//     B-operand registers (the weights stay in L2 across workgroups).
+//     rounded to bfloat16 on output.  Four waves: wave w computes channels
+//     32w .. 32w+31 of both 32-token tiles (measured faster than eight waves
+//     of one tile each, which load every weight row twice); its weight rows are
+//     read straight into B-operand registers (the weights stay in L2 across
+//     workgroups), the next matrix's while the current one is in use.  Output
+//     tiles are staged in LDS and stored as whole 256-byte rows.  The
+//     pass-through part of the stream is a separate streaming kernel.
 //   * prism_plain_kernel (float32 or bfloat16, any supported size): the same
 //     arithmetic with float32 FMAs, 16 tokens per workgroup.
 #include "common.hpp"
@@ -48,7 +52,7 @@ __device__ __forceinline__ float gelu(float x) {
 // 16-byte vector copies of the pass-through part of the stream (rows tG of k and
 // v, every row of q, the gates) for tokens [t0, t0 + n) of head bh.
 template <typename E>
-__device__ void copy_stream(const PrismJob& j, int bh, int t0, int n) {
+__device__ __forceinline__ void copy_stream(const PrismJob& j, int bh, int t0, int n) {
     constexpr int V = 16 / sizeof(E);  // elements per 16-byte vector
     const int G = j.L + 1;
     const int tid = threadIdx.x;
@@ -95,6 +99,17 @@ __device__ void copy_stream(const PrismJob& j, int bh, int t0, int n) {
     }
 }
 
+// The pass-through part as a streaming kernel of its own (no arithmetic, few
+// registers: many workgroups per CU keep HBM busy), 64 tokens per workgroup.
+constexpr int kCopyTokens = 64;
+template <typename E>
+__global__ __launch_bounds__(kThreads) void prism_copy_kernel(const PrismJob j) {
+    const int tiles = (j.T + kCopyTokens - 1) / kCopyTokens;
+    const int bh = blockIdx.x / tiles;
+    const int t0 = (blockIdx.x - bh * tiles) * kCopyTokens;
+    copy_stream<E>(j, bh, t0, min(kCopyTokens, j.T - t0));
+}
+
 // ---------------------------------------------------------------------------
 // plain kernel: float32 arithmetic, 16 tokens per workgroup
 // ---------------------------------------------------------------------------
@@ -119,10 +134,6 @@ __global__ __launch_bounds__(kThreads) void prism_plain_kernel(const PrismJob j)
     const E* Wp = static_cast<const E*>(j.Wp);
     E* k2 = static_cast<E*>(j.k2);
     E* v2 = static_cast<E*>(j.v2);
-    if (j.L == 0) {  // no corrections: the stream is the gated-delta tokens themselves
-        copy_stream<E>(j, bh, t0, n);
-        return;
-    }
     const float* conv = j.conv + (size_t)head * j.W * j.dv;
 
     // anchor u and first residual r = v - u
@@ -155,7 +166,6 @@ __global__ __launch_bounds__(kThreads) void prism_plain_kernel(const PrismJob j)
             io<E>::store(v2, ((size_t)bh * T2 + (size_t)(t0 + t) * G + l + 1) * j.dv + i, d);
         }
     }
-    copy_stream<E>(j, bh, t0, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -163,17 +173,20 @@ __global__ __launch_bounds__(kThreads) void prism_plain_kernel(const PrismJob j)
 // ---------------------------------------------------------------------------
 constexpr int kTok = 64;
 constexpr int kD = 128;
+constexpr int kMfmaThreads = 256;  // 4 waves: wave w computes channels 32w .. 32w+31
 constexpr int kLdu = kD + 8;  // padded row stride of the anchor tiles (bf16 elements)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// (at most 256 VGPRs, two workgroups per CU: the projections hold their B
-// operands, the residual and an accumulator tile in registers)
-__global__ __launch_bounds__(kThreads, 2) void prism_mfma_kernel(const PrismJob j) {
+// Writes the computed rows only (elements tG + l, l >= 1); the pass-through part
+// comes from prism_copy_kernel.
+// (at most 256 VGPRs; 152 in use: three workgroups per CU)
+__global__ __launch_bounds__(kMfmaThreads, 2) void prism_mfma_kernel(const PrismJob j) {
     __shared__ uint16_t Uh[kTok * kLdu];  // u rounded to bfloat16      [token][channel]
     __shared__ uint16_t Ul[kTok * kLdu];  // u - u_hi rounded to bfloat16
+    __shared__ uint16_t Ob[kTok * kLdu];  // v, then each output tile    [token][channel]
     const int tiles = (j.T + kTok - 1) / kTok;
     const int bh = blockIdx.x / tiles;
     const int t0 = (blockIdx.x - bh * tiles) * kTok;
@@ -187,13 +200,35 @@ __global__ __launch_bounds__(kThreads, 2) void prism_mfma_kernel(const PrismJob 
     const uint16_t* v = static_cast<const uint16_t*>(j.v);
     uint16_t* k2 = static_cast<uint16_t*>(j.k2);
     uint16_t* v2 = static_cast<uint16_t*>(j.v2);
-    if (j.L == 0) {  // no corrections: the stream is the gated-delta tokens themselves
-        copy_stream<uint16_t>(j, bh, t0, n);
-        return;
-    }
     const float* conv = j.conv + (size_t)head * j.W * kD;
+    const uint16_t* Wk = static_cast<const uint16_t*>(j.Wk) + (size_t)head * j.L * kD * kD;
+    const uint16_t* Wp = static_cast<const uint16_t*>(j.Wp) + (size_t)head * j.L * kD * kD;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int nc = 32 * w + l32;
 
-    // ---- anchor: thread (token tid/4, channels 32 (tid%4) .. +31), float32 ----
+    // B operands of weight matrix W [128 out][128 in]: rows nc of this wave
+    auto load_b = [&](const uint16_t* W, bf16x8 (&b)[8]) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            b[k] = *reinterpret_cast<const bf16x8*>(W + (size_t)nc * kD + 16 * k + 8 * hh);
+    };
+    bf16x8 bcur[8], bnext[8];
+    load_b(Wk, bcur);  // first matrix in flight during the anchor
+
+    // rows [t0, t0 + n) of a [T][128] bf16 tensor of head bh: thread tid moves
+    // 16 bytes of row r = tid / 16 + 32 i
+    auto tile_rows = [&](const uint16_t* src, uint4 (&dst)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 4) + 16 * i;
+            dst[i] = r < n ? *reinterpret_cast<const uint4*>(src + ((size_t)bh * j.T + t0 + r) * kD + 8 * (tid & 15))
+                           : make_uint4(0, 0, 0, 0);
+        }
+    };
+    uint4 vrow[4];
+    tile_rows(v, vrow);
+
+    // ---- anchor: thread (token tid/8, channels 16 (tid%8) .. +15), float32 ----
     {
         const int t = tid >> 2, cb = 32 * (tid & 3);
         const int tok = t0 + t;
@@ -233,42 +268,23 @@ __global__ __launch_bounds__(kThreads, 2) void prism_mfma_kernel(const PrismJob 
             *reinterpret_cast<uint4*>(&Ul[t * kLdu + c0]) = pl;
         }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(&Ob[((tid >> 4) + 16 * i) * kLdu + 8 * (tid & 15)]) = vrow[i];
     __syncthreads();
 
-    // ---- projections: wave w owns channels nc = 32 w + l32 of both 32-token tiles ----
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int nc = 32 * w + l32;
-    // accumulator element e of tile tt is token 32 tt + row(e)
+    // accumulator element e of token tile tt is token 32 tt + row(e), channel nc
     auto row = [&](int e) { return 8 * (e >> 2) + 4 * hh + (e & 3); };
-    // Buffer resources over this tile's tokens: rows past the sequence end read
-    // as zero and their stores are dropped by the hardware range check.  Byte
-    // offsets split into a lane part (voffset) and a wave-uniform part.
-    const int nn = __builtin_amdgcn_readfirstlane(n);
-    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(v + ((size_t)bh * j.T + t0) * kD), (short)0, nn * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-        k2 + ((size_t)bh * T2 + (size_t)t0 * G) * kD, (short)0, nn * G * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t dres = __builtin_amdgcn_make_buffer_rsrc(
-        v2 + ((size_t)bh * T2 + (size_t)t0 * G) * kD, (short)0, nn * G * kD * 2, 0x00020000);
     // residual r = v - u in the accumulator layout
     float res[2][16];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int t = 32 * tt + row(e);
-            const float uu = bf16_to_f32(Uh[t * kLdu + nc]) + bf16_to_f32(Ul[t * kLdu + nc]);
-            const int rt = 32 * tt + 8 * (e >> 2) + (e & 3);  // row(e) without the lane part
-            const uint16_t vb = __builtin_amdgcn_raw_buffer_load_b16(vres, (4 * hh * kD + nc) * 2,
-                                                                     rt * kD * 2, 0);
-            res[tt][e] = bf16_to_f32(vb) - uu;
-        }
-    // B operands of one weight matrix W [128 out][128 in]: rows nc of this wave
-    auto load_b = [&](const uint16_t* W, bf16x8 (&b)[8]) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            b[k] = *reinterpret_cast<const bf16x8*>(W + (size_t)nc * kD + 16 * k + 8 * hh);
-    };
+    for (int e = 0; e < 16; ++e) {
+        const int t = 32 * tt + row(e);
+        const float uu = bf16_to_f32(Uh[t * kLdu + nc]) + bf16_to_f32(Ul[t * kLdu + nc]);
+        res[tt][e] = bf16_to_f32(Ob[t * kLdu + nc]) - uu;
+    }
     // token tile tt of u W^T (u = u_hi + u_lo)
     auto project = [&](const bf16x8 (&b)[8], int tt) {
         f32x16 a = {};
@@ -281,36 +297,41 @@ __global__ __launch_bounds__(kThreads, 2) void prism_mfma_kernel(const PrismJob 
         }
         return a;
     };
-    const uint16_t* Wk = static_cast<const uint16_t*>(j.Wk);
-    const uint16_t* Wp = static_cast<const uint16_t*>(j.Wp);
-    // element tG + l + 1 of token t0 + 32 tt + row(e), channel nc
-    const int ovoff = (4 * hh * G * kD + nc) * 2;
-    auto osoff = [&](int tt, int e, int l) {
-        return ((32 * tt + 8 * (e >> 2) + (e & 3)) * G + l + 1) * kD * 2;
-    };
-    for (int l = 0; l < j.L; ++l) {
-        bf16x8 b[8];
-        load_b(Wk + ((size_t)head * j.L + l) * kD * kD, b);
+    // Ob -> element rows tG + l + 1 of the tile's tokens, 16 bytes a thread
+    auto store_rows = [&](uint16_t* dst, int l) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const f32x16 acc = project(b, tt);
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), kres, ovoff, osoff(tt, e, l), 0);
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 4) + 16 * i;
+            if (r < n)
+                *reinterpret_cast<uint4*>(dst + ((size_t)bh * T2 + (size_t)(t0 + r) * G + l + 1) * kD + 8 * (tid & 15)) =
+                    *reinterpret_cast<const uint4*>(&Ob[r * kLdu + 8 * (tid & 15)]);
         }
-        load_b(Wp + ((size_t)head * j.L + l) * kD * kD, b);
+    };
+    // 2L projections in the order Wk[0], Wp[0], Wk[1], ...; the next matrix's
+    // operands load while the current one is in use
+    for (int m = 0; m < 2 * j.L; ++m) {
+        const int l = m >> 1;
+        const bool is_p = m & 1;
+        if (m + 1 < 2 * j.L) load_b(((m + 1) & 1 ? Wp : Wk) + (size_t)((m + 1) >> 1) * kD * kD, bnext);
+        __syncthreads();  // Ob free (v read, or the previous rows stored)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const f32x16 acc = project(b, tt);
+            const f32x16 acc = project(bcur, tt);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float d = gelu(acc[e] * res[tt][e]);
-                res[tt][e] -= d;
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(d), dres, ovoff, osoff(tt, e, l), 0);
+                float y = acc[e];
+                if (is_p) {  // delta = GELU(p r), r -= delta
+                    y = gelu(acc[e] * res[tt][e]);
+                    res[tt][e] -= y;
+                }
+                Ob[(32 * tt + row(e)) * kLdu + nc] = f32_to_bf16(y);
             }
         }
+        __syncthreads();
+        store_rows(is_p ? v2 : k2, l);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bcur[k] = bnext[k];
     }
-    copy_stream<uint16_t>(j, bh, t0, n);
 }
 
 }  // namespace
@@ -323,9 +344,16 @@ bool prism_supported(int dtype, int dk, int dv) {
 }
 
 hipError_t launch_prism_expand(int dtype, const PrismJob& j, hipStream_t stream) {
+    const unsigned cgrid = (unsigned)((size_t)j.BH * ((j.T + kCopyTokens - 1) / kCopyTokens));
+    if (dtype == 0)
+        hipLaunchKernelGGL(prism_copy_kernel<float>, dim3(cgrid), dim3(kThreads), 0, stream, j);
+    else
+        hipLaunchKernelGGL(prism_copy_kernel<uint16_t>, dim3(cgrid), dim3(kThreads), 0, stream, j);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || j.L == 0) return e;  // no corrections: the copy is the stream
     if (dtype == 1 && j.dk == kD && j.dv == kD) {
         const unsigned grid = (unsigned)((size_t)j.BH * ((j.T + kTok - 1) / kTok));
-        hipLaunchKernelGGL(prism_mfma_kernel, dim3(grid), dim3(kThreads), 0, stream, j);
+        hipLaunchKernelGGL(prism_mfma_kernel, dim3(grid), dim3(kMfmaThreads), 0, stream, j);
     } else {
         const unsigned grid = (unsigned)((size_t)j.BH * ((j.T + kPlainTokens - 1) / kPlainTokens));
         if (dtype == 0)
