@@ -185,6 +185,42 @@ int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
                  const float *conv, const void *Wk, const void *Wp,
                  void *q2, void *k2, void *v2, float *alpha2, float *beta2, void *stream);
 
+/* lact_fwd order */
+#define LACT_UPDATE_THEN_APPLY 0  /* chunk b read with W_{b+1}: each token sees its whole chunk */
+#define LACT_APPLY_THEN_UPDATE 1  /* chunk b read with W_b: the mask shifted by one chunk */
+
+/*
+ * Large-chunk fast-weight update with linear fast weights ("块级更新与端到端
+ * TTT", PaperTrace 5.2, opening section; the LaCT news article on
+ * senqingzn.com, the large-chunk test-time-training layer and its update/apply
+ * paragraph).  Per head a fast weight W (dv x dk, float32) learns the
+ * key-value reconstruction loss |W k - v|^2 / 2 with one gradient step per
+ * chunk of `chunk` tokens, every gradient of the chunk taken at the chunk's
+ * starting weight:
+ *
+ *   W_{b+1} = W_b - sum_{i in chunk b} eta_i (W_b k_i - v_i) k_i^T
+ *   o_i     = W_{b+1} q_i  (LACT_UPDATE_THEN_APPLY)   or   W_b q_i  (LACT_APPLY_THEN_UPDATE)
+ *
+ * A ragged last chunk holds the remaining tokens.
+ *   q, k : [B, H, T, dk] dtype      v, o : [B, H, T, dv] dtype
+ *   eta  : [B, H, T] float32 learning rates (a constant array is the pages' scalar)
+ *   W0   : [B, H, dv, dk] float32 initial weight, or NULL for zero
+ *   WT   : [B, H, dv, dk] float32 final weight, or NULL; may equal W0
+ *   workspace: lact_fwd_workspace_size(...) bytes of device scratch (NULL if 0),
+ *          256-byte aligned; reusable across calls ordered on one stream.
+ * Supported: dtype SCAN_BF16 with dk = dv = 128 and chunk a multiple of 64
+ * (MFMA path: chunk statistics G = K^T diag(eta) K and F = V^T diag(eta) K for
+ * every chunk in parallel, the chunk recursion per head in float32, then
+ * O = Q W^T for every token in parallel), or either dtype with dk, dv in
+ * {16, 32, 64} and any chunk >= 1 (plain float32 kernel, one workgroup per head).
+ * Returns SCAN_OK or an error status; lact_fwd_workspace_size returns
+ * (size_t)-1 for invalid or unsupported arguments.
+ */
+size_t lact_fwd_workspace_size(int dtype, int B, int H, int T, int dk, int dv, int chunk);
+int lact_fwd(int dtype, int B, int H, int T, int dk, int dv, int chunk, int order,
+             const void *q, const void *k, const void *v, const float *eta, const float *W0,
+             void *o, float *WT, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message describing the last non-zero status returned on this host thread. */
 const char *scan_last_error(void);
 

@@ -1,6 +1,7 @@
 """gfx950 (MI355X) matrix-state affine prefix scan: gated delta rule (with
 optionally split erase/write strengths), gated linear attention, and PRISM's
-rank-L write expanded onto the same scan.
+rank-L write expanded onto the same scan; and the large-chunk fast-weight
+update (LaCT-style test-time training with linear fast weights).
 
 The compute path is the C-ABI library ``libgdscan.so`` (``include/gdscan.h``,
 sources in ``csrc/``); this package is its Python binding.  The library is
@@ -8,5 +9,6 @@ loaded on first use.
 """
 from ._lib import (  # noqa: F401
     PATHS, SCAN_BF16, SCAN_F32, SCAN_GDN, SCAN_GDN_EW, SCAN_GLA, ScanError, decode_step,
-    last_error, lib, prism_expand, prism_scan_fwd, scan_fwd, scan_fwd_workspace_size, version,
+    last_error, lact_fwd, lact_fwd_workspace_size, lib, prism_expand, prism_scan_fwd, scan_fwd,
+    scan_fwd_workspace_size, version,
 )

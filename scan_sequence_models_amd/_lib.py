@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.decode_step.restype = i
         L.prism_expand.argtypes = [i] * 8 + [p] * 15 + [p]
         L.prism_expand.restype = i
+        L.lact_fwd_workspace_size.argtypes = [i] * 7
+        L.lact_fwd_workspace_size.restype = sz
+        L.lact_fwd.argtypes = [i] * 8 + [p] * 7 + [p, sz, p]
+        L.lact_fwd.restype = i
         L.scan_last_error.restype = ctypes.c_char_p
         L.scan_version.restype = ctypes.c_char_p
         _lib = L
@@ -268,3 +272,52 @@ def prism_scan_fwd(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None
     B, H, T, _ = q.shape
     G = q2.shape[2] // T
     return o2.view(B, H, T, G, o2.shape[-1])[:, :, :, G - 1], ST
+
+
+LACT_ORDERS = {"update_then_apply": 0, "apply_then_update": 1}
+
+
+def lact_fwd_workspace_size(dtype: int, B: int, H: int, T: int, dk: int, dv: int, chunk: int) -> int:
+    n = lib().lact_fwd_workspace_size(dtype, B, H, T, dk, dv, chunk)
+    if n == ctypes.c_size_t(-1).value:
+        raise ScanError(SCAN_EINVAL, last_error())
+    return n
+
+
+def lact_fwd(q, k, v, eta, W0=None, *, chunk: int, order: str = "update_then_apply", o=None,
+             WT=None, workspace=None, write_state: bool = True):
+    """Large-chunk fast-weight update over [B, H, T, d] tensors; returns (o, WT).
+
+    eta [B, H, T] float32; W0 [B, H, dv, dk] float32 or None (zero); ``order``
+    is "update_then_apply" or "apply_then_update".
+    """
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", dt, (B, H, T, dk), dev)
+    _need(v, "v", dt, (B, H, T, dv), dev)
+    _need(eta, "eta", torch.float32, (B, H, T), dev)
+    if W0 is not None:
+        _need(W0, "W0", torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _need(o, "o", dt, (B, H, T, dv), dev)
+    if WT is None and write_state:
+        WT = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if WT is not None:
+        _need(WT, "WT", torch.float32, (B, H, dv, dk), dev)
+    dcode = _dtype_code(q)
+    ws_bytes = lact_fwd_workspace_size(dcode, B, H, T, dk, dv, chunk)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().lact_fwd(dcode, B, H, T, dk, dv, chunk, LACT_ORDERS[order], _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(eta), _ptr(W0), _ptr(o), _ptr(WT), _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), _stream(dev))
+    _check(st)
+    return o, WT

@@ -276,4 +276,72 @@ int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W, c
     return SCAN_OK;
 }
 
+namespace {
+// Validates the sizes of a lact_fwd call; returns SCAN_OK and the workspace bytes.
+int plan_lact(int dtype, int B, int H, int T, int dk, int dv, int chunk, size_t* ws) {
+    if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
+    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1 || chunk < 1)
+        return fail(SCAN_EINVAL, "B, H, T, dk, dv, chunk must be >= 1 (got %d, %d, %d, %d, %d, %d)", B, H, T, dk, dv, chunk);
+    if ((int64_t)B * H > INT32_MAX / 64 || (int64_t)B * H * ((T + 63) / 64) > INT32_MAX)
+        return fail(SCAN_EINVAL, "B*H*T too large");
+    if (gds::lact_mfma_supported(dtype, dk, dv, chunk)) {
+        *ws = gds::lact_workspace_bytes((int64_t)B * H, T, chunk);
+        return SCAN_OK;
+    }
+    if (gds::lact_plain_supported(dk, dv)) {
+        *ws = 0;
+        return SCAN_OK;
+    }
+    return fail(SCAN_EUNSUPPORTED,
+                "lact_fwd supports bf16 with dk = dv = 128 and chunk a multiple of 64, or dk, dv in {16, 32, 64} "
+                "(got dtype %d, dk %d, dv %d, chunk %d)", dtype, dk, dv, chunk);
+}
+}  // namespace
+
+size_t lact_fwd_workspace_size(int dtype, int B, int H, int T, int dk, int dv, int chunk) {
+    size_t ws = 0;
+    if (plan_lact(dtype, B, H, T, dk, dv, chunk, &ws) != SCAN_OK) return (size_t)-1;
+    return ws;
+}
+
+int lact_fwd(int dtype, int B, int H, int T, int dk, int dv, int chunk, int order, const void* q,
+             const void* k, const void* v, const float* eta, const float* W0, void* o, float* WT,
+             void* workspace, size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    int st = plan_lact(dtype, B, H, T, dk, dv, chunk, &need);
+    if (st != SCAN_OK) return st;
+    if (order != LACT_UPDATE_THEN_APPLY && order != LACT_APPLY_THEN_UPDATE)
+        return fail(SCAN_EINVAL, "order must be LACT_UPDATE_THEN_APPLY or LACT_APPLY_THEN_UPDATE (got %d)", order);
+    if (!q || !k || !v || !eta || !o) return fail(SCAN_EINVAL, "q, k, v, eta and o must be non-null");
+    const void* a16[] = {q, k, v, o, W0, WT};
+    const char* n16[] = {"q", "k", "v", "o", "W0", "WT"};
+    for (int i = 0; i < 6; ++i)
+        if (a16[i] && !aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
+    if (!aligned(eta, 4)) return fail(SCAN_EALIGN, "eta is not 4-byte aligned");
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(SCAN_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        if (!aligned(workspace, 256)) return fail(SCAN_EALIGN, "workspace is not 256-byte aligned");
+    }
+    const size_t es = dtype == SCAN_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H;
+    const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
+                        range("v", v, BH * T * dv * es), range("eta", eta, BH * T * 4),
+                        range("W0", W0, BH * dv * dk * 4), range("workspace", workspace, need)};
+    const Range ro = range("o", o, BH * T * dv * es);
+    const Range rw = range("WT", WT, BH * dv * dk * 4);
+    for (const Range& r : in) {
+        if (overlaps(ro, r)) return fail(SCAN_EINVAL, "o overlaps %s", r.name);
+        if (overlaps(rw, r) && !(r.name[0] == 'W' && WT == W0))
+            return fail(SCAN_EINVAL, "WT overlaps %s (only WT == W0 is allowed)", r.name);
+    }
+    if (overlaps(ro, rw)) return fail(SCAN_EINVAL, "o overlaps WT");
+    gds::LactJob j{};
+    j.q = q; j.k = k; j.v = v; j.eta = eta; j.W0 = W0; j.o = o; j.WT = WT;
+    j.BH = (int)BH; j.T = T; j.dk = dk; j.dv = dv; j.chunk = chunk; j.order = order;
+    hipError_t e = gds::launch_lact(dtype, j, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lact_fwd launch");
+    return SCAN_OK;
+}
+
 }  // extern "C"

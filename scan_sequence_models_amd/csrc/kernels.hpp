@@ -66,4 +66,20 @@ struct PrismJob {
 bool prism_supported(int dtype, int dk, int dv);
 hipError_t launch_prism_expand(int dtype, const PrismJob& job, hipStream_t stream);
 
+// lact.hip -- large-chunk fast-weight update (linear fast weights) -----------
+struct LactJob {
+    const void *q, *k, *v;  // [BH, T, dk] / [BH, T, dv]
+    const float* eta;       // [BH, T] learning rates
+    const float* W0;        // [BH, dv, dk] or null (zero)
+    void* o;                // [BH, T, dv]
+    float* WT;              // [BH, dv, dk] or null
+    float* ws_stats;        // MFMA path: per (head, chunk, split) partial G, F
+    uint16_t* ws_wuse;      // MFMA path: per (head, chunk) applied weight, bf16
+    int BH, T, dk, dv, chunk, order, nsplit, split_tokens;
+};
+bool lact_mfma_supported(int dtype, int dk, int dv, int chunk);
+bool lact_plain_supported(int dk, int dv);
+size_t lact_workspace_bytes(int64_t heads, int T, int chunk);
+hipError_t launch_lact(int dtype, LactJob job, void* workspace, hipStream_t stream);
+
 }  // namespace gds

@@ -17,6 +17,10 @@ Decode workloads draw each state ``n`` from ``SeedSequence([seed, n])``: the
 initial state first, then all steps' q, k, v, alpha and beta (see
 ``decode_state_inputs``).
 
+Fast-weight workloads (mode "lact") use q, k, v and S0 (as W0) of the recipe
+above and draw learning rates ~ U(0, 1) dk / chunk from
+``SeedSequence([seed, b, h, 3])``.
+
 PRISM workloads (``prism_steps`` L > 0) add, per head (b, h), from
 ``SeedSequence([seed, b, h, 1])``: the anchor source x ~ N(0, 1) (T x dv) and
 the step gates beta^(l) = sigmoid(N(0, 1)) (T x L); and per head index h,
@@ -148,6 +152,12 @@ WORKLOADS = {
     "tiny-prism": Workload("tiny-prism", "gdn", 1, 2, 64, 16, 16, "f32", 16,
                            ("uniform", 0.9, 1.0), ("uniform", 0.0, 1.0), None, seed=7,
                            prism_steps=2, prism_window=4),
+    # Large-chunk fast-weight update: chunk = 2048 tokens, W0 ~ N(0, 0.01); the
+    # alpha field is unused (eta comes from lact_eta)
+    "lact-b8h16t8192-m2048": Workload("lact-b8h16t8192-m2048", "lact", 8, 16, 8192, 128, 128,
+                                      "bf16", 2048, ("const", 1.0), None, 0.01, seed=8),
+    "tiny-lact": Workload("tiny-lact", "lact", 1, 2, 100, 16, 16, "f32", 16, ("const", 1.0),
+                          None, 0.01, seed=9),
 }
 
 
@@ -301,3 +311,12 @@ def prism_token_inputs(w: Workload, b: int, h: int, T: int | None = None):
     z = rng.normal(0.0, 1.0, size=(T, w.prism_steps))
     beta_l = cast(1.0 / (1.0 + np.exp(-z)), "f32")
     return x, beta_l
+
+
+def lact_eta(w: Workload, b: int, h: int, T: int | None = None) -> np.ndarray:
+    """Learning rates of head (b, h) for a fast-weight workload: U(0, 1) * dk / chunk,
+    float32, from ``SeedSequence([seed, b, h, 3])`` (so that |eta K^T K| stays
+    near 1/2 and the chunk update is a contraction)."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 3]))
+    return cast(rng.uniform(0.0, 1.0, T) * w.dk / w.chunk, "f32")

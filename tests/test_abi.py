@@ -21,7 +21,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.header_functions()
     assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "decode_step", "prism_expand",
-                          "scan_last_error", "scan_version"}
+                          "lact_fwd_workspace_size", "lact_fwd", "scan_last_error", "scan_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -138,3 +138,41 @@ def _prism(lib, dtype=1, B=1, H=2, T=64, dk=128, dv=128, Lsteps=2, W=4, q=FAKE, 
 def test_prism_expand_rejects(lib, kw, code):
     assert _prism(lib, **kw) == code
     assert len(L.last_error()) > 0
+
+
+def _lact(lib, dtype=1, B=1, H=2, T=4096, dk=128, dv=128, chunk=2048, order=0, q=FAKE,
+          k=FAKE + STEP, v=FAKE + 2 * STEP, eta=FAKE + 3 * STEP, W0=None, o=FAKE + 5 * STEP,
+          WT=FAKE + 6 * STEP, ws=FAKE + 7 * STEP, wsb=1 << 30):
+    # a valid argument set would launch with fake pointers: only invalid ones are passed
+    return lib.lact_fwd(dtype, B, H, T, dk, dv, chunk, order, q, k, v, eta, W0, o, WT, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), L.SCAN_EINVAL),
+    (dict(T=0), L.SCAN_EINVAL),
+    (dict(chunk=0), L.SCAN_EINVAL),
+    (dict(chunk=100), L.SCAN_EUNSUPPORTED),           # bf16 d=128 needs a multiple of 64
+    (dict(dk=96), L.SCAN_EUNSUPPORTED),
+    (dict(dtype=0), L.SCAN_EUNSUPPORTED),             # float32 has no d = 128 path
+    (dict(order=2), L.SCAN_EINVAL),
+    (dict(q=None), L.SCAN_EINVAL),
+    (dict(eta=None), L.SCAN_EINVAL),
+    (dict(ws=None), L.SCAN_EWORKSPACE),
+    (dict(wsb=1024), L.SCAN_EWORKSPACE),
+    (dict(ws=FAKE + 7 * STEP + 64), L.SCAN_EALIGN),
+    (dict(k=FAKE + STEP + 8), L.SCAN_EALIGN),
+    (dict(eta=FAKE + 3 * STEP + 2), L.SCAN_EALIGN),
+    (dict(o=FAKE + 1024), L.SCAN_EINVAL),             # o overlaps q
+    (dict(WT=FAKE + 2 * STEP), L.SCAN_EINVAL),        # WT overlaps v
+])
+def test_lact_fwd_rejects(lib, kw, code):
+    assert _lact(lib, **kw) == code
+    assert len(L.last_error()) > 0
+
+
+def test_lact_workspace_sizes(lib):
+    # plain path (d <= 64): none; MFMA path: partial statistics and bf16 weights
+    assert lib.lact_fwd_workspace_size(0, 1, 1, 64, 16, 16, 16) == 0
+    n = lib.lact_fwd_workspace_size(1, 8, 16, 8192, 128, 128, 2048)
+    assert n == 128 * 4 * (2 * 128 * 128 * 4 + 128 * 128 * 2)
+    assert lib.lact_fwd_workspace_size(1, 1, 1, 64, 128, 128, 100) == ctypes.c_size_t(-1).value
