@@ -11,8 +11,10 @@ float64 CPU oracle timed on a bounded sample of the same workload.
 
 Other workloads: --workload gla-b4h8t4096 (gated linear attention),
 long-b2h8t262144 (the long-sequence path), decode-4096x100 (decode_step over
-4096 states, one timed step per token) and prism-b8h16t8192-l2 (the PRISM layer:
-prism_expand, then the split-strength scan of the 3x longer element stream).  Timing: W untimed steps (by default
+4096 states, one timed step per token), prism-b8h16t8192-l2 (the PRISM layer:
+prism_expand, then the split-strength scan of the 3x longer element stream) and
+lact-b8h16t8192-m2048 (lact_fwd: the large-chunk fast-weight update, chunks of
+2048 tokens).  Timing: W untimed steps (by default
 enough to cover the GPU's clock ramp), then two HIP events around K back-to-back
 steps on the launch stream.
 """
@@ -449,6 +451,133 @@ def bench_prism(args, w):
     print(json.dumps(result), flush=True)
 
 
+def lact_bytes(w) -> int:
+    """Algorithmic HBM bytes of one lact_fwd call: q, k, v read and o written
+    once (dtype), eta read once (fp32), W0 read and W_T written once (fp32)."""
+    es = 2 if w.dtype == "bf16" else 4
+    ht = w.B * w.H * w.T
+    return ht * (2 * w.dk + 2 * w.dv) * es + ht * 4 + 2 * w.B * w.H * w.dv * w.dk * 4
+
+
+def lact_flops(w) -> float:
+    """Algorithmic flops of one lact_fwd call: per token G = K^T diag(eta) K,
+    F = V^T diag(eta) K and the read-out (2 d^2 each), per chunk W G (2 d^3)."""
+    d = w.dk
+    nch = -(-w.T // w.chunk)
+    return w.B * w.H * (w.T * 6 * d * d + nch * 2 * d ** 3)
+
+
+def cpu_baseline_lact(w, heads: int):
+    """The float64 fast-weight oracle on the first ``heads`` heads of ``w``."""
+    import numpy as np
+
+    from oracle import lact as olact
+    from scan_sequence_models_amd import inputs as I
+
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
+    hs = [I.head_inputs(w, b, h) for b, h in sel]
+    etas = [I.lact_eta(w, b, h) for b, h in sel]
+    t0 = time.perf_counter()
+    for x, e in zip(hs, etas):
+        olact.lact(x.q, x.k, x.v, e, w.chunk, olact.UPDATE_THEN_APPLY, x.S0.astype(np.float64))
+    sec = time.perf_counter() - t0
+    head_tokens = len(sel) * w.T
+    return {
+        "value": head_tokens / w.H / sec,
+        "unit": "tokens/s",
+        "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"{len(sel)} of {w.B * w.H} heads x {w.T} tokens ({head_tokens} head-tokens), "
+                  f"float64 numpy chunk updates (BLAS threads), {sec:.2f} s",
+        "seconds": sec,
+    }
+
+
+def bench_lact(args, w):
+    """lact_fwd over the whole batch, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import scan_sequence_models_amd as gds
+    from scan_sequence_models_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating {w.name} (B={w.B} H={w.H} T={w.T} d={w.dk} chunk={w.chunk})")
+    b = I.batch_inputs(w, threads=16)
+    eta = np.stack([np.stack([I.lact_eta(w, bb, hh) for hh in range(w.H)]) for bb in range(w.B)])
+    bf = w.dtype == "bf16"
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    q, k, v = up(b.q, bf), up(b.k, bf), up(b.v, bf)
+    et, W0 = up(eta), up(b.S0)
+    del b, eta
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=q.dtype, device=dev)
+    WT = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    dcode = gds.SCAN_BF16 if bf else gds.SCAN_F32
+    nws = gds.lact_fwd_workspace_size(dcode, w.B, w.H, w.T, w.dk, w.dv, w.chunk)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        gds.lact_fwd(q, k, v, et, W0, chunk=w.chunk, o=o, WT=WT, workspace=ws)
+
+    copy_probe(args.copy_probe_mib, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    span_ms, wall = timed(lambda i: step(), args.steps, dev)
+    ms = span_ms / args.steps
+    log(f"bench: {args.steps} lact_fwd calls, {ms:.4f} ms per call, wall {wall * 1e3:.1f} ms")
+    alg = lact_bytes(w)
+    flops = lact_flops(w)
+    src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "lact.hip")
+    result = {
+        "metric": "tokens/s large-chunk fast-weight update fwd (H=16, d=128, T=8192, chunk 2048); "
+                  "% HBM / MFMA roofline",
+        "value": w.B * w.T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "order": "update_then_apply", "io_dtype": w.dtype,
+                   "weight_dtype": "f32"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": alg / (ms / 1e3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic(src, f"lact_{w.name}_traffic.txt"),
+            "kernel": "lact_fwd (stats + recursion + apply kernels)",
+            "algorithmic_bytes_per_launch": alg,
+            "kernel_ms": ms,
+        },
+        "mfma": {
+            "alg_tflops": flops / (ms / 1e3) / 1e12,
+            "peak_tflops": BF16_MFMA_PEAK_TFS,
+            "alg_frac": flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
+            "alg_flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        heads = min(args.cpu_heads, 16)
+        log(f"bench: timing the CPU oracle on {heads} heads")
+        result["cpu_baseline"] = cpu_baseline_lact(w, heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,6 +624,8 @@ def main():
         args.warmup = 30
     if w.prism_steps:
         return bench_prism(args, w)
+    if w.mode == "lact":
+        return bench_lact(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

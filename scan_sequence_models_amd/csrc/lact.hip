@@ -17,8 +17,8 @@
 // tokens, so the work splits in three:
 //
 //   lact_stats_kernel  (all chunks in parallel)  G_b, F_b, split-bf16 MFMA
-//   lact_recur_kernel  (per head, chunk by chunk) W_{b+1} = W_b + F_b - W_b G_b,
-//                                                  float32 MFMA, W in LDS
+//   lact_recur_kernel  (chunk by chunk; 16 rows of W per workgroup)
+//                      W_{b+1} = W_b + F_b - W_b G_b in float32
 //   lact_apply_kernel  (all tokens in parallel)   O = Q W_use^T, bf16 MFMA
 //
 // for bfloat16 data with d_k = d_v = 128 and m a multiple of 64, and
@@ -104,9 +104,6 @@ constexpr int kLdt = kD + 32;   // row stride (bf16) of staged [token][channel] 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // Operand of a 32x32x16 MFMA contracted over the rows (tokens) of a row-major
 // [token][channel] bf16 tile in LDS: lane (c = lane % 32, g = lane / 32) gets
@@ -146,11 +143,11 @@ __device__ __forceinline__ void scale_split(bf16x8 x, const float (&e)[8], bf16x
 
 // G_b (and F_b) partial sums over one split of a chunk: workgroup (unit, chunk,
 // split) of 4 waves; wave w owns rows 32w .. 32w+31 of G and F (four 32x32
-// tiles each).  Tokens come in tiles of 64, double-buffered in LDS.
-__global__ __launch_bounds__(kThreads, 1) void lact_stats_kernel(const LactJob j) {
+// tiles each).  Tokens come in tiles of 64, double-buffered in LDS (80 KB: two
+// workgroups per CU); eta of token t sits in the padding of row t of the k tile.
+__global__ __launch_bounds__(kThreads, 2) void lact_stats_kernel(const LactJob j) {
     __shared__ uint16_t Ks[2][kTok * kLdt];
     __shared__ uint16_t Vs[2][kTok * kLdt];
-    __shared__ float Es[2][kTok];
     const int nch = (j.T + j.chunk - 1) / j.chunk;
     const int x = blockIdx.x;
     const int split = x % j.nsplit, cb = (x / j.nsplit) % nch, bh = x / (j.nsplit * nch);
@@ -182,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void lact_stats_kernel(const LactJob j
             *reinterpret_cast<uint4*>(&Ks[buf][r * kLdt + 8 * (tid & 15)]) = kr[i];
             *reinterpret_cast<uint4*>(&Vs[buf][r * kLdt + 8 * (tid & 15)]) = vr[i];
         }
-        if (tid < kTok) Es[buf][tid] = er;
+        if (tid < kTok) *reinterpret_cast<float*>(&Ks[buf][tid * kLdt + kD]) = er;
     };
 
     f32x16 g[4], f[4];
@@ -203,15 +200,16 @@ __global__ __launch_bounds__(kThreads, 1) void lact_stats_kernel(const LactJob j
         for (int s = 0; s < kTok / 16; ++s) {
             // eta of this lane's eight tokens 16 s + 8 (lane / 32) + e
             float e8[8];
-            const f32x4 ea = *reinterpret_cast<const f32x4*>(&Es[buf][16 * s + 8 * (lane >> 5)]);
-            const f32x4 eb = *reinterpret_cast<const f32x4*>(&Es[buf][16 * s + 8 * (lane >> 5) + 4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { e8[i] = ea[i]; e8[4 + i] = eb[i]; }
+            for (int i = 0; i < 8; ++i)
+                e8[i] = *reinterpret_cast<const float*>(&K[(16 * s + 8 * (lane >> 5) + i) * kLdt + kD]);
             bf16x8 b[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) b[J] = tr_operand(K, 16 * s, 32 * J, lane);
             bf16x8 gh, gl, fh, fl;
-            scale_split(b[w], e8, gh, gl);                        // rows 32w.. of eta K
+            // rows 32w.. of eta K (read again: indexing b[] by the wave would
+            // compile to a select over every element)
+            scale_split(tr_operand(K, 16 * s, 32 * w, lane), e8, gh, gl);
             scale_split(tr_operand(V, 16 * s, 32 * w, lane), e8, fh, fl);  // rows of eta V
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
@@ -237,118 +235,144 @@ __global__ __launch_bounds__(kThreads, 1) void lact_stats_kernel(const LactJob j
         }
 }
 
-// Chunk-by-chunk recursion of one head: W (fp32) in LDS; W G on the fp32 MFMA
-// (16x16x4); each chunk's applied weight leaves as bf16 for the apply kernel.
-constexpr int kLdw = kD + 4;  // fp32 row stride in LDS
-__global__ __launch_bounds__(kThreads, 1) void lact_recur_kernel(const LactJob j) {
-    __shared__ float Wl[kD * kLdw];  // W_b       [dv][dk]
-    __shared__ float Gl[kD * kLdw];  // G_b       [dk][dk]
-    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Chunk-by-chunk recursion, W_{b+1} = W_b + F_b - W_b G_b, in float32.  Rows
+// of W are independent, so a workgroup owns 16 rows of one head (8 workgroups
+// per head): G_b (summed over the splits) is staged in LDS, thread t computes
+// column t % 128 of rows 8 (t / 128) .. +7 with float32 FMAs (the row values
+// are wave-uniform LDS broadcasts).  Each chunk's applied weight leaves as
+// bf16 for the apply kernel.
+constexpr int kRecurRows = 16;
+constexpr int kLdg = kD + 4;  // fp32 row stride of G in LDS
+__global__ __launch_bounds__(kThreads) void lact_recur_kernel(const LactJob j) {
+    __shared__ float Gl[kD * kLdg];         // G_b [dk][dk]
+    __shared__ float Wr[kRecurRows * kD];   // rows r0 .. r0+15 of W_b
+    const int bh = blockIdx.x / (kD / kRecurRows);
+    const int r0 = (blockIdx.x % (kD / kRecurRows)) * kRecurRows;
+    const int tid = threadIdx.x;
+    const int col = tid & (kD - 1), rg = 8 * (tid >> 7);  // rows rg .. rg+7 of the block
     const int nch = (j.T + j.chunk - 1) / j.chunk;
-    for (int x = tid; x < kD * kD; x += kThreads)
-        Wl[(x >> 7) * kLdw + (x & 127)] = j.W0 ? j.W0[(size_t)bh * kD * kD + x] : 0.f;
-    // wave w: rows 32w .. 32w+31 of the product, as 2 x 8 blocks of 16x16;
-    // lane (c = lane % 16, g = lane / 16) holds rows 4g .. 4g+3 of column c
-    const int c16 = lane & 15, g4 = lane >> 4;
-    auto store_bf16 = [&](uint16_t* dst) {  // Wl -> bf16 [dv][dk]
-        for (int x = tid; x < kD * kD; x += kThreads)
-            dst[x] = f32_to_bf16(Wl[(x >> 7) * kLdw + (x & 127)]);
+    const size_t wbase = ((size_t)bh * kD + r0) * kD;   // this block's rows in [BH][dv][dk]
+    for (int x = tid; x < kRecurRows * kD; x += kThreads) Wr[x] = j.W0 ? j.W0[wbase + x] : 0.f;
+    auto store_use = [&](int cb) {  // rows of the applied weight, bf16
+        uint16_t* dst = j.ws_wuse + ((size_t)(bh * nch + cb) * kD + r0) * kD;
+        for (int x = tid; x < kRecurRows * kD; x += kThreads) dst[x] = f32_to_bf16(Wr[x]);
     };
     for (int cb = 0; cb < nch; ++cb) {
         const float* st = j.ws_stats + (size_t)(bh * nch + cb) * j.nsplit * 2 * kD * kD;
-        __syncthreads();  // previous W final in Wl
-        for (int x = tid; x < kD * kD; x += kThreads) {
-            float gsum = 0.f;
-            for (int s = 0; s < j.nsplit; ++s) gsum += st[(size_t)s * 2 * kD * kD + x];
-            Gl[(x >> 7) * kLdw + (x & 127)] = gsum;
-        }
-        if (j.order == 1) store_bf16(j.ws_wuse + (size_t)(bh * nch + cb) * kD * kD);
-        __syncthreads();
-        // new rows of W: W + F - W G, accumulated in registers
-        f32x4 acc[2][8];
+        __syncthreads();  // Wr holds W_b
+        {
+            // G_b: 16 float4 per thread, every load of a split in flight at once
+            f32x4 gv[16];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+            for (int i = 0; i < 16; ++i) gv[i] = *reinterpret_cast<const f32x4*>(st + 4 * (tid + kThreads * i));
+            for (int s = 1; s < j.nsplit; ++s) {
+                const float* sp = st + (size_t)s * 2 * kD * kD;
 #pragma unroll
-            for (int cbk = 0; cbk < 8; ++cbk) {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
-                const int r0 = 32 * w + 16 * rb;
-                for (int kk = 0; kk < kD; kk += 4) {
-                    const float av = Wl[(r0 + c16) * kLdw + kk + g4];  // A[m = c16][k = g4]
-                    const float bv = Gl[(kk + g4) * kLdw + 16 * cbk + c16];  // B[k = g4][n = c16]
-                    a = mfma4(av, bv, a);
-                }
-                acc[rb][cbk] = a;
+                for (int i = 0; i < 16; ++i) gv[i] += *reinterpret_cast<const f32x4*>(sp + 4 * (tid + kThreads * i));
             }
-        __syncthreads();  // every read of the old W done
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int cbk = 0; cbk < 8; ++cbk)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 32 * w + 16 * rb + 4 * g4 + r, col = 16 * cbk + c16;
-                    float fsum = 0.f;
-                    for (int s = 0; s < j.nsplit; ++s)
-                        fsum += st[(size_t)s * 2 * kD * kD + kD * kD + row * kD + col];
-                    Wl[row * kLdw + col] += fsum - acc[rb][cbk][r];
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int x = 4 * (tid + kThreads * i);
+                *reinterpret_cast<f32x4*>(&Gl[(x >> 7) * kLdg + (x & 127)]) = gv[i];
+            }
+        }
+        if (j.order == 1) store_use(cb);
         __syncthreads();
-        if (j.order == 0) store_bf16(j.ws_wuse + (size_t)(bh * nch + cb) * kD * kD);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < kD; k += 4) {
+            float g4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g4[i] = Gl[(k + i) * kLdg + col];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(&Wr[(rg + r) * kD + k]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[r] += w4[i] * g4[i];
+            }
+        }
+        __syncthreads();  // every read of W_b done
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = rg + r;
+            float fsum = 0.f;
+            for (int s = 0; s < j.nsplit; ++s)
+                fsum += st[(size_t)s * 2 * kD * kD + kD * kD + (size_t)(r0 + row) * kD + col];
+            Wr[row * kD + col] += fsum - acc[r];
+        }
+        __syncthreads();
+        if (j.order == 0) store_use(cb);
     }
     __syncthreads();
     if (j.WT)
-        for (int x = tid; x < kD * kD; x += kThreads) j.WT[(size_t)bh * kD * kD + x] = Wl[(x >> 7) * kLdw + (x & 127)];
+        for (int x = tid; x < kRecurRows * kD; x += kThreads) j.WT[wbase + x] = Wr[x];
 }
 
-// O = Q W_use^T for 64 tokens of one head: wave w computes channels 32w ..
-// 32w+31 for both 32-token tiles; W rows go straight into B-operand registers;
-// the output is staged in LDS and stored as whole 256-byte rows.
+// O = Q W_use^T for 256 tokens of one head (four tiles of 64 in one chunk):
+// wave w computes channels 32w .. 32w+31; its W rows go straight into
+// B-operand registers once; q tiles are staged in LDS (the next one in flight
+// in registers) and the output is staged in LDS and stored as whole 256-byte
+// rows.
 constexpr int kLdo = kD + 8;
+constexpr int kApplyTiles = 4;
 __global__ __launch_bounds__(kThreads, 2) void lact_apply_kernel(const LactJob j) {
     __shared__ uint16_t Qs[kTok * kLdo];
     __shared__ uint16_t Os[kTok * kLdo];
-    const int tiles = (j.T + kTok - 1) / kTok;
-    const int bh = blockIdx.x / tiles;
-    const int t0 = (blockIdx.x - bh * tiles) * kTok;
-    const int n = min(kTok, j.T - t0);
+    constexpr int kSpan = kApplyTiles * kTok;
+    const int spans = (j.T + kSpan - 1) / kSpan;
+    const int bh = blockIdx.x / spans;
+    const int s0 = (blockIdx.x - bh * spans) * kSpan;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
     const int nch = (j.T + j.chunk - 1) / j.chunk;
     const uint16_t* q = static_cast<const uint16_t*>(j.q) + (size_t)bh * j.T * kD;
     uint16_t* o = static_cast<uint16_t*>(j.o) + (size_t)bh * j.T * kD;
+    uint4 qn[4];
+    auto fetch = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 4) + 16 * i;
-        *reinterpret_cast<uint4*>(&Qs[r * kLdo + 8 * (tid & 15)]) =
-            r < n ? *reinterpret_cast<const uint4*>(q + (size_t)(t0 + r) * kD + 8 * (tid & 15)) : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
-    // the 64 tokens may span two chunks (chunk is a multiple of 64: they do not)
-    const int cb = t0 / j.chunk;
-    const uint16_t* Wu = j.ws_wuse + ((size_t)bh * nch + cb) * kD * kD;
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + (tid >> 4) + 16 * i;
+            qn[i] = t < j.T ? *reinterpret_cast<const uint4*>(q + (size_t)t * kD + 8 * (tid & 15)) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    const int nt = min(kApplyTiles, (j.T - s0 + kTok - 1) / kTok);
+    fetch(s0);
+    int cb_loaded = -1;
     const int nc = 32 * w + l32;
     bf16x8 b[8];
+    for (int it = 0; it < nt; ++it) {
+        const int t0 = s0 + it * kTok;
+        const int n = min(kTok, j.T - t0);
+        __syncthreads();  // previous tile's Qs reads and Os stores done
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) b[kk] = *reinterpret_cast<const bf16x8*>(Wu + (size_t)nc * kD + 16 * kk + 8 * hh);
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Qs[((tid >> 4) + 16 * i) * kLdo + 8 * (tid & 15)]) = qn[i];
+        if (it + 1 < nt) fetch(t0 + kTok);
+        const int cb = t0 / j.chunk;  // a 64-token tile lies in one chunk (chunk % 64 == 0)
+        if (cb != cb_loaded) {
+            const uint16_t* Wu = j.ws_wuse + ((size_t)bh * nch + cb) * kD * kD;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        f32x16 acc = {};
-        const uint16_t* qr = &Qs[(32 * tt + l32) * kLdo + 8 * hh];
+            for (int kk = 0; kk < 8; ++kk) b[kk] = *reinterpret_cast<const bf16x8*>(Wu + (size_t)nc * kD + 16 * kk + 8 * hh);
+            cb_loaded = cb;
+        }
+        __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) acc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * kk), b[kk], acc);
+        for (int tt = 0; tt < 2; ++tt) {
+            f32x16 acc = {};
+            const uint16_t* qr = &Qs[(32 * tt + l32) * kLdo + 8 * hh];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            Os[(32 * tt + 8 * (e >> 2) + 4 * hh + (e & 3)) * kLdo + nc] = f32_to_bf16(acc[e]);
-    }
-    __syncthreads();
+            for (int kk = 0; kk < 8; ++kk) acc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * kk), b[kk], acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 4) + 16 * i;
-        if (r < n)
-            *reinterpret_cast<uint4*>(o + (size_t)(t0 + r) * kD + 8 * (tid & 15)) =
-                *reinterpret_cast<const uint4*>(&Os[r * kLdo + 8 * (tid & 15)]);
+            for (int e = 0; e < 16; ++e)
+                Os[(32 * tt + 8 * (e >> 2) + 4 * hh + (e & 3)) * kLdo + nc] = f32_to_bf16(acc[e]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 4) + 16 * i;
+            if (r < n)
+                *reinterpret_cast<uint4*>(o + (size_t)(t0 + r) * kD + 8 * (tid & 15)) =
+                    *reinterpret_cast<const uint4*>(&Os[r * kLdo + 8 * (tid & 15)]);
+        }
     }
 }
 
@@ -386,10 +410,10 @@ hipError_t launch_lact(int dtype, LactJob j, void* workspace, hipStream_t stream
                        stream, j);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lact_recur_kernel, dim3(j.BH), dim3(kThreads), 0, stream, j);
+    hipLaunchKernelGGL(lact_recur_kernel, dim3((unsigned)j.BH * (kD / kRecurRows)), dim3(kThreads), 0, stream, j);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lact_apply_kernel, dim3((unsigned)((size_t)j.BH * ((j.T + kTok - 1) / kTok))),
+    hipLaunchKernelGGL(lact_apply_kernel, dim3((unsigned)((size_t)j.BH * ((j.T + kApplyTiles * kTok - 1) / (kApplyTiles * kTok)))),
                        dim3(kThreads), 0, stream, j);
     return hipGetLastError();
 }
