@@ -17,8 +17,8 @@
 // tokens, so the work splits in three:
 //
 //   lact_stats_kernel  (all chunks in parallel)  G_b, F_b, split-bf16 MFMA
-//   lact_recur_kernel  (chunk by chunk; 16 rows of W per workgroup)
-//                      W_{b+1} = W_b + F_b - W_b G_b in float32
+//   lact_recur_kernel  (per head, chunk by chunk) W_{b+1} = W_b + F_b - W_b G_b,
+//                      W in float32 registers, W G on split-bf16 MFMA
 //   lact_apply_kernel  (all tokens in parallel)   O = Q W_use^T, bf16 MFMA
 //
 // for bfloat16 data with d_k = d_v = 128 and m a multiple of 64, and
@@ -33,6 +33,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+
+// (unit, part) of block x when each unit is split into `parts` blocks: blocks
+// are dealt round-robin over the 8 XCDs, so when the unit count is a multiple
+// of 8 the parts of a unit are placed on one XCD and share its L2.
+__device__ __forceinline__ void unit_part(int x, int units, int parts, int& unit, int& part) {
+    if ((units & 7) == 0) {
+        const int xcd = x & 7, j = x >> 3;
+        unit = (j / parts) * 8 + xcd;
+        part = j % parts;
+    } else {
+        unit = x / parts;
+        part = x % parts;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // plain kernel: one workgroup per head, everything in LDS (d <= 64)
@@ -235,76 +249,117 @@ __global__ __launch_bounds__(kThreads, 2) void lact_stats_kernel(const LactJob j
         }
 }
 
-// Chunk-by-chunk recursion, W_{b+1} = W_b + F_b - W_b G_b, in float32.  Rows
-// of W are independent, so a workgroup owns 16 rows of one head (8 workgroups
-// per head): G_b (summed over the splits) is staged in LDS, thread t computes
-// column t % 128 of rows 8 (t / 128) .. +7 with float32 FMAs (the row values
-// are wave-uniform LDS broadcasts).  Each chunk's applied weight leaves as
-// bf16 for the apply kernel.
-constexpr int kRecurRows = 16;
-constexpr int kLdg = kD + 4;  // fp32 row stride of G in LDS
-__global__ __launch_bounds__(kThreads) void lact_recur_kernel(const LactJob j) {
-    __shared__ float Gl[kD * kLdg];         // G_b [dk][dk]
-    __shared__ float Wr[kRecurRows * kD];   // rows r0 .. r0+15 of W_b
-    const int bh = blockIdx.x / (kD / kRecurRows);
-    const int r0 = (blockIdx.x % (kD / kRecurRows)) * kRecurRows;
-    const int tid = threadIdx.x;
-    const int col = tid & (kD - 1), rg = 8 * (tid >> 7);  // rows rg .. rg+7 of the block
+// Chunk-by-chunk recursion of one head, W_{b+1} = W_b + F_b - W_b G_b.  W stays
+// in float32 registers (wave w: rows 32w .. 32w+31, four 32x32 accumulator
+// tiles); W G runs on the bf16 MFMA in split form (W_hi G_hi + W_hi G_lo +
+// W_lo G_hi, ~16 significant bits per operand) from LDS copies of W (rows) and
+// G^T (rows = G's columns), rewritten every chunk.  Each chunk's applied weight
+// leaves as bf16 for the apply kernel.
+constexpr int kLdr = kD + 8;  // bf16 row stride of the LDS operand copies
+__global__ __launch_bounds__(kThreads, 1) void lact_recur_kernel(const LactJob j) {
+    __shared__ uint16_t Wh[kD * kLdr], Wl[kD * kLdr];    // W_b rows, split
+    __shared__ uint16_t Gh[kD * kLdr], Gl[kD * kLdr];    // G_b^T rows, split
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
     const int nch = (j.T + j.chunk - 1) / j.chunk;
-    const size_t wbase = ((size_t)bh * kD + r0) * kD;   // this block's rows in [BH][dv][dk]
-    for (int x = tid; x < kRecurRows * kD; x += kThreads) Wr[x] = j.W0 ? j.W0[wbase + x] : 0.f;
-    auto store_use = [&](int cb) {  // rows of the applied weight, bf16
-        uint16_t* dst = j.ws_wuse + ((size_t)(bh * nch + cb) * kD + r0) * kD;
-        for (int x = tid; x < kRecurRows * kD; x += kThreads) dst[x] = f32_to_bf16(Wr[x]);
+    const size_t wbase = (size_t)bh * kD * kD;
+    // element e of tile J of this lane: row 32w + row(e), column 32J + l32
+    auto row = [&](int e) { return 32 * w + 8 * (e >> 2) + 4 * hh + (e & 3); };
+    f32x16 W[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) W[J][e] = j.W0 ? j.W0[wbase + (size_t)row(e) * kD + 32 * J + l32] : 0.f;
+    auto split_store = [&]() {  // W -> Wh, Wl (and its bf16 rounding to the applied weight)
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint16_t hi = f32_to_bf16(W[J][e]);
+                Wh[row(e) * kLdr + 32 * J + l32] = hi;
+                Wl[row(e) * kLdr + 32 * J + l32] = f32_to_bf16(W[J][e] - bf16_to_f32(hi));
+            }
     };
+    auto store_use = [&](int cb) {  // Wh (W rounded to bf16) -> applied weight of chunk cb
+        uint16_t* dst = j.ws_wuse + (size_t)(bh * nch + cb) * kD * kD;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = (tid >> 4) + 16 * i;
+            *reinterpret_cast<uint4*>(dst + r * kD + 8 * (tid & 15)) =
+                *reinterpret_cast<const uint4*>(&Wh[r * kLdr + 8 * (tid & 15)]);
+        }
+    };
+    split_store();
     for (int cb = 0; cb < nch; ++cb) {
         const float* st = j.ws_stats + (size_t)(bh * nch + cb) * j.nsplit * 2 * kD * kD;
-        __syncthreads();  // Wr holds W_b
-        {
-            // G_b: 16 float4 per thread, every load of a split in flight at once
-            f32x4 gv[16];
+        __syncthreads();  // previous chunk's operand reads done; Wh/Wl of W_b complete
+        if (j.order == 1) store_use(cb);
+        // G_b summed over the splits, transposed into Gh/Gl: thread moves 16
+        // float4 of G, four at a time (their loads in flight together)
+#pragma unroll 1
+        for (int i0 = 0; i0 < 16; i0 += 4) {
+            f32x4 gv[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) gv[i] = *reinterpret_cast<const f32x4*>(st + 4 * (tid + kThreads * i));
+            for (int i = 0; i < 4; ++i) gv[i] = *reinterpret_cast<const f32x4*>(st + 4 * (tid + kThreads * (i0 + i)));
             for (int s = 1; s < j.nsplit; ++s) {
                 const float* sp = st + (size_t)s * 2 * kD * kD;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) gv[i] += *reinterpret_cast<const f32x4*>(sp + 4 * (tid + kThreads * i));
+                for (int i = 0; i < 4; ++i) gv[i] += *reinterpret_cast<const f32x4*>(sp + 4 * (tid + kThreads * (i0 + i)));
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int x = 4 * (tid + kThreads * i);
-                *reinterpret_cast<f32x4*>(&Gl[(x >> 7) * kLdg + (x & 127)]) = gv[i];
+            for (int i = 0; i < 4; ++i) {
+                const int x = 4 * (tid + kThreads * (i0 + i)), kr = x >> 7, n0 = x & 127;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint16_t hi = f32_to_bf16(gv[i][c]);
+                    Gh[(n0 + c) * kLdr + kr] = hi;
+                    Gl[(n0 + c) * kLdr + kr] = f32_to_bf16(gv[i][c] - bf16_to_f32(hi));
+                }
             }
-        }
-        if (j.order == 1) store_use(cb);
-        __syncthreads();
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < kD; k += 4) {
-            float g4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) g4[i] = Gl[(k + i) * kLdg + col];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const f32x4 w4 = *reinterpret_cast<const f32x4*>(&Wr[(rg + r) * kD + k]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[r] += w4[i] * g4[i];
-            }
-        }
-        __syncthreads();  // every read of W_b done
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int row = rg + r;
-            float fsum = 0.f;
-            for (int s = 0; s < j.nsplit; ++s)
-                fsum += st[(size_t)s * 2 * kD * kD + kD * kD + (size_t)(r0 + row) * kD + col];
-            Wr[row * kD + col] += fsum - acc[r];
         }
         __syncthreads();
-        if (j.order == 0) store_use(cb);
+        // C = W G: A = W rows, B[k][n] = G[k][n] = G^T row n
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            f32x16 c = {};
+            const uint16_t* ah = &Wh[(32 * w + l32) * kLdr + 8 * hh];
+            const uint16_t* al = &Wl[(32 * w + l32) * kLdr + 8 * hh];
+            const uint16_t* bhp = &Gh[(32 * J + l32) * kLdr + 8 * hh];
+            const uint16_t* blp = &Gl[(32 * J + l32) * kLdr + 8 * hh];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 a_h = *reinterpret_cast<const bf16x8*>(ah + 16 * kk);
+                const bf16x8 a_l = *reinterpret_cast<const bf16x8*>(al + 16 * kk);
+                const bf16x8 b_h = *reinterpret_cast<const bf16x8*>(bhp + 16 * kk);
+                const bf16x8 b_l = *reinterpret_cast<const bf16x8*>(blp + 16 * kk);
+                c = mfma32(a_h, b_h, c);
+                c = mfma32(a_h, b_l, c);
+                c = mfma32(a_l, b_h, c);
+            }
+            // W + F - W G in the accumulator layout
+            const float* fp = st + kD * kD;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const size_t fi = (size_t)row(e) * kD + 32 * J + l32;
+                float fsum = fp[fi];
+                for (int s = 1; s < j.nsplit; ++s) fsum += fp[(size_t)s * 2 * kD * kD + fi];
+                W[J][e] += fsum - c[e];
+            }
+        }
+        __syncthreads();  // every read of the old Wh/Wl done
+        split_store();
+        if (j.order == 0) {
+            __syncthreads();
+            store_use(cb);
+        }
     }
-    __syncthreads();
-    if (j.WT)
-        for (int x = tid; x < kRecurRows * kD; x += kThreads) j.WT[wbase + x] = Wr[x];
+    if (j.WT) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) j.WT[wbase + (size_t)row(e) * kD + 32 * J + l32] = W[J][e];
+    }
 }
 
 // O = Q W_use^T for 256 tokens of one head (four tiles of 64 in one chunk):
@@ -319,8 +374,9 @@ __global__ __launch_bounds__(kThreads, 2) void lact_apply_kernel(const LactJob j
     __shared__ uint16_t Os[kTok * kLdo];
     constexpr int kSpan = kApplyTiles * kTok;
     const int spans = (j.T + kSpan - 1) / kSpan;
-    const int bh = blockIdx.x / spans;
-    const int s0 = (blockIdx.x - bh * spans) * kSpan;
+    int bh, sp;
+    unit_part(blockIdx.x, j.BH, spans, bh, sp);  // a head's spans share its weights via L2
+    const int s0 = sp * kSpan;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
@@ -410,7 +466,7 @@ hipError_t launch_lact(int dtype, LactJob j, void* workspace, hipStream_t stream
                        stream, j);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lact_recur_kernel, dim3((unsigned)j.BH * (kD / kRecurRows)), dim3(kThreads), 0, stream, j);
+    hipLaunchKernelGGL(lact_recur_kernel, dim3((unsigned)j.BH), dim3(kThreads), 0, stream, j);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lact_apply_kernel, dim3((unsigned)((size_t)j.BH * ((j.T + kApplyTiles * kTok - 1) / (kApplyTiles * kTok)))),
