@@ -25,7 +25,7 @@ _CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-p
            "-std=c11", "-Wall", "-Wextra"]
 _lib = None
 
-GDN, GLA, GDN_EW = 0, 1, 2
+GDN, GLA, GDN_EW, GDN_DIAG, GLA_DIAG = 0, 1, 2, 3, 4
 
 
 def build(force: bool = True) -> str:
@@ -76,6 +76,10 @@ def _mode(mode) -> int:
         return GLA
     if mode in (GDN_EW, "gdn_ew"):
         return GDN_EW
+    if mode in (GDN_DIAG, "gdn_diag"):
+        return GDN_DIAG
+    if mode in (GLA_DIAG, "gla_diag"):
+        return GLA_DIAG
     raise ValueError(f"unknown mode {mode!r}")
 
 
@@ -83,9 +87,10 @@ def scan(mode, q, k, v, alpha, beta=None, S0=None, threads: int | None = None,
          store_o: bool = True, return_threads: bool = False):
     """Token-by-token scan in float64.
 
-    q, k: [..., T, dk]; v: [..., T, dv]; alpha: [..., T]; beta: [..., T] for
-    "gdn", None for "gla", [2, ..., T] (erase strengths, then write strengths)
-    for "gdn_ew"; S0: [..., dv, dk] or None (zero).  Leading dimensions are
+    q, k: [..., T, dk]; v: [..., T, dv]; alpha: [..., T], or [..., T, dk] (one
+    decay per key channel) for "gdn_diag" and "gla_diag"; beta: [..., T] for
+    "gdn" and "gdn_diag", None for "gla" and "gla_diag", [2, ..., T] (erase
+    strengths, then write strengths) for "gdn_ew"; S0: [..., dv, dk] or None (zero).  Leading dimensions are
     independent heads.  Inputs are taken as float32 (exact for bfloat16
     values), S0 as float64.
     Returns (o [..., T, dv] float64 or None, ST [..., dv, dk] float64).
@@ -96,13 +101,15 @@ def scan(mode, q, k, v, alpha, beta=None, S0=None, threads: int | None = None,
     T, dk = q.shape[-2:]
     dv = v.shape[-1]
     BH = int(np.prod(lead)) if lead else 1
-    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or alpha.shape != q.shape[:-1]:
+    diag = m in (GDN_DIAG, GLA_DIAG)
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or \
+            alpha.shape != (q.shape if diag else q.shape[:-1]):
         raise ValueError("shape mismatch among q, k, v, alpha")
-    if m != GLA:
+    if m not in (GLA, GLA_DIAG):
         if beta is None:
             raise ValueError("gdn modes need beta")
         beta = _f32(beta)
-        if beta.shape != ((2, *alpha.shape) if m == GDN_EW else alpha.shape):
+        if beta.shape != ((2, *q.shape[:-1]) if m == GDN_EW else q.shape[:-1]):
             raise ValueError("beta shape mismatch")
     else:
         beta = None
@@ -123,7 +130,8 @@ def scan(mode, q, k, v, alpha, beta=None, S0=None, threads: int | None = None,
 def decode_step(mode, q, k, v, alpha, beta, S, threads: int | None = None):
     """One token per state, S ([N, dv, dk] float64, C-contiguous) updated in place.
 
-    beta: [N] ("gdn"), None ("gla") or [2, N] ("gdn_ew": erase, write).
+    alpha: [N], or [N, dk] for "gdn_diag" and "gla_diag"; beta: [N] ("gdn",
+    "gdn_diag"), None ("gla", "gla_diag") or [2, N] ("gdn_ew": erase, write).
     Returns o [N, dv] float64 = S_new q.
     """
     m = _mode(mode)
@@ -134,7 +142,9 @@ def decode_step(mode, q, k, v, alpha, beta, S, threads: int | None = None):
     dv = v.shape[1]
     if S.shape != (N, dv, dk):
         raise ValueError("S shape mismatch")
-    if m != GLA:
+    if alpha.shape != ((N, dk) if m in (GDN_DIAG, GLA_DIAG) else (N,)):
+        raise ValueError("alpha shape mismatch")
+    if m not in (GLA, GLA_DIAG):
         beta = _f32(beta)
         if beta.shape != ((2, N) if m == GDN_EW else (N,)):
             raise ValueError("beta shape mismatch")

@@ -20,6 +20,13 @@
  *   operator stays the Gated-DeltaNet rank-1 form while the write is free; a
  *   token with alpha = 1, be = 0 is a pure write, which is how PRISM's rank-L
  *   corrections enter the scan)
+ * gated delta rule with a diagonal gate (mode 3):
+ *                             E_t = diag(a_t) (I - beta_t k_t k_t^T),
+ *                             f_t = beta_t v_t k_t^T
+ * gated linear attention with a diagonal gate (mode 4):
+ *                             E_t = diag(a_t),  f_t = v_t k_t^T
+ *   (the prefix-scan notes, key design 2, list the diagonal gate among the
+ *   forms E_t takes; a_t holds one decay per key channel)
  *
  * Sources:
  *  - "Sequential Parallel Duality in Prefix Scannable Models" (papernotes.org
@@ -46,6 +53,8 @@
  *   S_ij <- alpha (S_ij - beta a_i k_j) + beta v_i k_j      [gdn]
  *   S_ij <- alpha S_ij + v_i k_j                            [gla]
  *   S_ij <- alpha (S_ij - be a_i k_j) + bw v_i k_j          [gdn, split strengths]
+ *   X_ij  = a_j S_ij;  S_ij <- X_ij - beta (X k)_i k_j + beta v_i k_j   [gdn, diagonal gate]
+ *   S_ij <- a_j S_ij + v_i k_j                              [gla, diagonal gate]
  *   o_i   = sum_j S_ij q_j                       (row of S_t q_t)
  * Inputs arrive as float32 (bfloat16 inputs are exact in float32) and are
  * widened exactly to float64.  Rows of S are independent, so work is split over
@@ -59,7 +68,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_GDN = 0, ORACLE_GLA = 1, ORACLE_GDN_EW = 2 };
+enum { ORACLE_GDN = 0, ORACLE_GLA = 1, ORACLE_GDN_EW = 2, ORACLE_GDN_DIAG = 3, ORACLE_GLA_DIAG = 4 };
 
 typedef struct {
     int mode;
@@ -91,14 +100,25 @@ static int run_rows(const job_t *J, int64_t h, int r0, int r1)
         const float *qt = J->q + tok * dk;
         const float *kt = J->k + tok * dk;
         const float *vt = J->v + tok * dv;
-        const double al = (double)J->alpha[tok];
+        const int diag = J->mode == ORACLE_GDN_DIAG || J->mode == ORACLE_GLA_DIAG;
+        const double al = diag ? 0.0 : (double)J->alpha[tok];
+        const float *ad = diag ? J->alpha + tok * dk : NULL;   /* per-key-channel decay */
         /* erase and write strengths; mode 2 reads them from two planes of BH*T */
-        const double be = J->mode != ORACLE_GLA ? (double)J->beta[tok] : 0.0;
+        const double be = (J->mode != ORACLE_GLA && J->mode != ORACLE_GLA_DIAG) ? (double)J->beta[tok] : 0.0;
         const double bw = J->mode == ORACLE_GDN_EW ? (double)J->beta[(size_t)(J->BH * T) + tok] : be;
         for (int r = 0; r < nrows; ++r) {
             double *Si = S + (size_t)r * dk;
             const double vi = (double)vt[r0 + r];
-            if (J->mode != ORACLE_GLA) {
+            if (diag) {
+                for (int j = 0; j < dk; ++j) Si[j] *= (double)ad[j];
+                if (J->mode == ORACLE_GDN_DIAG) {
+                    double a = 0.0;
+                    for (int j = 0; j < dk; ++j) a += Si[j] * (double)kt[j];
+                    for (int j = 0; j < dk; ++j) Si[j] = Si[j] - be * a * (double)kt[j] + be * vi * (double)kt[j];
+                } else {
+                    for (int j = 0; j < dk; ++j) Si[j] += vi * (double)kt[j];
+                }
+            } else if (J->mode != ORACLE_GLA) {
                 double a = 0.0;
                 for (int j = 0; j < dk; ++j) a += Si[j] * (double)kt[j];
                 for (int j = 0; j < dk; ++j)
@@ -136,8 +156,8 @@ static void *worker(void *arg)
 /*
  * Full-sequence scan of BH independent heads.
  *   q, k: [BH, T, dk] float32     v: [BH, T, dv] float32
- *   alpha: [BH, T] float32
- *   beta: [BH, T] float32 (mode 0); ignored, may be NULL (mode 1); [2, BH, T]
+ *   alpha: [BH, T] float32; [BH, T, dk] float32 (modes 3, 4: one decay per key channel)
+ *   beta: [BH, T] float32 (modes 0, 3); ignored, may be NULL (modes 1, 4); [2, BH, T]
  *         float32 (mode 2: erase strengths, then write strengths)
  *   S0: [BH, dv, dk] float64 or NULL (zero state)
  *   o:  [BH, T, dv] float64 or NULL (not stored; still computed)
@@ -150,10 +170,9 @@ int oracle_scan_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
                     const float *alpha, const float *beta, const double *S0,
                     double *o, double *ST, int nthreads)
 {
-    if ((mode != ORACLE_GDN && mode != ORACLE_GLA && mode != ORACLE_GDN_EW) || BH < 0 || T < 0 ||
-        dk <= 0 || dv <= 0)
+    if (mode < ORACLE_GDN || mode > ORACLE_GLA_DIAG || BH < 0 || T < 0 || dk <= 0 || dv <= 0)
         return -1;
-    if (mode != ORACLE_GLA && !beta && BH * T > 0) return -1;
+    if (mode != ORACLE_GLA && mode != ORACLE_GLA_DIAG && !beta && BH * T > 0) return -1;
     if (BH * T > 0 && (!q || !k || !v || !alpha)) return -1;
     if (nthreads < 1) nthreads = 1;
 
@@ -185,7 +204,8 @@ int oracle_scan_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
 
 /*
  * One token for each of N independent states, state updated in place:
- *   q, k: [N, dk]   v: [N, dv]   alpha: [N]   beta: [N] ([2, N] in mode 2)
+ *   q, k: [N, dk]   v: [N, dv]   alpha: [N] ([N, dk] in modes 3, 4)
+ *   beta: [N] ([2, N] in mode 2)
  *   S: [N, dv, dk] float64
  *   o: [N, dv] float64 = S_new q
  * Same arithmetic as oracle_scan_f64 with T = 1 (the per-token update of the
