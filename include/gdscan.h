@@ -14,6 +14,14 @@
  *                                      E_t = alpha_t (I - be_t k_t k_t^T),
  *                                      f_t = bw_t v_t k_t^T
  *
+ *   SCAN_GDN_DIAG (gated delta rule, diagonal gate):
+ *                                      E_t = diag(a_t) (I - beta_t k_t k_t^T),
+ *                                      f_t = beta_t v_t k_t^T
+ *   SCAN_GLA_DIAG (gated linear attention, diagonal gate):
+ *                                      E_t = diag(a_t),  f_t = v_t k_t^T
+ *   with a_t one decay per key channel (the prefix-scan notes, key design 2,
+ *   list the diagonal gate among the forms of E_t).
+ *
  * SCAN_GDN_EW is PRISM's write-forget decoupling ("PRISM: Parallel Residual
  * Iterative Sequence Model", gist.science explainer, technical summary 2.1:
  * the forget operator stays the Gated-DeltaNet rank-1 form, the write is
@@ -62,6 +70,8 @@ extern "C" {
 #define SCAN_GDN 0
 #define SCAN_GLA 1
 #define SCAN_GDN_EW 2
+#define SCAN_GDN_DIAG 3
+#define SCAN_GLA_DIAG 4
 
 /* element type of q, k, v and o (alpha, beta and all states are float32) */
 #define SCAN_F32 0
@@ -100,8 +110,10 @@ size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk,
  * out from its exclusive prefix state).
  *
  *   q, k : [B, H, T, dk]  dtype          v, o : [B, H, T, dv]  dtype
- *   alpha: [B, H, T] float32 in (0, 1]
- *   beta : [B, H, T] float32 for SCAN_GDN; must be NULL for SCAN_GLA;
+ *   alpha: [B, H, T] float32 in (0, 1]; [B, H, T, dk] for SCAN_GDN_DIAG and
+ *          SCAN_GLA_DIAG (16-byte aligned), one decay per key channel
+ *   beta : [B, H, T] float32 for SCAN_GDN and SCAN_GDN_DIAG; NULL for SCAN_GLA and
+ *          SCAN_GLA_DIAG;
  *          [2, B, H, T] float32 for SCAN_GDN_EW (plane 0: erase strengths be,
  *          plane 1: write strengths bw)
  *   S0   : [B, H, dv, dk] float32 initial state, or NULL for the zero state
@@ -117,7 +129,10 @@ size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk,
  *          Reusable across calls that are ordered on one stream.
  * Supported: dtype SCAN_BF16 with dk = dv = 128 (chunk 64 on the fast path;
  * chunk 16/32 and other sizes take the float32 kernel); dtype SCAN_F32 with
- * dk, dv in {16, 32, 64, 128}.  T >= 1; B, H >= 1.
+ * dk, dv in {16, 32, 64, 128}.  T >= 1; B, H >= 1.  The diagonal-gate modes
+ * run a float32 chunk kernel on the sequential path (its own 32-token chunks;
+ * `chunk` is validated but the result does not depend on it) for either dtype
+ * with dk in {16, 32, 64, 128} and dv a multiple of 16.
  * Returns SCAN_OK or an error status (see above).
  */
 int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
@@ -133,8 +148,9 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
  *   S <- S E + f,   o = S q   (with the updated S)
  *
  *   q, k : [N, dk] dtype     v, o : [N, dv] dtype
- *   alpha: [N] float32       beta : [N] float32 (SCAN_GDN), NULL (SCAN_GLA) or
- *                            [2, N] float32 (SCAN_GDN_EW: erase, then write)
+ *   alpha: [N] float32 ([N, dk] with diagonal gates)
+ *   beta : [N] float32 (SCAN_GDN, SCAN_GDN_DIAG), NULL (SCAN_GLA, SCAN_GLA_DIAG)
+ *          or [2, N] float32 (SCAN_GDN_EW: erase, then write)
  *   S    : [N, dv, dk] float32, read and written in place
  * Supported: dk in {16, 32, 64, 128}, dv >= 1, either dtype.
  * o must not overlap any input or S.  Returns SCAN_OK or an error status.

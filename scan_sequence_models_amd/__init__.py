@@ -8,7 +8,8 @@ sources in ``csrc/``); this package is its Python binding.  The library is
 loaded on first use.
 """
 from ._lib import (  # noqa: F401
-    PATHS, SCAN_BF16, SCAN_F32, SCAN_GDN, SCAN_GDN_EW, SCAN_GLA, ScanError, decode_step,
+    PATHS, SCAN_BF16, SCAN_F32, SCAN_GDN, SCAN_GDN_DIAG, SCAN_GDN_EW, SCAN_GLA, SCAN_GLA_DIAG,
+    ScanError, decode_step,
     last_error, lact_fwd, lact_fwd_workspace_size, lib, prism_expand, prism_scan_fwd, scan_fwd,
     scan_fwd_workspace_size, version,
 )

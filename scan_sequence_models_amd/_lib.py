@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdscan.s
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "gdscan.h")
 
-SCAN_GDN, SCAN_GLA, SCAN_GDN_EW = 0, 1, 2
+SCAN_GDN, SCAN_GLA, SCAN_GDN_EW, SCAN_GDN_DIAG, SCAN_GLA_DIAG = 0, 1, 2, 3, 4
 SCAN_F32, SCAN_BF16 = 0, 1
 SCAN_OK, SCAN_EINVAL, SCAN_EUNSUPPORTED, SCAN_EWORKSPACE, SCAN_EALIGN, SCAN_EHIP = range(6)
 PATHS = {"auto": 0, "sequential": 1, "blelloch": 2}
@@ -133,7 +133,9 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
     ``beta is None`` selects gated linear attention (E = alpha I, f = v k^T),
     a [B, H, T] ``beta`` the gated delta rule, and a [2, B, H, T] ``beta``
     (erase strengths, then write strengths) the gated delta rule with split
-    strengths (SCAN_GDN_EW).  ``S0=None`` is the zero state.  ``ST`` may
+    strengths (SCAN_GDN_EW).  A [B, H, T, dk] ``alpha`` (one decay per key
+    channel) selects the diagonal-gate modes (SCAN_GDN_DIAG with beta,
+    SCAN_GLA_DIAG without).  ``S0=None`` is the zero state.  ``ST`` may
     be ``S0`` itself (in-place carry).  ``write_state=False`` skips S_T.
     """
     _need(q, "q")
@@ -145,8 +147,12 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
     dv = v.shape[-1]
     _need(k, "k", dt, (B, H, T, dk), dev)
     _need(v, "v", dt, (B, H, T, dv), dev)
-    _need(alpha, "alpha", torch.float32, (B, H, T), dev)
-    mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 4 else SCAN_GDN
+    diag = alpha.dim() == 4
+    _need(alpha, "alpha", torch.float32, (B, H, T, dk) if diag else (B, H, T), dev)
+    if diag:
+        mode = SCAN_GLA_DIAG if beta is None else SCAN_GDN_DIAG
+    else:
+        mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 4 else SCAN_GDN
     if beta is not None:
         _need(beta, "beta", torch.float32, (2, B, H, T) if mode == SCAN_GDN_EW else (B, H, T), dev)
     if S0 is not None:
@@ -178,7 +184,7 @@ def decode_step(q, k, v, alpha, beta, S, o=None):
     """One token per state: S [N, dv, dk] float32 updated in place; returns o [N, dv].
 
     ``beta is None`` selects gated linear attention; a [2, N] ``beta`` (erase,
-    write) the split-strength mode.
+    write) the split-strength mode; an [N, dk] ``alpha`` the diagonal gates.
     """
     _need(q, "q")
     dev, dt = q.device, q.dtype
@@ -188,8 +194,12 @@ def decode_step(q, k, v, alpha, beta, S, o=None):
     dv = v.shape[-1]
     _need(k, "k", dt, (N, dk), dev)
     _need(v, "v", dt, (N, dv), dev)
-    _need(alpha, "alpha", torch.float32, (N,), dev)
-    mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 2 else SCAN_GDN
+    diag = alpha.dim() == 2
+    _need(alpha, "alpha", torch.float32, (N, dk) if diag else (N,), dev)
+    if diag:
+        mode = SCAN_GLA_DIAG if beta is None else SCAN_GDN_DIAG
+    else:
+        mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 2 else SCAN_GDN
     if beta is not None:
         _need(beta, "beta", torch.float32, (2, N) if mode == SCAN_GDN_EW else (N,), dev)
     _need(S, "S", torch.float32, (N, dv, dk), dev)

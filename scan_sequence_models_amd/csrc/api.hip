@@ -57,20 +57,27 @@ int device_cus() {
 struct Plan {
     int path;          // SCAN_PATH_SEQUENTIAL or SCAN_PATH_BLELLOCH
     bool mfma;         // bf16 MFMA kernel (else float32 kernel)
+    bool diag;         // diagonal-gate kernel
     int leaf_chunks;   // Blelloch leaf size in chunks
     size_t workspace;  // bytes
 };
 
-bool valid_mode(int mode) { return mode == SCAN_GDN || mode == SCAN_GLA || mode == SCAN_GDN_EW; }
+bool valid_mode(int mode) {
+    return mode == SCAN_GDN || mode == SCAN_GLA || mode == SCAN_GDN_EW || mode == SCAN_GDN_DIAG ||
+           mode == SCAN_GLA_DIAG;
+}
+bool diag_mode(int mode) { return mode == SCAN_GDN_DIAG || mode == SCAN_GLA_DIAG; }
+bool gla_mode(int mode) { return mode == SCAN_GLA || mode == SCAN_GLA_DIAG; }
 // Kernel mode: 0 = gated delta rule (erase and write strengths may differ), 1 = GLA.
-int kernel_mode(int mode) { return mode == SCAN_GLA ? 1 : 0; }
+int kernel_mode(int mode) { return gla_mode(mode) ? 1 : 0; }
 // Elements of the beta argument per token: 1, none (GLA), or 2 planes (split strengths).
-int beta_planes(int mode) { return mode == SCAN_GLA ? 0 : mode == SCAN_GDN_EW ? 2 : 1; }
+int beta_planes(int mode) { return gla_mode(mode) ? 0 : mode == SCAN_GDN_EW ? 2 : 1; }
 
 // Validates the sizes/enums of a scan_fwd call and picks the kernels.
 int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
               const scan_opts* opts, Plan* plan) {
-    if (!valid_mode(mode)) return fail(SCAN_EINVAL, "mode must be SCAN_GDN, SCAN_GLA or SCAN_GDN_EW (got %d)", mode);
+    if (!valid_mode(mode))
+        return fail(SCAN_EINVAL, "mode must be SCAN_GDN, SCAN_GLA, SCAN_GDN_EW, SCAN_GDN_DIAG or SCAN_GLA_DIAG (got %d)", mode);
     const int km = kernel_mode(mode);
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
     if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
@@ -84,6 +91,15 @@ int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chun
     if (leaf < 0 || (leaf & (leaf - 1)) != 0) return fail(SCAN_EINVAL, "opts->leaf_chunks must be 0 or a power of two (got %d)", leaf);
 
     Plan p{};
+    if (diag_mode(mode)) {  // float32 chunk kernel with per-channel gates, sequential path only
+        if (!gds::chunk_diag_supported(dk, dv))
+            return fail(SCAN_EUNSUPPORTED, "diagonal gates support dk in {16,32,64,128} and dv a multiple of 16 (got dk=%d dv=%d)", dk, dv);
+        if (path == SCAN_PATH_BLELLOCH) return fail(SCAN_EUNSUPPORTED, "diagonal gates run on the sequential path only");
+        p.diag = true;
+        p.path = SCAN_PATH_SEQUENTIAL;
+        *plan = p;
+        return SCAN_OK;
+    }
     p.mfma = dtype == SCAN_BF16 && gds::chunk_mfma_supported(km, dk, dv, chunk);
     if (!p.mfma && !gds::chunk_f32_supported(km, dk, dv, chunk))
         return fail(SCAN_EUNSUPPORTED, "unsupported size: dk=%d dv=%d chunk=%d (dk in {16,32,64,128}, dv a multiple of 16)", dk, dv, chunk);
@@ -140,13 +156,14 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     int st = plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p);
     if (st != SCAN_OK) return st;
     if (!q || !k || !v || !alpha || !o) return fail(SCAN_EINVAL, "q, k, v, alpha and o must be non-null");
-    if (mode != SCAN_GLA && !beta) return fail(SCAN_EINVAL, "SCAN_GDN and SCAN_GDN_EW need beta");
-    if (mode == SCAN_GLA && beta) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta (pass NULL)");
+    if (!gla_mode(mode) && !beta) return fail(SCAN_EINVAL, "the gated-delta modes need beta");
+    if (gla_mode(mode) && beta) return fail(SCAN_EINVAL, "the GLA modes take no beta (pass NULL)");
     const void* a16[] = {q, k, v, o, S0, ST};
     const char* n16[] = {"q", "k", "v", "o", "S0", "ST"};
     for (int i = 0; i < 6; ++i)
         if (a16[i] && !aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
-    if (!aligned(alpha, 4) || (beta && !aligned(beta, 4))) return fail(SCAN_EALIGN, "alpha/beta not 4-byte aligned");
+    if (!aligned(alpha, diag_mode(mode) ? 16 : 4) || (beta && !aligned(beta, 4)))
+        return fail(SCAN_EALIGN, "alpha/beta not aligned (alpha 16 bytes with diagonal gates, else 4)");
     if (p.workspace > 0) {
         if (!workspace || workspace_bytes < p.workspace)
             return fail(SCAN_EWORKSPACE, "workspace of %zu bytes required (got %zu)", p.workspace, workspace_bytes);
@@ -155,7 +172,8 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     const size_t es = dtype == SCAN_BF16 ? 2 : 4;
     const size_t BH = (size_t)B * H;
     const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
-                        range("v", v, BH * T * dv * es), range("alpha", alpha, BH * T * 4),
+                        range("v", v, BH * T * dv * es),
+                        range("alpha", alpha, BH * T * 4 * (diag_mode(mode) ? dk : 1)),
                         range("beta", beta, BH * T * 4 * beta_planes(mode)),
                         range("S0", S0, BH * dv * dk * 4),
                         range("workspace", workspace, p.workspace)};
@@ -173,7 +191,9 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     // split strengths: the write plane follows the erase plane
     const float* beta_w = mode == SCAN_GDN_EW ? beta + BH * T : beta;
     hipError_t e;
-    if (p.path == SCAN_PATH_BLELLOCH) {
+    if (p.diag) {
+        e = gds::launch_chunk_diag(km, dtype, (int)BH, T, dk, dv, q, k, v, alpha, beta, S0, o, ST, s);
+    } else if (p.path == SCAN_PATH_BLELLOCH) {
         e = gds::launch_blelloch(km, (int)BH, T, dk, dv, chunk, p.leaf_chunks, q, k, v, alpha, beta,
                                  beta_w, S0, o, ST, workspace, s);
     } else if (p.mfma) {
@@ -190,22 +210,25 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
 int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const void* k,
                 const void* v, const float* alpha, const float* beta, float* S, void* o,
                 void* stream) {
-    if (!valid_mode(mode)) return fail(SCAN_EINVAL, "mode must be SCAN_GDN, SCAN_GLA or SCAN_GDN_EW (got %d)", mode);
+    if (!valid_mode(mode))
+        return fail(SCAN_EINVAL, "mode must be SCAN_GDN, SCAN_GLA, SCAN_GDN_EW, SCAN_GDN_DIAG or SCAN_GLA_DIAG (got %d)", mode);
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
     if (N < 1 || dk < 1 || dv < 1) return fail(SCAN_EINVAL, "N, dk, dv must be >= 1 (got %d, %d, %d)", N, dk, dv);
     if (!gds::decode_supported(dk)) return fail(SCAN_EUNSUPPORTED, "decode_step supports dk in {16,32,64,128} (got %d)", dk);
     if ((int64_t)N * ((dv + 127) / 128) > INT32_MAX) return fail(SCAN_EINVAL, "N*dv too large");
     if (!q || !k || !v || !alpha || !S || !o) return fail(SCAN_EINVAL, "q, k, v, alpha, S and o must be non-null");
-    if (mode != SCAN_GLA && !beta) return fail(SCAN_EINVAL, "SCAN_GDN and SCAN_GDN_EW need beta");
-    if (mode == SCAN_GLA && beta) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta (pass NULL)");
+    if (!gla_mode(mode) && !beta) return fail(SCAN_EINVAL, "the gated-delta modes need beta");
+    if (gla_mode(mode) && beta) return fail(SCAN_EINVAL, "the GLA modes take no beta (pass NULL)");
     const void* a16[] = {q, k, v, o, S};
     const char* n16[] = {"q", "k", "v", "o", "S"};
     for (int i = 0; i < 5; ++i)
         if (!aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
-    if (!aligned(alpha, 4) || (beta && !aligned(beta, 4))) return fail(SCAN_EALIGN, "alpha/beta not 4-byte aligned");
+    if (!aligned(alpha, diag_mode(mode) ? 16 : 4) || (beta && !aligned(beta, 4)))
+        return fail(SCAN_EALIGN, "alpha/beta not aligned (alpha 16 bytes with diagonal gates, else 4)");
     const size_t es = dtype == SCAN_BF16 ? 2 : 4;
     const Range in[] = {range("q", q, (size_t)N * dk * es), range("k", k, (size_t)N * dk * es),
-                        range("v", v, (size_t)N * dv * es), range("alpha", alpha, (size_t)N * 4),
+                        range("v", v, (size_t)N * dv * es),
+                        range("alpha", alpha, (size_t)N * 4 * (diag_mode(mode) ? dk : 1)),
                         range("beta", beta, (size_t)N * 4 * beta_planes(mode)),
                         range("S", S, (size_t)N * dv * dk * 4)};
     const Range ro = range("o", o, (size_t)N * dv * es);
@@ -215,8 +238,9 @@ int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const
     for (int i = 0; i < 5; ++i)
         if (overlaps(rS, in[i])) return fail(SCAN_EINVAL, "S overlaps %s", in[i].name);
     const float* beta_w = mode == SCAN_GDN_EW ? beta + N : beta;
-    hipError_t e = gds::launch_decode(kernel_mode(mode), dtype, N, dk, dv, q, k, v, alpha, beta, beta_w,
-                                      S, o, static_cast<hipStream_t>(stream));
+    const int dmode = kernel_mode(mode) + (diag_mode(mode) ? 2 : 0);
+    hipError_t e = gds::launch_decode(dmode, dtype, N, dk, dv, q, k, v, alpha, beta, beta_w, S, o,
+                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode_step launch");
     return SCAN_OK;
 }

@@ -5,6 +5,7 @@
 // papernotes.org notes, key design 1; constant-size state, key design 2).  Per
 // state S (dv x dk, fp32, in place) and token (q, k, v, alpha, beta):
 //
+//   (diagonal gates: S <- S diag(a) first, then alpha = 1 below)
 //   a = S k,  b = S q                         (row dot products of the old S)
 //   gdn: u = beta_w v - beta alpha a      gla: u = v
 //   (beta_w, the write strength, is beta unless erase and write are split)
@@ -28,7 +29,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 128;
 
-template <int DK, int MODE, typename E>
+template <int DK, int MODE, bool DIAG, typename E>
 __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks,
                                                           const E* __restrict__ q,
                                                           const E* __restrict__ k,
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
     }
     const float4 k4 = io<E>::load4(k, (size_t)n * DK + sub * 4);
     const float4 q4 = io<E>::load4(q, (size_t)n * DK + sub * 4);
-    const float al = alpha[n];
+    const float al = DIAG ? 1.f : alpha[n];
     const float be = MODE == 0 ? beta[n] : 0.f;
     const float bw = MODE == 0 ? beta_w[n] : 0.f;
     float vr[kPasses];
@@ -72,6 +73,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(int dv, int row_blocks
     for (int p = 0; p < kPasses; ++p)
         vr[p] = io<E>::load(v, (size_t)n * dv + (rows[p] < dv ? rows[p] : dv - 1));
     const float kq = group_sum<L>(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
+    if constexpr (DIAG) {  // per-key-channel decay of the state before the update reads it
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(alpha + (size_t)n * DK + sub * 4);
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) s[p] *= a4;
+    }
 
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -96,6 +102,8 @@ template <int DK, typename E>
 hipError_t launch_typed(int mode, int N, int dv, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const float* beta_w, float* S, void* o,
                         hipStream_t stream) {
+    // mode: 0 gated delta rule, 1 gated linear attention, 2 and 3 the same with
+    // diagonal gates (alpha holds dk decays per state)
     const int rb = (dv + kRowsPerBlock - 1) / kRowsPerBlock;
     const dim3 grid((unsigned)((size_t)N * rb));
     const E* qq = static_cast<const E*>(q);
@@ -103,10 +111,16 @@ hipError_t launch_typed(int mode, int N, int dv, const void* q, const void* k, c
     const E* vv = static_cast<const E*>(v);
     E* oo = static_cast<E*>(o);
     if (mode == 0)
-        hipLaunchKernelGGL((decode_kernel<DK, 0, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
+        hipLaunchKernelGGL((decode_kernel<DK, 0, false, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
+                           kk, vv, alpha, beta, beta_w, S, oo);
+    else if (mode == 1)
+        hipLaunchKernelGGL((decode_kernel<DK, 1, false, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
+                           kk, vv, alpha, beta, beta_w, S, oo);
+    else if (mode == 2)
+        hipLaunchKernelGGL((decode_kernel<DK, 0, true, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
                            kk, vv, alpha, beta, beta_w, S, oo);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, 1, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
+        hipLaunchKernelGGL((decode_kernel<DK, 1, true, E>), grid, dim3(kThreads), 0, stream, dv, rb, qq,
                            kk, vv, alpha, beta, beta_w, S, oo);
     return hipGetLastError();
 }

@@ -13,8 +13,10 @@ namespace gds {
 
 // decode.hip -------------------------------------------------------------
 bool decode_supported(int dk);
-// beta_w: write strengths (the gated delta rule's f_t = beta_w v k^T); equal to
-// beta except for split erase/write strengths.  Ignored in mode 1.
+// mode: 0 gated delta rule, 1 gated linear attention, 2 / 3 the same with
+// diagonal gates (alpha [N, dk]).  beta_w: write strengths (the gated delta
+// rule's f_t = beta_w v k^T); equal to beta except for split erase/write
+// strengths.  Ignored in modes 1 and 3.
 hipError_t launch_decode(int mode, int dtype, int N, int dk, int dv, const void* q,
                          const void* k, const void* v, const float* alpha, const float* beta,
                          const float* beta_w, float* S, void* o, hipStream_t stream);
@@ -25,6 +27,13 @@ hipError_t launch_chunk_f32(int mode, int dtype, int BH, int T, int dk, int dv, 
                             const void* q, const void* k, const void* v, const float* alpha,
                             const float* beta, const float* beta_w, const float* S0, void* o,
                             float* ST, hipStream_t stream);
+
+// chunk_diag.hip -- float32 chunkwise kernel with diagonal (per-key-channel) gates
+// (mode 0: gated delta rule, 1: gated linear attention; alpha is [BH, T, dk])
+bool chunk_diag_supported(int dk, int dv);
+hipError_t launch_chunk_diag(int mode, int dtype, int BH, int T, int dk, int dv, const void* q,
+                             const void* k, const void* v, const float* alpha, const float* beta,
+                             const float* S0, void* o, float* ST, hipStream_t stream);
 
 // chunk_bf16.hip -- bfloat16 MFMA chunkwise kernel ---------------------------
 // (dk = dv = 128, chunk 64; q, k, v, o bfloat16; states float32)

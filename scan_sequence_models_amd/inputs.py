@@ -17,6 +17,10 @@ Decode workloads draw each state ``n`` from ``SeedSequence([seed, n])``: the
 initial state first, then all steps' q, k, v, alpha and beta (see
 ``decode_state_inputs``).
 
+Diagonal-gate workloads (``diag_gates``) replace alpha by one decay per key
+channel, [T, dk] from the alpha distribution, drawn from
+``SeedSequence([seed, b, h, 4])``.
+
 Fast-weight workloads (mode "lact") use q, k, v and S0 (as W0) of the recipe
 above and draw learning rates ~ U(0, 1) dk / chunk from
 ``SeedSequence([seed, b, h, 3])``.
@@ -123,6 +127,7 @@ class Workload:
     steps: int = 0       # decode workloads only: number of consecutive tokens
     prism_steps: int = 0   # PRISM workloads: L rank-1 corrections per token
     prism_window: int = 4  # PRISM workloads: taps W of the anchor convolution
+    diag_gates: bool = False  # alpha is one decay per key channel ([T, dk])
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -158,6 +163,13 @@ WORKLOADS = {
                                       "bf16", 2048, ("const", 1.0), None, 0.01, seed=8),
     "tiny-lact": Workload("tiny-lact", "lact", 1, 2, 100, 16, 16, "f32", 16, ("const", 1.0),
                           None, 0.01, seed=9),
+    # Diagonal (per-key-channel) gates: the training shape with alpha drawn per
+    # channel from the gated-delta distribution
+    "gdn-diag-b8h16t8192": Workload("gdn-diag-b8h16t8192", "gdn", 8, 16, 8192, 128, 128, "bf16",
+                                    64, ("sigmoid_normal", 3.0, 1.0), ("sigmoid_normal", 0.0, 1.0),
+                                    0.01, seed=10, diag_gates=True),
+    "tiny-gla-diag": Workload("tiny-gla-diag", "gla", 1, 2, 77, 16, 16, "f32", 16,
+                              ("uniform", 0.8, 1.0), None, 0.01, seed=11, diag_gates=True),
 }
 
 
@@ -320,3 +332,12 @@ def lact_eta(w: Workload, b: int, h: int, T: int | None = None) -> np.ndarray:
     T = w.T if T is None else T
     rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 3]))
     return cast(rng.uniform(0.0, 1.0, T) * w.dk / w.chunk, "f32")
+
+
+def diag_alpha(w: Workload, b: int, h: int, T: int | None = None) -> np.ndarray:
+    """Per-key-channel decays [T, dk] of head (b, h) for a diagonal-gate workload,
+    drawn from the workload's alpha distribution, float32, from
+    ``SeedSequence([seed, b, h, 4])``."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 4]))
+    return cast(_draw_gate(rng, w.alpha, T * w.dk).reshape(T, w.dk), "f32")

@@ -65,6 +65,14 @@ def _scan(lib, mode=0, dtype=1, B=1, H=2, T=64, dk=128, dv=128, chunk=64, q=FAKE
     # an output starting 768 bytes after beta overlaps its write plane (with
     # one plane counted it would not)
     (dict(mode=2, o=FAKE + 4 * STEP + 768), L.SCAN_EINVAL),
+    (dict(mode=3, beta=None), L.SCAN_EINVAL),
+    (dict(mode=4), L.SCAN_EINVAL),                    # diagonal gla takes no beta
+    (dict(mode=3, alpha=FAKE + 3 * STEP + 8), L.SCAN_EALIGN),
+    (dict(mode=3, opts=_opts(path=2)), L.SCAN_EUNSUPPORTED),   # sequential path only
+    (dict(mode=3, dk=96), L.SCAN_EUNSUPPORTED),
+    # per-channel alpha is B*H*T*dk floats (64 KB here): o 32 KB after its start
+    # overlaps it (a scalar alpha would end at 512 bytes)
+    (dict(mode=3, o=FAKE + 3 * STEP + 32768), L.SCAN_EINVAL),
 ])
 def test_scan_fwd_rejects(lib, kw, code):
     assert _scan(lib, **kw) == code
@@ -88,8 +96,12 @@ def _decode(lib, mode=0, dtype=1, N=4, dk=128, dv=128, q=FAKE, k=FAKE + STEP, v=
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(mode=3), L.SCAN_EINVAL),
+    (dict(mode=7), L.SCAN_EINVAL),
     (dict(mode=2, beta=None), L.SCAN_EINVAL),
+    (dict(mode=3, beta=None), L.SCAN_EINVAL),               # diagonal gdn needs beta
+    (dict(mode=4), L.SCAN_EINVAL),                          # diagonal gla takes no beta
+    (dict(mode=3, alpha=FAKE + 3 * STEP + 4), L.SCAN_EALIGN),  # per-channel alpha: 16 bytes
+    (dict(mode=3, o=FAKE + 3 * STEP + 1024), L.SCAN_EINVAL),   # o inside alpha [N, dk] (2 KB)
     (dict(mode=2, o=FAKE + 4 * STEP + 16), L.SCAN_EINVAL),  # o inside beta's write plane
     (dict(N=0), L.SCAN_EINVAL),
     (dict(dk=96), L.SCAN_EUNSUPPORTED),
