@@ -14,7 +14,8 @@ long-b2h8t262144 (the long-sequence path), decode-4096x100 (decode_step over
 4096 states, one timed step per token), prism-b8h16t8192-l2 (the PRISM layer:
 prism_expand, then the split-strength scan of the 3x longer element stream) and
 lact-b8h16t8192-m2048 (lact_fwd: the large-chunk fast-weight update, chunks of
-2048 tokens).  Timing: W untimed steps (by default
+2048 tokens) and gdn-diag-b8h16t8192 (the gated delta rule with one decay per
+key channel).  Timing: W untimed steps (by default
 enough to cover the GPU's clock ramp), then two HIP events around K back-to-back
 steps on the launch stream.
 """
@@ -120,9 +121,13 @@ def cpu_baseline(w, heads: int):
     st = lambda f: None if getattr(hs[0], f) is None else np.stack([getattr(x, f) for x in hs])  # noqa: E731
     q, k, v, a, be, S0 = st("q"), st("k"), st("v"), st("alpha"), st("beta"), st("S0")
     S0 = None if S0 is None else S0.astype(np.float64)
+    mode = w.mode
+    if w.diag_gates:
+        a = np.stack([I.diag_alpha(w, b, h) for b, h in sel])
+        mode = w.mode + "_diag"
     oracle.build(force=False)
     t0 = time.perf_counter()
-    _, _, threads = oracle.scan(w.mode, q, k, v, a, be, S0, return_threads=True)
+    _, _, threads = oracle.scan(mode, q, k, v, a, be, S0, return_threads=True)
     sec = time.perf_counter() - t0
     head_tokens = len(sel) * w.T
     return {
@@ -631,6 +636,9 @@ def main():
 
     log(f"bench: generating {w.name} (B={w.B} H={w.H} T={w.T} d={w.dk})")
     b = I.batch_inputs(w, threads=16)
+    if w.diag_gates:  # one decay per key channel replaces the scalar alpha
+        b.alpha = np.stack([np.stack([I.diag_alpha(w, bb, hh) for hh in range(w.H)])
+                            for bb in range(w.B)])
 
     def up(x, bf16=False):
         t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
@@ -645,6 +653,8 @@ def main():
     o = torch.empty((w.B, w.H, w.T, w.dv), dtype=q.dtype, device=dev)
     ST = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
     mode = gds.SCAN_GDN if w.mode == "gdn" else gds.SCAN_GLA
+    if w.diag_gates:
+        mode = gds.SCAN_GDN_DIAG if w.mode == "gdn" else gds.SCAN_GLA_DIAG
     dcode = gds.SCAN_BF16 if bf else gds.SCAN_F32
     path = args.path if args.path != "auto" else w.path if w.path == "blelloch" else "auto"
     ws_bytes = gds.scan_fwd_workspace_size(mode, dcode, w.B, w.H, w.T, w.dk, w.dv, w.chunk, path,
@@ -670,14 +680,17 @@ def main():
     log(f"bench: {args.steps} steps back to back, span {span_ms:.3f} ms "
         f"({kern_ms:.4f} ms per step), wall {wall * 1e3:.1f} ms")
 
-    alg_bytes = scan_bytes(w)
+    alg_bytes = scan_bytes(w) + (w.B * w.H * w.T * (w.dk - 1) * 4 if w.diag_gates else 0)
     flops = scan_flops(w)
     flops_alg = scan_flops_alg(w)
     achieved_gbs = alg_bytes / (kern_ms / 1e3) / 1e9
     achieved_tfs = flops / (kern_ms / 1e3) / 1e12
     kernel_src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_bf16.hip")
     traffic = None
-    if path != "blelloch" and w.dk == 128 and w.chunk == 64 and bf:
+    if w.diag_gates:
+        kernel_src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_diag.hip")
+        traffic = measured_traffic(kernel_src, f"chunk_diag_{w.name}_traffic.txt")
+    elif path != "blelloch" and w.dk == 128 and w.chunk == 64 and bf:
         traffic = measured_traffic(kernel_src, f"chunk_mfma_{w.name}_traffic.txt")
     result = {
         "metric": METRIC,
@@ -702,7 +715,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "chunk_mfma_kernel" if path != "blelloch" else "blelloch path (all kernels)",
+            "kernel": ("chunk_diag_kernel" if w.diag_gates else
+                       "chunk_mfma_kernel" if path != "blelloch" else "blelloch path (all kernels)"),
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_ms": kern_ms,
         },
