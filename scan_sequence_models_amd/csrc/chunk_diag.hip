@@ -169,6 +169,265 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
         for (int x = tid; x < SL * DK; x += kThreads) ST[s_base + x] = Ss[x];
 }
 
+// The same chunk algorithm with its products on the float32 MFMA
+// (v_mfma_f32_32x32x2f32, fp32 accuracy) for slices of 64 value rows and
+// dk >= 32.  Per chunk:
+//   1. q, k, log2 a and the value slice come in; log2 a is summed along the
+//      chunk per channel;
+//   2. the decayed Gram A and scores P over the 496 strictly lower token pairs
+//      (one exp2 per pair and channel, float4 loads along the channels; the
+//      diagonal of P needs no exponential), and the scaled copies q gamma,
+//      -beta k gamma and k e^{g_C - g};
+//   3. T = (I + A)^-1 by one wave (a lane per column, forward substitution with
+//      the rows of A read as float4), beside X = R_v - R_w S^T and the start of
+//      O = (Q gamma) S^T on the other three waves;
+//   4. U = T X, then O += P U beside the state update
+//      S <- S diag(gamma_C) + U^T (K e^{g_C - g}), all as 32x32 tiles.
+// U = T (R_v - R_w S^T) is the same product as T R_v - (T R_w) S^T, grouped so
+// that the key-long product does not wait for the inverse.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma2(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+constexpr int kSL = 64;      // value rows per workgroup
+constexpr int kLT = kC + 4;  // row stride of the 32x32 T and P tiles (float4 rows)
+constexpr int kPairs = kC * (kC - 1) / 2;
+
+template <int MODE, int DK, typename E>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_diag_mfma_kernel(
+    int T, int dv, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
+    E* __restrict__ o, float* __restrict__ ST) {
+    constexpr bool GDN = MODE == 0;
+    constexpr int NJ = DK / 32;  // 32-column tiles of a key-wide row
+    // Row strides.  The Gram reads float4 runs of channels with one token per
+    // lane: a stride of DK + 4 keeps those 16-byte loads aligned and spreads
+    // eight consecutive lanes over distinct bank groups.  The MFMA operands
+    // read one float per lane down a column: an odd stride (DK + 1) puts the
+    // 32 lanes into 32 banks.
+    constexpr int L4 = DK + 4;
+    constexpr int L1 = DK + 1;
+    __shared__ __align__(16) float Qs[kC * L4];  // q
+    __shared__ __align__(16) float Ks[kC * L4];  // k
+    __shared__ __align__(16) float Gs[kC * L4];  // cumulative log2 decay
+    __shared__ float Qg[kC * L1];                // q * gamma
+    __shared__ float Kt[kC * L1];                // k * e^{g_C - g}
+    __shared__ float Rw[GDN ? kC * L1 : 1];      // -beta (k * gamma)
+    __shared__ float Us[kC * kSL];               // v slice (GDN: beta v), then U
+    __shared__ __align__(16) float Am[GDN ? kC * kC : 1];  // A (strictly lower)
+    __shared__ float Tm[GDN ? kC * kLT : 1];
+    __shared__ float Pm[kC * kLT];               // P (lower, inclusive; zero above)
+    __shared__ float Ss[kSL * L1];               // state slice
+    __shared__ float Ob[GDN ? 16 * 64 : 1];      // a partial O tile (accumulator layout)
+    __shared__ float bet[kC];
+
+    const int slices = dv / kSL;
+    const int bh = blockIdx.x / slices;
+    const int r0 = (blockIdx.x - bh * slices) * kSL;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, kg = lane >> 5;
+    const size_t qk_base = (size_t)bh * T * DK;
+    const size_t v_base = (size_t)bh * T * dv;
+    const size_t s_base = ((size_t)bh * dv + r0) * DK;
+    // accumulator element e of a 32x32 tile: row 8 (e / 4) + 4 kg + e % 4, column l32
+    auto row = [&](int e) { return 8 * (e >> 2) + 4 * kg + (e & 3); };
+
+    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = S0 ? S0[s_base + x] : 0.f;
+    for (int x = tid; x < kC * kLT; x += kThreads) Pm[x] = 0.f;
+
+    const int nchunks = (T + kC - 1) / kC;
+    for (int n = 0; n < nchunks; ++n) {
+        const int c0 = n * kC;
+        __syncthreads();  // the previous chunk is done with every array
+        for (int x = tid; x < kC * DK; x += kThreads) {
+            const int t = x / DK, y = t * L4 + x % DK;
+            const bool in = c0 + t < T;  // past T: identity tokens (a = 1, beta = 0, q = k = v = 0)
+            const size_t gi = qk_base + (size_t)c0 * DK + x;
+            Qs[y] = in ? io<E>::load(q, gi) : 0.f;
+            Ks[y] = in ? io<E>::load(k, gi) : 0.f;
+            Gs[y] = in ? __log2f(alpha[gi]) : 0.f;
+        }
+        if (tid < kC) bet[tid] = (GDN && c0 + tid < T) ? beta[(size_t)bh * T + c0 + tid] : 0.f;
+        __syncthreads();
+        for (int x = tid; x < kC * kSL; x += kThreads) {
+            const int t = x / kSL, i = x - t * kSL;
+            const float vv = c0 + t < T ? io<E>::load(v, v_base + (size_t)(c0 + t) * dv + r0 + i) : 0.f;
+            Us[x] = GDN ? bet[t] * vv : vv;
+        }
+        for (int c = tid; c < DK; c += kThreads) {
+            float run = 0.f;
+#pragma unroll 8
+            for (int t = 0; t < kC; ++t) {
+                run += Gs[t * L4 + c];
+                Gs[t * L4 + c] = run;
+            }
+        }
+        __syncthreads();
+        // decayed Gram and scores over the strictly lower pairs s < t
+        for (int p = tid; p < kPairs; p += kThreads) {
+            int t = (int)((1.f + __builtin_sqrtf(1.f + 8.f * (float)p)) * 0.5f);
+            if (t * (t - 1) / 2 > p) --t;
+            if (t * (t + 1) / 2 <= p) ++t;
+            const int s = p - t * (t - 1) / 2;
+            const float4* gt = reinterpret_cast<const float4*>(Gs + t * L4);
+            const float4* gs = reinterpret_cast<const float4*>(Gs + s * L4);
+            const float4* kt = reinterpret_cast<const float4*>(Ks + t * L4);
+            const float4* ksv = reinterpret_cast<const float4*>(Ks + s * L4);
+            const float4* qt = reinterpret_cast<const float4*>(Qs + t * L4);
+            float pa = 0.f, pp = 0.f;
+#pragma unroll 4
+            for (int c = 0; c < DK / 4; ++c) {
+                const float4 g1 = gt[c], g0 = gs[c], k0 = ksv[c], q1 = qt[c];
+                const float e0 = __builtin_amdgcn_exp2f(g1.x - g0.x) * k0.x;
+                const float e1 = __builtin_amdgcn_exp2f(g1.y - g0.y) * k0.y;
+                const float e2 = __builtin_amdgcn_exp2f(g1.z - g0.z) * k0.z;
+                const float e3 = __builtin_amdgcn_exp2f(g1.w - g0.w) * k0.w;
+                pp += q1.x * e0 + q1.y * e1 + q1.z * e2 + q1.w * e3;
+                if constexpr (GDN) {
+                    const float4 k1 = kt[c];
+                    pa += k1.x * e0 + k1.y * e1 + k1.z * e2 + k1.w * e3;
+                }
+            }
+            if constexpr (GDN) Am[t * kC + s] = bet[t] * pa;
+            Pm[t * kLT + s] = pp;
+        }
+        if (tid < kC) {  // diagonal of P: q_t . k_t
+            float pp = 0.f;
+            for (int c = 0; c < DK; ++c) pp += Qs[tid * L4 + c] * Ks[tid * L4 + c];
+            Pm[tid * kLT + tid] = pp;
+        }
+        for (int x = tid; x < kC * DK; x += kThreads) {
+            const int t = x / DK, c = x - t * DK, y = t * L4 + c, z = t * L1 + c;
+            const float g = Gs[y];
+            const float gam = __builtin_amdgcn_exp2f(g);
+            Qg[z] = Qs[y] * gam;
+            Kt[z] = Ks[y] * __builtin_amdgcn_exp2f(Gs[(kC - 1) * L4 + c] - g);
+            if constexpr (GDN) Rw[z] = -(bet[t] * Ks[y] * gam);
+        }
+        __syncthreads();
+        // c += A B^T over key steps [k0, k1), A and B both read along key rows
+        // (A: 32 token rows, B: 32 state rows, row stride L1)
+        auto rows_dot = [&](const float* A, const float* B, int k0, int k1, f32x16 c) {
+            for (int ks = k0; ks < k1; ++ks) c = mfma2(A[l32 * L1 + 2 * ks + kg], B[l32 * L1 + 2 * ks + kg], c);
+            return c;
+        };
+        // c += P U or T X on value columns 32 I ..: B read along token rows of Us
+        auto tok_dot = [&](const float* A, int I, f32x16 c) {
+#pragma unroll
+            for (int ks = 0; ks < kC / 2; ++ks)
+                c = mfma2(A[l32 * kLT + 2 * ks + kg], Us[(2 * ks + kg) * kSL + 32 * I + l32], c);
+            return c;
+        };
+        auto store_o = [&](int I, const f32x16& c) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                if (c0 + t < T) io<E>::store(o, v_base + (size_t)(c0 + t) * dv + r0 + 32 * I + l32, c[e]);
+            }
+        };
+        if constexpr (GDN) {
+            // U = T (R_v - R_w S^T) = T X.  Phase A: wave 0 inverts I + A while
+            // waves 1 and 2 form X in place of R_v (value columns 32 (w - 1) ..)
+            // and wave 3 starts O = (Q gamma) S^T on value columns 0 .. 31.
+            f32x16 oacc = {};
+            if (w == 0) {
+                const float4* A4 = reinterpret_cast<const float4*>(Am);
+                float xcol[kC];
+                // row r + 1 of A is in flight while row r is reduced
+                float4 cur[kC / 4], nxt[kC / 4];
+                cur[0] = A4[kC / 4];
+                xcol[0] = l32 == 0 ? 1.f : 0.f;
+#pragma unroll
+                for (int r = 1; r < kC; ++r) {
+                    if (r + 1 < kC) {
+                        // the offset is tied to the previous row's result, so
+                        // these loads issue after it and one row ahead of use
+                        int off = (r + 1) * (kC / 4);
+                        asm volatile("" : "+v"(off) : "v"(xcol[r - 1]));
+#pragma unroll
+                        for (int m = 0; m < (r + 4) / 4; ++m) nxt[m] = A4[off + m];
+                    }
+                    float acc = r == l32 ? 1.f : 0.f;
+#pragma unroll
+                    for (int j = 0; j < r; ++j) {
+                        const float4 aj = cur[j / 4];
+                        const float av = (j & 3) == 0 ? aj.x : (j & 3) == 1 ? aj.y : (j & 3) == 2 ? aj.z : aj.w;
+                        acc -= av * xcol[j];
+                    }
+                    xcol[r] = acc;
+                    if (r + 1 < kC) {
+#pragma unroll
+                        for (int m = 0; m < (r + 4) / 4; ++m) cur[m] = nxt[m];
+                    }
+                }
+                if (kg == 0) {
+#pragma unroll
+                    for (int r = 0; r < kC; ++r) Tm[r * kLT + l32] = xcol[r];
+                }
+            } else if (w < 3) {
+                const int I = w - 1;
+                f32x16 c;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * kSL + 32 * I + l32];
+                c = rows_dot(Rw, Ss + 32 * I * L1, 0, DK / 2, c);  // Rw holds -beta k gamma
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
+            } else {
+                oacc = rows_dot(Qg, Ss, 0, DK / 2, oacc);
+            }
+            __syncthreads();
+            // Phase B: U = T X (waves 1, 2); waves 0 and 3 share (Q gamma) S^T on
+            // value columns 32 .. 63, one half of the keys each.
+            if (w == 1 || w == 2) {
+                const int I = w - 1;
+                const f32x16 c = tok_dot(Tm, I, f32x16{});
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
+            } else if (w == 0) {
+                oacc = rows_dot(Qg, Ss + 32 * L1, 0, DK / 4, oacc);
+            } else {
+                const f32x16 part = rows_dot(Qg, Ss + 32 * L1, DK / 4, DK / 2, f32x16{});
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Ob[e * 64 + lane] = part[e];
+            }
+            __syncthreads();
+            // Phase C: O += P U (wave 3: columns 0 .. 31, wave 0: 32 .. 63) beside
+            // the state update (no wave reads the old state any more).
+            if (w == 3) {
+                store_o(0, tok_dot(Pm, 0, oacc));
+            } else if (w == 0) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[e] += Ob[e * 64 + lane];
+                store_o(1, tok_dot(Pm, 1, oacc));
+            }
+        } else {
+            // O = (Q gamma) S^T + P V: waves 2, 3 (value columns 32 (w - 2) ..)
+            if (w >= 2) store_o(w - 2, tok_dot(Pm, w - 2, rows_dot(Qg, Ss + 32 * (w - 2) * L1, 0, DK / 2, f32x16{})));
+            __syncthreads();  // every read of the old state done
+        }
+        // S <- S diag(gamma_C) + U^T K~: 2 x NJ tiles; with the delta rule waves
+        // 1 and 2 take most of them (0 and 3 are busy with O)
+        for (int tl = 0; tl < 2 * NJ; ++tl) {
+            const int owner = GDN ? (tl < 2 * NJ - 2 ? 1 + (tl & 1) : (tl == 2 * NJ - 2 ? 0 : 3)) : (tl & 3);
+            if (owner != w) continue;
+            const int I = tl / NJ, J = tl - I * NJ;
+            const float gC = __builtin_amdgcn_exp2f(Gs[(kC - 1) * L4 + 32 * J + l32]);
+            f32x16 c;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L1 + 32 * J + l32] * gC;
+#pragma unroll
+            for (int ks = 0; ks < kC / 2; ++ks)
+                c = mfma2(Us[(2 * ks + kg) * kSL + 32 * I + l32], Kt[(2 * ks + kg) * L1 + 32 * J + l32], c);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * J + l32] = c[e];
+        }
+    }
+    __syncthreads();
+    if (ST)
+        for (int x = tid; x < kSL * DK; x += kThreads) ST[s_base + x] = Ss[x / DK * L1 + x % DK];
+}
+
 template <int MODE, int DK, typename E>
 hipError_t launch_dk(int BH, int T, int dv, const void* q, const void* k, const void* v,
                      const float* alpha, const float* beta, const float* S0, void* o, float* ST,
@@ -177,6 +436,13 @@ hipError_t launch_dk(int BH, int T, int dv, const void* q, const void* k, const 
     const E* kk = static_cast<const E*>(k);
     const E* vv = static_cast<const E*>(v);
     E* oo = static_cast<E*>(o);
+    if constexpr (DK >= 32) {
+        if (dv % kSL == 0) {
+            hipLaunchKernelGGL((chunk_diag_mfma_kernel<MODE, DK, E>), dim3((unsigned)((size_t)BH * (dv / kSL))),
+                               dim3(kThreads), 0, s, T, dv, qq, kk, vv, alpha, beta, S0, oo, ST);
+            return hipGetLastError();
+        }
+    }
     if (dv % 64 == 0) {
         hipLaunchKernelGGL((chunk_diag_kernel<MODE, DK, 64, E>), dim3((unsigned)((size_t)BH * (dv / 64))),
                            dim3(kThreads), 0, s, T, dv, qq, kk, vv, alpha, beta, S0, oo, ST);

@@ -31,6 +31,10 @@ CASES = [
     ("tiny-gla-diag", "gla", 1, 2, 77, 16, 16),
     ("tiny-gla-diag", "gdn", 2, 1, 64, 16, 32),
     ("tiny-gla-diag", "gdn", 1, 2, 100, 64, 64),
+    ("tiny-gla-diag", "gdn", 1, 1, 70, 16, 64),
+    ("tiny-gla-diag", "gdn", 1, 2, 130, 32, 192),
+    ("tiny-gla-diag", "gla", 1, 1, 45, 128, 64),
+    ("tiny-gla-diag", "gdn", 1, 1, 33, 64, 48),
     ("gdn-diag-b8h16t8192", "gdn", 1, 2, 200, 128, 128),
     ("gdn-diag-b8h16t8192", "gla", 1, 2, 97, 128, 128),
 ]
