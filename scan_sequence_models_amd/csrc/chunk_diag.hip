@@ -185,6 +185,8 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 //      S <- S diag(gamma_C) + U^T (K e^{g_C - g}), all as 32x32 tiles.
 // U = T (R_v - R_w S^T) is the same product as T R_v - (T R_w) S^T, grouped so
 // that the key-long product does not wait for the inverse.
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma2(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -236,25 +238,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = S0 ? S0[s_base + x] : 0.f;
     for (int x = tid; x < kC * kLT; x += kThreads) Pm[x] = 0.f;
 
+    // The next chunk's inputs are fetched into registers while this chunk
+    // computes (one wave per SIMD leaves no other way to hide HBM latency).
+    // The loads are unconditional, from a token index clamped into the
+    // sequence, and keep the raw element; masking and conversion happen when
+    // they are written to LDS, so no load waits inside the fetch.
+    constexpr int NQ = kC * DK / kThreads;   // key-wide elements per thread and chunk
+    constexpr int NV = kC * kSL / kThreads;  // value elements per thread and chunk
+    E pq[NQ], pk[NQ], pv[NV];
+    float pa[NQ], pb = 0.f;
+    auto fetch = [&](int cn) {
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int x = tid + m * kThreads, t = min(cn + x / DK, T - 1);
+            const size_t gi = qk_base + (size_t)t * DK + x % DK;
+            pq[m] = q[gi];
+            pk[m] = k[gi];
+            pa[m] = alpha[gi];
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int x = tid + m * kThreads, t = min(cn + x / kSL, T - 1);
+            pv[m] = v[v_base + (size_t)t * dv + r0 + x % kSL];
+        }
+        if (GDN && tid < kC) pb = beta[(size_t)bh * T + min(cn + tid, T - 1)];
+    };
+    fetch(0);
+
     const int nchunks = (T + kC - 1) / kC;
     for (int n = 0; n < nchunks; ++n) {
         const int c0 = n * kC;
         __syncthreads();  // the previous chunk is done with every array
-        for (int x = tid; x < kC * DK; x += kThreads) {
-            const int t = x / DK, y = t * L4 + x % DK;
-            const bool in = c0 + t < T;  // past T: identity tokens (a = 1, beta = 0, q = k = v = 0)
-            const size_t gi = qk_base + (size_t)c0 * DK + x;
-            Qs[y] = in ? io<E>::load(q, gi) : 0.f;
-            Ks[y] = in ? io<E>::load(k, gi) : 0.f;
-            Gs[y] = in ? __log2f(alpha[gi]) : 0.f;
+        // past T: identity tokens (a = 1, beta = 0, q = k = v = 0)
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int x = tid + m * kThreads, y = x / DK * L4 + x % DK;
+            const bool in = c0 + x / DK < T;
+            Qs[y] = in ? to_f32(pq[m]) : 0.f;
+            Ks[y] = in ? to_f32(pk[m]) : 0.f;
+            Gs[y] = in ? __log2f(pa[m]) : 0.f;
         }
-        if (tid < kC) bet[tid] = (GDN && c0 + tid < T) ? beta[(size_t)bh * T + c0 + tid] : 0.f;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int x = tid + m * kThreads;
+            Us[x] = c0 + x / kSL < T ? to_f32(pv[m]) : 0.f;
+        }
+        if (tid < kC) bet[tid] = c0 + tid < T ? pb : 0.f;
+        if (n + 1 < nchunks) fetch(c0 + kC);
         __syncthreads();
-        for (int x = tid; x < kC * kSL; x += kThreads) {
-            const int t = x / kSL, i = x - t * kSL;
-            const float vv = c0 + t < T ? io<E>::load(v, v_base + (size_t)(c0 + t) * dv + r0 + i) : 0.f;
-            Us[x] = GDN ? bet[t] * vv : vv;
-        }
+        if constexpr (GDN)
+            for (int x = tid; x < kC * kSL; x += kThreads) Us[x] *= bet[x / kSL];
         for (int c = tid; c < DK; c += kThreads) {
             float run = 0.f;
 #pragma unroll 8
@@ -292,10 +325,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             if constexpr (GDN) Am[t * kC + s] = bet[t] * pa;
             Pm[t * kLT + s] = pp;
         }
-        if (tid < kC) {  // diagonal of P: q_t . k_t
+        if (tid < 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
+            const int t = tid >> 2, part = tid & 3;
+            const float4* qa = reinterpret_cast<const float4*>(Qs + t * L4) + part * (DK / 16);
+            const float4* ka = reinterpret_cast<const float4*>(Ks + t * L4) + part * (DK / 16);
             float pp = 0.f;
-            for (int c = 0; c < DK; ++c) pp += Qs[tid * L4 + c] * Ks[tid * L4 + c];
-            Pm[tid * kLT + tid] = pp;
+#pragma unroll
+            for (int c = 0; c < DK / 16; ++c) {
+                const float4 a = qa[c], b = ka[c];
+                pp += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+            }
+            pp += dpp_move<0xB1>(pp);  // lane ^ 1
+            pp += dpp_move<0x4E>(pp);  // lane ^ 2
+            if (part == 0) Pm[t * kLT + t] = pp;
         }
         for (int x = tid; x < kC * DK; x += kThreads) {
             const int t = x / DK, c = x - t * DK, y = t * L4 + c, z = t * L1 + c;
