@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tokens/s fwd gated-delta scan (H=16,d=128,T=8192); % MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFS = 157.3   # MI355X dense fp32 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -71,6 +72,18 @@ def scan_flops_alg(w) -> float:
     C, d = w.chunk, w.dk
     per = (5 * C * d + 6 * d * d + C * C / 3) if w.mode == "gdn" else (2 * C * d + 4 * d * d)
     return per * w.B * w.H * w.T
+
+
+def diag_mfma_flops(w) -> float:
+    """Executed float32 MFMA flops of one diagonal-gate call: per 32-token chunk
+    and 64-row value slice, X = R_v - R_w S^T and (Q gamma) S^T (2 * 32 * 64 * dk
+    each), T X and P U (2 * 32 * 64 * 32 each) and the state update
+    (2 * 64 * dk * 32); the linear-attention mode has no X and no T X.  The
+    decayed Gram and scores (one exp2 per token pair and channel) run on the
+    vector ALUs and are not counted."""
+    C, S, d = 32, 64, w.dk
+    per = 2 * C * S * (3 * d + 2 * C) if w.mode == "gdn" else 2 * C * S * (2 * d + C)
+    return per * -(-w.T // C) * (w.dv // S) * w.B * w.H
 
 
 def source_sha(path: str) -> str:
@@ -708,6 +721,44 @@ def main():
         "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "T": w.T,
                    "dk": w.dk, "dv": w.dv, "chunk": w.chunk, "path": path,
                    "io_dtype": w.dtype, "state_dtype": "f32"},
+    }
+    if w.diag_gates:
+        # float32 kernel: its products run on the fp32 MFMA, whose floor
+        # (about 0.8 ms here) lies above the HBM floor (about 0.2 ms)
+        dflops = diag_mfma_flops(w)
+        dtfs = dflops / (kern_ms / 1e3) / 1e12
+        result["dtype"] = "f32"
+        result["config"]["io_dtype"] = w.dtype
+        result["roofline"] = {
+            "bound": "mfma",
+            "achieved": dtfs,
+            "peak": FP32_MFMA_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": dtfs / FP32_MFMA_PEAK_TFS,
+            "traffic": traffic,
+            "kernel": "chunk_diag_mfma_kernel",
+            "flops_per_launch": dflops,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "hbm_achieved_gbs": achieved_gbs,
+            "hbm_frac": achieved_gbs / HBM_PEAK_GBS,
+            "kernel_ms": kern_ms,
+        }
+        result["head_tokens_per_s"] = w.B * w.H * w.T / (ms_per_step / 1e3)
+    else:
+        result.update(plain_scan_rooflines(path, achieved_gbs, traffic, alg_bytes, kern_ms,
+                                           achieved_tfs, flops, flops_alg))
+        result["head_tokens_per_s"] = w.B * w.H * w.T / (ms_per_step / 1e3)
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle on {args.cpu_heads} heads")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def plain_scan_rooflines(path, achieved_gbs, traffic, alg_bytes, kern_ms, achieved_tfs, flops, flops_alg):
+    """The roofline and MFMA blocks of a scalar-gate scan line."""
+    return {
         "roofline": {
             "bound": "hbm",
             "achieved": achieved_gbs,
@@ -715,8 +766,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": ("chunk_diag_kernel" if w.diag_gates else
-                       "chunk_mfma_kernel" if path != "blelloch" else "blelloch path (all kernels)"),
+            "kernel": "chunk_mfma_kernel" if path != "blelloch" else "blelloch path (all kernels)",
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_ms": kern_ms,
         },
@@ -730,14 +780,7 @@ def main():
             "alg_frac": flops_alg / (kern_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
             "alg_flops_per_launch": flops_alg,
         },
-        "head_tokens_per_s": w.B * w.H * w.T / (ms_per_step / 1e3),
     }
-    if not args.no_cpu_baseline:
-        log(f"bench: timing the CPU oracle on {args.cpu_heads} heads")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
-    else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
