@@ -5,10 +5,11 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 (``scan_sequence_models_amd``) and never imports it; the GPU library never
 imports this package.
 
-``oracle.c`` holds the arithmetic (the token-by-token recurrence, see its
-header for the passages it follows); this module compiles it with gcc and
-marshals numpy arrays.  Every function here is pinned by the CPU tests in
-``tests/test_oracle_pins.py``.
+``oracle.c`` holds the arithmetic (the token-by-token recurrence and its
+reverse-mode gradient, see its comments for the passages they follow); this
+module compiles it with gcc and marshals numpy arrays.  The functions here are
+pinned by the CPU tests in ``tests/test_oracle_pins.py``,
+``tests/test_oracle_diag.py`` and ``tests/test_oracle_bwd.py``.
 """
 from __future__ import annotations
 
@@ -50,6 +51,9 @@ def _load():
         lib.oracle_decode_f64.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                           p, p, p, p, p, p, p, ctypes.c_int]
         lib.oracle_decode_f64.restype = ctypes.c_int
+        lib.oracle_scan_bwd_f64.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.c_int] + [p] * 14 + [ctypes.c_int]
+        lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -156,6 +160,58 @@ def decode_step(mode, q, k, v, alpha, beta, S, threads: int | None = None):
     if n < 0:
         raise RuntimeError("oracle_decode_f64 failed")
     return o
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def scan_bwd(mode, q, k, v, alpha, beta=None, S0=None, dO=None, dST=None,
+             threads: int | None = None):
+    """Gradients of L = sum <dO, o> + <dST, S_T> of ``scan`` with respect to
+    every input, in float64 (inputs are taken as float64, unrounded).
+
+    Shapes as in ``scan`` (modes "gdn", "gla", "gdn_diag", "gla_diag"); dO like
+    o ([..., T, dv]) or None (zero), dST like S_T or None (zero).
+    Returns (dq, dk, dv, dalpha, dbeta or None, dS0).
+    """
+    m = _mode(mode)
+    if m == GDN_EW:
+        raise ValueError("scan_bwd covers modes gdn, gla, gdn_diag, gla_diag")
+    q, k, v, alpha = _f64(q), _f64(k), _f64(v), _f64(alpha)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    diag = m in (GDN_DIAG, GLA_DIAG)
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or \
+            alpha.shape != (q.shape if diag else q.shape[:-1]):
+        raise ValueError("shape mismatch among q, k, v, alpha")
+    delta = m in (GDN, GDN_DIAG)
+    if delta:
+        beta = _f64(beta)
+        if beta is None or beta.shape != q.shape[:-1]:
+            raise ValueError("beta shape mismatch")
+    else:
+        beta = None
+    S0, dO, dST = _f64(S0), _f64(dO), _f64(dST)
+    if S0 is not None and S0.shape != (*lead, dv, dk):
+        raise ValueError("S0 shape mismatch")
+    if dO is not None and dO.shape != v.shape:
+        raise ValueError("dO shape mismatch")
+    if dST is not None and dST.shape != (*lead, dv, dk):
+        raise ValueError("dST shape mismatch")
+    gq, gk, gv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    ga = np.empty_like(alpha)
+    gb = np.empty(q.shape[:-1], np.float64) if delta else None
+    gS0 = np.empty((*lead, dv, dk), np.float64)
+    n = _load().oracle_scan_bwd_f64(m, BH, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                    _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(gq), _ptr(gk),
+                                    _ptr(gv), _ptr(ga), _ptr(gb), _ptr(gS0),
+                                    threads or default_threads())
+    if n < 0:
+        raise RuntimeError("oracle_scan_bwd_f64 failed")
+    return gq, gk, gv, ga, gb, gS0
 
 
 def rel_err_per_head(x, ref, head_dims: int):

@@ -218,3 +218,194 @@ int oracle_decode_f64(int mode, int64_t N, int dk, int dv,
 {
     return oracle_scan_f64(mode, N, 1, dk, dv, q, k, v, alpha, beta, S, o, S, nthreads);
 }
+
+/*
+ * Gradient of the scan (reverse mode through the token recurrence above).
+ *
+ * The loss is L = sum_t <dO_t, o_t> + <dST, S_T>: dO and dST are the gradients
+ * arriving at the outputs.  The prefix-scan notes (key design 1) give the
+ * sequential view, one state update per token; its chain rule, per row i of S
+ * (a row only meets its own v_i, and meets k, q, the gates and the strengths),
+ * is written here with the decay as a vector d_t over key channels (d_t = a_t
+ * for modes 3, 4 and alpha_t in every channel for modes 0, 1):
+ *
+ *   forward   x = d_t * s_{t-1}            (elementwise)
+ *             p = x . k_t
+ *             s_t = x + beta_t (v_ti - p) k_t       [delta rule, modes 0, 3]
+ *             s_t = x + v_ti k_t                    [linear attention, modes 1, 4]
+ *             o_ti = s_t . q_t
+ *   backward  with y the gradient reaching s_t (dST's row at t = T):
+ *             dq_t += dO_ti s_t,   y += dO_ti q_t
+ *             delta rule:  yk = y . k_t
+ *                          dv_ti = beta_t yk
+ *                          dbeta_t += yk (v_ti - p)
+ *                          dk_t += beta_t (v_ti - p) y - beta_t yk x
+ *                          dx = y - beta_t yk k_t
+ *             linear attention:  dv_ti = y . k_t,  dk_t += v_ti y,  dx = y
+ *             dd_t += dx * s_{t-1}  (summed over key channels for a scalar gate)
+ *             y <- dx * d_t        (the gradient reaching s_{t-1})
+ *   and dS0's row is the final y.
+ * The row's states s_0 .. s_T are kept (T + 1 rows of d_k) so that the
+ * backward sweep reads s_{t-1} and s_t as stored.  Rows are taken in order
+ * 0 .. d_v - 1 and the shared gradients (dq, dk, dalpha, dbeta) accumulate in
+ * that order, one thread per head, so results do not depend on thread count.
+ * Modes 0, 1, 3, 4; every input is float64 (no rounding on the way in), so
+ * finite differences of the same function can check it.
+ */
+typedef struct {
+    int mode;
+    int64_t BH, T;
+    int dk, dv;
+    const double *q, *k, *v, *alpha, *beta, *S0, *dO, *dST;
+    double *gq, *gk, *gv, *galpha, *gbeta, *gS0;
+    int64_t next;
+    int failed;
+} bjob_t;
+
+static int bwd_head(const bjob_t *J, int64_t h)
+{
+    const int dk = J->dk, dv = J->dv;
+    const int64_t T = J->T;
+    const int diag = J->mode == ORACLE_GDN_DIAG || J->mode == ORACLE_GLA_DIAG;
+    const int delta = J->mode == ORACLE_GDN || J->mode == ORACLE_GDN_DIAG;
+    const int da = diag ? dk : 1;  /* decay entries per token */
+    double *traj = (double *)malloc(sizeof(double) * (size_t)(T + 1) * (size_t)dk);
+    double *x = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *y = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *dx = (double *)malloc(sizeof(double) * (size_t)dk);
+    if (!traj || !x || !y || !dx) {
+        free(traj); free(x); free(y); free(dx);
+        return -1;
+    }
+    const size_t tok0 = (size_t)(h * T);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < dk; ++j) {
+            J->gq[(tok0 + t) * dk + j] = 0.0;
+            J->gk[(tok0 + t) * dk + j] = 0.0;
+        }
+        for (int j = 0; j < da; ++j) J->galpha[(tok0 + t) * da + j] = 0.0;
+        if (J->gbeta) J->gbeta[tok0 + t] = 0.0;
+    }
+    for (int i = 0; i < dv; ++i) {
+        const size_t srow = ((size_t)h * dv + i) * dk;
+        for (int j = 0; j < dk; ++j) traj[j] = J->S0 ? J->S0[srow + j] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const size_t tok = tok0 + (size_t)t;
+            const double *kt = J->k + tok * dk;
+            const double *s0 = traj + (size_t)t * dk;
+            double *s1 = traj + (size_t)(t + 1) * dk;
+            const double vi = J->v[tok * dv + i];
+            for (int j = 0; j < dk; ++j) x[j] = (diag ? J->alpha[tok * dk + j] : J->alpha[tok]) * s0[j];
+            if (delta) {
+                const double be = J->beta[tok];
+                double p = 0.0;
+                for (int j = 0; j < dk; ++j) p += x[j] * kt[j];
+                for (int j = 0; j < dk; ++j) s1[j] = x[j] + be * (vi - p) * kt[j];
+            } else {
+                for (int j = 0; j < dk; ++j) s1[j] = x[j] + vi * kt[j];
+            }
+        }
+        for (int j = 0; j < dk; ++j) y[j] = J->dST ? J->dST[srow + j] : 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const size_t tok = tok0 + (size_t)t;
+            const double *kt = J->k + tok * dk;
+            const double *qt = J->q + tok * dk;
+            const double *s0 = traj + (size_t)t * dk;
+            const double *s1 = traj + (size_t)(t + 1) * dk;
+            const double vi = J->v[tok * dv + i];
+            const double g = J->dO ? J->dO[tok * dv + i] : 0.0;
+            for (int j = 0; j < dk; ++j) {
+                J->gq[tok * dk + j] += g * s1[j];
+                y[j] += g * qt[j];
+            }
+            for (int j = 0; j < dk; ++j) x[j] = (diag ? J->alpha[tok * dk + j] : J->alpha[tok]) * s0[j];
+            double yk = 0.0;
+            for (int j = 0; j < dk; ++j) yk += y[j] * kt[j];
+            if (delta) {
+                const double be = J->beta[tok];
+                double p = 0.0;
+                for (int j = 0; j < dk; ++j) p += x[j] * kt[j];
+                J->gv[tok * dv + i] = be * yk;
+                J->gbeta[tok] += yk * (vi - p);
+                for (int j = 0; j < dk; ++j) {
+                    J->gk[tok * dk + j] += be * (vi - p) * y[j] - be * yk * x[j];
+                    dx[j] = y[j] - be * yk * kt[j];
+                }
+            } else {
+                J->gv[tok * dv + i] = yk;
+                for (int j = 0; j < dk; ++j) {
+                    J->gk[tok * dk + j] += vi * y[j];
+                    dx[j] = y[j];
+                }
+            }
+            if (diag) {
+                for (int j = 0; j < dk; ++j) J->galpha[tok * dk + j] += dx[j] * s0[j];
+            } else {
+                double acc = 0.0;
+                for (int j = 0; j < dk; ++j) acc += dx[j] * s0[j];
+                J->galpha[tok] += acc;
+            }
+            for (int j = 0; j < dk; ++j) y[j] = dx[j] * (diag ? J->alpha[tok * dk + j] : J->alpha[tok]);
+        }
+        for (int j = 0; j < dk; ++j) J->gS0[srow + j] = y[j];
+    }
+    free(traj); free(x); free(y); free(dx);
+    return 0;
+}
+
+static void *bwd_worker(void *arg)
+{
+    bjob_t *J = (bjob_t *)arg;
+    for (;;) {
+        int64_t h = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+        if (h >= J->BH) break;
+        if (bwd_head(J, h) != 0) __atomic_store_n(&J->failed, 1, __ATOMIC_RELAXED);
+    }
+    return NULL;
+}
+
+/*
+ * Gradients of L = sum <dO, o> + <dST, S_T> with respect to every input.
+ *   q, k: [BH, T, dk]   v: [BH, T, dv]   alpha: [BH, T] ([BH, T, dk] in modes 3, 4)
+ *   beta: [BH, T] (modes 0, 3; NULL in modes 1, 4)   S0: [BH, dv, dk] or NULL (zero)
+ *   dO: [BH, T, dv] or NULL (zero)   dST: [BH, dv, dk] or NULL (zero)
+ *   outputs: gq, gk like q; gv like v; galpha like alpha; gbeta like beta (modes
+ *   0, 3; may be NULL otherwise); gS0 [BH, dv, dk].  All float64.
+ * Returns the number of threads used, or -1 on bad arguments or allocation
+ * failure.
+ */
+int oracle_scan_bwd_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
+                        const double *q, const double *k, const double *v,
+                        const double *alpha, const double *beta, const double *S0,
+                        const double *dO, const double *dST,
+                        double *gq, double *gk, double *gv, double *galpha, double *gbeta,
+                        double *gS0, int nthreads)
+{
+    if (!(mode == ORACLE_GDN || mode == ORACLE_GLA || mode == ORACLE_GDN_DIAG || mode == ORACLE_GLA_DIAG))
+        return -1;
+    if (BH < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
+    const int delta = mode == ORACLE_GDN || mode == ORACLE_GDN_DIAG;
+    if (BH * T > 0 && (!q || !k || !v || !alpha || !gq || !gk || !gv || !galpha)) return -1;
+    if (delta && BH * T > 0 && (!beta || !gbeta)) return -1;
+    if (BH > 0 && !gS0) return -1;
+    if (nthreads < 1) nthreads = 1;
+    bjob_t J;
+    memset(&J, 0, sizeof J);
+    J.mode = mode; J.BH = BH; J.T = T; J.dk = dk; J.dv = dv;
+    J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = delta ? beta : NULL; J.S0 = S0;
+    J.dO = dO; J.dST = dST;
+    J.gq = gq; J.gk = gk; J.gv = gv; J.galpha = galpha; J.gbeta = delta ? gbeta : NULL; J.gS0 = gS0;
+    if (BH == 0) return 1;
+    if ((int64_t)nthreads > BH) nthreads = (int)BH;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) return -1;
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, bwd_worker, &J) != 0) break;
+        ++started;
+    }
+    bwd_worker(&J);
+    for (int i = 1; i <= started; ++i) pthread_join(tid[i], NULL);
+    free(tid);
+    return J.failed ? -1 : started + 1;
+}
