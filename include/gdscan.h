@@ -201,6 +201,35 @@ int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
                  const float *conv, const void *Wk, const void *Wp,
                  void *q2, void *k2, void *v2, float *alpha2, float *beta2, void *stream);
 
+/*
+ * Gradient of scan_fwd (reverse mode through the chunkwise form of the scan;
+ * the prefix-scan notes, key design 2, define the affine state update it
+ * differentiates).  For incoming gradients dO (at o) and dST (at S_T) it
+ * returns the gradients of L = sum <dO, o> + <dST, S_T> with respect to every
+ * input of a SCAN_GDN or SCAN_GLA scan_fwd call with the same arguments:
+ *   q, k : [B, H, T, dk] dtype       v, dO : [B, H, T, dv] dtype (dO NULL: zero)
+ *   alpha: [B, H, T] float32 in (0, 1]    beta: [B, H, T] float32 (SCAN_GDN; NULL for SCAN_GLA)
+ *   S0, dST: [B, H, dv, dk] float32 or NULL (zero)
+ *   dq, dk_out: [B, H, T, dk] float32    dv_out: [B, H, T, dv] float32
+ *   dalpha: [B, H, T] float32        dbeta: [B, H, T] float32 (SCAN_GDN; NULL for SCAN_GLA)
+ *   dS0: [B, H, dv, dk] float32 (the gradient at the initial state, also when S0 is NULL)
+ *   workspace: scan_bwd_workspace_size(...) bytes of device scratch, 256-byte
+ *          aligned (the state entering every 32-token chunk, and per value-slice
+ *          partial sums); reusable across calls ordered on one stream.
+ * All gradients are float32 whatever dtype is.  Outputs may not overlap inputs,
+ * each other or the workspace.  Supported: dk in {32, 64, 128}, dv a multiple of
+ * 64 (at most 4096).  Three kernels run on `stream`: a forward pass storing the
+ * chunk states, the reverse chunk pass, and a reduction over value slices.
+ * Returns SCAN_OK or an error status; scan_bwd_workspace_size returns
+ * (size_t)-1 for invalid or unsupported arguments.
+ */
+size_t scan_bwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk, int dv);
+int scan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv,
+             const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+             const float *S0, const void *dO, const float *dST,
+             float *dq, float *dk_out, float *dv_out, float *dalpha, float *dbeta, float *dS0,
+             void *workspace, size_t workspace_bytes, void *stream);
+
 /* lact_fwd order */
 #define LACT_UPDATE_THEN_APPLY 0  /* chunk b read with W_{b+1}: each token sees its whole chunk */
 #define LACT_APPLY_THEN_UPDATE 1  /* chunk b read with W_b: the mask shifted by one chunk */

@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.lact_fwd_workspace_size.restype = sz
         L.lact_fwd.argtypes = [i] * 8 + [p] * 7 + [p, sz, p]
         L.lact_fwd.restype = i
+        L.scan_bwd_workspace_size.argtypes = [i] * 7
+        L.scan_bwd_workspace_size.restype = sz
+        L.scan_bwd.argtypes = [i] * 7 + [p] * 15 + [sz, p]
+        L.scan_bwd.restype = i
         L.scan_last_error.restype = ctypes.c_char_p
         L.scan_version.restype = ctypes.c_char_p
         _lib = L
@@ -331,3 +335,62 @@ def lact_fwd(q, k, v, eta, W0=None, *, chunk: int, order: str = "update_then_app
                             0 if workspace is None else workspace.numel(), _stream(dev))
     _check(st)
     return o, WT
+
+
+def scan_bwd_workspace_size(mode: int, dtype: int, B: int, H: int, T: int, dk: int, dv: int) -> int:
+    n = lib().scan_bwd_workspace_size(mode, dtype, B, H, T, dk, dv)
+    if n == ctypes.c_size_t(-1).value:
+        raise ScanError(SCAN_EINVAL, last_error())
+    return n
+
+
+def scan_bwd(q, k, v, alpha, beta=None, S0=None, dO=None, dST=None, *, workspace=None, out=None):
+    """Gradients of a scan_fwd call (gated delta rule when ``beta`` is given,
+    gated linear attention when it is None) for incoming gradients dO (at o,
+    dtype of q; None: zero) and dST (at S_T, float32; None: zero).
+
+    Returns (dq, dk, dv, dalpha, dbeta or None, dS0), all float32; ``out`` may
+    give those six tensors preallocated.
+    """
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", dt, (B, H, T, dk), dev)
+    _need(v, "v", dt, (B, H, T, dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    mode = SCAN_GLA if beta is None else SCAN_GDN
+    if beta is not None:
+        _need(beta, "beta", torch.float32, (B, H, T), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dv, dk), dev)
+    if dO is not None:
+        _need(dO, "dO", dt, (B, H, T, dv), dev)
+    if dST is not None:
+        _need(dST, "dST", torch.float32, (B, H, dv, dk), dev)
+    f32 = torch.float32
+    shapes = [(B, H, T, dk), (B, H, T, dk), (B, H, T, dv), (B, H, T), (B, H, T), (B, H, dv, dk)]
+    if out is None:
+        out = [None if (i == 4 and beta is None) else torch.empty(sh, dtype=f32, device=dev)
+               for i, sh in enumerate(shapes)]
+    out = list(out)
+    for i, (name, sh) in enumerate(zip(["dq", "dk", "dv", "dalpha", "dbeta", "dS0"], shapes)):
+        if i == 4 and beta is None:
+            if out[i] is not None:
+                raise ValueError("dbeta must be None for gated linear attention")
+            continue
+        _need(out[i], name, f32, sh, dev)
+    dcode = _dtype_code(q)
+    ws_bytes = scan_bwd_workspace_size(mode, dcode, B, H, T, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().scan_bwd(mode, dcode, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                            _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dST), *[_ptr(x) for x in out],
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st)
+    return tuple(out)
+

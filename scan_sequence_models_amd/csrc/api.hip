@@ -368,4 +368,77 @@ int lact_fwd(int dtype, int B, int H, int T, int dk, int dv, int chunk, int orde
     return SCAN_OK;
 }
 
+namespace {
+// Validates the sizes of a scan_bwd call; returns SCAN_OK and the workspace bytes.
+int plan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv, size_t* ws) {
+    if (mode != SCAN_GDN && mode != SCAN_GLA)
+        return fail(SCAN_EUNSUPPORTED, "scan_bwd supports SCAN_GDN and SCAN_GLA (got mode %d)", mode);
+    if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
+    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
+        return fail(SCAN_EINVAL, "B, H, T, dk, dv must be >= 1 (got %d, %d, %d, %d, %d)", B, H, T, dk, dv);
+    if ((int64_t)B * H * (dv / 64 + 1) > INT32_MAX / 2 || (int64_t)B * H * T > INT32_MAX)
+        return fail(SCAN_EINVAL, "B*H*T too large");
+    if (!gds::scan_bwd_supported(dk, dv))
+        return fail(SCAN_EUNSUPPORTED, "scan_bwd supports dk in {32, 64, 128} and dv a multiple of 64 up to 4096 "
+                    "(got dk %d, dv %d)", dk, dv);
+    *ws = gds::scan_bwd_workspace_floats(B * H, T, dk, dv) * sizeof(float);
+    return SCAN_OK;
+}
+}  // namespace
+
+size_t scan_bwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk, int dv) {
+    size_t ws = 0;
+    if (plan_bwd(mode, dtype, B, H, T, dk, dv, &ws) != SCAN_OK) return (size_t)-1;
+    return ws;
+}
+
+int scan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv, const void* q, const void* k,
+             const void* v, const float* alpha, const float* beta, const float* S0, const void* dO,
+             const float* dST, float* dq, float* dk_out, float* dv_out, float* dalpha, float* dbeta,
+             float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    int st = plan_bwd(mode, dtype, B, H, T, dk, dv, &need);
+    if (st != SCAN_OK) return st;
+    const bool gdn = mode == SCAN_GDN;
+    if (!q || !k || !v || !alpha || !dq || !dk_out || !dv_out || !dalpha || !dS0)
+        return fail(SCAN_EINVAL, "q, k, v, alpha, dq, dk, dv, dalpha and dS0 must be non-null");
+    if (gdn && (!beta || !dbeta)) return fail(SCAN_EINVAL, "SCAN_GDN needs beta and dbeta");
+    if (!gdn && (beta || dbeta)) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta and no dbeta (pass NULL)");
+    const void* a16[] = {q, k, v, dO, S0, dST, dq, dk_out, dv_out, dS0};
+    const char* n16[] = {"q", "k", "v", "dO", "S0", "dST", "dq", "dk", "dv", "dS0"};
+    for (int i = 0; i < 10; ++i)
+        if (a16[i] && !aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
+    const void* a4[] = {alpha, beta, dalpha, dbeta};
+    for (const void* p : a4)
+        if (p && !aligned(p, 4)) return fail(SCAN_EALIGN, "alpha, beta, dalpha, dbeta must be 4-byte aligned");
+    if (!workspace || workspace_bytes < need)
+        return fail(SCAN_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(SCAN_EALIGN, "workspace is not 256-byte aligned");
+    const size_t es = dtype == SCAN_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H;
+    const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
+                        range("v", v, BH * T * dv * es), range("alpha", alpha, BH * T * 4),
+                        range("beta", beta, BH * T * 4), range("S0", S0, BH * dv * dk * 4),
+                        range("dO", dO, BH * T * dv * es), range("dST", dST, BH * dv * dk * 4)};
+    const Range out[] = {range("dq", dq, BH * T * dk * 4), range("dk", dk_out, BH * T * dk * 4),
+                         range("dv", dv_out, BH * T * dv * 4), range("dalpha", dalpha, BH * T * 4),
+                         range("dbeta", dbeta, BH * T * 4), range("dS0", dS0, BH * dv * dk * 4),
+                         range("workspace", workspace, need)};
+    for (size_t a = 0; a < sizeof(out) / sizeof(out[0]); ++a) {
+        for (const Range& r : in)
+            if (overlaps(out[a], r)) return fail(SCAN_EINVAL, "%s overlaps %s", out[a].name, r.name);
+        for (size_t b = a + 1; b < sizeof(out) / sizeof(out[0]); ++b)
+            if (overlaps(out[a], out[b])) return fail(SCAN_EINVAL, "%s overlaps %s", out[a].name, out[b].name);
+    }
+    gds::BwdJob j{};
+    j.q = q; j.k = k; j.v = v; j.dO = dO;
+    j.alpha = alpha; j.beta = beta; j.S0 = S0; j.dST = dST;
+    j.dq = dq; j.dk_out = dk_out; j.dv_out = dv_out; j.dalpha = dalpha; j.dbeta = dbeta; j.dS0 = dS0;
+    j.ckpt = static_cast<float*>(workspace);
+    j.BH = (int)BH; j.T = T; j.dk = dk; j.dv = dv;
+    hipError_t e = gds::launch_scan_bwd(gdn ? 0 : 1, dtype == SCAN_BF16 ? 1 : 0, j, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "scan_bwd launch");
+    return SCAN_OK;
+}
+
 }  // extern "C"

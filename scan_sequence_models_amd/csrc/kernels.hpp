@@ -62,6 +62,19 @@ hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk,
                              const float* beta, const float* beta_w, const float* S0, void* o,
                              float* ST, hipStream_t stream);
 
+// scan_bwd.hip -- gradient of the scan through the chunkwise form ------------
+struct BwdJob {
+    const void *q, *k, *v, *dO;             // element type of dtype; dO may be null (zero)
+    const float *alpha, *beta, *S0, *dST;   // beta null for linear attention; S0, dST may be null
+    float *dq, *dk_out, *dv_out, *dalpha, *dbeta, *dS0;  // dbeta null for linear attention
+    float* ckpt;                            // workspace: states entering each chunk, then partials
+    float* part;                            // set by launch_scan_bwd
+    int BH, T, dk, dv, nchunks;
+};
+bool scan_bwd_supported(int dk, int dv);
+size_t scan_bwd_workspace_floats(int BH, int T, int dk, int dv);
+hipError_t launch_scan_bwd(int mode, int dtype, BwdJob job, hipStream_t stream);
+
 // prism.hip -- PRISM write factors expanded into a split-strength scan stream ---
 struct PrismJob {
     const void *q, *k, *v, *x;           // [BH, T, dk] / [BH, T, dv], element type of dtype

@@ -1,0 +1,669 @@
+// scan_bwd.hip -- gradient of the scan through the chunkwise form, float32.
+//
+// The forward is the chunkwise (UT) form of the gated delta rule (and of gated
+// linear attention): with S the state entering a 32-token chunk, g the
+// cumulative log decay inside it, gamma = e^g, Gamma_ts = e^{g_t - g_s}:
+//
+//   B = strict_lower(Gamma o K K^T),  A = diag(beta) B,  T = (I + A)^-1
+//   X = diag(beta) V - diag(beta gamma) K S^T,   U = T X            (GLA: U = V)
+//   P = lower(Gamma o Q K^T),   O = diag(gamma) Q S^T + P U
+//   S' = gamma_C S + U^T diag(e^{g_C - g}) K
+//
+// (the prefix-scan notes, key design 2, give the affine state update; the
+// chunk form is its unrolling over the chunk).  Its reverse mode, for incoming
+// gradients dO and dS', is (Kd = diag(e^{g_C - g}) K, dX = T^T dU):
+//
+//   dS  = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K
+//   dU  = Kd dS'^T + P^T dO,     dP = lower(dO U^T)
+//   dQ  = diag(gamma) dO S + (dP o Gamma) K
+//   dK  = diag(e^{g_C-g}) U dS' + (dP o Gamma)^T Q - diag(beta gamma) dX S
+//         + (dKK + dKK^T) K,     dKK = diag(beta) dA o Gamma
+//   dV  = diag(beta) dX          (GLA: dV = dU)
+//   dA  = strict_lower(-dX U^T)  (because T (I + A) = I, -T^T dU X^T T^T = -dX U^T)
+//   dbeta_t = <dX_t, V_t> + gamma_t <dRw_t, K_t> + sum_s dA_ts B_ts,  dRw = -dX S
+//   dg_t    = gamma_t <(dO S)_t, Q_t> - e^{g_C-g_t} <(U dS')_t, K_t> + beta_t gamma_t <dRw_t, K_t>
+//             + rows - columns of (dP o P) and of (dA o A),
+//   dg_C   += gamma_C <dS', S> + sum_t e^{g_C-g_t} <(U dS')_t, K_t>,
+// and d ln alpha_s = sum over t >= s in the chunk of dg_t.
+//
+// Three kernels:
+//   bwd_states_kernel: the forward chunk recursion, storing the state entering
+//     every chunk (one workgroup per head and 64-row value slice);
+//   bwd_chunk_kernel: the chunks in reverse order, recomputing each chunk's
+//     factors from its stored state and carrying dS in LDS; dv and dS0 rows
+//     belong to the slice and are written in full, dq, dk, d ln alpha and dbeta
+//     are sums over value rows and are written as per-slice partials;
+//   bwd_reduce_kernel: the sum over slices and dalpha = d ln alpha / alpha.
+// Products are 32x32 tiles on the float32 MFMA (v_mfma_f32_32x32x2f32).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gds {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kC = 32;       // tokens per chunk
+constexpr int kSL = 64;      // value rows per workgroup
+constexpr int LV = kSL + 1;  // row stride of [32][64] value-row arrays
+constexpr int LM = kC + 1;   // row stride of 32x32 matrices
+constexpr int LB = kC + 4;   // row stride of the k-Gram (float4 rows for the solve)
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma2(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+
+// accumulator element e of a 32x32 tile sits at row 8 (e / 4) + 4 kg + e % 4,
+// column l32 (lane = 32 kg + l32)
+__device__ __forceinline__ int acc_row(int e, int kg) { return 8 * (e >> 2) + 4 * kg + (e & 3); }
+
+// Row sums of a tile: rows of the lane's half go to out[row] from lane l32 == 0.
+__device__ __forceinline__ void store_row_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float s = group_sum<32>(x[e]);
+        if (l32 == 0) out[acc_row(e, kg)] = sign * s;
+    }
+}
+// Column sums of a tile: out[column] from the lanes of half 0.
+__device__ __forceinline__ void store_col_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += x[e];
+    s += __shfl_xor(s, 32, 64);
+    if (kg == 0) out[l32] = sign * s;
+}
+
+// Chunk gates by wave 0 (lanes 0..31 hold tokens): log2 cumulative decay G2,
+// gamma = 2^G2, Dd = 2^(G2_C - G2), beta and beta gamma; past T: identity
+// tokens (alpha = 1, beta = 0).
+template <bool GDN>
+__device__ __forceinline__ void chunk_gates(const float* alpha, const float* beta, size_t tok0, int c0, int T,
+                                            int lane, float* G2, float* gam, float* Dd, float* bet,
+                                            float* bg, float* gC) {
+    const int t = lane & 31;
+    const bool in = c0 + t < T;
+    float la = in ? __log2f(alpha[tok0 + c0 + t]) : 0.f;
+    const float b = (GDN && in) ? beta[tok0 + c0 + t] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+        const float y = __shfl_up(la, off, 32);
+        if (t >= off) la += y;
+    }
+    const float last = __shfl(la, 31, 32);
+    if (lane < 32) {
+        const float g = __builtin_amdgcn_exp2f(la);
+        G2[t] = la;
+        gam[t] = g;
+        Dd[t] = __builtin_amdgcn_exp2f(last - la);
+        bet[t] = b;
+        bg[t] = b * g;
+        if (t == 0) *gC = __builtin_amdgcn_exp2f(last);
+    }
+}
+
+// T = (I + diag(beta) B)^-1 for strictly lower B (row stride LB), by one wave:
+// lane l32 solves for column l32 by forward substitution; each row of B is read
+// as float4 one row ahead of its use (the offset is tied to the previous row's
+// result so the compiler keeps the loads there).  Lanes 32..63 repeat 0..31.
+__device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* bet, float* Tm, int l32, int kg) {
+    const float4* B4 = reinterpret_cast<const float4*>(Bm);
+    constexpr int R4 = LB / 4;
+    float xcol[kC];
+    float4 cur[kC / 4], nxt[kC / 4];
+    cur[0] = B4[R4];
+    xcol[0] = l32 == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < kC; ++r) {
+        if (r + 1 < kC) {
+            int off = (r + 1) * R4;
+            asm volatile("" : "+v"(off) : "v"(xcol[r - 1]));
+#pragma unroll
+            for (int m = 0; m < (r + 4) / 4; ++m) nxt[m] = B4[off + m];
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < r; ++j) {
+            const float4 bj = cur[j / 4];
+            const float bv = (j & 3) == 0 ? bj.x : (j & 3) == 1 ? bj.y : (j & 3) == 2 ? bj.z : bj.w;
+            acc += bv * xcol[j];
+        }
+        xcol[r] = (r == l32 ? 1.f : 0.f) - bet[r] * acc;
+        if (r + 1 < kC) {
+#pragma unroll
+            for (int m = 0; m < (r + 4) / 4; ++m) cur[m] = nxt[m];
+        }
+    }
+    if (kg == 0) {
+#pragma unroll
+        for (int r = 0; r < kC; ++r) Tm[r * LM + l32] = xcol[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward states: S entering chunk n goes to ckpt[bh][n][rows of the slice].
+template <int MODE, int DK, typename E>
+__global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
+    constexpr bool GDN = MODE == 0;
+    constexpr int NJ = DK / 32;
+    constexpr int L1 = DK + 1;
+    __shared__ float Ks[kC * L1];
+    __shared__ float Us[kC * LV];  // V, then X, then U
+    __shared__ float Ss[kSL * L1];
+    __shared__ __align__(16) float Bm[GDN ? kC * LB : 4];
+    __shared__ float Tm[GDN ? kC * LM : 1];
+    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bg[kC], gC[1];
+
+    const int slices = J.dv / kSL;
+    const int bh = blockIdx.x / slices;
+    const int r0 = (blockIdx.x - bh * slices) * kSL;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, kg = lane >> 5;
+    const int T = J.T, dv = J.dv;
+    const E* k = static_cast<const E*>(J.k);
+    const E* v = static_cast<const E*>(J.v);
+    const size_t tok0 = (size_t)bh * T;
+    const size_t s_base = ((size_t)bh * dv + r0) * DK;
+    auto row = [&](int e) { return acc_row(e, kg); };
+
+    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
+
+    for (int n = 0; n < J.nchunks; ++n) {
+        const int c0 = n * kC;
+        __syncthreads();
+        float* ck = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
+        for (int x = tid; x < kSL * DK; x += kThreads) ck[x] = Ss[x / DK * L1 + x % DK];
+        for (int x = tid; x < kC * DK; x += kThreads) {
+            const int t = x / DK;
+            Ks[t * L1 + x % DK] = c0 + t < T ? to_f32(k[(tok0 + c0) * DK + x]) : 0.f;
+        }
+        for (int x = tid; x < kC * kSL; x += kThreads) {
+            const int t = x / kSL, i = x % kSL;
+            Us[t * LV + i] = c0 + t < T ? to_f32(v[(tok0 + c0 + t) * dv + r0 + i]) : 0.f;
+        }
+        if (w == 0) chunk_gates<GDN>(J.alpha, J.beta, tok0, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        __syncthreads();
+        if constexpr (GDN) {
+            if (w == 0) {  // B = strict_lower(Gamma o K K^T)
+                f32x16 c = {};
+                for (int ks = 0; ks < DK / 2; ++ks) {
+                    const float kk = Ks[l32 * L1 + 2 * ks + kg];
+                    c = mfma2(kk, kk, c);
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e);
+                    Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+                }
+            } else if (w < 3) {  // X = beta V - beta gamma K S^T, value columns 32 (w - 1) ..
+                const int I = w - 1;
+                f32x16 c;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) c[e] = bet[row(e)] * Us[row(e) * LV + 32 * I + l32];
+                const float nbg = -bg[l32];
+                for (int ks = 0; ks < DK / 2; ++ks)
+                    c = mfma2(nbg * Ks[l32 * L1 + 2 * ks + kg], Ss[(32 * I + l32) * L1 + 2 * ks + kg], c);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+            }
+            __syncthreads();
+            if (w == 0) {  // T, then U = T X in place
+                solve_unit_lower(Bm, bet, Tm, l32, kg);
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+                    f32x16 c = {};
+#pragma unroll
+                    for (int ks = 0; ks < kC / 2; ++ks)
+                        c = mfma2(Tm[l32 * LM + 2 * ks + kg], Us[(2 * ks + kg) * LV + 32 * I + l32], c);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+                }
+            }
+            __syncthreads();
+        }
+        // S <- gamma_C S + U^T diag(e^{g_C - g}) K
+        for (int tile = w; tile < 2 * NJ; tile += 4) {
+            const int I = tile / NJ, Jt = tile - I * NJ;
+            f32x16 c;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) c[e] = gC[0] * Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
+#pragma unroll
+            for (int ks = 0; ks < kC / 2; ++ks) {
+                const int t = 2 * ks + kg;
+                c = mfma2(Us[t * LV + 32 * I + l32], Dd[t] * Ks[t * L1 + 32 * Jt + l32], c);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The reverse chunk pass.
+template <int MODE, int DK, typename E>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_chunk_kernel(
+    BwdJob J) {
+    constexpr bool GDN = MODE == 0;
+    constexpr int NJ = DK / 32;  // key-column tiles: wave w < NJ owns dq and dk tile w
+    constexpr int L1 = DK + 1;
+    __shared__ float Qs[kC * L1];
+    __shared__ float Ks[kC * L1];
+    __shared__ float Ss[kSL * L1];   // state entering the chunk
+    __shared__ float dSs[kSL * L1];  // gradient at the state leaving it, then entering it
+    __shared__ float Vs[kC * LV];    // V, then dX
+    __shared__ float dOs[kC * LV];
+    __shared__ float Us[kC * LV];    // V, then X, then U
+    __shared__ float dUs[kC * LV];
+    __shared__ __align__(16) float Bm[GDN ? kC * LB : 4];
+    __shared__ float Pm[kC * LM];
+    __shared__ float Tm[GDN ? kC * LM : 1];
+    __shared__ float dQKm[kC * LM];  // dP o Gamma
+    __shared__ float dKKm[GDN ? kC * LM : 1];
+    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bg[kC], gC[1];
+    __shared__ float dgp[16 * kC];   // per-product contributions to dg (fixed slots)
+    __shared__ float dbp[8 * kC];    // ... to dbeta
+    __shared__ float dgc[16];        // ... to dg_C
+
+    const int slices = J.dv / kSL;
+    const int slice = blockIdx.x % slices;
+    const int bh = blockIdx.x / slices;
+    const int r0 = slice * kSL;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, kg = lane >> 5;
+    const int T = J.T, dv = J.dv;
+    const E* q = static_cast<const E*>(J.q);
+    const E* k = static_cast<const E*>(J.k);
+    const E* v = static_cast<const E*>(J.v);
+    const E* dO = static_cast<const E*>(J.dO);
+    const size_t tok0 = (size_t)bh * T;
+    const size_t s_base = ((size_t)bh * dv + r0) * DK;
+    const size_t part_tok = ((size_t)slice * J.BH + bh) * T;  // this slice's partial rows
+    float* pdq = J.part;
+    float* pdk = pdq + (size_t)slices * J.BH * T * DK;
+    float* pdl = pdk + (size_t)slices * J.BH * T * DK;
+    float* pdb = pdl + (size_t)slices * J.BH * T;
+    auto row = [&](int e) { return acc_row(e, kg); };
+
+    for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
+
+    for (int n = J.nchunks - 1; n >= 0; --n) {
+        const int c0 = n * kC;
+        __syncthreads();  // the previous chunk is done with every array
+        const float* ck = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
+        for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = ck[x];
+        for (int x = tid; x < kC * DK; x += kThreads) {
+            const int t = x / DK, y = t * L1 + x % DK;
+            const bool in = c0 + t < T;
+            Qs[y] = in ? to_f32(q[(tok0 + c0) * DK + x]) : 0.f;
+            Ks[y] = in ? to_f32(k[(tok0 + c0) * DK + x]) : 0.f;
+        }
+        for (int x = tid; x < kC * kSL; x += kThreads) {
+            const int t = x / kSL, i = x % kSL;
+            const bool in = c0 + t < T;
+            const size_t gi = (tok0 + c0 + t) * dv + r0 + i;
+            const float vv = in ? to_f32(v[gi]) : 0.f;
+            Vs[t * LV + i] = vv;
+            Us[t * LV + i] = vv;
+            dOs[t * LV + i] = in && dO ? to_f32(dO[gi]) : 0.f;
+        }
+        for (int x = tid; x < 16 * kC; x += kThreads) dgp[x] = 0.f;
+        for (int x = tid; x < 8 * kC; x += kThreads) dbp[x] = 0.f;
+        if (tid < 16) dgc[tid] = 0.f;
+        if (w == 0) chunk_gates<GDN>(J.alpha, J.beta, tok0, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        __syncthreads();
+
+        f32x16 accQ = {}, accK = {};
+        // Phase 1: B, P, X; the owners start dQ = diag(gamma) dO S (+ its dg share)
+        if (GDN && w == 0) {
+            f32x16 c = {};
+            for (int ks = 0; ks < DK / 2; ++ks) {
+                const float kk = Ks[l32 * L1 + 2 * ks + kg];
+                c = mfma2(kk, kk, c);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+            }
+        } else if (w == 1) {
+            f32x16 c = {};
+            for (int ks = 0; ks < DK / 2; ++ks)
+                c = mfma2(Qs[l32 * L1 + 2 * ks + kg], Ks[l32 * L1 + 2 * ks + kg], c);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                Pm[t * LM + l32] = l32 <= t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+            }
+        } else if (GDN && w >= 2) {
+            const int I = w - 2;
+            f32x16 c;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) c[e] = bet[row(e)] * Us[row(e) * LV + 32 * I + l32];
+            const float nbg = -bg[l32];
+            for (int ks = 0; ks < DK / 2; ++ks)
+                c = mfma2(nbg * Ks[l32 * L1 + 2 * ks + kg], Ss[(32 * I + l32) * L1 + 2 * ks + kg], c);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+        } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
+            const int I = w - 2;
+            f32x16 c = {};
+            const float dd = Dd[l32];
+            for (int ks = 0; ks < DK / 2; ++ks)
+                c = mfma2(dd * Ks[l32 * L1 + 2 * ks + kg], dSs[(32 * I + l32) * L1 + 2 * ks + kg], c);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
+        }
+        if (w < NJ) {
+            const float gl = gam[l32];
+            for (int ks = 0; ks < kSL / 2; ++ks)
+                accQ = mfma2(gl * dOs[l32 * LV + 2 * ks + kg], Ss[(2 * ks + kg) * L1 + 32 * w + l32], accQ);
+            f32x16 x;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = accQ[e] * Qs[row(e) * L1 + 32 * w + l32];
+            store_row_sums(x, dgp + w * kC, l32, kg, 1.f);  // dg slots 0..3
+        }
+        __syncthreads();
+        // Phase 2 (delta rule): T and U = T X; dU = Kd dS'^T
+        if constexpr (GDN) {
+            if (w == 0) {
+                solve_unit_lower(Bm, bet, Tm, l32, kg);
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+                    f32x16 c = {};
+#pragma unroll
+                    for (int ks = 0; ks < kC / 2; ++ks)
+                        c = mfma2(Tm[l32 * LM + 2 * ks + kg], Us[(2 * ks + kg) * LV + 32 * I + l32], c);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+                }
+            } else if (w < 3) {
+                const int I = w - 1;
+                f32x16 c = {};
+                const float dd = Dd[l32];
+                for (int ks = 0; ks < DK / 2; ++ks)
+                    c = mfma2(dd * Ks[l32 * L1 + 2 * ks + kg], dSs[(32 * I + l32) * L1 + 2 * ks + kg], c);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
+            }
+            __syncthreads();
+        }
+        // Phase 3: dP (wave 0), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
+        if (w == 0) {
+            f32x16 c = {};
+            for (int ks = 0; ks < kSL / 2; ++ks)
+                c = mfma2(dOs[l32 * LV + 2 * ks + kg], Us[l32 * LV + 2 * ks + kg], c);
+            f32x16 L;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                const bool m = l32 <= t;
+                const float dp = m ? c[e] : 0.f;
+                dQKm[t * LM + l32] = m ? dp * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                L[e] = dp * Pm[t * LM + l32];
+            }
+            store_row_sums(L, dgp + 8 * kC, l32, kg, 1.f);   // dg slot 8
+            store_col_sums(L, dgp + 9 * kC, l32, kg, -1.f);  // dg slot 9
+        } else if (w < 3) {
+            const int I = w - 1;
+            f32x16 c;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
+#pragma unroll
+            for (int ks = 0; ks < kC / 2; ++ks)
+                c = mfma2(Pm[(2 * ks + kg) * LM + l32], dOs[(2 * ks + kg) * LV + 32 * I + l32], c);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
+        }
+        if (w < NJ) {  // dKd = U dS'
+            f32x16 c = {};
+            for (int ks = 0; ks < kSL / 2; ++ks)
+                c = mfma2(Us[l32 * LV + 2 * ks + kg], dSs[(2 * ks + kg) * L1 + 32 * w + l32], c);
+            f32x16 x;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                const float d = Dd[t] * c[e];
+                accK[e] += d;
+                x[e] = d * Ks[t * L1 + 32 * w + l32];
+            }
+            float tot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float s = group_sum<32>(x[e]);
+                if (l32 == 0) dgp[(4 + w) * kC + row(e)] = -s;  // dg slots 4..7
+                tot += s;
+            }
+            tot += __shfl_xor(tot, 32, 64);
+            if (lane == 0) dgc[w] = tot;
+        }
+        __syncthreads();
+        // Phase 4: dX = T^T dU with dV, or dV = dU; the owners' dQ, dK += dQK parts
+        if (w == 1 || w == 2) {
+            const int I = w - 1;
+            f32x16 c;
+            if constexpr (GDN) {
+                c = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < kC / 2; ++ks)
+                    c = mfma2(Tm[(2 * ks + kg) * LM + l32], dUs[(2 * ks + kg) * LV + 32 * I + l32], c);
+                f32x16 x;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) x[e] = c[e] * Vs[row(e) * LV + 32 * I + l32];
+                store_row_sums(x, dbp + I * kC, l32, kg, 1.f);  // dbeta slots 0, 1
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Vs[row(e) * LV + 32 * I + l32] = c[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                if (c0 + t < T) J.dv_out[(tok0 + c0 + t) * dv + r0 + 32 * I + l32] = (GDN ? bet[t] : 1.f) * c[e];
+            }
+        }
+        if (w < NJ) {
+#pragma unroll
+            for (int ks = 0; ks < kC / 2; ++ks) {
+                const int s = 2 * ks + kg;
+                accQ = mfma2(dQKm[l32 * LM + s], Ks[s * L1 + 32 * w + l32], accQ);
+                accK = mfma2(dQKm[s * LM + l32], Qs[s * L1 + 32 * w + l32], accK);
+            }
+        }
+        __syncthreads();
+        // Phase 5: dA (wave 0), dRw (owners), dS
+        if constexpr (GDN) {
+            if (w == 0) {
+                f32x16 c = {};
+                for (int ks = 0; ks < kSL / 2; ++ks)
+                    c = mfma2(-Vs[l32 * LV + 2 * ks + kg], Us[l32 * LV + 2 * ks + kg], c);
+                f32x16 xb, xa;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e);
+                    const bool m = l32 < t;
+                    const float da = m ? c[e] : 0.f;
+                    const float b = Bm[t * LB + l32];
+                    xb[e] = da * b;
+                    xa[e] = da * bet[t] * b;
+                    dKKm[t * LM + l32] = m ? bet[t] * da * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                }
+                store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6
+                store_row_sums(xa, dgp + 14 * kC, l32, kg, 1.f);   // dg slot 14
+                store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
+            }
+            if (w < NJ) {  // dRw = -dX S
+                f32x16 c = {};
+                for (int ks = 0; ks < kSL / 2; ++ks)
+                    c = mfma2(-Vs[l32 * LV + 2 * ks + kg], Ss[(2 * ks + kg) * L1 + 32 * w + l32], c);
+                f32x16 x;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e);
+                    accK[e] += bg[t] * c[e];
+                    x[e] = c[e] * Ks[t * L1 + 32 * w + l32];
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float s = group_sum<32>(x[e]);
+                    if (l32 == 0) {
+                        const int t = row(e);
+                        dbp[(2 + w) * kC + t] = gam[t] * s;  // dbeta slots 2..5
+                        dgp[(10 + w) * kC + t] = bg[t] * s;  // dg slots 10..13
+                    }
+                }
+            }
+        }
+        // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K, and <dS', S>
+        for (int tile = w; tile < 2 * NJ; tile += 4) {
+            const int I = tile / NJ, Jt = tile - I * NJ;
+            f32x16 c;
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int y = (32 * I + row(e)) * L1 + 32 * Jt + l32;
+                const float d = dSs[y];
+                ss += d * Ss[y];
+                c[e] = gC[0] * d;
+            }
+#pragma unroll
+            for (int ks = 0; ks < kC / 2; ++ks) {
+                const int t = 2 * ks + kg;
+                c = mfma2(dOs[t * LV + 32 * I + l32], gam[t] * Qs[t * L1 + 32 * Jt + l32], c);
+                if constexpr (GDN) c = mfma2(-Vs[t * LV + 32 * I + l32], bg[t] * Ks[t * L1 + 32 * Jt + l32], c);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dSs[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
+            ss = group_sum<64>(ss);
+            if (lane == 0) dgc[4 + tile] = ss;
+        }
+        __syncthreads();
+        // Phase 6: dK += (dKK + dKK^T) K; partial dq, dk; dg -> d ln alpha, dbeta
+        if (w < NJ) {
+            if constexpr (GDN) {
+#pragma unroll
+                for (int ks = 0; ks < kC / 2; ++ks) {
+                    const int s = 2 * ks + kg;
+                    accK = mfma2(dKKm[l32 * LM + s] + dKKm[s * LM + l32], Ks[s * L1 + 32 * w + l32], accK);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = row(e);
+                if (c0 + t < T) {
+                    const size_t o = (part_tok + c0 + t) * DK + 32 * w + l32;
+                    pdq[o] = accQ[e];
+                    pdk[o] = accK[e];
+                }
+            }
+        }
+        if (w == 3) {
+            // one wave (lanes 0..31 hold tokens) sums the slots in a fixed order
+            const int t = l32;
+            float dg = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) dg += dgp[s * kC + t];
+            if (t == kC - 1) {
+                float c = 0.f, sc = 0.f;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) c += dgc[s];
+#pragma unroll
+                for (int s = 4; s < 12; ++s) sc += dgc[s];
+                dg += c + gC[0] * sc;
+            }
+            // reverse cumulative sum over the chunk: d ln alpha_s = sum_{t >= s} dg_t
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                const float y = __shfl_down(dg, off, 32);
+                if (t + off < 32) dg += y;
+            }
+            float db = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) db += dbp[s * kC + t];
+            if (kg == 0 && c0 + t < T) {
+                pdl[part_tok + c0 + t] = dg;
+                pdb[part_tok + c0 + t] = db;
+            }
+        }
+    }
+    __syncthreads();
+    for (int x = tid; x < kSL * DK; x += kThreads) J.dS0[s_base + x] = dSs[x / DK * L1 + x % DK];
+}
+
+// Sum of the per-slice partials; dalpha = d ln alpha / alpha.
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdJob J) {
+    const size_t n_tok = (size_t)J.BH * J.T;
+    const size_t n_el = n_tok * J.dk;
+    const int slices = J.dv / kSL;
+    const float* pdq = J.part;
+    const float* pdk = pdq + (size_t)slices * n_el;
+    const float* pdl = pdk + (size_t)slices * n_el;
+    const float* pdb = pdl + (size_t)slices * n_tok;
+    for (size_t x = (size_t)blockIdx.x * kThreads + threadIdx.x; x < n_el; x += (size_t)gridDim.x * kThreads) {
+        float a = 0.f, b = 0.f;
+        for (int s = 0; s < slices; ++s) {
+            a += pdq[s * n_el + x];
+            b += pdk[s * n_el + x];
+        }
+        J.dq[x] = a;
+        J.dk_out[x] = b;
+        if (x % J.dk == 0) {
+            const size_t tk = x / J.dk;
+            float l = 0.f, d = 0.f;
+            for (int s = 0; s < slices; ++s) {
+                l += pdl[s * n_tok + tk];
+                d += pdb[s * n_tok + tk];
+            }
+            J.dalpha[tk] = l / J.alpha[tk];
+            if (J.dbeta) J.dbeta[tk] = d;
+        }
+    }
+}
+
+template <int MODE, int DK, typename E>
+hipError_t launch_typed(const BwdJob& J, hipStream_t s) {
+    const dim3 grid((unsigned)((size_t)J.BH * (J.dv / kSL)));
+    hipLaunchKernelGGL((bwd_states_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
+    hipLaunchKernelGGL((bwd_chunk_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
+    const size_t n_el = (size_t)J.BH * J.T * J.dk;
+    const size_t want = (n_el + kThreads - 1) / kThreads;
+    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(blocks), dim3(kThreads), 0, s, J);
+    return hipGetLastError();
+}
+
+template <int MODE, typename E>
+hipError_t launch_mode(const BwdJob& J, hipStream_t s) {
+    switch (J.dk) {
+        case 32: return launch_typed<MODE, 32, E>(J, s);
+        case 64: return launch_typed<MODE, 64, E>(J, s);
+        case 128: return launch_typed<MODE, 128, E>(J, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool scan_bwd_supported(int dk, int dv) {
+    return (dk == 32 || dk == 64 || dk == 128) && dv >= kSL && dv % kSL == 0 && dv <= 4096;
+}
+
+size_t scan_bwd_workspace_floats(int BH, int T, int dk, int dv) {
+    const size_t nchunks = ((size_t)T + kC - 1) / kC;
+    const size_t slices = (size_t)dv / kSL;
+    return (size_t)BH * nchunks * dv * dk + slices * BH * T * (2 * (size_t)dk + 2);
+}
+
+hipError_t launch_scan_bwd(int mode, int dtype, BwdJob J, hipStream_t s) {
+    J.nchunks = (J.T + kC - 1) / kC;
+    J.part = J.ckpt + (size_t)J.BH * J.nchunks * J.dv * J.dk;
+    if (dtype == 0)
+        return mode == 0 ? launch_mode<0, float>(J, s) : launch_mode<1, float>(J, s);
+    return mode == 0 ? launch_mode<0, uint16_t>(J, s) : launch_mode<1, uint16_t>(J, s);
+}
+
+}  // namespace gds

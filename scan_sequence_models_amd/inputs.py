@@ -341,3 +341,15 @@ def diag_alpha(w: Workload, b: int, h: int, T: int | None = None) -> np.ndarray:
     T = w.T if T is None else T
     rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 4]))
     return cast(_draw_gate(rng, w.alpha, T * w.dk).reshape(T, w.dk), "f32")
+
+
+def output_grads(w: Workload, b: int, h: int, T: int | None = None):
+    """Incoming gradients for the backward pass of head (b, h): dO [T, dv] ~ N(0, 1)
+    cast like the data, and dST [dv, dk] ~ N(0, 1) float32, from
+    ``SeedSequence([seed, b, h, 5])``."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, h, 5]))
+    dO = cast(rng.standard_normal((T, w.dv)), w.dtype)
+    dST = cast(rng.standard_normal((w.dv, w.dk)), "f32")
+    return dO, dST
+

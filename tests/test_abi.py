@@ -21,7 +21,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.header_functions()
     assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "decode_step", "prism_expand",
-                          "lact_fwd_workspace_size", "lact_fwd", "scan_last_error", "scan_version"}
+                          "lact_fwd_workspace_size", "lact_fwd", "scan_bwd_workspace_size", "scan_bwd",
+                          "scan_last_error", "scan_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -188,3 +189,48 @@ def test_lact_workspace_sizes(lib):
     n = lib.lact_fwd_workspace_size(1, 8, 16, 8192, 128, 128, 2048)
     assert n == 128 * 4 * (2 * 128 * 128 * 4 + 128 * 128 * 2)
     assert lib.lact_fwd_workspace_size(1, 1, 1, 64, 128, 128, 100) == ctypes.c_size_t(-1).value
+
+
+def _bwd(lib, mode=0, dtype=1, B=1, H=2, T=64, dk=128, dv=128, q=FAKE, k=FAKE + STEP,
+         v=FAKE + 2 * STEP, alpha=FAKE + 3 * STEP, beta=FAKE + 4 * STEP, S0=None, dO=FAKE + 6 * STEP,
+         dST=None, dq=FAKE + 8 * STEP, dk_=FAKE + 9 * STEP, dv_=FAKE + 10 * STEP,
+         dalpha=FAKE + 11 * STEP, dbeta=FAKE + 12 * STEP, dS0=FAKE + 13 * STEP, ws=FAKE + 14 * STEP,
+         wsb=1 << 31):
+    # a valid argument set would launch with fake pointers: only invalid ones are passed
+    return lib.scan_bwd(mode, dtype, B, H, T, dk, dv, q, k, v, alpha, beta, S0, dO, dST, dq, dk_, dv_,
+                        dalpha, dbeta, dS0, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=2), L.SCAN_EUNSUPPORTED),
+    (dict(dtype=2), L.SCAN_EINVAL),
+    (dict(T=0), L.SCAN_EINVAL),
+    (dict(dk=96), L.SCAN_EUNSUPPORTED),
+    (dict(dv=96), L.SCAN_EUNSUPPORTED),
+    (dict(q=None), L.SCAN_EINVAL),
+    (dict(beta=None), L.SCAN_EINVAL),                  # the delta rule needs beta
+    (dict(mode=1), L.SCAN_EINVAL),                     # linear attention takes no beta
+    (dict(dbeta=None), L.SCAN_EINVAL),
+    (dict(dS0=None), L.SCAN_EINVAL),
+    (dict(ws=None), L.SCAN_EWORKSPACE),
+    (dict(wsb=1024), L.SCAN_EWORKSPACE),
+    (dict(ws=FAKE + 14 * STEP + 64), L.SCAN_EALIGN),
+    (dict(k=FAKE + STEP + 8), L.SCAN_EALIGN),
+    (dict(alpha=FAKE + 3 * STEP + 2), L.SCAN_EALIGN),
+    (dict(dq=FAKE + 1024), L.SCAN_EINVAL),             # dq overlaps q
+    (dict(dS0=FAKE + 10 * STEP + 4096), L.SCAN_EINVAL),  # dS0 overlaps dv
+])
+def test_scan_bwd_rejects(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert len(L.last_error()) > 0
+
+
+def test_scan_bwd_workspace_sizes(lib):
+    # the state entering every 32-token chunk, then per-64-row-slice partials of
+    # dq, dk (dk floats per token) and of d ln alpha, dbeta (one float each)
+    n = lib.scan_bwd_workspace_size(0, 1, 8, 16, 8192, 128, 128)
+    assert n == 4 * (128 * 256 * 128 * 128 + 2 * 128 * 8192 * (2 * 128 + 2))
+    assert lib.scan_bwd_workspace_size(1, 0, 1, 1, 33, 32, 64) == 4 * (2 * 64 * 32 + 1 * 33 * 66)
+    assert lib.scan_bwd_workspace_size(0, 1, 1, 1, 64, 128, 96) == ctypes.c_size_t(-1).value
+    assert lib.scan_bwd_workspace_size(3, 1, 1, 1, 64, 128, 128) == ctypes.c_size_t(-1).value
+
