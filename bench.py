@@ -14,8 +14,9 @@ long-b2h8t262144 (the long-sequence path), decode-4096x100 (decode_step over
 4096 states, one timed step per token), prism-b8h16t8192-l2 (the PRISM layer:
 prism_expand, then the split-strength scan of the 3x longer element stream) and
 lact-b8h16t8192-m2048 (lact_fwd: the large-chunk fast-weight update, chunks of
-2048 tokens) and gdn-diag-b8h16t8192 (the gated delta rule with one decay per
-key channel).  Timing: W untimed steps (by default
+2048 tokens), gdn-diag-b8h16t8192 (the gated delta rule with one decay per
+key channel) and gdn-bwd-b8h16t8192 (scan_bwd: the gradient of the training
+shape with respect to every input).  Timing: W untimed steps (by default
 enough to cover the GPU's clock ramp), then two HIP events around K back-to-back
 steps on the launch stream.
 """
@@ -596,6 +597,153 @@ def bench_lact(args, w):
     print(json.dumps(result), flush=True)
 
 
+def bwd_mfma_flops(w) -> float:
+    """Executed float32 MFMA flops of one scan_bwd call (32-token chunks, 64-row
+    value slices; S = 64, C = 32, d = dk).  States pass per chunk and slice:
+    K K^T (2 C^2 d), X (2 C S d), T X (2 C^2 S), state update (2 S d C).  Reverse
+    pass: K K^T and Q K^T (2 C^2 d each), X, dO S, Kd dS'^T, U dS', dX S (2 C S d
+    each), T X, dO U^T, P^T dO, T^T dU, dX U^T (2 C^2 S each), dQK K, dQK^T Q,
+    (dKK + dKK^T) K (2 C^2 d each) and dS (two products, 4 S d C).  Linear
+    attention drops K K^T, X, T X, dX S, T^T dU, dX U^T, dKK and one dS product."""
+    C, S, d = 32, 64, w.dk
+    if w.mode == "gdn":
+        states = 2 * C * C * d + 2 * C * S * d + 2 * C * C * S + 2 * S * d * C
+        rev = 5 * (2 * C * C * d) + 5 * (2 * C * S * d) + 5 * (2 * C * C * S) + 4 * S * d * C
+    else:
+        states = 2 * S * d * C
+        rev = 3 * (2 * C * C * d) + 3 * (2 * C * S * d) + 2 * (2 * C * C * S) + 2 * S * d * C
+    return (states + rev) * -(-w.T // C) * (w.dv // S) * w.B * w.H
+
+
+def cpu_baseline_bwd(w, heads: int):
+    """The float64 gradient oracle on the first ``heads`` heads of ``w``."""
+    import numpy as np
+
+    import oracle
+    from scan_sequence_models_amd import inputs as I
+
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
+    hs = [I.head_inputs(w, b, h) for b, h in sel]
+    gs = [I.output_grads(w, b, h) for b, h in sel]
+    st = lambda f: np.stack([f(x) for x in hs])  # noqa: E731
+    dO = np.stack([g[0] for g in gs])
+    dST = np.stack([g[1] for g in gs])
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.scan_bwd(w.mode, st(lambda x: x.q), st(lambda x: x.k), st(lambda x: x.v),
+                    st(lambda x: x.alpha), st(lambda x: x.beta) if w.beta is not None else None,
+                    st(lambda x: x.S0), dO, dST, threads=threads)
+    sec = time.perf_counter() - t0
+    head_tokens = len(sel) * w.T
+    return {
+        "value": head_tokens / w.H / sec,
+        "unit": "tokens/s",
+        "cores": min(threads, len(sel)),
+        "kind": "oracle",
+        "sample": f"{len(sel)} of {w.B * w.H} heads x {w.T} tokens ({head_tokens} head-tokens), "
+                  f"float64 reverse sweep per state row, one thread per head, {sec:.2f} s",
+        "head_tokens_per_s": head_tokens / sec,
+        "seconds": sec,
+    }
+
+
+def bench_bwd(args, w):
+    """scan_bwd over the whole batch (inputs and incoming gradients resident in HBM)."""
+    import numpy as np
+    import torch
+
+    import scan_sequence_models_amd as gds
+    from scan_sequence_models_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating {w.name} (B={w.B} H={w.H} T={w.T} d={w.dk})")
+    b = I.batch_inputs(w, threads=16)
+    dO = np.empty((w.B, w.H, w.T, w.dv), np.float32)
+    dST = np.empty((w.B, w.H, w.dv, w.dk), np.float32)
+    for bb in range(w.B):
+        for hh in range(w.H):
+            dO[bb, hh], dST[bb, hh] = I.output_grads(w, bb, hh)
+    bf = w.dtype == "bf16"
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    q, k, v, g_o = up(b.q, bf), up(b.k, bf), up(b.v, bf), up(dO, bf)
+    alpha, beta, S0, g_s = up(b.alpha), up(b.beta), up(b.S0), up(dST)
+    del b, dO, dST
+    f32 = torch.float32
+    outs = [torch.empty((w.B, w.H, w.T, w.dk), dtype=f32, device=dev),
+            torch.empty((w.B, w.H, w.T, w.dk), dtype=f32, device=dev),
+            torch.empty((w.B, w.H, w.T, w.dv), dtype=f32, device=dev),
+            torch.empty((w.B, w.H, w.T), dtype=f32, device=dev),
+            torch.empty((w.B, w.H, w.T), dtype=f32, device=dev),
+            torch.empty((w.B, w.H, w.dv, w.dk), dtype=f32, device=dev)]
+    dcode = gds.SCAN_BF16 if bf else gds.SCAN_F32
+    nws = gds.scan_bwd_workspace_size(gds.SCAN_GDN, dcode, w.B, w.H, w.T, w.dk, w.dv)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step():
+        gds.scan_bwd(q, k, v, alpha, beta, S0, g_o, g_s, workspace=ws, out=outs)
+
+    copy_probe(args.copy_probe_mib, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    span_ms, wall = timed(lambda i: step(), args.steps, dev)
+    ms = span_ms / args.steps
+    log(f"bench: {args.steps} scan_bwd calls, {ms:.4f} ms per call, wall {wall * 1e3:.1f} ms")
+    flops = bwd_mfma_flops(w)
+    tfs = flops / (ms / 1e3) / 1e12
+    es = 2 if bf else 4
+    ht = w.B * w.H * w.T
+    # inputs and incoming gradients read once, gradients written once (float32);
+    # the chunk states and slice partials are the workspace's round trips
+    alg = ht * (2 * w.dk + 2 * w.dv) * es + ht * 8 + w.B * w.H * w.dv * w.dk * 4 * 3 \
+        + ht * (2 * w.dk + w.dv + 2) * 4
+    ws_bytes = 2 * nws
+    src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "scan_bwd.hip")
+    result = {
+        "metric": "tokens/s gradient of the gated-delta scan (H=16, d=128, T=8192); % MFMA roofline",
+        "value": w.B * w.T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk,
+                   "dv": w.dv, "chunk": 32, "io_dtype": w.dtype, "grad_dtype": "f32"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tfs,
+            "peak": FP32_MFMA_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": tfs / FP32_MFMA_PEAK_TFS,
+            "traffic": measured_traffic(src, f"scan_bwd_{w.name}_traffic.txt"),
+            "kernel": "scan_bwd (states + reverse chunk + slice reduction kernels)",
+            "flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": alg,
+            "workspace_round_trip_bytes": ws_bytes,
+            "hbm_achieved_gbs": (alg + ws_bytes) / (ms / 1e3) / 1e9,
+            "kernel_ms": ms,
+        },
+        "head_tokens_per_s": ht / (ms / 1e3),
+    }
+    if not args.no_cpu_baseline:
+        heads = min(args.cpu_heads, 16)
+        log(f"bench: timing the CPU gradient oracle on {heads} heads")
+        result["cpu_baseline"] = cpu_baseline_bwd(w, heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -644,6 +792,8 @@ def main():
         return bench_prism(args, w)
     if w.mode == "lact":
         return bench_lact(args, w)
+    if w.backward:
+        return bench_bwd(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

@@ -128,6 +128,7 @@ class Workload:
     prism_steps: int = 0   # PRISM workloads: L rank-1 corrections per token
     prism_window: int = 4  # PRISM workloads: taps W of the anchor convolution
     diag_gates: bool = False  # alpha is one decay per key channel ([T, dk])
+    backward: bool = False  # the workload times the gradient (scan_bwd), not the forward
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -170,6 +171,11 @@ WORKLOADS = {
                                     0.01, seed=10, diag_gates=True),
     "tiny-gla-diag": Workload("tiny-gla-diag", "gla", 1, 2, 77, 16, 16, "f32", 16,
                               ("uniform", 0.8, 1.0), None, 0.01, seed=11, diag_gates=True),
+    # The gradient of the training shape: the inputs of gdn-b8h16t8192 (same
+    # seed) and incoming gradients dO, dST from output_grads
+    "gdn-bwd-b8h16t8192": Workload("gdn-bwd-b8h16t8192", "gdn", 8, 16, 8192, 128, 128, "bf16", 32,
+                                   ("sigmoid_normal", 3.0, 1.0), ("sigmoid_normal", 0.0, 1.0),
+                                   0.01, seed=3, backward=True),
 }
 
 
