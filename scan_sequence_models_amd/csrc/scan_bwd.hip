@@ -76,17 +76,16 @@ __device__ __forceinline__ void store_col_sums(const f32x16& x, float* out, int 
     if (kg == 0) out[l32] = sign * s;
 }
 
-// Chunk gates by wave 0 (lanes 0..31 hold tokens): log2 cumulative decay G2,
-// gamma = 2^G2, Dd = 2^(G2_C - G2), beta and beta gamma; past T: identity
-// tokens (alpha = 1, beta = 0).
+// Chunk gates by wave 0 (lanes 0..31 hold tokens, with their alpha and beta
+// already loaded): log2 cumulative decay G2, gamma = 2^G2, Dd = 2^(G2_C - G2),
+// beta and beta gamma; past T: identity tokens (alpha = 1, beta = 0).
 template <bool GDN>
-__device__ __forceinline__ void chunk_gates(const float* alpha, const float* beta, size_t tok0, int c0, int T,
-                                            int lane, float* G2, float* gam, float* Dd, float* bet,
-                                            float* bg, float* gC) {
+__device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, int c0, int T, int lane, float* G2,
+                                            float* gam, float* Dd, float* bet, float* bg, float* gC) {
     const int t = lane & 31;
     const bool in = c0 + t < T;
-    float la = in ? __log2f(alpha[tok0 + c0 + t]) : 0.f;
-    const float b = (GDN && in) ? beta[tok0 + c0 + t] : 0.f;
+    float la = in ? __log2f(a_raw) : 0.f;
+    const float b = (GDN && in) ? b_raw : 0.f;
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) {
         const float y = __shfl_up(la, off, 32);
@@ -171,20 +170,48 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
 
     for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
 
+    // The next chunk's k, v and gates are fetched into registers while this
+    // chunk computes (unconditional loads from a clamped token index; masking
+    // on the way into LDS), which hides HBM latency at one workgroup per CU.
+    constexpr int NK = kC * DK / kThreads, NV = kC * kSL / kThreads;
+    E pk[NK], pv[NV];
+    float pa = 1.f, pb = 0.f;
+    auto fetch = [&](int cn) {
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            const int x = tid + m * kThreads, t = min(cn + x / DK, T - 1);
+            pk[m] = k[(tok0 + t) * DK + x % DK];
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int x = tid + m * kThreads, t = min(cn + x / kSL, T - 1);
+            pv[m] = v[(tok0 + t) * dv + r0 + x % kSL];
+        }
+        if (w == 0) {
+            const int t = min(cn + l32, T - 1);
+            pa = J.alpha[tok0 + t];
+            if (GDN) pb = J.beta[tok0 + t];
+        }
+    };
+    fetch(0);
+
     for (int n = 0; n < J.nchunks; ++n) {
         const int c0 = n * kC;
         __syncthreads();
         float* ck = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
         for (int x = tid; x < kSL * DK; x += kThreads) ck[x] = Ss[x / DK * L1 + x % DK];
-        for (int x = tid; x < kC * DK; x += kThreads) {
-            const int t = x / DK;
-            Ks[t * L1 + x % DK] = c0 + t < T ? to_f32(k[(tok0 + c0) * DK + x]) : 0.f;
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            const int x = tid + m * kThreads, t = x / DK;
+            Ks[t * L1 + x % DK] = c0 + t < T ? to_f32(pk[m]) : 0.f;
         }
-        for (int x = tid; x < kC * kSL; x += kThreads) {
-            const int t = x / kSL, i = x % kSL;
-            Us[t * LV + i] = c0 + t < T ? to_f32(v[(tok0 + c0 + t) * dv + r0 + i]) : 0.f;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int x = tid + m * kThreads, t = x / kSL;
+            Us[t * LV + x % kSL] = c0 + t < T ? to_f32(pv[m]) : 0.f;
         }
-        if (w == 0) chunk_gates<GDN>(J.alpha, J.beta, tok0, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        if (w == 0) chunk_gates<GDN>(pa, pb, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        if (n + 1 < J.nchunks) fetch(c0 + kC);
         __syncthreads();
         if constexpr (GDN) {
             if (w == 0) {  // B = strict_lower(Gamma o K K^T)
@@ -290,30 +317,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
 
+    // The next chunk's (in reverse order) q, k, v, dO and gates are fetched
+    // into registers during this one's last two phases (unconditional loads
+    // from a clamped token index; masking on the way into LDS).  Issued
+    // earlier, the registers would be live through the phases with the most
+    // accumulators.  Its stored state, 32 more registers per lane, is read at
+    // the chunk's start instead: prefetched, it made the kernel spill more and
+    // ran slower.
+    constexpr int NK = kC * DK / kThreads, NV = kC * kSL / kThreads;
+    E pq[NK], pk[NK], pv[NV], pd[NV];
+    float pa = 1.f, pb = 0.f;
+    auto fetch = [&](int n) {
+        const int cn = n * kC;
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            const int x = tid + m * kThreads, t = min(cn + x / DK, T - 1);
+            const size_t gi = (tok0 + t) * DK + x % DK;
+            pq[m] = q[gi];
+            pk[m] = k[gi];
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int x = tid + m * kThreads, t = min(cn + x / kSL, T - 1);
+            const size_t gi = (tok0 + t) * dv + r0 + x % kSL;
+            pv[m] = v[gi];
+            pd[m] = dO ? dO[gi] : E(0);
+        }
+        if (w == 0) {
+            const int t = min(cn + l32, T - 1);
+            pa = J.alpha[tok0 + t];
+            if (GDN) pb = J.beta[tok0 + t];
+        }
+    };
+    fetch(J.nchunks - 1);
+
     for (int n = J.nchunks - 1; n >= 0; --n) {
         const int c0 = n * kC;
         __syncthreads();  // the previous chunk is done with every array
-        const float* ck = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
-        for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = ck[x];
-        for (int x = tid; x < kC * DK; x += kThreads) {
-            const int t = x / DK, y = t * L1 + x % DK;
-            const bool in = c0 + t < T;
-            Qs[y] = in ? to_f32(q[(tok0 + c0) * DK + x]) : 0.f;
-            Ks[y] = in ? to_f32(k[(tok0 + c0) * DK + x]) : 0.f;
+        {
+            const float* ckn = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
+            for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = ckn[x];
         }
-        for (int x = tid; x < kC * kSL; x += kThreads) {
-            const int t = x / kSL, i = x % kSL;
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            const int x = tid + m * kThreads, t = x / DK, y = t * L1 + x % DK;
             const bool in = c0 + t < T;
-            const size_t gi = (tok0 + c0 + t) * dv + r0 + i;
-            const float vv = in ? to_f32(v[gi]) : 0.f;
-            Vs[t * LV + i] = vv;
-            Us[t * LV + i] = vv;
-            dOs[t * LV + i] = in && dO ? to_f32(dO[gi]) : 0.f;
+            Qs[y] = in ? to_f32(pq[m]) : 0.f;
+            Ks[y] = in ? to_f32(pk[m]) : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int x = tid + m * kThreads, t = x / kSL, y = t * LV + x % kSL;
+            const bool in = c0 + t < T;
+            const float vv = in ? to_f32(pv[m]) : 0.f;
+            Vs[y] = vv;
+            Us[y] = vv;
+            dOs[y] = in ? to_f32(pd[m]) : 0.f;
         }
         for (int x = tid; x < 16 * kC; x += kThreads) dgp[x] = 0.f;
         for (int x = tid; x < 8 * kC; x += kThreads) dbp[x] = 0.f;
         if (tid < 16) dgc[tid] = 0.f;
-        if (w == 0) chunk_gates<GDN>(J.alpha, J.beta, tok0, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        if (w == 0) chunk_gates<GDN>(pa, pb, c0, T, lane, G2, gam, Dd, bet, bg, gC);
         __syncthreads();
 
         f32x16 accQ = {}, accK = {};
@@ -475,6 +539,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         __syncthreads();
+        // the next chunk's inputs are in flight through phases 5 and 6
+        if (n > 0) fetch(n - 1);
         // Phase 5: dA (wave 0), dRw (owners), dS
         if constexpr (GDN) {
             if (w == 0) {
