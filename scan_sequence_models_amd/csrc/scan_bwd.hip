@@ -198,8 +198,13 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     for (int n = 0; n < J.nchunks; ++n) {
         const int c0 = n * kC;
         __syncthreads();
-        float* ck = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
-        for (int x = tid; x < kSL * DK; x += kThreads) ck[x] = Ss[x / DK * L1 + x % DK];
+        float4* ck4 = reinterpret_cast<float4*>(J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK);
+#pragma unroll
+        for (int m = 0; m < kSL * DK / 4 / kThreads; ++m) {
+            const int x = 4 * (tid + m * kThreads);
+            const float* src = Ss + x / DK * L1 + x % DK;
+            ck4[tid + m * kThreads] = make_float4(src[0], src[1], src[2], src[3]);
+        }
 #pragma unroll
         for (int m = 0; m < NK; ++m) {
             const int x = tid + m * kThreads, t = x / DK;
@@ -354,9 +359,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int n = J.nchunks - 1; n >= 0; --n) {
         const int c0 = n * kC;
         __syncthreads();  // the previous chunk is done with every array
-        {
-            const float* ckn = J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK;
-            for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = ckn[x];
+        {  // the stored state: all of a thread's 16-byte loads are issued before any is used
+            constexpr int NS4 = kSL * DK / 4 / kThreads;
+            const float4* ck4 =
+                reinterpret_cast<const float4*>(J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK);
+            float4 sv[NS4];
+#pragma unroll
+            for (int m = 0; m < NS4; ++m) sv[m] = ck4[tid + m * kThreads];
+#pragma unroll
+            for (int m = 0; m < NS4; ++m) {
+                const int x = 4 * (tid + m * kThreads);
+                float* dst = Ss + x / DK * L1 + x % DK;
+                dst[0] = sv[m].x;
+                dst[1] = sv[m].y;
+                dst[2] = sv[m].z;
+                dst[3] = sv[m].w;
+            }
         }
 #pragma unroll
         for (int m = 0; m < NK; ++m) {
