@@ -59,6 +59,33 @@ __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 // column l32 (lane = 32 kg + l32)
 __device__ __forceinline__ int acc_row(int e, int kg) { return 8 * (e >> 2) + 4 * kg + (e & 3); }
 
+// c + the product of STEPS MFMA steps; A(s) and B(s) give the lane's operands
+// of step s (key index 2 s + kg).  Each step's operands are loaded two steps
+// ahead of its MFMA and sched_barrier pins that order: left alone, the compiler
+// waits for each LDS read right before its MFMA, and with one wave per SIMD
+// nothing hides that latency.
+template <int STEPS, class FA, class FB>
+__device__ __forceinline__ f32x16 chain(FA A, FB B, f32x16 c) {
+    float a0 = A(0), b0 = B(0);
+    float a1 = STEPS > 1 ? A(1) : 0.f, b1 = STEPS > 1 ? B(1) : 0.f;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        float a2 = 0.f, b2 = 0.f;
+        if (s + 2 < STEPS) {
+            a2 = A(s + 2);
+            b2 = B(s + 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        c = mfma2(a0, b0, c);
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = a1;
+        b0 = b1;
+        a1 = a2;
+        b1 = b2;
+    }
+    return c;
+}
+
 // Row sums of a tile: rows of the lane's half go to out[row] from lane l32 == 0.
 __device__ __forceinline__ void store_row_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
 #pragma unroll
@@ -220,11 +247,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
         __syncthreads();
         if constexpr (GDN) {
             if (w == 0) {  // B = strict_lower(Gamma o K K^T)
-                f32x16 c = {};
-                for (int ks = 0; ks < DK / 2; ++ks) {
-                    const float kk = Ks[l32 * L1 + 2 * ks + kg];
-                    c = mfma2(kk, kk, c);
-                }
+                auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
+                const f32x16 c = chain<DK / 2>(kr, kr, f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
@@ -236,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) c[e] = bet[row(e)] * Us[row(e) * LV + 32 * I + l32];
                 const float nbg = -bg[l32];
-                for (int ks = 0; ks < DK / 2; ++ks)
-                    c = mfma2(nbg * Ks[l32 * L1 + 2 * ks + kg], Ss[(32 * I + l32) * L1 + 2 * ks + kg], c);
+                c = chain<DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
+                                  [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; }, c);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
             }
@@ -246,10 +270,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
                 solve_unit_lower(Bm, bet, Tm, l32, kg);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
-                    f32x16 c = {};
-#pragma unroll
-                    for (int ks = 0; ks < kC / 2; ++ks)
-                        c = mfma2(Tm[l32 * LM + 2 * ks + kg], Us[(2 * ks + kg) * LV + 32 * I + l32], c);
+                    const f32x16 c = chain<kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
+                                                   [&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
+                                                   f32x16{});
 #pragma unroll
                     for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
                 }
@@ -262,11 +285,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = gC[0] * Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
-#pragma unroll
-            for (int ks = 0; ks < kC / 2; ++ks) {
-                const int t = 2 * ks + kg;
-                c = mfma2(Us[t * LV + 32 * I + l32], Dd[t] * Ks[t * L1 + 32 * Jt + l32], c);
-            }
+            c = chain<kC / 2>([&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
+                              [&](int s) { return Dd[2 * s + kg] * Ks[(2 * s + kg) * L1 + 32 * Jt + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
         }
@@ -401,20 +421,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         f32x16 accQ = {}, accK = {};
         // Phase 1: B, P, X; the owners start dQ = diag(gamma) dO S (+ its dg share)
         if (GDN && w == 0) {
-            f32x16 c = {};
-            for (int ks = 0; ks < DK / 2; ++ks) {
-                const float kk = Ks[l32 * L1 + 2 * ks + kg];
-                c = mfma2(kk, kk, c);
-            }
+            auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
+            const f32x16 c = chain<DK / 2>(kr, kr, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
                 Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
             }
         } else if (w == 1) {
-            f32x16 c = {};
-            for (int ks = 0; ks < DK / 2; ++ks)
-                c = mfma2(Qs[l32 * L1 + 2 * ks + kg], Ks[l32 * L1 + 2 * ks + kg], c);
+            const f32x16 c = chain<DK / 2>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
+                                           [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
@@ -426,23 +442,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = bet[row(e)] * Us[row(e) * LV + 32 * I + l32];
             const float nbg = -bg[l32];
-            for (int ks = 0; ks < DK / 2; ++ks)
-                c = mfma2(nbg * Ks[l32 * L1 + 2 * ks + kg], Ss[(32 * I + l32) * L1 + 2 * ks + kg], c);
+            c = chain<DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
+                              [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
         } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
             const int I = w - 2;
-            f32x16 c = {};
             const float dd = Dd[l32];
-            for (int ks = 0; ks < DK / 2; ++ks)
-                c = mfma2(dd * Ks[l32 * L1 + 2 * ks + kg], dSs[(32 * I + l32) * L1 + 2 * ks + kg], c);
+            const f32x16 c = chain<DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
+                                           [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
         if (w < NJ) {
             const float gl = gam[l32];
-            for (int ks = 0; ks < kSL / 2; ++ks)
-                accQ = mfma2(gl * dOs[l32 * LV + 2 * ks + kg], Ss[(2 * ks + kg) * L1 + 32 * w + l32], accQ);
+            accQ = chain<kSL / 2>([&](int s) { return gl * dOs[l32 * LV + 2 * s + kg]; },
+                                  [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
             f32x16 x;
 #pragma unroll
             for (int e = 0; e < 16; ++e) x[e] = accQ[e] * Qs[row(e) * L1 + 32 * w + l32];
@@ -455,19 +470,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 solve_unit_lower(Bm, bet, Tm, l32, kg);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
-                    f32x16 c = {};
-#pragma unroll
-                    for (int ks = 0; ks < kC / 2; ++ks)
-                        c = mfma2(Tm[l32 * LM + 2 * ks + kg], Us[(2 * ks + kg) * LV + 32 * I + l32], c);
+                    const f32x16 c = chain<kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
+                                                   [&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
+                                                   f32x16{});
 #pragma unroll
                     for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
                 }
             } else if (w < 3) {
                 const int I = w - 1;
-                f32x16 c = {};
                 const float dd = Dd[l32];
-                for (int ks = 0; ks < DK / 2; ++ks)
-                    c = mfma2(dd * Ks[l32 * L1 + 2 * ks + kg], dSs[(32 * I + l32) * L1 + 2 * ks + kg], c);
+                const f32x16 c = chain<DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
+                                               [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
+                                               f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
             }
@@ -475,9 +489,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
         // Phase 3: dP (wave 0), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
         if (w == 0) {
-            f32x16 c = {};
-            for (int ks = 0; ks < kSL / 2; ++ks)
-                c = mfma2(dOs[l32 * LV + 2 * ks + kg], Us[l32 * LV + 2 * ks + kg], c);
+            const f32x16 c = chain<kSL / 2>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
+                                            [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
             f32x16 L;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -494,16 +507,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
-#pragma unroll
-            for (int ks = 0; ks < kC / 2; ++ks)
-                c = mfma2(Pm[(2 * ks + kg) * LM + l32], dOs[(2 * ks + kg) * LV + 32 * I + l32], c);
+            c = chain<kC / 2>([&](int s) { return Pm[(2 * s + kg) * LM + l32]; },
+                              [&](int s) { return dOs[(2 * s + kg) * LV + 32 * I + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
         if (w < NJ) {  // dKd = U dS'
-            f32x16 c = {};
-            for (int ks = 0; ks < kSL / 2; ++ks)
-                c = mfma2(Us[l32 * LV + 2 * ks + kg], dSs[(2 * ks + kg) * L1 + 32 * w + l32], c);
+            const f32x16 c = chain<kSL / 2>([&](int s) { return Us[l32 * LV + 2 * s + kg]; },
+                                            [&](int s) { return dSs[(2 * s + kg) * L1 + 32 * w + l32]; }, f32x16{});
             f32x16 x;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -528,10 +539,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int I = w - 1;
             f32x16 c;
             if constexpr (GDN) {
-                c = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < kC / 2; ++ks)
-                    c = mfma2(Tm[(2 * ks + kg) * LM + l32], dUs[(2 * ks + kg) * LV + 32 * I + l32], c);
+                c = chain<kC / 2>([&](int s) { return Tm[(2 * s + kg) * LM + l32]; },
+                                  [&](int s) { return dUs[(2 * s + kg) * LV + 32 * I + l32]; }, f32x16{});
                 f32x16 x;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) x[e] = c[e] * Vs[row(e) * LV + 32 * I + l32];
@@ -549,12 +558,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         if (w < NJ) {
-#pragma unroll
-            for (int ks = 0; ks < kC / 2; ++ks) {
-                const int s = 2 * ks + kg;
-                accQ = mfma2(dQKm[l32 * LM + s], Ks[s * L1 + 32 * w + l32], accQ);
-                accK = mfma2(dQKm[s * LM + l32], Qs[s * L1 + 32 * w + l32], accK);
-            }
+            accQ = chain<kC / 2>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
+                                 [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
+            accK = chain<kC / 2>([&](int s) { return dQKm[(2 * s + kg) * LM + l32]; },
+                                 [&](int s) { return Qs[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
         }
         __syncthreads();
         // the next chunk's inputs are in flight through phases 5 and 6
@@ -562,9 +569,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 5: dA (wave 0), dRw (owners), dS
         if constexpr (GDN) {
             if (w == 0) {
-                f32x16 c = {};
-                for (int ks = 0; ks < kSL / 2; ++ks)
-                    c = mfma2(-Vs[l32 * LV + 2 * ks + kg], Us[l32 * LV + 2 * ks + kg], c);
+                const f32x16 c = chain<kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
+                                                [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
                 f32x16 xb, xa;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -581,9 +587,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
             }
             if (w < NJ) {  // dRw = -dX S
-                f32x16 c = {};
-                for (int ks = 0; ks < kSL / 2; ++ks)
-                    c = mfma2(-Vs[l32 * LV + 2 * ks + kg], Ss[(2 * ks + kg) * L1 + 32 * w + l32], c);
+                const f32x16 c = chain<kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
+                                                [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; },
+                                                f32x16{});
                 f32x16 x;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -614,12 +620,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 ss += d * Ss[y];
                 c[e] = gC[0] * d;
             }
-#pragma unroll
-            for (int ks = 0; ks < kC / 2; ++ks) {
-                const int t = 2 * ks + kg;
-                c = mfma2(dOs[t * LV + 32 * I + l32], gam[t] * Qs[t * L1 + 32 * Jt + l32], c);
-                if constexpr (GDN) c = mfma2(-Vs[t * LV + 32 * I + l32], bg[t] * Ks[t * L1 + 32 * Jt + l32], c);
-            }
+            // the two products as one chain over 2 C (GDN) or C tokens
+            constexpr int H2 = kC / 2;
+            c = chain<GDN ? kC : H2>(
+                [&](int s) {
+                    const int t = 2 * (s % H2) + kg;
+                    return s < H2 ? dOs[t * LV + 32 * I + l32] : -Vs[t * LV + 32 * I + l32];
+                },
+                [&](int s) {
+                    const int t = 2 * (s % H2) + kg;
+                    return s < H2 ? gam[t] * Qs[t * L1 + 32 * Jt + l32] : bg[t] * Ks[t * L1 + 32 * Jt + l32];
+                },
+                c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dSs[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
             ss = group_sum<64>(ss);
@@ -628,13 +640,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         __syncthreads();
         // Phase 6: dK += (dKK + dKK^T) K; partial dq, dk; dg -> d ln alpha, dbeta
         if (w < NJ) {
-            if constexpr (GDN) {
-#pragma unroll
-                for (int ks = 0; ks < kC / 2; ++ks) {
-                    const int s = 2 * ks + kg;
-                    accK = mfma2(dKKm[l32 * LM + s] + dKKm[s * LM + l32], Ks[s * L1 + 32 * w + l32], accK);
-                }
-            }
+            if constexpr (GDN)
+                accK = chain<kC / 2>(
+                    [&](int s) { return dKKm[l32 * LM + 2 * s + kg] + dKKm[(2 * s + kg) * LM + l32]; },
+                    [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
