@@ -26,8 +26,11 @@
 //
 // One workgroup owns one head and a slice of up to 64 value rows of the state,
 // walking the chunks in order with the slice in LDS.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_f32.hpp"
 
 namespace gds {
 namespace {
@@ -187,10 +190,6 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 // that the key-long product does not wait for the inverse.
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ f32x16 mfma2(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
 constexpr int kSL = 64;      // value rows per workgroup
 constexpr int kLT = kC + 4;  // row stride of the 32x32 T and P tiles (float4 rows)
 constexpr int kPairs = kC * (kC - 1) / 2;
@@ -348,18 +347,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             if constexpr (GDN) Rw[z] = -(bet[t] * Ks[y] * gam);
         }
         __syncthreads();
-        // c += A B^T over key steps [k0, k1), A and B both read along key rows
+        // c += A B^T over `steps` key steps from k0, A and B both read along key rows
         // (A: 32 token rows, B: 32 state rows, row stride L1)
-        auto rows_dot = [&](const float* A, const float* B, int k0, int k1, f32x16 c) {
-            for (int ks = k0; ks < k1; ++ks) c = mfma2(A[l32 * L1 + 2 * ks + kg], B[l32 * L1 + 2 * ks + kg], c);
-            return c;
+        auto rows_dot = [&](const float* A, const float* B, auto steps, int k0, f32x16 c) {
+            return chain<decltype(steps)::value>([&](int s) { return A[l32 * L1 + 2 * (k0 + s) + kg]; },
+                                                 [&](int s) { return B[l32 * L1 + 2 * (k0 + s) + kg]; }, c);
         };
+        using Full = std::integral_constant<int, DK / 2>;
+        using Half = std::integral_constant<int, DK / 4>;
         // c += P U or T X on value columns 32 I ..: B read along token rows of Us
         auto tok_dot = [&](const float* A, int I, f32x16 c) {
-#pragma unroll
-            for (int ks = 0; ks < kC / 2; ++ks)
-                c = mfma2(A[l32 * kLT + 2 * ks + kg], Us[(2 * ks + kg) * kSL + 32 * I + l32], c);
-            return c;
+            return chain<kC / 2>([&](int s) { return A[l32 * kLT + 2 * s + kg]; },
+                                 [&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; }, c);
         };
         auto store_o = [&](int I, const f32x16& c) {
 #pragma unroll
@@ -412,11 +411,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 f32x16 c;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * kSL + 32 * I + l32];
-                c = rows_dot(Rw, Ss + 32 * I * L1, 0, DK / 2, c);  // Rw holds -beta k gamma
+                c = rows_dot(Rw, Ss + 32 * I * L1, Full{}, 0, c);  // Rw holds -beta k gamma
 #pragma unroll
                 for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
             } else {
-                oacc = rows_dot(Qg, Ss, 0, DK / 2, oacc);
+                oacc = rows_dot(Qg, Ss, Full{}, 0, oacc);
             }
             __syncthreads();
             // Phase B: U = T X (waves 1, 2); waves 0 and 3 share (Q gamma) S^T on
@@ -427,9 +426,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
                 for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
             } else if (w == 0) {
-                oacc = rows_dot(Qg, Ss + 32 * L1, 0, DK / 4, oacc);
+                oacc = rows_dot(Qg, Ss + 32 * L1, Half{}, 0, oacc);
             } else {
-                const f32x16 part = rows_dot(Qg, Ss + 32 * L1, DK / 4, DK / 2, f32x16{});
+                const f32x16 part = rows_dot(Qg, Ss + 32 * L1, Half{}, DK / 4, f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) Ob[e * 64 + lane] = part[e];
             }
@@ -445,7 +444,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         } else {
             // O = (Q gamma) S^T + P V: waves 2, 3 (value columns 32 (w - 2) ..)
-            if (w >= 2) store_o(w - 2, tok_dot(Pm, w - 2, rows_dot(Qg, Ss + 32 * (w - 2) * L1, 0, DK / 2, f32x16{})));
+            if (w >= 2) store_o(w - 2, tok_dot(Pm, w - 2, rows_dot(Qg, Ss + 32 * (w - 2) * L1, Full{}, 0, f32x16{})));
             __syncthreads();  // every read of the old state done
         }
         // S <- S diag(gamma_C) + U^T K~: 2 x NJ tiles; with the delta rule waves
@@ -458,9 +457,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L1 + 32 * J + l32] * gC;
-#pragma unroll
-            for (int ks = 0; ks < kC / 2; ++ks)
-                c = mfma2(Us[(2 * ks + kg) * kSL + 32 * I + l32], Kt[(2 * ks + kg) * L1 + 32 * J + l32], c);
+            c = chain<kC / 2>([&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; },
+                              [&](int s) { return Kt[(2 * s + kg) * L1 + 32 * J + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * J + l32] = c[e];
         }

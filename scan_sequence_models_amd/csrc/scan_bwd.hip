@@ -37,6 +37,7 @@
 // Products are 32x32 tiles on the float32 MFMA (v_mfma_f32_32x32x2f32).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_f32.hpp"
 
 namespace gds {
 namespace {
@@ -48,43 +49,12 @@ constexpr int LV = kSL + 1;  // row stride of [32][64] value-row arrays
 constexpr int LM = kC + 1;   // row stride of 32x32 matrices
 constexpr int LB = kC + 4;   // row stride of the k-Gram (float4 rows for the solve)
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ f32x16 mfma2(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 
 // accumulator element e of a 32x32 tile sits at row 8 (e / 4) + 4 kg + e % 4,
 // column l32 (lane = 32 kg + l32)
 __device__ __forceinline__ int acc_row(int e, int kg) { return 8 * (e >> 2) + 4 * kg + (e & 3); }
-
-// c + the product of STEPS MFMA steps; A(s) and B(s) give the lane's operands
-// of step s (key index 2 s + kg).  Each step's operands are loaded two steps
-// ahead of its MFMA and sched_barrier pins that order: left alone, the compiler
-// waits for each LDS read right before its MFMA, and with one wave per SIMD
-// nothing hides that latency.
-template <int STEPS, class FA, class FB>
-__device__ __forceinline__ f32x16 chain(FA A, FB B, f32x16 c) {
-    float a0 = A(0), b0 = B(0);
-    float a1 = STEPS > 1 ? A(1) : 0.f, b1 = STEPS > 1 ? B(1) : 0.f;
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        float a2 = 0.f, b2 = 0.f;
-        if (s + 2 < STEPS) {
-            a2 = A(s + 2);
-            b2 = B(s + 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        c = mfma2(a0, b0, c);
-        __builtin_amdgcn_sched_barrier(0);
-        a0 = a1;
-        b0 = b1;
-        a1 = a2;
-        b1 = b2;
-    }
-    return c;
-}
 
 // Row sums of a tile: rows of the lane's half go to out[row] from lane l32 == 0.
 __device__ __forceinline__ void store_row_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
