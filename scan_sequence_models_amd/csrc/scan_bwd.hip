@@ -56,11 +56,23 @@ __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 // column l32 (lane = 32 kg + l32)
 __device__ __forceinline__ int acc_row(int e, int kg) { return 8 * (e >> 2) + 4 * kg + (e & 3); }
 
+// Sum over the 32 lanes of each half-wave: quad and row steps on DPP, the
+// lane ^ 16 step on v_permlane16_swap (a VALU exchange of the two 16-lane rows
+// of each 32-lane group), not on the LDS-path swizzle.
+__device__ __forceinline__ float sum32(float x) {
+    x += dpp_move<0xB1>(x);   // lane ^ 1
+    x += dpp_move<0x4E>(x);   // lane ^ 2
+    x += dpp_move<0x141>(x);  // row half mirror
+    x += dpp_move<0x140>(x);  // row mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Row sums of a tile: rows of the lane's half go to out[row] from lane l32 == 0.
 __device__ __forceinline__ void store_row_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const float s = group_sum<32>(x[e]);
+        const float s = sum32(x[e]);
         if (l32 == 0) out[acc_row(e, kg)] = sign * s;
     }
 }
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             float tot = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float s = group_sum<32>(x[e]);
+                const float s = sum32(x[e]);
                 if (l32 == 0) dgp[(4 + w) * kC + row(e)] = -s;  // dg slots 4..7
                 tot += s;
             }
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float s = group_sum<32>(x[e]);
+                    const float s = sum32(x[e]);
                     if (l32 == 0) {
                         const int t = row(e);
                         dbp[(2 + w) * kC + t] = gam[t] * s;  // dbeta slots 2..5
