@@ -486,6 +486,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             store_col_sums(L, dgp + 9 * kC, l32, kg, -1.f);  // dg slot 9
         } else if (w < 3) {
             const int I = w - 1;
+            {  // e^{g_C - g_t} <(U dS')_t, K_t> = <U_t, dU_t> while dU holds Kd dS'^T: lane l32 takes
+               // token l32, each half 16 of the tile's value columns
+                float t1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int y = l32 * LV + 32 * I + 16 * kg + i;
+                    t1 += Us[y] * dUs[y];
+                }
+                t1 += __shfl_xor(t1, 32, 64);
+                if (kg == 0) dgp[(4 + I) * kC + l32] = -t1;  // dg slots 4, 5
+            }
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
@@ -497,23 +508,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (w < NJ) {  // dKd = U dS'
             const f32x16 c = chain<kSL / 2>([&](int s) { return Us[l32 * LV + 2 * s + kg]; },
                                             [&](int s) { return dSs[(2 * s + kg) * L1 + 32 * w + l32]; }, f32x16{});
-            f32x16 x;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int t = row(e);
-                const float d = Dd[t] * c[e];
-                accK[e] += d;
-                x[e] = d * Ks[t * L1 + 32 * w + l32];
-            }
-            float tot = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float s = sum32(x[e]);
-                if (l32 == 0) dgp[(4 + w) * kC + row(e)] = -s;  // dg slots 4..7
-                tot += s;
-            }
-            tot += __shfl_xor(tot, 32, 64);
-            if (lane == 0) dgc[w] = tot;
+            for (int e = 0; e < 16; ++e) accK[e] += Dd[row(e)] * c[e];
         }
         __syncthreads();
         // Phase 4: dX = T^T dU with dV, or dV = dU; the owners' dQ, dK += dQK parts
@@ -564,8 +560,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     xa[e] = da * bet[t] * b;
                     dKKm[t * LM + l32] = m ? bet[t] * da * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
                 }
-                store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6
-                store_row_sums(xa, dgp + 14 * kC, l32, kg, 1.f);   // dg slot 14
+                store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6 (dg: beta_t times it)
                 store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
             }
             if (w < NJ) {  // dRw = -dX S
@@ -642,13 +637,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             float dg = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) dg += dgp[s * kC + t];
+            if constexpr (GDN) dg += bet[t] * dbp[6 * kC + t];  // the rows of dA o A
+            // d g_C: gamma_C <dS', S> and the sum over tokens of e^{g_C - g_t} <(U dS')_t, K_t>
+            const float t1 = group_sum<32>(dgp[4 * kC + t] + dgp[5 * kC + t]);
             if (t == kC - 1) {
-                float c = 0.f, sc = 0.f;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) c += dgc[s];
+                float sc = 0.f;
 #pragma unroll
                 for (int s = 4; s < 12; ++s) sc += dgc[s];
-                dg += c + gC[0] * sc;
+                dg += gC[0] * sc - t1;
             }
             // reverse cumulative sum over the chunk: d ln alpha_s = sum_{t >= s} dg_t
 #pragma unroll
