@@ -401,6 +401,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         __syncthreads();
 
         f32x16 accQ = {}, accK = {};
+        f32x16 ksT = {};  // waves 2, 3 (delta rule): (K S^T)^T on value columns 32 (w - 2) .., kept to phase 5
         // Phase 1: B, P, X; the owners start dQ = diag(gamma) dO S (+ its dg share)
         if (GDN && w == 0) {
             auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
@@ -420,14 +421,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         } else if (GDN && w >= 2) {
             const int I = w - 2;
-            f32x16 c;
+            // (K S^T)^T = S K^T with the token along the lanes: X_t = beta_t V_t - beta_t gamma_t (K S^T)_t
+            // is written row by row, and the tile serves <dX_t, (K S^T)_t> in phase 5 as an in-lane sum
+            ksT = chain<DK / 2>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
+                                [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
+            const float b = bet[l32], nbg = -bg[l32];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) c[e] = bet[row(e)] * Us[row(e) * LV + 32 * I + l32];
-            const float nbg = -bg[l32];
-            c = chain<DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
-                              [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; }, c);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+            for (int e = 0; e < 16; ++e) {
+                const int y = l32 * LV + 32 * I + row(e);
+                Us[y] = b * Us[y] + nbg * ksT[e];
+            }
         } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
             const int I = w - 2;
             const float dd = Dd[l32];
@@ -512,28 +515,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int e = 0; e < 16; ++e) accK[e] += Dd[row(e)] * c[e];
         }
         __syncthreads();
-        // Phase 4: dX = T^T dU with dV, or dV = dU; the owners' dQ, dK += dQK parts
-        if (w == 1 || w == 2) {
+        // Phase 4: dX = T^T dU (delta rule; computed as dX^T = dU^T T, the token along the lanes, so
+        // <dX_t, V_t> is an in-lane sum; dX replaces V row by row); the owners' dQ, dK += dQK parts
+        if (GDN && (w == 1 || w == 2)) {
             const int I = w - 1;
-            f32x16 c;
-            if constexpr (GDN) {
-                c = chain<kC / 2>([&](int s) { return Tm[(2 * s + kg) * LM + l32]; },
-                                  [&](int s) { return dUs[(2 * s + kg) * LV + 32 * I + l32]; }, f32x16{});
-                f32x16 x;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) x[e] = c[e] * Vs[row(e) * LV + 32 * I + l32];
-                store_row_sums(x, dbp + I * kC, l32, kg, 1.f);  // dbeta slots 0, 1
-#pragma unroll
-                for (int e = 0; e < 16; ++e) Vs[row(e) * LV + 32 * I + l32] = c[e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
-            }
+            const f32x16 c = chain<kC / 2>([&](int s) { return dUs[(2 * s + kg) * LV + 32 * I + l32]; },
+                                           [&](int s) { return Tm[(2 * s + kg) * LM + l32]; }, f32x16{});
+            float db = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int t = row(e);
-                if (c0 + t < T) J.dv_out[(tok0 + c0 + t) * dv + r0 + 32 * I + l32] = (GDN ? bet[t] : 1.f) * c[e];
+                const int y = l32 * LV + 32 * I + row(e);
+                db += c[e] * Vs[y];
+                Vs[y] = c[e];
             }
+            db += __shfl_xor(db, 32, 64);
+            if (kg == 0) dbp[I * kC + l32] = db;  // dbeta slots 0, 1
         }
         if (w < NJ) {
             accQ = chain<kC / 2>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
@@ -563,27 +559,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6 (dg: beta_t times it)
                 store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
             }
+            if (w >= 2) {  // <dRw_t, K_t> = -<dX_t, (K S^T)_t> over this wave's value columns
+                const int I = w - 2;
+                float wt = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) wt += ksT[e] * Vs[l32 * LV + 32 * I + row(e)];
+                wt = -(wt + __shfl_xor(wt, 32, 64));
+                if (kg == 0) {
+                    dbp[(2 + I) * kC + l32] = gam[l32] * wt;  // dbeta slots 2, 3
+                    dgp[(10 + I) * kC + l32] = bg[l32] * wt;  // dg slots 10, 11
+                }
+            }
             if (w < NJ) {  // dRw = -dX S
                 const f32x16 c = chain<kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
                                                 [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; },
                                                 f32x16{});
-                f32x16 x;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = row(e);
-                    accK[e] += bg[t] * c[e];
-                    x[e] = c[e] * Ks[t * L1 + 32 * w + l32];
-                }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float s = sum32(x[e]);
-                    if (l32 == 0) {
-                        const int t = row(e);
-                        dbp[(2 + w) * kC + t] = gam[t] * s;  // dbeta slots 2..5
-                        dgp[(10 + w) * kC + t] = bg[t] * s;  // dg slots 10..13
-                    }
-                }
+                for (int e = 0; e < 16; ++e) accK[e] += bg[row(e)] * c[e];
             }
+        }
+        // dV = diag(beta) dX (delta rule) or dU (linear attention), row-major from LDS
+        for (int x = tid; x < kC * kSL; x += kThreads) {
+            const int t = x / kSL, i = x % kSL;
+            if (c0 + t < T)
+                J.dv_out[(tok0 + c0 + t) * dv + r0 + i] = GDN ? bet[t] * Vs[t * LV + i] : dUs[t * LV + i];
         }
         // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K, and <dS', S>
         for (int tile = w; tile < 2 * NJ; tile += 4) {
