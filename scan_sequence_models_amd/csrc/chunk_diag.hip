@@ -178,8 +178,9 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 //   1. q, k, log2 a and the value slice come in; log2 a is summed along the
 //      chunk per channel;
 //   2. the decayed Gram A and scores P over the 496 strictly lower token pairs
-//      (one exp2 per pair and channel, float4 loads along the channels; the
-//      diagonal of P needs no exponential), and the scaled copies q gamma,
+//      (one exp2 per pair and channel, float4 loads along the channels, two
+//      pairs per thread sharing token t's loads; the diagonal of P needs no
+//      exponential), and the scaled copies q gamma,
 //      -beta k gamma and k e^{g_C - g};
 //   3. T = (I + A)^-1 by one wave (a lane per column, forward substitution with
 //      the rows of A read as float4), beside X = R_v - R_w S^T and the start of
@@ -192,7 +193,6 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 constexpr int kSL = 64;      // value rows per workgroup
 constexpr int kLT = kC + 4;  // row stride of the 32x32 T and P tiles (float4 rows)
-constexpr int kPairs = kC * (kC - 1) / 2;
 
 template <int MODE, int DK, typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_diag_mfma_kernel(
@@ -296,33 +296,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         __syncthreads();
-        // decayed Gram and scores over the strictly lower pairs s < t
-        for (int p = tid; p < kPairs; p += kThreads) {
-            int t = (int)((1.f + __builtin_sqrtf(1.f + 8.f * (float)p)) * 0.5f);
-            if (t * (t - 1) / 2 > p) --t;
-            if (t * (t + 1) / 2 <= p) ++t;
-            const int s = p - t * (t - 1) / 2;
+        // decayed Gram and scores over the strictly lower pairs s < t, two pairs (t, 2b) and
+        // (t, 2b + 1) per thread so that they share the loads of token t: row t holds
+        // ceil(t / 2) such blocks, floor(t^2 / 4) of them precede it, and rows 1 .. 31 hold
+        // exactly 256, one per thread (the second pair of the last block of an odd row is the
+        // diagonal, which is not stored here)
+        {
+            static_assert(kC == 32 && kThreads == 256, "one Gram block per thread");
+            const int p = tid;
+            int t = (int)__builtin_sqrtf(4.f * (float)p + 1.f);
+            if ((t * t) / 4 > p) --t;
+            if (((t + 1) * (t + 1)) / 4 <= p) ++t;
+            const int s1 = 2 * (p - (t * t) / 4), s2 = s1 + 1;
             const float4* gt = reinterpret_cast<const float4*>(Gs + t * L4);
-            const float4* gs = reinterpret_cast<const float4*>(Gs + s * L4);
             const float4* kt = reinterpret_cast<const float4*>(Ks + t * L4);
-            const float4* ksv = reinterpret_cast<const float4*>(Ks + s * L4);
             const float4* qt = reinterpret_cast<const float4*>(Qs + t * L4);
-            float pa = 0.f, pp = 0.f;
-#pragma unroll 4
+            const float4* g1p = reinterpret_cast<const float4*>(Gs + s1 * L4);
+            const float4* k1p = reinterpret_cast<const float4*>(Ks + s1 * L4);
+            const float4* g2p = reinterpret_cast<const float4*>(Gs + s2 * L4);
+            const float4* k2p = reinterpret_cast<const float4*>(Ks + s2 * L4);
+            float pa1 = 0.f, pp1 = 0.f, pa2 = 0.f, pp2 = 0.f;
+#pragma unroll 2
             for (int c = 0; c < DK / 4; ++c) {
-                const float4 g1 = gt[c], g0 = gs[c], k0 = ksv[c], q1 = qt[c];
-                const float e0 = __builtin_amdgcn_exp2f(g1.x - g0.x) * k0.x;
-                const float e1 = __builtin_amdgcn_exp2f(g1.y - g0.y) * k0.y;
-                const float e2 = __builtin_amdgcn_exp2f(g1.z - g0.z) * k0.z;
-                const float e3 = __builtin_amdgcn_exp2f(g1.w - g0.w) * k0.w;
-                pp += q1.x * e0 + q1.y * e1 + q1.z * e2 + q1.w * e3;
+                const float4 g = gt[c], q = qt[c], ga = g1p[c], ka = k1p[c], gb = g2p[c], kb = k2p[c];
+                const float a0 = __builtin_amdgcn_exp2f(g.x - ga.x) * ka.x;
+                const float a1 = __builtin_amdgcn_exp2f(g.y - ga.y) * ka.y;
+                const float a2 = __builtin_amdgcn_exp2f(g.z - ga.z) * ka.z;
+                const float a3 = __builtin_amdgcn_exp2f(g.w - ga.w) * ka.w;
+                const float b0 = __builtin_amdgcn_exp2f(g.x - gb.x) * kb.x;
+                const float b1 = __builtin_amdgcn_exp2f(g.y - gb.y) * kb.y;
+                const float b2 = __builtin_amdgcn_exp2f(g.z - gb.z) * kb.z;
+                const float b3 = __builtin_amdgcn_exp2f(g.w - gb.w) * kb.w;
+                pp1 += q.x * a0 + q.y * a1 + q.z * a2 + q.w * a3;
+                pp2 += q.x * b0 + q.y * b1 + q.z * b2 + q.w * b3;
                 if constexpr (GDN) {
-                    const float4 k1 = kt[c];
-                    pa += k1.x * e0 + k1.y * e1 + k1.z * e2 + k1.w * e3;
+                    const float4 k = kt[c];
+                    pa1 += k.x * a0 + k.y * a1 + k.z * a2 + k.w * a3;
+                    pa2 += k.x * b0 + k.y * b1 + k.z * b2 + k.w * b3;
                 }
             }
-            if constexpr (GDN) Am[t * kC + s] = bet[t] * pa;
-            Pm[t * kLT + s] = pp;
+            if constexpr (GDN) Am[t * kC + s1] = bet[t] * pa1;
+            Pm[t * kLT + s1] = pp1;
+            if (s2 < t) {
+                if constexpr (GDN) Am[t * kC + s2] = bet[t] * pa2;
+                Pm[t * kLT + s2] = pp2;
+            }
         }
         if (tid < 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
             const int t = tid >> 2, part = tid & 3;
