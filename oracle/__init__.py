@@ -171,13 +171,12 @@ def scan_bwd(mode, q, k, v, alpha, beta=None, S0=None, dO=None, dST=None,
     """Gradients of L = sum <dO, o> + <dST, S_T> of ``scan`` with respect to
     every input, in float64 (inputs are taken as float64, unrounded).
 
-    Shapes as in ``scan`` (modes "gdn", "gla", "gdn_diag", "gla_diag"); dO like
-    o ([..., T, dv]) or None (zero), dST like S_T or None (zero).
+    Shapes as in ``scan`` (every mode; "gdn_ew" takes beta [2, ..., T], erase
+    then write strengths, and returns dbeta in the same layout); dO like o
+    ([..., T, dv]) or None (zero), dST like S_T or None (zero).
     Returns (dq, dk, dv, dalpha, dbeta or None, dS0).
     """
     m = _mode(mode)
-    if m == GDN_EW:
-        raise ValueError("scan_bwd covers modes gdn, gla, gdn_diag, gla_diag")
     q, k, v, alpha = _f64(q), _f64(k), _f64(v), _f64(alpha)
     lead = q.shape[:-2]
     T, dk = q.shape[-2:]
@@ -187,10 +186,11 @@ def scan_bwd(mode, q, k, v, alpha, beta=None, S0=None, dO=None, dST=None,
     if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or \
             alpha.shape != (q.shape if diag else q.shape[:-1]):
         raise ValueError("shape mismatch among q, k, v, alpha")
-    delta = m in (GDN, GDN_DIAG)
+    delta = m in (GDN, GDN_DIAG, GDN_EW)
+    bshape = (2, *q.shape[:-1]) if m == GDN_EW else q.shape[:-1]
     if delta:
         beta = _f64(beta)
-        if beta is None or beta.shape != q.shape[:-1]:
+        if beta is None or beta.shape != bshape:
             raise ValueError("beta shape mismatch")
     else:
         beta = None
@@ -203,7 +203,7 @@ def scan_bwd(mode, q, k, v, alpha, beta=None, S0=None, dO=None, dST=None,
         raise ValueError("dST shape mismatch")
     gq, gk, gv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     ga = np.empty_like(alpha)
-    gb = np.empty(q.shape[:-1], np.float64) if delta else None
+    gb = np.empty(bshape, np.float64) if delta else None
     gS0 = np.empty((*lead, dv, dk), np.float64)
     n = _load().oracle_scan_bwd_f64(m, BH, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                     _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(gq), _ptr(gk),

@@ -232,6 +232,7 @@ int oracle_decode_f64(int mode, int64_t N, int dk, int dv,
  *   forward   x = d_t * s_{t-1}            (elementwise)
  *             p = x . k_t
  *             s_t = x + beta_t (v_ti - p) k_t       [delta rule, modes 0, 3]
+ *             s_t = x - be_t p k_t + bw_t v_ti k_t  [split strengths, mode 2]
  *             s_t = x + v_ti k_t                    [linear attention, modes 1, 4]
  *             o_ti = s_t . q_t
  *   backward  with y the gradient reaching s_t (dST's row at t = T):
@@ -241,6 +242,8 @@ int oracle_decode_f64(int mode, int64_t N, int dk, int dv,
  *                          dbeta_t += yk (v_ti - p)
  *                          dk_t += beta_t (v_ti - p) y - beta_t yk x
  *                          dx = y - beta_t yk k_t
+ *             split strengths:  dv_ti = bw_t yk,  dbe_t -= yk p,  dbw_t += yk v_ti,
+ *                               dk_t += (bw_t v_ti - be_t p) y - be_t yk x,  dx = y - be_t yk k_t
  *             linear attention:  dv_ti = y . k_t,  dk_t += v_ti y,  dx = y
  *             dd_t += dx * s_{t-1}  (summed over key channels for a scalar gate)
  *             y <- dx * d_t        (the gradient reaching s_{t-1})
@@ -249,7 +252,7 @@ int oracle_decode_f64(int mode, int64_t N, int dk, int dv,
  * backward sweep reads s_{t-1} and s_t as stored.  Rows are taken in order
  * 0 .. d_v - 1 and the shared gradients (dq, dk, dalpha, dbeta) accumulate in
  * that order, one thread per head, so results do not depend on thread count.
- * Modes 0, 1, 3, 4; every input is float64 (no rounding on the way in), so
+ * Modes 0 to 4; every input is float64 (no rounding on the way in), so
  * finite differences of the same function can check it.
  */
 typedef struct {
@@ -267,8 +270,10 @@ static int bwd_head(const bjob_t *J, int64_t h)
     const int dk = J->dk, dv = J->dv;
     const int64_t T = J->T;
     const int diag = J->mode == ORACLE_GDN_DIAG || J->mode == ORACLE_GLA_DIAG;
-    const int delta = J->mode == ORACLE_GDN || J->mode == ORACLE_GDN_DIAG;
+    const int delta = J->mode == ORACLE_GDN || J->mode == ORACLE_GDN_DIAG || J->mode == ORACLE_GDN_EW;
+    const int split = J->mode == ORACLE_GDN_EW;
     const int da = diag ? dk : 1;  /* decay entries per token */
+    const size_t wplane = (size_t)(J->BH * T);  /* offset of the write-strength plane (mode 2) */
     double *traj = (double *)malloc(sizeof(double) * (size_t)(T + 1) * (size_t)dk);
     double *x = (double *)malloc(sizeof(double) * (size_t)dk);
     double *y = (double *)malloc(sizeof(double) * (size_t)dk);
@@ -285,6 +290,7 @@ static int bwd_head(const bjob_t *J, int64_t h)
         }
         for (int j = 0; j < da; ++j) J->galpha[(tok0 + t) * da + j] = 0.0;
         if (J->gbeta) J->gbeta[tok0 + t] = 0.0;
+        if (split) J->gbeta[wplane + tok0 + t] = 0.0;
     }
     for (int i = 0; i < dv; ++i) {
         const size_t srow = ((size_t)h * dv + i) * dk;
@@ -298,9 +304,10 @@ static int bwd_head(const bjob_t *J, int64_t h)
             for (int j = 0; j < dk; ++j) x[j] = (diag ? J->alpha[tok * dk + j] : J->alpha[tok]) * s0[j];
             if (delta) {
                 const double be = J->beta[tok];
+                const double bw = split ? J->beta[wplane + tok] : be;
                 double p = 0.0;
                 for (int j = 0; j < dk; ++j) p += x[j] * kt[j];
-                for (int j = 0; j < dk; ++j) s1[j] = x[j] + be * (vi - p) * kt[j];
+                for (int j = 0; j < dk; ++j) s1[j] = x[j] + (bw * vi - be * p) * kt[j];
             } else {
                 for (int j = 0; j < dk; ++j) s1[j] = x[j] + vi * kt[j];
             }
@@ -323,12 +330,18 @@ static int bwd_head(const bjob_t *J, int64_t h)
             for (int j = 0; j < dk; ++j) yk += y[j] * kt[j];
             if (delta) {
                 const double be = J->beta[tok];
+                const double bw = split ? J->beta[wplane + tok] : be;
                 double p = 0.0;
                 for (int j = 0; j < dk; ++j) p += x[j] * kt[j];
-                J->gv[tok * dv + i] = be * yk;
-                J->gbeta[tok] += yk * (vi - p);
+                J->gv[tok * dv + i] = bw * yk;
+                if (split) {
+                    J->gbeta[tok] -= yk * p;
+                    J->gbeta[wplane + tok] += yk * vi;
+                } else {
+                    J->gbeta[tok] += yk * (vi - p);
+                }
                 for (int j = 0; j < dk; ++j) {
-                    J->gk[tok * dk + j] += be * (vi - p) * y[j] - be * yk * x[j];
+                    J->gk[tok * dk + j] += (bw * vi - be * p) * y[j] - be * yk * x[j];
                     dx[j] = y[j] - be * yk * kt[j];
                 }
             } else {
@@ -367,10 +380,11 @@ static void *bwd_worker(void *arg)
 /*
  * Gradients of L = sum <dO, o> + <dST, S_T> with respect to every input.
  *   q, k: [BH, T, dk]   v: [BH, T, dv]   alpha: [BH, T] ([BH, T, dk] in modes 3, 4)
- *   beta: [BH, T] (modes 0, 3; NULL in modes 1, 4)   S0: [BH, dv, dk] or NULL (zero)
+ *   beta: [BH, T] (modes 0, 3; NULL in modes 1, 4; [2, BH, T] in mode 2: erase, then
+ *         write strengths)   S0: [BH, dv, dk] or NULL (zero)
  *   dO: [BH, T, dv] or NULL (zero)   dST: [BH, dv, dk] or NULL (zero)
  *   outputs: gq, gk like q; gv like v; galpha like alpha; gbeta like beta (modes
- *   0, 3; may be NULL otherwise); gS0 [BH, dv, dk].  All float64.
+ *   0, 2, 3; may be NULL otherwise); gS0 [BH, dv, dk].  All float64.
  * Returns the number of threads used, or -1 on bad arguments or allocation
  * failure.
  */
@@ -381,10 +395,9 @@ int oracle_scan_bwd_f64(int mode, int64_t BH, int64_t T, int dk, int dv,
                         double *gq, double *gk, double *gv, double *galpha, double *gbeta,
                         double *gS0, int nthreads)
 {
-    if (!(mode == ORACLE_GDN || mode == ORACLE_GLA || mode == ORACLE_GDN_DIAG || mode == ORACLE_GLA_DIAG))
-        return -1;
+    if (mode < ORACLE_GDN || mode > ORACLE_GLA_DIAG) return -1;
     if (BH < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
-    const int delta = mode == ORACLE_GDN || mode == ORACLE_GDN_DIAG;
+    const int delta = mode == ORACLE_GDN || mode == ORACLE_GDN_DIAG || mode == ORACLE_GDN_EW;
     if (BH * T > 0 && (!q || !k || !v || !alpha || !gq || !gk || !gv || !galpha)) return -1;
     if (delta && BH * T > 0 && (!beta || !gbeta)) return -1;
     if (BH > 0 && !gS0) return -1;

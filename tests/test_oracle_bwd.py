@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 
-MODES = ["gdn", "gla", "gdn_diag", "gla_diag"]
+MODES = ["gdn", "gla", "gdn_diag", "gla_diag", "gdn_ew"]
 
 
 def _inputs(rng, mode, T, dk, dv, f32=False):
@@ -25,7 +25,7 @@ def _inputs(rng, mode, T, dk, dv, f32=False):
     k /= np.linalg.norm(k, axis=1, keepdims=True)
     v = rng.standard_normal((T, dv))
     a = rng.uniform(0.6, 1.0, (T, dk) if mode.endswith("diag") else T)
-    beta = rng.uniform(0.05, 1.0, T) if mode.startswith("gdn") else None
+    beta = rng.uniform(0.05, 1.0, (2, T) if mode == "gdn_ew" else T) if mode.startswith("gdn") else None
     S0 = 0.5 * rng.standard_normal((dv, dk))
     dO = rng.standard_normal((T, dv))
     dST = rng.standard_normal((dv, dk))
@@ -41,7 +41,10 @@ def _dense_loss(mode, q, k, v, a, beta, S0, dO, dST):
     L = 0.0
     for t in range(T):
         d = a[t] if mode.endswith("diag") else np.full(dk, a[t])
-        if mode.startswith("gdn"):
+        if mode == "gdn_ew":  # erase strength in E, write strength in f
+            E = np.diag(d) @ (np.eye(dk) - beta[0, t] * np.outer(k[t], k[t]))
+            f = beta[1, t] * np.outer(v[t], k[t])
+        elif mode.startswith("gdn"):
             E = np.diag(d) @ (np.eye(dk) - beta[t] * np.outer(k[t], k[t]))
             f = beta[t] * np.outer(v[t], k[t])
         else:
@@ -134,3 +137,17 @@ def test_batched_heads_match_single_heads():
         gh = oracle.scan_bwd("gdn", *h, threads=1)
         for x, y in zip(g, gh):
             np.testing.assert_array_equal(x[n], y)
+
+
+def test_split_strengths_equal_planes_are_the_delta_rule():
+    """Equal erase and write strengths give the delta rule's gradients, and the
+    two planes of dbeta add up to its dbeta."""
+    rng = np.random.default_rng(16)
+    T, dk, dv = 30, 5, 4
+    q, k, v, a, beta, S0, dO, dST = _inputs(rng, "gdn", T, dk, dv)
+    g1 = oracle.scan_bwd("gdn", q, k, v, a, beta, S0, dO, dST)
+    g2 = oracle.scan_bwd("gdn_ew", q, k, v, a, np.stack([beta, beta]), S0, dO, dST)
+    for i in (0, 1, 2, 3, 5):
+        np.testing.assert_allclose(g1[i], g2[i], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g1[4], g2[4][0] + g2[4][1], rtol=1e-12, atol=1e-12)
+
