@@ -206,12 +206,14 @@ int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
  * the prefix-scan notes, key design 2, define the affine state update it
  * differentiates).  For incoming gradients dO (at o) and dST (at S_T) it
  * returns the gradients of L = sum <dO, o> + <dST, S_T> with respect to every
- * input of a SCAN_GDN or SCAN_GLA scan_fwd call with the same arguments:
+ * input of a SCAN_GDN, SCAN_GLA or SCAN_GDN_EW scan_fwd call with the same
+ * arguments:
  *   q, k : [B, H, T, dk] dtype       v, dO : [B, H, T, dv] dtype (dO NULL: zero)
- *   alpha: [B, H, T] float32 in (0, 1]    beta: [B, H, T] float32 (SCAN_GDN; NULL for SCAN_GLA)
+ *   alpha: [B, H, T] float32 in (0, 1]    beta: [B, H, T] float32 (SCAN_GDN; NULL for SCAN_GLA;
+ *          [2, B, H, T] for SCAN_GDN_EW: erase strengths, then write strengths)
  *   S0, dST: [B, H, dv, dk] float32 or NULL (zero)
  *   dq, dk_out: [B, H, T, dk] float32    dv_out: [B, H, T, dv] float32
- *   dalpha: [B, H, T] float32        dbeta: [B, H, T] float32 (SCAN_GDN; NULL for SCAN_GLA)
+ *   dalpha: [B, H, T] float32        dbeta: like beta, float32 (NULL for SCAN_GLA)
  *   dS0: [B, H, dv, dk] float32 (the gradient at the initial state, also when S0 is NULL)
  *   workspace: scan_bwd_workspace_size(...) bytes of device scratch, 256-byte
  *          aligned (the state entering every 32-token chunk, and per value-slice

@@ -345,9 +345,10 @@ def scan_bwd_workspace_size(mode: int, dtype: int, B: int, H: int, T: int, dk: i
 
 
 def scan_bwd(q, k, v, alpha, beta=None, S0=None, dO=None, dST=None, *, workspace=None, out=None):
-    """Gradients of a scan_fwd call (gated delta rule when ``beta`` is given,
-    gated linear attention when it is None) for incoming gradients dO (at o,
-    dtype of q; None: zero) and dST (at S_T, float32; None: zero).
+    """Gradients of a scan_fwd call (gated delta rule when ``beta`` is a
+    [B, H, T] tensor, with split strengths when it is [2, B, H, T], gated linear
+    attention when it is None) for incoming gradients dO (at o, dtype of q;
+    None: zero) and dST (at S_T, float32; None: zero).
 
     Returns (dq, dk, dv, dalpha, dbeta or None, dS0), all float32; ``out`` may
     give those six tensors preallocated.
@@ -361,9 +362,10 @@ def scan_bwd(q, k, v, alpha, beta=None, S0=None, dO=None, dST=None, *, workspace
     _need(k, "k", dt, (B, H, T, dk), dev)
     _need(v, "v", dt, (B, H, T, dv), dev)
     _need(alpha, "alpha", torch.float32, (B, H, T), dev)
-    mode = SCAN_GLA if beta is None else SCAN_GDN
+    mode = SCAN_GLA if beta is None else SCAN_GDN_EW if beta.dim() == 4 else SCAN_GDN
+    bshape = (2, B, H, T) if mode == SCAN_GDN_EW else (B, H, T)
     if beta is not None:
-        _need(beta, "beta", torch.float32, (B, H, T), dev)
+        _need(beta, "beta", torch.float32, bshape, dev)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, dv, dk), dev)
     if dO is not None:
@@ -371,7 +373,7 @@ def scan_bwd(q, k, v, alpha, beta=None, S0=None, dO=None, dST=None, *, workspace
     if dST is not None:
         _need(dST, "dST", torch.float32, (B, H, dv, dk), dev)
     f32 = torch.float32
-    shapes = [(B, H, T, dk), (B, H, T, dk), (B, H, T, dv), (B, H, T), (B, H, T), (B, H, dv, dk)]
+    shapes = [(B, H, T, dk), (B, H, T, dk), (B, H, T, dv), (B, H, T), bshape, (B, H, dv, dk)]
     if out is None:
         out = [None if (i == 4 and beta is None) else torch.empty(sh, dtype=f32, device=dev)
                for i, sh in enumerate(shapes)]

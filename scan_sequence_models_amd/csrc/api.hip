@@ -371,8 +371,8 @@ int lact_fwd(int dtype, int B, int H, int T, int dk, int dv, int chunk, int orde
 namespace {
 // Validates the sizes of a scan_bwd call; returns SCAN_OK and the workspace bytes.
 int plan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv, size_t* ws) {
-    if (mode != SCAN_GDN && mode != SCAN_GLA)
-        return fail(SCAN_EUNSUPPORTED, "scan_bwd supports SCAN_GDN and SCAN_GLA (got mode %d)", mode);
+    if (mode != SCAN_GDN && mode != SCAN_GLA && mode != SCAN_GDN_EW)
+        return fail(SCAN_EUNSUPPORTED, "scan_bwd supports SCAN_GDN, SCAN_GLA and SCAN_GDN_EW (got mode %d)", mode);
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
     if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1)
         return fail(SCAN_EINVAL, "B, H, T, dk, dv must be >= 1 (got %d, %d, %d, %d, %d)", B, H, T, dk, dv);
@@ -399,10 +399,11 @@ int scan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv, const voi
     size_t need = 0;
     int st = plan_bwd(mode, dtype, B, H, T, dk, dv, &need);
     if (st != SCAN_OK) return st;
-    const bool gdn = mode == SCAN_GDN;
+    const bool gdn = mode != SCAN_GLA;
+    const size_t planes = mode == SCAN_GDN_EW ? 2 : 1;
     if (!q || !k || !v || !alpha || !dq || !dk_out || !dv_out || !dalpha || !dS0)
         return fail(SCAN_EINVAL, "q, k, v, alpha, dq, dk, dv, dalpha and dS0 must be non-null");
-    if (gdn && (!beta || !dbeta)) return fail(SCAN_EINVAL, "SCAN_GDN needs beta and dbeta");
+    if (gdn && (!beta || !dbeta)) return fail(SCAN_EINVAL, "the delta rule needs beta and dbeta");
     if (!gdn && (beta || dbeta)) return fail(SCAN_EINVAL, "SCAN_GLA takes no beta and no dbeta (pass NULL)");
     const void* a16[] = {q, k, v, dO, S0, dST, dq, dk_out, dv_out, dS0};
     const char* n16[] = {"q", "k", "v", "dO", "S0", "dST", "dq", "dk", "dv", "dS0"};
@@ -418,11 +419,11 @@ int scan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv, const voi
     const size_t BH = (size_t)B * H;
     const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
                         range("v", v, BH * T * dv * es), range("alpha", alpha, BH * T * 4),
-                        range("beta", beta, BH * T * 4), range("S0", S0, BH * dv * dk * 4),
+                        range("beta", beta, planes * BH * T * 4), range("S0", S0, BH * dv * dk * 4),
                         range("dO", dO, BH * T * dv * es), range("dST", dST, BH * dv * dk * 4)};
     const Range out[] = {range("dq", dq, BH * T * dk * 4), range("dk", dk_out, BH * T * dk * 4),
                          range("dv", dv_out, BH * T * dv * 4), range("dalpha", dalpha, BH * T * 4),
-                         range("dbeta", dbeta, BH * T * 4), range("dS0", dS0, BH * dv * dk * 4),
+                         range("dbeta", dbeta, planes * BH * T * 4), range("dS0", dS0, BH * dv * dk * 4),
                          range("workspace", workspace, need)};
     for (size_t a = 0; a < sizeof(out) / sizeof(out[0]); ++a) {
         for (const Range& r : in)
@@ -433,7 +434,9 @@ int scan_bwd(int mode, int dtype, int B, int H, int T, int dk, int dv, const voi
     gds::BwdJob j{};
     j.q = q; j.k = k; j.v = v; j.dO = dO;
     j.alpha = alpha; j.beta = beta; j.S0 = S0; j.dST = dST;
+    j.beta_w = planes == 2 ? beta + BH * T : beta;
     j.dq = dq; j.dk_out = dk_out; j.dv_out = dv_out; j.dalpha = dalpha; j.dbeta = dbeta; j.dS0 = dS0;
+    j.dbeta_w = planes == 2 ? dbeta + BH * T : nullptr;
     j.ckpt = static_cast<float*>(workspace);
     j.BH = (int)BH; j.T = T; j.dk = dk; j.dv = dv;
     hipError_t e = gds::launch_scan_bwd(gdn ? 0 : 1, dtype == SCAN_BF16 ? 1 : 0, j, static_cast<hipStream_t>(stream));

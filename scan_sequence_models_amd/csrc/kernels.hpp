@@ -66,7 +66,9 @@ hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk,
 struct BwdJob {
     const void *q, *k, *v, *dO;             // element type of dtype; dO may be null (zero)
     const float *alpha, *beta, *S0, *dST;   // beta null for linear attention; S0, dST may be null
+    const float* beta_w;                    // write strengths; == beta unless split
     float *dq, *dk_out, *dv_out, *dalpha, *dbeta, *dS0;  // dbeta null for linear attention
+    float* dbeta_w;                         // split strengths: gradient of the write plane; else null
     float* ckpt;                            // workspace: states entering each chunk, then partials
     float* part;                            // set by launch_scan_bwd
     int BH, T, dk, dv, nchunks;

@@ -19,6 +19,8 @@
 //   dK  = diag(e^{g_C-g}) U dS' + (dP o Gamma)^T Q - diag(beta gamma) dX S
 //         + (dKK + dKK^T) K,     dKK = diag(beta) dA o Gamma
 //   dV  = diag(beta) dX          (GLA: dV = dU)
+// With split strengths (erase beta in E, write bw in f), bw replaces beta in X's
+// V term and in dV, and <dX_t, V_t> is the write strength's gradient.
 //   dA  = strict_lower(-dX U^T)  (because T (I + A) = I, -T^T dU X^T T^T = -dX U^T)
 //   dbeta_t = <dX_t, V_t> + gamma_t <dRw_t, K_t> + sum_s dA_ts B_ts,  dRw = -dX S
 //   dg_t    = gamma_t <(dO S)_t, Q_t> - e^{g_C-g_t} <(U dS')_t, K_t> + beta_t gamma_t <dRw_t, K_t>
@@ -85,16 +87,19 @@ __device__ __forceinline__ void store_col_sums(const f32x16& x, float* out, int 
     if (kg == 0) out[l32] = sign * s;
 }
 
-// Chunk gates by wave 0 (lanes 0..31 hold tokens, with their alpha and beta
-// already loaded): log2 cumulative decay G2, gamma = 2^G2, Dd = 2^(G2_C - G2),
-// beta and beta gamma; past T: identity tokens (alpha = 1, beta = 0).
+// Chunk gates by wave 0 (lanes 0..31 hold tokens, with their alpha and the
+// erase and write strengths already loaded): log2 cumulative decay G2,
+// gamma = 2^G2, Dd = 2^(G2_C - G2), beta (erase), bw (write) and beta gamma;
+// past T: identity tokens (alpha = 1, beta = 0).
 template <bool GDN>
-__device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, int c0, int T, int lane, float* G2,
-                                            float* gam, float* Dd, float* bet, float* bg, float* gC) {
+__device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, float w_raw, int c0, int T, int lane,
+                                            float* G2, float* gam, float* Dd, float* bet, float* bw, float* bg,
+                                            float* gC) {
     const int t = lane & 31;
     const bool in = c0 + t < T;
     float la = in ? __log2f(a_raw) : 0.f;
     const float b = (GDN && in) ? b_raw : 0.f;
+    const float bwv = (GDN && in) ? w_raw : 0.f;
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) {
         const float y = __shfl_up(la, off, 32);
@@ -107,6 +112,7 @@ __device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, int c0, in
         gam[t] = g;
         Dd[t] = __builtin_amdgcn_exp2f(last - la);
         bet[t] = b;
+        bw[t] = bwv;
         bg[t] = b * g;
         if (t == 0) *gC = __builtin_amdgcn_exp2f(last);
     }
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     __shared__ float Ss[kSL * L1];
     __shared__ __align__(16) float Bm[GDN ? kC * LB : 4];
     __shared__ float Tm[GDN ? kC * LM : 1];
-    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bg[kC], gC[1];
+    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
 
     const int slices = J.dv / kSL;
     const int bh = blockIdx.x / slices;
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     // on the way into LDS), which hides HBM latency at one workgroup per CU.
     constexpr int NK = kC * DK / kThreads, NV = kC * kSL / kThreads;
     E pk[NK], pv[NV];
-    float pa = 1.f, pb = 0.f;
+    float pa = 1.f, pb = 0.f, pw = 0.f;
     auto fetch = [&](int cn) {
 #pragma unroll
         for (int m = 0; m < NK; ++m) {
@@ -199,7 +205,10 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
         if (w == 0) {
             const int t = min(cn + l32, T - 1);
             pa = J.alpha[tok0 + t];
-            if (GDN) pb = J.beta[tok0 + t];
+            if (GDN) {
+                pb = J.beta[tok0 + t];
+                pw = J.beta_w[tok0 + t];
+            }
         }
     };
     fetch(0);
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
             const int x = tid + m * kThreads, t = x / kSL;
             Us[t * LV + x % kSL] = c0 + t < T ? to_f32(pv[m]) : 0.f;
         }
-        if (w == 0) chunk_gates<GDN>(pa, pb, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        if (w == 0) chunk_gates<GDN>(pa, pb, pw, c0, T, lane, G2, gam, Dd, bet, bw, bg, gC);
         if (n + 1 < J.nchunks) fetch(c0 + kC);
         __syncthreads();
         if constexpr (GDN) {
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
                 const int I = w - 1;
                 f32x16 c;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = bet[row(e)] * Us[row(e) * LV + 32 * I + l32];
+                for (int e = 0; e < 16; ++e) c[e] = bw[row(e)] * Us[row(e) * LV + 32 * I + l32];
                 const float nbg = -bg[l32];
                 c = chain<DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
                                   [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; }, c);
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ float Tm[GDN ? kC * LM : 1];
     __shared__ float dQKm[kC * LM];  // dP o Gamma
     __shared__ float dKKm[GDN ? kC * LM : 1];
-    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bg[kC], gC[1];
+    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
     __shared__ float dgp[16 * kC];   // per-product contributions to dg (fixed slots)
     __shared__ float dbp[8 * kC];    // ... to dbeta
     __shared__ float dgc[16];        // ... to dg_C
@@ -320,6 +329,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     float* pdk = pdq + (size_t)slices * J.BH * T * DK;
     float* pdl = pdk + (size_t)slices * J.BH * T * DK;
     float* pdb = pdl + (size_t)slices * J.BH * T;
+    float* pdbw = pdb + (size_t)slices * J.BH * T;  // write strengths (split strengths only)
     auto row = [&](int e) { return acc_row(e, kg); };
 
     for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // ran slower.
     constexpr int NK = kC * DK / kThreads, NV = kC * kSL / kThreads;
     E pq[NK], pk[NK], pv[NV], pd[NV];
-    float pa = 1.f, pb = 0.f;
+    float pa = 1.f, pb = 0.f, pw = 0.f;
     auto fetch = [&](int n) {
         const int cn = n * kC;
 #pragma unroll
@@ -353,7 +363,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (w == 0) {
             const int t = min(cn + l32, T - 1);
             pa = J.alpha[tok0 + t];
-            if (GDN) pb = J.beta[tok0 + t];
+            if (GDN) {
+                pb = J.beta[tok0 + t];
+                pw = J.beta_w[tok0 + t];
+            }
         }
     };
     fetch(J.nchunks - 1);
@@ -397,7 +410,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int x = tid; x < 16 * kC; x += kThreads) dgp[x] = 0.f;
         for (int x = tid; x < 8 * kC; x += kThreads) dbp[x] = 0.f;
         if (tid < 16) dgc[tid] = 0.f;
-        if (w == 0) chunk_gates<GDN>(pa, pb, c0, T, lane, G2, gam, Dd, bet, bg, gC);
+        if (w == 0) chunk_gates<GDN>(pa, pb, pw, c0, T, lane, G2, gam, Dd, bet, bw, bg, gC);
         __syncthreads();
 
         f32x16 accQ = {}, accK = {};
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // is written row by row, and the tile serves <dX_t, (K S^T)_t> in phase 5 as an in-lane sum
             ksT = chain<DK / 2>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
                                 [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
-            const float b = bet[l32], nbg = -bg[l32];
+            const float b = bw[l32], nbg = -bg[l32];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int y = l32 * LV + 32 * I + row(e);
@@ -578,11 +591,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 for (int e = 0; e < 16; ++e) accK[e] += bg[row(e)] * c[e];
             }
         }
-        // dV = diag(beta) dX (delta rule) or dU (linear attention), row-major from LDS
+        // dV = diag(bw) dX (delta rule) or dU (linear attention), row-major from LDS
         for (int x = tid; x < kC * kSL; x += kThreads) {
             const int t = x / kSL, i = x % kSL;
             if (c0 + t < T)
-                J.dv_out[(tok0 + c0 + t) * dv + r0 + i] = GDN ? bet[t] * Vs[t * LV + i] : dUs[t * LV + i];
+                J.dv_out[(tok0 + c0 + t) * dv + r0 + i] = GDN ? bw[t] * Vs[t * LV + i] : dUs[t * LV + i];
         }
         // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K, and <dS', S>
         for (int tile = w; tile < 2 * NJ; tile += 4) {
@@ -651,12 +664,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const float y = __shfl_down(dg, off, 32);
                 if (t + off < 32) dg += y;
             }
-            float db = 0.f;
+            // dbeta slots 0, 1 belong to the write strength (they come from V), the rest to the erase one
+            const float dbw = dbp[t] + dbp[kC + t];
+            float dbe = 0.f;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) db += dbp[s * kC + t];
+            for (int s = 2; s < 8; ++s) dbe += dbp[s * kC + t];
             if (kg == 0 && c0 + t < T) {
                 pdl[part_tok + c0 + t] = dg;
-                pdb[part_tok + c0 + t] = db;
+                if (J.dbeta_w) {
+                    pdb[part_tok + c0 + t] = dbe;
+                    pdbw[part_tok + c0 + t] = dbw;
+                } else {
+                    pdb[part_tok + c0 + t] = dbe + dbw;
+                }
             }
         }
     }
@@ -673,6 +693,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdJob J) {
     const float* pdk = pdq + (size_t)slices * n_el;
     const float* pdl = pdk + (size_t)slices * n_el;
     const float* pdb = pdl + (size_t)slices * n_tok;
+    const float* pdbw = pdb + (size_t)slices * n_tok;
     for (size_t x = (size_t)blockIdx.x * kThreads + threadIdx.x; x < n_el; x += (size_t)gridDim.x * kThreads) {
         float a = 0.f, b = 0.f;
         for (int s = 0; s < slices; ++s) {
@@ -683,13 +704,15 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdJob J) {
         J.dk_out[x] = b;
         if (x % J.dk == 0) {
             const size_t tk = x / J.dk;
-            float l = 0.f, d = 0.f;
+            float l = 0.f, d = 0.f, dw = 0.f;
             for (int s = 0; s < slices; ++s) {
                 l += pdl[s * n_tok + tk];
                 d += pdb[s * n_tok + tk];
+                if (J.dbeta_w) dw += pdbw[s * n_tok + tk];
             }
             J.dalpha[tk] = l / J.alpha[tk];
             if (J.dbeta) J.dbeta[tk] = d;
+            if (J.dbeta_w) J.dbeta_w[tk] = dw;
         }
     }
 }
@@ -725,7 +748,7 @@ bool scan_bwd_supported(int dk, int dv) {
 size_t scan_bwd_workspace_floats(int BH, int T, int dk, int dv) {
     const size_t nchunks = ((size_t)T + kC - 1) / kC;
     const size_t slices = (size_t)dv / kSL;
-    return (size_t)BH * nchunks * dv * dk + slices * BH * T * (2 * (size_t)dk + 2);
+    return (size_t)BH * nchunks * dv * dk + slices * BH * T * (2 * (size_t)dk + 3);
 }
 
 hipError_t launch_scan_bwd(int mode, int dtype, BwdJob J, hipStream_t s) {

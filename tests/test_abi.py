@@ -202,7 +202,7 @@ def _bwd(lib, mode=0, dtype=1, B=1, H=2, T=64, dk=128, dv=128, q=FAKE, k=FAKE + 
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(mode=2), L.SCAN_EUNSUPPORTED),
+    (dict(mode=3), L.SCAN_EUNSUPPORTED),
     (dict(dtype=2), L.SCAN_EINVAL),
     (dict(T=0), L.SCAN_EINVAL),
     (dict(dk=96), L.SCAN_EUNSUPPORTED),
@@ -211,6 +211,9 @@ def _bwd(lib, mode=0, dtype=1, B=1, H=2, T=64, dk=128, dv=128, q=FAKE, k=FAKE + 
     (dict(beta=None), L.SCAN_EINVAL),                  # the delta rule needs beta
     (dict(mode=1), L.SCAN_EINVAL),                     # linear attention takes no beta
     (dict(dbeta=None), L.SCAN_EINVAL),
+    # split strengths: dbeta holds two planes of B*H*T floats (512 bytes each here), so
+    # its second plane would overlap dS0 (one plane would end right where dS0 starts)
+    (dict(mode=2, dbeta=FAKE + 13 * STEP - 512), L.SCAN_EINVAL),
     (dict(dS0=None), L.SCAN_EINVAL),
     (dict(ws=None), L.SCAN_EWORKSPACE),
     (dict(wsb=1024), L.SCAN_EWORKSPACE),
@@ -227,10 +230,12 @@ def test_scan_bwd_rejects(lib, kw, code):
 
 def test_scan_bwd_workspace_sizes(lib):
     # the state entering every 32-token chunk, then per-64-row-slice partials of
-    # dq, dk (dk floats per token) and of d ln alpha, dbeta (one float each)
+    # dq, dk (dk floats per token) and of d ln alpha and the two strength planes
+    # (one float each)
     n = lib.scan_bwd_workspace_size(0, 1, 8, 16, 8192, 128, 128)
-    assert n == 4 * (128 * 256 * 128 * 128 + 2 * 128 * 8192 * (2 * 128 + 2))
-    assert lib.scan_bwd_workspace_size(1, 0, 1, 1, 33, 32, 64) == 4 * (2 * 64 * 32 + 1 * 33 * 66)
+    assert n == 4 * (128 * 256 * 128 * 128 + 2 * 128 * 8192 * (2 * 128 + 3))
+    assert lib.scan_bwd_workspace_size(1, 0, 1, 1, 33, 32, 64) == 4 * (2 * 64 * 32 + 1 * 33 * 67)
+    assert lib.scan_bwd_workspace_size(2, 1, 1, 1, 64, 128, 128) == 4 * (2 * 128 * 128 + 2 * 64 * 259)
     assert lib.scan_bwd_workspace_size(0, 1, 1, 1, 64, 128, 96) == ctypes.c_size_t(-1).value
     assert lib.scan_bwd_workspace_size(3, 1, 1, 1, 64, 128, 128) == ctypes.c_size_t(-1).value
 

@@ -120,3 +120,27 @@ def test_scan_bwd_full_workload_sampled_heads():
         sel = [None if x is None else x[bb, hh][None] for x in got]
         refs = [None if r is None else r[None] for r in ref]
         _check(sel, refs, f"head ({bb},{hh})", head_dims=1)
+
+
+@pytest.mark.parametrize("dtype,T,dk,dv", [("f32", 90, 64, 64), ("bf16", 133, 128, 128)])
+def test_scan_bwd_split_strengths(dtype, T, dk, dv):
+    """SCAN_GDN_EW: erase strengths beta, write strengths bw (as in PRISM's
+    element stream); dbeta comes back in the same two planes."""
+    w = I.WORKLOADS["gdn-b8h16t8192"].replace(dtype=dtype, dk=dk, dv=dv)
+    B, H = 1, 2
+    say(f"scan_bwd split strengths {dtype} B{B} H{H} T{T} dk{dk} dv{dv}")
+    q, k, v, a, beta, S0, dO, dST = _batch(w, T, B, H)
+    bw = np.stack([np.stack([I.write_strengths(w, b, h, T) for h in range(H)]) for b in range(B)])
+    be2 = np.stack([beta, bw])
+    got = _run(w, q, k, v, a, be2, S0, dO, dST)
+    ref = oracle.scan_bwd("gdn_ew", q, k, v, a, be2, S0, dO, dST)
+    # dbeta [2, B, H, T]: compare each plane per head
+    _check(got[:4] + [None, got[5]], list(ref[:4]) + [None, ref[5]], f"ew {dtype} T{T}")
+    for pl, name in ((0, "erase"), (1, "write")):
+        e = max_err(got[4][pl], ref[4][pl], 2)
+        say(f"  dbeta {name} plane: {e:.2e}")
+        assert e <= GATE
+    # equal planes reduce to the delta rule: dbeta planes add up to its dbeta
+    g1 = _run(w, q, k, v, a, beta, S0, dO, dST)
+    g2 = _run(w, q, k, v, a, np.stack([beta, beta]), S0, dO, dST)
+    assert max_err(g2[4][0] + g2[4][1], g1[4], 2) <= GATE
