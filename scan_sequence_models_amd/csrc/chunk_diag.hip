@@ -175,24 +175,34 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 // The same chunk algorithm with its products on the float32 MFMA
 // (v_mfma_f32_32x32x2f32, fp32 accuracy) for slices of 64 value rows and
 // dk >= 32.  Per chunk:
-//   1. q, k, log2 a and the value slice come in; log2 a is summed along the
-//      chunk per channel;
-//   2. the decayed Gram A and scores P over the 496 strictly lower token pairs
-//      (one exp2 per pair and channel, float4 loads along the channels, two
-//      pairs per thread sharing token t's loads; the diagonal of P needs no
-//      exponential), and the scaled copies q gamma,
-//      -beta k gamma and k e^{g_C - g};
-//   3. T = (I + A)^-1 by one wave (a lane per column, forward substitution with
-//      the rows of A read as float4), beside X = R_v - R_w S^T and the start of
-//      O = (Q gamma) S^T on the other three waves;
-//   4. U = T X, then O += P U beside the state update
+//   1. q, k and log2 a arrive in registers, one key channel and a run of
+//      consecutive tokens per thread; log2 a is summed along the chunk there,
+//      the runs exchanging their totals through LDS.  The value slice goes to
+//      LDS;
+//   2. the scaled copies q gamma, -k gamma and k e^{g_C - g} are written
+//      from the registers, and so are the operands of the decayed Gram:
+//      splitting each pair's factor through the middle token m,
+//      e^{g_t - g_s} = e^{g_t - g_m} e^{g_m - g_s}, turns A and P into two
+//      plain 32x32 products of rows scaled by e^{+-(g - g_m)}.  In float32 that
+//      is safe while every |g_t - g_m| stays within kSpread (log2 units); a
+//      chunk with a wider span stores q, k and g instead and takes the
+//      pairwise form (one exp2 per token pair and channel);
+//   3. A and P on two waves beside X = V - (K gamma) S^T on the other two;
+//   4. T = (I + A)^-1 by one wave (a lane per column, forward substitution
+//      with the rows of A read as float4) beside O = (Q gamma) S^T on two more;
+//   5. U = T diag(beta) X; then O += P U beside the state update
 //      S <- S diag(gamma_C) + U^T (K e^{g_C - g}), all as 32x32 tiles.
-// U = T (R_v - R_w S^T) is the same product as T R_v - (T R_w) S^T, grouped so
-// that the key-long product does not wait for the inverse.
+// U = T (R_v - R_w S^T) = T diag(beta) (V - (K gamma) S^T) is the product
+// T R_v - (T R_w) S^T grouped so that the key-long part does not wait for the
+// inverse, with the strengths applied to the columns of T.
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 constexpr int kSL = 64;      // value rows per workgroup
 constexpr int kLT = kC + 4;  // row stride of the 32x32 T and P tiles (float4 rows)
+// widest |g_t - g_m| (log2) of the factored Gram: its operands stay within
+// 2^(+-64), far from float32 overflow, and a term lost to underflow there is
+// below 2^-62 of the unit-scale ones
+constexpr float kSpread = 64.f;
 
 template <int MODE, int DK, typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_diag_mfma_kernel(
@@ -200,27 +210,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     E* __restrict__ o, float* __restrict__ ST) {
     constexpr bool GDN = MODE == 0;
-    constexpr int NJ = DK / 32;  // 32-column tiles of a key-wide row
-    // Row strides.  The Gram reads float4 runs of channels with one token per
-    // lane: a stride of DK + 4 keeps those 16-byte loads aligned and spreads
-    // eight consecutive lanes over distinct bank groups.  The MFMA operands
-    // read one float per lane down a column: an odd stride (DK + 1) puts the
-    // 32 lanes into 32 banks.
+    constexpr int NJ = DK / 32;              // 32-column tiles of a key-wide row
+    constexpr int NQ = kC * DK / kThreads;   // tokens per thread, all of one key channel
+    constexpr int NR = kThreads / DK;        // runs of NQ tokens per chunk
+    constexpr int NV = kC * kSL / kThreads;  // value elements per thread and chunk
+    static_assert((kC / 2) % NQ == 0, "the middle token m = kC/2 - 1 ends a run");
+    static_assert(DK < 64 || kC * (DK + 4) >= 2048, "KA holds two partial O tiles");
+    // Row strides.  The pairwise Gram reads float4 runs of channels with one
+    // token per lane: a stride of DK + 4 keeps those 16-byte loads aligned and
+    // spreads eight consecutive lanes over distinct bank groups.  The MFMA
+    // operands read one float per lane down a column: an odd stride (DK + 1)
+    // puts the 32 lanes into 32 banks.
     constexpr int L4 = DK + 4;
     constexpr int L1 = DK + 1;
-    __shared__ __align__(16) float Qs[kC * L4];  // q
-    __shared__ __align__(16) float Ks[kC * L4];  // k
-    __shared__ __align__(16) float Gs[kC * L4];  // cumulative log2 decay
+    // Gram operands: q e^{g - g_m}, k e^{g - g_m} and k e^{g_m - g} (stride L1)
+    // in a factored chunk; q, k and the cumulative log2 decay g (stride L4) in a
+    // wide one
+    __shared__ __align__(16) float QA[kC * L4];
+    __shared__ __align__(16) float KA[kC * L4];
+    __shared__ __align__(16) float KB[kC * L4];
     __shared__ float Qg[kC * L1];                // q * gamma
-    __shared__ float Kt[kC * L1];                // k * e^{g_C - g}
-    __shared__ float Rw[GDN ? kC * L1 : 1];      // -beta (k * gamma)
-    __shared__ float Us[kC * kSL];               // v slice (GDN: beta v), then U
-    __shared__ __align__(16) float Am[GDN ? kC * kC : 1];  // A (strictly lower)
-    __shared__ float Tm[GDN ? kC * kLT : 1];
+    __shared__ float Kt[kC * L1];                // k * e^{g_C - g} (wide chunks)
+    __shared__ float Rw[GDN ? kC * L1 : 1];      // -(k * gamma)
+    __shared__ float Us[kC * kSL];               // v slice, then X (without beta), then U
+    __shared__ __align__(16) float Am[GDN ? kC * kC : 1];  // A without beta (strictly lower)
+    __shared__ float Tm[GDN ? kC * kLT : 1];     // T diag(beta)
     __shared__ float Pm[kC * kLT];               // P (lower, inclusive; zero above)
     __shared__ float Ss[kSL * L1];               // state slice
-    __shared__ float Ob[GDN ? 16 * 64 : 1];      // a partial O tile (accumulator layout)
-    __shared__ float bet[kC];
+    __shared__ float Gr[NR * DK];                // run totals of log2 a
+    __shared__ float sIn[DK];                    // per-channel factors of the state update:
+    __shared__ float sOut[DK];                   // e^{g_m}, e^{g_C - g_m} (wide: gamma_C, 1)
+    __shared__ __align__(16) float bet[kC];
 
     const int slices = dv / kSL;
     const int bh = blockIdx.x / slices;
@@ -228,6 +248,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, kg = lane >> 5;
+    const int ch = tid % DK, run = tid / DK;  // this thread's key channel and run of tokens
     const size_t qk_base = (size_t)bh * T * DK;
     const size_t v_base = (size_t)bh * T * dv;
     const size_t s_base = ((size_t)bh * dv + r0) * DK;
@@ -241,16 +262,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // computes (one wave per SIMD leaves no other way to hide HBM latency).
     // The loads are unconditional, from a token index clamped into the
     // sequence, and keep the raw element; masking and conversion happen when
-    // they are written to LDS, so no load waits inside the fetch.
-    constexpr int NQ = kC * DK / kThreads;   // key-wide elements per thread and chunk
-    constexpr int NV = kC * kSL / kThreads;  // value elements per thread and chunk
+    // they are used, so no load waits inside the fetch.
     E pq[NQ], pk[NQ], pv[NV];
     float pa[NQ], pb = 0.f;
     auto fetch = [&](int cn) {
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
-            const int x = tid + m * kThreads, t = min(cn + x / DK, T - 1);
-            const size_t gi = qk_base + (size_t)t * DK + x % DK;
+            const int t = min(cn + run * NQ + m, T - 1);
+            const size_t gi = qk_base + (size_t)t * DK + ch;
             pq[m] = q[gi];
             pk[m] = k[gi];
             pa[m] = alpha[gi];
@@ -264,134 +283,248 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     };
     fetch(0);
 
+    // c += A B^T over `steps` key steps from k0, A and B both read along key rows
+    // (A: 32 token rows, B: 32 state rows, row stride L1)
+    auto rows_dot = [&](const float* A, const float* B, auto steps, int k0, f32x16 c) {
+        return chain<decltype(steps)::value>([&](int s) { return A[l32 * L1 + 2 * (k0 + s) + kg]; },
+                                             [&](int s) { return B[l32 * L1 + 2 * (k0 + s) + kg]; }, c);
+    };
+    using Full = std::integral_constant<int, DK / 2>;
+    // c += P U or T X on value columns 32 I ..: B read along token rows of Us
+    auto tok_dot = [&](const float* A, int I, f32x16 c) {
+        return chain<kC / 2>([&](int s) { return A[l32 * kLT + 2 * s + kg]; },
+                             [&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; }, c);
+    };
+
     const int nchunks = (T + kC - 1) / kC;
     for (int n = 0; n < nchunks; ++n) {
         const int c0 = n * kC;
+        const int o0 = min(kC, T - c0);  // tokens of this chunk inside the sequence
         __syncthreads();  // the previous chunk is done with every array
-        // past T: identity tokens (a = 1, beta = 0, q = k = v = 0)
+        // 1. past T: identity tokens (a = 1, beta = 0, q = k = v = 0)
+        float g[NQ];
+        float acc = 0.f;
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
-            const int x = tid + m * kThreads, y = x / DK * L4 + x % DK;
-            const bool in = c0 + x / DK < T;
-            Qs[y] = in ? to_f32(pq[m]) : 0.f;
-            Ks[y] = in ? to_f32(pk[m]) : 0.f;
-            Gs[y] = in ? __log2f(pa[m]) : 0.f;
+            acc += run * NQ + m < o0 ? __log2f(pa[m]) : 0.f;
+            g[m] = acc;
+        }
+        Gr[run * DK + ch] = acc;
+        if (tid < kC) bet[tid] = tid < o0 ? pb : 0.f;
+        __syncthreads();
+        float off = 0.f, gm = 0.f, gc = 0.f;  // this run's offset, g_m, g_C
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float x = Gr[r * DK + ch];
+            if (r < run) off += x;
+            if (r < kC / 2 / NQ) gm += x;
+            gc += x;
+        }
+        bool narrow = true;  // false for a zero, infinite or NaN gate too
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            g[m] += off;
+            narrow = narrow && __builtin_fabsf(g[m] - gm) <= kSpread;
         }
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
             const int x = tid + m * kThreads;
-            Us[x] = c0 + x / kSL < T ? to_f32(pv[m]) : 0.f;
+            Us[x] = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
         }
-        if (tid < kC) bet[tid] = c0 + tid < T ? pb : 0.f;
+        const bool wide = __syncthreads_or(!narrow);
+        // 2. scaled copies and Gram operands.  The bases are opaque to the
+        // compiler, so each store below is one base register plus an immediate
+        // offset instead of an address hoisted out of the chunk loop.
+        int b1 = run * NQ * L1 + ch, b4 = run * NQ * L4 + ch;
+        asm volatile("" : "+v"(b1), "+v"(b4));
+        auto put = [&](auto factored) {
+            constexpr bool F = decltype(factored)::value;
+            // factored: gamma_t = e^{g_t - g_m} e^{g_m}, and k e^{g_C - g} is not
+            // formed (the state update scales by e^{g_C - g_m} per column instead)
+            const float em = __builtin_amdgcn_exp2f(gm);
+            if (run == 0) {
+                sIn[ch] = F ? em : __builtin_amdgcn_exp2f(gc);
+                sOut[ch] = F ? __builtin_amdgcn_exp2f(gc - gm) : 1.f;
+            }
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                const bool in = run * NQ + m < o0;
+                const float qq = in ? to_f32(pq[m]) : 0.f, kk = in ? to_f32(pk[m]) : 0.f;
+                const int y = b1 + m * L1;
+                if constexpr (F) {
+                    const float up = __builtin_amdgcn_exp2f(g[m] - gm), dn = __builtin_amdgcn_exp2f(gm - g[m]);
+                    const float qu = qq * up, ku = kk * up;
+                    QA[y] = qu;
+                    Qg[y] = qu * em;
+                    if constexpr (GDN) {
+                        KA[y] = ku;
+                        Rw[y] = -(ku * em);
+                    }
+                    KB[y] = kk * dn;
+                } else {
+                    const float gam = __builtin_amdgcn_exp2f(g[m]);
+                    Qg[y] = qq * gam;
+                    Kt[y] = kk * __builtin_amdgcn_exp2f(gc - g[m]);
+                    if constexpr (GDN) Rw[y] = -(kk * gam);
+                    const int z = b4 + m * L4;
+                    QA[z] = qq;
+                    KA[z] = kk;
+                    KB[z] = g[m];
+                }
+            }
+        };
+        if (wide) put(std::false_type{});
+        else put(std::true_type{});
         if (n + 1 < nchunks) fetch(c0 + kC);
         __syncthreads();
-        if constexpr (GDN)
-            for (int x = tid; x < kC * kSL; x += kThreads) Us[x] *= bet[x / kSL];
-        for (int c = tid; c < DK; c += kThreads) {
-            float run = 0.f;
-#pragma unroll 8
-            for (int t = 0; t < kC; ++t) {
-                run += Gs[t * L4 + c];
-                Gs[t * L4 + c] = run;
-            }
-        }
-        __syncthreads();
-        // decayed Gram and scores over the strictly lower pairs s < t, two pairs (t, 2b) and
-        // (t, 2b + 1) per thread so that they share the loads of token t: row t holds
-        // ceil(t / 2) such blocks, floor(t^2 / 4) of them precede it, and rows 1 .. 31 hold
-        // exactly 256, one per thread (the second pair of the last block of an odd row is the
-        // diagonal, which is not stored here)
-        {
+        if (wide) {
+            // decayed Gram and scores over the strictly lower pairs s < t, two pairs (t, 2b)
+            // and (t, 2b + 1) per thread so that they share the loads of token t: row t holds
+            // ceil(t / 2) such blocks, floor(t^2 / 4) of them precede it, and rows 1 .. 31
+            // hold exactly 256, one per thread (the second pair of the last block of an odd
+            // row is the diagonal, which is not stored here)
             static_assert(kC == 32 && kThreads == 256, "one Gram block per thread");
             const int p = tid;
             int t = (int)__builtin_sqrtf(4.f * (float)p + 1.f);
             if ((t * t) / 4 > p) --t;
             if (((t + 1) * (t + 1)) / 4 <= p) ++t;
             const int s1 = 2 * (p - (t * t) / 4), s2 = s1 + 1;
-            const float4* gt = reinterpret_cast<const float4*>(Gs + t * L4);
-            const float4* kt = reinterpret_cast<const float4*>(Ks + t * L4);
-            const float4* qt = reinterpret_cast<const float4*>(Qs + t * L4);
-            const float4* g1p = reinterpret_cast<const float4*>(Gs + s1 * L4);
-            const float4* k1p = reinterpret_cast<const float4*>(Ks + s1 * L4);
-            const float4* g2p = reinterpret_cast<const float4*>(Gs + s2 * L4);
-            const float4* k2p = reinterpret_cast<const float4*>(Ks + s2 * L4);
+            const float4* gt = reinterpret_cast<const float4*>(KB + t * L4);
+            const float4* kt = reinterpret_cast<const float4*>(KA + t * L4);
+            const float4* qt = reinterpret_cast<const float4*>(QA + t * L4);
+            const float4* g1p = reinterpret_cast<const float4*>(KB + s1 * L4);
+            const float4* k1p = reinterpret_cast<const float4*>(KA + s1 * L4);
+            const float4* g2p = reinterpret_cast<const float4*>(KB + s2 * L4);
+            const float4* k2p = reinterpret_cast<const float4*>(KA + s2 * L4);
             float pa1 = 0.f, pp1 = 0.f, pa2 = 0.f, pp2 = 0.f;
 #pragma unroll 2
             for (int c = 0; c < DK / 4; ++c) {
-                const float4 g = gt[c], q = qt[c], ga = g1p[c], ka = k1p[c], gb = g2p[c], kb = k2p[c];
-                const float a0 = __builtin_amdgcn_exp2f(g.x - ga.x) * ka.x;
-                const float a1 = __builtin_amdgcn_exp2f(g.y - ga.y) * ka.y;
-                const float a2 = __builtin_amdgcn_exp2f(g.z - ga.z) * ka.z;
-                const float a3 = __builtin_amdgcn_exp2f(g.w - ga.w) * ka.w;
-                const float b0 = __builtin_amdgcn_exp2f(g.x - gb.x) * kb.x;
-                const float b1 = __builtin_amdgcn_exp2f(g.y - gb.y) * kb.y;
-                const float b2 = __builtin_amdgcn_exp2f(g.z - gb.z) * kb.z;
-                const float b3 = __builtin_amdgcn_exp2f(g.w - gb.w) * kb.w;
-                pp1 += q.x * a0 + q.y * a1 + q.z * a2 + q.w * a3;
-                pp2 += q.x * b0 + q.y * b1 + q.z * b2 + q.w * b3;
+                const float4 gg = gt[c], qv = qt[c], ga = g1p[c], ka = k1p[c], gb = g2p[c], kb = k2p[c];
+                const float a0 = __builtin_amdgcn_exp2f(gg.x - ga.x) * ka.x;
+                const float a1 = __builtin_amdgcn_exp2f(gg.y - ga.y) * ka.y;
+                const float a2 = __builtin_amdgcn_exp2f(gg.z - ga.z) * ka.z;
+                const float a3 = __builtin_amdgcn_exp2f(gg.w - ga.w) * ka.w;
+                const float b0 = __builtin_amdgcn_exp2f(gg.x - gb.x) * kb.x;
+                const float b1 = __builtin_amdgcn_exp2f(gg.y - gb.y) * kb.y;
+                const float b2 = __builtin_amdgcn_exp2f(gg.z - gb.z) * kb.z;
+                const float b3 = __builtin_amdgcn_exp2f(gg.w - gb.w) * kb.w;
+                pp1 += qv.x * a0 + qv.y * a1 + qv.z * a2 + qv.w * a3;
+                pp2 += qv.x * b0 + qv.y * b1 + qv.z * b2 + qv.w * b3;
                 if constexpr (GDN) {
-                    const float4 k = kt[c];
-                    pa1 += k.x * a0 + k.y * a1 + k.z * a2 + k.w * a3;
-                    pa2 += k.x * b0 + k.y * b1 + k.z * b2 + k.w * b3;
+                    const float4 kk = kt[c];
+                    pa1 += kk.x * a0 + kk.y * a1 + kk.z * a2 + kk.w * a3;
+                    pa2 += kk.x * b0 + kk.y * b1 + kk.z * b2 + kk.w * b3;
                 }
             }
-            if constexpr (GDN) Am[t * kC + s1] = bet[t] * pa1;
+            if constexpr (GDN) Am[t * kC + s1] = pa1;
             Pm[t * kLT + s1] = pp1;
             if (s2 < t) {
-                if constexpr (GDN) Am[t * kC + s2] = bet[t] * pa2;
+                if constexpr (GDN) Am[t * kC + s2] = pa2;
                 Pm[t * kLT + s2] = pp2;
             }
-        }
-        if (tid < 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
-            const int t = tid >> 2, part = tid & 3;
-            const float4* qa = reinterpret_cast<const float4*>(Qs + t * L4) + part * (DK / 16);
-            const float4* ka = reinterpret_cast<const float4*>(Ks + t * L4) + part * (DK / 16);
-            float pp = 0.f;
+            if (tid < 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
+                const int td = tid >> 2, part = tid & 3;
+                const float4* qa = reinterpret_cast<const float4*>(QA + td * L4) + part * (DK / 16);
+                const float4* ka = reinterpret_cast<const float4*>(KA + td * L4) + part * (DK / 16);
+                float pp = 0.f;
 #pragma unroll
-            for (int c = 0; c < DK / 16; ++c) {
-                const float4 a = qa[c], b = ka[c];
-                pp += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+                for (int c = 0; c < DK / 16; ++c) {
+                    const float4 a = qa[c], b = ka[c];
+                    pp += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+                }
+                pp += dpp_move<0xB1>(pp);  // lane ^ 1
+                pp += dpp_move<0x4E>(pp);  // lane ^ 2
+                if (part == 0) Pm[td * kLT + td] = pp;
             }
-            pp += dpp_move<0xB1>(pp);  // lane ^ 1
-            pp += dpp_move<0x4E>(pp);  // lane ^ 2
-            if (part == 0) Pm[t * kLT + t] = pp;
+            __syncthreads();
         }
-        for (int x = tid; x < kC * DK; x += kThreads) {
-            const int t = x / DK, c = x - t * DK, y = t * L4 + c, z = t * L1 + c;
-            const float g = Gs[y];
-            const float gam = __builtin_amdgcn_exp2f(g);
-            Qg[z] = Qs[y] * gam;
-            Kt[z] = Ks[y] * __builtin_amdgcn_exp2f(Gs[(kC - 1) * L4 + c] - g);
-            if constexpr (GDN) Rw[z] = -(bet[t] * Ks[y] * gam);
-        }
-        __syncthreads();
-        // c += A B^T over `steps` key steps from k0, A and B both read along key rows
-        // (A: 32 token rows, B: 32 state rows, row stride L1)
-        auto rows_dot = [&](const float* A, const float* B, auto steps, int k0, f32x16 c) {
-            return chain<decltype(steps)::value>([&](int s) { return A[l32 * L1 + 2 * (k0 + s) + kg]; },
-                                                 [&](int s) { return B[l32 * L1 + 2 * (k0 + s) + kg]; }, c);
-        };
-        using Full = std::integral_constant<int, DK / 2>;
-        using Half = std::integral_constant<int, DK / 4>;
-        // c += P U or T X on value columns 32 I ..: B read along token rows of Us
-        auto tok_dot = [&](const float* A, int I, f32x16 c) {
-            return chain<kC / 2>([&](int s) { return A[l32 * kLT + 2 * s + kg]; },
-                                 [&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; }, c);
-        };
+        // factored Gram tile: C[t][s] = sum_i X_ti e^{g_ti - g_mi} k_si e^{g_mi - g_si}
+        auto gram = [&](const float* X) { return rows_dot(X, KB, Full{}, 0, f32x16{}); };
         auto store_o = [&](int I, const f32x16& c) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
-                if (c0 + t < T) io<E>::store(o, v_base + (size_t)(c0 + t) * dv + r0 + 32 * I + l32, c[e]);
+                if (t < o0) io<E>::store(o, v_base + (size_t)(c0 + t) * dv + r0 + 32 * I + l32, c[e]);
             }
         };
+        // O = (Q gamma) S^T: two waves take the first three quarters of the keys of
+        // one value tile each and a third wave the last quarter of both, its
+        // partial tiles passing through KA (free once the Gram is done)
+        constexpr bool kSplitO = DK >= 64;  // KA holds the two partial tiles
+        using OHead = std::integral_constant<int, kSplitO ? 3 * DK / 8 : DK / 2>;
+        auto o_tail = [&](int I) {
+            const f32x16 c = rows_dot(Qg, Ss + 32 * I * L1, std::integral_constant<int, DK / 8>{}, 3 * DK / 8,
+                                      f32x16{});
+#pragma unroll
+            for (int e = 0; e < 16; ++e) KA[I * 1024 + e * 64 + lane] = c[e];
+        };
+        auto o_add_tail = [&](int I, f32x16 c) {
+            if constexpr (kSplitO) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) c[e] += KA[I * 1024 + e * 64 + lane];
+            }
+            return c;
+        };
+        // S <- S diag(gamma_C) + U^T (K e^{g_C - g}) as 2 NJ tiles of 32 x 32; a
+        // factored chunk forms (S e^{g_m} + U^T (K e^{g_m - g})) e^{g_C - g_m}
+        // column by column
+        const float* KS = wide ? Kt : KB;
+        auto s_init = [&](int tl) {
+            const int I = tl / NJ, J = tl - I * NJ;
+            const float f = sIn[32 * J + l32];
+            f32x16 c;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L1 + 32 * J + l32] * f;
+            return c;
+        };
+        auto s_done = [&](int tl, f32x16 c) {
+            const int I = tl / NJ, J = tl - I * NJ;
+            c = chain<kC / 2>([&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; },
+                              [&](int s) { return KS[(2 * s + kg) * L1 + 32 * J + l32]; }, c);
+            const float f = sOut[32 * J + l32];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * J + l32] = c[e] * f;
+        };
+        f32x16 oacc = {};
         if constexpr (GDN) {
-            // U = T (R_v - R_w S^T) = T X.  Phase A: wave 0 inverts I + A while
-            // waves 1 and 2 form X in place of R_v (value columns 32 (w - 1) ..)
-            // and wave 3 starts O = (Q gamma) S^T on value columns 0 .. 31.
-            f32x16 oacc = {};
+            // 3. A (wave 0) and P (wave 1) beside X = V - (K gamma) S^T in place
+            // of V on value columns 32 (w - 2) .. (waves 2, 3); with the
+            // strengths in the columns of T, T diag(beta) X is U = T (R_v - R_w S^T)
+            if (w == 0) {
+                if (!wide) {
+                    const f32x16 c = gram(KA);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = row(e);
+                        Am[t * kC + l32] = l32 < t ? c[e] : 0.f;
+                    }
+                }
+            } else if (w == 1) {
+                if (!wide) {
+                    const f32x16 c = gram(QA);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = row(e);
+                        Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
+                    }
+                }
+            } else {
+                const int I = w - 2;
+                f32x16 c;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * kSL + 32 * I + l32];
+                c = rows_dot(Rw, Ss + 32 * I * L1, Full{}, 0, c);  // Rw holds -k gamma
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
+            }
+            __syncthreads();
+            // 4. the inverse (wave 0) beside O = (Q gamma) S^T on value columns
+            // 32 (w - 1) .. (waves 1, 2)
             if (w == 0) {
                 const float4* A4 = reinterpret_cast<const float4*>(Am);
+                float4 b4[kC / 4];  // the strengths, applied to the rows of A
+#pragma unroll
+                for (int m = 0; m < kC / 4; ++m) b4[m] = reinterpret_cast<const float4*>(bet)[m];
                 float xcol[kC];
                 // row r + 1 of A is in flight while row r is reduced
                 float4 cur[kC / 4], nxt[kC / 4];
@@ -402,83 +535,82 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     if (r + 1 < kC) {
                         // the offset is tied to the previous row's result, so
                         // these loads issue after it and one row ahead of use
-                        int off = (r + 1) * (kC / 4);
-                        asm volatile("" : "+v"(off) : "v"(xcol[r - 1]));
+                        int off4 = (r + 1) * (kC / 4);
+                        asm volatile("" : "+v"(off4) : "v"(xcol[r - 1]));
 #pragma unroll
-                        for (int m = 0; m < (r + 4) / 4; ++m) nxt[m] = A4[off + m];
+                        for (int m = 0; m < (r + 4) / 4; ++m) nxt[m] = A4[off4 + m];
                     }
-                    float acc = r == l32 ? 1.f : 0.f;
+                    float a = 0.f;
 #pragma unroll
                     for (int j = 0; j < r; ++j) {
                         const float4 aj = cur[j / 4];
                         const float av = (j & 3) == 0 ? aj.x : (j & 3) == 1 ? aj.y : (j & 3) == 2 ? aj.z : aj.w;
-                        acc -= av * xcol[j];
+                        a += av * xcol[j];
                     }
-                    xcol[r] = acc;
+                    const float4 bq = b4[r / 4];
+                    const float br = (r & 3) == 0 ? bq.x : (r & 3) == 1 ? bq.y : (r & 3) == 2 ? bq.z : bq.w;
+                    xcol[r] = (r == l32 ? 1.f : 0.f) - br * a;
                     if (r + 1 < kC) {
 #pragma unroll
                         for (int m = 0; m < (r + 4) / 4; ++m) cur[m] = nxt[m];
                     }
                 }
                 if (kg == 0) {
+                    const float bl = bet[l32];
 #pragma unroll
-                    for (int r = 0; r < kC; ++r) Tm[r * kLT + l32] = xcol[r];
+                    for (int r = 0; r < kC; ++r) Tm[r * kLT + l32] = xcol[r] * bl;
                 }
             } else if (w < 3) {
-                const int I = w - 1;
-                f32x16 c;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * kSL + 32 * I + l32];
-                c = rows_dot(Rw, Ss + 32 * I * L1, Full{}, 0, c);  // Rw holds -beta k gamma
-#pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
-            } else {
-                oacc = rows_dot(Qg, Ss, Full{}, 0, oacc);
+                oacc = rows_dot(Qg, Ss + 32 * (w - 1) * L1, OHead{}, 0, oacc);
+            } else if (kSplitO) {
+                o_tail(0);
+                o_tail(1);
             }
             __syncthreads();
-            // Phase B: U = T X (waves 1, 2); waves 0 and 3 share (Q gamma) S^T on
-            // value columns 32 .. 63, one half of the keys each.
+            // 5. U = T diag(beta) X (waves 1, 2) while waves 0 and 3 read their state
+            // tiles; then O += P U on the same value columns beside the state update.
+            // State tiles 0, 1, .. go to waves 0, 3, 1, 2, 0, 3, 0, 3.
+            auto tile_of = [&](int i) { return (w == 3 ? 1 : 0) + (i ? 2 * i + 2 : 0); };
+            f32x16 sreg[3];
             if (w == 1 || w == 2) {
                 const int I = w - 1;
                 const f32x16 c = tok_dot(Tm, I, f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
-            } else if (w == 0) {
-                oacc = rows_dot(Qg, Ss + 32 * L1, Half{}, 0, oacc);
             } else {
-                const f32x16 part = rows_dot(Qg, Ss + 32 * L1, Half{}, DK / 4, f32x16{});
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Ob[e * 64 + lane] = part[e];
+                for (int i = 0; i < 3; ++i)
+                    if (tile_of(i) < 2 * NJ) sreg[i] = s_init(tile_of(i));
             }
             __syncthreads();
-            // Phase C: O += P U (wave 3: columns 0 .. 31, wave 0: 32 .. 63) beside
-            // the state update (no wave reads the old state any more).
-            if (w == 3) {
-                store_o(0, tok_dot(Pm, 0, oacc));
-            } else if (w == 0) {
+            if (w == 1 || w == 2) {
+                store_o(w - 1, tok_dot(Pm, w - 1, o_add_tail(w - 1, oacc)));
+                if (w + 1 < 2 * NJ) s_done(w + 1, s_init(w + 1));
+            } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[e] += Ob[e * 64 + lane];
-                store_o(1, tok_dot(Pm, 1, oacc));
+                for (int i = 0; i < 3; ++i)
+                    if (tile_of(i) < 2 * NJ) s_done(tile_of(i), sreg[i]);
             }
         } else {
-            // O = (Q gamma) S^T + P V: waves 2, 3 (value columns 32 (w - 2) ..)
-            if (w >= 2) store_o(w - 2, tok_dot(Pm, w - 2, rows_dot(Qg, Ss + 32 * (w - 2) * L1, Full{}, 0, f32x16{})));
-            __syncthreads();  // every read of the old state done
-        }
-        // S <- S diag(gamma_C) + U^T K~: 2 x NJ tiles; with the delta rule waves
-        // 1 and 2 take most of them (0 and 3 are busy with O)
-        for (int tl = 0; tl < 2 * NJ; ++tl) {
-            const int owner = GDN ? (tl < 2 * NJ - 2 ? 1 + (tl & 1) : (tl == 2 * NJ - 2 ? 0 : 3)) : (tl & 3);
-            if (owner != w) continue;
-            const int I = tl / NJ, J = tl - I * NJ;
-            const float gC = __builtin_amdgcn_exp2f(Gs[(kC - 1) * L4 + 32 * J + l32]);
-            f32x16 c;
+            // P (wave 0) beside O = (Q gamma) S^T on value columns 32 (w - 2) .. (waves 2, 3)
+            if (w == 0) {
+                if (!wide) {
+                    const f32x16 c = gram(QA);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L1 + 32 * J + l32] * gC;
-            c = chain<kC / 2>([&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; },
-                              [&](int s) { return Kt[(2 * s + kg) * L1 + 32 * J + l32]; }, c);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * J + l32] = c[e];
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = row(e);
+                        Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
+                    }
+                }
+            } else if (w >= 2) {
+                oacc = rows_dot(Qg, Ss + 32 * (w - 2) * L1, OHead{}, 0, oacc);
+            } else if (kSplitO) {
+                o_tail(0);
+                o_tail(1);
+            }
+            __syncthreads();  // P done, every read of the old state done
+            if (w >= 2) store_o(w - 2, tok_dot(Pm, w - 2, o_add_tail(w - 2, oacc)));
+            for (int tl = w; tl < 2 * NJ; tl += 4) s_done(tl, s_init(tl));
         }
     }
     __syncthreads();

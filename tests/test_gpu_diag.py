@@ -108,3 +108,37 @@ def test_diag_full_workload_sampled_heads():
         es = max_err(ST[bb, hh][None], S_ref[None], 1)
         say(f"  head ({bb},{hh}): o {eo:.3e}  S_T {es:.3e}  (gate {TOL['bf16']:.0e})")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def _wide_chunks(a, chunk, limit=64.0):
+    """Fraction of (head, chunk) pairs in which some key channel's cumulative
+    log2 decay spans more than `limit` (the range over which the kernel forms
+    the decayed Gram as two scaled products; wider chunks take a pairwise form)."""
+    T = a.shape[-2]
+    lg = np.log2(a.astype(np.float64))
+    wide = []
+    for c0 in range(0, T, chunk):
+        g = np.cumsum(lg[..., c0:c0 + chunk, :], axis=-2)
+        wide.append((g.max(axis=-2) - g.min(axis=-2)).max(axis=-1) > limit)
+    return float(np.mean(wide))
+
+
+@pytest.mark.parametrize("gate,regime", [(("uniform", 0.02, 0.3), "wide"),
+                                         (("exp_uniform", -2.25, 0.0), "mixed")])
+@pytest.mark.parametrize("mode,dk", [("gdn", 128), ("gla", 64)])
+def test_diag_scan_decay_regimes(gate, regime, mode, dk):
+    """Strong per-channel decays: every chunk (wide) or some chunks (mixed)
+    exceed the span of the factored Gram, so both of the kernel's forms run,
+    in one launch for the mixed case."""
+    w = I.WORKLOADS["tiny-gla-diag"].replace(mode=mode, dk=dk, dv=64, alpha=gate,
+                                             beta=("uniform", 0.0, 1.0) if mode == "gdn" else None)
+    T = 260
+    say(f"diagonal-gate scan, {regime} decays {gate} {mode} dk{dk} T{T}")
+    q, k, v, a, beta, S0 = _batch(w, T, 1, 2)
+    frac = _wide_chunks(a, 32)
+    assert (frac > 0.85) if regime == "wide" else (0.2 < frac < 0.8), frac  # wide: all but the tail
+    o, ST = gds.scan_fwd(dev(q), dev(k), dev(v), dev(a), None if beta is None else dev(beta),
+                         dev(S0), chunk=32)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.scan(mode + "_diag", q, k, v, a, beta, S0.astype(np.float64))
+    assert_parity(host(o), host(ST), o_ref, S_ref, "f32", what=f"{regime} {mode}_diag")
