@@ -55,8 +55,9 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
     __shared__ float bet[kC];
 
     const int slices = dv / SL;
-    const int bh = blockIdx.x / slices;
-    const int r0 = (blockIdx.x - bh * slices) * SL;
+    int bh, sl;
+    unit_part(blockIdx.x, gridDim.x / slices, slices, bh, sl);  // a head's slices share its q, k reads in L2
+    const int r0 = sl * SL;
     const int tid = threadIdx.x;
     const size_t qk_base = (size_t)bh * T * DK;
     const size_t v_base = (size_t)bh * T * dv;
@@ -243,8 +244,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ __align__(16) float bet[kC];
 
     const int slices = dv / kSL;
-    const int bh = blockIdx.x / slices;
-    const int r0 = (blockIdx.x - bh * slices) * kSL;
+    int bh, sl;
+    unit_part(blockIdx.x, gridDim.x / slices, slices, bh, sl);  // a head's slices share its q, k reads in L2
+    const int r0 = sl * kSL;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, kg = lane >> 5;

@@ -34,20 +34,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-// (unit, part) of block x when each unit is split into `parts` blocks: blocks
-// are dealt round-robin over the 8 XCDs, so when the unit count is a multiple
-// of 8 the parts of a unit are placed on one XCD and share its L2.
-__device__ __forceinline__ void unit_part(int x, int units, int parts, int& unit, int& part) {
-    if ((units & 7) == 0) {
-        const int xcd = x & 7, j = x >> 3;
-        unit = (j / parts) * 8 + xcd;
-        part = j % parts;
-    } else {
-        unit = x / parts;
-        part = x % parts;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // plain kernel: one workgroup per head, everything in LDS (d <= 64)
 // ---------------------------------------------------------------------------

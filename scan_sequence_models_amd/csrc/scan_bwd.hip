@@ -171,8 +171,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
 
     const int slices = J.dv / kSL;
-    const int bh = blockIdx.x / slices;
-    const int r0 = (blockIdx.x - bh * slices) * kSL;
+    int bh, sl;
+    unit_part(blockIdx.x, J.BH, slices, bh, sl);  // a head's slices share its input reads in L2
+    const int r0 = sl * kSL;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, kg = lane >> 5;
@@ -311,8 +312,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ float dgc[16];        // ... to dg_C
 
     const int slices = J.dv / kSL;
-    const int slice = blockIdx.x % slices;
-    const int bh = blockIdx.x / slices;
+    int bh, slice;
+    unit_part(blockIdx.x, J.BH, slices, bh, slice);  // a head's slices share its input reads in L2
     const int r0 = slice * kSL;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
