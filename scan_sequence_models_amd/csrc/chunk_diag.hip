@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ float sIn[DK];                    // per-channel factors of the state update:
     __shared__ float sOut[DK];                   // e^{g_m}, e^{g_C - g_m} (wide: gamma_C, 1)
     __shared__ __align__(16) float bet[kC];
+    __shared__ int wflag[kThreads / 64];         // a wave holds a chunk too wide to factor
 
     const int slices = dv / kSL;
     int bh, sl;
@@ -333,7 +334,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int x = tid + m * kThreads;
             Us[x] = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
         }
-        const bool wide = __syncthreads_or(!narrow);
+        // one flag per wave, one barrier (the flags are next written after the
+        // following chunk's first barrier)
+        const bool wave_wide = __builtin_amdgcn_ballot_w64(!narrow) != 0;  // all lanes vote
+        if (lane == 0) wflag[w] = wave_wide;
+        __syncthreads();
+        const bool wide = wflag[0] | wflag[1] | wflag[2] | wflag[3];
         // 2. scaled copies and Gram operands.  The bases are opaque to the
         // compiler, so each store below is one base register plus an immediate
         // offset instead of an address hoisted out of the chunk loop.
