@@ -180,8 +180,9 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 //      consecutive tokens per thread; log2 a is summed along the chunk there,
 //      the runs exchanging their totals through LDS.  The value slice goes to
 //      LDS;
-//   2. the scaled copies q gamma, -k gamma and k e^{g_C - g} are written
-//      from the registers, and so are the operands of the decayed Gram:
+//   2. the scaled copies q gamma and -k gamma (and, in a wide chunk,
+//      k e^{g_C - g}) are written from the registers, and so are the operands
+//      of the decayed Gram:
 //      splitting each pair's factor through the middle token m,
 //      e^{g_t - g_s} = e^{g_t - g_m} e^{g_m - g_s}, turns A and P into two
 //      plain 32x32 products of rows scaled by e^{+-(g - g_m)}.  In float32 that
@@ -189,10 +190,13 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 //      chunk with a wider span stores q, k and g instead and takes the
 //      pairwise form (one exp2 per token pair and channel);
 //   3. A and P on two waves beside X = V - (K gamma) S^T on the other two;
-//   4. T = (I + A)^-1 by one wave (a lane per column, forward substitution
-//      with the rows of A read as float4) beside O = (Q gamma) S^T on two more;
+//   4. T = (I + diag(beta) A)^-1 by one wave (a lane per column, forward
+//      substitution with the rows of A read as float4) beside
+//      O = (Q gamma) S^T on the other three;
 //   5. U = T diag(beta) X; then O += P U beside the state update
-//      S <- S diag(gamma_C) + U^T (K e^{g_C - g}), all as 32x32 tiles.
+//      S <- S diag(gamma_C) + U^T (K e^{g_C - g}), all as 32x32 tiles (a
+//      factored chunk scales by e^{g_C - g_m} per column instead of forming
+//      K e^{g_C - g}).
 // U = T (R_v - R_w S^T) = T diag(beta) (V - (K gamma) S^T) is the product
 // T R_v - (T R_w) S^T grouped so that the key-long part does not wait for the
 // inverse, with the strengths applied to the columns of T.
