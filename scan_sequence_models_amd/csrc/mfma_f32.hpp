@@ -6,6 +6,14 @@ namespace gds {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16x16x4 step: lane (16 g + n16) gives A[n16][g] and B[g][n16]; the result
+// holds rows 4 g .. 4 g + 3 of column n16.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // One 32x32x2 step: lane (32 kg + l32) gives A[l32][kg] and B[kg][l32].
 __device__ __forceinline__ f32x16 mfma2(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);

@@ -118,42 +118,60 @@ __device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, float w_ra
     }
 }
 
-// T = (I + diag(beta) B)^-1 for strictly lower B (row stride LB), by one wave:
-// lane l32 solves for column l32 by forward substitution; each row of B is read
-// as float4 one row ahead of its use (the offset is tied to the previous row's
-// result so the compiler keeps the loads there).  Lanes 32..63 repeat 0..31.
-__device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* bet, float* Tm, int l32, int kg) {
-    const float4* B4 = reinterpret_cast<const float4*>(Bm);
-    constexpr int R4 = LB / 4;
-    float xcol[kC];
-    float4 cur[kC / 4], nxt[kC / 4];
-    cur[0] = B4[R4];
-    xcol[0] = l32 == 0 ? 1.f : 0.f;
+// T = (I + diag(bet) B)^-1 for the strictly lower part of B (row stride LB, as
+// float4 rows) into Tm (row stride LM), from its 16x16 blocks: the two diagonal
+// blocks D0, D1 by forward substitution side by side (lane (b, c) of each
+// half-wave owns column c of block b, x_r = [r == c] - bet_r sum_{j<r} B_rj x_j,
+// rows read as float4 two rows ahead), then T10 = -D1 diag(bet) B10 D0 on the
+// fp32 MFMA (16x16x4).  The upper right block of Tm stays zero from the start.
+// All 64 lanes of the wave take part.
+__device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* bet, float* Tm, int lane) {
+    const int b = (lane >> 4) & 1, c = lane & 15, kg = lane >> 5;
+    const float* Bb = Bm + 16 * b * LB + 16 * b;
+    float br[16];
 #pragma unroll
-    for (int r = 1; r < kC; ++r) {
-        if (r + 1 < kC) {
-            int off = (r + 1) * R4;
-            asm volatile("" : "+v"(off) : "v"(xcol[r - 1]));
+    for (int r = 0; r < 16; ++r) br[r] = bet[16 * b + r];
+    f32x4 rw[3][4];  // rows r, r + 1, r + 2 in flight
+    auto load_row = [&](int r, f32x4 (&dst)[4]) {
 #pragma unroll
-            for (int m = 0; m < (r + 4) / 4; ++m) nxt[m] = B4[off + m];
-        }
-        float acc = 0.f;
+        for (int q = 0; q < (r + 3) / 4; ++q) dst[q] = *reinterpret_cast<const f32x4*>(&Bb[r * LB + 4 * q]);
+    };
+    load_row(1, rw[1]);
+    load_row(2, rw[2]);
+    float x[16];
 #pragma unroll
-        for (int j = 0; j < r; ++j) {
-            const float4 bj = cur[j / 4];
-            const float bv = (j & 3) == 0 ? bj.x : (j & 3) == 1 ? bj.y : (j & 3) == 2 ? bj.z : bj.w;
-            acc += bv * xcol[j];
-        }
-        xcol[r] = (r == l32 ? 1.f : 0.f) - bet[r] * acc;
-        if (r + 1 < kC) {
+    for (int r = 0; r < 16; ++r) {
+        if (r + 2 < 16) load_row(r + 2, rw[(r + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int m = 0; m < (r + 4) / 4; ++m) cur[m] = nxt[m];
-        }
+        for (int q = 0; q < (r + 3) / 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * q + i;
+                if (j < r) {
+                    if (i & 1) s1 += rw[r % 3][q][i] * x[j];
+                    else s0 += rw[r % 3][q][i] * x[j];
+                }
+            }
+        x[r] = (r == c ? 1.f : 0.f) - br[r] * (s0 + s1);
     }
     if (kg == 0) {
 #pragma unroll
-        for (int r = 0; r < kC; ++r) Tm[r * LM + l32] = xcol[r];
+        for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LM + 16 * b + c] = x[r];
     }
+    // T10 = -D1 (diag(bet) B10) D0: lane (n16, g4) supplies contraction indices
+    // 4 g4 .. 4 g4 + 3 and holds rows 4 g4 .. 4 g4 + 3 of column n16
+    const int n16 = lane & 15, g4 = lane >> 4;
+    f32x4 y = {}, t10 = {};
+    const f32x4 br10 = *reinterpret_cast<const f32x4*>(&Bm[(16 + n16) * LB + 4 * g4]);
+    const float bs = bet[16 + n16];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) y = mfma4(br10[kk] * bs, Tm[(4 * g4 + kk) * LM + n16], y);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t10 = mfma4(Tm[(16 + n16) * LM + 16 + 4 * g4 + kk], y[kk], t10);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Tm[(16 + 4 * g4 + r) * LM + n16] = -t10[r];
 }
 
 // ---------------------------------------------------------------------------
@@ -185,6 +203,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     auto row = [&](int e) { return acc_row(e, kg); };
 
     for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
+    if constexpr (GDN)
+        for (int x = tid; x < kC * LM; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
 
     // The next chunk's k, v and gates are fetched into registers while this
     // chunk computes (unconditional loads from a clamped token index; masking
@@ -259,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
             }
             __syncthreads();
             if (w == 0) {  // T, then U = T X in place
-                solve_unit_lower(Bm, bet, Tm, l32, kg);
+                solve_unit_lower(Bm, bet, Tm, lane);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
                     const f32x16 c = chain<kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
@@ -334,6 +354,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto row = [&](int e) { return acc_row(e, kg); };
 
     for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
+    if constexpr (GDN)
+        for (int x = tid; x < kC * LM; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
 
     // The next chunk's (in reverse order) q, k, v, dO and gates are fetched
     // into registers during this one's last two phases (unconditional loads
@@ -466,7 +488,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 2 (delta rule): T and U = T X; dU = Kd dS'^T
         if constexpr (GDN) {
             if (w == 0) {
-                solve_unit_lower(Bm, bet, Tm, l32, kg);
+                solve_unit_lower(Bm, bet, Tm, lane);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
                     const f32x16 c = chain<kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
