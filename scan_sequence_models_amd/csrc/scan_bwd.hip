@@ -508,21 +508,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
             __syncthreads();
         }
-        // Phase 3: dP (wave 0), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
-        if (w == 0) {
+        // Phase 3: dP (waves 0 and 3 both form it: wave 0 writes dP * Gamma, wave 3 the
+        // row and column sums of dP * P), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
+        if (w == 0 || w == 3) {
             const f32x16 c = chain<kSL / 2>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
                                             [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
-            f32x16 L;
+            if (w == 0) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int t = row(e);
-                const bool m = l32 <= t;
-                const float dp = m ? c[e] : 0.f;
-                dQKm[t * LM + l32] = m ? dp * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
-                L[e] = dp * Pm[t * LM + l32];
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e);
+                    dQKm[t * LM + l32] = l32 <= t ? c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                }
+            } else {
+                f32x16 L;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e);
+                    L[e] = l32 <= t ? c[e] * Pm[t * LM + l32] : 0.f;
+                }
+                store_row_sums(L, dgp + 8 * kC, l32, kg, 1.f);   // dg slot 8
+                store_col_sums(L, dgp + 9 * kC, l32, kg, -1.f);  // dg slot 9
             }
-            store_row_sums(L, dgp + 8 * kC, l32, kg, 1.f);   // dg slot 8
-            store_col_sums(L, dgp + 9 * kC, l32, kg, -1.f);  // dg slot 9
         } else if (w < 3) {
             const int I = w - 1;
             {  // e^{g_C - g_t} <(U dS')_t, K_t> = <U_t, dU_t> while dU holds Kd dS'^T: lane l32 takes
@@ -576,24 +582,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         __syncthreads();
         // the next chunk's inputs are in flight through phases 5 and 6
         if (n > 0) fetch(n - 1);
-        // Phase 5: dA (wave 0), dRw (owners), dS
+        // Phase 5: dA (waves 0 and 1 both form it: wave 0 writes dKK, wave 1 the sums),
+        // dRw (owners), dS
         if constexpr (GDN) {
-            if (w == 0) {
+            if (w < 2) {
                 const f32x16 c = chain<kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
                                                 [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
-                f32x16 xb, xa;
+                if (w == 0) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = row(e);
-                    const bool m = l32 < t;
-                    const float da = m ? c[e] : 0.f;
-                    const float b = Bm[t * LB + l32];
-                    xb[e] = da * b;
-                    xa[e] = da * bet[t] * b;
-                    dKKm[t * LM + l32] = m ? bet[t] * da * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = row(e);
+                        dKKm[t * LM + l32] = l32 < t ? bet[t] * c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                    }
+                } else {
+                    f32x16 xb, xa;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = row(e);
+                        const float da = l32 < t ? c[e] : 0.f;
+                        const float b = Bm[t * LB + l32];
+                        xb[e] = da * b;
+                        xa[e] = da * bet[t] * b;
+                    }
+                    store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6 (dg: beta_t times it)
+                    store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
                 }
-                store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6 (dg: beta_t times it)
-                store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
             }
             if (w >= 2) {  // <dRw_t, K_t> = -<dX_t, (K S^T)_t> over this wave's value columns
                 const int I = w - 2;
