@@ -35,6 +35,8 @@ CASES = [
     ("tiny-gla-diag", "gdn", 1, 2, 130, 32, 192),
     ("tiny-gla-diag", "gla", 1, 1, 45, 128, 64),
     ("tiny-gla-diag", "gdn", 1, 1, 33, 64, 48),
+    ("tiny-gla-diag", "gdn", 1, 1, 1, 128, 64),     # one token: a single ragged chunk
+    ("tiny-gla-diag", "gla", 2, 1, 31, 64, 128),    # one chunk short of its end
     ("gdn-diag-b8h16t8192", "gdn", 1, 2, 200, 128, 128),
     ("gdn-diag-b8h16t8192", "gla", 1, 2, 97, 128, 128),
 ]
