@@ -22,7 +22,8 @@
 //     right child (a 128x128x128 fp32 product); the top state is S0;
 //  4. output pass (chunk kernel, kLeafOutput): every leaf from its prefix
 //     state, writing o; the last real leaf writes S_T.
-// Products of steps 2-3 run on the fp32 MFMA (v_mfma_f32_16x16x4_f32).
+// Products of steps 2-3 run on the fp32 MFMA (v_mfma_f32_16x16x4_f32); with
+// gated linear attention every E is gamma I and they are scalings.
 #include "blelloch.hpp"
 
 #include "common.hpp"
@@ -123,9 +124,43 @@ __global__ __launch_bounds__(256) void affine_kernel(const Affine p) {
     }
 }
 
-hipError_t launch_affine(const Affine& p, int heads, hipStream_t s) {
-    const unsigned blocks = (unsigned)(heads * p.items * (p.rows / 64) * 2);
-    hipLaunchKernelGGL(affine_kernel, dim3(blocks), dim3(256), 0, s, p);
+// The same C = A B + F when B is gamma I (gated linear attention: every E is a
+// multiple of the identity), so the product is a scaling by B's first entry.
+// One workgroup: 64 rows of C.
+__global__ __launch_bounds__(256) void affine_scaled_kernel(const Affine p) {
+    const int nrb = p.rows / 64;
+    int x = blockIdx.x;
+    const int rb = x % nrb;
+    x /= nrb;
+    const int item = x % p.items;
+    const int head = x / p.items;
+    const float* A = p.A ? p.A + head * p.a_head + item * p.a_item + (size_t)rb * 64 * D : nullptr;
+    const float gam = p.B[head * p.b_head + item * p.b_item];
+    const float* F = p.F ? p.F + head * p.f_head + item * p.f_item : nullptr;
+    float* C = p.C + head * p.c_head + item * p.c_item + (size_t)rb * 64 * D;
+    float* Dst = p.Dst ? p.Dst + head * p.d_head + item * p.d_item + (size_t)rb * 64 * D : nullptr;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int e = threadIdx.x + 256 * m;  // 2048 float4 of the 64 x 128 block
+        const int r = e >> 5, c4 = (e & 31) * 4, row = rb * 64 + r;
+        const float4 a = A ? *reinterpret_cast<const float4*>(A + (size_t)r * D + c4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (Dst) *reinterpret_cast<float4*>(Dst + (size_t)r * D + c4) = a;
+        float4 c = make_float4(gam * a.x, gam * a.y, gam * a.z, gam * a.w);
+        if (F && row < p.f_rows) {
+            const float4 f = *reinterpret_cast<const float4*>(F + (size_t)row * D + c4);
+            c.x += f.x; c.y += f.y; c.z += f.z; c.w += f.w;
+        }
+        *reinterpret_cast<float4*>(C + (size_t)r * D + c4) = c;
+    }
+}
+
+hipError_t launch_affine(const Affine& p, int heads, bool scaled, hipStream_t s) {
+    const unsigned rblocks = (unsigned)(heads * p.items * (p.rows / 64));
+    if (scaled)
+        hipLaunchKernelGGL(affine_scaled_kernel, dim3(rblocks), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(affine_kernel, dim3(rblocks * 2), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -234,7 +269,7 @@ hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, i
         p.c_head = nl * kAgg; p.c_item = kAgg;
         p.rows = 2 * D;
         p.items = (int)nl;
-        if ((e = launch_affine(p, BH, stream)) != hipSuccess) return e;
+        if ((e = launch_affine(p, BH, mode == 1, stream)) != hipSuccess) return e;
     }
 
     // 3. down-sweep on states
@@ -258,7 +293,7 @@ hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, i
         p.d_head = nc * kSt; p.d_item = 2 * kSt;
         p.rows = D;
         p.items = (int)nl;
-        if ((e = launch_affine(p, BH, stream)) != hipSuccess) return e;
+        if ((e = launch_affine(p, BH, mode == 1, stream)) != hipSuccess) return e;
     }
 
     // 4. output pass from every leaf's prefix state
