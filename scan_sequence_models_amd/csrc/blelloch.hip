@@ -155,6 +155,78 @@ __global__ __launch_bounds__(256) void affine_scaled_kernel(const Affine p) {
     }
 }
 
+// Gated linear attention (every E is gamma I).  Sum of ln alpha over leaf i
+// of head `head` (tokens [i G C, (i+1) G C) within T), by the threads of one
+// workgroup; groups of 256/m lanes per leaf when m <= 64.
+__device__ __forceinline__ void leaf_log_decays(const float* alpha, int head, int T, int leaf_tokens, int m,
+                                                float* out) {
+    __shared__ float part[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (m <= 4) {  // whole waves per leaf
+        const int per = 4 / m, li = w / per, sub = w % per;
+        const int t0 = li * leaf_tokens, t1 = min(t0 + leaf_tokens, T);
+        float s = 0.f;
+        for (int t = t0 + sub * 64 + lane; t < t1; t += per * 64) s += __logf(alpha[(size_t)head * T + t]);
+        s = group_sum<64>(s);
+        if (lane == 0) part[w] = s;
+        __syncthreads();
+        if (tid < m) {
+            float g = 0.f;
+            for (int j = 0; j < per; ++j) g += part[tid * per + j];
+            out[tid] = g;
+        }
+    } else {  // m in 8 .. 64: a lane group of G = 256 / m per leaf
+        const int G = 256 / m, li = tid / G, sub = tid % G;
+        const int t0 = li * leaf_tokens, t1 = min(t0 + leaf_tokens, T);
+        float s = 0.f;
+        for (int t = t0 + sub; t < t1; t += G) s += __logf(alpha[(size_t)head * T + t]);
+        s = G == 32 ? group_sum<32>(s) : G == 16 ? group_sum<16>(s) : G == 8 ? group_sum<8>(s) : group_sum<4>(s);
+        if (sub == 0) out[li] = s;
+    }
+    __syncthreads();
+}
+
+// With at most 64 leaves: the state entering each leaf as a left fold over the
+// leaves before it, element by element (S_0 = S0, S_{i+1} = gamma_i S_i + f_i);
+// the bracketing only changes rounding.  Workgroup (head, block of 1024 state
+// elements); the leaves' E rows are not needed.
+__global__ __launch_bounds__(256) void gla_prefix_kernel(const float* S0, const float* alpha, const float* agg,
+                                                         float* st, int T, int m, int leaf_tokens) {
+    __shared__ float lg[64];
+    const int head = blockIdx.x / 16, e4 = (blockIdx.x % 16) * 1024 + 4 * threadIdx.x;
+    leaf_log_decays(alpha, head, T, leaf_tokens, m, lg);
+    float4 cur = S0 ? *reinterpret_cast<const float4*>(S0 + (size_t)head * kSt + e4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < m; ++i) {
+        const size_t leaf = (size_t)head * m + i;
+        *reinterpret_cast<float4*>(st + leaf * kSt + e4) = cur;
+        const float g = __expf(lg[i]);
+        const float4 f = *reinterpret_cast<const float4*>(agg + leaf * kAgg + e4);
+        cur = make_float4(g * cur.x + f.x, g * cur.y + f.y, g * cur.z + f.z, g * cur.w + f.w);
+    }
+}
+
+// With more leaves: E = gamma I written into every leaf aggregate for the
+// (scaled) sweeps.  One workgroup per (head, leaf).
+__global__ __launch_bounds__(256) void gla_leaf_decay_kernel(const float* alpha, float* agg, int T, int m,
+                                                             int leaf_tokens) {
+    __shared__ float part[4];
+    const int u = blockIdx.x, tid = threadIdx.x;
+    const int head = u / m, leaf = u - head * m;
+    const int t0 = leaf * leaf_tokens, t1 = min(t0 + leaf_tokens, T);
+    float s = 0.f;
+    for (int t = t0 + tid; t < t1; t += 256) s += __logf(alpha[(size_t)head * T + t]);
+    s = group_sum<64>(s);
+    if ((tid & 63) == 0) part[tid >> 6] = s;
+    __syncthreads();
+    const float gam = __expf(part[0] + part[1] + part[2] + part[3]);
+    float* E = agg + (size_t)u * kAgg + kSt;
+    for (int x = 4 * tid; x < D * D; x += 4 * 256) {
+        const int r = x / D, c = x - r * D;
+        *reinterpret_cast<float4*>(E + x) =
+            make_float4(c == r ? gam : 0.f, c + 1 == r ? gam : 0.f, c + 2 == r ? gam : 0.f, c + 3 == r ? gam : 0.f);
+    }
+}
+
 hipError_t launch_affine(const Affine& p, int heads, bool scaled, hipStream_t s) {
     const unsigned rblocks = (unsigned)(heads * p.items * (p.rows / 64));
     if (scaled)
@@ -254,6 +326,18 @@ hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, i
     job.S_out = ws + L.agg_off[0];
     hipError_t e = launch_chunk_job(mode, kLeafAggregate, job, stream);
     if (e != hipSuccess) return e;
+    const int leaf_tokens = leaf_chunks * kChunk;
+    if (mode == 1 && L.m <= 64) {
+        // gated linear attention: a left fold per state element replaces the sweeps
+        hipLaunchKernelGGL(gla_prefix_kernel, dim3((unsigned)(BH * 16)), dim3(256), 0, stream, S0, alpha,
+                           ws + L.agg_off[0], ws + L.st_off[0], T, (int)L.m, leaf_tokens);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        if (mode == 1) {
+            hipLaunchKernelGGL(gla_leaf_decay_kernel, dim3((unsigned)(BH * L.m)), dim3(256), 0, stream, alpha,
+                               ws + L.agg_off[0], T, (int)L.m, leaf_tokens);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
 
     // 2. up-sweep
     for (int l = 1; l < L.levels; ++l) {
@@ -295,6 +379,8 @@ hipError_t launch_blelloch(int mode, int BH, int T, int dk, int dv, int chunk, i
         p.items = (int)nl;
         if ((e = launch_affine(p, BH, mode == 1, stream)) != hipSuccess) return e;
     }
+
+    }  // sweeps
 
     // 4. output pass from every leaf's prefix state
     job.o = static_cast<uint16_t*>(o);

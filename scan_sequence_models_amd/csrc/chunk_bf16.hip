@@ -390,7 +390,8 @@ struct Unit {
 
 // Slices per unit: two of value rows, plus (delta rule, leaf aggregates) two of
 // E's rows carried from the identity.  With gated linear attention E is
-// gamma I, written by gla_leaf_decay_kernel instead.
+// gamma I and the tree path forms it from the gates (the E rows of a leaf
+// aggregate are not written here).
 template <int MODE, int ROLE>
 __device__ __forceinline__ Unit unit_of(const ChunkJob& job) {
     constexpr int NS = ROLE == kLeafAggregate && MODE == 0 ? 4 : 2;
@@ -872,28 +873,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(const ChunkJob job) {
         gram_role<MODE, ROLE>(sm, job, un);
 }
 
-// Gated linear attention: a leaf's E is gamma I with gamma the product of its
-// tokens' alpha (1 for a leaf past the sequence).  One workgroup per (head,
-// leaf) writes the E rows of its [f; E] aggregate.
-__global__ __launch_bounds__(256) void gla_leaf_decay_kernel(const ChunkJob job) {
-    __shared__ float part[4];
-    const int u = blockIdx.x, tid = threadIdx.x;
-    const int head = u / job.leaves, leaf = u - head * job.leaves;
-    const int t0 = leaf * job.leaf_chunks * C, t1 = min(t0 + job.leaf_chunks * C, job.T);
-    float s = 0.f;
-    for (int t = t0 + tid; t < t1; t += 256) s += __logf(job.alpha[(size_t)head * job.T + t]);
-    s = group_sum<64>(s);
-    if ((tid & 63) == 0) part[tid >> 6] = s;
-    __syncthreads();
-    const float gam = __expf(part[0] + part[1] + part[2] + part[3]);
-    float* E = job.S_out + ((size_t)u * (DV + DK) + DV) * DK;
-    for (int x = 4 * tid; x < DK * DK; x += 4 * 256) {
-        const int r = x / DK, c = x - r * DK;
-        *reinterpret_cast<f32x4*>(E + x) =
-            f32x4{c == r ? gam : 0.f, c + 1 == r ? gam : 0.f, c + 2 == r ? gam : 0.f, c + 3 == r ? gam : 0.f};
-    }
-}
-
 }  // namespace
 
 bool chunk_mfma_supported(int mode, int dk, int dv, int chunk) {
@@ -910,7 +889,6 @@ static hipError_t launch_role(int role, const ChunkJob& job, hipStream_t stream)
     else if (role == kLeafAggregate) {
         hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kLeafAggregate>), dim3((MODE == 0 ? 4 : 2) * units), block, 0,
                            stream, job);
-        if (MODE == 1) hipLaunchKernelGGL(gla_leaf_decay_kernel, dim3(units), dim3(256), 0, stream, job);
     }
     else
         hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kLeafOutput>), dim3(2 * units), block, 0, stream, job);

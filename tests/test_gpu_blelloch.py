@@ -21,10 +21,12 @@ def _w(mode, T, B=1, H=3):
 
 @pytest.mark.parametrize("mode", ["gdn", "gla"])
 @pytest.mark.parametrize("T,leaf", [(64 * 37 + 5, 1), (64 * 37 + 5, 4), (64 * 64, 8),
-                                    (64 * 2, 1), (64 * 5, 2), (100, 1)])
+                                    (64 * 2, 1), (64 * 5, 2), (100, 1), (64 * 130, 1)])
 def test_blelloch_matches_oracle(mode, T, leaf):
     """Leaf counts that are and are not powers of two (identity padding), a
-    ragged last chunk, a tree of one level, and a last leaf shorter than G."""
+    ragged last chunk, a tree of one level, and a last leaf shorter than G.
+    With gated linear attention up to 64 leaves take the per-element fold and
+    more (256 here) the scaled sweeps."""
     w = _w(mode, T)
     b = I.batch_inputs(w)
     say(f"blelloch {mode} T={T} leaf_chunks={leaf}")
