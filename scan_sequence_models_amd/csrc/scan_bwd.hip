@@ -573,6 +573,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             db += __shfl_xor(db, 32, 64);
             if (kg == 0) dbp[I * kC + l32] = db;  // dbeta slots 0, 1
         }
+        if (w == 0 || w == 3) {  // dO's last reader is the dS update: scale its rows by gamma in place
+            for (int x = (w == 0 ? 0 : 64) + lane; x < kC * kSL; x += 128) {
+                const int t = x / kSL;
+                dOs[t * LV + x - t * kSL] *= gam[t];
+            }
+        }
         if (w < NJ) {
             accQ = chain<kC / 2>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
                                  [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
@@ -654,7 +660,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 },
                 [&](int s) {
                     const int t = 2 * (s % H2) + kg;
-                    return s < H2 ? gam[t] * Qs[t * L1 + 32 * Jt + l32] : bg[t] * Ks[t * L1 + 32 * Jt + l32];
+                    return s < H2 ? Qs[t * L1 + 32 * Jt + l32] : bg[t] * Ks[t * L1 + 32 * Jt + l32];
                 },
                 c);
 #pragma unroll
