@@ -112,14 +112,17 @@ int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chun
     } else if (path == SCAN_PATH_AUTO) {
         // The sequential pass runs one workgroup per (head, value slice); when
         // that cannot fill the GPU, split the sequence into leaves and combine
-        // their aggregates with the Blelloch tree.  The tree pass costs about
-        // three times the chunk work, so it pays when the sequential grid
-        // fills at most a quarter of the CUs (at least two leaves of 16
-        // chunks), or half of them on long sequences.
+        // their aggregates with the Blelloch tree.  With the delta rule the tree
+        // costs about three times the chunk work, so it pays when the
+        // sequential grid fills at most a quarter of the CUs (at least two
+        // leaves of 16 chunks), or half of them on long sequences; gated linear
+        // attention (E = gamma I: no E rows, no dense sweeps) costs about twice
+        // the chunk work and pays whenever the grid fills at most half of them.
         const int64_t wgs = heads * gds::sequential_workgroups_per_head(p.mfma, dv);
         const int cus = device_cus();
+        const bool gla = km == 1;
         if (gds::blelloch_supported(km, dtype, dk, dv, chunk) &&
-            ((wgs * 4 <= cus && nchunks >= 32) || (wgs * 2 <= cus && nchunks >= 256)))
+            ((wgs * 4 <= cus && nchunks >= 32) || (wgs * 2 <= cus && (nchunks >= 256 || (gla && nchunks >= 32)))))
             p.path = SCAN_PATH_BLELLOCH;
     }
     if (p.path == SCAN_PATH_BLELLOCH) {
