@@ -31,12 +31,12 @@
 //                  of S^T (128 keys, fp32) in four 32x32 MFMA accumulator tiles
 //                  for the whole sequence and runs chunk n's S-dependent
 //                  products (U, O, the state update);
-//   waves 2,3,6,7  chunk n+1's k-Gram tiles and UT solve: the two diagonal
+//   waves 2,3,6,7  chunk n+1's off-diagonal k-Gram tile and UT solve: the two diagonal
 //                  32x32 blocks of T are inverted inside one wave each (no
 //                  barrier), the off-diagonal block by two waves, then W;
 //   waves 4-5      load chunk n+2 (coalesced 16-byte rows), stage it in LDS
-//                  (q, k row-major; k^T, v^T transposed), build its gates, and
-//                  compute two of chunk n+1's score tiles.
+//                  (q, k row-major; k^T, v^T transposed), compute its two
+//                  diagonal k-Gram tiles and two of chunk n+1's score tiles.
 // Everything meets through LDS and all waves pass the same three barriers per
 // chunk.  Products are v_mfma_f32_32x32x16_bf16 (fp32 accumulation, bf16
 // operands) except the UT solve, which stays in fp32: diagonal 16x16 blocks by
@@ -641,12 +641,13 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
         const int m = it + 1;
         const bool act = m < un.ne;
         const Gates& G = sm.gate[m % 3];
-        // ---- phase A: k-Gram tiles; diagonal 32x32 blocks of T in-wave ----
+        // ---- phase A: off-diagonal k-Gram tile; diagonal 32x32 blocks of T in-wave ----
         if (gi == 0 && m + 1 < un.ne) load_ab(m + 1);
         if (act) {
             if (GDN && gi <= 1) {
                 float* X = sm.Tm[gi];
-                a_tile(sm, G, gi, gi, X, l32, h);
+                // later chunks' diagonal tiles come from the load waves (phase C)
+                if (m == un.nb) a_tile(sm, G, gi, gi, X, l32, h);
                 diag_inverse2(X, lane);
                 // T_10 = -D_1 A_10 D_0 within the 32x32 block
                 const f32x4 mm = sv.mul_lds(X + 16 * LS, X, z);
@@ -724,6 +725,9 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 }
             }
         }
+        // chunk m+1's gates: the load waves mask its k-Gram tiles in phase C
+        if (gi == 0 && m + 1 < un.ne)
+            stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, split ? pw : pb, T, lane);
         lds_barrier();  // B
         // ---- phase C: W = T diag(beta gamma) K (stored -W) for key tile gi; scores ----
         if (act) {
@@ -746,18 +750,23 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
             }
             if (OUT && gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
         }
-        if (gi == 0 && m + 1 < un.ne)
-            stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, split ? pw : pb, T, lane);
         lds_barrier();  // C
     }
 }
 
 // ----------------------------------------------------------------------------
-// load / transpose waves (4, 5): stage chunk n+2; score tiles (0,0), (1,1) of n+1
+// load / transpose waves (4, 5): stage chunk n+2 and its diagonal k-Gram
+// tiles; score tiles (0,0), (1,1) of n+1
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Unit& un) {
+    constexpr bool GDN = MODE == 0;
     constexpr bool OUT = ROLE != kLeafAggregate;  // q and scores needed only where o is read out
+    // The roles share one control-flow graph, so the compiler's wait-count
+    // analysis can take another role's loads as still in flight here and wait
+    // for every load at each reuse of their registers inside the loop below.
+    // An explicit vmcnt(0) (free: this wave has issued no load yet) clears that.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int ti = w - 4;     // score tile (ti, ti)
     const int x = tid - 256;  // 0..127
@@ -835,6 +844,10 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
         const bool act = m < un.ne;
         const bool nxt = m + 1 < un.ne;
         const Gates& G = sm.gate[m % 3];
+        // Every load of this wave is a chunk old here; stating so keeps the
+        // compiler from waiting on the loads issued just below (its analysis
+        // loses track of the older ones across the conditional steps).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         // ---- phase A: chunk m+1 in flight; k^T of chunk m; score tile (ti, ti) of m ----
         if (act) {
             if (nxt) load(m + 1, knext, vne);
@@ -842,14 +855,13 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
             if (OUT) score_tile(sm, m & 1, G, ti, ti, l32, h, preg);
         }
         lds_barrier();  // A
-        // ---- phase B: v^T of chunk m ----
+        // ---- phase B: v^T of chunk m; k, q of chunk m+1 ----
         if (act) stage_vt(vcu);
+        if (nxt) stage(m + 1, knext);
         lds_barrier();  // B
-        // ---- phase C: scores of m; k, q, gates of chunk m+1 ----
-        if (act) {
-            if (OUT) store_score_tile(sm, ti, ti, l32, h, preg);
-            if (nxt) stage(m + 1, knext);
-        }
+        // ---- phase C: scores of m; diagonal k-Gram tile (ti, ti) of chunk m+1 ----
+        if (act && OUT) store_score_tile(sm, ti, ti, l32, h, preg);
+        if (GDN && nxt) a_tile(sm, sm.gate[(m + 1) % 3], ti, ti, sm.Tm[ti], l32, h);
         lds_barrier();  // C
     };
     // two steps per trip so that the current / next register sets alternate
