@@ -31,9 +31,10 @@
 //                  of S^T (128 keys, fp32) in four 32x32 MFMA accumulator tiles
 //                  for the whole sequence and runs chunk n's S-dependent
 //                  products (U, O, the state update);
-//   waves 2,3,6,7  chunk n+1's off-diagonal k-Gram tile and UT solve: the two diagonal
-//                  32x32 blocks of T are inverted inside one wave each (no
-//                  barrier), the off-diagonal block by two waves, then W;
+//   waves 2,3,6,7  chunk n+1's UT solve: the two diagonal 32x32 blocks of T
+//                  are inverted inside one wave each (no barrier), the
+//                  off-diagonal block by two waves, then W; one of them builds
+//                  chunk n+2's off-diagonal k-Gram tile beside W;
 //   waves 4-5      load chunk n+2 (coalesced 16-byte rows), stage it in LDS
 //                  (q, k row-major; k^T, v^T transposed), compute its two
 //                  diagonal k-Gram tiles and two of chunk n+1's score tiles.
@@ -641,7 +642,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
         const int m = it + 1;
         const bool act = m < un.ne;
         const Gates& G = sm.gate[m % 3];
-        // ---- phase A: off-diagonal k-Gram tile; diagonal 32x32 blocks of T in-wave ----
+        // ---- phase A: diagonal 32x32 blocks of T in-wave (the first chunk also builds its k-Gram tiles) ----
         if (gi == 0 && m + 1 < un.ne) load_ab(m + 1);
         if (act) {
             if (GDN && gi <= 1) {
@@ -653,7 +654,8 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 const f32x4 mm = sv.mul_lds(X + 16 * LS, X, z);
                 sv.put(X + 16 * LS, sv.mul_acc(X + 16 * LS + 16, mm, z), -1.f);
             } else if (GDN && gi == 2) {
-                a_tile(sm, G, 1, 0, sm.Abl, l32, h);
+                // later chunks' tile is built in the previous phase C
+                if (m == un.nb) a_tile(sm, G, 1, 0, sm.Abl, l32, h);
             } else if (OUT && gi == 3) {
                 score_tile(sm, m & 1, G, 1, 0, l32, h, preg);
             }
@@ -729,24 +731,29 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
         if (gi == 0 && m + 1 < un.ne)
             stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, split ? pw : pb, T, lane);
         lds_barrier();  // B
-        // ---- phase C: W = T diag(beta gamma) K (stored -W) for key tile gi; scores ----
+        // ---- phase C: W = T diag(beta gamma) K (stored -W): key tile gi, and tile 2 on
+        // gi 1; gi 2 builds chunk m+1's off-diagonal k-Gram tile; scores ----
+        auto w_tile = [&](int jt) {
+            const uint16_t* KT = sm.KT[m & 1];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const uint16_t* tr = &sm.Tbg[(32 * tt + l32) * LT + 8 * h];
+                auto lk = [&](int k) { return lds8(&KT[tsw(32 * jt + l32, 16 * k + 8 * h)]); };
+                auto lt = [&](int k) { return lds8(tr + 16 * k); };
+                // T is lower triangular: token tile 0 needs columns 0..31 only
+                const f32x16 acc = tt == 0 ? mfma_chain2<2>(lk, lt, f32x16{}) : mfma_chain2<4>(lk, lt, f32x16{});
+                uint16_t* wrow = &sm.W[(32 * tt + l32) * LW + 32 * jt];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    *reinterpret_cast<uint2*>(wrow + elem_index(0, 4 * b, h)) =
+                        pack4(-acc[4 * b], -acc[4 * b + 1], -acc[4 * b + 2], -acc[4 * b + 3]);
+            }
+        };
         if (act) {
             if (GDN) {
-                const uint16_t* KT = sm.KT[m & 1];
-                const int jt = gi;
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const uint16_t* tr = &sm.Tbg[(32 * tt + l32) * LT + 8 * h];
-                    auto lk = [&](int k) { return lds8(&KT[tsw(32 * jt + l32, 16 * k + 8 * h)]); };
-                    auto lt = [&](int k) { return lds8(tr + 16 * k); };
-                    // T is lower triangular: token tile 0 needs columns 0..31 only
-                    const f32x16 acc = tt == 0 ? mfma_chain2<2>(lk, lt, f32x16{}) : mfma_chain2<4>(lk, lt, f32x16{});
-                    uint16_t* wrow = &sm.W[(32 * tt + l32) * LW + 32 * jt];
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        *reinterpret_cast<uint2*>(wrow + elem_index(0, 4 * b, h)) =
-                            pack4(-acc[4 * b], -acc[4 * b + 1], -acc[4 * b + 2], -acc[4 * b + 3]);
-                }
+                if (gi != 2) w_tile(gi);
+                if (gi == 1) w_tile(2);
+                if (gi == 2 && m + 1 < un.ne) a_tile(sm, sm.gate[(m + 1) % 3], 1, 0, sm.Abl, l32, h);
             }
             if (OUT && gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
         }
