@@ -56,7 +56,10 @@ def scan_bytes(w) -> int:
 
 
 def scan_flops(w) -> float:
-    """Executed MFMA flops of the chunk algorithm per call (dense tiles):
+    """Dense-tile MFMA flops of the chunk algorithm per call, every C x C-sized
+    product counted in full (the kernels skip tiles above the diagonal, so
+    this is neither the executed nor the useful count; reported beside the
+    algorithmic figure for comparison):
     gdn: 5 C^2-sized products (K K^T, Q K^T, W, U~, P U) = 10 C d per
     head-token, 3 state products (W S^T, Q S^T, U^T D K) = 6 d^2, UT solve C^2/3;
     gla: 2 C^2 products (Q K^T, P V) and 2 state products."""
@@ -204,6 +207,37 @@ def timed(step, K: int, dev):
     return e0.elapsed_time(e1), time.perf_counter() - t0
 
 
+def warm_up(step, W: int, min_ms: float) -> int:
+    """W untimed calls of step(i), then more, in groups of 8, until at least
+    ``min_ms`` of back-to-back work has run: the GPU raises its clock over the
+    first ~15 ms of sustained load, so a fixed count alone can stop inside that
+    ramp.  Returns the number of calls made."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(W):
+        step(n)
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def rotation_sets(set_bytes: int, min_sets: int, min_total: int) -> int:
+    """Input sets the timed calls cycle through so that no set is still in the
+    256 MB MALL when it comes round again: at least ``min_sets`` and more than
+    ``min_total`` bytes in all."""
+    return max(min_sets, -(-(min_total + 1) // max(set_bytes, 1)))
+
+
+MALL_BYTES = 256 << 20
+
+
 def copy_probe(mib: int, dev):
     """One plain device copy of ``mib`` MiB (a kernel of known traffic that
     calibrates the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)."""
@@ -241,25 +275,32 @@ def bench_decode(args, w):
         t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         return t.to(torch.bfloat16) if bf16 else t
 
-    S = up(S0)
+    # R disjoint state sets (more than twice the MALL in all) taken in turn,
+    # so that a step never finds its states left in the MALL by the step
+    # before; set r is a head-rolled copy of the generated states (the same
+    # distribution, other addresses) and advances by one token every R steps
+    R = args.rotate if args.rotate else rotation_sets(N * w.dv * w.dk * 4, 3, 2 * MALL_BYTES)
+    S_sets = [up(np.roll(S0, r, axis=0)) for r in range(R)]
+    del S0
     q, k, v, a = up(q, bf), up(k, bf), up(v, bf), up(a)
     be = up(be) if be is not None else None
-    o = torch.empty((N, w.dv), dtype=q.dtype, device=dev)
+    o_sets = [torch.empty((N, w.dv), dtype=q.dtype, device=dev) for _ in range(R)]
 
-    def step(t):
-        gds.decode_step(q[t], k[t], v[t], a[t], None if be is None else be[t], S, o=o)
+    def step(i):
+        t, r = i % nsteps, i % R
+        gds.decode_step(q[t], k[t], v[t], a[t], None if be is None else be[t], S_sets[r],
+                        o=o_sets[r])
 
     copy_probe(args.copy_probe_mib, dev)
 
-    for i in range(args.warmup):
-        step(i % nsteps)
-    torch.cuda.synchronize()
+    warm_calls = warm_up(step, args.warmup, args.warmup_ms)
     K = args.steps if args.steps else nsteps
-    span_ms, wall = timed(lambda i: step(i % nsteps), K, dev)
+    span_ms, wall = timed(lambda i: step(warm_calls + i), K, dev)
     ms_per_step = span_ms / K
     kern_ms = ms_per_step  # one kernel launch per step
-    log(f"bench: {K} decode steps back to back, span {span_ms:.3f} ms "
-        f"({kern_ms * 1e3:.2f} us per launch), wall {wall * 1e3:.1f} ms")
+    log(f"bench: {warm_calls} warm-up steps, then {K} decode steps back to back over {R} "
+        f"state sets, span {span_ms:.3f} ms ({kern_ms * 1e3:.2f} us per launch), "
+        f"wall {wall * 1e3:.1f} ms")
     alg = decode_bytes(w)
     gbs = alg / (kern_ms / 1e3) / 1e9
     src = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "decode.hip")
@@ -277,7 +318,9 @@ def bench_decode(args, w):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "mode": w.mode, "states": N, "sequences": w.B, "H": w.H,
-                   "dk": w.dk, "dv": w.dv, "io_dtype": w.dtype, "state_dtype": "f32"},
+                   "dk": w.dk, "dv": w.dv, "io_dtype": w.dtype, "state_dtype": "f32",
+                   "rotated_state_sets": R, "rotated_bytes": R * N * w.dv * w.dk * 4,
+                   "warmup_calls_run": warm_calls},
         "roofline": {
             "bound": "hbm",
             "achieved": gbs,
@@ -403,9 +446,7 @@ def bench_prism(args, w):
         scan()
 
     copy_probe(args.copy_probe_mib, dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls = warm_up(lambda i: step(), args.warmup, args.warmup_ms)
     span_ms, wall = timed(lambda i: step(), args.steps, dev)
     ms_per_step = span_ms / args.steps
     # each kernel alone, back to back, for the per-kernel rooflines
@@ -435,7 +476,8 @@ def bench_prism(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "mode": "gdn_ew (PRISM)", "B": B, "H": H, "T": T,
                    "elements_per_token": G, "L": L, "W": w.prism_window, "dk": w.dk, "dv": w.dv,
-                   "chunk": w.chunk, "io_dtype": w.dtype, "state_dtype": "f32"},
+                   "chunk": w.chunk, "io_dtype": w.dtype, "state_dtype": "f32",
+                   "warmup_calls_run": warm_calls},
         "roofline": {
             "bound": "hbm",
             "achieved": scan_alg / (scan_ms / 1e3) / 1e9,
@@ -544,9 +586,7 @@ def bench_lact(args, w):
         gds.lact_fwd(q, k, v, et, W0, chunk=w.chunk, o=o, WT=WT, workspace=ws)
 
     copy_probe(args.copy_probe_mib, dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls = warm_up(lambda i: step(), args.warmup, args.warmup_ms)
     span_ms, wall = timed(lambda i: step(), args.steps, dev)
     ms = span_ms / args.steps
     log(f"bench: {args.steps} lact_fwd calls, {ms:.4f} ms per call, wall {wall * 1e3:.1f} ms")
@@ -569,7 +609,7 @@ def bench_lact(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                    "chunk": w.chunk, "order": "update_then_apply", "io_dtype": w.dtype,
-                   "weight_dtype": "f32"},
+                   "weight_dtype": "f32", "warmup_calls_run": warm_calls},
         "roofline": {
             "bound": "hbm",
             "achieved": alg / (ms / 1e3) / 1e9,
@@ -688,9 +728,7 @@ def bench_bwd(args, w):
         gds.scan_bwd(q, k, v, alpha, beta, S0, g_o, g_s, workspace=ws, out=outs)
 
     copy_probe(args.copy_probe_mib, dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls = warm_up(lambda i: step(), args.warmup, args.warmup_ms)
     span_ms, wall = timed(lambda i: step(), args.steps, dev)
     ms = span_ms / args.steps
     log(f"bench: {args.steps} scan_bwd calls, {ms:.4f} ms per call, wall {wall * 1e3:.1f} ms")
@@ -718,7 +756,8 @@ def bench_bwd(args, w):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk,
-                   "dv": w.dv, "chunk": 32, "io_dtype": w.dtype, "grad_dtype": "f32"},
+                   "dv": w.dv, "chunk": 32, "io_dtype": w.dtype, "grad_dtype": "f32",
+                   "warmup_calls_run": warm_calls},
         "roofline": {
             "bound": "mfma",
             "achieved": tfs,
@@ -752,6 +791,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: enough to cover the GPU's clock ramp, "
                          "~15 ms: 30 scan calls or 300 decode steps)")
+    ap.add_argument("--warmup-ms", type=float, default=200.0,
+                    help="after the --warmup calls, keep warming up until this much "
+                         "back-to-back work has run (covers the clock ramp whatever --warmup is)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input (decode: state) sets the timed calls take in turn; 0 = enough "
+                         "for at least 3 and more than twice the 256 MB MALL")
     ap.add_argument("--workload", default="gdn-b8h16t8192")
     ap.add_argument("--path", default="auto", choices=["auto", "sequential", "blelloch"])
     ap.add_argument("--leaf-chunks", type=int, default=0)
@@ -808,13 +853,26 @@ def main():
         return t.to(torch.bfloat16) if bf16 else t
 
     bf = w.dtype == "bf16"
-    q, k, v = up(b.q, bf), up(b.k, bf), up(b.v, bf)
-    alpha = up(b.alpha)
-    beta = up(b.beta) if b.beta is not None else None
-    S0 = up(b.S0) if b.S0 is not None else None
+    # R input sets taken in turn by the timed calls (at least 3, more than
+    # twice the 256 MB MALL in all), so that no call finds its inputs left in
+    # the MALL by an earlier one; set r rolls the generated batch by r heads
+    # (the same distribution at other addresses), each with its own o and S_T
+    R = args.rotate if args.rotate else rotation_sets(scan_bytes(w), 3, 2 * MALL_BYTES)
+
+    def rolled(x, r, bf16=False):
+        if x is None:
+            return None
+        y = np.roll(x.reshape(w.B * w.H, *x.shape[2:]), r, axis=0).reshape(x.shape)
+        return up(y, bf16)
+
+    sets = []
+    for r in range(R):
+        sets.append(dict(q=rolled(b.q, r, bf), k=rolled(b.k, r, bf), v=rolled(b.v, r, bf),
+                         alpha=rolled(b.alpha, r), beta=rolled(b.beta, r), S0=rolled(b.S0, r),
+                         o=torch.empty((w.B, w.H, w.T, w.dv),
+                                       dtype=torch.bfloat16 if bf else torch.float32, device=dev),
+                         ST=torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)))
     del b
-    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=q.dtype, device=dev)
-    ST = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
     mode = gds.SCAN_GDN if w.mode == "gdn" else gds.SCAN_GLA
     if w.diag_gates:
         mode = gds.SCAN_GDN_DIAG if w.mode == "gdn" else gds.SCAN_GLA_DIAG
@@ -824,24 +882,22 @@ def main():
                                            args.leaf_chunks)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
-    def step():
-        gds.scan_fwd(q, k, v, alpha, beta, S0, chunk=w.chunk, path=path,
-                     leaf_chunks=args.leaf_chunks, o=o, ST=ST, workspace=ws)
+    def step(i):
+        x = sets[i % R]
+        gds.scan_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"], chunk=w.chunk,
+                     path=path, leaf_chunks=args.leaf_chunks, o=x["o"], ST=x["ST"], workspace=ws)
 
     copy_probe(args.copy_probe_mib, dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    span_ms, wall = timed(lambda i: step(), args.steps, dev)
+    warm_calls = warm_up(step, args.warmup, args.warmup_ms)
+    span_ms, wall = timed(lambda i: step(warm_calls + i), args.steps, dev)
     ms_per_step = span_ms / args.steps
     # the sequential path is one kernel launch per step; the long path's
     # figure covers all of its kernels
     kern_ms = ms_per_step
     tokens = w.B * w.T
     value = tokens / (ms_per_step / 1e3)
-    log(f"bench: {args.steps} steps back to back, span {span_ms:.3f} ms "
-        f"({kern_ms:.4f} ms per step), wall {wall * 1e3:.1f} ms")
+    log(f"bench: {warm_calls} warm-up calls, then {args.steps} calls back to back over {R} "
+        f"input sets, span {span_ms:.3f} ms ({kern_ms:.4f} ms per step), wall {wall * 1e3:.1f} ms")
 
     alg_bytes = scan_bytes(w) + (w.B * w.H * w.T * (w.dk - 1) * 4 if w.diag_gates else 0)
     flops = scan_flops(w)
@@ -870,7 +926,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "T": w.T,
                    "dk": w.dk, "dv": w.dv, "chunk": w.chunk, "path": path,
-                   "io_dtype": w.dtype, "state_dtype": "f32"},
+                   "io_dtype": w.dtype, "state_dtype": "f32", "rotated_input_sets": R,
+                   "rotated_bytes": R * scan_bytes(w), "warmup_calls_run": warm_calls},
     }
     if w.diag_gates:
         # float32 kernel: its products run on the fp32 MFMA, whose floor
@@ -921,14 +978,15 @@ def plain_scan_rooflines(path, achieved_gbs, traffic, alg_bytes, kern_ms, achiev
             "kernel_ms": kern_ms,
         },
         "mfma": {
-            "achieved_tflops": achieved_tfs,
+            "achieved_tflops": flops_alg / (kern_ms / 1e3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFS,
-            "frac": achieved_tfs / BF16_MFMA_PEAK_TFS,
-            "flops_per_launch": flops,
-            "count": "executed dense-tile flops of the chunk algorithm",
-            "alg_tflops": flops_alg / (kern_ms / 1e3) / 1e12,
-            "alg_frac": flops_alg / (kern_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
-            "alg_flops_per_launch": flops_alg,
+            "frac": flops_alg / (kern_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
+            "flops_per_launch": flops_alg,
+            "count": "algorithmic flops: triangular C x C products at their useful size, "
+                     "state products in full, UT solve C^2/3 per head-token",
+            "dense_tile_tflops": achieved_tfs,
+            "dense_tile_frac": achieved_tfs / BF16_MFMA_PEAK_TFS,
+            "dense_tile_flops_per_launch": flops,
         },
     }
 

@@ -57,11 +57,52 @@ def max_err(x, ref, head_dims):
     return float(np.max(oracle.rel_err_per_head(x, ref, head_dims)))
 
 
+BLOCK = 64        # tokens per block of the local check
+BLOCK_FACTOR = 4  # block gate = BLOCK_FACTOR x the head-wide gate
+
+
+def block_err(x, ref, head_dims, block=BLOCK):
+    """Local companion of the head-wide error, for outputs laid out
+    [heads..., T, d]: the largest ||x_b - ref_b||_F over 64-token blocks b (a
+    ragged last block holds the remaining tokens), divided by the head's RMS
+    norm of a 64-token block, ||ref||_F sqrt(64 / T) (the absolute norm where
+    a head's reference is zero).  With a uniform relative error e every block
+    reads e, so the head-wide error is the RMS of these ratios; one wrong token
+    in a long sequence moves the head-wide figure by 1/sqrt(T / 64) of what it
+    moves its block's."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    T = ref.shape[-2]
+    heads = ref.shape[:head_dims]
+    nb = -(-T // block)
+    pad = nb * block - T
+    d2 = (x - ref) ** 2
+    d2 = d2.reshape(*heads, T, -1).sum(axis=-1)
+    if pad:
+        d2 = np.concatenate([d2, np.zeros((*heads, pad))], axis=-1)
+    blk = np.sqrt(d2.reshape(*heads, nb, block).sum(axis=-1))
+    den = np.sqrt(np.sum(ref.reshape(*heads, -1) ** 2, axis=-1)) * np.sqrt(block / T)
+    den = np.where(den > 0, den, 1.0)[..., None]
+    return float(np.max(blk / den))
+
+
+def assert_local(o, o_ref, head_dims, tol, what=""):
+    """The block check alone, for tests that gate the head-wide error themselves."""
+    eb = block_err(o, o_ref, head_dims)
+    say(f"  {what} o worst 64-token block {eb:.3e} (block gate {BLOCK_FACTOR * tol:.0e})")
+    assert eb <= BLOCK_FACTOR * tol, f"o block error {eb:.3e} > {BLOCK_FACTOR * tol:.0e}"
+    return eb
+
+
 def assert_parity(o, ST, o_ref, ST_ref, dtype, head_dims=2, tol=None, what=""):
     tol = TOL[dtype] if tol is None else tol
     eo = max_err(o, o_ref, head_dims)
     es = max_err(ST, ST_ref, head_dims) if ST is not None else 0.0
-    say(f"  parity {what}: o {eo:.3e}  S_T {es:.3e}  (gate {tol:.0e})")
+    # the block check needs a token axis: o laid out [heads..., T, d]
+    eb = block_err(o, o_ref, head_dims) if np.ndim(o_ref) >= head_dims + 2 else 0.0
+    say(f"  parity {what}: o {eo:.3e}  S_T {es:.3e}  o worst 64-token block {eb:.3e}  "
+        f"(gate {tol:.0e}, block gate {BLOCK_FACTOR * tol:.0e})")
     assert eo <= tol, f"o error {eo:.3e} > {tol:.0e}"
     assert es <= tol, f"S_T error {es:.3e} > {tol:.0e}"
+    assert eb <= BLOCK_FACTOR * tol, f"o block error {eb:.3e} > {BLOCK_FACTOR * tol:.0e}"
     return eo, es

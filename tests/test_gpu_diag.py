@@ -12,7 +12,7 @@ import oracle
 import scan_sequence_models_amd as gds
 from scan_sequence_models_amd import inputs as I
 
-from _parity import TOL, assert_parity, dev, host, max_err, say
+from _parity import TOL, assert_local, assert_parity, dev, host, max_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +110,7 @@ def test_diag_full_workload_sampled_heads():
         es = max_err(ST[bb, hh][None], S_ref[None], 1)
         say(f"  head ({bb},{hh}): o {eo:.3e}  S_T {es:.3e}  (gate {TOL['bf16']:.0e})")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+        assert_local(o[bb, hh][None], o_ref[None], 1, TOL["bf16"], f"head ({bb},{hh})")
 
 
 def _wide_chunks(a, limit=64.0):

@@ -13,7 +13,7 @@ from oracle import lact as olact
 import scan_sequence_models_amd as gds
 from scan_sequence_models_amd import inputs as I
 
-from _parity import TOL, assert_parity, dev, host, max_err, say
+from _parity import TOL, assert_local, assert_parity, dev, host, max_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +83,4 @@ def test_lact_full_workload_sampled_heads():
         ew = max_err(WT[bb, hh][None], W_ref[None], 1)
         say(f"  head ({bb},{hh}): o {eo:.3e}  W_T {ew:.3e}  (gate {TOL['bf16']:.0e})")
         assert eo <= TOL["bf16"] and ew <= TOL["bf16"]
+        assert_local(o[bb, hh][None], o_ref[None], 1, TOL["bf16"], f"head ({bb},{hh})")

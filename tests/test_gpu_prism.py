@@ -17,7 +17,7 @@ from oracle import prism as oprism
 import scan_sequence_models_amd as gds
 from scan_sequence_models_amd import inputs as I
 
-from _parity import TOL, assert_parity, dev, host, max_err, say
+from _parity import TOL, assert_local, assert_parity, dev, host, max_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -229,3 +229,4 @@ def test_prism_full_workload_sampled_heads():
         es = max_err(ST[bb, hh][None], S_ref[None], 1)
         say(f"  head ({bb},{hh}): o {eo:.3e}  S_T {es:.3e}  (gate {TOL[dt]:.0e})")
         assert eo <= TOL[dt] and es <= TOL[dt]
+        assert_local(o[bb, hh][None], o_ref[None], 1, TOL[dt], f"head ({bb},{hh})")
