@@ -13,36 +13,52 @@
 // entering the chunk:
 //
 //   A    = strict_lower(diag(beta) (Gamma * K K^T))        k-Gram      (MFMA)
-//   T    = (I + A)^-1                                       UT solve    (fp32)
-//   W    = T diag(beta gamma) K                             WY factor   (MFMA)
+//   T    = (I + A)^-1                                       UT solve
+//   X    = K S^T                                            (MFMA, needs S)
+//   U    = T diag(bw) V - T diag(beta gamma) X              (MFMA)
 //   P    = (Q K^T) * Gamma * M_incl                         scores      (MFMA)
-//   U    = T diag(bw) V - W S^T                             (MFMA, needs S)
 //   O    = diag(gamma) Q S^T + P U                          (MFMA, needs S)
 //   S   <- gamma_C S + U^T diag(dec) K                      (MFMA, fp32 state)
 //
-// gated linear attention: U = V and A, T, W vanish.
+// U = T (diag(bw) V - diag(beta gamma) K S^T) is the WY form's U with the
+// factor W = T diag(beta gamma) K never formed; gated linear attention has
+// U = V and no A, T, X.
 //
 // Mapping onto gfx950.  A workgroup of 8 waves owns one head and a 64-row slice
 // of its value channels (B*H*2 workgroups on the sequential path); all slices of
 // a head go to one XCD (blocks are dealt round-robin over the 8 XCDs) so their
-// repeated q/k reads share that XCD's L2.  The waves specialise and work on
-// three chunks at once:
-//   waves 0-1      state waves: wave w keeps the 32 value columns [32w, 32w+32)
-//                  of S^T (128 keys, fp32) in four 32x32 MFMA accumulator tiles
-//                  for the whole sequence and runs chunk n's S-dependent
-//                  products (U, O, the state update);
-//   waves 2,3,6,7  chunk n+1's UT solve: the two diagonal 32x32 blocks of T
-//                  are inverted inside one wave each (no barrier), the
-//                  off-diagonal block by two waves, then W; one of them builds
-//                  chunk n+2's off-diagonal k-Gram tile beside W;
-//   waves 4-5      load chunk n+2 (coalesced 16-byte rows), stage it in LDS
-//                  (q, k row-major; k^T, v^T transposed), compute its two
-//                  diagonal k-Gram tiles and two of chunk n+1's score tiles.
-// Everything meets through LDS and all waves pass the same three barriers per
-// chunk.  Products are v_mfma_f32_32x32x16_bf16 (fp32 accumulation, bf16
-// operands) except the UT solve, which stays in fp32: diagonal 16x16 blocks by
-// forward substitution on the VALU, off-diagonal blocks on the fp32 MFMA
-// (16x16x4).
+// repeated q/k reads share that XCD's L2.  The waves specialise; wave w runs on
+// SIMD w % 4, and each chunk step has two halves separated by LDS barriers.  In
+// step j, chunk j is read out:
+//
+//   waves 0, 1  state: wave w keeps the 32 value columns [32w, 32w+32) of S^T
+//               (128 keys, fp32) in four 32x32 MFMA accumulator tiles for the
+//               whole sequence.  First half: X = K S^T and Q S^T of chunk j;
+//               second half: U, O (written out) and the state update.
+//   waves 4, 5  first half: T's two diagonal 32x32 blocks of chunk j scaled into
+//               the bf16 factors Tb = T diag(bw), Tbn = -T diag(beta gamma);
+//               second half: chunk j+1's q, k, v staged in LDS, then chunk j+2's
+//               rows loaded into registers (coalesced 16-byte loads).
+//   wave 2      first half: chunk j+1's two diagonal k-Gram tiles; second
+//               half: the gates of chunk j+2 (a wave scan of ln alpha).
+//   wave 3      first half: chunk j+1's off-diagonal k-Gram tile and chunk j's
+//               score tile (0,0).
+//   wave 6      first half: T's off-diagonal block of chunk j,
+//               -D_bot A_bl D_top, by split-bf16 products (hi/lo parts, three
+//               MFMAs per product), scaled into Tb, Tbn; second half: the top
+//               diagonal 32x32 block of chunk j+1's T (16x16 blocks by forward
+//               substitution, the block below their diagonal on the fp32 MFMA).
+//   wave 7      first half: chunk j's score tiles (1,0) and (1,1); second half:
+//               the bottom diagonal block of chunk j+1's T.
+//
+// The k-Gram waves read k straight from global memory into MFMA operand
+// registers (a chunk ahead); the other products read LDS.  Operands contracted
+// over tokens (k for the state update, v for T V) come from row-major tiles
+// through ds_read_b64_tr_b16 transposed reads.  LDS strides: q rows 136
+// elements (16-row 16-byte reads conflict-free), k rows 160 with 16-byte
+// granules XOR-swizzled by (row / 4) mod 4 (conflict-free for both 16-row
+// reads and 4-row transposed reads), v rows 96 (transposed reads only), the
+// [token][token] bf16 tiles 72.
 //
 // Operand trick: a 32x32 accumulator tile holds, in lane (n, h), rows
 // 8b + 4h + r (b, r < 4) of column n.  Elements 8s..8s+7 of a lane are then the
@@ -50,9 +66,7 @@
 // tile's row.  Rows are therefore numbered with bits 2 and 3 swapped (perm5):
 // accumulator row rho holds key/token perm5(rho), and elements 8s..8s+7 are the
 // consecutive keys/tokens 16s + 8h .. 16s + 8h + 7.  Every LDS array whose
-// rows are read as an A operand stores logical row r at physical row perm5(r),
-// so that all operand reads are natural 16-byte row reads (conflict-free with
-// the padded strides below).
+// rows are read as an A operand stores logical row r at physical row perm5(r).
 //
 // Tokens past T in the last chunk are identity tokens (alpha = 1, beta = 0,
 // q = k = v = 0), which leave S unchanged; their outputs are not written.
@@ -67,34 +81,47 @@ constexpr int DK = 128;      // key channels
 constexpr int DV = 128;      // value channels
 constexpr int DVS = 64;      // value channels per workgroup
 constexpr int NT = 512;      // 8 waves
-constexpr int LW = DK + 8;   // row stride (elements) of [token][key] bf16 arrays
-constexpr int LT = C + 8;    // row stride of [*][token] bf16 arrays
-constexpr int LS = 32 + 4;   // row stride of fp32 32x32 solve tiles
+constexpr int LK = 160;      // row stride (elements) of k [token][key], granules swizzled
+constexpr int LQ = DK + 8;   // row stride of q [token][key]
+constexpr int LV = 96;       // row stride of the v slice [token][value]
+constexpr int LT = C + 8;    // row stride of [token][token] bf16 tiles
+constexpr int LS = 32 + 4;   // row stride of fp32 32x32 tiles
+constexpr int LO = DVS + 8;  // row stride of the staged o tile [token][value]
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Gates of one chunk: g = in-chunk cumulative ln alpha, gamma = e^g,
-// dec = e^(g_C - g), beta (erase) and bw (write strength); gl = g log2(e) and
-// gb = gl + log2(beta) feed the masks as exp2(gl_t - gl_s) = Gamma_ts and
-// exp2(gb_t - gl_s) = beta_t Gamma_ts.
-struct Gates {
-    float g[C], gam[C], dec[C], bet[C], bw[C], gl[C], gb[C];
+// Gates of one chunk: gamma = e^g, dec = e^(g_C - g), bw (write strength),
+// bg = beta gamma; gl = g log2(e) and gb = gl + log2(beta) feed the masks as
+// exp2(gl_t - gl_s) = Gamma_ts and exp2(gb_t - gl_s) = beta_t Gamma_ts.  When
+// the chunk's log2 decay spans at most kSpan (`fast`), the masks use the
+// factored form Gamma_ts = el_t fl_s with el = exp2(gl - gl_32) and
+// fl = exp2(gl_32 - gl) (every factor within 2^+-kSpan, no overflow), and
+// ebt = beta el: two multiplies per element instead of an exponential.
+constexpr float kSpan = 100.f;
+struct alignas(16) Gates {
+    float gam[C], dec[C], bw[C], bg[C], gl[C], gb[C], el[C], fl[C], ebt[C];
+    int fast, pad[3];  // (16-byte size: every slot's arrays take 16-byte reads)
 };
+static_assert(sizeof(Gates) % 16 == 0, "gate slots must stay 16-byte aligned");
 
-// Shared memory of one workgroup (159 KB).  Chunk c's gates live in gate[c % 3],
-// its q in Q[c % 2], its k^T in KT[c % 2]; the other arrays are single.
+// Shared memory of one workgroup (155 KB).  Chunk c's k and v live in slot
+// c % 2 (so do the off-diagonal k-Gram tiles), its gates in slot c % 3; the
+// other arrays are single.
 struct Smem {
-    uint16_t Q[2][C * LW];    // q [token][key]                        (rows perm5)
-    uint16_t K[C * LW];       // k [token][key]                        (rows perm5)
-    uint16_t W[C * LW];       // -W [token][key]                       (rows perm5)
-    uint16_t KT[2][DK * LT];  // k^T [key][token]     (rows perm5, token granules swizzled)
-    uint16_t VT[DVS * LT];    // v slice^T [value][token]              (token granules swizzled)
-    uint16_t P[C * LT];       // scores [token][token]                 (rows perm5)
-    uint16_t Tb[C * LT];      // T diag(bw) [token][token]             (rows perm5)
-    uint16_t Tbg[C * LT];     // T diag(beta gamma)                    (rows perm5)
-    float Tm[2][32 * LS];     // diagonal 32x32 blocks of A, then of T (fp32, natural)
-    float Abl[32 * LS];       // A rows 32..63, columns 0..31 (fp32, natural)
+    uint16_t K[2][C * LK];    // k [token][key]                 (rows perm5, granules swizzled)
+    uint16_t Q[C * LQ];       // q [token][key]                 (rows perm5)
+    uint16_t V[2][C * LV];    // v slice [token][value]         (natural rows)
+    uint16_t Tb[C * LT];      // T diag(bw) [token][token]      (rows perm5)
+    uint16_t Tbn[C * LT];     // -T diag(beta gamma)            (rows perm5)
+    uint16_t P[C * LT];       // scores [token][token]          (rows perm5)
+    float At[2][32 * LS];     // diagonal k-Gram tiles of A, transposed: At[b][s][t] = A[32b+t][32b+s]
+    float Ablt[2][32 * LS];   // A rows 32..63, columns 0..31, transposed
+    float D[2][32 * LS];      // diagonal 32x32 blocks of T (natural)
+    float Dt[32 * LS];        // the top one, transposed
+    uint16_t Ost[C * LO];     // o of the chunk just read out [token][value] (natural rows)
     Gates gate[3];
 };
 
@@ -117,16 +144,8 @@ __device__ __forceinline__ bf16x8 half8(const f32x16& x) {
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
     return __builtin_bit_cast(uint2, __builtin_convertvector((f32x4{a, b, c, d}), bf16x4));
 }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
-}
-// low (high) 16-bit halves of a and b, a's in the low half of the result
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-__device__ __forceinline__ uint32_t word(const uint4& u, int i) {
-    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+__device__ __forceinline__ uint4 pack8(const f32x8& x) {
+    return __builtin_bit_cast(uint4, __builtin_convertvector(x, bf16x8));
 }
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits
 // for every outstanding global load and store of the wave (vmcnt), which would
@@ -134,6 +153,11 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int i) {
 // keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Completes this wave's own LDS accesses before the ones that follow (a wave
+// reading back what its other lanes wrote).
+__device__ __forceinline__ void lds_fence() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value,
 // so that role and tile choices compile to scalar branches.
@@ -148,10 +172,10 @@ __device__ __forceinline__ int perm5(int r) { return (r & ~12) | ((r & 4) << 1) 
 __device__ __forceinline__ int elem_index(int tile, int e, int h) {
     return 32 * tile + 16 * (e >> 3) + 8 * h + 4 * ((e >> 2) & 1) + (e & 3);
 }
-// [row][token] arrays with 8-token granules XOR-swizzled by row, so that the
-// transposed 8-byte stores spread over the LDS banks (prow: physical row).
-__device__ __forceinline__ int tsw(int prow, int tok) {
-    return prow * LT + ((((tok >> 3) ^ (prow >> 3)) & 7) << 3) + (tok & 7);
+// Element offset of column `col` of physical row `prow` in the k tile: 16-byte
+// granules XOR-swizzled by (prow / 4) mod 4.
+__device__ __forceinline__ int kidx(int prow, int col) {
+    return prow * LK + ((((col >> 3) ^ (prow >> 2)) & 3) | ((col >> 3) & ~3)) * 8 + (col & 7);
 }
 
 // Rows of chunk m of one head's [T][ld] bf16 tensor, read through a buffer
@@ -190,75 +214,6 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
     return x;
-}
-
-// 16x16 block products of the UT solve (fp32 MFMA 16x16x4); lane (n16, g4)
-// holds rows 4 g4 .. 4 g4 + 3 of column n16 of a result.
-struct Solve {
-    int n16, g4;
-    // acc += X Y, both 16x16 blocks of fp32 tiles with row stride LS; lane
-    // (n16, g4) supplies the contraction indices 4 g4 .. 4 g4 + 3, so its X
-    // operands are one 16-byte row read
-    __device__ __forceinline__ f32x4 mul_lds(const float* X, const float* Y, f32x4 acc) const {
-        const f32x4 xr = *reinterpret_cast<const f32x4*>(&X[n16 * LS + 4 * g4]);
-        float yc[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) yc[kk] = Y[(4 * g4 + kk) * LS + n16];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma4(xr[kk], yc[kk], acc);
-        return acc;
-    }
-    // acc += X Y, X a block in LDS, Y an accumulator block (k = 4 g4 + kk)
-    __device__ __forceinline__ f32x4 mul_acc(const float* X, f32x4 Yacc, f32x4 acc) const {
-        const f32x4 xr = *reinterpret_cast<const f32x4*>(&X[n16 * LS + 4 * g4]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma4(xr[kk], Yacc[kk], acc);
-        return acc;
-    }
-    __device__ __forceinline__ void put(float* dst, f32x4 acc, float sign) const {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * LS + n16] = sign * acc[r];
-    }
-};
-
-// In place: the two 16x16 diagonal blocks of the fp32 32x32 tile X (unit lower
-// triangular I + A_bb, strictly lower part stored) are replaced by their
-// inverses, by forward substitution in fp32.  Lane (b, c) (lanes 0..31; lanes
-// 32..63 repeat them and store nothing) owns column c of block b's inverse:
-// x_r = [r == c] - sum_{j<r} A_rj x_j (left-looking), with row r read as
-// broadcast 16-byte loads issued two rows ahead.
-__device__ __forceinline__ void diag_inverse2(float* X, int lane) {
-    const int b = (lane >> 4) & 1, c = lane & 15;
-    const float* A = X + 16 * b * LS + 16 * b;
-    float x[16];
-    f32x4 row[3][4];  // rows r, r+1, r+2 in flight (columns 0 .. 4*ceil(r/4)-1)
-    auto load_row = [&](int r, f32x4 (&dst)[4]) {
-#pragma unroll
-        for (int q = 0; q < (r + 3) / 4; ++q) dst[q] = *reinterpret_cast<const f32x4*>(&A[r * LS + 4 * q]);
-    };
-    load_row(1, row[1]);
-    load_row(2, row[2]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (r + 2 < 16) load_row(r + 2, row[(r + 2) % 3]);
-        __builtin_amdgcn_sched_barrier(0);
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int q = 0; q < (r + 3) / 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * q + i;
-                if (j < r) {
-                    if (i & 1) s1 += row[r % 3][q][i] * x[j];
-                    else s0 += row[r % 3][q][i] * x[j];
-                }
-            }
-        x[r] = (r == c ? 1.f : 0.f) - (s0 + s1);
-    }
-    if (lane < 32) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) X[(16 * b + r) * LS + 16 * b + c] = x[r];
-    }
 }
 
 // acc += sum_{k < N} A(k) B(k) with the LDS operand A(k) loaded two steps
@@ -302,86 +257,56 @@ __device__ __forceinline__ bf16x8 sop(const f32x16 (&t)[N], int kk) {
     return (kk & 1) ? half8<8>(t[kk >> 1]) : half8<0>(t[kk >> 1]);
 }
 
-// One 32x32 k-Gram or score tile of chunk-local tokens, computed transposed:
-// acc[s][t] = sum_key Y[s][key] X[t][key] with s = 32J + row, t = 32I + column.
-// X and Y are [token][key] LDS arrays with rows perm5, read at natural rows, so
-// lane l32 holds column t = 32I + perm5(l32) and element e row
-// s = 32J + elem_index(0, e, h).
-__device__ __forceinline__ f32x16 gram_tile(const uint16_t* X, int I, const uint16_t* Y, int J,
-                                            int l32, int h) {
-    const uint16_t* xr = X + (32 * I + l32) * LW + 8 * h;
-    const uint16_t* yr = Y + (32 * J + l32) * LW + 8 * h;
-    return mfma_chain2<8>([&](int k) { return lds8(yr + 16 * k); },
-                          [&](int k) { return lds8(xr + 16 * k); }, f32x16{});
+// MFMA operand contracted over the tokens of the v slice (natural rows): lane
+// (m = lane % 32, g = lane / 32) gets tokens 16 kk + 8 g .. +7 of value
+// column col0 + perm5(m), by two ds_read_b64_tr_b16 (in each 16-lane group,
+// lane l receives element l % 4 of the 8-byte pieces that lanes 4 i + l / 4
+// address, i = 0..3: four consecutive rows of one column; the supplied column
+// swaps the two bits of the 4-value piece index, which perm5's the columns).
+__device__ __forceinline__ bf16x8 v_operand(const uint16_t* V, int kk, int col0, int lane) {
+    const int l = lane & 15, grp = lane >> 4;
+    const int r = 16 * kk + 8 * (grp >> 1) + (l >> 2);
+    const int piece = ((l & 1) << 1) | ((l >> 1) & 1);
+    const int c = col0 + 16 * (grp & 1) + 4 * piece;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(V + r * LV + c));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(V + (r + 4) * LV + c));
+    const s16x4 ab[2] = {a, b};
+    return __builtin_bit_cast(bf16x8, ab);
+}
+// A operand of the state update, (K^T)[key][token], from the k tile (rows
+// perm5): lane (m = lane % 32, g = lane / 32) gets key 32 jt + perm5(m) of
+// tokens 16 kk + 8 g .. +7.  Token 16kk + 8g + i sits in physical row
+// 16kk + 4g + i (i < 4) or 16kk + 8 + 4g + (i - 4); the supplied column swaps
+// the two bits of the 4-key piece index so that the keys come out perm5'd.
+__device__ __forceinline__ bf16x8 kt_operand(const uint16_t* K, int kk, int jt, int lane) {
+    const int l = lane & 15, grp = lane >> 4, g = grp >> 1;
+    const int r = 16 * kk + 4 * g + (l >> 2);
+    const int piece = ((l & 1) << 1) | ((l >> 1) & 1);
+    const int c = 32 * jt + 16 * (grp & 1) + 4 * piece;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(K + kidx(r, c)));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(K + kidx(r + 8, c)));
+    const s16x4 ab[2] = {a, b};
+    return __builtin_bit_cast(bf16x8, ab);
 }
 
-// Decay mask of tile (I, J): element e of lane (l32, h) is scaled by
-// e^(g_t - g_s) (times beta_t for A) where t >= s (t > s for A), else zeroed;
-// tiles below the diagonal (I > J) need no comparison.  Results in the same
-// layout, 4 consecutive s per element group.
-template <bool IS_A>
-__device__ __forceinline__ f32x16 mask_tile(const f32x16& acc, const Gates& G, int I, int J,
-                                            int l32, int h) {
-    const int t = 32 * I + perm5(l32);
-    const float et = IS_A ? G.gb[t] : G.gl[t];
-    f32x16 r;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int s0 = 32 * J + elem_index(0, 4 * b, h);
-        const f32x4 gs = *reinterpret_cast<const f32x4*>(&G.gl[s0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float d = __builtin_amdgcn_exp2f(et - gs[i]) * acc[4 * b + i];
-            if (I > J) r[4 * b + i] = d;
-            else r[4 * b + i] = (IS_A ? t > s0 + i : t >= s0 + i) ? d : 0.f;
-        }
-    }
-    return r;
+// hi + lo split of 8 floats into two bf16 vectors (hi = RNE(x), lo = RNE(x - hi)).
+__device__ __forceinline__ void split8(const f32x8& x, bf16x8& hi, bf16x8& lo) {
+    hi = __builtin_convertvector(x, bf16x8);
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), bf16x8);
 }
-
-// Scores tile (I, J) of chunk m, masked, packed to bf16 (lane's row of P:
-// physical row 32I + l32, columns 32J + elem_index(0, 4b, h) .. +3).
-__device__ __forceinline__ void score_tile(const Smem& sm, int qbuf, const Gates& G, int I, int J,
-                                           int l32, int h, uint2 (&out)[4]) {
-    const f32x16 acc = gram_tile(sm.Q[qbuf], I, sm.K, J, l32, h);
-    const f32x16 p = mask_tile<false>(acc, G, I, J, l32, h);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) out[b] = pack4(p[4 * b], p[4 * b + 1], p[4 * b + 2], p[4 * b + 3]);
+__device__ __forceinline__ f32x8 ld8f(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ void store_score_tile(Smem& sm, int I, int J, int l32, int h,
-                                                 const uint2 (&p)[4]) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<uint2*>(&sm.P[(32 * I + l32) * LT + 32 * J + elem_index(0, 4 * b, h)]) = p[b];
-}
-
-// k-Gram tile (I, J) of chunk m masked into A (fp32, natural indices, local to
-// the 32x32 destination tile `dst`).
-__device__ __forceinline__ void a_tile(const Smem& sm, const Gates& G, int I, int J, float* dst,
-                                       int l32, int h) {
-    const f32x16 acc = gram_tile(sm.K, I, sm.K, J, l32, h);
-    const f32x16 a = mask_tile<true>(acc, G, I, J, l32, h);
-    const int tl = perm5(l32);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<f32x4*>(&dst[tl * LS + elem_index(0, 4 * b, h)]) =
-            f32x4{a[4 * b], a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]};
-}
-
-// Gates of chunk c from alpha, beta, bw of token `lane` (0 past T; identity
-// tokens there: alpha = 1, beta = bw = 0): an inclusive wave scan of ln alpha.
-__device__ __forceinline__ void stage_gates(Gates& G, int c, float pa, float pb, float pw, int T,
-                                            int lane) {
-    const float x = wave_inclusive_sum(c * C + lane < T ? __logf(pa) : 0.f);
-    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-    const float xl = x * 1.4426950408889634f;  // log2(e)
-    G.g[lane] = x;
-    G.gam[lane] = __expf(x);
-    G.dec[lane] = __expf(last - x);
-    G.bet[lane] = pb;
-    G.bw[lane] = pw;
-    G.gl[lane] = xl;
-    G.gb[lane] = xl + __builtin_amdgcn_logf(pb);  // log2; -inf where beta = 0
+// acc += X Y in split bf16 (X_hi Y_hi + X_hi Y_lo + X_lo Y_hi)
+__device__ __forceinline__ f32x16 mfma_split(const f32x8& x, const f32x8& y, f32x16 acc) {
+    bf16x8 xh, xl, yh, yl;
+    split8(x, xh, xl);
+    split8(y, yh, yl);
+    acc = mfma32(xh, yh, acc);
+    acc = mfma32(xh, yl, acc);
+    return mfma32(xl, yh, acc);
 }
 
 struct Unit {
@@ -418,17 +343,132 @@ __device__ __forceinline__ Unit unit_of(const ChunkJob& job) {
     return un;
 }
 
+// Gates of chunk c from alpha, beta, bw of token `lane` (0 past T; identity
+// tokens there: alpha = 1, beta = bw = 0): an inclusive wave scan of ln alpha.
+struct LaneGates {
+    float gam, dec, bw, bg, gl, gb, el, fl, ebt;
+    bool fast;
+};
+__device__ __forceinline__ LaneGates lane_gates(int c, float pa, float pb, float pw, int T, int lane) {
+    const float x = wave_inclusive_sum(c * C + lane < T ? __logf(pa) : 0.f);
+    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    LaneGates g;
+    g.gl = x * 1.4426950408889634f;  // log2(e)
+    g.gam = __expf(x);
+    g.dec = __expf(last - x);
+    g.bw = pw;
+    g.bg = pb * g.gam;
+    g.gb = g.gl + __builtin_amdgcn_logf(pb);  // log2; -inf where beta = 0
+    const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g.gl), 0));
+    const float g63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g.gl), 63));
+    const float ref = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g.gl), 32));
+    g.fast = g0 - g63 <= kSpan;  // false for NaN or infinite decays
+    g.el = __builtin_amdgcn_exp2f(g.gl - ref);
+    g.fl = __builtin_amdgcn_exp2f(ref - g.gl);
+    g.ebt = pb * g.el;
+    return g;
+}
+
+// One 32x32 score tile of chunk-local tokens, computed transposed:
+// acc[s][t] = sum_key K[s][key] Q[t][key], s = 32J + row, t = 32I + column;
+// lane l32 holds column t = 32I + perm5(l32) and element e row
+// s = 32J + elem_index(0, e, h).  Masked (e^(g_t - g_s) where t >= s, else 0),
+// packed to bf16 and stored into P (physical row 32I + l32).
+__device__ __forceinline__ void score_tile(Smem& sm, const uint16_t* Kb, const Gates& G, int I, int J,
+                                           int l32, int h) {
+    const int qrow = 32 * I + l32, krow = 32 * J + l32;
+    const f32x16 acc = mfma_chain2<8>([&](int k) { return lds8(Kb + kidx(krow, 16 * k + 8 * h)); },
+                                      [&](int k) { return lds8(&sm.Q[qrow * LQ + 16 * k + 8 * h]); },
+                                      f32x16{});
+    const int t = 32 * I + perm5(l32);
+    auto mask = [&](auto weight, const float* ws, float et) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int s0 = 32 * J + elem_index(0, 4 * b, h);
+            const f32x4 gs = *reinterpret_cast<const f32x4*>(&ws[s0]);
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float d = weight(et, gs[i]) * acc[4 * b + i];
+                p[i] = (I > J || t >= s0 + i) ? d : 0.f;
+            }
+            *reinterpret_cast<uint2*>(&sm.P[qrow * LT + s0]) = pack4(p[0], p[1], p[2], p[3]);
+        }
+    };
+    if (__builtin_amdgcn_readfirstlane(G.fast))
+        mask([](float a, float b) { return a * b; }, G.fl, G.el[t]);
+    else
+        mask([](float a, float b) { return __builtin_amdgcn_exp2f(a - b); }, G.gl, G.gl[t]);
+}
+
+// Top (blk 0) or bottom (blk 1) diagonal 32x32 block of T = (I + A)^-1 from
+// the transposed k-Gram tile At[blk]: its two 16x16 diagonal blocks by
+// forward substitution (lane (sb, c) of the first 32 builds column c of
+// block sb; lanes 32..63 repeat them), then T10 = -T11 A10 T00 on the fp32
+// MFMA.  Written to D[blk] (natural) and Dt[blk] (transposed).
+__device__ __forceinline__ void solve_block(Smem& sm, int blk, int lane) {
+    const float* At = sm.At[blk];
+    float* Db = sm.D[blk];
+    const int sb = (lane >> 4) & 1, cc = lane & 15;
+    const float* Ab = At + 16 * sb * LS + 16 * sb;  // Ab[i * LS + r] = A[r][i] within the 16x16 block
+    float x[16], acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    f32x4 row[3][4];  // rows i, i+1, i+2 of Ab in flight (4-entry groups from (i+1)/4 on)
+    auto load_row = [&](int i, f32x4 (&dst)[4]) {
+#pragma unroll
+        for (int q = (i + 1) / 4; q < 4; ++q) dst[q] = *reinterpret_cast<const f32x4*>(&Ab[i * LS + 4 * q]);
+    };
+    load_row(0, row[0]);
+    load_row(1, row[1]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i + 2 < 16) load_row(i + 2, row[(i + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        const float xi = i == cc ? 1.f : -acc[i];
+        x[i] = xi;
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) acc[r] = fmaf(row[i % 3][r >> 2][r & 3], xi, acc[r]);
+    }
+    if (lane < 32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Db[(16 * sb + r) * LS + 16 * sb + cc] = x[r];
+        if (blk == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(&sm.Dt[(16 * sb + cc) * LS + 16 * sb + 4 * q]) =
+                    f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        }
+    }
+    lds_fence();
+    // T10 = -T11 (A10 T00): lane (n16, g4) holds rows 4 g4 .. +3 of column n16
+    const int n16 = lane & 15, g4 = lane >> 4;
+    f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)  // A10[n16][4g4+kk] T00[4g4+kk][n16]
+        y = mfma4(At[(4 * g4 + kk) * LS + 16 + n16], Db[(4 * g4 + kk) * LS + n16], y);
+    const f32x4 at = *reinterpret_cast<const f32x4*>(&Db[(16 + n16) * LS + 16 + 4 * g4]);  // T11[n16][4g4+kk]
+    f32x4 t10 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t10 = mfma4(at[kk], y[kk], t10);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Db[(16 + 4 * g4 + r) * LS + n16] = -t10[r];
+    if (blk == 0) *reinterpret_cast<f32x4*>(&sm.Dt[n16 * LS + 16 + 4 * g4]) = -t10;
+}
+
 // ----------------------------------------------------------------------------
-// state waves (0, 1): chunk n's S-dependent products
+// state waves (0, 1): chunk j's S-dependent products
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
     constexpr bool OUT = ROLE != kLeafAggregate;  // o is read out (not for leaf aggregates)
-    const int tid = threadIdx.x, lane = tid & 63, ib = wave_id();
+    const int lane = threadIdx.x & 63, vb = wave_id();
     const int l32 = lane & 31, h = lane >> 5;
-    const int T = job.T;
-    const int vl = 32 * ib + l32;   // value channel of this lane within the slice
+    // value channel of this lane within the slice, numbered through perm5 so
+    // that the transposed read-out O^T (values as accumulator rows) holds 8
+    // consecutive values per element group
+    const int vl = 32 * vb + perm5(l32);
     const int vcol = un.r0 + vl;    // state row (value channel) of this lane
 
     // sacc[jt] element e = S[vcol][elem_index(jt, e, h)]
@@ -456,105 +496,111 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                 }
             }
     }
-
-    // sbf[kk]: the state rounded to bf16 as B operands (contraction step kk);
-    // qacc[tt] = Q S^T of the chunk the next iteration reads out (old state)
+    // sbf[kk]: the state rounded to bf16 as B operands (contraction step kk)
     bf16x8 sbf[8];
     auto round_state = [&]() {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) sbf[kk] = sop(sacc, kk);
     };
-    f32x16 qacc[2];
-    auto q_state = [&](int c) {
-        const uint16_t* Q = sm.Q[c & 1];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const uint16_t* qr = &Q[(32 * tt + l32) * LW + 8 * h];
-            qacc[tt] = mfma_chain<8>([&](int k) { return lds8(qr + 16 * k); },
-                                     [&](int k) { return sbf[k]; }, f32x16{});
-        }
-    };
     round_state();
 
-    lds_barrier();  // prologue: chunk nb staged
-    for (int it = un.nb - 1; it < un.ne; ++it) {
-        const bool act = it >= un.nb;
-        const int n = it;
-        const Gates& G = sm.gate[(n + 3) % 3];
-        f32x16 uacc[2];
-        // ---- phase A: U = T diag(beta) V - W S^T ----
+    f32x16 qacc[2], xacc[2];
+    for (int j = un.nb - 2; j < un.ne; ++j) {
+        const bool act = j >= un.nb;
+        const uint16_t* Kb = sm.K[j & 1];
+        // ---- first half: X = K S^T and O^T = S Q^T, four independent chains ----
         if (act) {
+            // operands of contraction step k (keys 16k + 8h ..): k rows and q rows of
+            // token tiles 0 and 1, loaded two steps ahead
+            auto ka = [&](int k, int tt) { return lds8(Kb + kidx(32 * tt + l32, 16 * k + 8 * h)); };
+            auto qb = [&](int k, int tt) { return lds8(&sm.Q[(32 * tt + l32) * LQ + 16 * k + 8 * h]); };
+            bf16x8 kr[3][2], qr[3][2];
+            auto fetch = [&](int k) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    if (GDN) kr[k % 3][tt] = ka(k, tt);
+                    if (OUT) qr[k % 3][tt] = qb(k, tt);
+                }
+            };
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                if (GDN) {
-                    // T diag(beta) V operands read first (T is lower triangular:
-                    // tile 0 contracts over tokens 0..31 only); they arrive while
-                    // the W S^T chain runs
-                    const uint16_t* tr = &sm.Tb[(32 * tt + l32) * LT + 8 * h];
-                    bf16x8 ta[4], va[4];
-                    const int nk = un.erows ? 0 : tt == 0 ? 2 : 4;  // rows of E: v = 0
+                xacc[tt] = f32x16{};
+                qacc[tt] = f32x16{};
+            }
+            fetch(0);
+            fetch(1);
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        if (kk >= nk) continue;
-                        ta[kk] = lds8(tr + 16 * kk);
-                        va[kk] = lds8(&sm.VT[tsw(vl, 16 * kk + 8 * h)]);
-                    }
-                    const uint16_t* wr = &sm.W[(32 * tt + l32) * LW + 8 * h];
-                    f32x16 acc = mfma_chain<8>([&](int k) { return lds8(wr + 16 * k); },
-                                               [&](int k) { return sbf[k]; }, f32x16{});
+            for (int k = 0; k < 8; ++k) {
+                if (k + 2 < 8) fetch(k + 2);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        if (kk >= nk) continue;
-                        acc = mfma32(ta[kk], va[kk], acc);
-                    }
-                    uacc[tt] = acc;
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const bf16x8 v8 = lds8(&sm.VT[tsw(vl, 32 * tt + 16 * s + 8 * h)]);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) uacc[tt][8 * s + i] = static_cast<float>(v8[i]);
-                    }
+                for (int tt = 0; tt < 2; ++tt) {
+                    if (GDN) xacc[tt] = mfma32(kr[k % 3][tt], sbf[k], xacc[tt]);
+                    if (OUT) qacc[tt] = mfma32(sbf[k], qr[k % 3][tt], qacc[tt]);
                 }
             }
         }
-        lds_barrier();  // A
-        // ---- phase B: O = diag(gamma) Q S^T + P U, written out; S^T <- gamma_C S^T + K^T diag(dec) U ----
-        if (OUT && act) {
+        lds_barrier();
+        // ---- second half: U, O (staged for the load waves), the state update ----
+        if (act) {
+            const Gates& G = sm.gate[j % 3];
+            const uint16_t* Vb = sm.V[j & 1];
+            // independent of U (free to overlap its products): gamma_C S^T, and the
+            // gamma scaling of the read-out (column l32 of tile tt is token
+            // t = 32 tt + perm5(l32): one gate per lane)
+            const float gC = G.gam[C - 1];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x16 acc = qacc[tt];
+            for (int jt = 0; jt < 4; ++jt) sacc[jt] *= gC;
+            f32x16 oacc[2];
+            if (OUT) {
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const f32x4 g0 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h]);
-                    const f32x4 g1 = *reinterpret_cast<const f32x4*>(&G.gam[32 * tt + 16 * b + 8 * h + 4]);
+                for (int tt = 0; tt < 2; ++tt) oacc[tt] = qacc[tt] * G.gam[32 * tt + perm5(l32)];
+            }
+            f32x16 uacc[2];
+            if (GDN) {
+                // U = Tb V + Tbn X; T is lower triangular: token tile 0 contracts over
+                // tokens 0..31 only
+                uacc[0] = f32x16{};
+                uacc[1] = f32x16{};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[8 * b + i] *= g0[i];
-                        acc[8 * b + 4 + i] *= g1[i];
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x8 xo = sop(xacc, kk);
+                    if (!un.erows) {  // rows of E: v = 0
+                        const bf16x8 vo = v_operand(Vb, kk, 32 * vb, lane);
+                        uacc[1] = mfma32(lds8(&sm.Tb[(32 + l32) * LT + 16 * kk + 8 * h]), vo, uacc[1]);
+                        if (kk < 2) uacc[0] = mfma32(lds8(&sm.Tb[l32 * LT + 16 * kk + 8 * h]), vo, uacc[0]);
                     }
+                    uacc[1] = mfma32(lds8(&sm.Tbn[(32 + l32) * LT + 16 * kk + 8 * h]), xo, uacc[1]);
+                    if (kk < 2) uacc[0] = mfma32(lds8(&sm.Tbn[l32 * LT + 16 * kk + 8 * h]), xo, uacc[0]);
                 }
-                const uint16_t* pr = &sm.P[(32 * tt + l32) * LT + 8 * h];
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const bf16x8 v8 = v_operand(Vb, 2 * tt + s2, 32 * vb, lane);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) uacc[tt][8 * s2 + i] = static_cast<float>(v8[i]);
+                    }
+            }
+            if (OUT) {
+                // O^T = S Q^T diag(gamma) + U^T P^T
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    if (tt == 0 && ks >= 2) continue;  // P is lower triangular
-                    acc = mfma32(lds8(pr + 16 * ks), sop(uacc, ks), acc);
+                    const bf16x8 uo = sop(uacc, ks);
+                    oacc[1] = mfma32(uo, lds8(&sm.P[(32 + l32) * LT + 16 * ks + 8 * h]), oacc[1]);
+                    if (ks < 2) oacc[0] = mfma32(uo, lds8(&sm.P[l32 * LT + 16 * ks + 8 * h]), oacc[0]);
                 }
-                if (job.o) {
-                    // rows past T fall outside the resource and are dropped
-                    const int valid = __builtin_amdgcn_readfirstlane(min(T - n * C, C));
-                    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                        job.o + ((size_t)un.head * T + (size_t)n * C) * DV + un.r0, (short)0,
-                        valid * DV * 2 - un.r0 * 2, 0x00020000);
-                    const int voff = (8 * h * DV + vl) * 2;
+                // element e holds value 32 vb + elem_index(0, e, h): elements 8s .. 8s+7 are
+                // 8 consecutive values, one 16-byte LDS write each
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), orsrc, voff,
-                                                              (elem_index(tt, e, 0)) * DV * 2, 0);
+                for (int tt = 0; tt < 2; ++tt) {
+                    uint16_t* orow = &sm.Ost[(32 * tt + perm5(l32)) * LO + 32 * vb + 8 * h];
+                    *reinterpret_cast<bf16x8*>(orow) = half8<0>(oacc[tt]);
+                    *reinterpret_cast<bf16x8*>(orow + 16) = half8<8>(oacc[tt]);
                 }
             }
-        }
-        if (act) {
+            // S^T <- gamma_C S^T + K^T diag(dec) U
             bf16x8 db[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -570,20 +616,21 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                 }
                 db[ks] = __builtin_convertvector(x, bf16x8);
             }
-            const float gC = G.gam[C - 1];
-            const uint16_t* KT = sm.KT[n & 1];
+            bf16x8 ko[2][4];
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const int prow = 32 * jt + l32;
-                sacc[jt] = mfma_chain<4>([&](int k) { return lds8(&KT[tsw(prow, 16 * k + 8 * h)]); },
-                                         [&](int k) { return db[k]; }, sacc[jt] * gC);
+            for (int jt = 0; jt < 4; ++jt) ko[0][jt] = kt_operand(Kb, 0, jt, lane);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (k + 1 < 4) {
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt) ko[(k + 1) & 1][jt] = kt_operand(Kb, k + 1, jt, lane);
+                }
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) sacc[jt] = mfma32(ko[k & 1][jt], db[k], sacc[jt]);
             }
             round_state();
         }
-        lds_barrier();  // B
-        // ---- phase C: Q S^T of chunk n+1 with the state entering it ----
-        if (OUT && n + 1 < un.ne) q_state(n + 1);
-        lds_barrier();  // C
+        lds_barrier();
     }
 
     float* dst = nullptr;
@@ -608,176 +655,15 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 }
 
 // ----------------------------------------------------------------------------
-// k-Gram / UT solve / W waves (2, 3, 6, 7 -> gi 0..3): chunk n+1
+// load waves (4, 5): stage chunk j+1 and load chunk j+2; Tb, Tbn of T's
+// diagonal block w - 4 of chunk j
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
-__device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
+__device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
-    constexpr bool OUT = ROLE != kLeafAggregate;  // scores needed only where o is read out
-    const int lane = threadIdx.x & 63, w = wave_id();
-    const int gi = w == 2 ? 0 : w == 3 ? 1 : w == 6 ? 2 : 3;
-    const int l32 = lane & 31, h = lane >> 5;
-    const Solve sv{lane & 15, lane >> 4};
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    uint2 preg[4];  // gi 3: chunk m's score tile (1, 0), stored in phase C
-    // gi 0: alpha, beta of chunk m+1's token `lane` (0 past T); its gates
-    const int T = job.T;
-    const size_t a_base = (size_t)un.head * T;
-    float pa = 1.f, pb = 0.f, pw = 0.f;
-    const bool split = job.beta_w != job.beta;  // separate write strengths
-    auto load_ab = [&](int c) {
-        pa = ldtok(job.alpha + a_base, c, lane, T);
-        if (GDN) {
-            pb = ldtok(job.beta + a_base, c, lane, T);
-            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
-        }
-    };
-    if (gi == 0 && un.nb < un.ne) {
-        load_ab(un.nb);
-        stage_gates(sm.gate[un.nb % 3], un.nb, pa, pb, split ? pw : pb, T, lane);
-    }
-
-    lds_barrier();  // prologue
-    for (int it = un.nb - 1; it < un.ne; ++it) {
-        const int m = it + 1;
-        const bool act = m < un.ne;
-        const Gates& G = sm.gate[m % 3];
-        // ---- phase A: diagonal 32x32 blocks of T in-wave (the first chunk also builds its k-Gram tiles) ----
-        if (gi == 0 && m + 1 < un.ne) load_ab(m + 1);
-        if (act) {
-            if (GDN && gi <= 1) {
-                float* X = sm.Tm[gi];
-                // later chunks' diagonal tiles come from the load waves (phase C)
-                if (m == un.nb) a_tile(sm, G, gi, gi, X, l32, h);
-                diag_inverse2(X, lane);
-                // T_10 = -D_1 A_10 D_0 within the 32x32 block
-                const f32x4 mm = sv.mul_lds(X + 16 * LS, X, z);
-                sv.put(X + 16 * LS, sv.mul_acc(X + 16 * LS + 16, mm, z), -1.f);
-            } else if (GDN && gi == 2) {
-                // later chunks' tile is built in the previous phase C
-                if (m == un.nb) a_tile(sm, G, 1, 0, sm.Abl, l32, h);
-            } else if (OUT && gi == 3) {
-                score_tile(sm, m & 1, G, 1, 0, l32, h, preg);
-            }
-        }
-        lds_barrier();  // A
-        // ---- phase B: off-diagonal 32x32 block of T; bf16 Tb = T diag(bw), Tbg = T diag(beta gamma) ----
-        if (GDN && act) {
-            if (gi <= 1) {
-                // rows 32gi + tl of the diagonal block, 16 columns from c0
-                const float* X = sm.Tm[gi];
-                const int tl = lane >> 1, c0 = 16 * (lane & 1);
-                const int prow = 32 * gi + perm5(tl);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    uint32_t b[4], bg[4];
-                    const int s0 = 32 * gi + c0 + 8 * hh;
-                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&X[tl * LS + c0 + 8 * hh]);
-                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&X[tl * LS + c0 + 8 * hh + 4]);
-                    const f32x4 be0 = *reinterpret_cast<const f32x4*>(&G.bet[s0]);
-                    const f32x4 be1 = *reinterpret_cast<const f32x4*>(&G.bet[s0 + 4]);
-                    const f32x4 bw0 = *reinterpret_cast<const f32x4*>(&G.bw[s0]);
-                    const f32x4 bw1 = *reinterpret_cast<const f32x4*>(&G.bw[s0 + 4]);
-                    const f32x4 ga0 = *reinterpret_cast<const f32x4*>(&G.gam[s0]);
-                    const f32x4 ga1 = *reinterpret_cast<const f32x4*>(&G.gam[s0 + 4]);
-                    float tv[8], bv[8], wv[8], gv[8];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        tv[i] = x0[i]; tv[4 + i] = x1[i];
-                        bv[i] = be0[i]; bv[4 + i] = be1[i];
-                        wv[i] = bw0[i]; wv[4 + i] = bw1[i];
-                        gv[i] = ga0[i]; gv[4 + i] = ga1[i];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int sa = c0 + 8 * hh + 2 * i;  // local column of element 2i
-                        const float t0 = sa <= tl ? tv[2 * i] : 0.f;
-                        const float t1 = sa + 1 <= tl ? tv[2 * i + 1] : 0.f;
-                        b[i] = pack2(t0 * wv[2 * i], t1 * wv[2 * i + 1]);
-                        bg[i] = pack2(t0 * bv[2 * i] * gv[2 * i], t1 * bv[2 * i + 1] * gv[2 * i + 1]);
-                    }
-                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + s0]) = make_uint4(b[0], b[1], b[2], b[3]);
-                    *reinterpret_cast<uint4*>(&sm.Tbg[prow * LT + s0]) = make_uint4(bg[0], bg[1], bg[2], bg[3]);
-                }
-            } else {
-                // columns 16J .. 16J+15 of T rows 32..63:
-                //   Y_iJ = sum_K A_bl(i, K) T_0(K, J),  T_bl(i, J) = -sum_K T_1(i, K) Y_KJ
-                const int J = gi - 2;
-                const float* T0 = sm.Tm[0];
-                const float* T1 = sm.Tm[1];
-                f32x4 y0, y1;
-                if (J == 0) {
-                    y0 = sv.mul_lds(sm.Abl + 16, T0 + 16 * LS, sv.mul_lds(sm.Abl, T0, z));
-                    y1 = sv.mul_lds(sm.Abl + 16 * LS + 16, T0 + 16 * LS, sv.mul_lds(sm.Abl + 16 * LS, T0, z));
-                } else {
-                    y0 = sv.mul_lds(sm.Abl + 16, T0 + 16 * LS + 16, z);
-                    y1 = sv.mul_lds(sm.Abl + 16 * LS + 16, T0 + 16 * LS + 16, z);
-                }
-                const f32x4 t0 = sv.mul_acc(T1, y0, z);
-                const f32x4 t1 = sv.mul_acc(T1 + 16 * LS + 16, y1, sv.mul_acc(T1 + 16 * LS, y0, z));
-                const int s = 16 * J + sv.n16;
-                const float bs = G.bw[s], bgs = G.bet[s] * G.gam[s];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p0 = 32 + perm5(4 * sv.g4 + r), p1 = 32 + perm5(16 + 4 * sv.g4 + r);
-                    sm.Tb[p0 * LT + s] = f32_to_bf16(-t0[r] * bs);
-                    sm.Tbg[p0 * LT + s] = f32_to_bf16(-t0[r] * bgs);
-                    sm.Tb[p1 * LT + s] = f32_to_bf16(-t1[r] * bs);
-                    sm.Tbg[p1 * LT + s] = f32_to_bf16(-t1[r] * bgs);
-                }
-            }
-        }
-        // chunk m+1's gates: the load waves mask its k-Gram tiles in phase C
-        if (gi == 0 && m + 1 < un.ne)
-            stage_gates(sm.gate[(m + 1) % 3], m + 1, pa, pb, split ? pw : pb, T, lane);
-        lds_barrier();  // B
-        // ---- phase C: W = T diag(beta gamma) K (stored -W): key tile gi, and tile 2 on
-        // gi 1; gi 2 builds chunk m+1's off-diagonal k-Gram tile; scores ----
-        auto w_tile = [&](int jt) {
-            const uint16_t* KT = sm.KT[m & 1];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const uint16_t* tr = &sm.Tbg[(32 * tt + l32) * LT + 8 * h];
-                auto lk = [&](int k) { return lds8(&KT[tsw(32 * jt + l32, 16 * k + 8 * h)]); };
-                auto lt = [&](int k) { return lds8(tr + 16 * k); };
-                // T is lower triangular: token tile 0 needs columns 0..31 only
-                const f32x16 acc = tt == 0 ? mfma_chain2<2>(lk, lt, f32x16{}) : mfma_chain2<4>(lk, lt, f32x16{});
-                uint16_t* wrow = &sm.W[(32 * tt + l32) * LW + 32 * jt];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    *reinterpret_cast<uint2*>(wrow + elem_index(0, 4 * b, h)) =
-                        pack4(-acc[4 * b], -acc[4 * b + 1], -acc[4 * b + 2], -acc[4 * b + 3]);
-            }
-        };
-        if (act) {
-            if (GDN) {
-                if (gi != 2) w_tile(gi);
-                if (gi == 1) w_tile(2);
-                if (gi == 2 && m + 1 < un.ne) a_tile(sm, sm.gate[(m + 1) % 3], 1, 0, sm.Abl, l32, h);
-            }
-            if (OUT && gi == 3) store_score_tile(sm, 1, 0, l32, h, preg);
-        }
-        lds_barrier();  // C
-    }
-}
-
-// ----------------------------------------------------------------------------
-// load / transpose waves (4, 5): stage chunk n+2 and its diagonal k-Gram
-// tiles; score tiles (0,0), (1,1) of n+1
-// ----------------------------------------------------------------------------
-template <int MODE, int ROLE>
-__device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Unit& un) {
-    constexpr bool GDN = MODE == 0;
-    constexpr bool OUT = ROLE != kLeafAggregate;  // q and scores needed only where o is read out
-    // The roles share one control-flow graph, so the compiler's wait-count
-    // analysis can take another role's loads as still in flight here and wait
-    // for every load at each reuse of their registers inside the loop below.
-    // An explicit vmcnt(0) (free: this wave has issued no load yet) clears that.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int ti = w - 4;     // score tile (ti, ti)
+    constexpr bool OUT = ROLE != kLeafAggregate;  // q needed only where o is read out
+    const int tid = threadIdx.x, lane = tid & 63, blk = wave_id() - 4;
     const int x = tid - 256;  // 0..127
-    const int l32 = lane & 31, h = lane >> 5;
     const int T = job.T;
     const size_t qk_base = (size_t)un.head * T * DK;
     const size_t v_base = (size_t)un.head * T * DV + un.r0;
@@ -785,97 +671,267 @@ __device__ __forceinline__ void tp_role(Smem& sm, const ChunkJob& job, const Uni
     // v: values 8vc..8vc+7 of tokens 4vt + i, i < 4
     const int jc = x & 15, tg = x >> 4;
     const int vc = x & 7, vt = x >> 3;
-    uint4 qr[8], kc[8], kn[8], vcur[4], vnx[4];
-    auto load = [&](int c, uint4 (&kk)[8], uint4 (&vv)[4]) {
+    uint4 qr[8], kr[8], vr[4];
+    auto load = [&](int c) {
         const Rows rq(job.q + qk_base, c, T, DK), rk(job.k + qk_base, c, T, DK), rv(job.v + v_base, c, T, DV);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 32 * (i >> 2) + 4 * tg + (i & 3);
-            kk[i] = rk.at(row, 8 * jc);
+            kr[i] = rk.at(row, 8 * jc);
             if (OUT) qr[i] = rq.at(row, 8 * jc);
         }
-        if (un.erows) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vv[i] = make_uint4(0, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vv[i] = rv.at(4 * vt + i, 8 * vc);
-        }
+        for (int i = 0; i < 4; ++i) vr[i] = rv.at(4 * vt + i, 8 * vc);
     };
-    // k, q rows of chunk c (from kk, qr) and its gates into LDS
-    auto stage = [&](int c, const uint4 (&kk)[8]) {
+    auto stage = [&](int c) {
+        uint16_t* Kb = sm.K[c & 1];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int prow = perm5(32 * (i >> 2) + 4 * tg + (i & 3));
-            *reinterpret_cast<uint4*>(&sm.K[prow * LW + 8 * jc]) = kk[i];
-            if (OUT) *reinterpret_cast<uint4*>(&sm.Q[c & 1][prow * LW + 8 * jc]) = qr[i];
+            *reinterpret_cast<uint4*>(Kb + kidx(prow, 8 * jc)) = kr[i];
+            if (OUT) *reinterpret_cast<uint4*>(&sm.Q[prow * LQ + 8 * jc]) = qr[i];
+        }
+        uint16_t* Vb = sm.V[c & 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Vb[(4 * vt + i) * LV + 8 * vc]) = vr[i];
+    };
+    // o of chunk c from the staged tile: 64 rows of 64 values (128 bytes), 8
+    // rows of 8 16-byte pieces per store instruction; rows past T fall outside
+    // the resource and are dropped
+    auto store_o = [&](int c) {
+        if (!job.o) return;
+        const int valid = __builtin_amdgcn_readfirstlane(min(T - c * C, C));
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            job.o + ((size_t)un.head * T + (size_t)c * C) * DV + un.r0, (short)0,
+            valid * DV * 2 - un.r0 * 2, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = x + 128 * i, row = g >> 3, col = 8 * (g & 7);
+            const uint4 w = *reinterpret_cast<const uint4*>(&sm.Ost[row * LO + col]);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), orsrc,
+                (row * DV + col) * 2, 0, 0);
         }
     };
-    // k^T of chunk c (from kk) into KT[c % 2]: keys 8jc + e, tokens 32half + 4tg .. +3
-    auto stage_kt = [&](int c, const uint4 (&kk)[8]) {
-        uint16_t* KT = sm.KT[c & 1];
+    // Tb = T diag(bw), Tbn = -T diag(beta gamma) over T's diagonal block blk:
+    // lane (t, hh) converts row t, columns 16 hh .. 16 hh + 15 of the block
+    auto convert = [&](int c) {
+        const Gates& G = sm.gate[c % 3];
+        const int t = lane & 31, hh = lane >> 5;
+        const float* dr = sm.D[blk] + t * LS + 16 * hh;
+        const int prow = 32 * blk + perm5(t);
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int wi = e >> 1;
-                const uint4* k4 = &kk[4 * half];
-                uint2 u;
-                u.x = (e & 1) ? hi16x2(word(k4[0], wi), word(k4[1], wi)) : lo16x2(word(k4[0], wi), word(k4[1], wi));
-                u.y = (e & 1) ? hi16x2(word(k4[2], wi), word(k4[3], wi)) : lo16x2(word(k4[2], wi), word(k4[3], wi));
-                *reinterpret_cast<uint2*>(&KT[tsw(perm5(8 * jc + e), 32 * half + 4 * tg)]) = u;
-            }
-    };
-    // v^T of the chunk (from vv) into VT: values 8vc + e, tokens 4vt .. 4vt+3
-    auto stage_vt = [&](const uint4 (&vv)[4]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int wi = e >> 1;
-            uint2 u;
-            u.x = (e & 1) ? hi16x2(word(vv[0], wi), word(vv[1], wi)) : lo16x2(word(vv[0], wi), word(vv[1], wi));
-            u.y = (e & 1) ? hi16x2(word(vv[2], wi), word(vv[3], wi)) : lo16x2(word(vv[2], wi), word(vv[3], wi));
-            *reinterpret_cast<uint2*>(&sm.VT[tsw(8 * vc + e, 4 * vt)]) = u;
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const int s0 = 32 * blk + 16 * hh + 8 * q2;
+            const f32x8 d = ld8f(dr + 8 * q2), w = ld8f(&G.bw[s0]), g = ld8f(&G.bg[s0]);
+            *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + s0]) = pack8(d * w);
+            *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + s0]) = pack8(-(d * g));
         }
+    };
+    for (int j = un.nb - 2; j < un.ne; ++j) {
+        if (OUT && j - 1 >= un.nb) store_o(j - 1);
+        if (GDN && j >= un.nb) convert(j);
+        lds_barrier();
+        if (j + 1 >= un.nb && j + 1 < un.ne) stage(j + 1);
+        // the next chunk's rows overwrite the registers just staged: keep the
+        // loads after the LDS writes (hoisted above them they would need a
+        // second register set)
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 2 < un.ne) load(j + 2);
+        lds_barrier();
+    }
+    if (OUT && un.ne - 1 >= un.nb) store_o(un.ne - 1);
+}
+
+// ----------------------------------------------------------------------------
+// k-Gram waves (2, 3): chunk j+1's k-Gram tiles; wave 3 also chunk j's score
+// tile (0,0), wave 2 the gates of chunk j+2
+// ----------------------------------------------------------------------------
+template <int MODE, int ROLE>
+__device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
+    constexpr bool GDN = MODE == 0;
+    constexpr bool OUT = ROLE != kLeafAggregate;
+    const int lane = threadIdx.x & 63, blk = wave_id() - 2;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int T = job.T;
+    const size_t qk_base = (size_t)un.head * T * DK;
+    // wave 2: alpha, beta, bw of token `lane` of the chunk whose gates come next
+    const size_t a_base = (size_t)un.head * T;
+    const bool split = job.beta_w != job.beta;  // separate write strengths
+    float pa = 1.f, pb = 0.f, pw = 0.f;
+    auto load_ab = [&](int c) {
+        pa = ldtok(job.alpha + a_base, c, lane, T);
+        if (GDN) {
+            pb = ldtok(job.beta + a_base, c, lane, T);
+            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
+        }
+    };
+    if (blk == 0 && un.nb < un.ne) load_ab(un.nb);
+    // chunk c's k rows as MFMA operands, kreg[b][kk] = k[32b + l32][16kk + 8h .. +7],
+    // loaded a chunk ahead of their use
+    bf16x8 kreg[1][2][8];
+    auto load = [&](int c) {
+        constexpr int st = 0;
+        const Rows rk(job.k + qk_base, c, T, DK);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                kreg[st][b][kk] = __builtin_bit_cast(bf16x8, rk.at(32 * b + l32, 16 * kk + 8 * h));
     };
 
-    // prologue: chunk nb's k, q, gates in LDS; its k, v kept for k^T / v^T
-    if (un.nb < un.ne) {
-        load(un.nb, kc, vcur);
-        stage(un.nb, kc);
-    }
-    lds_barrier();  // prologue
-    uint2 preg[4];
-    // one chunk step; kc/vcur hold chunk m's k and v, kn/vnx receive chunk m+1's
-    auto step = [&](int it, uint4 (&kcur)[8], uint4 (&knext)[8], uint4 (&vcu)[4], uint4 (&vne)[4]) {
-        const int m = it + 1;
-        const bool act = m < un.ne;
-        const bool nxt = m + 1 < un.ne;
-        const Gates& G = sm.gate[m % 3];
-        // Every load of this wave is a chunk old here; stating so keeps the
-        // compiler from waiting on the loads issued just below (its analysis
-        // loses track of the older ones across the conditional steps).
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        // ---- phase A: chunk m+1 in flight; k^T of chunk m; score tile (ti, ti) of m ----
-        if (act) {
-            if (nxt) load(m + 1, knext, vne);
-            stage_kt(m, kcur);
-            if (OUT) score_tile(sm, m & 1, G, ti, ti, l32, h, preg);
-        }
-        lds_barrier();  // A
-        // ---- phase B: v^T of chunk m; k, q of chunk m+1 ----
-        if (act) stage_vt(vcu);
-        if (nxt) stage(m + 1, knext);
-        lds_barrier();  // B
-        // ---- phase C: scores of m; diagonal k-Gram tile (ti, ti) of chunk m+1 ----
-        if (act && OUT) store_score_tile(sm, ti, ti, l32, h, preg);
-        if (GDN && nxt) a_tile(sm, sm.gate[(m + 1) % 3], ti, ti, sm.Tm[ti], l32, h);
-        lds_barrier();  // C
+    // k-Gram tile (I, J) masked into A, stored transposed: lane l32 holds
+    // column s = 32J + l32, element e row t = 32I + 8(e>>2) + 4h + (e&3);
+    // A_ts = exp2(gb_t - gl_s) (k_t . k_s) for t > s
+    // (fast chunks: the weight is wt_t ws_s with ws = fl, wt = ebt; else
+    // exp2(wt_t - ws_s) with ws = gl, wt = gb; w_s and w_t[b] = wt[32I + 8b + 4h ..]
+    // are read before the products)
+    auto gram_mask = [&](const f32x16& acc, int I, int J, bool fast, float w_s, const f32x4 (&w_t)[4],
+                         float* dst) {
+        const int s = 32 * J + l32;
+        auto mask = [&](auto weight) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int t0 = 32 * I + 8 * b + 4 * h;
+                f32x4 a;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d = weight(w_t[b][i], w_s) * acc[4 * b + i];
+                    a[i] = (I > J || t0 + i > s) ? d : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(&dst[l32 * LS + 8 * b + 4 * h]) = a;
+            }
+        };
+        if (fast)
+            mask([](float a, float b) { return a * b; });
+        else
+            mask([](float a, float b) { return __builtin_amdgcn_exp2f(a - b); });
     };
-    // two steps per trip so that the current / next register sets alternate
-    // without copies
-    for (int it = un.nb - 1; it < un.ne; it += 2) {
-        step(it, kc, kn, vcur, vnx);
-        if (it + 1 < un.ne) step(it + 1, kn, kc, vnx, vcur);
+
+    for (int j = un.nb - 2; j < un.ne; ++j) {
+        constexpr int st = 0;
+        const int c = j + 1;  // chunk whose gates, k-Gram and diagonal T blocks are built
+        // ---- first half ----
+        if (GDN && c >= un.nb && c < un.ne) {
+            const Gates& G = sm.gate[c % 3];
+            const bool fast = __builtin_amdgcn_readfirstlane(G.fast);
+            const float* ws = fast ? G.fl : G.gl;
+            const float* wt = fast ? G.ebt : G.gb;
+            f32x4 wt1[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
+            const float ws0 = ws[l32];
+            if (blk == 0) {
+                f32x4 wt0[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) wt0[b] = *reinterpret_cast<const f32x4*>(&wt[8 * b + 4 * h]);
+                const float ws1 = ws[32 + l32];
+                f32x16 a0 = f32x16{}, a1 = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    a0 = mfma32(kreg[st][0][kk], kreg[st][0][kk], a0);
+                    a1 = mfma32(kreg[st][1][kk], kreg[st][1][kk], a1);
+                }
+                gram_mask(a0, 0, 0, fast, ws0, wt0, sm.At[0]);
+                gram_mask(a1, 1, 1, fast, ws1, wt1, sm.At[1]);
+            } else {
+                f32x16 a = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
+                gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
+            }
+        }
+        if (OUT && blk == 1 && j >= un.nb) score_tile(sm, sm.K[j & 1], sm.gate[j % 3], 0, 0, l32, h);
+        // chunk c + 1 goes into the registers just used: keep the loads after
+        // their last use (hoisted above it they would need a second set)
+        __builtin_amdgcn_sched_barrier(0);
+        if (GDN && c + 1 < un.ne) load(c + 1);
+        lds_barrier();
+        // ---- second half: wave 2 forms the gates of chunk j + 2 (slot (j+2) % 3;
+        // slots j % 3 and (j+1) % 3 are in use) and loads the next chunk's ----
+        const int c2 = j + 2;
+        if (blk == 0 && c2 < un.ne) {
+            const LaneGates g = lane_gates(c2, pa, pb, split ? pw : pb, T, lane);
+            Gates& G = sm.gate[c2 % 3];
+            G.gam[lane] = g.gam;
+            G.dec[lane] = g.dec;
+            G.bw[lane] = g.bw;
+            G.bg[lane] = g.bg;
+            G.gl[lane] = g.gl;
+            G.gb[lane] = g.gb;
+            G.el[lane] = g.el;
+            G.fl[lane] = g.fl;
+            G.ebt[lane] = g.ebt;
+            if (lane == 0) G.fast = g.fast;
+            if (c2 + 1 < un.ne) load_ab(c2 + 1);
+        }
+        lds_barrier();
+    }
+}
+
+// ----------------------------------------------------------------------------
+// wave 6: T's off-diagonal block of chunk j; wave 7: chunk j's score tiles
+// (1,0) and (1,1); then the diagonal blocks of chunk j+1's T
+// ----------------------------------------------------------------------------
+template <int MODE, int ROLE>
+__device__ __forceinline__ void aux_role(Smem& sm, const ChunkJob& job, const Unit& un) {
+    constexpr bool GDN = MODE == 0;
+    constexpr bool OUT = ROLE != kLeafAggregate;
+    (void)job;
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int l32 = lane & 31, h = lane >> 5;
+    if (w == 6) {
+        // the block of D above its diagonal (16x16, rows 0..15 x columns 16..31)
+        // and its transpose are zero for every chunk
+        for (int i = lane; i < 2 * 256; i += 64) {
+            const int b = i >> 8, r = (i >> 4) & 15, cc = i & 15;
+            sm.D[b][r * LS + 16 + cc] = 0.f;
+            if (b == 0) sm.Dt[(16 + r) * LS + cc] = 0.f;
+        }
+    }
+    for (int j = un.nb - 2; j < un.ne; ++j) {
+        if (j >= un.nb) {
+            const Gates& G = sm.gate[j % 3];
+            if (GDN && w == 6) {
+                // T_bl = -D_bot A_bl D_top (rows 32 + i, columns jj), as
+                // T_bl^T = -D_top^T Z with Z = A_bl^T D_bot^T, split bf16
+                const float* Ab = sm.Ablt[j & 1];
+                const float* Db = sm.D[1];
+                const float* Dtt = sm.Dt;
+                const int pr = perm5(l32);
+                f32x16 z = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    z = mfma_split(ld8f(&Ab[pr * LS + 16 * kk + 8 * h]), ld8f(&Db[l32 * LS + 16 * kk + 8 * h]), z);
+                f32x16 tacc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const f32x8 zb = kk ? __builtin_shufflevector(z, z, 8, 9, 10, 11, 12, 13, 14, 15)
+                                        : __builtin_shufflevector(z, z, 0, 1, 2, 3, 4, 5, 6, 7);
+                    tacc = mfma_split(ld8f(&Dtt[pr * LS + 16 * kk + 8 * h]), zb, tacc);
+                }
+                // lane l32: row 32 + l32 of T (physical row 32 + perm5(l32)); elements
+                // 8s2 .. 8s2+7: columns 16 s2 + 8 h .. +7 of -T_bl
+                const int prow = 32 + perm5(l32);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int c0 = 16 * s2 + 8 * h;
+                    const f32x8 tn = s2 ? __builtin_shufflevector(tacc, tacc, 8, 9, 10, 11, 12, 13, 14, 15)
+                                        : __builtin_shufflevector(tacc, tacc, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const f32x8 wv = ld8f(&G.bw[c0]), gv = ld8f(&G.bg[c0]);
+                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + c0]) = pack8(-(tn * wv));
+                    *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + c0]) = pack8(tn * gv);
+                }
+            }
+            if (OUT && w == 7) {
+                score_tile(sm, sm.K[j & 1], G, 1, 0, l32, h);
+                score_tile(sm, sm.K[j & 1], G, 1, 1, l32, h);
+            }
+        }
+        lds_barrier();
+        // ---- second half: diagonal block w - 6 of chunk j+1's T ----
+        if (GDN && j + 1 >= un.nb && j + 1 < un.ne) solve_block(sm, w - 6, lane);
+        lds_barrier();
     }
 }
 
@@ -886,10 +942,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_mfma_kernel(const ChunkJob job) {
     const int w = wave_id();
     if (w < 2)
         state_role<MODE, ROLE>(sm, job, un);
-    else if (w == 4 || w == 5)
-        tp_role<MODE, ROLE>(sm, job, un);
-    else
+    else if (w == 2 || w == 3)
         gram_role<MODE, ROLE>(sm, job, un);
+    else if (w == 4 || w == 5)
+        load_role<MODE, ROLE>(sm, job, un);
+    else
+        aux_role<MODE, ROLE>(sm, job, un);
 }
 
 }  // namespace
