@@ -96,18 +96,25 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Gates of one chunk: gamma = e^g, dec = e^(g_C - g), bw (write strength),
 // bg = beta gamma; gl = g log2(e) and gb = gl + log2(beta) feed the masks as
 // exp2(gl_t - gl_s) = Gamma_ts and exp2(gb_t - gl_s) = beta_t Gamma_ts.  When
-// the chunk's log2 decay spans at most kSpan (`fast`), the masks use the
-// factored form Gamma_ts = el_t fl_s with el = exp2(gl - gl_32) and
-// fl = exp2(gl_32 - gl) (every factor within 2^+-kSpan, no overflow), and
-// ebt = beta el: two multiplies per element instead of an exponential.
+// the chunk's log2 decay spans at most kSpan (`fast`, every factor below stays
+// within 2^+-kSpan):
+//  - the k-Gram mask uses the factored form beta_t Gamma_ts = ebt_t fl_s with
+//    el = exp2(gl - gl_32), fl = exp2(gl_32 - gl), ebt = beta el (two
+//    multiplies per element instead of an exponential);
+//  - dec is folded into the rows of T's factors, so that U' = diag(dec) U comes
+//    out of the products and feeds the state update directly, and the scores
+//    become P'_ts = ec_t (q_t . k_s) with ec = exp2(gl - gl_C): P' U' = P U
+//    because Gamma_ts = ec_t dec_s.
+// Otherwise the exponentials of differences are taken per element and U is
+// scaled by dec on the vector units.
 constexpr float kSpan = 100.f;
 struct alignas(16) Gates {
-    float gam[C], dec[C], bw[C], bg[C], gl[C], gb[C], el[C], fl[C], ebt[C];
+    float gam[C], dec[C], bw[C], bg[C], gl[C], gb[C], el[C], fl[C], ebt[C], ec[C];
     int fast, pad[3];  // (16-byte size: every slot's arrays take 16-byte reads)
 };
 static_assert(sizeof(Gates) % 16 == 0, "gate slots must stay 16-byte aligned");
 
-// Shared memory of one workgroup (155 KB).  Chunk c's k and v live in slot
+// Shared memory of one workgroup (156 KB).  Chunk c's k and v live in slot
 // c % 2 (so do the off-diagonal k-Gram tiles), its gates in slot c % 3; the
 // other arrays are single.
 struct Smem {
@@ -346,7 +353,7 @@ __device__ __forceinline__ Unit unit_of(const ChunkJob& job) {
 // Gates of chunk c from alpha, beta, bw of token `lane` (0 past T; identity
 // tokens there: alpha = 1, beta = bw = 0): an inclusive wave scan of ln alpha.
 struct LaneGates {
-    float gam, dec, bw, bg, gl, gb, el, fl, ebt;
+    float gam, dec, bw, bg, gl, gb, el, fl, ebt, ec;
     bool fast;
 };
 __device__ __forceinline__ LaneGates lane_gates(int c, float pa, float pb, float pw, int T, int lane) {
@@ -366,6 +373,7 @@ __device__ __forceinline__ LaneGates lane_gates(int c, float pa, float pb, float
     g.el = __builtin_amdgcn_exp2f(g.gl - ref);
     g.fl = __builtin_amdgcn_exp2f(ref - g.gl);
     g.ebt = pb * g.el;
+    g.ec = __builtin_amdgcn_exp2f(g.gl - g63);
     return g;
 }
 
@@ -395,8 +403,8 @@ __device__ __forceinline__ void score_tile(Smem& sm, const uint16_t* Kb, const G
             *reinterpret_cast<uint2*>(&sm.P[qrow * LT + s0]) = pack4(p[0], p[1], p[2], p[3]);
         }
     };
-    if (__builtin_amdgcn_readfirstlane(G.fast))
-        mask([](float a, float b) { return a * b; }, G.fl, G.el[t]);
+    if (__builtin_amdgcn_readfirstlane(G.fast))  // P'_ts = ec_t (q_t . k_s)
+        mask([](float a, float) { return a; }, G.fl, G.ec[t]);
     else
         mask([](float a, float b) { return __builtin_amdgcn_exp2f(a - b); }, G.gl, G.gl[t]);
 }
@@ -504,12 +512,14 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
     };
     round_state();
 
-    f32x16 qacc[2], xacc[2];
+    f32x16 qacc[2], xacc[2], oacc[2];
     for (int j = un.nb - 2; j < un.ne; ++j) {
         const bool act = j >= un.nb;
         const uint16_t* Kb = sm.K[j & 1];
-        // ---- first half: X = K S^T and O^T = S Q^T, four independent chains ----
+        // ---- first half: X = K S^T and O^T = S Q^T, four independent chains;
+        // then the U-independent scalings of the second half ----
         if (act) {
+            round_state();  // the state entering chunk j (updated in the previous step)
             // operands of contraction step k (keys 16k + 8h ..): k rows and q rows of
             // token tiles 0 and 1, loaded two steps ahead
             auto ka = [&](int k, int tt) { return lds8(Kb + kidx(32 * tt + l32, 16 * k + 8 * h)); };
@@ -539,57 +549,66 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                     if (OUT) qacc[tt] = mfma32(sbf[k], qr[k % 3][tt], qacc[tt]);
                 }
             }
+            // gamma_C S^T, and the gamma scaling of the read-out (column l32 of tile tt
+            // is token t = 32 tt + perm5(l32): one gate per lane); the gates of chunk
+            // j were formed two steps ago
+            const Gates& G = sm.gate[j % 3];
+            const float gC = G.gam[C - 1];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) sacc[jt] *= gC;
+            if (OUT) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) oacc[tt] = qacc[tt] * G.gam[32 * tt + perm5(l32)];
+            }
         }
         lds_barrier();
         // ---- second half: U, O (staged for the load waves), the state update ----
         if (act) {
             const Gates& G = sm.gate[j % 3];
             const uint16_t* Vb = sm.V[j & 1];
-            // independent of U (free to overlap its products): gamma_C S^T, and the
-            // gamma scaling of the read-out (column l32 of tile tt is token
-            // t = 32 tt + perm5(l32): one gate per lane)
-            const float gC = G.gam[C - 1];
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) sacc[jt] *= gC;
-            f32x16 oacc[2];
-            if (OUT) {
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) oacc[tt] = qacc[tt] * G.gam[32 * tt + perm5(l32)];
-            }
+            const bool fast = __builtin_amdgcn_readfirstlane(G.fast);
             f32x16 uacc[2];
             if (GDN) {
                 // U = Tb V + Tbn X; T is lower triangular: token tile 0 contracts over
                 // tokens 0..31 only
-                uacc[0] = f32x16{};
-                uacc[1] = f32x16{};
+                // (two accumulators per token tile halve the dependent chains)
+                f32x16 va[2] = {f32x16{}, f32x16{}}, xa[2] = {f32x16{}, f32x16{}};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const bf16x8 xo = sop(xacc, kk);
                     if (!un.erows) {  // rows of E: v = 0
                         const bf16x8 vo = v_operand(Vb, kk, 32 * vb, lane);
-                        uacc[1] = mfma32(lds8(&sm.Tb[(32 + l32) * LT + 16 * kk + 8 * h]), vo, uacc[1]);
-                        if (kk < 2) uacc[0] = mfma32(lds8(&sm.Tb[l32 * LT + 16 * kk + 8 * h]), vo, uacc[0]);
+                        va[1] = mfma32(lds8(&sm.Tb[(32 + l32) * LT + 16 * kk + 8 * h]), vo, va[1]);
+                        if (kk < 2) va[0] = mfma32(lds8(&sm.Tb[l32 * LT + 16 * kk + 8 * h]), vo, va[0]);
                     }
-                    uacc[1] = mfma32(lds8(&sm.Tbn[(32 + l32) * LT + 16 * kk + 8 * h]), xo, uacc[1]);
-                    if (kk < 2) uacc[0] = mfma32(lds8(&sm.Tbn[l32 * LT + 16 * kk + 8 * h]), xo, uacc[0]);
+                    xa[1] = mfma32(lds8(&sm.Tbn[(32 + l32) * LT + 16 * kk + 8 * h]), xo, xa[1]);
+                    if (kk < 2) xa[0] = mfma32(lds8(&sm.Tbn[l32 * LT + 16 * kk + 8 * h]), xo, xa[0]);
                 }
+                uacc[0] = va[0] + xa[0];
+                uacc[1] = va[1] + xa[1];
             } else {
+                // U = V; on fast chunks U' = diag(dec) V
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
                         const bf16x8 v8 = v_operand(Vb, 2 * tt + s2, 32 * vb, lane);
+                        const f32x8 d = fast ? ld8f(&G.dec[32 * tt + 16 * s2 + 8 * h]) : f32x8{1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) uacc[tt][8 * s2 + i] = static_cast<float>(v8[i]);
+                        for (int i = 0; i < 8; ++i) uacc[tt][8 * s2 + i] = static_cast<float>(v8[i]) * d[i];
                     }
             }
+            // U (U' on fast chunks) as bf16 operands: read-out and, on fast chunks, the
+            // state update
+            bf16x8 uo[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) uo[ks] = sop(uacc, ks);
             if (OUT) {
                 // O^T = S Q^T diag(gamma) + U^T P^T
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 uo = sop(uacc, ks);
-                    oacc[1] = mfma32(uo, lds8(&sm.P[(32 + l32) * LT + 16 * ks + 8 * h]), oacc[1]);
-                    if (ks < 2) oacc[0] = mfma32(uo, lds8(&sm.P[l32 * LT + 16 * ks + 8 * h]), oacc[0]);
+                    oacc[1] = mfma32(uo[ks], lds8(&sm.P[(32 + l32) * LT + 16 * ks + 8 * h]), oacc[1]);
+                    if (ks < 2) oacc[0] = mfma32(uo[ks], lds8(&sm.P[l32 * LT + 16 * ks + 8 * h]), oacc[0]);
                 }
                 // element e holds value 32 vb + elem_index(0, e, h): elements 8s .. 8s+7 are
                 // 8 consecutive values, one 16-byte LDS write each
@@ -602,19 +621,20 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             }
             // S^T <- gamma_C S^T + K^T diag(dec) U
             bf16x8 db[4];
+            if (fast) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const f32x4 d0 = *reinterpret_cast<const f32x4*>(&G.dec[16 * ks + 8 * h]);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(&G.dec[16 * ks + 8 * h + 4]);
-                const f32x16& u = uacc[ks >> 1];
-                const int off = 8 * (ks & 1);
-                f32x8 x;
+                for (int ks = 0; ks < 4; ++ks) db[ks] = uo[ks];
+            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[i] = u[off + i] * d0[i];
-                    x[4 + i] = u[off + 4 + i] * d1[i];
+                for (int ks = 0; ks < 4; ++ks) {
+                    const f32x8 d = ld8f(&G.dec[16 * ks + 8 * h]);
+                    const f32x16& u = uacc[ks >> 1];
+                    const int off = 8 * (ks & 1);
+                    f32x8 x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[i] = u[off + i] * d[i];
+                    db[ks] = __builtin_convertvector(x, bf16x8);
                 }
-                db[ks] = __builtin_convertvector(x, bf16x8);
             }
             bf16x8 ko[2][4];
 #pragma unroll
@@ -628,7 +648,6 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) sacc[jt] = mfma32(ko[k & 1][jt], db[k], sacc[jt]);
             }
-            round_state();
         }
         lds_barrier();
     }
@@ -720,10 +739,12 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
         const int t = lane & 31, hh = lane >> 5;
         const float* dr = sm.D[blk] + t * LS + 16 * hh;
         const int prow = 32 * blk + perm5(t);
+        // row t scaled by dec_t on fast chunks (U' = diag(dec) U)
+        const float rs = __builtin_amdgcn_readfirstlane(G.fast) ? G.dec[32 * blk + t] : 1.f;
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
             const int s0 = 32 * blk + 16 * hh + 8 * q2;
-            const f32x8 d = ld8f(dr + 8 * q2), w = ld8f(&G.bw[s0]), g = ld8f(&G.bg[s0]);
+            const f32x8 d = ld8f(dr + 8 * q2) * rs, w = ld8f(&G.bw[s0]), g = ld8f(&G.bg[s0]);
             *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + s0]) = pack8(d * w);
             *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + s0]) = pack8(-(d * g));
         }
@@ -862,6 +883,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
             G.el[lane] = g.el;
             G.fl[lane] = g.fl;
             G.ebt[lane] = g.ebt;
+            G.ec[lane] = g.ec;
             if (lane == 0) G.fast = g.fast;
             if (c2 + 1 < un.ne) load_ab(c2 + 1);
         }
@@ -894,21 +916,32 @@ __device__ __forceinline__ void aux_role(Smem& sm, const ChunkJob& job, const Un
             const Gates& G = sm.gate[j % 3];
             if (GDN && w == 6) {
                 // T_bl = -D_bot A_bl D_top (rows 32 + i, columns jj), as
-                // T_bl^T = -D_top^T Z with Z = A_bl^T D_bot^T, split bf16
+                // T_bl^T = -D_top^T Z with Z = A_bl^T D_bot^T, split bf16; every LDS
+                // input is read up front
                 const float* Ab = sm.Ablt[j & 1];
                 const float* Db = sm.D[1];
                 const float* Dtt = sm.Dt;
                 const int pr = perm5(l32);
+                f32x8 ab[2], db[2], dt[2], wv[2], gv[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    ab[kk] = ld8f(&Ab[pr * LS + 16 * kk + 8 * h]);
+                    db[kk] = ld8f(&Db[l32 * LS + 16 * kk + 8 * h]);
+                    dt[kk] = ld8f(&Dtt[pr * LS + 16 * kk + 8 * h]);
+                    wv[kk] = ld8f(&G.bw[16 * kk + 8 * h]);
+                    gv[kk] = ld8f(&G.bg[16 * kk + 8 * h]);
+                }
+                // row 32 + l32 scaled by dec on fast chunks (U' = diag(dec) U)
+                const float rs = __builtin_amdgcn_readfirstlane(G.fast) ? G.dec[32 + l32] : 1.f;
                 f32x16 z = f32x16{};
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    z = mfma_split(ld8f(&Ab[pr * LS + 16 * kk + 8 * h]), ld8f(&Db[l32 * LS + 16 * kk + 8 * h]), z);
+                for (int kk = 0; kk < 2; ++kk) z = mfma_split(ab[kk], db[kk], z);
                 f32x16 tacc = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const f32x8 zb = kk ? __builtin_shufflevector(z, z, 8, 9, 10, 11, 12, 13, 14, 15)
                                         : __builtin_shufflevector(z, z, 0, 1, 2, 3, 4, 5, 6, 7);
-                    tacc = mfma_split(ld8f(&Dtt[pr * LS + 16 * kk + 8 * h]), zb, tacc);
+                    tacc = mfma_split(dt[kk], zb, tacc);
                 }
                 // lane l32: row 32 + l32 of T (physical row 32 + perm5(l32)); elements
                 // 8s2 .. 8s2+7: columns 16 s2 + 8 h .. +7 of -T_bl
@@ -916,11 +949,10 @@ __device__ __forceinline__ void aux_role(Smem& sm, const ChunkJob& job, const Un
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int c0 = 16 * s2 + 8 * h;
-                    const f32x8 tn = s2 ? __builtin_shufflevector(tacc, tacc, 8, 9, 10, 11, 12, 13, 14, 15)
-                                        : __builtin_shufflevector(tacc, tacc, 0, 1, 2, 3, 4, 5, 6, 7);
-                    const f32x8 wv = ld8f(&G.bw[c0]), gv = ld8f(&G.bg[c0]);
-                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + c0]) = pack8(-(tn * wv));
-                    *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + c0]) = pack8(tn * gv);
+                    const f32x8 tn = (s2 ? __builtin_shufflevector(tacc, tacc, 8, 9, 10, 11, 12, 13, 14, 15)
+                                         : __builtin_shufflevector(tacc, tacc, 0, 1, 2, 3, 4, 5, 6, 7)) * rs;
+                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + c0]) = pack8(-(tn * wv[s2]));
+                    *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + c0]) = pack8(tn * gv[s2]);
                 }
             }
             if (OUT && w == 7) {
