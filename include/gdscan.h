@@ -140,6 +140,32 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
              const float *beta, const float *S0, void *o, float *ST,
              void *workspace, size_t workspace_bytes, const scan_opts *opts, void *stream);
 
+/* Bytes of the fixed device scratch behind scan_fwd_noalloc (per GPU). */
+#define SCAN_NOALLOC_MAX_WORKSPACE (64u << 20)
+
+/*
+ * scan_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  Same
+ * arguments, results and validation as scan_fwd, without the workspace
+ * argument: where the chosen path needs scratch (see scan_fwd_workspace_size)
+ * the library uses a fixed array of SCAN_NOALLOC_MAX_WORKSPACE bytes in device
+ * memory, one per GPU, which that GPU holds from the library's first use on it
+ * until the process ends.  The call never allocates or frees device memory.
+ *   - Arguments whose workspace size exceeds SCAN_NOALLOC_MAX_WORKSPACE are
+ *     rejected with SCAN_EWORKSPACE before anything is launched.
+ *   - Every call on one GPU shares that GPU's array: calls that may run at the
+ *     same time on one GPU (different streams, or host threads without
+ *     ordering) race and give wrong results.  Order them on one stream.
+ *   - The array keeps whatever the last call left in it; no path reads it
+ *     before writing it.
+ *   - The first call on a device looks up the array's device address (a HIP
+ *     runtime query, no allocation) and caches it for later calls.
+ */
+int scan_fwd_noalloc(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+                     const void *q, const void *k, const void *v, const float *alpha,
+                     const float *beta, const float *S0, void *o, float *ST,
+                     const scan_opts *opts, void *stream);
+
 /*
  * One token for each of N independent states (the sequential view: state
  * update U and read-out F of key design 1 in the prefix-scan notes); exactly

@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 SCAN_GDN, SCAN_GLA, SCAN_GDN_EW, SCAN_GDN_DIAG, SCAN_GLA_DIAG = 0, 1, 2, 3, 4
 SCAN_F32, SCAN_BF16 = 0, 1
 SCAN_OK, SCAN_EINVAL, SCAN_EUNSUPPORTED, SCAN_EWORKSPACE, SCAN_EALIGN, SCAN_EHIP = range(6)
+SCAN_NOALLOC_MAX_WORKSPACE = 64 << 20
 PATHS = {"auto": 0, "sequential": 1, "blelloch": 2}
 STATUS_NAMES = {0: "SCAN_OK", 1: "SCAN_EINVAL", 2: "SCAN_EUNSUPPORTED", 3: "SCAN_EWORKSPACE",
                 4: "SCAN_EALIGN", 5: "SCAN_EHIP"}
@@ -52,6 +53,9 @@ def lib() -> ctypes.CDLL:
         L.scan_fwd.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p, sz,
                                ctypes.POINTER(ScanOpts), p]
         L.scan_fwd.restype = i
+        L.scan_fwd_noalloc.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p,
+                                       ctypes.POINTER(ScanOpts), p]
+        L.scan_fwd_noalloc.restype = i
         L.decode_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
         L.decode_step.restype = i
         L.prism_expand.argtypes = [i] * 8 + [p] * 15 + [p]
@@ -130,18 +134,9 @@ def scan_fwd_workspace_size(mode: int, dtype: int, B: int, H: int, T: int, dk: i
     return n
 
 
-def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str = "auto",
-             leaf_chunks: int = 0, o=None, ST=None, workspace=None, write_state: bool = True):
-    """Forward scan over [B, H, T, d] tensors; returns (o, ST).
-
-    ``beta is None`` selects gated linear attention (E = alpha I, f = v k^T),
-    a [B, H, T] ``beta`` the gated delta rule, and a [2, B, H, T] ``beta``
-    (erase strengths, then write strengths) the gated delta rule with split
-    strengths (SCAN_GDN_EW).  A [B, H, T, dk] ``alpha`` (one decay per key
-    channel) selects the diagonal-gate modes (SCAN_GDN_DIAG with beta,
-    SCAN_GLA_DIAG without).  ``S0=None`` is the zero state.  ``ST`` may
-    be ``S0`` itself (in-place carry).  ``write_state=False`` skips S_T.
-    """
+def _scan_args(q, k, v, alpha, beta, S0, o, ST, write_state):
+    """Checks the tensors of a forward scan and allocates missing outputs;
+    returns (mode, B, H, T, dk, dv, o, ST)."""
     _need(q, "q")
     dev = q.device
     dt = q.dtype
@@ -168,6 +163,23 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
         ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if ST is not None:
         _need(ST, "ST", torch.float32, (B, H, dv, dk), dev)
+    return mode, B, H, T, dk, dv, o, ST
+
+
+def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str = "auto",
+             leaf_chunks: int = 0, o=None, ST=None, workspace=None, write_state: bool = True):
+    """Forward scan over [B, H, T, d] tensors; returns (o, ST).
+
+    ``beta is None`` selects gated linear attention (E = alpha I, f = v k^T),
+    a [B, H, T] ``beta`` the gated delta rule, and a [2, B, H, T] ``beta``
+    (erase strengths, then write strengths) the gated delta rule with split
+    strengths (SCAN_GDN_EW).  A [B, H, T, dk] ``alpha`` (one decay per key
+    channel) selects the diagonal-gate modes (SCAN_GDN_DIAG with beta,
+    SCAN_GLA_DIAG without).  ``S0=None`` is the zero state.  ``ST`` may
+    be ``S0`` itself (in-place carry).  ``write_state=False`` skips S_T.
+    """
+    mode, B, H, T, dk, dv, o, ST = _scan_args(q, k, v, alpha, beta, S0, o, ST, write_state)
+    dev = q.device
     dcode = _dtype_code(q)
     ws_bytes = scan_fwd_workspace_size(mode, dcode, B, H, T, dk, dv, chunk, path, leaf_chunks)
     if ws_bytes and workspace is None:
@@ -180,6 +192,25 @@ def scan_fwd(q, k, v, alpha, beta=None, S0=None, *, chunk: int = 64, path: str =
                             _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace),
                             0 if workspace is None else workspace.numel(), ctypes.byref(opts),
                             _stream(dev))
+    _check(st)
+    return o, ST
+
+
+def scan_fwd_noalloc(q, k, v, alpha, beta=None, S0=None, *, o, ST=None, chunk: int = 64,
+                     path: str = "auto", leaf_chunks: int = 0):
+    """``scan_fwd`` through the C entry point of the same name, which takes no
+    workspace: the library's fixed per-GPU scratch stands in for it (at most
+    SCAN_NOALLOC_MAX_WORKSPACE bytes).  The caller passes the outputs (``o``,
+    and ``ST`` unless S_T is not wanted), so nothing is allocated here either."""
+    if o is None:
+        raise ValueError("scan_fwd_noalloc: pass the output tensor o")
+    mode, B, H, T, dk, dv, o, ST = _scan_args(q, k, v, alpha, beta, S0, o, ST, False)
+    dev = q.device
+    opts = ScanOpts(PATHS[path], leaf_chunks)
+    with torch.cuda.device(dev):
+        st = lib().scan_fwd_noalloc(mode, _dtype_code(q), B, H, T, dk, dv, chunk, _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
+                                    ctypes.byref(opts), _stream(dev))
     _check(st)
     return o, ST
 

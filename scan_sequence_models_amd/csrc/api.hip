@@ -136,28 +136,11 @@ int plan_scan(int mode, int dtype, int B, int H, int T, int dk, int dv, int chun
     return SCAN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* scan_last_error(void) { return g_err; }
-
-const char* scan_version(void) { return "gdscan 0.1.0 (gfx950, HIP)"; }
-
-size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
-                               const scan_opts* opts) {
-    Plan p;
-    if (plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p) != SCAN_OK) return (size_t)-1;
-    return p.workspace;
-}
-
-int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk, const void* q,
-             const void* k, const void* v, const float* alpha, const float* beta, const float* S0,
-             void* o, float* ST, void* workspace, size_t workspace_bytes, const scan_opts* opts,
-             void* stream) {
-    Plan p;
-    int st = plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p);
-    if (st != SCAN_OK) return st;
+// The rest of scan_fwd once the plan is made: pointer checks, then the launch.
+int scan_fwd_planned(const Plan& p, int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+                     const void* q, const void* k, const void* v, const float* alpha,
+                     const float* beta, const float* S0, void* o, float* ST, void* workspace,
+                     size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !alpha || !o) return fail(SCAN_EINVAL, "q, k, v, alpha and o must be non-null");
     if (!gla_mode(mode) && !beta) return fail(SCAN_EINVAL, "the gated-delta modes need beta");
     if (gla_mode(mode) && beta) return fail(SCAN_EINVAL, "the GLA modes take no beta (pass NULL)");
@@ -208,6 +191,55 @@ int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk
     }
     if (e != hipSuccess) return hip_fail(e, "scan_fwd launch");
     return SCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* scan_last_error(void) { return g_err; }
+
+const char* scan_version(void) { return "gdscan 0.1.0 (gfx950, HIP)"; }
+
+size_t scan_fwd_workspace_size(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+                               const scan_opts* opts) {
+    Plan p;
+    if (plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p) != SCAN_OK) return (size_t)-1;
+    return p.workspace;
+}
+
+int scan_fwd(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk, const void* q,
+             const void* k, const void* v, const float* alpha, const float* beta, const float* S0,
+             void* o, float* ST, void* workspace, size_t workspace_bytes, const scan_opts* opts,
+             void* stream) {
+    Plan p;
+    const int st = plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p);
+    if (st != SCAN_OK) return st;
+    return scan_fwd_planned(p, mode, dtype, B, H, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST,
+                            workspace, workspace_bytes, stream);
+}
+
+int scan_fwd_noalloc(int mode, int dtype, int B, int H, int T, int dk, int dv, int chunk,
+                     const void* q, const void* k, const void* v, const float* alpha,
+                     const float* beta, const float* S0, void* o, float* ST,
+                     const scan_opts* opts, void* stream) {
+    Plan p;
+    const int st = plan_scan(mode, dtype, B, H, T, dk, dv, chunk, opts, &p);
+    if (st != SCAN_OK) return st;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (p.workspace > 0) {
+        if (p.workspace > (size_t)SCAN_NOALLOC_MAX_WORKSPACE)
+            return fail(SCAN_EWORKSPACE,
+                        "scan_fwd_noalloc: these arguments need %zu bytes of scratch, above the fixed "
+                        "%zu bytes it has (use scan_fwd with a caller workspace)",
+                        p.workspace, (size_t)SCAN_NOALLOC_MAX_WORKSPACE);
+        const hipError_t e = gds::noalloc_scratch(&ws);
+        if (e != hipSuccess) return hip_fail(e, "scan_fwd_noalloc: address of the device scratch");
+        ws_bytes = SCAN_NOALLOC_MAX_WORKSPACE;
+    }
+    return scan_fwd_planned(p, mode, dtype, B, H, T, dk, dv, chunk, q, k, v, alpha, beta, S0, o, ST, ws,
+                            ws_bytes, stream);
 }
 
 int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const void* k,

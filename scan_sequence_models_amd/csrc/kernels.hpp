@@ -106,4 +106,9 @@ bool lact_plain_supported(int dk, int dv);
 size_t lact_workspace_bytes(int64_t heads, int T, int chunk);
 hipError_t launch_lact(int dtype, LactJob job, void* workspace, hipStream_t stream);
 
+// scratch.hip -- device address of the current device's fixed scratch array
+// (SCAN_NOALLOC_MAX_WORKSPACE bytes, 256-byte aligned), looked up once per
+// device and cached.  Allocates nothing.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace gds

@@ -20,7 +20,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = L.header_functions()
-    assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "decode_step", "prism_expand",
+    assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "scan_fwd_noalloc", "decode_step",
+                          "prism_expand",
                           "lact_fwd_workspace_size", "lact_fwd", "scan_bwd_workspace_size", "scan_bwd",
                           "scan_last_error", "scan_version"}
     for n in names:
@@ -89,6 +90,37 @@ def test_scan_fwd_workspace_size_invalid(lib):
 def test_sequential_path_needs_no_workspace(lib):
     assert lib.scan_fwd_workspace_size(0, 1, 8, 16, 8192, 128, 128, 64, _opts(1)) == 0
     assert lib.scan_fwd_workspace_size(0, 0, 1, 1, 64, 16, 16, 16, _opts(1)) == 0
+
+
+def _noalloc(lib, B=1, H=2, T=64, opts=None, q=FAKE, o=FAKE + 6 * STEP):
+    return lib.scan_fwd_noalloc(0, 1, B, H, T, 128, 128, 64, q, FAKE + STEP, FAKE + 2 * STEP,
+                                FAKE + 3 * STEP, FAKE + 4 * STEP, None, o, FAKE + 7 * STEP,
+                                opts if opts is not None else _opts(), None)
+
+
+def test_noalloc_rejects_workspace_above_its_scratch(lib):
+    """128 heads x 64 leaves need about 3 GB of tree workspace: above the fixed
+    scratch, so the call is refused before anything is launched."""
+    need = lib.scan_fwd_workspace_size(0, 1, 8, 16, 65536, 128, 128, 64, _opts(2, 16))
+    assert need > L.SCAN_NOALLOC_MAX_WORKSPACE
+    assert _noalloc(lib, B=8, H=16, T=65536, opts=_opts(2, 16)) == L.SCAN_EWORKSPACE
+    assert "scratch" in L.last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), L.SCAN_EINVAL),
+    (dict(q=None), L.SCAN_EINVAL),
+    (dict(o=FAKE + 256), L.SCAN_EINVAL),   # o overlaps q
+    (dict(opts=_opts(path=9)), L.SCAN_EINVAL),
+])
+def test_noalloc_validates_like_scan_fwd(lib, kw, code):
+    assert _noalloc(lib, **kw) == code
+
+
+def test_noalloc_limit_matches_header():
+    text = open(L.HEADER).read()
+    assert "#define SCAN_NOALLOC_MAX_WORKSPACE (64u << 20)" in text
+    assert L.SCAN_NOALLOC_MAX_WORKSPACE == 64 << 20
 
 
 def _decode(lib, mode=0, dtype=1, N=4, dk=128, dv=128, q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP,
