@@ -22,6 +22,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
 _CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
            "-std=c11", "-Wall", "-Wextra"]
 _lib = None
@@ -38,12 +39,26 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized() -> str:
+    """``liboracle_san.so``: the same source under AddressSanitizer and
+    UndefinedBehaviorSanitizer, built with clang so that it shares one sanitizer
+    runtime (clang's, preloaded by the process) with the library's sanitizer
+    build.  Load it by setting ORACLE_LIB to its path."""
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+    tmp = _LIB_SAN + f".tmp{os.getpid()}"
+    subprocess.run([clang, *_CFLAGS, "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                    "-fno-omit-frame-pointer", "-g", _SRC, "-o", tmp], check=True)
+    os.replace(tmp, _LIB_SAN)
+    return _LIB_SAN
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         lib.oracle_scan_f64.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_int, p, p, p, p, p, p, p, p, ctypes.c_int]

@@ -14,7 +14,9 @@ import re
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdscan.so")
+# GDSCAN_LIB names another build of the same library (the sanitizer build)
+LIB_PATH = os.environ.get("GDSCAN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libgdscan.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "gdscan.h")
 
