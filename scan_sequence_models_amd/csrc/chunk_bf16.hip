@@ -33,14 +33,15 @@
 //
 //   waves 0, 1  state: wave w keeps the 32 value columns [32w, 32w+32) of S^T
 //               (128 keys, fp32) in four 32x32 MFMA accumulator tiles for the
-//               whole sequence.  First half: X = K S^T and Q S^T of chunk j;
-//               second half: U, O (written out) and the state update.
-//   waves 4, 5  first half: T's two diagonal 32x32 blocks of chunk j scaled into
-//               the bf16 factors Tb = T diag(bw), Tbn = -T diag(beta gamma);
+//               whole sequence.  First half: X = K S^T and Q S^T of chunk j,
+//               and (wave 1) the gates of chunk j+2, a wave scan of ln alpha;
+//               second half: U, O (staged in LDS) and the state update.
+//   waves 4, 5  first half: o of chunk j-1 stored from LDS (16-byte stores),
+//               and T's two diagonal 32x32 blocks of chunk j scaled into the
+//               bf16 factors Tb = T diag(bw), Tbn = -T diag(beta gamma);
 //               second half: chunk j+1's q, k, v staged in LDS, then chunk j+2's
 //               rows loaded into registers (coalesced 16-byte loads).
-//   wave 2      first half: chunk j+1's two diagonal k-Gram tiles; second
-//               half: the gates of chunk j+2 (a wave scan of ln alpha).
+//   wave 2      first half: chunk j+1's two diagonal k-Gram tiles.
 //   wave 3      first half: chunk j+1's off-diagonal k-Gram tile and chunk j's
 //               score tile (0,0).
 //   wave 6      first half: T's off-diagonal block of chunk j,
@@ -377,17 +378,31 @@ __device__ __forceinline__ LaneGates lane_gates(int c, float pa, float pb, float
     return g;
 }
 
+// Gates of chunk c into slot G (one token per lane).
+__device__ __forceinline__ void form_gates(Gates& G, int c, float pa, float pb, float pw, int T, int lane) {
+    const LaneGates g = lane_gates(c, pa, pb, pw, T, lane);
+    G.gam[lane] = g.gam;
+    G.dec[lane] = g.dec;
+    G.bw[lane] = g.bw;
+    G.bg[lane] = g.bg;
+    G.gl[lane] = g.gl;
+    G.gb[lane] = g.gb;
+    G.el[lane] = g.el;
+    G.fl[lane] = g.fl;
+    G.ebt[lane] = g.ebt;
+    G.ec[lane] = g.ec;
+    if (lane == 0) G.fast = g.fast;
+}
+
 // One 32x32 score tile of chunk-local tokens, computed transposed:
 // acc[s][t] = sum_key K[s][key] Q[t][key], s = 32J + row, t = 32I + column;
 // lane l32 holds column t = 32I + perm5(l32) and element e row
 // s = 32J + elem_index(0, e, h).  Masked (e^(g_t - g_s) where t >= s, else 0),
 // packed to bf16 and stored into P (physical row 32I + l32).
-__device__ __forceinline__ void score_tile(Smem& sm, const uint16_t* Kb, const Gates& G, int I, int J,
+// score_mask masks and stores a tile whose products are in acc.
+__device__ __forceinline__ void score_mask(Smem& sm, const f32x16& acc, const Gates& G, int I, int J,
                                            int l32, int h) {
-    const int qrow = 32 * I + l32, krow = 32 * J + l32;
-    const f32x16 acc = mfma_chain2<8>([&](int k) { return lds8(Kb + kidx(krow, 16 * k + 8 * h)); },
-                                      [&](int k) { return lds8(&sm.Q[qrow * LQ + 16 * k + 8 * h]); },
-                                      f32x16{});
+    const int qrow = 32 * I + l32;
     const int t = 32 * I + perm5(l32);
     auto mask = [&](auto weight, const float* ws, float et) {
 #pragma unroll
@@ -407,6 +422,36 @@ __device__ __forceinline__ void score_tile(Smem& sm, const uint16_t* Kb, const G
         mask([](float a, float) { return a; }, G.fl, G.ec[t]);
     else
         mask([](float a, float b) { return __builtin_amdgcn_exp2f(a - b); }, G.gl, G.gl[t]);
+}
+// Operands of score tile (I, J) at contraction step k (keys 16k + 8h ..).
+__device__ __forceinline__ bf16x8 score_k(const uint16_t* Kb, int J, int k, int l32, int h) {
+    return lds8(Kb + kidx(32 * J + l32, 16 * k + 8 * h));
+}
+__device__ __forceinline__ bf16x8 score_q(const Smem& sm, int I, int k, int l32, int h) {
+    return lds8(&sm.Q[(32 * I + l32) * LQ + 16 * k + 8 * h]);
+}
+// Score tiles (1, 0) and (1, 1): one pass over their shared q rows, two
+// independent MFMA chains interleaved, operands loaded two steps ahead.
+__device__ __forceinline__ void score_tiles_row1(Smem& sm, const uint16_t* Kb, const Gates& G, int l32,
+                                                 int h) {
+    bf16x8 q[3], k0[3], k1[3];
+    auto fetch = [&](int k) {
+        q[k % 3] = score_q(sm, 1, k, l32, h);
+        k0[k % 3] = score_k(Kb, 0, k, l32, h);
+        k1[k % 3] = score_k(Kb, 1, k, l32, h);
+    };
+    fetch(0);
+    fetch(1);
+    f32x16 a0 = f32x16{}, a1 = f32x16{};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k + 2 < 8) fetch(k + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = mfma32(k0[k % 3], q[k % 3], a0);
+        a1 = mfma32(k1[k % 3], q[k % 3], a1);
+    }
+    score_mask(sm, a0, G, 1, 0, l32, h);
+    score_mask(sm, a1, G, 1, 1, l32, h);
 }
 
 // Top (blk 0) or bottom (blk 1) diagonal 32x32 block of T = (I + A)^-1 from
@@ -512,6 +557,22 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
     };
     round_state();
 
+    // wave 1 also forms the gates two chunks ahead, from alpha, beta, bw of token
+    // `lane` loaded a step earlier (this wave issues no other global loads in the
+    // loop, so waiting for them never waits for anything younger)
+    const int T = job.T;
+    const size_t a_base = (size_t)un.head * T;
+    const bool split = job.beta_w != job.beta;  // separate write strengths
+    float pa = 1.f, pb = 0.f, pw = 0.f;
+    auto load_ab = [&](int c) {
+        pa = ldtok(job.alpha + a_base, c, lane, T);
+        if (GDN) {
+            pb = ldtok(job.beta + a_base, c, lane, T);
+            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
+        }
+    };
+    if (vb == 1 && un.nb < un.ne) load_ab(un.nb);
+
     f32x16 qacc[2], xacc[2], oacc[2];
     for (int j = un.nb - 2; j < un.ne; ++j) {
         const bool act = j >= un.nb;
@@ -560,6 +621,12 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) oacc[tt] = qacc[tt] * G.gam[32 * tt + perm5(l32)];
             }
+        }
+        // gates of chunk j + 2 into slot (j + 2) % 3: that slot held chunk j - 1,
+        // which no wave reads after the previous step
+        if (vb == 1 && j + 2 < un.ne) {
+            form_gates(sm.gate[(j + 2) % 3], j + 2, pa, pb, split ? pw : pb, T, lane);
+            if (j + 3 < un.ne) load_ab(j + 3);
         }
         lds_barrier();
         // ---- second half: U, O (staged for the load waves), the state update ----
@@ -766,7 +833,7 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
 
 // ----------------------------------------------------------------------------
 // k-Gram waves (2, 3): chunk j+1's k-Gram tiles; wave 3 also chunk j's score
-// tile (0,0), wave 2 the gates of chunk j+2
+// tile (0,0)
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
@@ -776,18 +843,6 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     const int l32 = lane & 31, h = lane >> 5;
     const int T = job.T;
     const size_t qk_base = (size_t)un.head * T * DK;
-    // wave 2: alpha, beta, bw of token `lane` of the chunk whose gates come next
-    const size_t a_base = (size_t)un.head * T;
-    const bool split = job.beta_w != job.beta;  // separate write strengths
-    float pa = 1.f, pb = 0.f, pw = 0.f;
-    auto load_ab = [&](int c) {
-        pa = ldtok(job.alpha + a_base, c, lane, T);
-        if (GDN) {
-            pb = ldtok(job.beta + a_base, c, lane, T);
-            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
-        }
-    };
-    if (blk == 0 && un.nb < un.ne) load_ab(un.nb);
     // chunk c's k rows as MFMA operands, kreg[b][kk] = k[32b + l32][16kk + 8h .. +7],
     // loaded a chunk ahead of their use
     bf16x8 kreg[1][2][8];
@@ -832,6 +887,8 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     for (int j = un.nb - 2; j < un.ne; ++j) {
         constexpr int st = 0;
         const int c = j + 1;  // chunk whose gates, k-Gram and diagonal T blocks are built
+        // wave 3: score tile (0,0) of chunk j
+        bool score = OUT && blk == 1 && j >= un.nb;
         // ---- first half ----
         if (GDN && c >= un.nb && c < un.ne) {
             const Gates& G = sm.gate[c % 3];
@@ -855,6 +912,28 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 }
                 gram_mask(a0, 0, 0, fast, ws0, wt0, sm.At[0]);
                 gram_mask(a1, 1, 1, fast, ws1, wt1, sm.At[1]);
+            } else if (score) {
+                // the off-diagonal k-Gram tile and score tile (0,0) of chunk j as two
+                // interleaved chains (the score operands from LDS, two steps ahead)
+                const uint16_t* Kb = sm.K[j & 1];
+                bf16x8 sq[3], sk[3];
+                auto fetch = [&](int k) {
+                    sq[k % 3] = score_q(sm, 0, k, l32, h);
+                    sk[k % 3] = score_k(Kb, 0, k, l32, h);
+                };
+                fetch(0);
+                fetch(1);
+                f32x16 a = f32x16{}, sc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    if (kk + 2 < 8) fetch(kk + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
+                    sc = mfma32(sk[kk % 3], sq[kk % 3], sc);
+                }
+                gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
+                score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
+                score = false;
             } else {
                 f32x16 a = f32x16{};
 #pragma unroll
@@ -862,31 +941,17 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
             }
         }
-        if (OUT && blk == 1 && j >= un.nb) score_tile(sm, sm.K[j & 1], sm.gate[j % 3], 0, 0, l32, h);
+        if (score) {
+            const f32x16 sc = mfma_chain2<8>([&](int k) { return score_k(sm.K[j & 1], 0, k, l32, h); },
+                                             [&](int k) { return score_q(sm, 0, k, l32, h); }, f32x16{});
+            score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
+        }
         // chunk c + 1 goes into the registers just used: keep the loads after
         // their last use (hoisted above it they would need a second set)
         __builtin_amdgcn_sched_barrier(0);
         if (GDN && c + 1 < un.ne) load(c + 1);
         lds_barrier();
-        // ---- second half: wave 2 forms the gates of chunk j + 2 (slot (j+2) % 3;
-        // slots j % 3 and (j+1) % 3 are in use) and loads the next chunk's ----
-        const int c2 = j + 2;
-        if (blk == 0 && c2 < un.ne) {
-            const LaneGates g = lane_gates(c2, pa, pb, split ? pw : pb, T, lane);
-            Gates& G = sm.gate[c2 % 3];
-            G.gam[lane] = g.gam;
-            G.dec[lane] = g.dec;
-            G.bw[lane] = g.bw;
-            G.bg[lane] = g.bg;
-            G.gl[lane] = g.gl;
-            G.gb[lane] = g.gb;
-            G.el[lane] = g.el;
-            G.fl[lane] = g.fl;
-            G.ebt[lane] = g.ebt;
-            G.ec[lane] = g.ec;
-            if (lane == 0) G.fast = g.fast;
-            if (c2 + 1 < un.ne) load_ab(c2 + 1);
-        }
+        // (second half: nothing for these waves)
         lds_barrier();
     }
 }
@@ -956,8 +1021,7 @@ __device__ __forceinline__ void aux_role(Smem& sm, const ChunkJob& job, const Un
                 }
             }
             if (OUT && w == 7) {
-                score_tile(sm, sm.K[j & 1], G, 1, 0, l32, h);
-                score_tile(sm, sm.K[j & 1], G, 1, 1, l32, h);
+                score_tiles_row1(sm, sm.K[j & 1], G, l32, h);
             }
         }
         lds_barrier();
