@@ -22,7 +22,10 @@
 //
 // U = T (diag(bw) V - diag(beta gamma) K S^T) is the WY form's U with the
 // factor W = T diag(beta gamma) K never formed; gated linear attention has
-// U = V and no A, T, X.
+// U = V and no A, T, X.  T is applied by block forward substitution over the
+// chunk's two 32-token halves: with D_0, D_1 the inverses of the diagonal blocks
+// of I + A, A_bl its lower-left block and Y = diag(bw) V - diag(beta gamma) X,
+// U_top = D_0 Y_top and U_bot = D_1 Y_bot + G U_top, G = -D_1 A_bl.
 //
 // Mapping onto gfx950.  A workgroup of 8 waves owns one head and a 64-row slice
 // of its value channels (B*H*2 workgroups on the sequential path); all slices of
@@ -33,24 +36,24 @@
 //
 //   waves 0, 1  state: wave w keeps the 32 value columns [32w, 32w+32) of S^T
 //               (128 keys, fp32) in four 32x32 MFMA accumulator tiles for the
-//               whole sequence.  First half: X = K S^T and Q S^T of chunk j,
-//               and (wave 1) the gates of chunk j+2, a wave scan of ln alpha;
+//               whole sequence.  First half: X = K S^T and Q S^T of chunk j;
 //               second half: U, O (staged in LDS) and the state update.
 //   waves 4, 5  first half: o of chunk j-1 stored from LDS (16-byte stores),
-//               and T's two diagonal 32x32 blocks of chunk j scaled into the
-//               bf16 factors Tb = T diag(bw), Tbn = -T diag(beta gamma);
-//               second half: chunk j+1's q, k, v staged in LDS, then chunk j+2's
+//               and the two diagonal blocks D_0, D_1 of chunk j scaled into the
+//               bf16 factors Tb = D diag(bw), Tbn = -D diag(beta gamma);
+//               second half: chunk j+1's q, k, v staged in LDS, (wave 4) the
+//               gates of chunk j+2 (a wave scan of ln alpha), then chunk j+2's
 //               rows loaded into registers (coalesced 16-byte loads).
 //   wave 2      first half: chunk j+1's two diagonal k-Gram tiles.
 //   wave 3      first half: chunk j+1's off-diagonal k-Gram tile and chunk j's
 //               score tile (0,0).
-//   wave 6      first half: T's off-diagonal block of chunk j,
-//               -D_bot A_bl D_top, by split-bf16 products (hi/lo parts, three
-//               MFMAs per product), scaled into Tb, Tbn; second half: the top
-//               diagonal 32x32 block of chunk j+1's T (16x16 blocks by forward
-//               substitution, the block below their diagonal on the fp32 MFMA).
+//   wave 6      first half: G = -D_1 A_bl of chunk j by a split-bf16 product
+//               (hi/lo parts, three MFMAs per product), stored as bf16 in
+//               Tb's lower-left block; second half: D_0 of chunk j+1 (16x16
+//               blocks by forward substitution, the block below their
+//               diagonal on the fp32 MFMA).
 //   wave 7      first half: chunk j's score tiles (1,0) and (1,1); second half:
-//               the bottom diagonal block of chunk j+1's T.
+//               D_1 of chunk j+1.
 //
 // The k-Gram waves read k straight from global memory into MFMA operand
 // registers (a chunk ahead); the other products read LDS.  Operands contracted
@@ -102,8 +105,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 //  - the k-Gram mask uses the factored form beta_t Gamma_ts = ebt_t fl_s with
 //    el = exp2(gl - gl_32), fl = exp2(gl_32 - gl), ebt = beta el (two
 //    multiplies per element instead of an exponential);
-//  - dec is folded into the rows of T's factors, so that U' = diag(dec) U comes
-//    out of the products and feeds the state update directly, and the scores
+//  - dec is folded into the rows of T's factors (and G becomes
+//    diag(dec_bot) G diag(ec_top), which keeps its magnitude: the decays cancel),
+//    so that U' = diag(dec) U comes out of the products and feeds the state
+//    update directly, and the scores
 //    become P'_ts = ec_t (q_t . k_s) with ec = exp2(gl - gl_C): P' U' = P U
 //    because Gamma_ts = ec_t dec_s.
 // Otherwise the exponentials of differences are taken per element and U is
@@ -115,7 +120,7 @@ struct alignas(16) Gates {
 };
 static_assert(sizeof(Gates) % 16 == 0, "gate slots must stay 16-byte aligned");
 
-// Shared memory of one workgroup (156 KB).  Chunk c's k and v live in slot
+// Shared memory of one workgroup (152 KB).  Chunk c's k and v live in slot
 // c % 2 (so do the off-diagonal k-Gram tiles), its gates in slot c % 3; the
 // other arrays are single.
 struct Smem {
@@ -128,7 +133,6 @@ struct Smem {
     float At[2][32 * LS];     // diagonal k-Gram tiles of A, transposed: At[b][s][t] = A[32b+t][32b+s]
     float Ablt[2][32 * LS];   // A rows 32..63, columns 0..31, transposed
     float D[2][32 * LS];      // diagonal 32x32 blocks of T (natural)
-    float Dt[32 * LS];        // the top one, transposed
     uint16_t Ost[C * LO];     // o of the chunk just read out [token][value] (natural rows)
     Gates gate[3];
 };
@@ -458,7 +462,7 @@ __device__ __forceinline__ void score_tiles_row1(Smem& sm, const uint16_t* Kb, c
 // the transposed k-Gram tile At[blk]: its two 16x16 diagonal blocks by
 // forward substitution (lane (sb, c) of the first 32 builds column c of
 // block sb; lanes 32..63 repeat them), then T10 = -T11 A10 T00 on the fp32
-// MFMA.  Written to D[blk] (natural) and Dt[blk] (transposed).
+// MFMA.  Written to D[blk].
 __device__ __forceinline__ void solve_block(Smem& sm, int blk, int lane) {
     const float* At = sm.At[blk];
     float* Db = sm.D[blk];
@@ -486,12 +490,6 @@ __device__ __forceinline__ void solve_block(Smem& sm, int blk, int lane) {
     if (lane < 32) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) Db[(16 * sb + r) * LS + 16 * sb + cc] = x[r];
-        if (blk == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<f32x4*>(&sm.Dt[(16 * sb + cc) * LS + 16 * sb + 4 * q]) =
-                    f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-        }
     }
     lds_fence();
     // T10 = -T11 (A10 T00): lane (n16, g4) holds rows 4 g4 .. +3 of column n16
@@ -506,7 +504,6 @@ __device__ __forceinline__ void solve_block(Smem& sm, int blk, int lane) {
     for (int kk = 0; kk < 4; ++kk) t10 = mfma4(at[kk], y[kk], t10);
 #pragma unroll
     for (int r = 0; r < 4; ++r) Db[(16 + 4 * g4 + r) * LS + n16] = -t10[r];
-    if (blk == 0) *reinterpret_cast<f32x4*>(&sm.Dt[n16 * LS + 16 + 4 * g4]) = -t10;
 }
 
 // ----------------------------------------------------------------------------
@@ -557,21 +554,6 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
     };
     round_state();
 
-    // wave 1 also forms the gates two chunks ahead, from alpha, beta, bw of token
-    // `lane` loaded a step earlier (this wave issues no other global loads in the
-    // loop, so waiting for them never waits for anything younger)
-    const int T = job.T;
-    const size_t a_base = (size_t)un.head * T;
-    const bool split = job.beta_w != job.beta;  // separate write strengths
-    float pa = 1.f, pb = 0.f, pw = 0.f;
-    auto load_ab = [&](int c) {
-        pa = ldtok(job.alpha + a_base, c, lane, T);
-        if (GDN) {
-            pb = ldtok(job.beta + a_base, c, lane, T);
-            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
-        }
-    };
-    if (vb == 1 && un.nb < un.ne) load_ab(un.nb);
 
     f32x16 qacc[2], xacc[2], oacc[2];
     for (int j = un.nb - 2; j < un.ne; ++j) {
@@ -622,12 +604,6 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
                 for (int tt = 0; tt < 2; ++tt) oacc[tt] = qacc[tt] * G.gam[32 * tt + perm5(l32)];
             }
         }
-        // gates of chunk j + 2 into slot (j + 2) % 3: that slot held chunk j - 1,
-        // which no wave reads after the previous step
-        if (vb == 1 && j + 2 < un.ne) {
-            form_gates(sm.gate[(j + 2) % 3], j + 2, pa, pb, split ? pw : pb, T, lane);
-            if (j + 3 < un.ne) load_ab(j + 3);
-        }
         lds_barrier();
         // ---- second half: U, O (staged for the load waves), the state update ----
         if (act) {
@@ -636,23 +612,28 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             const bool fast = __builtin_amdgcn_readfirstlane(G.fast);
             f32x16 uacc[2];
             if (GDN) {
-                // U = Tb V + Tbn X; T is lower triangular: token tile 0 contracts over
-                // tokens 0..31 only
-                // (two accumulators per token tile halve the dependent chains)
+                // U by block forward substitution over the two 32-token halves:
+                // U_top = Tb_00 V_top + Tbn_00 X_top and
+                // U_bot = Tb_11 V_bot + Tbn_11 X_bot + G U_top, with the diagonal blocks'
+                // factors and G = -D_bot A_bl (conjugated by the decays on fast chunks)
+                // from LDS (two accumulators per half halve the dependent chains)
                 f32x16 va[2] = {f32x16{}, f32x16{}}, xa[2] = {f32x16{}, f32x16{}};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
+                    const int t = kk >> 1;  // token half of this contraction step
                     const bf16x8 xo = sop(xacc, kk);
                     if (!un.erows) {  // rows of E: v = 0
                         const bf16x8 vo = v_operand(Vb, kk, 32 * vb, lane);
-                        va[1] = mfma32(lds8(&sm.Tb[(32 + l32) * LT + 16 * kk + 8 * h]), vo, va[1]);
-                        if (kk < 2) va[0] = mfma32(lds8(&sm.Tb[l32 * LT + 16 * kk + 8 * h]), vo, va[0]);
+                        va[t] = mfma32(lds8(&sm.Tb[(32 * t + l32) * LT + 16 * kk + 8 * h]), vo, va[t]);
                     }
-                    xa[1] = mfma32(lds8(&sm.Tbn[(32 + l32) * LT + 16 * kk + 8 * h]), xo, xa[1]);
-                    if (kk < 2) xa[0] = mfma32(lds8(&sm.Tbn[l32 * LT + 16 * kk + 8 * h]), xo, xa[0]);
+                    xa[t] = mfma32(lds8(&sm.Tbn[(32 * t + l32) * LT + 16 * kk + 8 * h]), xo, xa[t]);
                 }
                 uacc[0] = va[0] + xa[0];
-                uacc[1] = va[1] + xa[1];
+                f32x16 ub = va[1] + xa[1];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    ub = mfma32(lds8(&sm.Tb[(32 + l32) * LT + 16 * ks + 8 * h]), sop(uacc, ks), ub);
+                uacc[1] = ub;
             } else {
                 // U = V; on fast chunks U' = diag(dec) V
 #pragma unroll
@@ -816,11 +797,31 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
             *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + s0]) = pack8(-(d * g));
         }
     };
+    // wave 4 also forms the gates two chunks ahead, from alpha, beta, bw of token
+    // `lane`, loaded a step earlier and before the rows it stages: once those are
+    // staged, the gate loads are complete too
+    const size_t a_base = (size_t)un.head * T;
+    const bool split = job.beta_w != job.beta;  // separate write strengths
+    float pa = 1.f, pb = 0.f, pw = 0.f;
+    auto load_ab = [&](int c) {
+        pa = ldtok(job.alpha + a_base, c, lane, T);
+        if (GDN) {
+            pb = ldtok(job.beta + a_base, c, lane, T);
+            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
+        }
+    };
+    if (blk == 0 && un.nb < un.ne) load_ab(un.nb);
     for (int j = un.nb - 2; j < un.ne; ++j) {
         if (OUT && j - 1 >= un.nb) store_o(j - 1);
         if (GDN && j >= un.nb) convert(j);
         lds_barrier();
         if (j + 1 >= un.nb && j + 1 < un.ne) stage(j + 1);
+        // gates of chunk j + 2 into slot (j + 2) % 3: it held chunk j - 1, which no
+        // wave reads after the previous step
+        if (blk == 0 && j + 2 < un.ne) {
+            form_gates(sm.gate[(j + 2) % 3], j + 2, pa, pb, split ? pw : pb, T, lane);
+            if (j + 3 < un.ne) load_ab(j + 3);
+        }
         // the next chunk's rows overwrite the registers just staged: keep the
         // loads after the LDS writes (hoisted above them they would need a
         // second register set)
@@ -964,60 +965,47 @@ template <int MODE, int ROLE>
 __device__ __forceinline__ void aux_role(Smem& sm, const ChunkJob& job, const Unit& un) {
     constexpr bool GDN = MODE == 0;
     constexpr bool OUT = ROLE != kLeafAggregate;
-    (void)job;
     const int lane = threadIdx.x & 63, w = wave_id();
     const int l32 = lane & 31, h = lane >> 5;
+    (void)job;
     if (w == 6) {
         // the block of D above its diagonal (16x16, rows 0..15 x columns 16..31)
-        // and its transpose are zero for every chunk
+        // is zero for every chunk
         for (int i = lane; i < 2 * 256; i += 64) {
             const int b = i >> 8, r = (i >> 4) & 15, cc = i & 15;
             sm.D[b][r * LS + 16 + cc] = 0.f;
-            if (b == 0) sm.Dt[(16 + r) * LS + cc] = 0.f;
         }
     }
     for (int j = un.nb - 2; j < un.ne; ++j) {
         if (j >= un.nb) {
             const Gates& G = sm.gate[j % 3];
             if (GDN && w == 6) {
-                // T_bl = -D_bot A_bl D_top (rows 32 + i, columns jj), as
-                // T_bl^T = -D_top^T Z with Z = A_bl^T D_bot^T, split bf16; every LDS
-                // input is read up front
+                // G = -D_bot A_bl (bottom tokens x top tokens), computed as
+                // Z^T = A_bl^T D_bot^T in split bf16 (every LDS input read up front):
+                // lane l32 ends with row 32 + l32 of G, elements 8s2 .. 8s2+7 its
+                // columns 16 s2 + 8 h .. +7.  On fast chunks U_top and U_bot come
+                // scaled by dec, so G is conjugated: G_ts dec_t / dec_s = G_ts dec_t ec_s.
                 const float* Ab = sm.Ablt[j & 1];
                 const float* Db = sm.D[1];
-                const float* Dtt = sm.Dt;
                 const int pr = perm5(l32);
-                f32x8 ab[2], db[2], dt[2], wv[2], gv[2];
+                f32x8 ab[2], db[2], ev[2];
+                const bool fast = __builtin_amdgcn_readfirstlane(G.fast);
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     ab[kk] = ld8f(&Ab[pr * LS + 16 * kk + 8 * h]);
                     db[kk] = ld8f(&Db[l32 * LS + 16 * kk + 8 * h]);
-                    dt[kk] = ld8f(&Dtt[pr * LS + 16 * kk + 8 * h]);
-                    wv[kk] = ld8f(&G.bw[16 * kk + 8 * h]);
-                    gv[kk] = ld8f(&G.bg[16 * kk + 8 * h]);
+                    ev[kk] = fast ? ld8f(&G.ec[16 * kk + 8 * h]) : f32x8{1, 1, 1, 1, 1, 1, 1, 1};
                 }
-                // row 32 + l32 scaled by dec on fast chunks (U' = diag(dec) U)
-                const float rs = __builtin_amdgcn_readfirstlane(G.fast) ? G.dec[32 + l32] : 1.f;
+                const float rs = fast ? -G.dec[32 + l32] : -1.f;
                 f32x16 z = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) z = mfma_split(ab[kk], db[kk], z);
-                f32x16 tacc = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const f32x8 zb = kk ? __builtin_shufflevector(z, z, 8, 9, 10, 11, 12, 13, 14, 15)
-                                        : __builtin_shufflevector(z, z, 0, 1, 2, 3, 4, 5, 6, 7);
-                    tacc = mfma_split(dt[kk], zb, tacc);
-                }
-                // lane l32: row 32 + l32 of T (physical row 32 + perm5(l32)); elements
-                // 8s2 .. 8s2+7: columns 16 s2 + 8 h .. +7 of -T_bl
                 const int prow = 32 + perm5(l32);
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const int c0 = 16 * s2 + 8 * h;
-                    const f32x8 tn = (s2 ? __builtin_shufflevector(tacc, tacc, 8, 9, 10, 11, 12, 13, 14, 15)
-                                         : __builtin_shufflevector(tacc, tacc, 0, 1, 2, 3, 4, 5, 6, 7)) * rs;
-                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + c0]) = pack8(-(tn * wv[s2]));
-                    *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + c0]) = pack8(tn * gv[s2]);
+                    const f32x8 zs = s2 ? __builtin_shufflevector(z, z, 8, 9, 10, 11, 12, 13, 14, 15)
+                                        : __builtin_shufflevector(z, z, 0, 1, 2, 3, 4, 5, 6, 7);
+                    *reinterpret_cast<uint4*>(&sm.Tb[prow * LT + 16 * s2 + 8 * h]) = pack8(zs * ev[s2] * rs);
                 }
             }
             if (OUT && w == 7) {
