@@ -45,8 +45,8 @@
 //               gates of chunk j+2 (a wave scan of ln alpha), then chunk j+2's
 //               rows loaded into registers (coalesced 16-byte loads).
 //   wave 2      first half: chunk j+1's two diagonal k-Gram tiles.
-//   wave 3      first half: chunk j+1's off-diagonal k-Gram tile and chunk j's
-//               score tile (0,0).
+//   wave 3      first half: chunk j's score tile (0,0); second half: chunk
+//               j+1's off-diagonal k-Gram tile.
 //   wave 6      first half: G = -D_1 A_bl of chunk j by a split-bf16 product
 //               (hi/lo parts, three MFMAs per product), stored as bf16 in
 //               Tb's lower-left block; second half: D_0 of chunk j+1 (16x16
@@ -115,7 +115,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // scaled by dec on the vector units.
 constexpr float kSpan = 100.f;
 struct alignas(16) Gates {
-    float gam[C], dec[C], bw[C], bg[C], gl[C], gb[C], el[C], fl[C], ebt[C], ec[C];
+    float gam[C], dec[C], bw[C], bg[C], gl[C], gb[C], fl[C], ebt[C], ec[C];
     int fast, pad[3];  // (16-byte size: every slot's arrays take 16-byte reads)
 };
 static_assert(sizeof(Gates) % 16 == 0, "gate slots must stay 16-byte aligned");
@@ -391,7 +391,6 @@ __device__ __forceinline__ void form_gates(Gates& G, int c, float pa, float pb, 
     G.bg[lane] = g.bg;
     G.gl[lane] = g.gl;
     G.gb[lane] = g.gb;
-    G.el[lane] = g.el;
     G.fl[lane] = g.fl;
     G.ebt[lane] = g.ebt;
     G.ec[lane] = g.ec;
@@ -833,8 +832,9 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
 }
 
 // ----------------------------------------------------------------------------
-// k-Gram waves (2, 3): chunk j+1's k-Gram tiles; wave 3 also chunk j's score
-// tile (0,0)
+// k-Gram waves (2, 3): chunk j+1's k-Gram tiles (wave 2 the diagonal ones in
+// the first half, wave 3 the off-diagonal one in the second); wave 3 also chunk
+// j's score tile (0,0)
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
@@ -887,24 +887,29 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
 
     for (int j = un.nb - 2; j < un.ne; ++j) {
         constexpr int st = 0;
-        const int c = j + 1;  // chunk whose gates, k-Gram and diagonal T blocks are built
-        // wave 3: score tile (0,0) of chunk j
-        bool score = OUT && blk == 1 && j >= un.nb;
-        // ---- first half ----
-        if (GDN && c >= un.nb && c < un.ne) {
+        const int c = j + 1;  // chunk whose k-Gram tiles are built
+        const bool build = GDN && c >= un.nb && c < un.ne;
+        // mask weights of chunk c (its gates were formed two steps ago)
+        auto weights = [&](bool& fast, const float*& ws, const float*& wt) {
             const Gates& G = sm.gate[c % 3];
-            const bool fast = __builtin_amdgcn_readfirstlane(G.fast);
-            const float* ws = fast ? G.fl : G.gl;
-            const float* wt = fast ? G.ebt : G.gb;
-            f32x4 wt1[4];
+            fast = __builtin_amdgcn_readfirstlane(G.fast);
+            ws = fast ? G.fl : G.gl;
+            wt = fast ? G.ebt : G.gb;
+        };
+        // ---- first half: wave 2 the diagonal k-Gram tiles of chunk c (the solve
+        // reads them in the second half); wave 3 score tile (0,0) of chunk j ----
+        if (blk == 0) {
+            if (build) {
+                bool fast;
+                const float *ws, *wt;
+                weights(fast, ws, wt);
+                f32x4 wt0[4], wt1[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
-            const float ws0 = ws[l32];
-            if (blk == 0) {
-                f32x4 wt0[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) wt0[b] = *reinterpret_cast<const f32x4*>(&wt[8 * b + 4 * h]);
-                const float ws1 = ws[32 + l32];
+                for (int b = 0; b < 4; ++b) {
+                    wt0[b] = *reinterpret_cast<const f32x4*>(&wt[8 * b + 4 * h]);
+                    wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
+                }
+                const float ws0 = ws[l32], ws1 = ws[32 + l32];
                 f32x16 a0 = f32x16{}, a1 = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
@@ -913,46 +918,36 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
                 }
                 gram_mask(a0, 0, 0, fast, ws0, wt0, sm.At[0]);
                 gram_mask(a1, 1, 1, fast, ws1, wt1, sm.At[1]);
-            } else if (score) {
-                // the off-diagonal k-Gram tile and score tile (0,0) of chunk j as two
-                // interleaved chains (the score operands from LDS, two steps ahead)
-                const uint16_t* Kb = sm.K[j & 1];
-                bf16x8 sq[3], sk[3];
-                auto fetch = [&](int k) {
-                    sq[k % 3] = score_q(sm, 0, k, l32, h);
-                    sk[k % 3] = score_k(Kb, 0, k, l32, h);
-                };
-                fetch(0);
-                fetch(1);
-                f32x16 a = f32x16{}, sc = f32x16{};
+            }
+            // chunk c + 1 goes into the registers just used: keep the loads after
+            // their last use (hoisted above it they would need a second set)
+            __builtin_amdgcn_sched_barrier(0);
+            if (GDN && c + 1 < un.ne) load(c + 1);
+        } else if (OUT && j >= un.nb) {
+            const f32x16 sc = mfma_chain2<8>([&](int k) { return score_k(sm.K[j & 1], 0, k, l32, h); },
+                                             [&](int k) { return score_q(sm, 0, k, l32, h); }, f32x16{});
+            score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
+        }
+        lds_barrier();
+        // ---- second half: wave 3 the off-diagonal k-Gram tile of chunk c into slot
+        // c % 2 (wave 6 reads it in the next step), then chunk c + 1's rows ----
+        if (blk == 1) {
+            if (build) {
+                bool fast;
+                const float *ws, *wt;
+                weights(fast, ws, wt);
+                f32x4 wt1[4];
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    if (kk + 2 < 8) fetch(kk + 2);
-                    __builtin_amdgcn_sched_barrier(0);
-                    a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
-                    sc = mfma32(sk[kk % 3], sq[kk % 3], sc);
-                }
-                gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
-                score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
-                score = false;
-            } else {
+                for (int b = 0; b < 4; ++b) wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
+                const float ws0 = ws[l32];
                 f32x16 a = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
                 gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (GDN && c + 1 < un.ne) load(c + 1);
         }
-        if (score) {
-            const f32x16 sc = mfma_chain2<8>([&](int k) { return score_k(sm.K[j & 1], 0, k, l32, h); },
-                                             [&](int k) { return score_q(sm, 0, k, l32, h); }, f32x16{});
-            score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
-        }
-        // chunk c + 1 goes into the registers just used: keep the loads after
-        // their last use (hoisted above it they would need a second set)
-        __builtin_amdgcn_sched_barrier(0);
-        if (GDN && c + 1 < un.ne) load(c + 1);
-        lds_barrier();
-        // (second half: nothing for these waves)
         lds_barrier();
     }
 }
