@@ -250,7 +250,7 @@ int decode_step(int mode, int dtype, int N, int dk, int dv, const void* q, const
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);
     if (N < 1 || dk < 1 || dv < 1) return fail(SCAN_EINVAL, "N, dk, dv must be >= 1 (got %d, %d, %d)", N, dk, dv);
     if (!gds::decode_supported(dk)) return fail(SCAN_EUNSUPPORTED, "decode_step supports dk in {16,32,64,128} (got %d)", dk);
-    if ((int64_t)N * ((dv + 127) / 128) > INT32_MAX) return fail(SCAN_EINVAL, "N*dv too large");
+    if ((int64_t)N * ((dv + 31) / 32) > INT32_MAX) return fail(SCAN_EINVAL, "N*dv too large");  // one workgroup per 32 rows
     if (!q || !k || !v || !alpha || !S || !o) return fail(SCAN_EINVAL, "q, k, v, alpha, S and o must be non-null");
     if (!gla_mode(mode) && !beta) return fail(SCAN_EINVAL, "the gated-delta modes need beta");
     if (gla_mode(mode) && beta) return fail(SCAN_EINVAL, "the GLA modes take no beta (pass NULL)");
