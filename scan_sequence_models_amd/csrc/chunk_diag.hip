@@ -215,7 +215,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     E* __restrict__ o, float* __restrict__ ST) {
     constexpr bool GDN = MODE == 0;
-    constexpr int NJ = DK / 32;              // 32-column tiles of a key-wide row
+    constexpr int NJ = DK / 32;
+    // bf16 data: the products in split bf16 (about 16 significant bits each)
+    constexpr bool SPLIT = std::is_same<E, uint16_t>::value;              // 32-column tiles of a key-wide row
     constexpr int NQ = kC * DK / kThreads;   // tokens per thread, all of one key channel
     constexpr int NR = kThreads / DK;        // runs of NQ tokens per chunk
     constexpr int NV = kC * kSL / kThreads;  // value elements per thread and chunk
@@ -293,13 +295,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // c += A B^T over `steps` key steps from k0, A and B both read along key rows
     // (A: 32 token rows, B: 32 state rows, row stride L1)
     auto rows_dot = [&](const float* A, const float* B, auto steps, int k0, f32x16 c) {
-        return chain<decltype(steps)::value>([&](int s) { return A[l32 * L1 + 2 * (k0 + s) + kg]; },
+        return chain_t<SPLIT, decltype(steps)::value>([&](int s) { return A[l32 * L1 + 2 * (k0 + s) + kg]; },
                                              [&](int s) { return B[l32 * L1 + 2 * (k0 + s) + kg]; }, c);
     };
     using Full = std::integral_constant<int, DK / 2>;
     // c += P U or T X on value columns 32 I ..: B read along token rows of Us
     auto tok_dot = [&](const float* A, int I, f32x16 c) {
-        return chain<kC / 2>([&](int s) { return A[l32 * kLT + 2 * s + kg]; },
+        return chain_t<SPLIT, kC / 2>([&](int s) { return A[l32 * kLT + 2 * s + kg]; },
                              [&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; }, c);
     };
 
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         };
         auto s_done = [&](int tl, f32x16 c) {
             const int I = tl / NJ, J = tl - I * NJ;
-            c = chain<kC / 2>([&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; },
+            c = chain_t<SPLIT, kC / 2>([&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; },
                               [&](int s) { return KS[(2 * s + kg) * L1 + 32 * J + l32]; }, c);
             const float f = sOut[32 * J + l32];
 #pragma unroll

@@ -1,12 +1,13 @@
-// mfma_f32.hpp -- float32 MFMA tiles fed from LDS (v_mfma_f32_32x32x2f32).
+// mfma_f32.hpp -- float32 products on the MFMA units, fed from LDS: on the
+// float32 MFMA (v_mfma_f32_32x32x2f32), or in split bf16 on the bf16 MFMA.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "common.hpp"
 
 namespace gds {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One 16x16x4 step: lane (16 g + n16) gives A[n16][g] and B[g][n16]; the result
 // holds rows 4 g .. 4 g + 3 of column n16.
@@ -44,6 +45,65 @@ __device__ __forceinline__ f32x16 chain(FA A, FB B, f32x16 c) {
         b1 = b2;
     }
     return c;
+}
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// hi + lo parts of 8 floats in bf16: hi = RNE(x), lo = RNE(x - hi).  The
+// product of two split operands as hi*hi + hi*lo + lo*hi misses the lo*lo term
+// and the rounding of each lo, both within about 2^-17 of the product.
+__device__ __forceinline__ void split_bf16(const f32x8& x, bf16x8& hi, bf16x8& lo) {
+    hi = __builtin_convertvector(x, bf16x8);
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), bf16x8);
+}
+
+// The product of chain<STEPS> (STEPS a multiple of 8) in split bf16 on the
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16, 8 times the k of a float32 step in half
+// its cycles): a lane's operands of steps 8i .. 8i+7 make its eight values of
+// one 32x32x16 step.  Which k a value stands for does not matter as long as A
+// and B agree, so A(s) and B(s) are the same accessors as for chain.  A group's
+// operands are read one group ahead of its products.
+template <int STEPS, class FA, class FB>
+__device__ __forceinline__ f32x16 chain_split(FA A, FB B, f32x16 c) {
+    static_assert(STEPS % 8 == 0, "groups of eight steps");
+    constexpr int G = STEPS / 8;
+    f32x8 a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = A(j);
+        b[j] = B(j);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        f32x8 an = a, bn = b;
+        if (i + 1 < G) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                an[j] = A(8 * (i + 1) + j);
+                bn[j] = B(8 * (i + 1) + j);
+            }
+        }
+        bf16x8 ah, al, bh, bl;
+        split_bf16(a, ah, al);
+        split_bf16(b, bh, bl);
+        __builtin_amdgcn_sched_barrier(0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        a = an;
+        b = bn;
+    }
+    return c;
+}
+
+// chain in float32 or, with SPLIT and whole groups of eight steps, in split bf16.
+template <bool SPLIT, int STEPS, class FA, class FB>
+__device__ __forceinline__ f32x16 chain_t(FA A, FB B, f32x16 c) {
+    if constexpr (SPLIT && STEPS % 8 == 0)
+        return chain_split<STEPS>(A, B, c);
+    else
+        return chain<STEPS>(A, B, c);
 }
 
 }  // namespace gds

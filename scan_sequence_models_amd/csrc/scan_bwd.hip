@@ -37,6 +37,8 @@
 //     are sums over value rows and are written as per-slice partials;
 //   bwd_reduce_kernel: the sum over slices and dalpha = d ln alpha / alpha.
 // Products are 32x32 tiles on the float32 MFMA (v_mfma_f32_32x32x2f32).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_f32.hpp"
@@ -179,6 +181,8 @@ __device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* b
 template <int MODE, int DK, typename E>
 __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     constexpr bool GDN = MODE == 0;
+    // bf16 data: the products in split bf16 (about 16 significant bits each)
+    constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
     constexpr int NJ = DK / 32;
     constexpr int L1 = DK + 1;
     __shared__ float Ks[kC * L1];
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
         if constexpr (GDN) {
             if (w == 0) {  // B = strict_lower(Gamma o K K^T)
                 auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
-                const f32x16 c = chain<DK / 2>(kr, kr, f32x16{});
+                const f32x16 c = chain_t<SPLIT, DK / 2>(kr, kr, f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) c[e] = bw[row(e)] * Us[row(e) * LV + 32 * I + l32];
                 const float nbg = -bg[l32];
-                c = chain<DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
+                c = chain_t<SPLIT, DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
                                   [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; }, c);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
                 solve_unit_lower(Bm, bet, Tm, lane);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
-                    const f32x16 c = chain<kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
+                    const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
                                                    [&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
                                                    f32x16{});
 #pragma unroll
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = gC[0] * Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
-            c = chain<kC / 2>([&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
+            c = chain_t<SPLIT, kC / 2>([&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
                               [&](int s) { return Dd[2 * s + kg] * Ks[(2 * s + kg) * L1 + 32 * Jt + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
@@ -311,6 +315,8 @@ template <int MODE, int DK, typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_chunk_kernel(
     BwdJob J) {
     constexpr bool GDN = MODE == 0;
+    // bf16 data: the products in split bf16 (about 16 significant bits each)
+    constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
     constexpr int NJ = DK / 32;  // key-column tiles: wave w < NJ owns dq and dk tile w
     constexpr int L1 = DK + 1;
     __shared__ float Qs[kC * L1];
@@ -441,14 +447,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 1: B, P, X; the owners start dQ = diag(gamma) dO S (+ its dg share)
         if (GDN && w == 0) {
             auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
-            const f32x16 c = chain<DK / 2>(kr, kr, f32x16{});
+            const f32x16 c = chain_t<SPLIT, DK / 2>(kr, kr, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
                 Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
             }
         } else if (w == 1) {
-            const f32x16 c = chain<DK / 2>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
+            const f32x16 c = chain_t<SPLIT, DK / 2>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
                                            [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int I = w - 2;
             // (K S^T)^T = S K^T with the token along the lanes: X_t = beta_t V_t - beta_t gamma_t (K S^T)_t
             // is written row by row, and the tile serves <dX_t, (K S^T)_t> in phase 5 as an in-lane sum
-            ksT = chain<DK / 2>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
+            ksT = chain_t<SPLIT, DK / 2>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
                                 [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
             const float b = bw[l32], nbg = -bg[l32];
 #pragma unroll
@@ -470,14 +476,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
             const int I = w - 2;
             const float dd = Dd[l32];
-            const f32x16 c = chain<DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
+            const f32x16 c = chain_t<SPLIT, DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
                                            [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
         if (w < NJ) {
             const float gl = gam[l32];
-            accQ = chain<kSL / 2>([&](int s) { return gl * dOs[l32 * LV + 2 * s + kg]; },
+            accQ = chain_t<SPLIT, kSL / 2>([&](int s) { return gl * dOs[l32 * LV + 2 * s + kg]; },
                                   [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
             f32x16 x;
 #pragma unroll
@@ -491,7 +497,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 solve_unit_lower(Bm, bet, Tm, lane);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
-                    const f32x16 c = chain<kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
+                    const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
                                                    [&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
                                                    f32x16{});
 #pragma unroll
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             } else if (w < 3) {
                 const int I = w - 1;
                 const float dd = Dd[l32];
-                const f32x16 c = chain<DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
+                const f32x16 c = chain_t<SPLIT, DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
                                                [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
                                                f32x16{});
 #pragma unroll
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 3: dP (waves 0 and 3 both form it: wave 0 writes dP * Gamma, wave 3 the
         // row and column sums of dP * P), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
         if (w == 0 || w == 3) {
-            const f32x16 c = chain<kSL / 2>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
+            const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
                                             [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
             if (w == 0) {
 #pragma unroll
@@ -545,13 +551,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
-            c = chain<kC / 2>([&](int s) { return Pm[(2 * s + kg) * LM + l32]; },
+            c = chain_t<SPLIT, kC / 2>([&](int s) { return Pm[(2 * s + kg) * LM + l32]; },
                               [&](int s) { return dOs[(2 * s + kg) * LV + 32 * I + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
         if (w < NJ) {  // dKd = U dS'
-            const f32x16 c = chain<kSL / 2>([&](int s) { return Us[l32 * LV + 2 * s + kg]; },
+            const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return Us[l32 * LV + 2 * s + kg]; },
                                             [&](int s) { return dSs[(2 * s + kg) * L1 + 32 * w + l32]; }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) accK[e] += Dd[row(e)] * c[e];
@@ -561,7 +567,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // <dX_t, V_t> is an in-lane sum; dX replaces V row by row); the owners' dQ, dK += dQK parts
         if (GDN && (w == 1 || w == 2)) {
             const int I = w - 1;
-            const f32x16 c = chain<kC / 2>([&](int s) { return dUs[(2 * s + kg) * LV + 32 * I + l32]; },
+            const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return dUs[(2 * s + kg) * LV + 32 * I + l32]; },
                                            [&](int s) { return Tm[(2 * s + kg) * LM + l32]; }, f32x16{});
             float db = 0.f;
 #pragma unroll
@@ -580,9 +586,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         if (w < NJ) {
-            accQ = chain<kC / 2>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
+            accQ = chain_t<SPLIT, kC / 2>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
                                  [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
-            accK = chain<kC / 2>([&](int s) { return dQKm[(2 * s + kg) * LM + l32]; },
+            accK = chain_t<SPLIT, kC / 2>([&](int s) { return dQKm[(2 * s + kg) * LM + l32]; },
                                  [&](int s) { return Qs[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
         }
         __syncthreads();
@@ -592,7 +598,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // dRw (owners), dS
         if constexpr (GDN) {
             if (w < 2) {
-                const f32x16 c = chain<kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
+                const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
                                                 [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
                 if (w == 0) {
 #pragma unroll
@@ -626,7 +632,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             }
             if (w < NJ) {  // dRw = -dX S
-                const f32x16 c = chain<kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
+                const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
                                                 [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; },
                                                 f32x16{});
 #pragma unroll
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
             // the two products as one chain over 2 C (GDN) or C tokens
             constexpr int H2 = kC / 2;
-            c = chain<GDN ? kC : H2>(
+            c = chain_t<SPLIT, GDN ? kC : H2>(
                 [&](int s) {
                     const int t = 2 * (s % H2) + kg;
                     return s < H2 ? dOs[t * LV + 32 * I + l32] : -Vs[t * LV + 32 * I + l32];
@@ -672,7 +678,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 6: dK += (dKK + dKK^T) K; partial dq, dk; dg -> d ln alpha, dbeta
         if (w < NJ) {
             if constexpr (GDN)
-                accK = chain<kC / 2>(
+                accK = chain_t<SPLIT, kC / 2>(
                     [&](int s) { return dKKm[l32 * LM + 2 * s + kg] + dKKm[(2 * s + kg) * LM + l32]; },
                     [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
 #pragma unroll
