@@ -12,7 +12,7 @@ float64 CPU oracle timed on a bounded sample of the same workload.
 Other workloads: --workload gla-b4h8t4096 (gated linear attention),
 long-b2h8t262144 (the long-sequence path), decode-4096x100 (decode_step over
 4096 states, one timed step per token), prism-b8h16t8192-l2 (the PRISM layer:
-prism_expand, then the split-strength scan of the 3x longer element stream) and
+the factor rows, then the 3x longer element stream scanned in place) and
 lact-b8h16t8192-m2048 (lact_fwd: the large-chunk fast-weight update, chunks of
 2048 tokens), gdn-diag-b8h16t8192 (the gated delta rule with one decay per
 key channel) and gdn-bwd-b8h16t8192 (scan_bwd: the gradient of the training
@@ -341,20 +341,6 @@ def bench_decode(args, w):
     print(json.dumps(result), flush=True)
 
 
-def prism_expand_bytes(w) -> int:
-    """Algorithmic HBM bytes of one prism_expand call: q, k, v, x read once and
-    the G = L+1 element stream (q2, k2, v2 in the data type; alpha2 and the two
-    strength planes in fp32) written once; alpha, beta, beta^(l) read once; the
-    per-head weights (L (dk + dv) dv elements, conv W dv fp32) read once."""
-    es = 2 if w.dtype == "bf16" else 4
-    L, G = w.prism_steps, w.prism_steps + 1
-    ht = w.B * w.H * w.T
-    b = ht * (2 * w.dk + 2 * w.dv) * es + ht * 4 * (2 + L)
-    b += ht * G * ((2 * w.dk + w.dv) * es + 3 * 4)
-    b += w.H * (L * (w.dk + w.dv) * w.dv * es + w.prism_window * w.dv * 4)
-    return b
-
-
 def cpu_baseline_prism(w, heads: int):
     """The float64 PRISM oracle (write factors, expansion, token recurrence) on
     the first ``heads`` heads of ``w``, full length each."""
@@ -390,8 +376,26 @@ def cpu_baseline_prism(w, heads: int):
     }
 
 
+def prism_layer_bytes(w) -> int:
+    """Algorithmic HBM bytes of one PRISM layer on the in-place path
+    (prism_scan): q, k, v, x read and o written once (dtype); alpha, beta and
+    beta^(l) read once (fp32); the factor rows k^(l), delta^(l) written once and
+    read once (dtype); the per-head weights (L (dk + dv) dv elements, conv
+    W dv fp32) read once; S0 read and S_T written once (fp32)."""
+    es = 2 if w.dtype == "bf16" else 4
+    L = w.prism_steps
+    ht = w.B * w.H * w.T
+    b = ht * (2 * w.dk + 3 * w.dv) * es + ht * 4 * (2 + L)
+    b += 2 * ht * L * (w.dk + w.dv) * es
+    b += w.H * (L * (w.dk + w.dv) * w.dv * es + w.prism_window * w.dv * 4)
+    b += 2 * w.B * w.H * w.dv * w.dk * 4
+    return b
+
+
 def bench_prism(args, w):
-    """The PRISM layer: prism_expand then scan_fwd over the expanded stream."""
+    """The PRISM layer: prism_scan (the factor rows, then the element stream
+    scanned in place); the materialised-stream path (prism_expand, then scan_fwd
+    over the stream) is timed beside it for comparison."""
     import numpy as np
     import torch
 
@@ -405,61 +409,74 @@ def bench_prism(args, w):
     log(f"bench: generating {w.name} (B={B} H={H} T={T} d={w.dk} L={L})")
     b = I.batch_inputs(w, threads=16)
     bf = w.dtype == "bf16"
-
-    def up(x, bf16=False):
-        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-        return t.to(torch.bfloat16) if bf16 else t
-
-    q, k, v = up(b.q, bf), up(b.k, bf), up(b.v, bf)
-    alpha, beta, S0 = up(b.alpha), up(b.beta), up(b.S0)
-    del b
     xs = np.empty((B, H, T, w.dv), np.float32)
     bl = np.empty((B, H, T, L), np.float32)
     for bb in range(B):
         for hh in range(H):
             xs[bb, hh], bl[bb, hh] = I.prism_token_inputs(w, bb, hh)
-    x, beta_l = up(xs, bf), up(bl)
-    del xs, bl
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    def rolled(x, r, bf16=False):
+        y = np.roll(x.reshape(B * H, *x.shape[2:]), r, axis=0).reshape(x.shape)
+        return up(y, bf16)
+
+    # input sets rotated across the timed calls (heads rolled), past the MALL
+    es = 2 if bf else 4
+    set_bytes = B * H * T * ((2 * w.dk + 2 * w.dv) * es + 4 * (2 + L))
+    R = args.rotate or rotation_sets(set_bytes, 3, 2 * MALL_BYTES)
+    sets = []
+    for r in range(R):
+        sets.append(dict(q=rolled(b.q, r, bf), k=rolled(b.k, r, bf), v=rolled(b.v, r, bf),
+                         alpha=rolled(b.alpha, r), beta=rolled(b.beta, r), x=rolled(xs, r, bf),
+                         beta_l=rolled(bl, r)))
+    S0 = up(b.S0)
+    del b, xs, bl
     wts = [I.prism_weights(w, hh) for hh in range(H)]
     conv = up(np.stack([p.conv for p in wts]))
     Wk = up(np.stack([p.Wk for p in wts]), bf)
     Wp = up(np.stack([p.Wp for p in wts]), bf)
+    dt = sets[0]["q"].dtype
+    o = torch.empty((B, H, T, w.dv), dtype=dt, device=dev)
+    ST = torch.empty((B, H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gds.prism_scan_workspace_size(gds.SCAN_BF16 if bf else gds.SCAN_F32,
+                                                   B, H, T, w.dk, w.dv, L),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        z = sets[i % R]
+        gds.prism_scan(z["q"], z["k"], z["v"], z["alpha"], z["beta"], z["x"], z["beta_l"], conv, Wk, Wp,
+                       S0, o=o, ST=ST, workspace=ws)
+
+    copy_probe(args.copy_probe_mib, dev)
+    warm_calls = warm_up(step, args.warmup, args.warmup_ms)
+    span_ms, wall = timed(step, args.steps, dev)
+    ms_per_step = span_ms / args.steps
+    # the materialised-stream path, for comparison (its own buffers)
     T2 = T * G
-    dt = q.dtype
     stream_bufs = (torch.empty((B, H, T2, w.dk), dtype=dt, device=dev),
                    torch.empty((B, H, T2, w.dk), dtype=dt, device=dev),
                    torch.empty((B, H, T2, w.dv), dtype=dt, device=dev),
                    torch.empty((B, H, T2), dtype=torch.float32, device=dev),
                    torch.empty((2, B, H, T2), dtype=torch.float32, device=dev))
     o2 = torch.empty((B, H, T2, w.dv), dtype=dt, device=dev)
-    ST = torch.empty((B, H, w.dv, w.dk), dtype=torch.float32, device=dev)
-    q2, k2, v2, a2, b2 = stream_bufs
+    del ws
 
-    def expand():
-        gds.prism_expand(q, k, v, alpha, beta, x, beta_l, conv, Wk, Wp, out=stream_bufs)
+    def stream_step(i):
+        z = sets[i % R]
+        gds.prism_expand(z["q"], z["k"], z["v"], z["alpha"], z["beta"], z["x"], z["beta_l"], conv, Wk, Wp,
+                         out=stream_bufs)
+        gds.scan_fwd(*stream_bufs, S0, chunk=w.chunk, o=o2, ST=ST)
 
-    def scan():
-        gds.scan_fwd(q2, k2, v2, a2, b2, S0, chunk=w.chunk, o=o2, ST=ST)
-
-    def step():
-        expand()
-        scan()
-
-    copy_probe(args.copy_probe_mib, dev)
-    warm_calls = warm_up(lambda i: step(), args.warmup, args.warmup_ms)
-    span_ms, wall = timed(lambda i: step(), args.steps, dev)
-    ms_per_step = span_ms / args.steps
-    # each kernel alone, back to back, for the per-kernel rooflines
-    exp_ms = timed(lambda i: expand(), args.steps, dev)[0] / args.steps
-    scan_ms = timed(lambda i: scan(), args.steps, dev)[0] / args.steps
-    log(f"bench: {args.steps} layer steps, {ms_per_step:.4f} ms per step "
-        f"(prism_expand {exp_ms:.4f} ms, scan {scan_ms:.4f} ms alone), wall {wall * 1e3:.1f} ms")
-    ws = w.replace(T=T2, mode="gdn_ew")
-    scan_alg = scan_bytes(ws)
+    warm_up(stream_step, 2, args.warmup_ms / 4)
+    stream_ms = timed(stream_step, args.steps, dev)[0] / args.steps
+    log(f"bench: {args.steps} layer steps, {ms_per_step:.4f} ms per step in place "
+        f"({stream_ms:.4f} ms through the materialised stream), wall {wall * 1e3:.1f} ms")
+    alg = prism_layer_bytes(w)
     scan_flops_alg_ = scan_flops_alg(w.replace(T=T2))
-    exp_alg = prism_expand_bytes(w)
     src_scan = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_bf16.hip")
-    src_exp = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "prism.hip")
     result = {
         "metric": "tokens/s PRISM layer fwd (rank-L write, L=2; H=16, d=128, T=8192); "
                   "% MFMA / HBM roofline",
@@ -474,34 +491,24 @@ def bench_prism(args, w):
         "vs_baseline": None,
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "mode": "gdn_ew (PRISM)", "B": B, "H": H, "T": T,
-                   "elements_per_token": G, "L": L, "W": w.prism_window, "dk": w.dk, "dv": w.dv,
-                   "chunk": w.chunk, "io_dtype": w.dtype, "state_dtype": "f32",
-                   "warmup_calls_run": warm_calls},
+        "config": {"workload": w.name, "mode": "gdn_ew (PRISM, element stream read in place)", "B": B,
+                   "H": H, "T": T, "elements_per_token": G, "L": L, "W": w.prism_window, "dk": w.dk,
+                   "dv": w.dv, "chunk": w.chunk, "io_dtype": w.dtype, "state_dtype": "f32",
+                   "rotated_input_sets": R, "rotated_bytes": R * set_bytes, "warmup_calls_run": warm_calls},
         "roofline": {
             "bound": "hbm",
-            "achieved": scan_alg / (scan_ms / 1e3) / 1e9,
+            "achieved": alg / (ms_per_step / 1e3) / 1e9,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": scan_alg / (scan_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": measured_traffic(src_scan, f"chunk_mfma_{w.name}_traffic.txt"),
-            "kernel": "chunk_mfma_kernel (expanded stream)",
-            "algorithmic_bytes_per_launch": scan_alg,
-            "kernel_ms": scan_ms,
-            "alg_tflops": scan_flops_alg_ / (scan_ms / 1e3) / 1e12,
-            "alg_mfma_frac": scan_flops_alg_ / (scan_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
+            "frac": alg / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "the layer: prism_mfma_kernel (factor rows) + chunk_mfma_kernel (in-place stream)",
+            "algorithmic_bytes_per_launch": alg,
+            "kernel_ms": ms_per_step,
+            "alg_tflops": scan_flops_alg_ / (ms_per_step / 1e3) / 1e12,
+            "alg_mfma_frac": scan_flops_alg_ / (ms_per_step / 1e3) / 1e12 / BF16_MFMA_PEAK_TFS,
         },
-        "expand_roofline": {
-            "bound": "hbm",
-            "achieved": exp_alg / (exp_ms / 1e3) / 1e9,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": exp_alg / (exp_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": measured_traffic(src_exp, f"prism_expand_{w.name}_traffic.txt"),
-            "kernel": "prism_mfma_kernel",
-            "algorithmic_bytes_per_launch": exp_alg,
-            "kernel_ms": exp_ms,
-        },
+        "materialised_stream_ms": stream_ms,
     }
     if not args.no_cpu_baseline:
         heads = min(args.cpu_heads, 16)

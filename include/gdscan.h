@@ -228,6 +228,36 @@ int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
                  void *q2, void *k2, void *v2, float *alpha2, float *beta2, void *stream);
 
 /*
+ * The PRISM layer's scan without a materialised element stream: the element
+ * stream that prism_expand would write (same arithmetic, same element order)
+ * is scanned in place.  The factor rows k^(l), delta^(l) go to the workspace;
+ * the scan reads every other element field from the token arrays (element
+ * t(L+1): k_t, v_t, alpha_t, beta_t; elements t(L+1)+l: the factor rows, alpha 1,
+ * erase 0, write beta_l[t, l-1]), reads q_t for element t(L+1)+L only, and
+ * writes o_t (that element's output) once per token ("PRISM: Parallel Residual
+ * Iterative Sequence Model", gist.science explainer, technical summary 2.1-2.2;
+ * PRISM article, banbantang.com, section 3(3): the L-step write in one pass).
+ *
+ *   inputs as prism_expand, plus S0 [B, H, dv, dk] float32 or NULL (zero state)
+ *   o    : [B, H, T, dv] bfloat16, o_t = S at token t's last element times q_t
+ *   ST   : [B, H, dv, dk] float32 final state, or NULL; may equal S0
+ *   workspace: prism_scan_workspace_size(...) bytes (B H T L (dk + dv) bf16
+ *          factor rows), 256-byte aligned; NULL when that is 0 (L = 0).
+ * Supported: dtype SCAN_BF16, dk = dv = 128, 0 <= L <= 8 (L = 0 is the gated
+ * delta rule), 1 <= W <= 8, T (L + 1) < 2^31.  The result equals scan_fwd
+ * (SCAN_GDN_EW) over prism_expand's stream bit for bit.  Returns SCAN_OK or an
+ * error status; prism_scan_workspace_size returns (size_t)-1 for invalid or
+ * unsupported arguments.
+ */
+size_t prism_scan_workspace_size(int dtype, int B, int H, int T, int dk, int dv, int L);
+int prism_scan(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
+               const void *q, const void *k, const void *v, const void *x,
+               const float *alpha, const float *beta, const float *beta_l,
+               const float *conv, const void *Wk, const void *Wp,
+               const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
  * Gradient of scan_fwd (reverse mode through the chunkwise form of the scan;
  * the prefix-scan notes, key design 2, define the affine state update it
  * differentiates).  For incoming gradients dO (at o) and dST (at S_T) it

@@ -11,6 +11,7 @@ loaded on first use.
 from ._lib import (  # noqa: F401
     PATHS, SCAN_BF16, SCAN_F32, SCAN_GDN, SCAN_GDN_DIAG, SCAN_GDN_EW, SCAN_GLA, SCAN_GLA_DIAG,
     ScanError, decode_step,
-    last_error, lact_fwd, lact_fwd_workspace_size, lib, prism_expand, prism_scan_fwd, scan_bwd,
+    last_error, lact_fwd, lact_fwd_workspace_size, lib, prism_expand, prism_scan, prism_scan_fwd,
+    prism_scan_workspace_size, scan_bwd,
     scan_bwd_workspace_size, scan_fwd, scan_fwd_noalloc, scan_fwd_workspace_size, version,
 )

@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.lact_fwd_workspace_size.restype = sz
         L.lact_fwd.argtypes = [i] * 8 + [p] * 7 + [p, sz, p]
         L.lact_fwd.restype = i
+        L.prism_scan_workspace_size.argtypes = [i] * 7
+        L.prism_scan_workspace_size.restype = sz
+        L.prism_scan.argtypes = [i] * 8 + [p] * 13 + [p, sz, p]
+        L.prism_scan.restype = i
         L.scan_bwd_workspace_size.argtypes = [i] * 7
         L.scan_bwd_workspace_size.restype = sz
         L.scan_bwd.argtypes = [i] * 7 + [p] * 15 + [sz, p]
@@ -305,14 +309,78 @@ def prism_expand(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, 
     return q2, k2, v2, a2, b2
 
 
+def prism_scan_workspace_size(dtype: int, B: int, H: int, T: int, dk: int, dv: int, L: int) -> int:
+    n = lib().prism_scan_workspace_size(dtype, B, H, T, dk, dv, L)
+    if n == ctypes.c_size_t(-1).value:
+        raise ScanError(SCAN_EINVAL, last_error())
+    return n
+
+
+def prism_scan(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, Wp=None, S0=None, *,
+               o=None, ST=None, workspace=None, write_state: bool = True):
+    """The PRISM layer's scan without a materialised element stream (bfloat16,
+    d = 128): the arguments of ``prism_expand`` plus S0; returns (o, ST) with o
+    [B, H, T, dv].  Equal bit for bit to ``scan_fwd`` over ``prism_expand``'s
+    stream, read at each token's last element."""
+    _need(q, "q")
+    dev, dt = q.device, q.dtype
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", dt, (B, H, T, dk), dev)
+    _need(v, "v", dt, (B, H, T, dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, H, T), dev)
+    _need(beta, "beta", torch.float32, (B, H, T), dev)
+    L = 0 if beta_l is None else beta_l.shape[-1]
+    W = 1
+    if L > 0:
+        _need(x, "x", dt, (B, H, T, dv), dev)
+        _need(beta_l, "beta_l", torch.float32, (B, H, T, L), dev)
+        _need(conv, "conv", torch.float32, None, dev)
+        if conv.dim() != 3 or conv.shape[0] != H or conv.shape[2] != dv:
+            raise ValueError(f"conv must be [H, W, dv] = [{H}, W, {dv}]")
+        W = conv.shape[1]
+        _need(Wk, "Wk", dt, (H, L, dk, dv), dev)
+        _need(Wp, "Wp", dt, (H, L, dv, dv), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _need(o, "o", dt, (B, H, T, dv), dev)
+    if ST is None and write_state:
+        ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if ST is not None:
+        _need(ST, "ST", torch.float32, (B, H, dv, dk), dev)
+    dcode = _dtype_code(q)
+    ws_bytes = prism_scan_workspace_size(dcode, B, H, T, dk, dv, L)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().prism_scan(dcode, B, H, T, dk, dv, L, W, _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(x) if L else None, _ptr(alpha), _ptr(beta),
+                              _ptr(beta_l) if L else None, _ptr(conv) if L else None,
+                              _ptr(Wk) if L else None, _ptr(Wp) if L else None, _ptr(S0), _ptr(o),
+                              _ptr(ST), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                              _stream(dev))
+    _check(st)
+    return o, ST
+
+
 def prism_scan_fwd(q, k, v, alpha, beta, x=None, beta_l=None, conv=None, Wk=None, Wp=None,
                    S0=None, *, chunk: int = 64, path: str = "auto", leaf_chunks: int = 0,
-                   write_state: bool = True):
-    """PRISM layer forward: ``prism_expand`` then the split-strength ``scan_fwd``.
-
-    Returns (o, ST) with o [B, H, T, dv] a view of the expanded output (every
-    (L+1)-th element, the last of each token's group).
+                   write_state: bool = True, stream: bool = False):
+    """PRISM layer forward.  bfloat16 with d = 128 (unless ``stream``) runs
+    ``prism_scan``; otherwise ``prism_expand`` then the split-strength
+    ``scan_fwd``.  Returns (o, ST) with o [B, H, T, dv] (on the stream path a
+    view of the expanded output: every (L+1)-th element, the last of each
+    token's group).
     """
+    if (not stream and q.dtype == torch.bfloat16 and q.shape[-1] == 128 and v.shape[-1] == 128
+            and path == "auto" and chunk == 64):
+        return prism_scan(q, k, v, alpha, beta, x, beta_l, conv, Wk, Wp, S0, write_state=write_state)
     q2, k2, v2, a2, b2 = prism_expand(q, k, v, alpha, beta, x, beta_l, conv, Wk, Wp)
     o2, ST = scan_fwd(q2, k2, v2, a2, b2, S0, chunk=chunk, path=path, leaf_chunks=leaf_chunks,
                       write_state=write_state)

@@ -336,6 +336,91 @@ int prism_expand(int dtype, int B, int H, int T, int dk, int dv, int L, int W, c
 }
 
 namespace {
+// Validates the sizes of a prism_scan call; returns SCAN_OK and the workspace bytes.
+int plan_prism_scan(int dtype, int B, int H, int T, int dk, int dv, int L, size_t* ws) {
+    if (dtype != SCAN_BF16) return fail(SCAN_EUNSUPPORTED, "prism_scan runs on bfloat16 data (dtype SCAN_BF16)");
+    if (B < 1 || H < 1 || T < 1) return fail(SCAN_EINVAL, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
+    if (dk != 128 || dv != 128) return fail(SCAN_EUNSUPPORTED, "prism_scan supports dk = dv = 128 (got %d, %d)", dk, dv);
+    if (L < 0 || L > PRISM_MAX_STEPS) return fail(SCAN_EINVAL, "L must be in [0, %d] (got %d)", PRISM_MAX_STEPS, L);
+    if ((int64_t)B * H > INT32_MAX / 64) return fail(SCAN_EINVAL, "B*H too large");
+    if (L > 0 && !gds::chunk_prism_supported(T, L))
+        return fail(SCAN_EUNSUPPORTED, "T (L + 1) = %lld elements is too long for prism_scan", (long long)T * (L + 1));
+    *ws = (size_t)B * H * T * L * (dk + dv) * 2;
+    return SCAN_OK;
+}
+}  // namespace
+
+size_t prism_scan_workspace_size(int dtype, int B, int H, int T, int dk, int dv, int L) {
+    size_t ws = 0;
+    if (plan_prism_scan(dtype, B, H, T, dk, dv, L, &ws) != SCAN_OK) return (size_t)-1;
+    return ws;
+}
+
+int prism_scan(int dtype, int B, int H, int T, int dk, int dv, int L, int W, const void* q,
+               const void* k, const void* v, const void* x, const float* alpha, const float* beta,
+               const float* beta_l, const float* conv, const void* Wk, const void* Wp,
+               const float* S0, void* o, float* ST, void* workspace, size_t workspace_bytes,
+               void* stream) {
+    size_t need = 0;
+    int st = plan_prism_scan(dtype, B, H, T, dk, dv, L, &need);
+    if (st != SCAN_OK) return st;
+    if (W < 1 || W > PRISM_MAX_WINDOW) return fail(SCAN_EINVAL, "W must be in [1, %d] (got %d)", PRISM_MAX_WINDOW, W);
+    if (!q || !k || !v || !alpha || !beta || !o) return fail(SCAN_EINVAL, "q, k, v, alpha, beta and o must be non-null");
+    if (L > 0 && (!x || !beta_l || !conv || !Wk || !Wp))
+        return fail(SCAN_EINVAL, "L > 0 needs x, beta_l, conv, Wk and Wp");
+    const void* a16[] = {q, k, v, x, conv, Wk, Wp, S0, o, ST};
+    const char* n16[] = {"q", "k", "v", "x", "conv", "Wk", "Wp", "S0", "o", "ST"};
+    for (int i = 0; i < 10; ++i)
+        if (a16[i] && !aligned(a16[i], 16)) return fail(SCAN_EALIGN, "%s is not 16-byte aligned", n16[i]);
+    const void* a4[] = {alpha, beta, beta_l};
+    for (const void* p : a4)
+        if (p && !aligned(p, 4)) return fail(SCAN_EALIGN, "gate arrays must be 4-byte aligned");
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(SCAN_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        if (!aligned(workspace, 256)) return fail(SCAN_EALIGN, "workspace is not 256-byte aligned");
+    }
+    const size_t BH = (size_t)B * H;
+    const size_t es = 2;
+    const Range in[] = {range("q", q, BH * T * dk * es), range("k", k, BH * T * dk * es),
+                        range("v", v, BH * T * dv * es), range("x", x, L ? BH * T * dv * es : 0),
+                        range("alpha", alpha, BH * T * 4), range("beta", beta, BH * T * 4),
+                        range("beta_l", beta_l, BH * T * L * 4),
+                        range("conv", conv, L ? (size_t)H * W * dv * 4 : 0),
+                        range("Wk", Wk, (size_t)H * L * dk * dv * es),
+                        range("Wp", Wp, (size_t)H * L * dv * dv * es),
+                        range("S0", S0, BH * dv * dk * 4),
+                        range("workspace", workspace, need)};
+    const Range ro = range("o", o, BH * T * dv * es);
+    const Range rs = range("ST", ST, BH * dv * dk * 4);
+    for (const Range& r : in) {
+        if (overlaps(ro, r)) return fail(SCAN_EINVAL, "o overlaps %s", r.name);
+        if (overlaps(rs, r) && !(r.name[0] == 'S' && ST == S0))
+            return fail(SCAN_EINVAL, "ST overlaps %s (only ST == S0 is allowed)", r.name);
+    }
+    if (overlaps(ro, rs)) return fail(SCAN_EINVAL, "o overlaps ST");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (L == 0) {  // no corrections: the gated-delta scan itself
+        e = gds::launch_chunk_mfma(0, (int)BH, T, dk, dv, 64, q, k, v, alpha, beta, beta, S0, o, ST, s);
+        if (e != hipSuccess) return hip_fail(e, "prism_scan launch");
+        return SCAN_OK;
+    }
+    gds::PrismJob j{};
+    j.q = q; j.k = k; j.v = v; j.x = x;
+    j.alpha = alpha; j.beta = beta; j.beta_l = beta_l; j.conv = conv;
+    j.Wk = Wk; j.Wp = Wp;
+    j.kf = workspace;
+    j.vf = static_cast<char*>(workspace) + BH * T * L * dk * es;
+    j.BH = (int)BH; j.H = H; j.T = T; j.dk = dk; j.dv = dv; j.L = L; j.W = W;
+    e = gds::launch_prism_factors(j, s);
+    if (e == hipSuccess)
+        e = gds::launch_chunk_prism((int)BH, T, L, q, k, v, j.kf, j.vf, alpha, beta, beta_l, S0, o, ST, s);
+    if (e != hipSuccess) return hip_fail(e, "prism_scan launch");
+    return SCAN_OK;
+}
+
+namespace {
 // Validates the sizes of a lact_fwd call; returns SCAN_OK and the workspace bytes.
 int plan_lact(int dtype, int B, int H, int T, int dk, int dv, int chunk, size_t* ws) {
     if (dtype != SCAN_F32 && dtype != SCAN_BF16) return fail(SCAN_EINVAL, "dtype must be SCAN_F32 or SCAN_BF16 (got %d)", dtype);

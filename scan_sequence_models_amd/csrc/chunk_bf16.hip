@@ -41,10 +41,10 @@
 //   waves 4, 5  first half: o of chunk j-1 stored from LDS (16-byte stores),
 //               and the two diagonal blocks D_0, D_1 of chunk j scaled into the
 //               bf16 factors Tb = D diag(bw), Tbn = -D diag(beta gamma);
-//               second half: chunk j+1's q, k, v staged in LDS, (wave 4) the
-//               gates of chunk j+2 (a wave scan of ln alpha), then chunk j+2's
-//               rows loaded into registers (coalesced 16-byte loads).
-//   wave 2      first half: chunk j+1's two diagonal k-Gram tiles.
+//               second half: chunk j+1's q, k, v staged in LDS, then chunk
+//               j+2's rows loaded into registers (coalesced 16-byte loads).
+//   wave 2      first half: chunk j+1's two diagonal k-Gram tiles; second
+//               half: the gates of chunk j+2 (a wave scan of ln alpha).
 //   wave 3      first half: chunk j's score tile (0,0); second half: chunk
 //               j+1's off-diagonal k-Gram tile.
 //   wave 6      first half: G = -D_1 A_bl of chunk j by a split-bf16 product
@@ -74,6 +74,8 @@
 //
 // Tokens past T in the last chunk are identity tokens (alpha = 1, beta = 0,
 // q = k = v = 0), which leave S unchanged; their outputs are not written.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -216,6 +218,100 @@ __device__ __forceinline__ float ldtok(const float* head, int m, int i, int T) {
         const_cast<float*>(head + (size_t)m * C), (short)0, valid * 4, 0x00020000);
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
 }
+// PRISM's element stream read in place (role kPrism).  Element e = t G + l
+// (G = L + 1) is token t's gated-delta element (l = 0: k_t, v_t, alpha_t,
+// erase and write beta_t) or its l-th correction (k and v from the factor rows,
+// alpha 1, erase 0, write beta_l[t][l-1]); q_t sits on element t G + L, whose
+// output is o_t.  Elements past the stream read as identity elements.
+// Every field is read with buffer loads from each of its possible sources: the
+// unused source gets an offset past its resource, which the hardware returns as
+// zero without a memory access.  (One load from a per-lane pointer would need
+// 64-bit address arithmetic per row, which costs more than the second load.)
+// The parts are merged (OR, sum) only where the value is used, half a step or
+// more after the loads, so that no wait lands on the loads themselves.
+struct PrismSrc {
+    static constexpr unsigned kOut = 0x80000000u;  // an offset past every resource
+    __amdgpu_buffer_rsrc_t q, k, v, kf, vf, alpha, beta, beta_l, o;
+    int L, G, E;
+    unsigned magic;
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    }
+    __device__ __forceinline__ PrismSrc(const ChunkJob& job, int head, int r0) {
+        L = job.prism_L;
+        G = L + 1;
+        E = job.T;
+        magic = job.prism_magic;
+        const size_t T = job.prism_T, tk = (size_t)head * T;
+        q = rsrc(job.q + tk * DK, T * DK * 2);
+        k = rsrc(job.k + tk * DK, T * DK * 2);
+        v = rsrc(job.v + tk * DV + r0, T * DV * 2 - r0 * 2);
+        kf = rsrc(job.kf + tk * L * DK, T * L * DK * 2);
+        vf = rsrc(job.vf + tk * L * DV + r0, T * L * DV * 2 - r0 * 2);
+        alpha = rsrc(job.alpha + tk, T * 4);
+        beta = rsrc(job.beta + tk, T * 4);
+        beta_l = rsrc(job.beta_l + tk * L, T * L * 4);
+        o = rsrc(job.o ? job.o + tk * DV + r0 : job.q, job.o ? T * DV * 2 - r0 * 2 : 0);
+    }
+    // token t and step l of element e
+    __device__ __forceinline__ void at(int e, int& t, int& l) const {
+        t = (int)__umulhi((unsigned)e, magic);
+        l = e - t * G;
+    }
+    // Byte offsets of the rows (ld elements) of element e in its token source
+    // (a) and in its factor-row source (b), kOut where unused; a column's bytes
+    // are added to them (offsets past the resource stay past it).
+    __device__ __forceinline__ void rows(int e, int ld, unsigned& a, unsigned& b) const {
+        int t, l;
+        at(e, t, l);
+        const bool in = e < E;
+        a = in && l == 0 ? (unsigned)(t * ld) * 2 : kOut;
+        b = in && l != 0 ? (unsigned)((t * L + l - 1) * ld) * 2 : kOut;
+    }
+    __device__ __forceinline__ unsigned q_rows(int e) const {
+        int t, l;
+        at(e, t, l);
+        return e < E && l == L ? (unsigned)(t * DK) * 2 : kOut;
+    }
+    __device__ __forceinline__ static uint4 ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+    __device__ __forceinline__ static float ldf(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+    // the raw gate loads of element e: alpha (token elements), beta (token
+    // elements) and beta_l (corrections), zero where unused; gates_of merges them
+    __device__ __forceinline__ void gate_loads(int e, float& a, float& b, float& bl) const {
+        int t, l;
+        at(e, t, l);
+        const bool in = e < E;
+        const unsigned o0 = in && l == 0 ? (unsigned)t * 4 : kOut;
+        a = ldf(alpha, o0);
+        b = ldf(beta, o0);
+        bl = ldf(beta_l, in && l != 0 ? (unsigned)(t * L + l - 1) * 4 : kOut);
+    }
+    // alpha, erase and write strength from the raw loads
+    __device__ __forceinline__ void gates_of(int e, float a, float b, float bl, float& pa, float& pb,
+                                             float& pw) const {
+        int t, l;
+        at(e, t, l);
+        pa = e < E && l == 0 ? a : 1.f;
+        pb = b;
+        pw = b + bl;  // one of the two is zero
+    }
+    // o_t from element e's output row (dropped unless e is a token's last element)
+    __device__ __forceinline__ void store_o(int e, int col, uint4 val) const {
+        int t, l;
+        at(e, t, l);
+        const unsigned off = e < E && l == L ? (unsigned)(t * DV) * 2 : kOut;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), o, (int)(off + col * 2), 0, 0);
+    }
+};
+__device__ __forceinline__ uint4 orv(uint4 a, uint4 b) {
+    return make_uint4(a.x | b.x, a.y | b.y, a.z | b.z, a.w | b.w);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
 // row broadcasts of lanes 15 and 31).
 __device__ __forceinline__ float wave_inclusive_sum(float x) {
@@ -529,7 +625,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
             for (int e = 0; e < 16; ++e)
                 sacc[jt][e] = un.erows && elem_index(jt, e, h) == vcol ? 1.f : 0.f;
     } else {
-        const int unit = ROLE == kSequential ? un.head : un.head * job.leaves + un.leaf;
+        const int unit = ROLE == kSequential || ROLE == kPrism ? un.head : un.head * job.leaves + un.leaf;
         const float* src = job.S_in ? job.S_in + ((size_t)unit * DV + vcol) * DK : nullptr;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
@@ -700,7 +796,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
     }
 
     float* dst = nullptr;
-    if (ROLE == kSequential && job.S_out) dst = job.S_out + ((size_t)un.head * DV + vcol) * DK;
+    if ((ROLE == kSequential || ROLE == kPrism) && job.S_out) dst = job.S_out + ((size_t)un.head * DV + vcol) * DK;
     if (ROLE == kLeafAggregate)
         dst = job.S_out + ((size_t)(un.head * job.leaves + un.leaf) * (DV + DK) + un.sl * DVS + vl) * DK;
     if (ROLE == kLeafOutput && job.S_out && un.leaf == job.last_leaf)
@@ -738,7 +834,28 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
     const int jc = x & 15, tg = x >> 4;
     const int vc = x & 7, vt = x >> 3;
     uint4 qr[8], kr[8], vr[4];
+    uint4 kr2[8], vr2[4];  // kPrism: the factor-row parts, merged at staging
     auto load = [&](int c) {
+        if constexpr (ROLE == kPrism) {
+            const PrismSrc P(job, un.head, un.r0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = c * C + 32 * (i >> 2) + 4 * tg + (i & 3);
+                unsigned a, b;
+                P.rows(e, DK, a, b);
+                kr[i] = P.ld(P.k, a + 16 * jc);
+                kr2[i] = P.ld(P.kf, b + 16 * jc);
+                qr[i] = P.ld(P.q, P.q_rows(e) + 16 * jc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                unsigned a, b;
+                P.rows(c * C + 4 * vt + i, DV, a, b);
+                vr[i] = P.ld(P.v, a + 16 * vc);
+                vr2[i] = P.ld(P.vf, b + 16 * vc);
+            }
+            return;
+        }
         const Rows rq(job.q + qk_base, c, T, DK), rk(job.k + qk_base, c, T, DK), rv(job.v + v_base, c, T, DV);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -754,18 +871,28 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int prow = perm5(32 * (i >> 2) + 4 * tg + (i & 3));
-            *reinterpret_cast<uint4*>(Kb + kidx(prow, 8 * jc)) = kr[i];
+            *reinterpret_cast<uint4*>(Kb + kidx(prow, 8 * jc)) = ROLE == kPrism ? orv(kr[i], kr2[i]) : kr[i];
             if (OUT) *reinterpret_cast<uint4*>(&sm.Q[prow * LQ + 8 * jc]) = qr[i];
         }
         uint16_t* Vb = sm.V[c & 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Vb[(4 * vt + i) * LV + 8 * vc]) = vr[i];
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(&Vb[(4 * vt + i) * LV + 8 * vc]) = ROLE == kPrism ? orv(vr[i], vr2[i]) : vr[i];
     };
     // o of chunk c from the staged tile: 64 rows of 64 values (128 bytes), 8
     // rows of 8 16-byte pieces per store instruction; rows past T fall outside
     // the resource and are dropped
     auto store_o = [&](int c) {
         if (!job.o) return;
+        if constexpr (ROLE == kPrism) {  // the token's last element only, as o_t
+            const PrismSrc P(job, un.head, un.r0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int g = x + 128 * i, row = g >> 3, col = 8 * (g & 7);
+                P.store_o(c * C + row, col, *reinterpret_cast<const uint4*>(&sm.Ost[row * LO + col]));
+            }
+            return;
+        }
         const int valid = __builtin_amdgcn_readfirstlane(min(T - c * C, C));
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
             job.o + ((size_t)un.head * T + (size_t)c * C) * DV + un.r0, (short)0,
@@ -796,31 +923,11 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
             *reinterpret_cast<uint4*>(&sm.Tbn[prow * LT + s0]) = pack8(-(d * g));
         }
     };
-    // wave 4 also forms the gates two chunks ahead, from alpha, beta, bw of token
-    // `lane`, loaded a step earlier and before the rows it stages: once those are
-    // staged, the gate loads are complete too
-    const size_t a_base = (size_t)un.head * T;
-    const bool split = job.beta_w != job.beta;  // separate write strengths
-    float pa = 1.f, pb = 0.f, pw = 0.f;
-    auto load_ab = [&](int c) {
-        pa = ldtok(job.alpha + a_base, c, lane, T);
-        if (GDN) {
-            pb = ldtok(job.beta + a_base, c, lane, T);
-            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
-        }
-    };
-    if (blk == 0 && un.nb < un.ne) load_ab(un.nb);
     for (int j = un.nb - 2; j < un.ne; ++j) {
         if (OUT && j - 1 >= un.nb) store_o(j - 1);
         if (GDN && j >= un.nb) convert(j);
         lds_barrier();
         if (j + 1 >= un.nb && j + 1 < un.ne) stage(j + 1);
-        // gates of chunk j + 2 into slot (j + 2) % 3: it held chunk j - 1, which no
-        // wave reads after the previous step
-        if (blk == 0 && j + 2 < un.ne) {
-            form_gates(sm.gate[(j + 2) % 3], j + 2, pa, pb, split ? pw : pb, T, lane);
-            if (j + 3 < un.ne) load_ab(j + 3);
-        }
         // the next chunk's rows overwrite the registers just staged: keep the
         // loads after the LDS writes (hoisted above them they would need a
         // second register set)
@@ -834,7 +941,7 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
 // ----------------------------------------------------------------------------
 // k-Gram waves (2, 3): chunk j+1's k-Gram tiles (wave 2 the diagonal ones in
 // the first half, wave 3 the off-diagonal one in the second); wave 3 also chunk
-// j's score tile (0,0)
+// j's score tile (0,0), wave 2 the gates of chunk j+2
 // ----------------------------------------------------------------------------
 template <int MODE, int ROLE>
 __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const Unit& un) {
@@ -847,14 +954,41 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     // chunk c's k rows as MFMA operands, kreg[b][kk] = k[32b + l32][16kk + 8h .. +7],
     // loaded a chunk ahead of their use
     bf16x8 kreg[1][2][8];
+    uint4 kreg2[2][8];  // kPrism: the factor-row parts, merged before the products
     auto load = [&](int c) {
         constexpr int st = 0;
+        if constexpr (ROLE == kPrism) {
+            const PrismSrc P(job, un.head, 0);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                unsigned oa, ob;
+                P.rows(c * C + 32 * b + l32, DK, oa, ob);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    kreg[st][b][kk] = __builtin_bit_cast(bf16x8, P.ld(P.k, oa + 32 * kk + 16 * h));
+                    kreg2[b][kk] = P.ld(P.kf, ob + 32 * kk + 16 * h);
+                }
+            }
+            return;
+        }
         const Rows rk(job.k + qk_base, c, T, DK);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
                 kreg[st][b][kk] = __builtin_bit_cast(bf16x8, rk.at(32 * b + l32, 16 * kk + 8 * h));
+    };
+
+    // kPrism: fold the factor-row parts in where the rows are first used
+    auto merge = [&]() {
+        if constexpr (ROLE == kPrism) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+                    kreg[0][b][kk] = __builtin_bit_cast(
+                        bf16x8, orv(__builtin_bit_cast(uint4, kreg[0][b][kk]), kreg2[b][kk]));
+        }
     };
 
     // k-Gram tile (I, J) masked into A, stored transposed: lane l32 holds
@@ -885,71 +1019,114 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
             mask([](float a, float b) { return __builtin_amdgcn_exp2f(a - b); });
     };
 
-    for (int j = un.nb - 2; j < un.ne; ++j) {
-        constexpr int st = 0;
-        const int c = j + 1;  // chunk whose k-Gram tiles are built
-        const bool build = GDN && c >= un.nb && c < un.ne;
-        // mask weights of chunk c (its gates were formed two steps ago)
-        auto weights = [&](bool& fast, const float*& ws, const float*& wt) {
-            const Gates& G = sm.gate[c % 3];
-            fast = __builtin_amdgcn_readfirstlane(G.fast);
-            ws = fast ? G.fl : G.gl;
-            wt = fast ? G.ebt : G.gb;
-        };
-        // ---- first half: wave 2 the diagonal k-Gram tiles of chunk c (the solve
-        // reads them in the second half); wave 3 score tile (0,0) of chunk j ----
-        if (blk == 0) {
-            if (build) {
-                bool fast;
-                const float *ws, *wt;
-                weights(fast, ws, wt);
-                f32x4 wt0[4], wt1[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    wt0[b] = *reinterpret_cast<const f32x4*>(&wt[8 * b + 4 * h]);
-                    wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
-                }
-                const float ws0 = ws[l32], ws1 = ws[32 + l32];
-                f32x16 a0 = f32x16{}, a1 = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    a0 = mfma32(kreg[st][0][kk], kreg[st][0][kk], a0);
-                    a1 = mfma32(kreg[st][1][kk], kreg[st][1][kk], a1);
-                }
-                gram_mask(a0, 0, 0, fast, ws0, wt0, sm.At[0]);
-                gram_mask(a1, 1, 1, fast, ws1, wt1, sm.At[1]);
-            }
-            // chunk c + 1 goes into the registers just used: keep the loads after
-            // their last use (hoisted above it they would need a second set)
-            __builtin_amdgcn_sched_barrier(0);
-            if (GDN && c + 1 < un.ne) load(c + 1);
-        } else if (OUT && j >= un.nb) {
-            const f32x16 sc = mfma_chain2<8>([&](int k) { return score_k(sm.K[j & 1], 0, k, l32, h); },
-                                             [&](int k) { return score_q(sm, 0, k, l32, h); }, f32x16{});
-            score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
+    // Wave 2 forms the gates two chunks ahead (second half, where it has no
+    // other work), from alpha, beta, bw of token `lane`.  Their loads are issued
+    // before the k rows of the next step, so the wait for them lets those rows
+    // stay in flight.
+    const size_t a_base = (size_t)un.head * T;
+    const bool split = ROLE == kPrism || job.beta_w != job.beta;  // separate write strengths
+    float pa = 1.f, pb = 0.f, pw = 0.f;
+    float pl = 0.f;  // kPrism: the beta_l part of the write strength
+    auto load_ab = [&](int c) {
+        if constexpr (ROLE == kPrism) {
+            PrismSrc(job, un.head, 0).gate_loads(c * C + lane, pa, pb, pl);
+            return;
         }
-        lds_barrier();
-        // ---- second half: wave 3 the off-diagonal k-Gram tile of chunk c into slot
-        // c % 2 (wave 6 reads it in the next step), then chunk c + 1's rows ----
-        if (blk == 1) {
-            if (build) {
-                bool fast;
-                const float *ws, *wt;
-                weights(fast, ws, wt);
-                f32x4 wt1[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
-                const float ws0 = ws[l32];
-                f32x16 a = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
-                gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (GDN && c + 1 < un.ne) load(c + 1);
+        pa = ldtok(job.alpha + a_base, c, lane, T);
+        if (GDN) {
+            pb = ldtok(job.beta + a_base, c, lane, T);
+            if (split) pw = ldtok(job.beta_w + a_base, c, lane, T);
         }
-        lds_barrier();
-    }
+    };
+    if (blk == 0 && un.nb < un.ne) load_ab(un.nb);
+
+    // the two waves' loops compiled apart: with the waves' branches in one loop,
+    // the compiler's memory-wait analysis merges their paths, and wave 2's wait
+    // for its gate loads would also wait for the k rows it has just requested
+    auto run = [&](auto blk_c) {
+        constexpr int B = decltype(blk_c)::value;
+        for (int j = un.nb - 2; j < un.ne; ++j) {
+            constexpr int st = 0;
+            const int c = j + 1;  // chunk whose k-Gram tiles are built
+            const bool build = GDN && c >= un.nb && c < un.ne;
+            // mask weights of chunk c (its gates were formed two steps ago)
+            auto weights = [&](bool& fast, const float*& ws, const float*& wt) {
+                const Gates& G = sm.gate[c % 3];
+                fast = __builtin_amdgcn_readfirstlane(G.fast);
+                ws = fast ? G.fl : G.gl;
+                wt = fast ? G.ebt : G.gb;
+            };
+            // ---- first half: wave 2 the diagonal k-Gram tiles of chunk c (the solve
+            // reads them in the second half); wave 3 score tile (0,0) of chunk j ----
+            if constexpr (B == 0) {
+                if (build) {
+                    merge();
+                    bool fast;
+                    const float *ws, *wt;
+                    weights(fast, ws, wt);
+                    f32x4 wt0[4], wt1[4];
+    #pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        wt0[b] = *reinterpret_cast<const f32x4*>(&wt[8 * b + 4 * h]);
+                        wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
+                    }
+                    const float ws0 = ws[l32], ws1 = ws[32 + l32];
+                    f32x16 a0 = f32x16{}, a1 = f32x16{};
+    #pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) {
+                        a0 = mfma32(kreg[st][0][kk], kreg[st][0][kk], a0);
+                        a1 = mfma32(kreg[st][1][kk], kreg[st][1][kk], a1);
+                    }
+                    gram_mask(a0, 0, 0, fast, ws0, wt0, sm.At[0]);
+                    gram_mask(a1, 1, 1, fast, ws1, wt1, sm.At[1]);
+                }
+                // chunk c + 1 goes into the registers just used: keep the loads after
+                // their last use (hoisted above it they would need a second set).
+                // Unconditional (chunks past the end read as zeros, with no memory
+                // access): loads skipped on one path would make the wait for the
+                // gate loads in the second half a wait for everything.
+                __builtin_amdgcn_sched_barrier(0);
+                if (GDN) load(c + 1);
+            } else if (OUT && j >= un.nb) {
+                const f32x16 sc = mfma_chain2<8>([&](int k) { return score_k(sm.K[j & 1], 0, k, l32, h); },
+                                                 [&](int k) { return score_q(sm, 0, k, l32, h); }, f32x16{});
+                score_mask(sm, sc, sm.gate[j % 3], 0, 0, l32, h);
+            }
+            lds_barrier();
+            // ---- second half: wave 3 the off-diagonal k-Gram tile of chunk c into slot
+            // c % 2 (wave 6 reads it in the next step), then chunk c + 1's rows ----
+            if constexpr (B == 1) {
+                if (build) {
+                    merge();
+                    bool fast;
+                    const float *ws, *wt;
+                    weights(fast, ws, wt);
+                    f32x4 wt1[4];
+    #pragma unroll
+                    for (int b = 0; b < 4; ++b) wt1[b] = *reinterpret_cast<const f32x4*>(&wt[32 + 8 * b + 4 * h]);
+                    const float ws0 = ws[l32];
+                    f32x16 a = f32x16{};
+    #pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
+                    gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (GDN && c + 1 < un.ne) load(c + 1);
+            } else if (j + 2 < un.ne) {
+                // gates of chunk j + 2 into slot (j + 2) % 3: it held chunk j - 1, which
+                // no wave reads after the previous step
+                if constexpr (ROLE == kPrism)  // the loads' parts, merged here where they are used
+                    PrismSrc(job, un.head, 0).gates_of((j + 2) * C + lane, pa, pb, pl, pa, pb, pw);
+                form_gates(sm.gate[(j + 2) % 3], j + 2, pa, pb, split ? pw : pb, T, lane);
+                load_ab(j + 3);  // (past the end: zeros, no memory access)
+            }
+            lds_barrier();
+        }
+    };
+    if (blk == 0)
+        run(std::integral_constant<int, 0>{});
+    else
+        run(std::integral_constant<int, 1>{});
 }
 
 // ----------------------------------------------------------------------------
@@ -1042,6 +1219,8 @@ static hipError_t launch_role(int role, const ChunkJob& job, hipStream_t stream)
     const dim3 block(NT);
     if (role == kSequential)
         hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kSequential>), dim3(2 * units), block, 0, stream, job);
+    else if (role == kPrism)
+        hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kPrism>), dim3(2 * units), block, 0, stream, job);
     else if (role == kLeafAggregate) {
         hipLaunchKernelGGL((chunk_mfma_kernel<MODE, kLeafAggregate>), dim3((MODE == 0 ? 4 : 2) * units), block, 0,
                            stream, job);
@@ -1052,7 +1231,49 @@ static hipError_t launch_role(int role, const ChunkJob& job, hipStream_t stream)
 }
 
 hipError_t launch_chunk_job(int mode, int role, const ChunkJob& job, hipStream_t stream) {
+    if (role == kPrism) return launch_role<0>(role, job, stream);  // gated delta rule only
     return mode == 0 ? launch_role<0>(role, job, stream) : launch_role<1>(role, job, stream);
+}
+
+// floor(e / G) = mulhi(e, m) with m = ceil(2^32 / G) while e (G m - 2^32) < 2^32
+static unsigned prism_magic(int G) { return (unsigned)(((1ull << 32) + G - 1) / G); }
+
+bool chunk_prism_supported(int T, int L) {
+    if (L < 1 || L > 8) return false;
+    const unsigned long long G = L + 1, E = (unsigned long long)T * G;
+    // byte offsets into one head's factor rows stay below 2^31 (buffer offsets
+    // are 32-bit; 2^31 marks an unused source)
+    return E < (1ull << 31) && E * (G * prism_magic((int)G) - (1ull << 32)) < (1ull << 32) &&
+           (unsigned long long)T * L * DK * 2 < (1ull << 31) && (unsigned long long)T * L * DV * 2 < (1ull << 31);
+}
+
+hipError_t launch_chunk_prism(int BH, int T, int L, const void* q, const void* k, const void* v,
+                              const void* kf, const void* vf, const float* alpha, const float* beta,
+                              const float* beta_l, const float* S0, void* o, float* ST,
+                              hipStream_t stream) {
+    ChunkJob job{};
+    job.q = static_cast<const uint16_t*>(q);
+    job.k = static_cast<const uint16_t*>(k);
+    job.v = static_cast<const uint16_t*>(v);
+    job.alpha = alpha;
+    job.beta = beta;
+    job.beta_w = beta;
+    job.o = static_cast<uint16_t*>(o);
+    job.S_in = S0;
+    job.S_out = ST;
+    job.heads = BH;
+    job.T = T * (L + 1);  // elements
+    job.nchunks = (job.T + C - 1) / C;
+    job.leaves = 1;
+    job.leaf_chunks = job.nchunks;
+    job.last_leaf = 0;
+    job.prism_L = L;
+    job.prism_T = T;
+    job.prism_magic = prism_magic(L + 1);
+    job.kf = static_cast<const uint16_t*>(kf);
+    job.vf = static_cast<const uint16_t*>(vf);
+    job.beta_l = beta_l;
+    return launch_chunk_job(0, kPrism, job, stream);
 }
 
 hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk, const void* q,

@@ -37,7 +37,9 @@ hipError_t launch_chunk_diag(int mode, int dtype, int BH, int T, int dk, int dv,
 
 // chunk_bf16.hip -- bfloat16 MFMA chunkwise kernel ---------------------------
 // (dk = dv = 128, chunk 64; q, k, v, o bfloat16; states float32)
-enum ChunkRole { kSequential = 0, kLeafAggregate = 1, kLeafOutput = 2 };
+// kPrism: the sequential pass over PRISM's element stream, read in place (see
+// ChunkJob::prism_L)
+enum ChunkRole { kSequential = 0, kLeafAggregate = 1, kLeafOutput = 2, kPrism = 3 };
 
 struct ChunkJob {
     const uint16_t* q;
@@ -53,6 +55,17 @@ struct ChunkJob {
     int leaves;          // leaves per head
     int leaf_chunks;     // chunks per leaf (the last real leaf may hold fewer)
     int last_leaf;       // kLeafOutput: the leaf whose final state is S_T
+    // kPrism: T counts elements, T = prism_T (L + 1).  Element t (L + 1) + l is
+    // token t's gated-delta element (l = 0: k, v, alpha, erase and write beta of
+    // the token) or its l-th correction (k, v from the factor rows kf, vf
+    // [head][prism_T][L][d], alpha 1, erase 0, write beta_l[head][t][l-1]); q_t
+    // sits on element l = L, whose output is o_t (o is [head][prism_T][dv]).
+    // floor(e / (L + 1)) = mulhi(e, prism_magic) for every element e.
+    int prism_L, prism_T;
+    unsigned prism_magic;
+    const uint16_t* kf;
+    const uint16_t* vf;
+    const float* beta_l;
 };
 
 bool chunk_mfma_supported(int mode, int dk, int dv, int chunk);
@@ -61,6 +74,13 @@ hipError_t launch_chunk_mfma(int mode, int BH, int T, int dk, int dv, int chunk,
                              const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* beta_w, const float* S0, void* o,
                              float* ST, hipStream_t stream);
+// PRISM's element stream scanned in place (bf16, d = 128, 1 <= L <= 8); false if
+// T (L + 1) is too long for the element index arithmetic
+bool chunk_prism_supported(int T, int L);
+hipError_t launch_chunk_prism(int BH, int T, int L, const void* q, const void* k, const void* v,
+                              const void* kf, const void* vf, const float* alpha, const float* beta,
+                              const float* beta_l, const float* S0, void* o, float* ST,
+                              hipStream_t stream);
 
 // scan_bwd.hip -- gradient of the scan through the chunkwise form ------------
 struct BwdJob {
@@ -85,10 +105,14 @@ struct PrismJob {
     const void *Wk, *Wp;                 // [H, L, dk, dv], [H, L, dv, dv]
     void *q2, *k2, *v2;                  // [BH, T (L+1), d]
     float *alpha2, *beta2;               // [BH, T (L+1)], [2, BH, T (L+1)]
+    // compact factor rows instead of the stream (launch_prism_factors):
+    void *kf, *vf;                       // [BH, T, L, d]
     int BH, H, T, dk, dv, L, W;
 };
 bool prism_supported(int dtype, int dk, int dv);
 hipError_t launch_prism_expand(int dtype, const PrismJob& job, hipStream_t stream);
+// the factor rows k^(l), delta^(l) only, into job.kf, job.vf (bf16, d = 128, L >= 1)
+hipError_t launch_prism_factors(const PrismJob& job, hipStream_t stream);
 
 // lact.hip -- large-chunk fast-weight update (linear fast weights) -----------
 struct LactJob {

@@ -35,7 +35,10 @@
 //     pass-through part of the stream is a separate streaming kernel.
 //   * prism_plain_kernel (float32 or bfloat16, any supported size): the same
 //     arithmetic with float32 FMAs, 16 tokens per workgroup.
+#include <type_traits>
+
 #include "common.hpp"
+#include "gdscan.h"
 #include "kernels.hpp"
 
 namespace gds {
@@ -45,8 +48,32 @@ constexpr int kThreads = 256;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, with erf from the rational
+// approximation of Abramowitz and Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (after Hastings): for z >= 0,
+//   erf z = 1 - (a1 s + a2 s^2 + a3 s^3 + a4 s^4 + a5 s^5) exp(-z^2),
+//   s = 1 / (1 + p z),
+// with absolute error at most 1.5e-7.  Branch-free (a library erff branches on
+// |z| < 1, so a wave with both kinds of argument runs both paths).  With
+// h = x (1 - erf z) / 2, z = |x| / sqrt 2, GELU is x - h for x >= 0 and h for
+// x < 0 (no cancellation in the negative tail).
 __device__ __forceinline__ float gelu(float x) {
-    return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
+    constexpr float p = 0.3275911f * 0.7071067811865476f;  // p / sqrt 2: s from |x|
+    // a1 .. a5 halved: the polynomial gives (1 - erf z) / (2 exp(-z^2))
+    constexpr float b1 = 0.5f * 0.254829592f, b2 = 0.5f * -0.284496736f, b3 = 0.5f * 1.421413741f,
+                    b4 = 0.5f * -1.453152027f, b5 = 0.5f * 1.061405429f;
+    const float sv = __builtin_amdgcn_rcpf(__builtin_fmaf(p, __builtin_fabsf(x), 1.f));
+    const float poly = sv * __builtin_fmaf(sv, __builtin_fmaf(sv, __builtin_fmaf(sv, __builtin_fmaf(sv, b5, b4), b3), b2), b1);
+    // exp(-z^2) = 2^(-x^2 log2(e) / 2)
+    const float e = __builtin_amdgcn_exp2f(x * -0.7213475204444817f * x);
+    const float h = x * poly * e;
+    return x >= 0.f ? x - h : h;
+}
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+// two floats rounded to bfloat16 (nearest even) in one register, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
 }
 
 // 16-byte vector copies of the pass-through part of the stream (rows tG of k and
@@ -180,13 +207,26 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Writes the computed rows only (elements tG + l, l >= 1); the pass-through part
-// comes from prism_copy_kernel.
-// (at most 256 VGPRs; 152 in use: three workgroups per CU)
-__global__ __launch_bounds__(kMfmaThreads, 2) void prism_mfma_kernel(const PrismJob j) {
-    __shared__ uint16_t Uh[kTok * kLdu];  // u rounded to bfloat16      [token][channel]
-    __shared__ uint16_t Ul[kTok * kLdu];  // u - u_hi rounded to bfloat16
-    __shared__ uint16_t Ob[kTok * kLdu];  // v, then each output tile    [token][channel]
+// Writes the computed rows only (elements tG + l, l >= 1; the pass-through part
+// comes from prism_copy_kernel), or, for the in-place scan, the same rows as
+// compact factor arrays kf, vf [BH, T, L, 128].
+// The products are formed transposed, D[channel][token] = W u^T (the weight
+// rows are the A operand): each lane then holds four consecutive channels of
+// one token per accumulator group and writes them to the LDS output tile as one
+// 8-byte piece; whole 256-byte rows then go out from there.  (Stored straight
+// from the accumulators, each store instruction would cover 32 rows with 16
+// bytes each, which the memory system merges poorly.)
+__global__ __launch_bounds__(kMfmaThreads, 3) void prism_mfma_kernel(const PrismJob j) {
+    __shared__ __align__(16) uint16_t lds[3 * kTok * kLdu];
+    uint16_t* const Uh = lds;                   // u rounded to bfloat16      [token][channel]
+    uint16_t* const Ul = lds + kTok * kLdu;     // u - u_hi rounded to bfloat16
+    uint16_t* const Ob = lds + 2 * kTok * kLdu; // v, then each output tile   [token][channel]
+    // the anchor's inputs, staged where Uh and Ul go afterwards: x rows
+    // t0 - (W - 1) .. t0 + n - 1 (zero before the sequence start) and the taps
+    uint16_t* const Xs = lds;                                                     // [kTok + W - 1][kLdu]
+    float* const Cs = reinterpret_cast<float*>(lds + (kTok + PRISM_MAX_WINDOW - 1) * kLdu);  // [W][128]
+    static_assert((kTok + PRISM_MAX_WINDOW - 1) * kLdu * 2 + PRISM_MAX_WINDOW * kD * 4 <= 2 * kTok * kLdu * 2,
+                  "anchor inputs fit over Uh and Ul");
     const int tiles = (j.T + kTok - 1) / kTok;
     const int bh = blockIdx.x / tiles;
     const int t0 = (blockIdx.x - bh * tiles) * kTok;
@@ -194,53 +234,74 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void prism_mfma_kernel(const Prism
     const int head = bh % j.H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int W = j.W;
     const int G = j.L + 1;
     const size_t T2 = (size_t)j.T * G;
     const uint16_t* x = static_cast<const uint16_t*>(j.x);
     const uint16_t* v = static_cast<const uint16_t*>(j.v);
-    uint16_t* k2 = static_cast<uint16_t*>(j.k2);
-    uint16_t* v2 = static_cast<uint16_t*>(j.v2);
-    const float* conv = j.conv + (size_t)head * j.W * kD;
+    const float* conv = j.conv + (size_t)head * W * kD;
     const uint16_t* Wk = static_cast<const uint16_t*>(j.Wk) + (size_t)head * j.L * kD * kD;
     const uint16_t* Wp = static_cast<const uint16_t*>(j.Wp) + (size_t)head * j.L * kD * kD;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int nc = 32 * w + l32;
 
-    // B operands of weight matrix W [128 out][128 in]: rows nc of this wave
-    auto load_b = [&](const uint16_t* W, bf16x8 (&b)[8]) {
+    // A operands of weight matrix W [128 out][128 in]: row 32 w + l32 (this
+    // wave's output channels), inputs 16 k + 8 hh .. + 7
+    auto load_w = [&](const uint16_t* Wm, bf16x8 (&a)[8]) {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            b[k] = *reinterpret_cast<const bf16x8*>(W + (size_t)nc * kD + 16 * k + 8 * hh);
+            a[k] = *reinterpret_cast<const bf16x8*>(Wm + (size_t)(32 * w + l32) * kD + 16 * k + 8 * hh);
     };
-    bf16x8 bcur[8], bnext[8];
-    load_b(Wk, bcur);  // first matrix in flight during the anchor
+    bf16x8 wcur[8], wnext[8];
 
-    // rows [t0, t0 + n) of a [T][128] bf16 tensor of head bh: thread tid moves
-    // 16 bytes of row r = tid / 16 + 32 i
-    auto tile_rows = [&](const uint16_t* src, uint4 (&dst)[4]) {
+    // ---- stage x rows and taps (16 bytes a thread and pass), v rows into registers ----
+    {
+        constexpr int kPasses = ((kTok + PRISM_MAX_WINDOW - 1) * 16 + kMfmaThreads - 1) / kMfmaThreads;
+        const int xrows = n + W - 1;
+        uint4 xr[kPasses];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid >> 4) + 16 * i;
-            dst[i] = r < n ? *reinterpret_cast<const uint4*>(src + ((size_t)bh * j.T + t0 + r) * kD + 8 * (tid & 15))
-                           : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < kPasses; ++i) {
+            const int idx = tid + kMfmaThreads * i, r = idx >> 4;
+            const int tok = t0 - (W - 1) + r;
+            xr[i] = r < xrows && tok >= 0
+                        ? *reinterpret_cast<const uint4*>(x + ((size_t)bh * j.T + tok) * kD + 8 * (idx & 15))
+                        : make_uint4(0, 0, 0, 0);
         }
-    };
-    uint4 vrow[4];
-    tile_rows(v, vrow);
+        f32x4 cr = {};
+        if (tid < W * (kD / 4)) cr = *reinterpret_cast<const f32x4*>(conv + 4 * tid);
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            const int idx = tid + kMfmaThreads * i, r = idx >> 4;
+            // (rows past the tile's tokens are zero: the anchor of every row is defined)
+            if (r < kTok + W - 1) *reinterpret_cast<uint4*>(&Xs[r * kLdu + 8 * (idx & 15)]) = xr[i];
+        }
+        if (tid < W * (kD / 4)) *reinterpret_cast<f32x4*>(&Cs[4 * tid]) = cr;
+    }
+    uint4 vrow[4];  // 16 bytes of row tid / 16 + 16 i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        vrow[i] = r < n ? *reinterpret_cast<const uint4*>(v + ((size_t)bh * j.T + t0 + r) * kD + 8 * (tid & 15))
+                        : make_uint4(0, 0, 0, 0);
+    }
+    load_w(Wk, wcur);  // first matrix in flight during the anchor
+    __syncthreads();
 
-    // ---- anchor: thread (token tid/8, channels 16 (tid%8) .. +15), float32 ----
+    // ---- anchor: thread (token tid/4, channels 32 (tid%4) .. +31), float32 ----
     {
         const int t = tid >> 2, cb = 32 * (tid & 3);
-        const int tok = t0 + t;
+        float acc[32];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int c0 = cb + 8 * g;
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (t < n) {
-                for (int i = 0; i < j.W && i <= tok; ++i) {
-                    const uint4 xv = *reinterpret_cast<const uint4*>(x + ((size_t)bh * j.T + tok - i) * kD + c0);
-                    const f32x4 c_lo = *reinterpret_cast<const f32x4*>(conv + i * kD + c0);
-                    const f32x4 c_hi = *reinterpret_cast<const f32x4*>(conv + i * kD + c0 + 4);
+        for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+        // tap i reads x row t - i, staged at t + W - 1 - i
+#pragma unroll
+        for (int i = 0; i < PRISM_MAX_WINDOW; ++i) {
+            if (i < W) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c0 = cb + 8 * g;
+                    const uint4 xv = *reinterpret_cast<const uint4*>(&Xs[(t + W - 1 - i) * kLdu + c0]);
+                    const f32x4 c_lo = *reinterpret_cast<const f32x4*>(&Cs[i * kD + c0]);
+                    const f32x4 c_hi = *reinterpret_cast<const f32x4*>(&Cs[i * kD + c0 + 4]);
                     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -248,24 +309,24 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void prism_mfma_kernel(const Prism
                         const float a1 = __uint_as_float(xw[q] & 0xffff0000u);
                         const float t0c = q < 2 ? c_lo[2 * q] : c_hi[2 * q - 4];
                         const float t1c = q < 2 ? c_lo[2 * q + 1] : c_hi[2 * q - 3];
-                        acc[2 * q] += t0c * a0;
-                        acc[2 * q + 1] += t1c * a1;
+                        acc[8 * g + 2 * q] += t0c * a0;
+                        acc[8 * g + 2 * q + 1] += t1c * a1;
                     }
                 }
             }
-            uint16_t hi[8], lo[8];
+        }
+        __syncthreads();  // every read of the staged inputs done: Uh, Ul go over them
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                hi[e] = f32_to_bf16(acc[e]);
-                lo[e] = f32_to_bf16(acc[e] - bf16_to_f32(hi[e]));
+        for (int g = 0; g < 4; ++g) {
+            uint32_t ph[4], pl[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float a = acc[8 * g + 2 * q], b = acc[8 * g + 2 * q + 1];
+                ph[q] = pack_bf16x2(a, b);
+                pl[q] = pack_bf16x2(a - __uint_as_float(ph[q] << 16), b - __uint_as_float(ph[q] & 0xffff0000u));
             }
-            uint4 ph, pl;
-            ph.x = hi[0] | (uint32_t)hi[1] << 16; ph.y = hi[2] | (uint32_t)hi[3] << 16;
-            ph.z = hi[4] | (uint32_t)hi[5] << 16; ph.w = hi[6] | (uint32_t)hi[7] << 16;
-            pl.x = lo[0] | (uint32_t)lo[1] << 16; pl.y = lo[2] | (uint32_t)lo[3] << 16;
-            pl.z = lo[4] | (uint32_t)lo[5] << 16; pl.w = lo[6] | (uint32_t)lo[7] << 16;
-            *reinterpret_cast<uint4*>(&Uh[t * kLdu + c0]) = ph;
-            *reinterpret_cast<uint4*>(&Ul[t * kLdu + c0]) = pl;
+            *reinterpret_cast<uint4*>(&Uh[t * kLdu + cb + 8 * g]) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+            *reinterpret_cast<uint4*>(&Ul[t * kLdu + cb + 8 * g]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
         }
     }
 #pragma unroll
@@ -273,68 +334,107 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void prism_mfma_kernel(const Prism
         *reinterpret_cast<uint4*>(&Ob[((tid >> 4) + 16 * i) * kLdu + 8 * (tid & 15)]) = vrow[i];
     __syncthreads();
 
-    // accumulator element e of token tile tt is token 32 tt + row(e), channel nc
-    auto row = [&](int e) { return 8 * (e >> 2) + 4 * hh + (e & 3); };
+    // Accumulator element e of token tile tt: token 32 tt + l32, channel
+    // ch(e) = 32 w + 8 (e >> 2) + 4 hh + (e & 3); group g = e >> 2 holds four
+    // consecutive channels from cg(g).
+    auto cg = [&](int g) { return 32 * w + 8 * g + 4 * hh; };
     // residual r = v - u in the accumulator layout
     float res[2][16];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int t = 32 * tt + row(e);
-        const float uu = bf16_to_f32(Uh[t * kLdu + nc]) + bf16_to_f32(Ul[t * kLdu + nc]);
-        res[tt][e] = bf16_to_f32(Ob[t * kLdu + nc]) - uu;
+    for (int g = 0; g < 4; ++g) {
+        const int o = (32 * tt + l32) * kLdu + cg(g);
+        const uint2 uh = *reinterpret_cast<const uint2*>(&Uh[o]);
+        const uint2 ul = *reinterpret_cast<const uint2*>(&Ul[o]);
+        const uint2 vv = *reinterpret_cast<const uint2*>(&Ob[o]);
+        const uint32_t h4[4] = {uh.x << 16, uh.x & 0xffff0000u, uh.y << 16, uh.y & 0xffff0000u};
+        const uint32_t l4[4] = {ul.x << 16, ul.x & 0xffff0000u, ul.y << 16, ul.y & 0xffff0000u};
+        const uint32_t v4[4] = {vv.x << 16, vv.x & 0xffff0000u, vv.y << 16, vv.y & 0xffff0000u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            res[tt][4 * g + i] = __uint_as_float(v4[i]) - (__uint_as_float(h4[i]) + __uint_as_float(l4[i]));
     }
-    // token tile tt of u W^T (u = u_hi + u_lo)
-    auto project = [&](const bf16x8 (&b)[8], int tt) {
-        f32x16 a = {};
+    // token tile tt of W u^T (u = u_hi + u_lo): B operands are u rows
+    auto project = [&](const bf16x8 (&a)[8], int tt) {
+        f32x16 acc = {};
         const uint16_t* uh = &Uh[(32 * tt + l32) * kLdu + 8 * hh];
         const uint16_t* ul = &Ul[(32 * tt + l32) * kLdu + 8 * hh];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            a = mfma32(*reinterpret_cast<const bf16x8*>(uh + 16 * k), b[k], a);
-            a = mfma32(*reinterpret_cast<const bf16x8*>(ul + 16 * k), b[k], a);
+            acc = mfma32(a[k], *reinterpret_cast<const bf16x8*>(uh + 16 * k), acc);
+            acc = mfma32(a[k], *reinterpret_cast<const bf16x8*>(ul + 16 * k), acc);
         }
-        return a;
+        return acc;
     };
-    // Ob -> element rows tG + l + 1 of the tile's tokens, 16 bytes a thread
+    // Ob -> element rows tG + l + 1 of the tile's tokens (or, with compact
+    // factor rows, rows t L + l), 16 bytes a thread
+    const bool compact = j.kf != nullptr;
     auto store_rows = [&](uint16_t* dst, int l) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = (tid >> 4) + 16 * i;
+            const size_t row = compact ? ((size_t)bh * j.T + t0 + r) * j.L + l
+                                       : (size_t)bh * T2 + (size_t)(t0 + r) * G + l + 1;
             if (r < n)
-                *reinterpret_cast<uint4*>(dst + ((size_t)bh * T2 + (size_t)(t0 + r) * G + l + 1) * kD + 8 * (tid & 15)) =
+                *reinterpret_cast<uint4*>(dst + row * kD + 8 * (tid & 15)) =
                     *reinterpret_cast<const uint4*>(&Ob[r * kLdu + 8 * (tid & 15)]);
         }
     };
-    // 2L projections in the order Wk[0], Wp[0], Wk[1], ...; the next matrix's
-    // operands load while the current one is in use
-    for (int m = 0; m < 2 * j.L; ++m) {
-        const int l = m >> 1;
-        const bool is_p = m & 1;
-        if (m + 1 < 2 * j.L) load_b(((m + 1) & 1 ? Wp : Wk) + (size_t)((m + 1) >> 1) * kD * kD, bnext);
+    // one projection into Ob, then its rows out: factor l from the weights in
+    // wcur; IS_P: the correction delta = GELU(p r), r -= delta, else the
+    // direction k itself
+    auto emit = [&](auto is_p, int l) {
+        constexpr bool IS_P = decltype(is_p)::value;
         __syncthreads();  // Ob free (v read, or the previous rows stored)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const f32x16 acc = project(bcur, tt);
+            const f32x16 acc = project(wcur, tt);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float y = acc[e];
-                if (is_p) {  // delta = GELU(p r), r -= delta
-                    y = gelu(acc[e] * res[tt][e]);
-                    res[tt][e] -= y;
+            for (int g = 0; g < 4; ++g) {
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * g + i;
+                    if constexpr (IS_P) {
+                        y[i] = gelu(acc[e] * res[tt][e]);
+                        res[tt][e] -= y[i];
+                    } else {
+                        y[i] = acc[e];
+                    }
                 }
-                Ob[(32 * tt + row(e)) * kLdu + nc] = f32_to_bf16(y);
+                const uint2 pk = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+                *reinterpret_cast<uint2*>(&Ob[(32 * tt + l32) * kLdu + cg(g)]) = pk;
             }
         }
         __syncthreads();
-        store_rows(is_p ? v2 : k2, l);
+        store_rows(static_cast<uint16_t*>(compact ? (IS_P ? j.vf : j.kf) : (IS_P ? j.v2 : j.k2)), l);
+    };
+    // 2L projections in the order Wk[0], Wp[0], Wk[1], ...; the next matrix's
+    // operands load while the current one is in use
+    for (int l = 0; l < j.L; ++l) {
+        // (keeps the u operand reads inside the loop: hoisted, the 32 of them
+        // would take 128 registers)
+        asm volatile("" ::: "memory");
+        load_w(Wp + (size_t)l * kD * kD, wnext);
+        emit(std::false_type{}, l);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) bcur[k] = bnext[k];
+        for (int k = 0; k < 8; ++k) wcur[k] = wnext[k];
+        if (l + 1 < j.L) load_w(Wk + (size_t)(l + 1) * kD * kD, wnext);
+        asm volatile("" ::: "memory");
+        emit(std::true_type{}, l);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) wcur[k] = wnext[k];
     }
 }
 
 }  // namespace
+
+hipError_t launch_prism_factors(const PrismJob& j, hipStream_t stream) {
+    const unsigned grid = (unsigned)((size_t)j.BH * ((j.T + kTok - 1) / kTok));
+    hipLaunchKernelGGL(prism_mfma_kernel, dim3(grid), dim3(kMfmaThreads), 0, stream, j);
+    return hipGetLastError();
+}
 
 bool prism_supported(int dtype, int dk, int dv) {
     (void)dtype;

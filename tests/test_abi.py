@@ -21,7 +21,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.header_functions()
     assert set(names) == {"scan_fwd_workspace_size", "scan_fwd", "scan_fwd_noalloc", "decode_step",
-                          "prism_expand",
+                          "prism_expand", "prism_scan_workspace_size", "prism_scan",
                           "lact_fwd_workspace_size", "lact_fwd", "scan_bwd_workspace_size", "scan_bwd",
                           "scan_last_error", "scan_version"}
     for n in names:
@@ -190,6 +190,38 @@ def _lact(lib, dtype=1, B=1, H=2, T=4096, dk=128, dv=128, chunk=2048, order=0, q
           WT=FAKE + 6 * STEP, ws=FAKE + 7 * STEP, wsb=1 << 30):
     # a valid argument set would launch with fake pointers: only invalid ones are passed
     return lib.lact_fwd(dtype, B, H, T, dk, dv, chunk, order, q, k, v, eta, W0, o, WT, ws, wsb, None)
+
+
+def _prism_scan(lib, dtype=1, B=1, H=2, T=64, dk=128, dv=128, L=2, W=4, q=FAKE, o=FAKE + 6 * STEP,
+                ws=FAKE + 9 * STEP, wsb=1 << 30, x=FAKE + 10 * STEP):
+    return lib.prism_scan(dtype, B, H, T, dk, dv, L, W, q, FAKE + STEP, FAKE + 2 * STEP, x,
+                          FAKE + 3 * STEP, FAKE + 4 * STEP, FAKE + 11 * STEP, FAKE + 12 * STEP,
+                          FAKE + 13 * STEP, FAKE + 14 * STEP, None, o, FAKE + 7 * STEP, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), L.SCAN_EUNSUPPORTED),       # bfloat16 only
+    (dict(dk=64), L.SCAN_EUNSUPPORTED),
+    (dict(L=9), L.SCAN_EINVAL),
+    (dict(W=0), L.SCAN_EINVAL),
+    (dict(T=0), L.SCAN_EINVAL),
+    (dict(x=None), L.SCAN_EINVAL),              # L > 0 needs the anchor source
+    (dict(ws=None), L.SCAN_EWORKSPACE),
+    (dict(wsb=1024), L.SCAN_EWORKSPACE),
+    (dict(ws=FAKE + 9 * STEP + 8), L.SCAN_EALIGN),
+    (dict(o=FAKE + 256), L.SCAN_EINVAL),        # o overlaps q
+    (dict(T=1 << 30), L.SCAN_EUNSUPPORTED),     # element index range
+])
+def test_prism_scan_rejects(lib, kw, code):
+    assert _prism_scan(lib, **kw) == code
+    assert len(L.last_error()) > 0
+
+
+def test_prism_scan_workspace_sizes(lib):
+    # the factor rows: B H T L (dk + dv) bfloat16 values; none without corrections
+    assert lib.prism_scan_workspace_size(1, 8, 16, 8192, 128, 128, 2) == 8 * 16 * 8192 * 2 * 256 * 2
+    assert lib.prism_scan_workspace_size(1, 8, 16, 8192, 128, 128, 0) == 0
+    assert lib.prism_scan_workspace_size(0, 1, 1, 64, 128, 128, 2) == ctypes.c_size_t(-1).value
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -1,6 +1,6 @@
 """GPU parity of split erase/write strengths (SCAN_GDN_EW) and of PRISM's
-rank-L write (prism_expand, then the split-strength scan) against the float64
-oracle, through the C ABI.
+rank-L write (prism_expand, then the split-strength scan; and prism_scan, the
+same stream scanned in place) against the float64 oracle, through the C ABI.
 
 Gates as for the plain scan: relative Frobenius error per head <= 1e-5 for
 float32 data, <= 5e-3 for bfloat16 data with float32 state.  The expanded
@@ -132,12 +132,18 @@ PRISM_CASES = [("tiny-prism", 1, 2, 64), ("tiny-prism", 2, 1, 45),
                ("prism-b8h16t8192-l2", 1, 2, 150)]
 
 
-@pytest.mark.parametrize("name,B,H,T", PRISM_CASES)
-def test_prism_expand_stream(name, B, H, T):
+@pytest.mark.parametrize("name,B,H,T,W", [c + (None,) for c in PRISM_CASES] +
+                         [("prism-b8h16t8192-l2", 1, 1, 70, 1), ("prism-b8h16t8192-l2", 1, 1, 70, 8)])
+def test_prism_expand_stream(name, B, H, T, W):
+    """Pass-through rows exact, factor rows within storage rounding; the last two
+    cases take the anchor window to its ends (1 and the largest, 8 taps) over a
+    ragged second tile."""
     w = I.WORKLOADS[name]
+    if W is not None:
+        w = w.replace(prism_window=W)
     L = w.prism_steps
     G = L + 1
-    say(f"prism_expand {name} B{B} H{H} T{T} L{L}")
+    say(f"prism_expand {name} B{B} H{H} T{T} L{L} W{w.prism_window}")
     a = _prism_batch(w, T, B, H)
     q, k, v, alpha, beta, S0, x, beta_l, conv, Wk, Wp = a
     args, _ = _prism_gpu_args(w, a)
@@ -184,6 +190,38 @@ def test_prism_layer(name, B, H, T):
                 beta_l[b, h], None if S0 is None else S0[b, h].astype(np.float64),
                 factor_round=_factor_round(w.dtype))
     assert_parity(host(o), host(ST), o_ref, S_ref, w.dtype, what=name)
+
+
+@pytest.mark.parametrize("L,T", [(1, 200), (2, 64 * 21 + 1), (3, 333)])
+def test_prism_scan_in_place_equals_stream_scan_bitwise(L, T):
+    """prism_scan reads PRISM's element stream in place (q only on a token's last
+    element, k, v and gates from the token arrays or the factor rows, o once per
+    token): its o and S_T equal the sequential scan_fwd over prism_expand's
+    materialised stream, read at each token's last element, bit for bit.
+    Ragged element counts, tokens that straddle chunks (L = 2, 3)."""
+    w = I.WORKLOADS["prism-b8h16t8192-l2"].replace(prism_steps=L)
+    say(f"prism_scan in place vs stream scan: L{L} T{T} (elements {T * (L + 1)})")
+    a = _prism_batch(w, T, 1, 2)
+    args, S0d = _prism_gpu_args(w, a)
+    o1, S1 = gds.prism_scan(*args, S0d)
+    # (the sequential path, as the in-place scan: the tree brackets differently)
+    o2, S2 = gds.prism_scan_fwd(*args, S0d, stream=True, path="sequential")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2.contiguous()), "o differs"
+    assert torch.equal(S1, S2), "S_T differs"
+
+
+def test_prism_scan_without_corrections_is_the_gdn_scan():
+    """prism_scan with L = 0 is the gated-delta scan, bit for bit."""
+    w = I.WORKLOADS["prism-b8h16t8192-l2"]
+    say("prism_scan L=0 vs gdn scan (bitwise)")
+    q, k, v, alpha, beta, S0 = _batch(w, 130, (1, 2))
+    dt = w.dtype
+    args = (dev(q, dt), dev(k, dt), dev(v, dt), dev(alpha), dev(beta))
+    o1, S1 = gds.prism_scan(*args, S0=dev(S0))
+    o2, S2 = gds.scan_fwd(*args, dev(S0))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
 def test_prism_without_corrections_is_the_gdn_scan():
