@@ -90,9 +90,14 @@ def diag_mfma_flops(w) -> float:
     return per * -(-w.T // C) * (w.dv // S) * w.B * w.H
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    """First 16 hex digits of the SHA-256 of a source file (or of several,
+    concatenated in the order given)."""
+    h = hashlib.sha256()
+    for path in [paths] if isinstance(paths, str) else paths:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def decode_bytes(w) -> int:
@@ -106,9 +111,10 @@ def decode_bytes(w) -> int:
     return b
 
 
-def measured_traffic(kernel_src: str, summary: str):
+def measured_traffic(kernel_src, summary: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
+    when there is none or the kernel source changed since it was taken
+    (``kernel_src``: one source file, or a list whose concatenation is hashed)."""
     path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
         return None
@@ -476,7 +482,8 @@ def bench_prism(args, w):
         f"({stream_ms:.4f} ms through the materialised stream), wall {wall * 1e3:.1f} ms")
     alg = prism_layer_bytes(w)
     scan_flops_alg_ = scan_flops_alg(w.replace(T=T2))
-    src_scan = os.path.join(ROOT, "scan_sequence_models_amd", "csrc", "chunk_bf16.hip")
+    csrc = os.path.join(ROOT, "scan_sequence_models_amd", "csrc")
+    src_layer = [os.path.join(csrc, "prism.hip"), os.path.join(csrc, "chunk_bf16.hip")]
     result = {
         "metric": "tokens/s PRISM layer fwd (rank-L write, L=2; H=16, d=128, T=8192); "
                   "% MFMA / HBM roofline",
@@ -501,7 +508,7 @@ def bench_prism(args, w):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": alg / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(src_layer, f"prism_layer_{w.name}_traffic.txt"),
             "kernel": "the layer: prism_mfma_kernel (factor rows) + chunk_mfma_kernel (in-place stream)",
             "algorithmic_bytes_per_launch": alg,
             "kernel_ms": ms_per_step,
