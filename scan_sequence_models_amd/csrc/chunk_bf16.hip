@@ -137,6 +137,7 @@ struct Smem {
     float D[2][32 * LS];      // diagonal 32x32 blocks of T (natural)
     uint16_t Ost[C * LO];     // o of the chunk just read out [token][value] (natural rows)
     Gates gate[3];
+    int ezero[2];             // leaf aggregates, rows of E: state wave w's state is exactly zero
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -428,17 +429,29 @@ struct Unit {
 // aggregate are not written here).
 template <int MODE, int ROLE>
 __device__ __forceinline__ Unit unit_of(const ChunkJob& job) {
-    constexpr int NS = ROLE == kLeafAggregate && MODE == 0 ? 4 : 2;
+    constexpr bool EROWS = ROLE == kLeafAggregate && MODE == 0;
     const int units = job.heads * job.leaves;
     int u, sl;
-    const int x = blockIdx.x;
+    int x = blockIdx.x;
+    // With rows of E (slices 2, 3), the grid holds all of them first and the
+    // value rows (slices 0, 1) after: rows of E can stop early (erows_done),
+    // and the value rows then start on the CUs they free instead of waiting
+    // for a whole round of value rows.
+    int base = 0;
+    if (EROWS) {
+        if (x < 2 * units) {
+            base = 2;
+        } else {
+            x -= 2 * units;
+        }
+    }
     if ((units & 7) == 0) {
         const int xcd = x & 7, j = x >> 3;
-        u = (j / NS) * 8 + xcd;
-        sl = j % NS;
+        u = (j / 2) * 8 + xcd;
+        sl = base + j % 2;
     } else {
-        u = x / NS;
-        sl = x % NS;
+        u = x / 2;
+        sl = base + x % 2;
     }
     Unit un;
     un.head = u / job.leaves;
@@ -449,6 +462,22 @@ __device__ __forceinline__ Unit unit_of(const ChunkJob& job) {
     un.erows = ROLE == kLeafAggregate && sl >= 2;
     un.r0 = (sl & 1) * DVS;
     return un;
+}
+
+// Rows of E in a leaf aggregate carry S_t = S_{t-1} E_t from the identity with
+// v = 0.  Once that state is exactly zero it stays zero: X = K S^T = 0, so
+// U = 0 and the update only scales it (exact for finite inputs; a NaN state
+// never reads as zero).  A long leaf with decaying gates gets there well before
+// its end: the state waves then report it (ezero), and every wave leaves the
+// chunk loop at the top of the next step, all at the same barrier count.  The
+// zeros already in the state are the aggregate's rows.
+template <int ROLE>
+__device__ __forceinline__ bool erows_done(const Smem& sm, const Unit& un, int j) {
+    if constexpr (ROLE != kLeafAggregate) {
+        return false;
+    } else {
+        return un.erows && j > un.nb && (sm.ezero[0] & sm.ezero[1]) != 0;
+    }
 }
 
 // Gates of chunk c from alpha, beta, bw of token `lane` (0 past T; identity
@@ -652,6 +681,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 
     f32x16 qacc[2], xacc[2], oacc[2];
     for (int j = un.nb - 2; j < un.ne; ++j) {
+        if (erows_done<ROLE>(sm, un, j)) break;
         const bool act = j >= un.nb;
         const uint16_t* Kb = sm.K[j & 1];
         // ---- first half: X = K S^T and O^T = S Q^T, four independent chains;
@@ -791,6 +821,15 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkJob& job, const 
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) sacc[jt] = mfma32(ko[k & 1][jt], db[k], sacc[jt]);
             }
+            if (ROLE == kLeafAggregate && un.erows) {  // rows of E: is the state exactly zero?
+                bool nz = false;
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) nz |= sacc[jt][e] != 0.f;
+                const bool any = __builtin_amdgcn_ballot_w64(nz) != 0;
+                if (lane == 0) sm.ezero[vb] = any ? 0 : 1;
+            }
         }
         lds_barrier();
     }
@@ -924,6 +963,7 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
         }
     };
     for (int j = un.nb - 2; j < un.ne; ++j) {
+        if (erows_done<ROLE>(sm, un, j)) break;
         if (OUT && j - 1 >= un.nb) store_o(j - 1);
         if (GDN && j >= un.nb) convert(j);
         lds_barrier();
@@ -1046,6 +1086,7 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     auto run = [&](auto blk_c) {
         constexpr int B = decltype(blk_c)::value;
         for (int j = un.nb - 2; j < un.ne; ++j) {
+            if (erows_done<ROLE>(sm, un, j)) break;
             constexpr int st = 0;
             const int c = j + 1;  // chunk whose k-Gram tiles are built
             const bool build = GDN && c >= un.nb && c < un.ne;
@@ -1149,6 +1190,7 @@ __device__ __forceinline__ void aux_role(Smem& sm, const ChunkJob& job, const Un
         }
     }
     for (int j = un.nb - 2; j < un.ne; ++j) {
+        if (erows_done<ROLE>(sm, un, j)) break;
         if (j >= un.nb) {
             const Gates& G = sm.gate[j % 3];
             if (GDN && w == 6) {

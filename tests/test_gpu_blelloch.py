@@ -46,6 +46,27 @@ def test_blelloch_and_sequential_agree():
     assert_parity(o2, S2, o_ref, ST_ref, "bf16", what="sequential")
 
 
+def test_blelloch_leaf_rows_of_E_that_reach_zero():
+    """The rows of E in a leaf aggregate leave the chunk loop once their state is
+    exactly zero.  Head 0 decays strongly everywhere (alpha ~ U(0.3, 0.5): E
+    underflows within a few chunks of every 16-chunk leaf), head 1 has the long
+    workload's mild gates (no leaf gets there), head 2 decays strongly in the
+    first half of the sequence only; one launch holds all three.  Against the
+    oracle and against the sequential path."""
+    w = _w("gdn", 64 * 64 + 9, B=1, H=3)
+    b = I.batch_inputs(w)
+    rng = np.random.default_rng(17)
+    T = w.T
+    b.alpha[0, 0] = rng.uniform(0.3, 0.5, T).astype(b.alpha.dtype)
+    b.alpha[0, 2, : T // 2] = rng.uniform(0.3, 0.5, T // 2).astype(b.alpha.dtype)
+    say("blelloch, rows of E that reach zero")
+    o1, S1 = gpu_scan(w, b, path="blelloch", leaf_chunks=16)
+    o2, S2 = gpu_scan(w, b, path="sequential")
+    o_ref, S_ref = oracle_scan(w, b)
+    assert_parity(o1, S1, o_ref, S_ref, "bf16", what="blelloch, E rows reaching zero")
+    assert_parity(o2, S2, o_ref, S_ref, "bf16", what="sequential, same gates")
+
+
 def test_blelloch_zero_state_and_repeatable():
     w = _w("gdn", 64 * 20, B=1, H=2).replace(s0_var=None)
     b = I.batch_inputs(w)
