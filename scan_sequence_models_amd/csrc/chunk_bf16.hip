@@ -41,12 +41,14 @@
 //   waves 4, 5  first half: o of chunk j-1 stored from LDS (16-byte stores),
 //               and the two diagonal blocks D_0, D_1 of chunk j scaled into the
 //               bf16 factors Tb = D diag(bw), Tbn = -D diag(beta gamma);
-//               second half: chunk j+1's q, k, v staged in LDS, then chunk
-//               j+2's rows loaded into registers (coalesced 16-byte loads).
+//               second half: chunk j+1's q and v (and, with gated linear
+//               attention, k) staged in LDS, then chunk j+2's rows loaded into
+//               registers (coalesced 16-byte loads).
 //   wave 2      first half: chunk j+1's two diagonal k-Gram tiles; second
 //               half: the gates of chunk j+2 (a wave scan of ln alpha).
 //   wave 3      first half: chunk j's score tile (0,0); second half: chunk
-//               j+1's off-diagonal k-Gram tile.
+//               j+1's off-diagonal k-Gram tile, then (delta rule) chunk j+1's k
+//               rows staged in LDS from the registers that tile read.
 //   wave 6      first half: G = -D_1 A_bl of chunk j by a split-bf16 product
 //               (hi/lo parts, three MFMAs per product), stored as bf16 in
 //               Tb's lower-left block; second half: D_0 of chunk j+1 (16x16
@@ -872,18 +874,16 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
     // v: values 8vc..8vc+7 of tokens 4vt + i, i < 4
     const int jc = x & 15, tg = x >> 4;
     const int vc = x & 7, vt = x >> 3;
+    // (with the delta rule, k-Gram wave 3 stages the k rows: it holds them in
+    // registers for its own products)
     uint4 qr[8], kr[8], vr[4];
-    uint4 kr2[8], vr2[4];  // kPrism: the factor-row parts, merged at staging
+    uint4 vr2[4];  // kPrism: the factor-row parts, merged at staging
     auto load = [&](int c) {
         if constexpr (ROLE == kPrism) {
             const PrismSrc P(job, un.head, un.r0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int e = c * C + 32 * (i >> 2) + 4 * tg + (i & 3);
-                unsigned a, b;
-                P.rows(e, DK, a, b);
-                kr[i] = P.ld(P.k, a + 16 * jc);
-                kr2[i] = P.ld(P.kf, b + 16 * jc);
                 qr[i] = P.ld(P.q, P.q_rows(e) + 16 * jc);
             }
 #pragma unroll
@@ -899,7 +899,7 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 32 * (i >> 2) + 4 * tg + (i & 3);
-            kr[i] = rk.at(row, 8 * jc);
+            if (!GDN) kr[i] = rk.at(row, 8 * jc);
             if (OUT) qr[i] = rq.at(row, 8 * jc);
         }
 #pragma unroll
@@ -910,7 +910,7 @@ __device__ __forceinline__ void load_role(Smem& sm, const ChunkJob& job, const U
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int prow = perm5(32 * (i >> 2) + 4 * tg + (i & 3));
-            *reinterpret_cast<uint4*>(Kb + kidx(prow, 8 * jc)) = ROLE == kPrism ? orv(kr[i], kr2[i]) : kr[i];
+            if (!GDN) *reinterpret_cast<uint4*>(Kb + kidx(prow, 8 * jc)) = kr[i];
             if (OUT) *reinterpret_cast<uint4*>(&sm.Q[prow * LQ + 8 * jc]) = qr[i];
         }
         uint16_t* Vb = sm.V[c & 1];
@@ -1150,6 +1150,15 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ChunkJob& job, const U
     #pragma unroll
                     for (int kk = 0; kk < 8; ++kk) a = mfma32(kreg[st][1][kk], kreg[st][0][kk], a);
                     gram_mask(a, 1, 0, fast, ws0, wt1, sm.Ablt[c & 1]);
+                    // chunk c's k rows into LDS for the other waves (row 32 b + l32 at
+                    // LDS row perm5 of it), before the registers take chunk c + 1
+                    uint16_t* Kb = sm.K[c & 1];
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk)
+                            *reinterpret_cast<bf16x8*>(Kb + kidx(perm5(32 * b + l32), 16 * kk + 8 * h)) =
+                                kreg[st][b][kk];
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (GDN && c + 1 < un.ne) load(c + 1);
