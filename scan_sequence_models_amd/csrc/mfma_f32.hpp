@@ -63,7 +63,10 @@ __device__ __forceinline__ void split_bf16(const f32x8& x, bf16x8& hi, bf16x8& l
 // one 32x32x16 step.  Which k a value stands for does not matter as long as A
 // and B agree, so A(s) and B(s) are the same accessors as for chain.  A group's
 // operands are read one group ahead of its products.
-template <int STEPS, class FA, class FB>
+// AX / BX: the A / B operands are bf16 values exactly (inputs given in bf16,
+// read before any scaling), so their lo parts are zero: the product then needs
+// two MFMAs (one if both are exact) and no lo conversion for that side.
+template <int STEPS, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ f32x16 chain_split(FA A, FB B, f32x16 c) {
     static_assert(STEPS % 8 == 0, "groups of eight steps");
     constexpr int G = STEPS / 8;
@@ -84,12 +87,18 @@ __device__ __forceinline__ f32x16 chain_split(FA A, FB B, f32x16 c) {
             }
         }
         bf16x8 ah, al, bh, bl;
-        split_bf16(a, ah, al);
-        split_bf16(b, bh, bl);
+        if constexpr (AX)
+            ah = __builtin_convertvector(a, bf16x8);
+        else
+            split_bf16(a, ah, al);
+        if constexpr (BX)
+            bh = __builtin_convertvector(b, bf16x8);
+        else
+            split_bf16(b, bh, bl);
         __builtin_amdgcn_sched_barrier(0);
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+        if constexpr (!BX) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+        if constexpr (!AX) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         a = an;
         b = bn;
@@ -97,11 +106,12 @@ __device__ __forceinline__ f32x16 chain_split(FA A, FB B, f32x16 c) {
     return c;
 }
 
-// chain in float32 or, with SPLIT and whole groups of eight steps, in split bf16.
-template <bool SPLIT, int STEPS, class FA, class FB>
+// chain in float32 or, with SPLIT and whole groups of eight steps, in split bf16
+// (AX, BX as for chain_split; they hold only where SPLIT does: bf16 inputs).
+template <bool SPLIT, int STEPS, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ f32x16 chain_t(FA A, FB B, f32x16 c) {
     if constexpr (SPLIT && STEPS % 8 == 0)
-        return chain_split<STEPS>(A, B, c);
+        return chain_split<STEPS, AX, BX>(A, B, c);
     else
         return chain<STEPS>(A, B, c);
 }

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
         if constexpr (GDN) {
             if (w == 0) {  // B = strict_lower(Gamma o K K^T)
                 auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
-                const f32x16 c = chain_t<SPLIT, DK / 2>(kr, kr, f32x16{});
+                const f32x16 c = chain_t<SPLIT, DK / 2, true, true>(kr, kr, f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
@@ -272,14 +272,15 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
                 }
             } else if (w < 3) {  // X = beta V - beta gamma K S^T, value columns 32 (w - 1) ..
                 const int I = w - 1;
-                f32x16 c;
+                // (K S^T with k exact in bf16; the row scalings after the product)
+                const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
+                                                     [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
+                                                     f32x16{});
 #pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = bw[row(e)] * Us[row(e) * LV + 32 * I + l32];
-                const float nbg = -bg[l32];
-                c = chain_t<SPLIT, DK / 2>([&](int s) { return nbg * Ks[l32 * L1 + 2 * s + kg]; },
-                                  [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; }, c);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e), y = t * LV + 32 * I + l32;
+                    Us[y] = bw[t] * Us[y] - bg[t] * c[e];
+                }
             }
             __syncthreads();
             if (w == 0) {  // T, then U = T X in place
@@ -301,8 +302,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = gC[0] * Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
-            c = chain_t<SPLIT, kC / 2>([&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
-                              [&](int s) { return Dd[2 * s + kg] * Ks[(2 * s + kg) * L1 + 32 * Jt + l32]; }, c);
+            c = chain_t<SPLIT, kC / 2, false, true>(
+                [&](int s) { return Dd[2 * s + kg] * Us[(2 * s + kg) * LV + 32 * I + l32]; },
+                [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * Jt + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
         }
@@ -447,15 +449,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 1: B, P, X; the owners start dQ = diag(gamma) dO S (+ its dg share)
         if (GDN && w == 0) {
             auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
-            const f32x16 c = chain_t<SPLIT, DK / 2>(kr, kr, f32x16{});
+            const f32x16 c = chain_t<SPLIT, DK / 2, true, true>(kr, kr, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
                 Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
             }
         } else if (w == 1) {
-            const f32x16 c = chain_t<SPLIT, DK / 2>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
-                                           [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
+            const f32x16 c = chain_t<SPLIT, DK / 2, true, true>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
+                                                       [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
@@ -465,8 +467,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int I = w - 2;
             // (K S^T)^T = S K^T with the token along the lanes: X_t = beta_t V_t - beta_t gamma_t (K S^T)_t
             // is written row by row, and the tile serves <dX_t, (K S^T)_t> in phase 5 as an in-lane sum
-            ksT = chain_t<SPLIT, DK / 2>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
-                                [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
+            ksT = chain_t<SPLIT, DK / 2, false, true>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
+                                             [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
             const float b = bw[l32], nbg = -bg[l32];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -475,16 +477,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
             const int I = w - 2;
-            const float dd = Dd[l32];
-            const f32x16 c = chain_t<SPLIT, DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
-                                           [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; }, f32x16{});
+            const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
+                                                 [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
+                                                 f32x16{});
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
+            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
         }
         if (w < NJ) {
-            const float gl = gam[l32];
-            accQ = chain_t<SPLIT, kSL / 2>([&](int s) { return gl * dOs[l32 * LV + 2 * s + kg]; },
-                                  [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
+            // diag(gamma) dO S, with dO exact in bf16 and gamma applied to the rows after
+            accQ = chain_t<SPLIT, kSL / 2, true>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
+                                        [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) accQ[e] *= gam[row(e)];
             f32x16 x;
 #pragma unroll
             for (int e = 0; e < 16; ++e) x[e] = accQ[e] * Qs[row(e) * L1 + 32 * w + l32];
@@ -505,20 +509,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             } else if (w < 3) {
                 const int I = w - 1;
-                const float dd = Dd[l32];
-                const f32x16 c = chain_t<SPLIT, DK / 2>([&](int s) { return dd * Ks[l32 * L1 + 2 * s + kg]; },
-                                               [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
-                                               f32x16{});
+                const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
+                                                     [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
+                                                     f32x16{});
 #pragma unroll
-                for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
+                for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
             }
             __syncthreads();
         }
         // Phase 3: dP (waves 0 and 3 both form it: wave 0 writes dP * Gamma, wave 3 the
         // row and column sums of dP * P), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
         if (w == 0 || w == 3) {
-            const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
-                                            [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
+            const f32x16 c = chain_t<SPLIT, kSL / 2, true>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
+                                                  [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
             if (w == 0) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -551,8 +554,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
-            c = chain_t<SPLIT, kC / 2>([&](int s) { return Pm[(2 * s + kg) * LM + l32]; },
-                              [&](int s) { return dOs[(2 * s + kg) * LV + 32 * I + l32]; }, c);
+            c = chain_t<SPLIT, kC / 2, false, true>([&](int s) { return Pm[(2 * s + kg) * LM + l32]; },
+                                           [&](int s) { return dOs[(2 * s + kg) * LV + 32 * I + l32]; }, c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
@@ -586,10 +589,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         if (w < NJ) {
-            accQ = chain_t<SPLIT, kC / 2>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
-                                 [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
-            accK = chain_t<SPLIT, kC / 2>([&](int s) { return dQKm[(2 * s + kg) * LM + l32]; },
-                                 [&](int s) { return Qs[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
+            accQ = chain_t<SPLIT, kC / 2, false, true>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
+                                              [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
+            accK = chain_t<SPLIT, kC / 2, false, true>([&](int s) { return dQKm[(2 * s + kg) * LM + l32]; },
+                                              [&](int s) { return Qs[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
         }
         __syncthreads();
         // the next chunk's inputs are in flight through phases 5 and 6
@@ -657,16 +660,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 ss += d * Ss[y];
                 c[e] = gC[0] * d;
             }
-            // the two products as one chain over 2 C (GDN) or C tokens
+            // the two products as one chain over 2 C (GDN) or C tokens; the token
+            // scalings sit on the dO and dX side, so q and k stay exact in bf16
             constexpr int H2 = kC / 2;
-            c = chain_t<SPLIT, GDN ? kC : H2>(
+            c = chain_t<SPLIT, GDN ? kC : H2, false, true>(
                 [&](int s) {
                     const int t = 2 * (s % H2) + kg;
-                    return s < H2 ? dOs[t * LV + 32 * I + l32] : -Vs[t * LV + 32 * I + l32];
+                    return s < H2 ? dOs[t * LV + 32 * I + l32] : -bg[t] * Vs[t * LV + 32 * I + l32];
                 },
                 [&](int s) {
                     const int t = 2 * (s % H2) + kg;
-                    return s < H2 ? Qs[t * L1 + 32 * Jt + l32] : bg[t] * Ks[t * L1 + 32 * Jt + l32];
+                    return s < H2 ? Qs[t * L1 + 32 * Jt + l32] : Ks[t * L1 + 32 * Jt + l32];
                 },
                 c);
 #pragma unroll
@@ -678,7 +682,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 6: dK += (dKK + dKK^T) K; partial dq, dk; dg -> d ln alpha, dbeta
         if (w < NJ) {
             if constexpr (GDN)
-                accK = chain_t<SPLIT, kC / 2>(
+                accK = chain_t<SPLIT, kC / 2, false, true>(
                     [&](int s) { return dKKm[l32 * LM + 2 * s + kg] + dKKm[(2 * s + kg) * LM + l32]; },
                     [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
 #pragma unroll
@@ -732,7 +736,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int x = tid; x < kSL * DK; x += kThreads) J.dS0[s_base + x] = dSs[x / DK * L1 + x % DK];
 }
 
-// Sum of the per-slice partials; dalpha = d ln alpha / alpha.
+// Sum of the per-slice partials; dalpha = d ln alpha / alpha.  dq and dk in
+// 16-byte pieces (dk is a multiple of 4), then the per-token values.
 __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdJob J) {
     const size_t n_tok = (size_t)J.BH * J.T;
     const size_t n_el = n_tok * J.dk;
@@ -742,26 +747,29 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdJob J) {
     const float* pdl = pdk + (size_t)slices * n_el;
     const float* pdb = pdl + (size_t)slices * n_tok;
     const float* pdbw = pdb + (size_t)slices * n_tok;
-    for (size_t x = (size_t)blockIdx.x * kThreads + threadIdx.x; x < n_el; x += (size_t)gridDim.x * kThreads) {
-        float a = 0.f, b = 0.f;
+    const size_t stride = (size_t)gridDim.x * kThreads, x0 = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const size_t n4 = n_el / 4;
+    const f32x4* pq4 = reinterpret_cast<const f32x4*>(pdq);
+    const f32x4* pk4 = reinterpret_cast<const f32x4*>(pdk);
+    for (size_t x = x0; x < n4; x += stride) {
+        f32x4 a = pq4[x], b = pk4[x];
+        for (int s = 1; s < slices; ++s) {
+            a += pq4[s * n4 + x];
+            b += pk4[s * n4 + x];
+        }
+        reinterpret_cast<f32x4*>(J.dq)[x] = a;
+        reinterpret_cast<f32x4*>(J.dk_out)[x] = b;
+    }
+    for (size_t tk = x0; tk < n_tok; tk += stride) {
+        float l = 0.f, d = 0.f, dw = 0.f;
         for (int s = 0; s < slices; ++s) {
-            a += pdq[s * n_el + x];
-            b += pdk[s * n_el + x];
+            l += pdl[s * n_tok + tk];
+            d += pdb[s * n_tok + tk];
+            if (J.dbeta_w) dw += pdbw[s * n_tok + tk];
         }
-        J.dq[x] = a;
-        J.dk_out[x] = b;
-        if (x % J.dk == 0) {
-            const size_t tk = x / J.dk;
-            float l = 0.f, d = 0.f, dw = 0.f;
-            for (int s = 0; s < slices; ++s) {
-                l += pdl[s * n_tok + tk];
-                d += pdb[s * n_tok + tk];
-                if (J.dbeta_w) dw += pdbw[s * n_tok + tk];
-            }
-            J.dalpha[tk] = l / J.alpha[tk];
-            if (J.dbeta) J.dbeta[tk] = d;
-            if (J.dbeta_w) J.dbeta_w[tk] = dw;
-        }
+        J.dalpha[tk] = l / J.alpha[tk];
+        if (J.dbeta) J.dbeta[tk] = d;
+        if (J.dbeta_w) J.dbeta_w[tk] = dw;
     }
 }
 
@@ -770,8 +778,8 @@ hipError_t launch_typed(const BwdJob& J, hipStream_t s) {
     const dim3 grid((unsigned)((size_t)J.BH * (J.dv / kSL)));
     hipLaunchKernelGGL((bwd_states_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
     hipLaunchKernelGGL((bwd_chunk_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
-    const size_t n_el = (size_t)J.BH * J.T * J.dk;
-    const size_t want = (n_el + kThreads - 1) / kThreads;
+    const size_t n4 = (size_t)J.BH * J.T * J.dk / 4;
+    const size_t want = (n4 + kThreads - 1) / kThreads;
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3(blocks), dim3(kThreads), 0, s, J);
     return hipGetLastError();
