@@ -272,12 +272,16 @@ int prism_scan(int dtype, int B, int H, int T, int dk, int dv, int L, int W,
  *   dalpha: [B, H, T] float32        dbeta: like beta, float32 (NULL for SCAN_GLA)
  *   dS0: [B, H, dv, dk] float32 (the gradient at the initial state, also when S0 is NULL)
  *   workspace: scan_bwd_workspace_size(...) bytes of device scratch, 256-byte
- *          aligned (the state entering every 32-token chunk, and per value-slice
- *          partial sums); reusable across calls ordered on one stream.
+ *          aligned (the state entering every 32-token chunk and, with more than
+ *          two 64-row value slices, per-slice partial sums); reusable across
+ *          calls ordered on one stream.
  * All gradients are float32 whatever dtype is.  Outputs may not overlap inputs,
  * each other or the workspace.  Supported: dk in {32, 64, 128}, dv a multiple of
  * 64 (at most 4096).  Three kernels run on `stream`: a forward pass storing the
- * chunk states, the reverse chunk pass, and a reduction over value slices.
+ * chunk states, the reverse chunk pass, and a reduction over value slices (with
+ * dv <= 128 the reverse pass adds the slices' sums into dq, dk_out, dalpha and
+ * dbeta itself and the last kernel only divides by alpha; the result is still
+ * the same bit for bit from run to run).
  * Returns SCAN_OK or an error status; scan_bwd_workspace_size returns
  * (size_t)-1 for invalid or unsupported arguments.
  */

@@ -34,8 +34,12 @@
 //   bwd_chunk_kernel: the chunks in reverse order, recomputing each chunk's
 //     factors from its stored state and carrying dS in LDS; dv and dS0 rows
 //     belong to the slice and are written in full, dq, dk, d ln alpha and dbeta
-//     are sums over value rows and are written as per-slice partials;
-//   bwd_reduce_kernel: the sum over slices and dalpha = d ln alpha / alpha.
+//     are sums over value rows: with one or two slices they go straight into the
+//     outputs (two slices add onto zeros written by the states pass, with float
+//     atomics: a + b = b + a, so the result does not depend on their order),
+//     with more as per-slice partials;
+//   bwd_reduce_kernel (more than two slices): the sum over slices and
+//     dalpha = d ln alpha / alpha; bwd_finish_kernel (else): the division.
 // Products are 32x32 tiles on the float32 MFMA (v_mfma_f32_32x32x2f32).
 #include <type_traits>
 
@@ -241,6 +245,16 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     for (int n = 0; n < J.nchunks; ++n) {
         const int c0 = n * kC;
         __syncthreads();
+        if (slices == 2) {  // the outputs the reverse pass adds into: slice 0 dq, slice 1 dk, slice 0 the rest
+            float* dst = (sl == 0 ? J.dq : J.dk_out) + (tok0 + c0) * DK;
+            const int n4 = min(kC, T - c0) * DK / 4;
+            for (int x = tid; x < n4; x += kThreads) reinterpret_cast<f32x4*>(dst)[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sl == 0 && tid < kC && c0 + tid < T) {
+                J.dalpha[tok0 + c0 + tid] = 0.f;
+                if (J.dbeta) J.dbeta[tok0 + c0 + tid] = 0.f;
+                if (J.dbeta_w) J.dbeta_w[tok0 + c0 + tid] = 0.f;
+            }
+        }
         float4* ck4 = reinterpret_cast<float4*>(J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK);
 #pragma unroll
         for (int m = 0; m < kSL * DK / 4 / kThreads; ++m) {
@@ -360,6 +374,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     float* pdb = pdl + (size_t)slices * J.BH * T;
     float* pdbw = pdb + (size_t)slices * J.BH * T;  // write strengths (split strengths only)
     auto row = [&](int e) { return acc_row(e, kg); };
+    // a sum over value rows into its output: stored (one slice) or added onto
+    // the zeros the states pass wrote (two slices)
+    auto put = [&](float* p, float x) {
+        if (slices == 1)
+            *p = x;
+        else
+            unsafeAtomicAdd(p, x);
+    };
 
     for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
     if constexpr (GDN)
@@ -689,9 +711,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
                 if (c0 + t < T) {
-                    const size_t o = (part_tok + c0 + t) * DK + 32 * w + l32;
-                    pdq[o] = accQ[e];
-                    pdk[o] = accK[e];
+                    if (slices > 2) {
+                        const size_t o = (part_tok + c0 + t) * DK + 32 * w + l32;
+                        pdq[o] = accQ[e];
+                        pdk[o] = accK[e];
+                    } else {
+                        const size_t o = (tok0 + c0 + t) * DK + 32 * w + l32;
+                        put(J.dq + o, accQ[e]);
+                        put(J.dk_out + o, accK[e]);
+                    }
                 }
             }
         }
@@ -722,12 +750,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int s = 2; s < 8; ++s) dbe += dbp[s * kC + t];
             if (kg == 0 && c0 + t < T) {
-                pdl[part_tok + c0 + t] = dg;
-                if (J.dbeta_w) {
-                    pdb[part_tok + c0 + t] = dbe;
-                    pdbw[part_tok + c0 + t] = dbw;
+                if (slices > 2) {
+                    pdl[part_tok + c0 + t] = dg;
+                    if (J.dbeta_w) {
+                        pdb[part_tok + c0 + t] = dbe;
+                        pdbw[part_tok + c0 + t] = dbw;
+                    } else {
+                        pdb[part_tok + c0 + t] = dbe + dbw;
+                    }
                 } else {
-                    pdb[part_tok + c0 + t] = dbe + dbw;
+                    const size_t tk = tok0 + c0 + t;
+                    put(J.dalpha + tk, dg);  // d ln alpha until bwd_finish_kernel
+                    if (J.dbeta_w) {
+                        put(J.dbeta + tk, dbe);
+                        put(J.dbeta_w + tk, dbw);
+                    } else if (J.dbeta) {
+                        put(J.dbeta + tk, dbe + dbw);
+                    }
                 }
             }
         }
@@ -773,15 +812,28 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdJob J) {
     }
 }
 
+// dalpha = d ln alpha / alpha (one or two value slices: the sums are in place).
+__global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdJob J) {
+    const size_t n_tok = (size_t)J.BH * J.T;
+    for (size_t tk = (size_t)blockIdx.x * kThreads + threadIdx.x; tk < n_tok; tk += (size_t)gridDim.x * kThreads)
+        J.dalpha[tk] /= J.alpha[tk];
+}
+
 template <int MODE, int DK, typename E>
 hipError_t launch_typed(const BwdJob& J, hipStream_t s) {
     const dim3 grid((unsigned)((size_t)J.BH * (J.dv / kSL)));
     hipLaunchKernelGGL((bwd_states_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
     hipLaunchKernelGGL((bwd_chunk_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
-    const size_t n4 = (size_t)J.BH * J.T * J.dk / 4;
-    const size_t want = (n4 + kThreads - 1) / kThreads;
-    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(blocks), dim3(kThreads), 0, s, J);
+    if (J.dv / kSL > 2) {
+        const size_t n4 = (size_t)J.BH * J.T * J.dk / 4;
+        const size_t want = (n4 + kThreads - 1) / kThreads;
+        const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3(blocks), dim3(kThreads), 0, s, J);
+    } else {
+        const size_t want = ((size_t)J.BH * J.T + kThreads - 1) / kThreads;
+        const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+        hipLaunchKernelGGL(bwd_finish_kernel, dim3(blocks), dim3(kThreads), 0, s, J);
+    }
     return hipGetLastError();
 }
 
@@ -804,7 +856,8 @@ bool scan_bwd_supported(int dk, int dv) {
 size_t scan_bwd_workspace_floats(int BH, int T, int dk, int dv) {
     const size_t nchunks = ((size_t)T + kC - 1) / kC;
     const size_t slices = (size_t)dv / kSL;
-    return (size_t)BH * nchunks * dv * dk + slices * BH * T * (2 * (size_t)dk + 3);
+    // per-slice partials only with more than two value slices
+    return (size_t)BH * nchunks * dv * dk + (slices > 2 ? slices * BH * T * (2 * (size_t)dk + 3) : 0);
 }
 
 hipError_t launch_scan_bwd(int mode, int dtype, BwdJob J, hipStream_t s) {
