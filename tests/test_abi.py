@@ -293,13 +293,15 @@ def test_scan_bwd_rejects(lib, kw, code):
 
 
 def test_scan_bwd_workspace_sizes(lib):
-    # the state entering every 32-token chunk, then per-64-row-slice partials of
-    # dq, dk (dk floats per token) and of d ln alpha and the two strength planes
-    # (one float each)
+    # the state entering every 32-token chunk; with more than two 64-row value
+    # slices also per-slice partials of dq, dk (dk floats per token) and of
+    # d ln alpha and the two strength planes (one float each); with one or two
+    # slices the sums go straight into the outputs
     n = lib.scan_bwd_workspace_size(0, 1, 8, 16, 8192, 128, 128)
-    assert n == 4 * (128 * 256 * 128 * 128 + 2 * 128 * 8192 * (2 * 128 + 3))
-    assert lib.scan_bwd_workspace_size(1, 0, 1, 1, 33, 32, 64) == 4 * (2 * 64 * 32 + 1 * 33 * 67)
-    assert lib.scan_bwd_workspace_size(2, 1, 1, 1, 64, 128, 128) == 4 * (2 * 128 * 128 + 2 * 64 * 259)
+    assert n == 4 * (128 * 256 * 128 * 128)
+    assert lib.scan_bwd_workspace_size(1, 0, 1, 1, 33, 32, 64) == 4 * (2 * 64 * 32)
+    assert lib.scan_bwd_workspace_size(2, 1, 1, 1, 64, 128, 128) == 4 * (2 * 128 * 128)
+    assert lib.scan_bwd_workspace_size(0, 0, 1, 1, 70, 128, 192) == 4 * (3 * 192 * 128 + 3 * 70 * 259)
     assert lib.scan_bwd_workspace_size(0, 1, 1, 1, 64, 128, 96) == ctypes.c_size_t(-1).value
     assert lib.scan_bwd_workspace_size(3, 1, 1, 1, 64, 128, 128) == ctypes.c_size_t(-1).value
 
