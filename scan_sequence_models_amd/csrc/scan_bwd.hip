@@ -468,7 +468,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
         f32x16 accQ = {}, accK = {};
         f32x16 ksT = {};  // waves 2, 3 (delta rule): (K S^T)^T on value columns 32 (w - 2) .., kept to phase 5
-        // Phase 1: B, P, X; the owners start dQ = diag(gamma) dO S (+ its dg share)
+        // the owners' dQ = diag(gamma) dO S (+ its dg share)
+        auto owner_dq = [&]() {
+            // dO exact in bf16, gamma applied to the rows after
+            accQ = chain_t<SPLIT, kSL / 2, true>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
+                                        [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) accQ[e] *= gam[row(e)];
+            f32x16 x;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = accQ[e] * Qs[row(e) * L1 + 32 * w + l32];
+            store_row_sums(x, dgp + w * kC, l32, kg, 1.f);  // dg slots 0..3
+        };
+        // Phase 1: B and then T (wave 0, delta rule), P, X; the other owners' dQ part
         if (GDN && w == 0) {
             auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
             const f32x16 c = chain_t<SPLIT, DK / 2, true, true>(kr, kr, f32x16{});
@@ -477,6 +489,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int t = row(e);
                 Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
             }
+            // the same wave solves right away: its own B rows are complete once
+            // its LDS writes are
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            solve_unit_lower(Bm, bet, Tm, lane);
         } else if (w == 1) {
             const f32x16 c = chain_t<SPLIT, DK / 2, true, true>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
                                                        [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
@@ -505,22 +521,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
         }
-        if (w < NJ) {
-            // diag(gamma) dO S, with dO exact in bf16 and gamma applied to the rows after
-            accQ = chain_t<SPLIT, kSL / 2, true>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
-                                        [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) accQ[e] *= gam[row(e)];
-            f32x16 x;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) x[e] = accQ[e] * Qs[row(e) * L1 + 32 * w + l32];
-            store_row_sums(x, dgp + w * kC, l32, kg, 1.f);  // dg slots 0..3
-        }
+        // (with the delta rule wave 0's share waits for phase 2, beside the others' work)
+        if (w < NJ && !(GDN && w == 0)) owner_dq();
         __syncthreads();
-        // Phase 2 (delta rule): T and U = T X; dU = Kd dS'^T
+        // Phase 2 (delta rule): wave 0's dQ part; U = T X (wave 3); dU = Kd dS'^T (waves 1, 2)
         if constexpr (GDN) {
             if (w == 0) {
-                solve_unit_lower(Bm, bet, Tm, lane);
+                owner_dq();
+            } else if (w == 3) {
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
                     const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
                     for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
                 }
-            } else if (w < 3) {
+            } else {
                 const int I = w - 1;
                 const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
                                                      [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
@@ -671,7 +679,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 J.dv_out[(tok0 + c0 + t) * dv + r0 + i] = GDN ? bw[t] * Vs[t * LV + i] : dUs[t * LV + i];
         }
         // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K, and <dS', S>
-        for (int tile = w; tile < 2 * NJ; tile += 4) {
+        // (delta rule, dk = 128: waves 0, 1 formed dA above, so they take one of
+        // the 8 tiles each and waves 2, 3 three each)
+        constexpr bool kSkew = GDN && NJ == 4;
+        const int t_lo = kSkew ? (w < 2 ? w : 3 * w - 4) : w;
+        const int t_hi = kSkew ? (w < 2 ? w + 1 : 3 * w - 1) : 2 * NJ;
+        for (int tile = t_lo; tile < t_hi; tile += kSkew ? 1 : 4) {
             const int I = tile / NJ, Jt = tile - I * NJ;
             f32x16 c;
             float ss = 0.f;
