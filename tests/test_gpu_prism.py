@@ -192,13 +192,14 @@ def test_prism_layer(name, B, H, T):
     assert_parity(host(o), host(ST), o_ref, S_ref, w.dtype, what=name)
 
 
-@pytest.mark.parametrize("L,T", [(1, 200), (2, 64 * 21 + 1), (3, 333)])
+@pytest.mark.parametrize("L,T", [(1, 200), (2, 64 * 21 + 1), (3, 333), (8, 100), (2, 1)])
 def test_prism_scan_in_place_equals_stream_scan_bitwise(L, T):
     """prism_scan reads PRISM's element stream in place (q only on a token's last
     element, k, v and gates from the token arrays or the factor rows, o once per
     token): its o and S_T equal the sequential scan_fwd over prism_expand's
     materialised stream, read at each token's last element, bit for bit.
-    Ragged element counts, tokens that straddle chunks (L = 2, 3)."""
+    Ragged element counts, tokens that straddle chunks (L = 2, 3), the largest
+    L (8: nine elements per token) and a single token."""
     w = I.WORKLOADS["prism-b8h16t8192-l2"].replace(prism_steps=L)
     say(f"prism_scan in place vs stream scan: L{L} T{T} (elements {T * (L + 1)})")
     a = _prism_batch(w, T, 1, 2)
