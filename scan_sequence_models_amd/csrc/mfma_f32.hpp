@@ -116,4 +116,60 @@ __device__ __forceinline__ f32x16 chain_t(FA A, FB B, f32x16 c) {
         return chain<STEPS>(A, B, c);
 }
 
+// chain_t over 8 G steps with the operands fetched a group at a time: A(i) and
+// B(i) give the lane's operands of steps 8 i .. 8 i + 7 as one f32x8, so an
+// operand laid out along k can come in two 16-byte LDS reads (with the usual
+// choice k = 16 i + 8 kg + j for step 8 i + j of lane half kg).  Group i + 1 is
+// read before group i's products.  AX / BX as for chain_split.
+template <bool SPLIT, int G, bool AX = false, bool BX = false, class FA, class FB>
+__device__ __forceinline__ f32x16 chain8_t(FA A, FB B, f32x16 c) {
+    f32x8 a = A(0), b = B(0);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        f32x8 an = a, bn = b;
+        if (i + 1 < G) {
+            an = A(i + 1);
+            bn = B(i + 1);
+        }
+        if constexpr (SPLIT) {
+            bf16x8 ah, al, bh, bl;
+            if constexpr (AX)
+                ah = __builtin_convertvector(a, bf16x8);
+            else
+                split_bf16(a, ah, al);
+            if constexpr (BX)
+                bh = __builtin_convertvector(b, bf16x8);
+            else
+                split_bf16(b, bh, bl);
+            __builtin_amdgcn_sched_barrier(0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+            if constexpr (!BX) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+            if constexpr (!AX) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c = mfma2(a[j], b[j], c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        a = an;
+        b = bn;
+    }
+    return c;
+}
+
+// Eight floats from 16-byte aligned LDS as two 16-byte reads.
+__device__ __forceinline__ f32x8 lds_f32x8(const float* p) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Eight floats down a column: p[0], p[ld], .., p[7 ld].
+template <int LD>
+__device__ __forceinline__ f32x8 lds_col8(const float* p) {
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = p[j * LD];
+    return r;
+}
+
 }  // namespace gds

@@ -125,12 +125,13 @@ __device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, float w_ra
 }
 
 // T = (I + diag(bet) B)^-1 for the strictly lower part of B (row stride LB, as
-// float4 rows) into Tm (row stride LM), from its 16x16 blocks: the two diagonal
+// float4 rows) into Tm (row stride LT), from its 16x16 blocks: the two diagonal
 // blocks D0, D1 by forward substitution side by side (lane (b, c) of each
 // half-wave owns column c of block b, x_r = [r == c] - bet_r sum_{j<r} B_rj x_j,
 // rows read as float4 two rows ahead), then T10 = -D1 diag(bet) B10 D0 on the
 // fp32 MFMA (16x16x4).  The upper right block of Tm stays zero from the start.
 // All 64 lanes of the wave take part.
+template <int LT = LM>
 __device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* bet, float* Tm, int lane) {
     const int b = (lane >> 4) & 1, c = lane & 15, kg = lane >> 5;
     const float* Bb = Bm + 16 * b * LB + 16 * b;
@@ -164,7 +165,7 @@ __device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* b
     }
     if (kg == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LM + 16 * b + c] = x[r];
+        for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LT + 16 * b + c] = x[r];
     }
     // T10 = -D1 (diag(bet) B10) D0: lane (n16, g4) supplies contraction indices
     // 4 g4 .. 4 g4 + 3 and holds rows 4 g4 .. 4 g4 + 3 of column n16
@@ -173,28 +174,51 @@ __device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* b
     const f32x4 br10 = *reinterpret_cast<const f32x4*>(&Bm[(16 + n16) * LB + 4 * g4]);
     const float bs = bet[16 + n16];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) y = mfma4(br10[kk] * bs, Tm[(4 * g4 + kk) * LM + n16], y);
+    for (int kk = 0; kk < 4; ++kk) y = mfma4(br10[kk] * bs, Tm[(4 * g4 + kk) * LT + n16], y);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) t10 = mfma4(Tm[(16 + n16) * LM + 16 + 4 * g4 + kk], y[kk], t10);
+    for (int kk = 0; kk < 4; ++kk) t10 = mfma4(Tm[(16 + n16) * LT + 16 + 4 * g4 + kk], y[kk], t10);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Tm[(16 + 4 * g4 + r) * LM + n16] = -t10[r];
+    for (int r = 0; r < 4; ++r) Tm[(16 + 4 * g4 + r) * LT + n16] = -t10[r];
 }
 
 // ---------------------------------------------------------------------------
 // Forward states: S entering chunk n goes to ckpt[bh][n][rows of the slice].
+//
+// Only X = beta V - beta gamma K S^T, U = T X and the update of S depend on the
+// state, so they alone make the serial chain; the rest runs ahead of it on the
+// waves the chain leaves idle.  In the loop over chunks n (three barriers):
+//   1: waves 1, 2 form X(n); wave 0 solves T(n + 1) from its k-Gram and (two
+//      value slices) zeroes the outputs the reverse pass adds into; wave 3
+//      moves k(n + 2) and v(n + 1) from its registers into LDS, forms the gates
+//      of chunk n + 2 and fetches k(n + 3) and v(n + 2) from HBM;
+//   2: waves 1, 2 form U(n) = T(n) X(n); wave 3 forms the k-Gram of chunk n + 2;
+//      waves 0 (half), 1 and 2 (a quarter each) store S entering chunk n;
+//   3: all waves update S, each on the tiles it keeps in registers.
+// k and the gates are held three chunks deep, v/U, T and the k-Gram two.
+// GLA (U = V, nothing to solve): wave 3 moves k(n + 1) and v(n + 1) and wave 0
+// stores the state; a barrier; the update.
+struct ChunkGatesLds {
+    float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
+};
+
 template <int MODE, int DK, typename E>
-__global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_states_kernel(
+    BwdJob J) {
     constexpr bool GDN = MODE == 0;
     // bf16 data: the products in split bf16 (about 16 significant bits each)
     constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
     constexpr int NJ = DK / 32;
-    constexpr int L1 = DK + 1;
-    __shared__ float Ks[kC * L1];
-    __shared__ float Us[kC * LV];  // V, then X, then U
-    __shared__ float Ss[kSL * L1];
-    __shared__ __align__(16) float Bm[GDN ? kC * LB : 4];
-    __shared__ float Tm[GDN ? kC * LM : 1];
-    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
+    // Row strides: 16-byte rows (vector reads and writes along a row), and
+    // k-operands read down a column as rows r and r + 8 (the two lane halves)
+    // land 32 banks apart.
+    constexpr int L1 = DK + 4, LU = kSL + 4, LT = kC + 4;
+    constexpr int NB = GDN ? 3 : 2;  // k and gate buffers
+    __shared__ __align__(16) float Ks[NB][kC * L1];
+    __shared__ __align__(16) float Us[2][kC * LU];  // v, then X, then diag(e^{g_C - g}) U
+    __shared__ __align__(16) float Ss[kSL * L1];
+    __shared__ __align__(16) float Bm[GDN ? 2 : 1][GDN ? kC * LB : 4];
+    __shared__ __align__(16) float Tm[GDN ? 2 : 1][GDN ? kC * LT : 1];
+    __shared__ ChunkGatesLds gt[NB];
 
     const int slices = J.dv / kSL;
     int bh, sl;
@@ -203,126 +227,254 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(BwdJob J) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, kg = lane >> 5;
-    const int T = J.T, dv = J.dv;
+    const int T = J.T, dv = J.dv, NC = J.nchunks;
     const E* k = static_cast<const E*>(J.k);
     const E* v = static_cast<const E*>(J.v);
     const size_t tok0 = (size_t)bh * T;
     const size_t s_base = ((size_t)bh * dv + r0) * DK;
     auto row = [&](int e) { return acc_row(e, kg); };
 
-    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
-    if constexpr (GDN)
-        for (int x = tid; x < kC * LM; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
-
-    // The next chunk's k, v and gates are fetched into registers while this
-    // chunk computes (unconditional loads from a clamped token index; masking
-    // on the way into LDS), which hides HBM latency at one workgroup per CU.
-    constexpr int NK = kC * DK / kThreads, NV = kC * kSL / kThreads;
-    E pk[NK], pv[NV];
-    float pa = 1.f, pb = 0.f, pw = 0.f;
-    auto fetch = [&](int cn) {
+    // Wave 3's inputs: a chunk of k or v in 16-byte loads from a token index
+    // clamped into the sequence (unconditional; tokens past T are masked on the
+    // way into LDS), the gates' inputs of a k chunk in lanes 0..31 (and 32..63).
+    constexpr int EV = 16 / (int)sizeof(E);  // elements per load
+    constexpr int RK = DK / EV, RV = kSL / EV;  // loads per row
+    constexpr int FK = kC * RK / 64, FV = kC * RV / 64;
+    uint4 rk[FK], rv[FV];
+    float ra = 1.f, rb = 0.f, rw = 0.f;
+    auto fetch_k = [&](int cn) {
 #pragma unroll
-        for (int m = 0; m < NK; ++m) {
-            const int x = tid + m * kThreads, t = min(cn + x / DK, T - 1);
-            pk[m] = k[(tok0 + t) * DK + x % DK];
+        for (int m = 0; m < FK; ++m) {
+            const int x = lane + 64 * m, t = min(cn * kC + x / RK, T - 1);
+            rk[m] = *reinterpret_cast<const uint4*>(k + (tok0 + t) * DK + (x % RK) * EV);
         }
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads, t = min(cn + x / kSL, T - 1);
-            pv[m] = v[(tok0 + t) * dv + r0 + x % kSL];
-        }
-        if (w == 0) {
-            const int t = min(cn + l32, T - 1);
-            pa = J.alpha[tok0 + t];
-            if (GDN) {
-                pb = J.beta[tok0 + t];
-                pw = J.beta_w[tok0 + t];
-            }
+        const int t = min(cn * kC + l32, T - 1);
+        ra = J.alpha[tok0 + t];
+        if (GDN) {
+            rb = J.beta[tok0 + t];
+            rw = J.beta_w[tok0 + t];
         }
     };
-    fetch(0);
+    auto fetch_v = [&](int cn) {
+#pragma unroll
+        for (int m = 0; m < FV; ++m) {
+            const int x = lane + 64 * m, t = min(cn * kC + x / RV, T - 1);
+            rv[m] = *reinterpret_cast<const uint4*>(v + (tok0 + t) * dv + r0 + (x % RV) * EV);
+        }
+    };
+    auto unpack = [&](const uint4& u, float (&f)[EV]) {
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+        if constexpr (EV == 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(wd[i] << 16);
+                f[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(wd[i]);
+        }
+    };
+    // k chunk cn into its buffer, and its gates
+    auto put_k = [&](int cn) {
+        float* dst = Ks[cn % NB];
+#pragma unroll
+        for (int m = 0; m < FK; ++m) {
+            const int x = lane + 64 * m, t = x / RK;
+            float f[EV];
+            unpack(rk[m], f);
+            const bool in = cn * kC + t < T;
+#pragma unroll
+            for (int i = 0; i < EV; i += 4)
+                *reinterpret_cast<f32x4*>(&dst[t * L1 + (x % RK) * EV + i]) =
+                    in ? f32x4{f[i], f[i + 1], f[i + 2], f[i + 3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        ChunkGatesLds& g = gt[cn % NB];
+        chunk_gates<GDN>(ra, rb, rw, cn * kC, T, lane, g.G2, g.gam, g.Dd, g.bet, g.bw, g.bg, g.gC);
+    };
+    // v chunk cn into its buffer (GLA: as diag(e^{g_C - g}) V, gates of cn formed)
+    auto put_v = [&](int cn) {
+        float* dst = Us[cn & 1];
+        const float* Dd = gt[cn % NB].Dd;
+#pragma unroll
+        for (int m = 0; m < FV; ++m) {
+            const int x = lane + 64 * m, t = x / RV;
+            float f[EV];
+            unpack(rv[m], f);
+            const bool in = cn * kC + t < T;
+            const float sc = in ? (GDN ? 1.f : Dd[t]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < EV; i += 4)
+                *reinterpret_cast<f32x4*>(&dst[t * LU + (x % RV) * EV + i]) =
+                    sc * f32x4{f[i], f[i + 1], f[i + 2], f[i + 3]};
+        }
+    };
+    // B(cn) = strict_lower(Gamma o K K^T) into its buffer
+    auto k_gram = [&](int cn) {
+        const float* Kb = Ks[cn % NB];
+        const float* G2 = gt[cn % NB].G2;
+        auto kr = [&](int i) { return lds_f32x8(&Kb[l32 * L1 + 16 * i + 8 * kg]); };
+        const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(kr, kr, f32x16{});
+        float* B = Bm[cn & 1];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = row(e);
+            B[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+        }
+    };
+    // the state entering chunk cn, from Ss: 16-byte pieces m0, m0 + 1, .. < m1
+    // of each lane (kSL DK / 256 in all)
+    auto stash = [&](int cn, auto m0, auto m1) {
+        f32x4* ck4 = reinterpret_cast<f32x4*>(J.ckpt + (((size_t)bh * NC + cn) * dv + r0) * DK);
+#pragma unroll
+        for (int m = decltype(m0)::value; m < decltype(m1)::value; ++m) {
+            const int x = 4 * (lane + 64 * m);
+            ck4[lane + 64 * m] = *reinterpret_cast<const f32x4*>(Ss + x / DK * L1 + x % DK);
+        }
+    };
+    // the outputs the reverse pass adds into, with two slices: slice 0 dq,
+    // slice 1 dk, slice 0 the token arrays
+    auto zero_outputs = [&](int c0) {
+        float* dst = (sl == 0 ? J.dq : J.dk_out) + (tok0 + c0) * DK;
+        const int n4 = min(kC, T - c0) * DK / 4;
+        for (int x = lane; x < n4; x += 64) reinterpret_cast<f32x4*>(dst)[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (sl == 0 && lane < kC && c0 + lane < T) {
+            J.dalpha[tok0 + c0 + lane] = 0.f;
+            if (J.dbeta) J.dbeta[tok0 + c0 + lane] = 0.f;
+            if (J.dbeta_w) J.dbeta_w[tok0 + c0 + lane] = 0.f;
+        }
+    };
 
-    for (int n = 0; n < J.nchunks; ++n) {
-        const int c0 = n * kC;
-        __syncthreads();
-        if (slices == 2) {  // the outputs the reverse pass adds into: slice 0 dq, slice 1 dk, slice 0 the rest
-            float* dst = (sl == 0 ? J.dq : J.dk_out) + (tok0 + c0) * DK;
-            const int n4 = min(kC, T - c0) * DK / 4;
-            for (int x = tid; x < n4; x += kThreads) reinterpret_cast<f32x4*>(dst)[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (sl == 0 && tid < kC && c0 + tid < T) {
-                J.dalpha[tok0 + c0 + tid] = 0.f;
-                if (J.dbeta) J.dbeta[tok0 + c0 + tid] = 0.f;
-                if (J.dbeta_w) J.dbeta_w[tok0 + c0 + tid] = 0.f;
-            }
-        }
-        float4* ck4 = reinterpret_cast<float4*>(J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK);
-#pragma unroll
-        for (int m = 0; m < kSL * DK / 4 / kThreads; ++m) {
-            const int x = 4 * (tid + m * kThreads);
-            const float* src = Ss + x / DK * L1 + x % DK;
-            ck4[tid + m * kThreads] = make_float4(src[0], src[1], src[2], src[3]);
-        }
-#pragma unroll
-        for (int m = 0; m < NK; ++m) {
-            const int x = tid + m * kThreads, t = x / DK;
-            Ks[t * L1 + x % DK] = c0 + t < T ? to_f32(pk[m]) : 0.f;
-        }
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads, t = x / kSL;
-            Us[t * LV + x % kSL] = c0 + t < T ? to_f32(pv[m]) : 0.f;
-        }
-        if (w == 0) chunk_gates<GDN>(pa, pb, pw, c0, T, lane, G2, gam, Dd, bet, bw, bg, gC);
-        if (n + 1 < J.nchunks) fetch(c0 + kC);
-        __syncthreads();
+    // Prologue: S0; k, v and gates of the first chunks; T(0) and B(1).
+    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
+    if constexpr (GDN)
+        for (int x = tid; x < 2 * kC * LT; x += kThreads) Tm[x / (kC * LT)][x % (kC * LT)] = 0.f;  // T's upper right block stays zero
+    if (w == 3) {
+        fetch_k(0);
+        fetch_v(0);
+        put_k(0);
+        put_v(0);
         if constexpr (GDN) {
-            if (w == 0) {  // B = strict_lower(Gamma o K K^T)
-                auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
-                const f32x16 c = chain_t<SPLIT, DK / 2, true, true>(kr, kr, f32x16{});
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = row(e);
-                    Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
-                }
-            } else if (w < 3) {  // X = beta V - beta gamma K S^T, value columns 32 (w - 1) ..
-                const int I = w - 1;
-                // (K S^T with k exact in bf16; the row scalings after the product)
-                const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
-                                                     [&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
-                                                     f32x16{});
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = row(e), y = t * LV + 32 * I + l32;
-                    Us[y] = bw[t] * Us[y] - bg[t] * c[e];
-                }
+            if (NC > 1) {
+                fetch_k(1);
+                put_k(1);
             }
-            __syncthreads();
-            if (w == 0) {  // T, then U = T X in place
-                solve_unit_lower(Bm, bet, Tm, lane);
-#pragma unroll
-                for (int I = 0; I < 2; ++I) {
-                    const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
-                                                   [&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
-                                                   f32x16{});
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
-                }
-            }
-            __syncthreads();
+            fetch_k(2);
+        } else {
+            fetch_k(1);
         }
-        // S <- gamma_C S + U^T diag(e^{g_C - g}) K
-        for (int tile = w; tile < 2 * NJ; tile += 4) {
-            const int I = tile / NJ, Jt = tile - I * NJ;
-            f32x16 c;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) c[e] = gC[0] * Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
-            c = chain_t<SPLIT, kC / 2, false, true>(
-                [&](int s) { return Dd[2 * s + kg] * Us[(2 * s + kg) * LV + 32 * I + l32]; },
-                [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * Jt + l32]; }, c);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
+        fetch_v(1);
+    }
+    __syncthreads();
+    if constexpr (GDN) {
+        if (w == 0) {
+            k_gram(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            solve_unit_lower<LT>(Bm[0], gt[0].bet, Tm[0], lane);
+        } else if (w == 3 && NC > 1) {
+            k_gram(1);
         }
     }
+    __syncthreads();
+    // Each wave runs its own copy of the loop (W a constant), so the registers
+    // wave 3 fetches into are never merged with other waves' values, which
+    // would make the compiler wait for the loads where they are issued.
+    auto run = [&](auto wc) {
+        constexpr int W = decltype(wc)::value;
+        constexpr int MS = kSL * DK / 4 / 64;  // 16-byte pieces of the state per lane
+        // The state's tiles stay in the registers of the wave that updates them
+        // (tile W + 4 it: value rows 32 (tile / NJ) .., key columns 32 (tile % NJ) ..);
+        // Ss holds a copy for the X products.
+        constexpr int NT = (2 * NJ - W + 3) / 4;
+        f32x16 st[NT > 0 ? NT : 1];
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+            const int tile = W + 4 * it, I = tile / NJ, Jt = tile - I * NJ;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st[it][e] = Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
+        }
+        __syncthreads();
+
+        for (int n = 0; n < NC; ++n) {
+            const int c0 = n * kC;
+            const float* Kn = Ks[n % NB];
+            const ChunkGatesLds& gn = gt[n % NB];
+            float* Un = Us[n & 1];
+            if constexpr (GDN) {
+                if constexpr (W == 1 || W == 2) {  // X = beta V - beta gamma K S^T, value columns 32 (W - 1) ..
+                    constexpr int I = W - 1;
+                    // (K S^T with k exact in bf16; the row scalings after the product)
+                    const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
+                        [&](int i) { return lds_f32x8(&Kn[l32 * L1 + 16 * i + 8 * kg]); },
+                        [&](int i) { return lds_f32x8(&Ss[(32 * I + l32) * L1 + 16 * i + 8 * kg]); }, f32x16{});
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = row(e), y = t * LU + 32 * I + l32;
+                        Un[y] = gn.bw[t] * Un[y] - gn.bg[t] * c[e];
+                    }
+                } else if constexpr (W == 0) {
+                    if (n + 1 < NC) solve_unit_lower<LT>(Bm[(n + 1) & 1], gt[(n + 1) % NB].bet, Tm[(n + 1) & 1], lane);
+                    if (slices == 2) zero_outputs(c0);
+                } else {
+                    if (n + 2 < NC) put_k(n + 2);
+                    if (n + 1 < NC) put_v(n + 1);
+                    fetch_k(n + 3 < NC ? n + 3 : NC - 1);
+                    fetch_v(n + 2 < NC ? n + 2 : NC - 1);
+                }
+                __syncthreads();
+                if constexpr (W == 1 || W == 2) {  // diag(e^{g_C - g}) U, U = T X in place, on this wave's X columns
+                    constexpr int I = W - 1;
+                    const float* Tn = Tm[n & 1];
+                    const f32x16 c = chain8_t<SPLIT, kC / 16>(
+                        [&](int i) { return lds_f32x8(&Tn[l32 * LT + 16 * i + 8 * kg]); },
+                        [&](int i) { return lds_col8<LU>(&Un[(16 * i + 8 * kg) * LU + 32 * I + l32]); }, f32x16{});
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) Un[row(e) * LU + 32 * I + l32] = gn.Dd[row(e)] * c[e];
+                    // a quarter of the state's store each
+                    stash(n, std::integral_constant<int, MS * (W + 1) / 4>{}, std::integral_constant<int, MS * (W + 2) / 4>{});
+                } else if constexpr (W == 3) {
+                    if (n + 2 < NC) k_gram(n + 2);
+                } else {  // the first half of the state's store
+                    stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS / 2>{});
+                }
+                __syncthreads();
+            } else {
+                if constexpr (W == 3) {
+                    if (n + 1 < NC) {
+                        put_k(n + 1);
+                        put_v(n + 1);
+                    }
+                    fetch_k(n + 2 < NC ? n + 2 : NC - 1);
+                    fetch_v(n + 2 < NC ? n + 2 : NC - 1);
+                    if (slices == 2) zero_outputs(c0);
+                } else if constexpr (W == 0) {
+                    stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS>{});
+                }
+                __syncthreads();  // the stash reads Ss before the update rewrites it
+            }
+            // S <- gamma_C S + U^T diag(e^{g_C - g}) K
+#pragma unroll
+            for (int it = 0; it < NT; ++it) {
+                const int tile = W + 4 * it, I = tile / NJ, Jt = tile - I * NJ;
+                f32x16 c = gn.gC[0] * st[it];
+                c = chain8_t<SPLIT, kC / 16, false, true>(
+                    [&](int i) { return lds_col8<LU>(&Un[(16 * i + 8 * kg) * LU + 32 * I + l32]); },
+                    [&](int i) { return lds_col8<L1>(&Kn[(16 * i + 8 * kg) * L1 + 32 * Jt + l32]); }, c);
+                st[it] = c;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
+            }
+            __syncthreads();
+        }
+    };
+    if (w == 0)
+        run(std::integral_constant<int, 0>{});
+    else if (w == 1)
+        run(std::integral_constant<int, 1>{});
+    else if (w == 2)
+        run(std::integral_constant<int, 2>{});
+    else
+        run(std::integral_constant<int, 3>{});
 }
 
 // ---------------------------------------------------------------------------
