@@ -40,7 +40,9 @@
 //     with more as per-slice partials;
 //   bwd_reduce_kernel (more than two slices): the sum over slices and
 //     dalpha = d ln alpha / alpha; bwd_finish_kernel (else): the division.
-// Products are 32x32 tiles on the float32 MFMA (v_mfma_f32_32x32x2f32).
+// Products are 32x32 tiles: in split bf16 on the bf16 MFMA for bf16 data, on
+// the float32 MFMA for float32 data, their operands read from LDS eight k at a
+// time (chain8_t).
 #include <type_traits>
 
 #include "common.hpp"
@@ -57,8 +59,21 @@ constexpr int LV = kSL + 1;  // row stride of [32][64] value-row arrays
 constexpr int LM = kC + 1;   // row stride of 32x32 matrices
 constexpr int LB = kC + 4;   // row stride of the k-Gram (float4 rows for the solve)
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+// The elements of a 16-byte load: eight bf16 or four floats.
+template <int EV>
+__device__ __forceinline__ void unpack16(const uint4& u, float (&f)[EV]) {
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (EV == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(wd[i] << 16);
+            f[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(wd[i]);
+    }
+}
 
 // accumulator element e of a 32x32 tile sits at row 8 (e / 4) + 4 kg + e % 4,
 // column l32 (lane = 32 kg + l32)
@@ -262,19 +277,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             rv[m] = *reinterpret_cast<const uint4*>(v + (tok0 + t) * dv + r0 + (x % RV) * EV);
         }
     };
-    auto unpack = [&](const uint4& u, float (&f)[EV]) {
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-        if constexpr (EV == 8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f[2 * i] = __uint_as_float(wd[i] << 16);
-                f[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(wd[i]);
-        }
-    };
     // k chunk cn into its buffer, and its gates
     auto put_k = [&](int cn) {
         float* dst = Ks[cn % NB];
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int m = 0; m < FK; ++m) {
             const int x = lane + 64 * m, t = x / RK;
             float f[EV];
-            unpack(rk[m], f);
+            unpack16(rk[m], f);
             const bool in = cn * kC + t < T;
 #pragma unroll
             for (int i = 0; i < EV; i += 4)
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int m = 0; m < FV; ++m) {
             const int x = lane + 64 * m, t = x / RV;
             float f[EV];
-            unpack(rv[m], f);
+            unpack16(rv[m], f);
             const bool in = cn * kC + t < T;
             const float sc = in ? (GDN ? 1.f : Dd[t]) : 0.f;
 #pragma unroll
@@ -323,13 +325,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
     };
     // the state entering chunk cn, from Ss: 16-byte pieces m0, m0 + 1, .. < m1
-    // of each lane (kSL DK / 256 in all)
+    // of each lane (kSL DK / 256 in all).  With rows of 64 floats or more the
+    // 16-byte units of row r are stored XOR-permuted by r mod 16, the layout
+    // the reverse pass reads them into LDS with.
     auto stash = [&](int cn, auto m0, auto m1) {
         f32x4* ck4 = reinterpret_cast<f32x4*>(J.ckpt + (((size_t)bh * NC + cn) * dv + r0) * DK);
 #pragma unroll
         for (int m = decltype(m0)::value; m < decltype(m1)::value; ++m) {
-            const int x = 4 * (lane + 64 * m);
-            ck4[lane + 64 * m] = *reinterpret_cast<const f32x4*>(Ss + x / DK * L1 + x % DK);
+            const int x = lane + 64 * m, r = x / (DK / 4), u = x % (DK / 4);
+            ck4[x] = *reinterpret_cast<const f32x4*>(Ss + r * L1 + 4 * (DK >= 64 ? u ^ (r & 15) : u));
         }
     };
     // the outputs the reverse pass adds into, with two slices: slice 0 dq,
@@ -486,20 +490,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // bf16 data: the products in split bf16 (about 16 significant bits each)
     constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
     constexpr int NJ = DK / 32;  // key-column tiles: wave w < NJ owns dq and dk tile w
-    constexpr int L1 = DK + 1;
-    __shared__ float Qs[kC * L1];
-    __shared__ float Ks[kC * L1];
-    __shared__ float Ss[kSL * L1];   // state entering the chunk
-    __shared__ float dSs[kSL * L1];  // gradient at the state leaving it, then entering it
+    // Rows of the key-wide arrays and of the 32x32 matrices are 16-byte rows
+    // (operands along a row come in 16-byte reads; down a column, the rows
+    // r and r + 8 of the two lane halves land 32 banks apart).
+    constexpr int L1 = DK + 4;
+    constexpr int LP = kC + 4;
+    __shared__ __align__(16) float Qs[kC * L1];
+    __shared__ __align__(16) float Ks[kC * L1];
+    // state entering the chunk: with rows of 64 floats or more, unpadded with
+    // the 16-byte units of row r XOR-permuted by r mod 16 (as the states pass
+    // stores it), so it arrives by LDS-direct loads of 1 KB; else padded rows
+    constexpr bool SWZ = DK >= 64;
+    __shared__ __align__(16) float Ss[kSL * (SWZ ? DK : L1)];
+    __shared__ __align__(16) float dSs[kSL * L1];  // gradient at the state leaving it, then entering it
     __shared__ float Vs[kC * LV];    // V, then dX
     __shared__ float dOs[kC * LV];
     __shared__ float Us[kC * LV];    // V, then X, then U
     __shared__ float dUs[kC * LV];
     __shared__ __align__(16) float Bm[GDN ? kC * LB : 4];
-    __shared__ float Pm[kC * LM];
-    __shared__ float Tm[GDN ? kC * LM : 1];
-    __shared__ float dQKm[kC * LM];  // dP o Gamma
-    __shared__ float dKKm[GDN ? kC * LM : 1];
+    __shared__ __align__(16) float Pm[kC * LP];
+    __shared__ __align__(16) float Tm[GDN ? kC * LP : 1];
+    __shared__ __align__(16) float dQKm[kC * LP];  // dP o Gamma
+    __shared__ __align__(16) float dKKm[GDN ? kC * LP : 1];
     __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
     __shared__ float dgp[16 * kC];   // per-product contributions to dg (fixed slots)
     __shared__ float dbp[8 * kC];    // ... to dbeta
@@ -509,9 +521,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int bh, slice;
     unit_part(blockIdx.x, J.BH, slices, bh, slice);  // a head's slices share its input reads in L2
     const int r0 = slice * kSL;
-    const int tid = threadIdx.x, lane = tid & 63;
+    int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, kg = lane >> 5;
+    int l32 = lane & 31, kg = lane >> 5;
     const int T = J.T, dv = J.dv;
     const E* q = static_cast<const E*>(J.q);
     const E* k = static_cast<const E*>(J.k);
@@ -526,6 +538,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     float* pdb = pdl + (size_t)slices * J.BH * T;
     float* pdbw = pdb + (size_t)slices * J.BH * T;  // write strengths (split strengths only)
     auto row = [&](int e) { return acc_row(e, kg); };
+    // index of S[r][c] in Ss
+    auto sx = [&](int r, int c) { return SWZ ? r * DK + 4 * ((c >> 2) ^ (r & 15)) + (c & 3) : r * L1 + c; };
+    // eight rows r0 .. r0 + 7 of S's column c
+    auto s_col8 = [&](int r0, int c) {
+        f32x8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = Ss[sx(r0 + j, c)];
+        return x;
+    };
+    // S[r][c .. c + 7] (c a multiple of 8)
+    auto s_row8 = [&](int r, int c) {
+        if constexpr (SWZ) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&Ss[sx(r, c)]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&Ss[sx(r, c + 4)]);
+            return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            return lds_f32x8(&Ss[r * L1 + c]);
+        }
+    };
+    // a group's eight operands (k = 16 i + 8 kg + j): along a 16-byte row, along
+    // a row of a value-wide array (stride LV, not 16-byte), down a column
+    auto rowv8 = [](const float* p) {
+        f32x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = p[j];
+        return r;
+    };
+    int k8 = 8 * kg;
     // a sum over value rows into its output: stored (one slice) or added onto
     // the zeros the states pass wrote (two slices)
     auto put = [&](float* p, float x) {
@@ -537,33 +577,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
     if constexpr (GDN)
-        for (int x = tid; x < kC * LM; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
+        for (int x = tid; x < kC * LP; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
 
     // The next chunk's (in reverse order) q, k, v, dO and gates are fetched
     // into registers during this one's last two phases (unconditional loads
     // from a clamped token index; masking on the way into LDS).  Issued
     // earlier, the registers would be live through the phases with the most
-    // accumulators.  Its stored state, 32 more registers per lane, is read at
-    // the chunk's start instead: prefetched, it made the kernel spill more and
-    // ran slower.
-    constexpr int NK = kC * DK / kThreads, NV = kC * kSL / kThreads;
-    E pq[NK], pk[NK], pv[NV], pd[NV];
+    // accumulators.
+    // (16-byte loads: EV elements each; RK, RV loads per row)
+    constexpr int EV = 16 / (int)sizeof(E), RK = DK / EV, RV = kSL / EV;
+    constexpr int QL = kC * RK, VL = kC * RV;  // loads per chunk
+    constexpr int NK = (QL + kThreads - 1) / kThreads, NV = (VL + kThreads - 1) / kThreads;
+    uint4 pq[NK], pk[NK], pv[NV], pd[NV];
     float pa = 1.f, pb = 0.f, pw = 0.f;
     auto fetch = [&](int n) {
         const int cn = n * kC;
 #pragma unroll
         for (int m = 0; m < NK; ++m) {
-            const int x = tid + m * kThreads, t = min(cn + x / DK, T - 1);
-            const size_t gi = (tok0 + t) * DK + x % DK;
-            pq[m] = q[gi];
-            pk[m] = k[gi];
+            const int x = min(tid + m * kThreads, QL - 1), t = min(cn + x / RK, T - 1);
+            const size_t gi = (tok0 + t) * DK + (x % RK) * EV;
+            pq[m] = *reinterpret_cast<const uint4*>(q + gi);
+            pk[m] = *reinterpret_cast<const uint4*>(k + gi);
         }
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads, t = min(cn + x / kSL, T - 1);
-            const size_t gi = (tok0 + t) * dv + r0 + x % kSL;
-            pv[m] = v[gi];
-            pd[m] = dO ? dO[gi] : E(0);
+            const int x = min(tid + m * kThreads, VL - 1), t = min(cn + x / RV, T - 1);
+            const size_t gi = (tok0 + t) * dv + r0 + (x % RV) * EV;
+            pv[m] = *reinterpret_cast<const uint4*>(v + gi);
+            pd[m] = dO ? *reinterpret_cast<const uint4*>(dO + gi) : uint4{0u, 0u, 0u, 0u};
         }
         if (w == 0) {
             const int t = min(cn + l32, T - 1);
@@ -575,42 +616,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
     };
     fetch(J.nchunks - 1);
-
-    for (int n = J.nchunks - 1; n >= 0; --n) {
-        const int c0 = n * kC;
-        __syncthreads();  // the previous chunk is done with every array
-        {  // the stored state: all of a thread's 16-byte loads are issued before any is used
+    // The stored state entering chunk n goes into Ss: for the first chunk
+    // here, for each later one during the previous chunk's last phase, which
+    // no longer reads Ss.  With rows of 64 floats or more, LDS-direct loads
+    // (a wave's 16-byte load puts 1 KB into LDS, no registers: the stored
+    // layout is Ss's); they are complete once vmcnt is 0, which the loop waits
+    // for before the barrier that starts a chunk.  Rows of 32: 16-byte loads
+    // and writes at the chunk's start.
+    auto load_state = [&](int cn) {
+        const float* src = J.ckpt + (((size_t)bh * J.nchunks + cn) * dv + r0) * DK;
+        if constexpr (SWZ) {
+#pragma unroll
+            for (int b = w; b < kSL * DK / 256; b += 4)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 256 * b + 4 * lane),
+                                                 (__attribute__((address_space(3))) void*)(Ss + 256 * b), 16, 0, 0);
+        } else {
             constexpr int NS4 = kSL * DK / 4 / kThreads;
-            const float4* ck4 =
-                reinterpret_cast<const float4*>(J.ckpt + (((size_t)bh * J.nchunks + n) * dv + r0) * DK);
             float4 sv[NS4];
 #pragma unroll
-            for (int m = 0; m < NS4; ++m) sv[m] = ck4[tid + m * kThreads];
+            for (int m = 0; m < NS4; ++m) sv[m] = reinterpret_cast<const float4*>(src)[tid + m * kThreads];
 #pragma unroll
             for (int m = 0; m < NS4; ++m) {
                 const int x = 4 * (tid + m * kThreads);
-                float* dst = Ss + x / DK * L1 + x % DK;
-                dst[0] = sv[m].x;
-                dst[1] = sv[m].y;
-                dst[2] = sv[m].z;
-                dst[3] = sv[m].w;
+                *reinterpret_cast<float4*>(Ss + x / DK * L1 + x % DK) = sv[m];
+            }
+        }
+    };
+    load_state(J.nchunks - 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    for (int n = J.nchunks - 1; n >= 0; --n) {
+        // The lane indices are opaque to the compiler from here on, so the
+        // address arithmetic built on them is redone in the loop rather than
+        // hoisted out of it into hundreds of live registers.
+        asm volatile("" : "+v"(tid), "+v"(lane), "+v"(l32), "+v"(kg), "+v"(k8));
+        const int c0 = n * kC;
+        __syncthreads();  // the previous chunk is done with every array
+        if (!SWZ && n < J.nchunks - 1) load_state(n);
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            const int x = tid + m * kThreads, t = x / RK, y = t * L1 + (x % RK) * EV;
+            if (QL % kThreads == 0 || x < QL) {
+                const bool in = c0 + t < T;
+                float fq[EV], fk[EV];
+                unpack16(pq[m], fq);
+                unpack16(pk[m], fk);
+#pragma unroll
+                for (int i = 0; i < EV; i += 4) {
+                    *reinterpret_cast<f32x4*>(&Qs[y + i]) =
+                        in ? f32x4{fq[i], fq[i + 1], fq[i + 2], fq[i + 3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+                    *reinterpret_cast<f32x4*>(&Ks[y + i]) =
+                        in ? f32x4{fk[i], fk[i + 1], fk[i + 2], fk[i + 3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
         }
 #pragma unroll
-        for (int m = 0; m < NK; ++m) {
-            const int x = tid + m * kThreads, t = x / DK, y = t * L1 + x % DK;
-            const bool in = c0 + t < T;
-            Qs[y] = in ? to_f32(pq[m]) : 0.f;
-            Ks[y] = in ? to_f32(pk[m]) : 0.f;
-        }
-#pragma unroll
         for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads, t = x / kSL, y = t * LV + x % kSL;
-            const bool in = c0 + t < T;
-            const float vv = in ? to_f32(pv[m]) : 0.f;
-            Vs[y] = vv;
-            Us[y] = vv;
-            dOs[y] = in ? to_f32(pd[m]) : 0.f;
+            const int x = tid + m * kThreads, t = x / RV, y = t * LV + (x % RV) * EV;
+            if (VL % kThreads == 0 || x < VL) {
+                const bool in = c0 + t < T;
+                float fv[EV], fd[EV];
+                unpack16(pv[m], fv);
+                unpack16(pd[m], fd);
+#pragma unroll
+                for (int i = 0; i < EV; ++i) {
+                    const float vv = in ? fv[i] : 0.f;
+                    Vs[y + i] = vv;
+                    Us[y + i] = vv;
+                    dOs[y + i] = in ? fd[i] : 0.f;
+                }
+            }
         }
         for (int x = tid; x < 16 * kC; x += kThreads) dgp[x] = 0.f;
         for (int x = tid; x < 8 * kC; x += kThreads) dbp[x] = 0.f;
@@ -623,8 +698,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // the owners' dQ = diag(gamma) dO S (+ its dg share)
         auto owner_dq = [&]() {
             // dO exact in bf16, gamma applied to the rows after
-            accQ = chain_t<SPLIT, kSL / 2, true>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
-                                        [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
+            accQ = chain8_t<SPLIT, kSL / 16, true>([&](int i) { return rowv8(&dOs[l32 * LV + 16 * i + k8]); },
+                                          [&](int i) { return s_col8(16 * i + k8, 32 * w + l32); },
+                                          accQ);
 #pragma unroll
             for (int e = 0; e < 16; ++e) accQ[e] *= gam[row(e)];
             f32x16 x;
@@ -634,8 +710,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         };
         // Phase 1: B and then T (wave 0, delta rule), P, X; the other owners' dQ part
         if (GDN && w == 0) {
-            auto kr = [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; };
-            const f32x16 c = chain_t<SPLIT, DK / 2, true, true>(kr, kr, f32x16{});
+            auto kr = [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); };
+            const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(kr, kr, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
@@ -644,21 +720,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // the same wave solves right away: its own B rows are complete once
             // its LDS writes are
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            solve_unit_lower(Bm, bet, Tm, lane);
+            solve_unit_lower<LP>(Bm, bet, Tm, lane);
         } else if (w == 1) {
-            const f32x16 c = chain_t<SPLIT, DK / 2, true, true>([&](int s) { return Qs[l32 * L1 + 2 * s + kg]; },
-                                                       [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
+            const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(
+                [&](int i) { return lds_f32x8(&Qs[l32 * L1 + 16 * i + k8]); },
+                [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
-                Pm[t * LM + l32] = l32 <= t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+                Pm[t * LP + l32] = l32 <= t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
             }
         } else if (GDN && w >= 2) {
             const int I = w - 2;
             // (K S^T)^T = S K^T with the token along the lanes: X_t = beta_t V_t - beta_t gamma_t (K S^T)_t
             // is written row by row, and the tile serves <dX_t, (K S^T)_t> in phase 5 as an in-lane sum
-            ksT = chain_t<SPLIT, DK / 2, false, true>([&](int s) { return Ss[(32 * I + l32) * L1 + 2 * s + kg]; },
-                                             [&](int s) { return Ks[l32 * L1 + 2 * s + kg]; }, f32x16{});
+            ksT = chain8_t<SPLIT, DK / 16, false, true>(
+                [&](int i) { return s_row8(32 * I + l32, 16 * i + k8); },
+                [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); }, f32x16{});
             const float b = bw[l32], nbg = -bg[l32];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -667,9 +745,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
             const int I = w - 2;
-            const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
-                                                 [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
-                                                 f32x16{});
+            const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
+                [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
+                [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
         }
@@ -683,17 +761,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             } else if (w == 3) {
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
-                    const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return Tm[l32 * LM + 2 * s + kg]; },
-                                                   [&](int s) { return Us[(2 * s + kg) * LV + 32 * I + l32]; },
-                                                   f32x16{});
+                    const f32x16 c = chain8_t<SPLIT, kC / 16>(
+                        [&](int i) { return lds_f32x8(&Tm[l32 * LP + 16 * i + k8]); },
+                        [&](int i) { return lds_col8<LV>(&Us[(16 * i + k8) * LV + 32 * I + l32]); }, f32x16{});
 #pragma unroll
                     for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
                 }
             } else {
                 const int I = w - 1;
-                const f32x16 c = chain_t<SPLIT, DK / 2, true>([&](int s) { return Ks[l32 * L1 + 2 * s + kg]; },
-                                                     [&](int s) { return dSs[(32 * I + l32) * L1 + 2 * s + kg]; },
-                                                     f32x16{});
+                const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
+                    [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
+                    [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
 #pragma unroll
                 for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
             }
@@ -702,20 +780,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Phase 3: dP (waves 0 and 3 both form it: wave 0 writes dP * Gamma, wave 3 the
         // row and column sums of dP * P), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
         if (w == 0 || w == 3) {
-            const f32x16 c = chain_t<SPLIT, kSL / 2, true>([&](int s) { return dOs[l32 * LV + 2 * s + kg]; },
-                                                  [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
+            const f32x16 c = chain8_t<SPLIT, kSL / 16, true>([&](int i) { return rowv8(&dOs[l32 * LV + 16 * i + k8]); },
+                                                    [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
+                                                    f32x16{});
             if (w == 0) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
-                    dQKm[t * LM + l32] = l32 <= t ? c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                    dQKm[t * LP + l32] = l32 <= t ? c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
                 }
             } else {
                 f32x16 L;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
-                    L[e] = l32 <= t ? c[e] * Pm[t * LM + l32] : 0.f;
+                    L[e] = l32 <= t ? c[e] * Pm[t * LP + l32] : 0.f;
                 }
                 store_row_sums(L, dgp + 8 * kC, l32, kg, 1.f);   // dg slot 8
                 store_col_sums(L, dgp + 9 * kC, l32, kg, -1.f);  // dg slot 9
@@ -736,14 +815,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x16 c;
 #pragma unroll
             for (int e = 0; e < 16; ++e) c[e] = dUs[row(e) * LV + 32 * I + l32];
-            c = chain_t<SPLIT, kC / 2, false, true>([&](int s) { return Pm[(2 * s + kg) * LM + l32]; },
-                                           [&](int s) { return dOs[(2 * s + kg) * LV + 32 * I + l32]; }, c);
+            c = chain8_t<SPLIT, kC / 16, false, true>([&](int i) { return lds_col8<LP>(&Pm[(16 * i + k8) * LP + l32]); },
+                                             [&](int i) { return lds_col8<LV>(&dOs[(16 * i + k8) * LV + 32 * I + l32]); },
+                                             c);
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
         if (w < NJ) {  // dKd = U dS'
-            const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return Us[l32 * LV + 2 * s + kg]; },
-                                            [&](int s) { return dSs[(2 * s + kg) * L1 + 32 * w + l32]; }, f32x16{});
+            const f32x16 c = chain8_t<SPLIT, kSL / 16>(
+                [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
+                [&](int i) { return lds_col8<L1>(&dSs[(16 * i + k8) * L1 + 32 * w + l32]); }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) accK[e] += Dd[row(e)] * c[e];
         }
@@ -752,8 +833,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // <dX_t, V_t> is an in-lane sum; dX replaces V row by row); the owners' dQ, dK += dQK parts
         if (GDN && (w == 1 || w == 2)) {
             const int I = w - 1;
-            const f32x16 c = chain_t<SPLIT, kC / 2>([&](int s) { return dUs[(2 * s + kg) * LV + 32 * I + l32]; },
-                                           [&](int s) { return Tm[(2 * s + kg) * LM + l32]; }, f32x16{});
+            const f32x16 c = chain8_t<SPLIT, kC / 16>(
+                [&](int i) { return lds_col8<LV>(&dUs[(16 * i + k8) * LV + 32 * I + l32]); },
+                [&](int i) { return lds_col8<LP>(&Tm[(16 * i + k8) * LP + l32]); }, f32x16{});
             float db = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -771,25 +853,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         if (w < NJ) {
-            accQ = chain_t<SPLIT, kC / 2, false, true>([&](int s) { return dQKm[l32 * LM + 2 * s + kg]; },
-                                              [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accQ);
-            accK = chain_t<SPLIT, kC / 2, false, true>([&](int s) { return dQKm[(2 * s + kg) * LM + l32]; },
-                                              [&](int s) { return Qs[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
+            accQ = chain8_t<SPLIT, kC / 16, false, true>(
+                [&](int i) { return lds_f32x8(&dQKm[l32 * LP + 16 * i + k8]); },
+                [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * w + l32]); }, accQ);
+            accK = chain8_t<SPLIT, kC / 16, false, true>(
+                [&](int i) { return lds_col8<LP>(&dQKm[(16 * i + k8) * LP + l32]); },
+                [&](int i) { return lds_col8<L1>(&Qs[(16 * i + k8) * L1 + 32 * w + l32]); }, accK);
         }
         __syncthreads();
         // the next chunk's inputs are in flight through phases 5 and 6
         if (n > 0) fetch(n - 1);
-        // Phase 5: dA (waves 0 and 1 both form it: wave 0 writes dKK, wave 1 the sums),
-        // dRw (owners), dS
+        // Phase 5: dRw (owners), dA (waves 0 and 1 both form it: wave 0 writes
+        // dKK, wave 1 the sums), dS
         if constexpr (GDN) {
+            if (w < NJ) {  // dRw = -dX S
+                const f32x16 c = chain8_t<SPLIT, kSL / 16>(
+                    [&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
+                    [&](int i) { return s_col8(16 * i + k8, 32 * w + l32); }, f32x16{});
+#pragma unroll
+                for (int e = 0; e < 16; ++e) accK[e] += bg[row(e)] * c[e];
+            }
             if (w < 2) {
-                const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
-                                                [&](int s) { return Us[l32 * LV + 2 * s + kg]; }, f32x16{});
+                const f32x16 c = chain8_t<SPLIT, kSL / 16>([&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
+                                                  [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
+                                                  f32x16{});
                 if (w == 0) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int t = row(e);
-                        dKKm[t * LM + l32] = l32 < t ? bet[t] * c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                        dKKm[t * LP + l32] = l32 < t ? bet[t] * c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
                     }
                 } else {
                     f32x16 xb, xa;
@@ -816,13 +908,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     dgp[(10 + I) * kC + l32] = bg[l32] * wt;  // dg slots 10, 11
                 }
             }
-            if (w < NJ) {  // dRw = -dX S
-                const f32x16 c = chain_t<SPLIT, kSL / 2>([&](int s) { return -Vs[l32 * LV + 2 * s + kg]; },
-                                                [&](int s) { return Ss[(2 * s + kg) * L1 + 32 * w + l32]; },
-                                                f32x16{});
-#pragma unroll
-                for (int e = 0; e < 16; ++e) accK[e] += bg[row(e)] * c[e];
-            }
         }
         // dV = diag(bw) dX (delta rule) or dU (linear attention), row-major from LDS
         for (int x = tid; x < kC * kSL; x += kThreads) {
@@ -844,20 +929,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int e = 0; e < 16; ++e) {
                 const int y = (32 * I + row(e)) * L1 + 32 * Jt + l32;
                 const float d = dSs[y];
-                ss += d * Ss[y];
+                ss += d * Ss[sx(32 * I + row(e), 32 * Jt + l32)];
                 c[e] = gC[0] * d;
             }
             // the two products as one chain over 2 C (GDN) or C tokens; the token
             // scalings sit on the dO and dX side, so q and k stay exact in bf16
-            constexpr int H2 = kC / 2;
-            c = chain_t<SPLIT, GDN ? kC : H2, false, true>(
-                [&](int s) {
-                    const int t = 2 * (s % H2) + kg;
-                    return s < H2 ? dOs[t * LV + 32 * I + l32] : -bg[t] * Vs[t * LV + 32 * I + l32];
+            constexpr int G1 = kC / 16;
+            c = chain8_t<SPLIT, GDN ? 2 * G1 : G1, false, true>(
+                [&](int i) {
+                    const int t = 16 * (i % G1) + k8;
+                    if (i < G1) return lds_col8<LV>(&dOs[t * LV + 32 * I + l32]);
+                    f32x8 r;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) r[j] = -bg[t + j] * Vs[(t + j) * LV + 32 * I + l32];
+                    return r;
                 },
-                [&](int s) {
-                    const int t = 2 * (s % H2) + kg;
-                    return s < H2 ? Qs[t * L1 + 32 * Jt + l32] : Ks[t * L1 + 32 * Jt + l32];
+                [&](int i) {
+                    const int t = 16 * (i % G1) + k8;
+                    return lds_col8<L1>(&(i < G1 ? Qs : Ks)[t * L1 + 32 * Jt + l32]);
                 },
                 c);
 #pragma unroll
@@ -866,12 +955,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             if (lane == 0) dgc[4 + tile] = ss;
         }
         __syncthreads();
+        if (SWZ && n > 0) load_state(n - 1);
         // Phase 6: dK += (dKK + dKK^T) K; partial dq, dk; dg -> d ln alpha, dbeta
         if (w < NJ) {
             if constexpr (GDN)
-                accK = chain_t<SPLIT, kC / 2, false, true>(
-                    [&](int s) { return dKKm[l32 * LM + 2 * s + kg] + dKKm[(2 * s + kg) * LM + l32]; },
-                    [&](int s) { return Ks[(2 * s + kg) * L1 + 32 * w + l32]; }, accK);
+                accK = chain8_t<SPLIT, kC / 16, false, true>(
+                    [&](int i) {
+                        return lds_f32x8(&dKKm[l32 * LP + 16 * i + k8]) + lds_col8<LP>(&dKKm[(16 * i + k8) * LP + l32]);
+                    },
+                    [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * w + l32]); }, accK);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
@@ -935,6 +1027,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the state's LDS-direct loads
     }
     __syncthreads();
     for (int x = tid; x < kSL * DK; x += kThreads) J.dS0[s_base + x] = dSs[x / DK * L1 + x % DK];
