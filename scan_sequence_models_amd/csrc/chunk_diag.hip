@@ -31,6 +31,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_f32.hpp"
+#include "solve.hpp"
 
 namespace gds {
 namespace {
@@ -223,27 +224,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int NV = kC * kSL / kThreads;  // value elements per thread and chunk
     static_assert((kC / 2) % NQ == 0, "the middle token m = kC/2 - 1 ends a run");
     static_assert(DK < 64 || kC * (DK + 4) >= 2048, "KA holds two partial O tiles");
-    // Row strides.  The pairwise Gram reads float4 runs of channels with one
-    // token per lane: a stride of DK + 4 keeps those 16-byte loads aligned and
-    // spreads eight consecutive lanes over distinct bank groups.  The MFMA
-    // operands read one float per lane down a column: an odd stride (DK + 1)
-    // puts the 32 lanes into 32 banks.
+    // Row strides: 16-byte rows.  The pairwise Gram reads float4 runs of
+    // channels with one token per lane, and the MFMA operands along a row come
+    // in 16-byte reads (eight k per lane half: k = 16 i + 8 kg + j), both
+    // conflict-free with 16 lanes on rows 4 banks apart; down a column, the
+    // rows r and r + 8 of the two lane halves land 32 banks apart.
     constexpr int L4 = DK + 4;
-    constexpr int L1 = DK + 1;
-    // Gram operands: q e^{g - g_m}, k e^{g - g_m} and k e^{g_m - g} (stride L1)
-    // in a factored chunk; q, k and the cumulative log2 decay g (stride L4) in a
-    // wide one
+    constexpr int LU = kSL + 4;
+    // Gram operands: q e^{g - g_m}, k e^{g - g_m} and k e^{g_m - g} in a
+    // factored chunk; q, k and the cumulative log2 decay g in a wide one
     __shared__ __align__(16) float QA[kC * L4];
     __shared__ __align__(16) float KA[kC * L4];
     __shared__ __align__(16) float KB[kC * L4];
-    __shared__ float Qg[kC * L1];                // q * gamma
-    __shared__ float Kt[kC * L1];                // k * e^{g_C - g} (wide chunks)
-    __shared__ float Rw[GDN ? kC * L1 : 1];      // -(k * gamma)
-    __shared__ float Us[kC * kSL];               // v slice, then X (without beta), then U
+    __shared__ __align__(16) float Qg[kC * L4];            // q * gamma
+    __shared__ __align__(16) float Kt[kC * L4];            // k * e^{g_C - g} (wide chunks)
+    __shared__ __align__(16) float Rw[GDN ? kC * L4 : 4];  // -(k * gamma)
+    __shared__ __align__(16) float Us[kC * LU];            // v slice, then X (without beta), then U
     __shared__ __align__(16) float Am[GDN ? kC * kC : 1];  // A without beta (strictly lower)
-    __shared__ float Tm[GDN ? kC * kLT : 1];     // T diag(beta)
-    __shared__ float Pm[kC * kLT];               // P (lower, inclusive; zero above)
-    __shared__ float Ss[kSL * L1];               // state slice
+    __shared__ __align__(16) float Tm[GDN ? kC * kLT : 4];  // T
+    __shared__ __align__(16) float Pm[kC * kLT];            // P (lower, inclusive; zero above)
+    __shared__ __align__(16) float Ss[kSL * L4];            // state slice
     __shared__ float Gr[NR * DK];                // run totals of log2 a
     __shared__ float sIn[DK];                    // per-channel factors of the state update:
     __shared__ float sOut[DK];                   // e^{g_m}, e^{g_C - g_m} (wide: gamma_C, 1)
@@ -264,8 +264,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // accumulator element e of a 32x32 tile: row 8 (e / 4) + 4 kg + e % 4, column l32
     auto row = [&](int e) { return 8 * (e >> 2) + 4 * kg + (e & 3); };
 
-    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = S0 ? S0[s_base + x] : 0.f;
+    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L4 + x % DK] = S0 ? S0[s_base + x] : 0.f;
     for (int x = tid; x < kC * kLT; x += kThreads) Pm[x] = 0.f;
+    if constexpr (GDN)
+        for (int x = tid; x < kC * kLT; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
 
     // The next chunk's inputs are fetched into registers while this chunk
     // computes (one wave per SIMD leaves no other way to hide HBM latency).
@@ -292,17 +294,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     };
     fetch(0);
 
-    // c += A B^T over `steps` key steps from k0, A and B both read along key rows
-    // (A: 32 token rows, B: 32 state rows, row stride L1)
+    // c += A B^T over `steps` key steps (two keys each) from step k0, A and B
+    // both read along key rows (A: 32 token rows, B: 32 state rows)
     auto rows_dot = [&](const float* A, const float* B, auto steps, int k0, f32x16 c) {
-        return chain_t<SPLIT, decltype(steps)::value>([&](int s) { return A[l32 * L1 + 2 * (k0 + s) + kg]; },
-                                             [&](int s) { return B[l32 * L1 + 2 * (k0 + s) + kg]; }, c);
+        constexpr int G = decltype(steps)::value / 8;
+        return chain8_t<SPLIT, G>([&](int i) { return lds_f32x8(&A[l32 * L4 + 2 * k0 + 16 * i + 8 * kg]); },
+                                  [&](int i) { return lds_f32x8(&B[l32 * L4 + 2 * k0 + 16 * i + 8 * kg]); }, c);
     };
     using Full = std::integral_constant<int, DK / 2>;
     // c += P U or T X on value columns 32 I ..: B read along token rows of Us
     auto tok_dot = [&](const float* A, int I, f32x16 c) {
-        return chain_t<SPLIT, kC / 2>([&](int s) { return A[l32 * kLT + 2 * s + kg]; },
-                             [&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; }, c);
+        return chain8_t<SPLIT, kC / 16>(
+            [&](int i) { return lds_f32x8(&A[l32 * kLT + 16 * i + 8 * kg]); },
+            [&](int i) { return lds_col8<LU>(&Us[(16 * i + 8 * kg) * LU + 32 * I + l32]); }, c);
     };
 
     const int nchunks = (T + kC - 1) / kC;
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
             const int x = tid + m * kThreads;
-            Us[x] = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
+            Us[x / kSL * LU + x % kSL] = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
         }
         // one flag per wave, one barrier (the flags are next written after the
         // following chunk's first barrier)
@@ -349,8 +353,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // 2. scaled copies and Gram operands.  The bases are opaque to the
         // compiler, so each store below is one base register plus an immediate
         // offset instead of an address hoisted out of the chunk loop.
-        int b1 = run * NQ * L1 + ch, b4 = run * NQ * L4 + ch;
-        asm volatile("" : "+v"(b1), "+v"(b4));
+        int b4 = run * NQ * L4 + ch;
+        asm volatile("" : "+v"(b4));
         auto put = [&](auto factored) {
             constexpr bool F = decltype(factored)::value;
             // factored: gamma_t = e^{g_t - g_m} e^{g_m}, and k e^{g_C - g} is not
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int m = 0; m < NQ; ++m) {
                 const bool in = run * NQ + m < o0;
                 const float qq = in ? to_f32(pq[m]) : 0.f, kk = in ? to_f32(pk[m]) : 0.f;
-                const int y = b1 + m * L1;
+                const int y = b4 + m * L4;
                 if constexpr (F) {
                     const float up = __builtin_amdgcn_exp2f(g[m] - gm), dn = __builtin_amdgcn_exp2f(gm - g[m]);
                     const float qu = qq * up, ku = kk * up;
@@ -380,10 +384,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     Qg[y] = qq * gam;
                     Kt[y] = kk * __builtin_amdgcn_exp2f(gc - g[m]);
                     if constexpr (GDN) Rw[y] = -(kk * gam);
-                    const int z = b4 + m * L4;
-                    QA[z] = qq;
-                    KA[z] = kk;
-                    KB[z] = g[m];
+                    QA[y] = qq;
+                    KA[y] = kk;
+                    KB[y] = g[m];
                 }
             }
         };
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         constexpr bool kSplitO = DK >= 64;  // KA holds the two partial tiles
         using OHead = std::integral_constant<int, kSplitO ? 3 * DK / 8 : DK / 2>;
         auto o_tail = [&](int I) {
-            const f32x16 c = rows_dot(Qg, Ss + 32 * I * L1, std::integral_constant<int, DK / 8>{}, 3 * DK / 8,
+            const f32x16 c = rows_dot(Qg, Ss + 32 * I * L4, std::integral_constant<int, DK / 8>{}, 3 * DK / 8,
                                       f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) KA[I * 1024 + e * 64 + lane] = c[e];
@@ -488,22 +491,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const float f = sIn[32 * J + l32];
             f32x16 c;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L1 + 32 * J + l32] * f;
+            for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L4 + 32 * J + l32] * f;
             return c;
         };
         auto s_done = [&](int tl, f32x16 c) {
             const int I = tl / NJ, J = tl - I * NJ;
-            c = chain_t<SPLIT, kC / 2>([&](int s) { return Us[(2 * s + kg) * kSL + 32 * I + l32]; },
-                              [&](int s) { return KS[(2 * s + kg) * L1 + 32 * J + l32]; }, c);
+            c = chain8_t<SPLIT, kC / 16>(
+                [&](int i) { return lds_col8<LU>(&Us[(16 * i + 8 * kg) * LU + 32 * I + l32]); },
+                [&](int i) { return lds_col8<L4>(&KS[(16 * i + 8 * kg) * L4 + 32 * J + l32]); }, c);
             const float f = sOut[32 * J + l32];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L1 + 32 * J + l32] = c[e] * f;
+            for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L4 + 32 * J + l32] = c[e] * f;
         };
         f32x16 oacc = {};
         if constexpr (GDN) {
-            // 3. A (wave 0) and P (wave 1) beside X = V - (K gamma) S^T in place
-            // of V on value columns 32 (w - 2) .. (waves 2, 3); with the
-            // strengths in the columns of T, T diag(beta) X is U = T (R_v - R_w S^T)
+            // 3. A (wave 0) and P (wave 1) beside diag(beta) X, X = V - (K gamma) S^T,
+            // in place of V on value columns 32 (w - 2) .. (waves 2, 3)
             if (w == 0) {
                 if (!wide) {
                     const f32x16 c = gram(KA);
@@ -526,62 +529,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int I = w - 2;
                 f32x16 c;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * kSL + 32 * I + l32];
-                c = rows_dot(Rw, Ss + 32 * I * L1, Full{}, 0, c);  // Rw holds -k gamma
+                for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * LU + 32 * I + l32];
+                c = rows_dot(Rw, Ss + 32 * I * L4, Full{}, 0, c);  // Rw holds -k gamma
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
+                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = bet[row(e)] * c[e];
             }
             __syncthreads();
-            // 4. the inverse (wave 0) beside O = (Q gamma) S^T on value columns
+            // 4. T = (I + diag(beta) A)^-1 (wave 0) beside O = (Q gamma) S^T on value columns
             // 32 (w - 1) .. (waves 1, 2)
             if (w == 0) {
-                const float4* A4 = reinterpret_cast<const float4*>(Am);
-                float4 b4[kC / 4];  // the strengths, applied to the rows of A
-#pragma unroll
-                for (int m = 0; m < kC / 4; ++m) b4[m] = reinterpret_cast<const float4*>(bet)[m];
-                float xcol[kC];
-                // row r + 1 of A is in flight while row r is reduced
-                float4 cur[kC / 4], nxt[kC / 4];
-                cur[0] = A4[kC / 4];
-                xcol[0] = l32 == 0 ? 1.f : 0.f;
-#pragma unroll
-                for (int r = 1; r < kC; ++r) {
-                    if (r + 1 < kC) {
-                        // the offset is tied to the previous row's result, so
-                        // these loads issue after it and one row ahead of use
-                        int off4 = (r + 1) * (kC / 4);
-                        asm volatile("" : "+v"(off4) : "v"(xcol[r - 1]));
-#pragma unroll
-                        for (int m = 0; m < (r + 4) / 4; ++m) nxt[m] = A4[off4 + m];
-                    }
-                    float a = 0.f;
-#pragma unroll
-                    for (int j = 0; j < r; ++j) {
-                        const float4 aj = cur[j / 4];
-                        const float av = (j & 3) == 0 ? aj.x : (j & 3) == 1 ? aj.y : (j & 3) == 2 ? aj.z : aj.w;
-                        a += av * xcol[j];
-                    }
-                    const float4 bq = b4[r / 4];
-                    const float br = (r & 3) == 0 ? bq.x : (r & 3) == 1 ? bq.y : (r & 3) == 2 ? bq.z : bq.w;
-                    xcol[r] = (r == l32 ? 1.f : 0.f) - br * a;
-                    if (r + 1 < kC) {
-#pragma unroll
-                        for (int m = 0; m < (r + 4) / 4; ++m) cur[m] = nxt[m];
-                    }
-                }
-                if (kg == 0) {
-                    const float bl = bet[l32];
-#pragma unroll
-                    for (int r = 0; r < kC; ++r) Tm[r * kLT + l32] = xcol[r] * bl;
-                }
+                solve_unit_lower<kC, kLT>(Am, bet, Tm, lane);
             } else if (w < 3) {
-                oacc = rows_dot(Qg, Ss + 32 * (w - 1) * L1, OHead{}, 0, oacc);
+                oacc = rows_dot(Qg, Ss + 32 * (w - 1) * L4, OHead{}, 0, oacc);
             } else if (kSplitO) {
                 o_tail(0);
                 o_tail(1);
             }
             __syncthreads();
-            // 5. U = T diag(beta) X (waves 1, 2) while waves 0 and 3 read their state
+            // 5. U = T (diag(beta) X) (waves 1, 2) while waves 0 and 3 read their state
             // tiles; then O += P U on the same value columns beside the state update.
             // State tiles 0, 1, .. go to waves 0, 3, 1, 2, 0, 3, 0, 3.
             auto tile_of = [&](int i) { return (w == 3 ? 1 : 0) + (i ? 2 * i + 2 : 0); };
@@ -590,7 +555,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int I = w - 1;
                 const f32x16 c = tok_dot(Tm, I, f32x16{});
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * kSL + 32 * I + l32] = c[e];
+                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = c[e];
             } else {
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
@@ -617,7 +582,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     }
                 }
             } else if (w >= 2) {
-                oacc = rows_dot(Qg, Ss + 32 * (w - 2) * L1, OHead{}, 0, oacc);
+                oacc = rows_dot(Qg, Ss + 32 * (w - 2) * L4, OHead{}, 0, oacc);
             } else if (kSplitO) {
                 o_tail(0);
                 o_tail(1);
@@ -629,7 +594,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     __syncthreads();
     if (ST)
-        for (int x = tid; x < kSL * DK; x += kThreads) ST[s_base + x] = Ss[x / DK * L1 + x % DK];
+        for (int x = tid; x < kSL * DK; x += kThreads) ST[s_base + x] = Ss[x / DK * L4 + x % DK];
 }
 
 template <int MODE, int DK, typename E>

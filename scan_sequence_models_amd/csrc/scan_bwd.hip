@@ -48,6 +48,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_f32.hpp"
+#include "solve.hpp"
 
 namespace gds {
 namespace {
@@ -139,62 +140,6 @@ __device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, float w_ra
     }
 }
 
-// T = (I + diag(bet) B)^-1 for the strictly lower part of B (row stride LB, as
-// float4 rows) into Tm (row stride LT), from its 16x16 blocks: the two diagonal
-// blocks D0, D1 by forward substitution side by side (lane (b, c) of each
-// half-wave owns column c of block b, x_r = [r == c] - bet_r sum_{j<r} B_rj x_j,
-// rows read as float4 two rows ahead), then T10 = -D1 diag(bet) B10 D0 on the
-// fp32 MFMA (16x16x4).  The upper right block of Tm stays zero from the start.
-// All 64 lanes of the wave take part.
-template <int LT = LM>
-__device__ __forceinline__ void solve_unit_lower(const float* Bm, const float* bet, float* Tm, int lane) {
-    const int b = (lane >> 4) & 1, c = lane & 15, kg = lane >> 5;
-    const float* Bb = Bm + 16 * b * LB + 16 * b;
-    float br[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) br[r] = bet[16 * b + r];
-    f32x4 rw[3][4];  // rows r, r + 1, r + 2 in flight
-    auto load_row = [&](int r, f32x4 (&dst)[4]) {
-#pragma unroll
-        for (int q = 0; q < (r + 3) / 4; ++q) dst[q] = *reinterpret_cast<const f32x4*>(&Bb[r * LB + 4 * q]);
-    };
-    load_row(1, rw[1]);
-    load_row(2, rw[2]);
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (r + 2 < 16) load_row(r + 2, rw[(r + 2) % 3]);
-        __builtin_amdgcn_sched_barrier(0);
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int q = 0; q < (r + 3) / 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * q + i;
-                if (j < r) {
-                    if (i & 1) s1 += rw[r % 3][q][i] * x[j];
-                    else s0 += rw[r % 3][q][i] * x[j];
-                }
-            }
-        x[r] = (r == c ? 1.f : 0.f) - br[r] * (s0 + s1);
-    }
-    if (kg == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LT + 16 * b + c] = x[r];
-    }
-    // T10 = -D1 (diag(bet) B10) D0: lane (n16, g4) supplies contraction indices
-    // 4 g4 .. 4 g4 + 3 and holds rows 4 g4 .. 4 g4 + 3 of column n16
-    const int n16 = lane & 15, g4 = lane >> 4;
-    f32x4 y = {}, t10 = {};
-    const f32x4 br10 = *reinterpret_cast<const f32x4*>(&Bm[(16 + n16) * LB + 4 * g4]);
-    const float bs = bet[16 + n16];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) y = mfma4(br10[kk] * bs, Tm[(4 * g4 + kk) * LT + n16], y);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) t10 = mfma4(Tm[(16 + n16) * LT + 16 + 4 * g4 + kk], y[kk], t10);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Tm[(16 + 4 * g4 + r) * LT + n16] = -t10[r];
-}
 
 // ---------------------------------------------------------------------------
 // Forward states: S entering chunk n goes to ckpt[bh][n][rows of the slice].
@@ -374,7 +319,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (w == 0) {
             k_gram(0);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            solve_unit_lower<LT>(Bm[0], gt[0].bet, Tm[0], lane);
+            solve_unit_lower<LB, LT>(Bm[0], gt[0].bet, Tm[0], lane);
         } else if (w == 3 && NC > 1) {
             k_gram(1);
         }
@@ -417,7 +362,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         Un[y] = gn.bw[t] * Un[y] - gn.bg[t] * c[e];
                     }
                 } else if constexpr (W == 0) {
-                    if (n + 1 < NC) solve_unit_lower<LT>(Bm[(n + 1) & 1], gt[(n + 1) % NB].bet, Tm[(n + 1) & 1], lane);
+                    if (n + 1 < NC) solve_unit_lower<LB, LT>(Bm[(n + 1) & 1], gt[(n + 1) % NB].bet, Tm[(n + 1) & 1], lane);
                     if (slices == 2) zero_outputs(c0);
                 } else {
                     if (n + 2 < NC) put_k(n + 2);
@@ -720,7 +665,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // the same wave solves right away: its own B rows are complete once
             // its LDS writes are
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            solve_unit_lower<LP>(Bm, bet, Tm, lane);
+            solve_unit_lower<LB, LP>(Bm, bet, Tm, lane);
         } else if (w == 1) {
             const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(
                 [&](int i) { return lds_f32x8(&Qs[l32 * L1 + 16 * i + k8]); },
