@@ -756,7 +756,7 @@ def bench_bwd(args, w):
         + ht * (2 * w.dk + w.dv + 2) * 4
     ws_bytes = 2 * nws
     csrc = os.path.join(ROOT, "scan_sequence_models_amd", "csrc")
-    src = [os.path.join(csrc, "scan_bwd.hip"), os.path.join(csrc, "mfma_f32.hpp")]
+    src = [os.path.join(csrc, f) for f in ("scan_bwd.hip", "mfma_f32.hpp", "solve.hpp")]
     result = {
         "metric": "tokens/s gradient of the gated-delta scan (H=16, d=128, T=8192); % MFMA roofline",
         "value": w.B * w.T / (ms / 1e3),
@@ -923,7 +923,7 @@ def main():
     traffic = None
     if w.diag_gates:
         kernel_src = [os.path.join(ROOT, "scan_sequence_models_amd", "csrc", f)
-                      for f in ("chunk_diag.hip", "mfma_f32.hpp")]
+                      for f in ("chunk_diag.hip", "mfma_f32.hpp", "solve.hpp")]
         traffic = measured_traffic(kernel_src, f"chunk_diag_{w.name}_traffic.txt")
     elif path != "blelloch" and w.dk == 128 and w.chunk == 64 and bf:
         traffic = measured_traffic(kernel_src, f"chunk_mfma_{w.name}_traffic.txt")
