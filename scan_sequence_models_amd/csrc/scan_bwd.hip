@@ -57,7 +57,6 @@ constexpr int kThreads = 256;
 constexpr int kC = 32;       // tokens per chunk
 constexpr int kSL = 64;      // value rows per workgroup
 constexpr int LV = kSL + 1;  // row stride of [32][64] value-row arrays
-constexpr int LM = kC + 1;   // row stride of 32x32 matrices
 constexpr int LB = kC + 4;   // row stride of the k-Gram (float4 rows for the solve)
 
 // The elements of a 16-byte load: eight bf16 or four floats.
