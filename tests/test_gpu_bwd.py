@@ -63,6 +63,10 @@ CASES = [
     ("gdn-b8h16t8192", "gdn", "bf16", 1, 2, 200, 128, 128),
     ("gdn-b8h16t8192", "gla", "bf16", 1, 2, 97, 128, 128),
     ("gdn-b8h16t8192", "gdn", "bf16", 1, 1, 5, 128, 128),
+    # bf16 at d_k = 64 (the stored state's permuted layout over 16 units of a
+    # row) and GLA at d_k = 64, with ragged tails
+    ("gdn-b8h16t8192", "gdn", "bf16", 1, 2, 150, 64, 64),
+    ("tiny-gdn", "gla", "f32", 1, 1, 95, 64, 128),
 ]
 
 
