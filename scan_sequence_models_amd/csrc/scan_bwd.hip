@@ -54,6 +54,7 @@ namespace gds {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kThreadsR = 512;  // the reverse chunk pass: 8 waves, two per SIMD
 constexpr int kC = 32;       // tokens per chunk
 constexpr int kSL = 64;      // value rows per workgroup
 constexpr int LV = kSL + 1;  // row stride of [32][64] value-row arrays
@@ -428,12 +429,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // ---------------------------------------------------------------------------
 // The reverse chunk pass.
 template <int MODE, int DK, typename E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_chunk_kernel(
+__global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_chunk_kernel(
     BwdJob J) {
     constexpr bool GDN = MODE == 0;
     // bf16 data: the products in split bf16 (about 16 significant bits each)
     constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
-    constexpr int NJ = DK / 32;  // key-column tiles: wave w < NJ owns dq and dk tile w
+    // key-column tiles: wave 4 + j (j < NJ) owns dq tile j, wave j owns dk tile j
+    constexpr int NJ = DK / 32;
     // Rows of the key-wide arrays and of the 32x32 matrices are 16-byte rows
     // (operands along a row come in 16-byte reads; down a column, the rows
     // r and r + 8 of the two lane halves land 32 banks apart).
@@ -519,9 +521,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             unsafeAtomicAdd(p, x);
     };
 
-    for (int x = tid; x < kSL * DK; x += kThreads) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
+    for (int x = tid; x < kSL * DK; x += kThreadsR) dSs[x / DK * L1 + x % DK] = J.dST ? J.dST[s_base + x] : 0.f;
     if constexpr (GDN)
-        for (int x = tid; x < kC * LP; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
+        for (int x = tid; x < kC * LP; x += kThreadsR) Tm[x] = 0.f;  // T's upper right block stays zero
 
     // The next chunk's (in reverse order) q, k, v, dO and gates are fetched
     // into registers during this one's last two phases (unconditional loads
@@ -531,21 +533,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // (16-byte loads: EV elements each; RK, RV loads per row)
     constexpr int EV = 16 / (int)sizeof(E), RK = DK / EV, RV = kSL / EV;
     constexpr int QL = kC * RK, VL = kC * RV;  // loads per chunk
-    constexpr int NK = (QL + kThreads - 1) / kThreads, NV = (VL + kThreads - 1) / kThreads;
+    constexpr int NK = (QL + kThreadsR - 1) / kThreadsR, NV = (VL + kThreadsR - 1) / kThreadsR;
     uint4 pq[NK], pk[NK], pv[NV], pd[NV];
     float pa = 1.f, pb = 0.f, pw = 0.f;
     auto fetch = [&](int n) {
         const int cn = n * kC;
 #pragma unroll
         for (int m = 0; m < NK; ++m) {
-            const int x = min(tid + m * kThreads, QL - 1), t = min(cn + x / RK, T - 1);
+            const int x = min(tid + m * kThreadsR, QL - 1), t = min(cn + x / RK, T - 1);
             const size_t gi = (tok0 + t) * DK + (x % RK) * EV;
             pq[m] = *reinterpret_cast<const uint4*>(q + gi);
             pk[m] = *reinterpret_cast<const uint4*>(k + gi);
         }
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
-            const int x = min(tid + m * kThreads, VL - 1), t = min(cn + x / RV, T - 1);
+            const int x = min(tid + m * kThreadsR, VL - 1), t = min(cn + x / RV, T - 1);
             const size_t gi = (tok0 + t) * dv + r0 + (x % RV) * EV;
             pv[m] = *reinterpret_cast<const uint4*>(v + gi);
             pd[m] = dO ? *reinterpret_cast<const uint4*>(dO + gi) : uint4{0u, 0u, 0u, 0u};
@@ -571,17 +573,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const float* src = J.ckpt + (((size_t)bh * J.nchunks + cn) * dv + r0) * DK;
         if constexpr (SWZ) {
 #pragma unroll
-            for (int b = w; b < kSL * DK / 256; b += 4)
+            for (int b = w; b < kSL * DK / 256; b += kThreadsR / 64)
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 256 * b + 4 * lane),
                                                  (__attribute__((address_space(3))) void*)(Ss + 256 * b), 16, 0, 0);
         } else {
-            constexpr int NS4 = kSL * DK / 4 / kThreads;
+            constexpr int NS4 = kSL * DK / 4 / kThreadsR;
             float4 sv[NS4];
 #pragma unroll
-            for (int m = 0; m < NS4; ++m) sv[m] = reinterpret_cast<const float4*>(src)[tid + m * kThreads];
+            for (int m = 0; m < NS4; ++m) sv[m] = reinterpret_cast<const float4*>(src)[tid + m * kThreadsR];
 #pragma unroll
             for (int m = 0; m < NS4; ++m) {
-                const int x = 4 * (tid + m * kThreads);
+                const int x = 4 * (tid + m * kThreadsR);
                 *reinterpret_cast<float4*>(Ss + x / DK * L1 + x % DK) = sv[m];
             }
         }
@@ -599,8 +601,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (!SWZ && n < J.nchunks - 1) load_state(n);
 #pragma unroll
         for (int m = 0; m < NK; ++m) {
-            const int x = tid + m * kThreads, t = x / RK, y = t * L1 + (x % RK) * EV;
-            if (QL % kThreads == 0 || x < QL) {
+            const int x = tid + m * kThreadsR, t = x / RK, y = t * L1 + (x % RK) * EV;
+            if (QL % kThreadsR == 0 || x < QL) {
                 const bool in = c0 + t < T;
                 float fq[EV], fk[EV];
                 unpack16(pq[m], fq);
@@ -616,8 +618,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads, t = x / RV, y = t * LV + (x % RV) * EV;
-            if (VL % kThreads == 0 || x < VL) {
+            const int x = tid + m * kThreadsR, t = x / RV, y = t * LV + (x % RV) * EV;
+            if (VL % kThreadsR == 0 || x < VL) {
                 const bool in = c0 + t < T;
                 float fv[EV], fd[EV];
                 unpack16(pv[m], fv);
@@ -631,28 +633,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             }
         }
-        for (int x = tid; x < 16 * kC; x += kThreads) dgp[x] = 0.f;
-        for (int x = tid; x < 8 * kC; x += kThreads) dbp[x] = 0.f;
+        for (int x = tid; x < 16 * kC; x += kThreadsR) dgp[x] = 0.f;
+        for (int x = tid; x < 8 * kC; x += kThreadsR) dbp[x] = 0.f;
         if (tid < 16) dgc[tid] = 0.f;
         if (w == 0) chunk_gates<GDN>(pa, pb, pw, c0, T, lane, G2, gam, Dd, bet, bw, bg, gC);
         __syncthreads();
 
-        f32x16 accQ = {}, accK = {};
-        f32x16 ksT = {};  // waves 2, 3 (delta rule): (K S^T)^T on value columns 32 (w - 2) .., kept to phase 5
-        // the owners' dQ = diag(gamma) dO S (+ its dg share)
-        auto owner_dq = [&]() {
-            // dO exact in bf16, gamma applied to the rows after
-            accQ = chain8_t<SPLIT, kSL / 16, true>([&](int i) { return rowv8(&dOs[l32 * LV + 16 * i + k8]); },
-                                          [&](int i) { return s_col8(16 * i + k8, 32 * w + l32); },
-                                          accQ);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) accQ[e] *= gam[row(e)];
-            f32x16 x;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) x[e] = accQ[e] * Qs[row(e) * L1 + 32 * w + l32];
-            store_row_sums(x, dgp + w * kC, l32, kg, 1.f);  // dg slots 0..3
-        };
-        // Phase 1: B and then T (wave 0, delta rule), P, X; the other owners' dQ part
+        // Roles (8 waves): dq owners 4 + j and dk owners j (j < NJ) keep their
+        // tiles in registers for the whole chunk; the rest of the work is
+        // spread per phase below.
+        const bool qown = w >= 4 && w - 4 < NJ, kown = w < NJ;
+        const int jq = w - 4, jk = w;  // the owned tiles
+        f32x16 acc = {};   // dq tile jq (qown) or dk tile jk (kown)
+        f32x16 ksT = {};   // waves 2, 3 (delta rule): (K S^T)^T on value columns 32 (w - 2) .., kept to phase 5
+        // waves 4 + h2 (h2 < 4): dS tiles 2 h2, 2 h2 + 1 from phase 2 to phase 5
+        f32x16 dsc[2];
+        float dss[2] = {0.f, 0.f};
+        const int h2 = w - 4;
+        auto ds_tile = [&](int h) { return 2 * h2 + h; };
+        constexpr int G1 = kC / 16;
+        // Phase 1: B and then T (wave 0, delta rule), P (wave 1), X (waves 2, 3,
+        // delta rule) or dU = Kd dS'^T (waves 2, 3, linear attention), and the dq
+        // owners' dQ = diag(gamma) dO S (+ its dg share)
         if (GDN && w == 0) {
             auto kr = [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); };
             const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(kr, kr, f32x16{});
@@ -674,7 +676,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int t = row(e);
                 Pm[t * LP + l32] = l32 <= t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
             }
-        } else if (GDN && w >= 2) {
+        } else if (GDN && (w == 2 || w == 3)) {
             const int I = w - 2;
             // (K S^T)^T = S K^T with the token along the lanes: X_t = beta_t V_t - beta_t gamma_t (K S^T)_t
             // is written row by row, and the tile serves <dX_t, (K S^T)_t> in phase 5 as an in-lane sum
@@ -687,47 +689,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int y = l32 * LV + 32 * I + row(e);
                 Us[y] = b * Us[y] + nbg * ksT[e];
             }
-        } else if (!GDN && w >= 2) {  // GLA: dU = Kd dS'^T starts here
+        } else if (!GDN && (w == 2 || w == 3)) {  // GLA: dU = Kd dS'^T
             const int I = w - 2;
             const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
                 [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
                 [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
+        } else if (qown) {
+            // dO exact in bf16, gamma applied to the rows after
+            acc = chain8_t<SPLIT, kSL / 16, true>([&](int i) { return rowv8(&dOs[l32 * LV + 16 * i + k8]); },
+                                         [&](int i) { return s_col8(16 * i + k8, 32 * jq + l32); }, acc);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] *= gam[row(e)];
+            f32x16 x;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = acc[e] * Qs[row(e) * L1 + 32 * jq + l32];
+            store_row_sums(x, dgp + jq * kC, l32, kg, 1.f);  // dg slots 0..3
         }
-        // (with the delta rule wave 0's share waits for phase 2, beside the others' work)
-        if (w < NJ && !(GDN && w == 0)) owner_dq();
         __syncthreads();
-        // Phase 2 (delta rule): wave 0's dQ part; U = T X (wave 3); dU = Kd dS'^T (waves 1, 2)
-        if constexpr (GDN) {
-            if (w == 0) {
-                owner_dq();
-            } else if (w == 3) {
+        // Phase 2: U = T X (waves 2, 3) and dU = Kd dS'^T (waves 0, 1) with the
+        // delta rule; the first part of the dS tiles, gamma_C dS' + dO^T diag(gamma) Q,
+        // and <dS', S> (waves 4 .. 7, held in registers until phase 5: dS' is read
+        // until then)
+        if (GDN && (w == 2 || w == 3)) {
+            const int I = w - 2;
+            const f32x16 c = chain8_t<SPLIT, kC / 16>(
+                [&](int i) { return lds_f32x8(&Tm[l32 * LP + 16 * i + k8]); },
+                [&](int i) { return lds_col8<LV>(&Us[(16 * i + k8) * LV + 32 * I + l32]); }, f32x16{});
 #pragma unroll
-                for (int I = 0; I < 2; ++I) {
-                    const f32x16 c = chain8_t<SPLIT, kC / 16>(
-                        [&](int i) { return lds_f32x8(&Tm[l32 * LP + 16 * i + k8]); },
-                        [&](int i) { return lds_col8<LV>(&Us[(16 * i + k8) * LV + 32 * I + l32]); }, f32x16{});
+            for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+        } else if (GDN && w < 2) {
+            const int I = w;
+            const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
+                [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
+                [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) Us[row(e) * LV + 32 * I + l32] = c[e];
+            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
+        } else if (w >= 4) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tile = ds_tile(h);
+                if (tile < 2 * NJ) {
+                    const int I = tile / NJ, Jt = tile - I * NJ;
+                    f32x16 c;
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float d = dSs[(32 * I + row(e)) * L1 + 32 * Jt + l32];
+                        ss += d * Ss[sx(32 * I + row(e), 32 * Jt + l32)];
+                        c[e] = gC[0] * d;
+                    }
+                    // dO gamma on the dO side, so q stays exact in bf16
+                    dsc[h] = chain8_t<SPLIT, G1, false, true>(
+                        [&](int i) {
+                            const int t = 16 * i + k8;
+                            f32x8 r = lds_col8<LV>(&dOs[t * LV + 32 * I + l32]);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) r[j] *= gam[t + j];
+                            return r;
+                        },
+                        [&](int i) { return lds_col8<L1>(&Qs[(16 * i + k8) * L1 + 32 * Jt + l32]); }, c);
+                    dss[h] = ss;
                 }
-            } else {
-                const int I = w - 1;
-                const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
-                    [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
-                    [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
-#pragma unroll
-                for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
             }
-            __syncthreads();
         }
-        // Phase 3: dP (waves 0 and 3 both form it: wave 0 writes dP * Gamma, wave 3 the
-        // row and column sums of dP * P), dU += P^T dO (waves 1, 2), the owners' dK += Kd-part
-        if (w == 0 || w == 3) {
+        __syncthreads();
+        // Phase 3: dP (waves 4 and 5 both form it: wave 4 writes dP * Gamma, wave 5
+        // the row and column sums of dP * P), dU += P^T dO (waves 0, 1 with the
+        // delta rule, 2, 3 without), the dk owners' dK += Kd-part
+        if (w == 4 || w == 5) {
             const f32x16 c = chain8_t<SPLIT, kSL / 16, true>([&](int i) { return rowv8(&dOs[l32 * LV + 16 * i + k8]); },
                                                     [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
                                                     f32x16{});
-            if (w == 0) {
+            if (w == 4) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
@@ -743,8 +778,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 store_row_sums(L, dgp + 8 * kC, l32, kg, 1.f);   // dg slot 8
                 store_col_sums(L, dgp + 9 * kC, l32, kg, -1.f);  // dg slot 9
             }
-        } else if (w < 3) {
-            const int I = w - 1;
+        }
+        if (GDN ? w < 2 : (w == 2 || w == 3)) {
+            const int I = GDN ? w : w - 2;
             {  // e^{g_C - g_t} <(U dS')_t, K_t> = <U_t, dU_t> while dU holds Kd dS'^T: lane l32 takes
                // token l32, each half 16 of the tile's value columns
                 float t1 = 0.f;
@@ -765,18 +801,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = c[e];
         }
-        if (w < NJ) {  // dKd = U dS'
+        if (kown) {  // dKd = U dS'
             const f32x16 c = chain8_t<SPLIT, kSL / 16>(
                 [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
-                [&](int i) { return lds_col8<L1>(&dSs[(16 * i + k8) * L1 + 32 * w + l32]); }, f32x16{});
+                [&](int i) { return lds_col8<L1>(&dSs[(16 * i + k8) * L1 + 32 * jk + l32]); }, f32x16{});
 #pragma unroll
-            for (int e = 0; e < 16; ++e) accK[e] += Dd[row(e)] * c[e];
+            for (int e = 0; e < 16; ++e) acc[e] += Dd[row(e)] * c[e];
         }
         __syncthreads();
-        // Phase 4: dX = T^T dU (delta rule; computed as dX^T = dU^T T, the token along the lanes, so
-        // <dX_t, V_t> is an in-lane sum; dX replaces V row by row); the owners' dQ, dK += dQK parts
-        if (GDN && (w == 1 || w == 2)) {
-            const int I = w - 1;
+        // Phase 4: dX = T^T dU (delta rule, waves 0, 1; computed as dX^T = dU^T T, the token
+        // along the lanes, so <dX_t, V_t> is an in-lane sum; dX replaces V row by row); the
+        // owners' dQ, dK += dQK parts
+        if (GDN && w < 2) {
+            const int I = w;
             const f32x16 c = chain8_t<SPLIT, kC / 16>(
                 [&](int i) { return lds_col8<LV>(&dUs[(16 * i + k8) * LV + 32 * I + l32]); },
                 [&](int i) { return lds_col8<LP>(&Tm[(16 * i + k8) * LP + l32]); }, f32x16{});
@@ -790,38 +827,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             db += __shfl_xor(db, 32, 64);
             if (kg == 0) dbp[I * kC + l32] = db;  // dbeta slots 0, 1
         }
-        if (w == 0 || w == 3) {  // dO's last reader is the dS update: scale its rows by gamma in place
-            for (int x = (w == 0 ? 0 : 64) + lane; x < kC * kSL; x += 128) {
-                const int t = x / kSL;
-                dOs[t * LV + x - t * kSL] *= gam[t];
-            }
-        }
-        if (w < NJ) {
-            accQ = chain8_t<SPLIT, kC / 16, false, true>(
+        if (qown)
+            acc = chain8_t<SPLIT, kC / 16, false, true>(
                 [&](int i) { return lds_f32x8(&dQKm[l32 * LP + 16 * i + k8]); },
-                [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * w + l32]); }, accQ);
-            accK = chain8_t<SPLIT, kC / 16, false, true>(
+                [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * jq + l32]); }, acc);
+        if (kown)
+            acc = chain8_t<SPLIT, kC / 16, false, true>(
                 [&](int i) { return lds_col8<LP>(&dQKm[(16 * i + k8) * LP + l32]); },
-                [&](int i) { return lds_col8<L1>(&Qs[(16 * i + k8) * L1 + 32 * w + l32]); }, accK);
-        }
+                [&](int i) { return lds_col8<L1>(&Qs[(16 * i + k8) * L1 + 32 * jk + l32]); }, acc);
         __syncthreads();
         // the next chunk's inputs are in flight through phases 5 and 6
         if (n > 0) fetch(n - 1);
-        // Phase 5: dRw (owners), dA (waves 0 and 1 both form it: wave 0 writes
-        // dKK, wave 1 the sums), dS
+        // Phase 5: dRw (dk owners), dA (waves 6 and 7 both form it: wave 6 writes
+        // dKK, wave 7 the sums), <dRw, K> (waves 2, 3), the rest of the dS tiles
+        // (waves 4 .. 7)
         if constexpr (GDN) {
-            if (w < NJ) {  // dRw = -dX S
+            if (kown) {  // dRw = -dX S
                 const f32x16 c = chain8_t<SPLIT, kSL / 16>(
                     [&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
-                    [&](int i) { return s_col8(16 * i + k8, 32 * w + l32); }, f32x16{});
+                    [&](int i) { return s_col8(16 * i + k8, 32 * jk + l32); }, f32x16{});
 #pragma unroll
-                for (int e = 0; e < 16; ++e) accK[e] += bg[row(e)] * c[e];
+                for (int e = 0; e < 16; ++e) acc[e] += bg[row(e)] * c[e];
             }
-            if (w < 2) {
+            if (w == 6 || w == 7) {
                 const f32x16 c = chain8_t<SPLIT, kSL / 16>([&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
                                                   [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
                                                   f32x16{});
-                if (w == 0) {
+                if (w == 6) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int t = row(e);
@@ -841,7 +873,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
                 }
             }
-            if (w >= 2) {  // <dRw_t, K_t> = -<dX_t, (K S^T)_t> over this wave's value columns
+            if (w == 2 || w == 3) {  // <dRw_t, K_t> = -<dX_t, (K S^T)_t> over this wave's value columns
                 const int I = w - 2;
                 float wt = 0.f;
 #pragma unroll
@@ -854,77 +886,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         // dV = diag(bw) dX (delta rule) or dU (linear attention), row-major from LDS
-        for (int x = tid; x < kC * kSL; x += kThreads) {
+        for (int x = tid; x < kC * kSL; x += kThreadsR) {
             const int t = x / kSL, i = x % kSL;
             if (c0 + t < T)
                 J.dv_out[(tok0 + c0 + t) * dv + r0 + i] = GDN ? bw[t] * Vs[t * LV + i] : dUs[t * LV + i];
         }
-        // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K, and <dS', S>
-        // (delta rule, dk = 128: waves 0, 1 formed dA above, so they take one of
-        // the 8 tiles each and waves 2, 3 three each)
-        constexpr bool kSkew = GDN && NJ == 4;
-        const int t_lo = kSkew ? (w < 2 ? w : 3 * w - 4) : w;
-        const int t_hi = kSkew ? (w < 2 ? w + 1 : 3 * w - 1) : 2 * NJ;
-        for (int tile = t_lo; tile < t_hi; tile += kSkew ? 1 : 4) {
-            const int I = tile / NJ, Jt = tile - I * NJ;
-            f32x16 c;
-            float ss = 0.f;
+        // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K: the last
+        // term (delta rule; k exact in bf16, beta gamma on the dX side), then dS into LDS
+        if (w >= 4) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int y = (32 * I + row(e)) * L1 + 32 * Jt + l32;
-                const float d = dSs[y];
-                ss += d * Ss[sx(32 * I + row(e), 32 * Jt + l32)];
-                c[e] = gC[0] * d;
+            for (int h = 0; h < 2; ++h) {
+                const int tile = ds_tile(h);
+                if (tile < 2 * NJ) {
+                    const int I = tile / NJ, Jt = tile - I * NJ;
+                    f32x16 c = dsc[h];
+                    if constexpr (GDN)
+                        c = chain8_t<SPLIT, G1, false, true>(
+                            [&](int i) {
+                                const int t = 16 * i + k8;
+                                f32x8 r;
+#pragma unroll
+                                for (int j = 0; j < 8; ++j) r[j] = -bg[t + j] * Vs[(t + j) * LV + 32 * I + l32];
+                                return r;
+                            },
+                            [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * Jt + l32]); }, c);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dSs[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
+                    const float ss = group_sum<64>(dss[h]);
+                    if (lane == 0) dgc[4 + tile] = ss;
+                }
             }
-            // the two products as one chain over 2 C (GDN) or C tokens; the token
-            // scalings sit on the dO and dX side, so q and k stay exact in bf16
-            constexpr int G1 = kC / 16;
-            c = chain8_t<SPLIT, GDN ? 2 * G1 : G1, false, true>(
-                [&](int i) {
-                    const int t = 16 * (i % G1) + k8;
-                    if (i < G1) return lds_col8<LV>(&dOs[t * LV + 32 * I + l32]);
-                    f32x8 r;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) r[j] = -bg[t + j] * Vs[(t + j) * LV + 32 * I + l32];
-                    return r;
-                },
-                [&](int i) {
-                    const int t = 16 * (i % G1) + k8;
-                    return lds_col8<L1>(&(i < G1 ? Qs : Ks)[t * L1 + 32 * Jt + l32]);
-                },
-                c);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) dSs[(32 * I + row(e)) * L1 + 32 * Jt + l32] = c[e];
-            ss = group_sum<64>(ss);
-            if (lane == 0) dgc[4 + tile] = ss;
         }
         __syncthreads();
         if (SWZ && n > 0) load_state(n - 1);
-        // Phase 6: dK += (dKK + dKK^T) K; partial dq, dk; dg -> d ln alpha, dbeta
-        if (w < NJ) {
-            if constexpr (GDN)
-                accK = chain8_t<SPLIT, kC / 16, false, true>(
-                    [&](int i) {
-                        return lds_f32x8(&dKKm[l32 * LP + 16 * i + k8]) + lds_col8<LP>(&dKKm[(16 * i + k8) * LP + l32]);
-                    },
-                    [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * w + l32]); }, accK);
+        // Phase 6: dK += (dKK + dKK^T) K (dk owners); dq, dk; dg -> d ln alpha, dbeta (wave 7)
+        if (GDN && kown)
+            acc = chain8_t<SPLIT, kC / 16, false, true>(
+                [&](int i) {
+                    return lds_f32x8(&dKKm[l32 * LP + 16 * i + k8]) + lds_col8<LP>(&dKKm[(16 * i + k8) * LP + l32]);
+                },
+                [&](int i) { return lds_col8<L1>(&Ks[(16 * i + k8) * L1 + 32 * jk + l32]); }, acc);
+        if (qown || kown) {
+            const int jt = qown ? jq : jk;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
                 if (c0 + t < T) {
                     if (slices > 2) {
-                        const size_t o = (part_tok + c0 + t) * DK + 32 * w + l32;
-                        pdq[o] = accQ[e];
-                        pdk[o] = accK[e];
+                        const size_t o = (part_tok + c0 + t) * DK + 32 * jt + l32;
+                        (qown ? pdq : pdk)[o] = acc[e];
                     } else {
-                        const size_t o = (tok0 + c0 + t) * DK + 32 * w + l32;
-                        put(J.dq + o, accQ[e]);
-                        put(J.dk_out + o, accK[e]);
+                        const size_t o = (tok0 + c0 + t) * DK + 32 * jt + l32;
+                        put((qown ? J.dq : J.dk_out) + o, acc[e]);
                     }
                 }
             }
         }
-        if (w == 3) {
+        if (w == 7) {
             // one wave (lanes 0..31 hold tokens) sums the slots in a fixed order
             const int t = l32;
             float dg = 0.f;
@@ -974,7 +992,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the state's LDS-direct loads
     }
     __syncthreads();
-    for (int x = tid; x < kSL * DK; x += kThreads) J.dS0[s_base + x] = dSs[x / DK * L1 + x % DK];
+    for (int x = tid; x < kSL * DK; x += kThreadsR) J.dS0[s_base + x] = dSs[x / DK * L1 + x % DK];
 }
 
 // Sum of the per-slice partials; dalpha = d ln alpha / alpha.  dq and dk in
@@ -1025,7 +1043,7 @@ template <int MODE, int DK, typename E>
 hipError_t launch_typed(const BwdJob& J, hipStream_t s) {
     const dim3 grid((unsigned)((size_t)J.BH * (J.dv / kSL)));
     hipLaunchKernelGGL((bwd_states_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
-    hipLaunchKernelGGL((bwd_chunk_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
+    hipLaunchKernelGGL((bwd_chunk_kernel<MODE, DK, E>), grid, dim3(kThreadsR), 0, s, J);
     if (J.dv / kSL > 2) {
         const size_t n4 = (size_t)J.BH * J.T * J.dk / 4;
         const size_t want = (n4 + kThreads - 1) / kThreads;
