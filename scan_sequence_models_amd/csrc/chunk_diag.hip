@@ -204,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 constexpr int kSL = 64;      // value rows per workgroup
+constexpr int kThreadsM = 512;  // 8 waves, two per SIMD
 constexpr int kLT = kC + 4;  // row stride of the 32x32 T and P tiles (float4 rows)
 // widest |g_t - g_m| (log2) of the factored Gram: its operands stay within
 // 2^(+-64), far from float32 overflow, and a term lost to underflow there is
@@ -211,7 +212,7 @@ constexpr int kLT = kC + 4;  // row stride of the 32x32 T and P tiles (float4 ro
 constexpr float kSpread = 64.f;
 
 template <int MODE, int DK, typename E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_diag_mfma_kernel(
+__global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_diag_mfma_kernel(
     int T, int dv, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     E* __restrict__ o, float* __restrict__ ST) {
@@ -219,9 +220,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int NJ = DK / 32;
     // bf16 data: the products in split bf16 (about 16 significant bits each)
     constexpr bool SPLIT = std::is_same<E, uint16_t>::value;              // 32-column tiles of a key-wide row
-    constexpr int NQ = kC * DK / kThreads;   // tokens per thread, all of one key channel
-    constexpr int NR = kThreads / DK;        // runs of NQ tokens per chunk
-    constexpr int NV = kC * kSL / kThreads;  // value elements per thread and chunk
+    constexpr int NQ = kC * DK / kThreadsM;   // tokens per thread, all of one key channel
+    constexpr int NR = kThreadsM / DK;        // runs of NQ tokens per chunk
+    constexpr int NV = kC * kSL / kThreadsM;  // value elements per thread and chunk
     static_assert((kC / 2) % NQ == 0, "the middle token m = kC/2 - 1 ends a run");
     static_assert(DK < 64 || kC * (DK + 4) >= 2048, "KA holds two partial O tiles");
     // Row strides: 16-byte rows.  The pairwise Gram reads float4 runs of
@@ -248,29 +249,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ float sIn[DK];                    // per-channel factors of the state update:
     __shared__ float sOut[DK];                   // e^{g_m}, e^{g_C - g_m} (wide: gamma_C, 1)
     __shared__ __align__(16) float bet[kC];
-    __shared__ int wflag[kThreads / 64];         // a wave holds a chunk too wide to factor
+    __shared__ int wflag[kThreadsM / 64];        // a wave holds a chunk too wide to factor
 
     const int slices = dv / kSL;
     int bh, sl;
     unit_part(blockIdx.x, gridDim.x / slices, slices, bh, sl);  // a head's slices share its q, k reads in L2
     const int r0 = sl * kSL;
-    const int tid = threadIdx.x, lane = tid & 63;
+    int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, kg = lane >> 5;
-    const int ch = tid % DK, run = tid / DK;  // this thread's key channel and run of tokens
+    int l32 = lane & 31, kg = lane >> 5;
+    int ch = tid % DK, run = tid / DK;  // this thread's key channel and run of tokens
     const size_t qk_base = (size_t)bh * T * DK;
     const size_t v_base = (size_t)bh * T * dv;
     const size_t s_base = ((size_t)bh * dv + r0) * DK;
     // accumulator element e of a 32x32 tile: row 8 (e / 4) + 4 kg + e % 4, column l32
     auto row = [&](int e) { return 8 * (e >> 2) + 4 * kg + (e & 3); };
 
-    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L4 + x % DK] = S0 ? S0[s_base + x] : 0.f;
-    for (int x = tid; x < kC * kLT; x += kThreads) Pm[x] = 0.f;
+    for (int x = tid; x < kSL * DK; x += kThreadsM) Ss[x / DK * L4 + x % DK] = S0 ? S0[s_base + x] : 0.f;
+    for (int x = tid; x < kC * kLT; x += kThreadsM) Pm[x] = 0.f;
     if constexpr (GDN)
-        for (int x = tid; x < kC * kLT; x += kThreads) Tm[x] = 0.f;  // T's upper right block stays zero
+        for (int x = tid; x < kC * kLT; x += kThreadsM) Tm[x] = 0.f;  // T's upper right block stays zero
 
     // The next chunk's inputs are fetched into registers while this chunk
-    // computes (one wave per SIMD leaves no other way to hide HBM latency).
+    // computes (every wave works on the chunk; nothing else hides HBM latency).
     // The loads are unconditional, from a token index clamped into the
     // sequence, and keep the raw element; masking and conversion happen when
     // they are used, so no load waits inside the fetch.
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads, t = min(cn + x / kSL, T - 1);
+            const int x = tid + m * kThreadsM, t = min(cn + x / kSL, T - 1);
             pv[m] = v[v_base + (size_t)t * dv + r0 + x % kSL];
         }
         if (GDN && tid < kC) pb = beta[(size_t)bh * T + min(cn + tid, T - 1)];
@@ -311,6 +312,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     const int nchunks = (T + kC - 1) / kC;
     for (int n = 0; n < nchunks; ++n) {
+        // The lane indices are opaque to the compiler from here on, so the
+        // address arithmetic built on them is redone in the loop rather than
+        // hoisted out of it into live registers.
+        asm volatile("" : "+v"(tid), "+v"(lane), "+v"(l32), "+v"(kg), "+v"(ch), "+v"(run));
         const int c0 = n * kC;
         const int o0 = min(kC, T - c0);  // tokens of this chunk inside the sequence
         __syncthreads();  // the previous chunk is done with every array
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreads;
+            const int x = tid + m * kThreadsM;
             Us[x / kSL * LU + x % kSL] = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
         }
         // one flag per wave, one barrier (the flags are next written after the
@@ -349,7 +354,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const bool wave_wide = __builtin_amdgcn_ballot_w64(!narrow) != 0;  // all lanes vote
         if (lane == 0) wflag[w] = wave_wide;
         __syncthreads();
-        const bool wide = wflag[0] | wflag[1] | wflag[2] | wflag[3];
+        bool wide = false;
+#pragma unroll
+        for (int i = 0; i < kThreadsM / 64; ++i) wide |= wflag[i] != 0;
         // 2. scaled copies and Gram operands.  The bases are opaque to the
         // compiler, so each store below is one base register plus an immediate
         // offset instead of an address hoisted out of the chunk loop.
@@ -398,49 +405,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // decayed Gram and scores over the strictly lower pairs s < t, two pairs (t, 2b)
             // and (t, 2b + 1) per thread so that they share the loads of token t: row t holds
             // ceil(t / 2) such blocks, floor(t^2 / 4) of them precede it, and rows 1 .. 31
-            // hold exactly 256, one per thread (the second pair of the last block of an odd
-            // row is the diagonal, which is not stored here)
-            static_assert(kC == 32 && kThreads == 256, "one Gram block per thread");
-            const int p = tid;
-            int t = (int)__builtin_sqrtf(4.f * (float)p + 1.f);
-            if ((t * t) / 4 > p) --t;
-            if (((t + 1) * (t + 1)) / 4 <= p) ++t;
-            const int s1 = 2 * (p - (t * t) / 4), s2 = s1 + 1;
-            const float4* gt = reinterpret_cast<const float4*>(KB + t * L4);
-            const float4* kt = reinterpret_cast<const float4*>(KA + t * L4);
-            const float4* qt = reinterpret_cast<const float4*>(QA + t * L4);
-            const float4* g1p = reinterpret_cast<const float4*>(KB + s1 * L4);
-            const float4* k1p = reinterpret_cast<const float4*>(KA + s1 * L4);
-            const float4* g2p = reinterpret_cast<const float4*>(KB + s2 * L4);
-            const float4* k2p = reinterpret_cast<const float4*>(KA + s2 * L4);
-            float pa1 = 0.f, pp1 = 0.f, pa2 = 0.f, pp2 = 0.f;
+            // hold exactly 256, one per thread of waves 0 .. 3 (the second pair of the last
+            // block of an odd row is the diagonal, which is not stored here)
+            static_assert(kC == 32 && kThreadsM >= 256, "one Gram block per thread");
+            if (tid < 256) {
+                const int p = tid;
+                int t = (int)__builtin_sqrtf(4.f * (float)p + 1.f);
+                if ((t * t) / 4 > p) --t;
+                if (((t + 1) * (t + 1)) / 4 <= p) ++t;
+                const int s1 = 2 * (p - (t * t) / 4), s2 = s1 + 1;
+                const float4* gt = reinterpret_cast<const float4*>(KB + t * L4);
+                const float4* kt = reinterpret_cast<const float4*>(KA + t * L4);
+                const float4* qt = reinterpret_cast<const float4*>(QA + t * L4);
+                const float4* g1p = reinterpret_cast<const float4*>(KB + s1 * L4);
+                const float4* k1p = reinterpret_cast<const float4*>(KA + s1 * L4);
+                const float4* g2p = reinterpret_cast<const float4*>(KB + s2 * L4);
+                const float4* k2p = reinterpret_cast<const float4*>(KA + s2 * L4);
+                float pa1 = 0.f, pp1 = 0.f, pa2 = 0.f, pp2 = 0.f;
 #pragma unroll 2
-            for (int c = 0; c < DK / 4; ++c) {
-                const float4 gg = gt[c], qv = qt[c], ga = g1p[c], ka = k1p[c], gb = g2p[c], kb = k2p[c];
-                const float a0 = __builtin_amdgcn_exp2f(gg.x - ga.x) * ka.x;
-                const float a1 = __builtin_amdgcn_exp2f(gg.y - ga.y) * ka.y;
-                const float a2 = __builtin_amdgcn_exp2f(gg.z - ga.z) * ka.z;
-                const float a3 = __builtin_amdgcn_exp2f(gg.w - ga.w) * ka.w;
-                const float b0 = __builtin_amdgcn_exp2f(gg.x - gb.x) * kb.x;
-                const float b1 = __builtin_amdgcn_exp2f(gg.y - gb.y) * kb.y;
-                const float b2 = __builtin_amdgcn_exp2f(gg.z - gb.z) * kb.z;
-                const float b3 = __builtin_amdgcn_exp2f(gg.w - gb.w) * kb.w;
-                pp1 += qv.x * a0 + qv.y * a1 + qv.z * a2 + qv.w * a3;
-                pp2 += qv.x * b0 + qv.y * b1 + qv.z * b2 + qv.w * b3;
-                if constexpr (GDN) {
-                    const float4 kk = kt[c];
-                    pa1 += kk.x * a0 + kk.y * a1 + kk.z * a2 + kk.w * a3;
-                    pa2 += kk.x * b0 + kk.y * b1 + kk.z * b2 + kk.w * b3;
+                for (int c = 0; c < DK / 4; ++c) {
+                    const float4 gg = gt[c], qv = qt[c], ga = g1p[c], ka = k1p[c], gb = g2p[c], kb = k2p[c];
+                    const float a0 = __builtin_amdgcn_exp2f(gg.x - ga.x) * ka.x;
+                    const float a1 = __builtin_amdgcn_exp2f(gg.y - ga.y) * ka.y;
+                    const float a2 = __builtin_amdgcn_exp2f(gg.z - ga.z) * ka.z;
+                    const float a3 = __builtin_amdgcn_exp2f(gg.w - ga.w) * ka.w;
+                    const float b0 = __builtin_amdgcn_exp2f(gg.x - gb.x) * kb.x;
+                    const float b1 = __builtin_amdgcn_exp2f(gg.y - gb.y) * kb.y;
+                    const float b2 = __builtin_amdgcn_exp2f(gg.z - gb.z) * kb.z;
+                    const float b3 = __builtin_amdgcn_exp2f(gg.w - gb.w) * kb.w;
+                    pp1 += qv.x * a0 + qv.y * a1 + qv.z * a2 + qv.w * a3;
+                    pp2 += qv.x * b0 + qv.y * b1 + qv.z * b2 + qv.w * b3;
+                    if constexpr (GDN) {
+                        const float4 kk = kt[c];
+                        pa1 += kk.x * a0 + kk.y * a1 + kk.z * a2 + kk.w * a3;
+                        pa2 += kk.x * b0 + kk.y * b1 + kk.z * b2 + kk.w * b3;
+                    }
+                }
+                if constexpr (GDN) Am[t * kC + s1] = pa1;
+                Pm[t * kLT + s1] = pp1;
+                if (s2 < t) {
+                    if constexpr (GDN) Am[t * kC + s2] = pa2;
+                    Pm[t * kLT + s2] = pp2;
                 }
             }
-            if constexpr (GDN) Am[t * kC + s1] = pa1;
-            Pm[t * kLT + s1] = pp1;
-            if (s2 < t) {
-                if constexpr (GDN) Am[t * kC + s2] = pa2;
-                Pm[t * kLT + s2] = pp2;
-            }
-            if (tid < 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
-                const int td = tid >> 2, part = tid & 3;
+            if (tid >= 256 && tid < 256 + 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
+                const int td = (tid - 256) >> 2, part = tid & 3;
                 const float4* qa = reinterpret_cast<const float4*>(QA + td * L4) + part * (DK / 16);
                 const float4* ka = reinterpret_cast<const float4*>(KA + td * L4) + part * (DK / 16);
                 float pp = 0.f;
@@ -464,9 +473,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 if (t < o0) io<E>::store(o, v_base + (size_t)(c0 + t) * dv + r0 + 32 * I + l32, c[e]);
             }
         };
-        // O = (Q gamma) S^T: two waves take the first three quarters of the keys of
-        // one value tile each and a third wave the last quarter of both, its
-        // partial tiles passing through KA (free once the Gram is done)
+        // O = (Q gamma) S^T: two waves on two SIMDs take the first three quarters of
+        // the keys of one value tile each, and the two waves of a third SIMD the last
+        // quarter of one tile each, their partial tiles passing through KA (free once
+        // the Gram is done)
         constexpr bool kSplitO = DK >= 64;  // KA holds the two partial tiles
         using OHead = std::integral_constant<int, kSplitO ? 3 * DK / 8 : DK / 2>;
         auto o_tail = [&](int I) {
@@ -506,7 +516,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         f32x16 oacc = {};
         if constexpr (GDN) {
             // 3. A (wave 0) and P (wave 1) beside diag(beta) X, X = V - (K gamma) S^T,
-            // in place of V on value columns 32 (w - 2) .. (waves 2, 3)
+            // in place of V on value columns 32 (w - 2) .. (waves 2, 3).  Waves 4 .. 7 wait:
+            // splitting these products by key halves over the two waves of a SIMD, with
+            // the partial tiles passed through LDS, was slower.
             if (w == 0) {
                 if (!wide) {
                     const f32x16 c = gram(KA);
@@ -525,7 +537,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
                     }
                 }
-            } else {
+            } else if (w < 4) {
                 const int I = w - 2;
                 f32x16 c;
 #pragma unroll
@@ -536,42 +548,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
             __syncthreads();
             // 4. T = (I + diag(beta) A)^-1 (wave 0) beside O = (Q gamma) S^T on value columns
-            // 32 (w - 1) .. (waves 1, 2)
+            // 32 (w - 1) .. (waves 1, 2; waves 3, 7 the last key quarter of tiles 0, 1)
             if (w == 0) {
                 solve_unit_lower<kC, kLT>(Am, bet, Tm, lane);
             } else if (w < 3) {
                 oacc = rows_dot(Qg, Ss + 32 * (w - 1) * L4, OHead{}, 0, oacc);
-            } else if (kSplitO) {
-                o_tail(0);
-                o_tail(1);
+            } else if (kSplitO && (w == 3 || w == 7)) {
+                o_tail(w == 7);
             }
             __syncthreads();
-            // 5. U = T (diag(beta) X) (waves 1, 2) while waves 0 and 3 read their state
+            // 5. U = T (diag(beta) X) (waves 1, 2) while the other waves read their state
             // tiles; then O += P U on the same value columns beside the state update.
-            // State tiles 0, 1, .. go to waves 0, 3, 1, 2, 0, 3, 0, 3.
-            auto tile_of = [&](int i) { return (w == 3 ? 1 : 0) + (i ? 2 * i + 2 : 0); };
-            f32x16 sreg[3];
+            // State tile i goes to the wave in position i of 0, 3, 4, 5, 6, 7, 1, 2.
+            const int slot = w == 0 ? 0 : w == 3 ? 1 : w >= 4 ? w - 2 : w + 5;
+            const bool has_tile = slot < 2 * NJ;
+            f32x16 sreg;
             if (w == 1 || w == 2) {
                 const int I = w - 1;
-                const f32x16 c = tok_dot(Tm, I, f32x16{});
+                const f32x16 u = tok_dot(Tm, I, f32x16{});
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = c[e];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-                    if (tile_of(i) < 2 * NJ) sreg[i] = s_init(tile_of(i));
+                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = u[e];
+            } else if (has_tile) {
+                sreg = s_init(slot);
             }
             __syncthreads();
             if (w == 1 || w == 2) {
                 store_o(w - 1, tok_dot(Pm, w - 1, o_add_tail(w - 1, oacc)));
-                if (w + 1 < 2 * NJ) s_done(w + 1, s_init(w + 1));
-            } else {
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-                    if (tile_of(i) < 2 * NJ) s_done(tile_of(i), sreg[i]);
+                if (has_tile) s_done(slot, s_init(slot));
+            } else if (has_tile) {
+                s_done(slot, sreg);
             }
         } else {
-            // P (wave 0) beside O = (Q gamma) S^T on value columns 32 (w - 2) .. (waves 2, 3)
+            // P (wave 0) beside O = (Q gamma) S^T on value columns 32 (w - 2) ..
+            // (waves 2, 3; waves 1, 5 the last key quarter of tiles 0, 1)
             if (w == 0) {
                 if (!wide) {
                     const f32x16 c = gram(QA);
@@ -581,20 +590,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
                     }
                 }
-            } else if (w >= 2) {
+            } else if (w == 2 || w == 3) {
                 oacc = rows_dot(Qg, Ss + 32 * (w - 2) * L4, OHead{}, 0, oacc);
-            } else if (kSplitO) {
-                o_tail(0);
-                o_tail(1);
+            } else if (kSplitO && (w == 1 || w == 5)) {
+                o_tail(w == 5);
             }
             __syncthreads();  // P done, every read of the old state done
-            if (w >= 2) store_o(w - 2, tok_dot(Pm, w - 2, o_add_tail(w - 2, oacc)));
-            for (int tl = w; tl < 2 * NJ; tl += 4) s_done(tl, s_init(tl));
+            // state tile i goes to the wave in position i of 0, 1, 4, 5, 6, 7, 2, 3
+            const int slot = w < 2 ? w : w >= 4 ? w - 2 : w + 4;
+            if (w == 2 || w == 3) store_o(w - 2, tok_dot(Pm, w - 2, o_add_tail(w - 2, oacc)));
+            if (slot < 2 * NJ) s_done(slot, s_init(slot));
         }
     }
     __syncthreads();
     if (ST)
-        for (int x = tid; x < kSL * DK; x += kThreads) ST[s_base + x] = Ss[x / DK * L4 + x % DK];
+        for (int x = tid; x < kSL * DK; x += kThreadsM) ST[s_base + x] = Ss[x / DK * L4 + x % DK];
 }
 
 template <int MODE, int DK, typename E>
@@ -608,7 +618,7 @@ hipError_t launch_dk(int BH, int T, int dv, const void* q, const void* k, const 
     if constexpr (DK >= 32) {
         if (dv % kSL == 0) {
             hipLaunchKernelGGL((chunk_diag_mfma_kernel<MODE, DK, E>), dim3((unsigned)((size_t)BH * (dv / kSL))),
-                               dim3(kThreads), 0, s, T, dv, qq, kk, vv, alpha, beta, S0, oo, ST);
+                               dim3(kThreadsM), 0, s, T, dv, qq, kk, vv, alpha, beta, S0, oo, ST);
             return hipGetLastError();
         }
     }
