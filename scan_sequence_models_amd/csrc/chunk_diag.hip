@@ -232,15 +232,32 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
     // rows r and r + 8 of the two lane halves land 32 banks apart.
     constexpr int L4 = DK + 4;
     constexpr int LU = kSL + 4;
+    // With bf16 data, Qg, Rw and (in a factored chunk) QA, KA, KB hold bf16 hi / lo
+    // planes instead of floats, split once by their producer rather than by every
+    // product that reads them: row t of such an array is the hi parts of its d_k
+    // keys, then the lo parts, in the row's L4 floats (LP bf16; 16-byte reads of
+    // 16 rows stay conflict-free).  Kt holds the state update's keys as floats in
+    // every chunk.
+    constexpr bool PL = SPLIT;
+    constexpr int LP = 2 * L4;
+    // The operands of P U and of the state update, which run along tokens, are
+    // held transposed in the same way (bf16 data): U^T [value][token] and the
+    // update's keys Kt^T [key][token], row r the hi parts of its 32 tokens, then
+    // the lo parts (LT2 bf16 per row: 16-byte reads of 16 rows conflict-free).
+    constexpr int LT2 = 2 * kC + 8;
     // Gram operands: q e^{g - g_m}, k e^{g - g_m} and k e^{g_m - g} in a
     // factored chunk; q, k and the cumulative log2 decay g in a wide one
     __shared__ __align__(16) float QA[kC * L4];
     __shared__ __align__(16) float KA[kC * L4];
     __shared__ __align__(16) float KB[kC * L4];
     __shared__ __align__(16) float Qg[kC * L4];            // q * gamma
-    __shared__ __align__(16) float Kt[kC * L4];            // k * e^{g_C - g} (wide chunks)
+    // the state update's keys: k e^{g_m - g} (factored) or k e^{g_C - g} (wide)
+    __shared__ __align__(16) float Kt[PL ? DK * LT2 / 2 : kC * L4];
     __shared__ __align__(16) float Rw[GDN ? kC * L4 : 4];  // -(k * gamma)
     __shared__ __align__(16) float Us[kC * LU];            // v slice, then X (without beta), then U
+    // U^T planes: in Qg (free once the read-out's first product is done) with the
+    // delta rule; gated linear attention (U = V) keeps V^T in an array of its own
+    __shared__ __align__(16) float UTs[!GDN && PL ? kSL * LT2 / 2 : 4];
     __shared__ __align__(16) float Am[GDN ? kC * kC : 1];  // A without beta (strictly lower)
     __shared__ __align__(16) float Tm[GDN ? kC * kLT : 4];  // T
     __shared__ __align__(16) float Pm[kC * kLT];            // P (lower, inclusive; zero above)
@@ -277,21 +294,39 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
     // they are used, so no load waits inside the fetch.
     E pq[NQ], pk[NQ], pv[NV];
     float pa[NQ], pb = 0.f;
+    // Per-head buffer resources: one instruction per load, its offset a 32-bit
+    // register plus a constant, and reads past the sequence's end return zeros
+    // (those tokens are masked where they are used).  Byte offsets stay below
+    // 2^31 (checked at launch).
+    auto rsrc = [](const void* base, size_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q + qk_base, (size_t)T * DK * sizeof(E));
+    const __amdgpu_buffer_rsrc_t rk = rsrc(k + qk_base, (size_t)T * DK * sizeof(E));
+    const __amdgpu_buffer_rsrc_t ra = rsrc(alpha + qk_base, (size_t)T * DK * 4);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(v + v_base + r0, ((size_t)T * dv - r0) * sizeof(E));
+    const __amdgpu_buffer_rsrc_t rb = rsrc(beta ? beta + (size_t)bh * T : alpha, beta ? (size_t)T * 4 : 0);
+    auto ld_e = [](__amdgpu_buffer_rsrc_t r, int off) {
+        if constexpr (std::is_same<E, uint16_t>::value)
+            return (E)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+        else
+            return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    };
+    auto ld_f = [](__amdgpu_buffer_rsrc_t r, int off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    };
     auto fetch = [&](int cn) {
+        const int e0 = (cn + run * NQ) * DK + ch;  // element of (first token, channel) in the head
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
-            const int t = min(cn + run * NQ + m, T - 1);
-            const size_t gi = qk_base + (size_t)t * DK + ch;
-            pq[m] = q[gi];
-            pk[m] = k[gi];
-            pa[m] = alpha[gi];
+            pq[m] = ld_e(rq, (e0 + m * DK) * (int)sizeof(E));
+            pk[m] = ld_e(rk, (e0 + m * DK) * (int)sizeof(E));
+            pa[m] = ld_f(ra, (e0 + m * DK) * 4);
         }
+        const int v0 = (cn + tid / kSL) * dv + tid % kSL;
 #pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int x = tid + m * kThreadsM, t = min(cn + x / kSL, T - 1);
-            pv[m] = v[v_base + (size_t)t * dv + r0 + x % kSL];
-        }
-        if (GDN && tid < kC) pb = beta[(size_t)bh * T + min(cn + tid, T - 1)];
+        for (int m = 0; m < NV; ++m) pv[m] = ld_e(rv, (v0 + m * (kThreadsM / kSL) * dv) * (int)sizeof(E));
+        if (GDN && tid < kC) pb = ld_f(rb, (cn + tid) * 4);
     };
     fetch(0);
 
@@ -347,7 +382,14 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
             const int x = tid + m * kThreadsM;
-            Us[x / kSL * LU + x % kSL] = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
+            const float vx = x / kSL < o0 ? to_f32(pv[m]) : 0.f;
+            if constexpr (!GDN && PL) {  // U = V: V^T planes, (value, token) at value LT2 + token
+                uint16_t* P = reinterpret_cast<uint16_t*>(UTs) + (x % kSL) * LT2 + x / kSL;
+                P[0] = f32_to_bf16(vx);  // exact: bf16 data
+                P[kC] = 0;
+            } else {
+                Us[x / kSL * LU + x % kSL] = vx;
+            }
         }
         // one flag per wave, one barrier (the flags are next written after the
         // following chunk's first barrier)
@@ -360,17 +402,31 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
         // 2. scaled copies and Gram operands.  The bases are opaque to the
         // compiler, so each store below is one base register plus an immediate
         // offset instead of an address hoisted out of the chunk loop.
-        int b4 = run * NQ * L4 + ch;
-        asm volatile("" : "+v"(b4));
+        int b4 = run * NQ * L4 + ch, p4 = 2 * run * NQ * L4 + ch;
+        asm volatile("" : "+v"(b4), "+v"(p4));
+        // element (t, ch) of an operand array: a float at t L4 + ch, or hi / lo bf16
+        // at t LP + ch and t LP + DK + ch
+        auto put_op = [&](float* X, int m, float x) {
+            if constexpr (PL) {
+                uint16_t* P = reinterpret_cast<uint16_t*>(X) + p4 + m * LP;
+                const uint16_t h = f32_to_bf16(x);
+                P[0] = h;
+                P[DK] = f32_to_bf16(x - bf16_to_f32(h));
+            } else {
+                X[b4 + m * L4] = x;
+            }
+        };
         auto put = [&](auto factored) {
             constexpr bool F = decltype(factored)::value;
-            // factored: gamma_t = e^{g_t - g_m} e^{g_m}, and k e^{g_C - g} is not
-            // formed (the state update scales by e^{g_C - g_m} per column instead)
-            const float em = __builtin_amdgcn_exp2f(gm);
+            // factored: gamma_t = e^{g_t - g_m} e^{g_m}, with e^{g_m} moved onto the
+            // state's columns (below), so that (Q gamma) S^T = QA (S e^{g_m})^T and
+            // (K gamma) S^T = KA (S e^{g_m})^T need no copies of their own; k e^{g_C - g}
+            // is not formed either (the state update scales by e^{g_C - g_m} per column)
             if (run == 0) {
-                sIn[ch] = F ? em : __builtin_amdgcn_exp2f(gc);
+                sIn[ch] = F ? 1.f : __builtin_amdgcn_exp2f(gc);
                 sOut[ch] = F ? __builtin_amdgcn_exp2f(gc - gm) : 1.f;
             }
+            float kt[NQ];  // the state update's keys of this thread's tokens
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
                 const bool in = run * NQ + m < o0;
@@ -378,27 +434,55 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const int y = b4 + m * L4;
                 if constexpr (F) {
                     const float up = __builtin_amdgcn_exp2f(g[m] - gm), dn = __builtin_amdgcn_exp2f(gm - g[m]);
-                    const float qu = qq * up, ku = kk * up;
-                    QA[y] = qu;
-                    Qg[y] = qu * em;
-                    if constexpr (GDN) {
-                        KA[y] = ku;
-                        Rw[y] = -(ku * em);
-                    }
-                    KB[y] = kk * dn;
+                    const float qu = qq * up, ku = kk * up, kd = kk * dn;
+                    put_op(QA, m, qu);
+                    if constexpr (GDN) put_op(KA, m, ku);
+                    put_op(KB, m, kd);
+                    kt[m] = kd;
                 } else {
                     const float gam = __builtin_amdgcn_exp2f(g[m]);
-                    Qg[y] = qq * gam;
-                    Kt[y] = kk * __builtin_amdgcn_exp2f(gc - g[m]);
-                    if constexpr (GDN) Rw[y] = -(kk * gam);
+                    put_op(Qg, m, qq * gam);
+                    kt[m] = kk * __builtin_amdgcn_exp2f(gc - g[m]);
+                    if constexpr (GDN) put_op(Rw, m, -(kk * gam));
                     QA[y] = qq;
                     KA[y] = kk;
                     KB[y] = g[m];
                 }
             }
+            if constexpr (PL) {
+                // Kt^T planes: this thread's NQ consecutive tokens of key ch, one vector
+                // store per plane
+                typedef __bf16 bfq __attribute__((ext_vector_type(NQ)));
+                bfq hi, lo;
+#pragma unroll
+                for (int m = 0; m < NQ; ++m) {
+                    hi[m] = static_cast<__bf16>(kt[m]);
+                    lo[m] = static_cast<__bf16>(kt[m] - static_cast<float>(hi[m]));
+                }
+                uint16_t* P = reinterpret_cast<uint16_t*>(Kt) + ch * LT2 + run * NQ;
+                *reinterpret_cast<bfq*>(P) = hi;
+                *reinterpret_cast<bfq*>(P + kC) = lo;
+            } else {
+#pragma unroll
+                for (int m = 0; m < NQ; ++m) Kt[b4 + m * L4] = kt[m];
+            }
         };
-        if (wide) put(std::false_type{});
-        else put(std::true_type{});
+        if (wide) {
+            put(std::false_type{});
+        } else {
+            put(std::true_type{});
+            // S <- S diag(e^{g_m}) in place, tile w on wave w (the state update starts from
+            // it); e^{g_m} of key column c from the run totals: the runs before the middle
+            if (w < 2 * NJ) {
+                const int I = w / NJ, J = w - I * NJ, col = 32 * J + l32;
+                float gmc = 0.f;
+#pragma unroll
+                for (int r = 0; r < kC / 2 / NQ; ++r) gmc += Gr[r * DK + col];
+                const float f = __builtin_amdgcn_exp2f(gmc);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L4 + col] *= f;
+            }
+        }
         if (n + 1 < nchunks) fetch(c0 + kC);
         __syncthreads();
         if (wide) {
@@ -464,8 +548,82 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
             }
             __syncthreads();
         }
+        // c += A B^T over G groups of 16 keys from key 16 g0, A in planes and B in
+        // planes (dot_pp) or floats (dot_pf, split here): three bf16 MFMAs per group,
+        // hi hi + hi lo + lo hi; each group's operands are read one group ahead
+        auto plane8 = [&](const float* X, int g) {
+            return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(X) + l32 * LP + 16 * g + 8 * kg);
+        };
+        auto plane8lo = [&](const float* X, int g) {
+            return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(X) + l32 * LP + DK + 16 * g + 8 * kg);
+        };
+        auto dot_pp = [&](const float* A, const float* B, auto groups, int g0, f32x16 c) {
+            constexpr int G = decltype(groups)::value;
+            bf16x8 ah = plane8(A, g0), al = plane8lo(A, g0), bh = plane8(B, g0), bl = plane8lo(B, g0);
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                bf16x8 ahn = ah, aln = al, bhn = bh, bln = bl;
+                if (i + 1 < G) {
+                    ahn = plane8(A, g0 + i + 1);
+                    aln = plane8lo(A, g0 + i + 1);
+                    bhn = plane8(B, g0 + i + 1);
+                    bln = plane8lo(B, g0 + i + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                ah = ahn;
+                al = aln;
+                bh = bhn;
+                bl = bln;
+            }
+            return c;
+        };
+        auto dot_pf = [&](const float* A, const float* B, auto groups, int g0, f32x16 c) {
+            constexpr int G = decltype(groups)::value;
+            const float* bp = B + l32 * L4 + 16 * g0 + 8 * kg;
+            bf16x8 ah = plane8(A, g0), al = plane8lo(A, g0);
+            f32x8 b = lds_f32x8(bp);
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                bf16x8 ahn = ah, aln = al;
+                f32x8 bn = b;
+                if (i + 1 < G) {
+                    ahn = plane8(A, g0 + i + 1);
+                    aln = plane8lo(A, g0 + i + 1);
+                    bn = lds_f32x8(bp + 16 * (i + 1));
+                }
+                bf16x8 bh, bl;
+                split_bf16(b, bh, bl);
+                __builtin_amdgcn_sched_barrier(0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                ah = ahn;
+                al = aln;
+                b = bn;
+            }
+            return c;
+        };
+        // c += X Y^T over keys [2 k0, 2 k0 + 2 STEPS) with X an operand array (planes
+        // with bf16 data) and Y the state (floats)
+        auto op_dot_s = [&](const float* X, const float* Y, auto steps, int k0, f32x16 c) {
+            constexpr int STEPS = decltype(steps)::value;
+            if constexpr (PL)
+                return dot_pf(X, Y, std::integral_constant<int, STEPS / 8>{}, k0 / 8, c);
+            else
+                return rows_dot(X, Y, steps, k0, c);
+        };
         // factored Gram tile: C[t][s] = sum_i X_ti e^{g_ti - g_mi} k_si e^{g_mi - g_si}
-        auto gram = [&](const float* X) { return rows_dot(X, KB, Full{}, 0, f32x16{}); };
+        auto gram = [&](const float* X) {
+            if constexpr (PL)
+                return dot_pp(X, KB, std::integral_constant<int, DK / 16>{}, 0, f32x16{});
+            else
+                return rows_dot(X, KB, Full{}, 0, f32x16{});
+        };
         auto store_o = [&](int I, const f32x16& c) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -480,7 +638,7 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
         constexpr bool kSplitO = DK >= 64;  // KA holds the two partial tiles
         using OHead = std::integral_constant<int, kSplitO ? 3 * DK / 8 : DK / 2>;
         auto o_tail = [&](int I) {
-            const f32x16 c = rows_dot(Qg, Ss + 32 * I * L4, std::integral_constant<int, DK / 8>{}, 3 * DK / 8,
+            const f32x16 c = op_dot_s(wide ? Qg : QA, Ss + 32 * I * L4, std::integral_constant<int, DK / 8>{}, 3 * DK / 8,
                                       f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) KA[I * 1024 + e * 64 + lane] = c[e];
@@ -495,7 +653,7 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
         // S <- S diag(gamma_C) + U^T (K e^{g_C - g}) as 2 NJ tiles of 32 x 32; a
         // factored chunk forms (S e^{g_m} + U^T (K e^{g_m - g})) e^{g_C - g_m}
         // column by column
-        const float* KS = wide ? Kt : KB;
+        const float* KS = Kt;
         auto s_init = [&](int tl) {
             const int I = tl / NJ, J = tl - I * NJ;
             const float f = sIn[32 * J + l32];
@@ -504,21 +662,58 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
             for (int e = 0; e < 16; ++e) c[e] = Ss[(32 * I + row(e)) * L4 + 32 * J + l32] * f;
             return c;
         };
+        float* UT = GDN ? Qg : UTs;
+        // hi / lo parts of tokens 16 i + 8 kg .. + 7 of row r of a transposed plane array
+        auto tplane = [&](const float* X, int r, int i, int part) {
+            return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(X) + r * LT2 + part * kC +
+                                                    16 * i + 8 * kg);
+        };
         auto s_done = [&](int tl, f32x16 c) {
             const int I = tl / NJ, J = tl - I * NJ;
-            c = chain8_t<SPLIT, kC / 16>(
-                [&](int i) { return lds_col8<LU>(&Us[(16 * i + 8 * kg) * LU + 32 * I + l32]); },
-                [&](int i) { return lds_col8<L4>(&KS[(16 * i + 8 * kg) * L4 + 32 * J + l32]); }, c);
+            if constexpr (PL) {
+                const int ru = 32 * I + l32, rk = 32 * J + l32;
+#pragma unroll
+                for (int i = 0; i < kC / 16; ++i) {
+                    const bf16x8 ah = tplane(UT, ru, i, 0), al = tplane(UT, ru, i, 1);
+                    const bf16x8 bh = tplane(Kt, rk, i, 0), bl = tplane(Kt, rk, i, 1);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+                }
+            } else {
+                c = chain8_t<SPLIT, kC / 16>(
+                    [&](int i) { return lds_col8<LU>(&Us[(16 * i + 8 * kg) * LU + 32 * I + l32]); },
+                    [&](int i) { return lds_col8<L4>(&KS[(16 * i + 8 * kg) * L4 + 32 * J + l32]); }, c);
+            }
             const float f = sOut[32 * J + l32];
 #pragma unroll
             for (int e = 0; e < 16; ++e) Ss[(32 * I + row(e)) * L4 + 32 * J + l32] = c[e] * f;
         };
+        // c += P U on value columns 32 I ..
+        auto pu_dot = [&](int I, f32x16 c) {
+            if constexpr (PL) {
+                const int ru = 32 * I + l32;
+#pragma unroll
+                for (int i = 0; i < kC / 16; ++i) {
+                    bf16x8 ah, al;
+                    split_bf16(lds_f32x8(&Pm[l32 * kLT + 16 * i + 8 * kg]), ah, al);
+                    const bf16x8 bh = tplane(UT, ru, i, 0), bl = tplane(UT, ru, i, 1);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+                }
+                return c;
+            } else {
+                return tok_dot(Pm, I, c);
+            }
+        };
         f32x16 oacc = {};
         if constexpr (GDN) {
-            // 3. A (wave 0) and P (wave 1) beside diag(beta) X, X = V - (K gamma) S^T,
-            // in place of V on value columns 32 (w - 2) .. (waves 2, 3).  Waves 4 .. 7 wait:
-            // splitting these products by key halves over the two waves of a SIMD, with
-            // the partial tiles passed through LDS, was slower.
+            // 3. One phase: wave 0 forms A and at once inverts I + diag(beta) A with the
+            // blocked solve (its own writes of A need only its LDS counter); wave 1 forms P,
+            // waves 2, 3 diag(beta) X, X = V - (K gamma) S^T, in place of V on value columns
+            // 32 (w - 2) .., and waves 6, 7 O = (Q gamma) S^T on value tiles 0, 1.  None of
+            // them reads another's result.
             if (w == 0) {
                 if (!wide) {
                     const f32x16 c = gram(KA);
@@ -527,7 +722,9 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                         const int t = row(e);
                         Am[t * kC + l32] = l32 < t ? c[e] : 0.f;
                     }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 }
+                solve_unit_lower<kC, kLT>(Am, bet, Tm, lane);
             } else if (w == 1) {
                 if (!wide) {
                     const f32x16 c = gram(QA);
@@ -539,45 +736,51 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
             } else if (w < 4) {
                 const int I = w - 2;
+                const float sg = wide ? 1.f : -1.f;
                 f32x16 c;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = Us[row(e) * LU + 32 * I + l32];
-                c = rows_dot(Rw, Ss + 32 * I * L4, Full{}, 0, c);  // Rw holds -k gamma
+                for (int e = 0; e < 16; ++e) c[e] = sg * Us[row(e) * LU + 32 * I + l32];
+                // wide: V + Rw S^T (Rw holds -k gamma); factored: -(-V + KA (S e^{g_m})^T)
+                c = op_dot_s(wide ? Rw : KA, Ss + 32 * I * L4, Full{}, 0, c);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = bet[row(e)] * c[e];
+                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = sg * bet[row(e)] * c[e];
+            } else if (w >= 6) {
+                oacc = op_dot_s(wide ? Qg : QA, Ss + 32 * (w - 6) * L4, Full{}, 0, oacc);
             }
             __syncthreads();
-            // 4. T = (I + diag(beta) A)^-1 (wave 0) beside O = (Q gamma) S^T on value columns
-            // 32 (w - 1) .. (waves 1, 2; waves 3, 7 the last key quarter of tiles 0, 1)
-            if (w == 0) {
-                solve_unit_lower<kC, kLT>(Am, bet, Tm, lane);
-            } else if (w < 3) {
-                oacc = rows_dot(Qg, Ss + 32 * (w - 1) * L4, OHead{}, 0, oacc);
-            } else if (kSplitO && (w == 3 || w == 7)) {
-                o_tail(w == 7);
-            }
-            __syncthreads();
-            // 5. U = T (diag(beta) X) (waves 1, 2) while the other waves read their state
-            // tiles; then O += P U on the same value columns beside the state update.
-            // State tile i goes to the wave in position i of 0, 3, 4, 5, 6, 7, 1, 2.
-            const int slot = w == 0 ? 0 : w == 3 ? 1 : w >= 4 ? w - 2 : w + 5;
-            const bool has_tile = slot < 2 * NJ;
+            // 4. U = T (diag(beta) X) (waves 1, 2; as U^T planes with bf16 data) while the
+            // others read their first state tile; then O += P U (waves 6, 7) beside the
+            // state update, state tiles i and i + 6 on wave i < 6.
+            const bool has_tile = w < 6 && w < 2 * NJ;
             f32x16 sreg;
             if (w == 1 || w == 2) {
                 const int I = w - 1;
                 const f32x16 u = tok_dot(Tm, I, f32x16{});
+                if constexpr (PL) {
+                    // lane: value 32 I + l32, tokens 8 b + 4 kg .. + 3 in elements 4 b .. 4 b + 3
+                    uint16_t* P = reinterpret_cast<uint16_t*>(UT) + (32 * I + l32) * LT2 + 4 * kg;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = u[e];
+                    for (int b = 0; b < 4; ++b) {
+                        bf16x4 hi, lo;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            hi[r] = static_cast<__bf16>(u[4 * b + r]);
+                            lo[r] = static_cast<__bf16>(u[4 * b + r] - static_cast<float>(hi[r]));
+                        }
+                        *reinterpret_cast<bf16x4*>(P + 8 * b) = hi;
+                        *reinterpret_cast<bf16x4*>(P + kC + 8 * b) = lo;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) Us[row(e) * LU + 32 * I + l32] = u[e];
+                }
             } else if (has_tile) {
-                sreg = s_init(slot);
+                sreg = s_init(w);
             }
             __syncthreads();
-            if (w == 1 || w == 2) {
-                store_o(w - 1, tok_dot(Pm, w - 1, o_add_tail(w - 1, oacc)));
-                if (has_tile) s_done(slot, s_init(slot));
-            } else if (has_tile) {
-                s_done(slot, sreg);
-            }
+            if (w >= 6) store_o(w - 6, pu_dot(w - 6, oacc));
+            if (has_tile) s_done(w, (w == 1 || w == 2) ? s_init(w) : sreg);
+            if (w < 6 && w + 6 < 2 * NJ) s_done(w + 6, s_init(w + 6));
         } else {
             // P (wave 0) beside O = (Q gamma) S^T on value columns 32 (w - 2) ..
             // (waves 2, 3; waves 1, 5 the last key quarter of tiles 0, 1)
@@ -591,15 +794,20 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                     }
                 }
             } else if (w == 2 || w == 3) {
-                oacc = rows_dot(Qg, Ss + 32 * (w - 2) * L4, OHead{}, 0, oacc);
+                oacc = op_dot_s(wide ? Qg : QA, Ss + 32 * (w - 2) * L4, OHead{}, 0, oacc);
             } else if (kSplitO && (w == 1 || w == 5)) {
                 o_tail(w == 5);
             }
             __syncthreads();  // P done, every read of the old state done
-            // state tile i goes to the wave in position i of 0, 1, 4, 5, 6, 7, 2, 3
-            const int slot = w < 2 ? w : w >= 4 ? w - 2 : w + 4;
-            if (w == 2 || w == 3) store_o(w - 2, tok_dot(Pm, w - 2, o_add_tail(w - 2, oacc)));
-            if (slot < 2 * NJ) s_done(slot, s_init(slot));
+            // O += P U (waves 2, 3) beside the state update: state tiles i and i + 6 go to
+            // the wave in position i of 0, 1, 4, 5, 6, 7
+            const int slot = w < 2 ? w : w - 2;
+            if (w == 2 || w == 3) {
+                store_o(w - 2, pu_dot(w - 2, o_add_tail(w - 2, oacc)));
+            } else {
+                if (slot < 2 * NJ) s_done(slot, s_init(slot));
+                if (slot + 6 < 2 * NJ) s_done(slot + 6, s_init(slot + 6));
+            }
         }
     }
     __syncthreads();
@@ -616,7 +824,9 @@ hipError_t launch_dk(int BH, int T, int dv, const void* q, const void* k, const 
     const E* vv = static_cast<const E*>(v);
     E* oo = static_cast<E*>(o);
     if constexpr (DK >= 32) {
-        if (dv % kSL == 0) {
+        // the MFMA kernel's per-head byte offsets are 32-bit
+        const bool fits = (size_t)T * (size_t)(dv > DK ? dv : DK) * 4 < (size_t(1) << 31);
+        if (dv % kSL == 0 && fits) {
             hipLaunchKernelGGL((chunk_diag_mfma_kernel<MODE, DK, E>), dim3((unsigned)((size_t)BH * (dv / kSL))),
                                dim3(kThreadsM), 0, s, T, dv, qq, kk, vv, alpha, beta, S0, oo, ST);
             return hipGetLastError();
