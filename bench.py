@@ -923,7 +923,7 @@ def main():
     traffic = None
     if w.diag_gates:
         kernel_src = [os.path.join(ROOT, "scan_sequence_models_amd", "csrc", f)
-                      for f in ("chunk_diag.hip", "mfma_f32.hpp", "solve.hpp")]
+                      for f in ("chunk_diag.hip", "mfma_f32.hpp")]
         traffic = measured_traffic(kernel_src, f"chunk_diag_{w.name}_traffic.txt")
     elif path != "blelloch" and w.dk == 128 and w.chunk == 64 and bf:
         traffic = measured_traffic(kernel_src, f"chunk_mfma_{w.name}_traffic.txt")

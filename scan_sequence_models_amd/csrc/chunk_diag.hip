@@ -31,7 +31,6 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_f32.hpp"
-#include "solve.hpp"
 
 namespace gds {
 namespace {
@@ -174,33 +173,90 @@ __global__ __launch_bounds__(kThreads) void chunk_diag_kernel(
         for (int x = tid; x < SL * DK; x += kThreads) ST[s_base + x] = Ss[x];
 }
 
-// The same chunk algorithm with its products on the float32 MFMA
-// (v_mfma_f32_32x32x2f32, fp32 accuracy) for slices of 64 value rows and
-// dk >= 32.  Per chunk:
+// The same chunk algorithm with its products on the MFMA (float32, or split
+// bf16 with bf16 data) for slices of 64 value rows and dk >= 32, on 8 waves.
+// Per chunk:
 //   1. q, k and log2 a arrive in registers, one key channel and a run of
 //      consecutive tokens per thread; log2 a is summed along the chunk there,
 //      the runs exchanging their totals through LDS.  The value slice goes to
 //      LDS;
-//   2. the scaled copies q gamma and -k gamma (and, in a wide chunk,
-//      k e^{g_C - g}) are written from the registers, and so are the operands
-//      of the decayed Gram:
+//   2. the operands of the decayed Gram are written from the registers:
 //      splitting each pair's factor through the middle token m,
 //      e^{g_t - g_s} = e^{g_t - g_m} e^{g_m - g_s}, turns A and P into two
 //      plain 32x32 products of rows scaled by e^{+-(g - g_m)}.  In float32 that
 //      is safe while every |g_t - g_m| stays within kSpread (log2 units); a
 //      chunk with a wider span stores q, k and g instead and takes the
-//      pairwise form (one exp2 per token pair and channel);
-//   3. A and P on two waves beside X = V - (K gamma) S^T on the other two;
-//   4. T = (I + diag(beta) A)^-1 by one wave (a lane per column, forward
-//      substitution with the rows of A read as float4) beside
-//      O = (Q gamma) S^T on the other three;
-//   5. U = T diag(beta) X; then O += P U beside the state update
-//      S <- S diag(gamma_C) + U^T (K e^{g_C - g}), all as 32x32 tiles (a
-//      factored chunk scales by e^{g_C - g_m} per column instead of forming
-//      K e^{g_C - g}).
+//      pairwise form (one exp2 per token pair and channel), with the scaled
+//      copies q gamma, -k gamma and k e^{g_C - g}.  In a factored chunk
+//      e^{g_m} moves onto the state's columns instead (S~ = S diag(e^{g_m})),
+//      so that (Q gamma) S^T and (K gamma) S^T read the Gram's operands;
+//   3. one phase: A and at once T = (I + diag(beta) A)^-1 on one wave, P on
+//      another, X = V - (K gamma) S^T and O = (Q gamma) S^T on two each;
+//   4. U = T diag(beta) X;
+//   5. O += P U beside the state update S <- S diag(gamma_C) + U^T (K e^{g_C - g}),
+//      all as 32x32 tiles (a factored chunk forms
+//      (S~ + U^T (K e^{g_m - g})) diag(e^{g_C - g_m}) instead).
+// With bf16 data the operands are stored as bf16 hi / lo planes by the code
+// that forms them (the products' split done once), the token-long ones (U, P,
+// the update's keys) transposed so that they are read as 16-byte rows.
 // U = T (R_v - R_w S^T) = T diag(beta) (V - (K gamma) S^T) is the product
 // T R_v - (T R_w) S^T grouped so that the key-long part does not wait for the
 // inverse, with the strengths applied to the columns of T.
+// T = (I + diag(bet) B)^-1 for the strictly lower part of the 32x32 matrix B,
+// given as its transpose Bt (Bt[s][t] = B[t][s], row stride LB, 16-byte rows),
+// into Tm (row stride LT): the two 16x16 diagonal blocks side by side on the two
+// halves of the wave (lane (b, c) owns column c of block b) by right-looking
+// substitution, x_i = [i == c] - bet_i acc_i, then acc_r += B_ri x_i for r > i
+// (row i of Bt read as float4 rows ahead: each step waits on one product, not
+// on a sum over every earlier row), then T10 = -D1 diag(bet) B10 D0 on the
+// 16x16x4 fp32 MFMA.  The upper right block of Tm is not written: it stays zero
+// from the start.  All 64 lanes of the wave take part.
+template <int LB, int LT>
+__device__ __forceinline__ void solve_unit_lower_t(const float* Bt, const float* bet, float* Tm, int lane) {
+    const int b = (lane >> 4) & 1, c = lane & 15, kg = lane >> 5;
+    const float* Bb = Bt + 16 * b * LB + 16 * b;  // Bb[i * LB + r] = B[16 b + r][16 b + i]
+    float br[16], acc[16], x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        br[r] = bet[16 * b + r];
+        acc[r] = 0.f;
+    }
+    constexpr int AH = 2;  // rows read ahead of their step (LDS latency, not the
+                           // products, sets the pace of the substitution)
+    f32x4 rw[AH + 1][4];   // 4-entry groups from (i + 1) / 4 on of rows i .. i + AH
+    auto load_row = [&](int i, f32x4 (&dst)[4]) {
+#pragma unroll
+        for (int q = (i + 1) / 4; q < 4; ++q) dst[q] = *reinterpret_cast<const f32x4*>(&Bb[i * LB + 4 * q]);
+    };
+#pragma unroll
+    for (int i = 0; i < AH; ++i) load_row(i, rw[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i + AH < 16) load_row(i + AH, rw[(i + AH) % (AH + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        const float xi = (i == c ? 1.f : 0.f) - br[i] * acc[i];
+        x[i] = xi;
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) acc[r] = fmaf(rw[i % (AH + 1)][r >> 2][r & 3], xi, acc[r]);
+    }
+    if (kg == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LT + 16 * b + c] = x[r];
+    }
+    // T10 = -D1 (diag(bet) B10) D0: lane (n16, g4) supplies contraction indices
+    // 4 g4 .. 4 g4 + 3 and holds rows 4 g4 .. 4 g4 + 3 of column n16
+    const int n16 = lane & 15, g4 = lane >> 4;
+    f32x4 y = {}, t10 = {};
+    const float bs = bet[16 + n16];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)  // B10[n16][4 g4 + kk] = Bt[4 g4 + kk][16 + n16]
+        y = mfma4(Bt[(4 * g4 + kk) * LB + 16 + n16] * bs, Tm[(4 * g4 + kk) * LT + n16], y);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t10 = mfma4(Tm[(16 + n16) * LT + 16 + 4 * g4 + kk], y[kk], t10);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Tm[(16 + 4 * g4 + r) * LT + n16] = -t10[r];
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 constexpr int kSL = 64;      // value rows per workgroup
@@ -258,9 +314,9 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
     // U^T planes: in Qg (free once the read-out's first product is done) with the
     // delta rule; gated linear attention (U = V) keeps V^T in an array of its own
     __shared__ __align__(16) float UTs[!GDN && PL ? kSL * LT2 / 2 : 4];
-    __shared__ __align__(16) float Am[GDN ? kC * kC : 1];  // A without beta (strictly lower)
+    __shared__ __align__(16) float Am[GDN ? kC * kLT : 1];  // A^T without beta (A strictly lower)
     __shared__ __align__(16) float Tm[GDN ? kC * kLT : 4];  // T
-    __shared__ __align__(16) float Pm[kC * kLT];            // P (lower, inclusive; zero above)
+    __shared__ __align__(16) float Pm[kC * kLT];            // P (lower, inclusive; zero above; planes like U^T)
     __shared__ __align__(16) float Ss[kSL * L4];            // state slice
     __shared__ float Gr[NR * DK];                // run totals of log2 a
     __shared__ float sIn[DK];                    // per-channel factors of the state update:
@@ -485,6 +541,17 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         if (n + 1 < nchunks) fetch(c0 + kC);
         __syncthreads();
+        // P[t][s]: a float, or (bf16 data) hi / lo at t LT2 + s and t LT2 + kC + s
+        auto put_pm = [&](int t, int si, float x) {
+            if constexpr (PL) {
+                uint16_t* P = reinterpret_cast<uint16_t*>(Pm) + t * LT2 + si;
+                const uint16_t h = f32_to_bf16(x);
+                P[0] = h;
+                P[kC] = f32_to_bf16(x - bf16_to_f32(h));
+            } else {
+                Pm[t * kLT + si] = x;
+            }
+        };
         if (wide) {
             // decayed Gram and scores over the strictly lower pairs s < t, two pairs (t, 2b)
             // and (t, 2b + 1) per thread so that they share the loads of token t: row t holds
@@ -525,11 +592,11 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                         pa2 += kk.x * b0 + kk.y * b1 + kk.z * b2 + kk.w * b3;
                     }
                 }
-                if constexpr (GDN) Am[t * kC + s1] = pa1;
-                Pm[t * kLT + s1] = pp1;
+                if constexpr (GDN) Am[s1 * kLT + t] = pa1;
+                put_pm(t, s1, pp1);
                 if (s2 < t) {
-                    if constexpr (GDN) Am[t * kC + s2] = pa2;
-                    Pm[t * kLT + s2] = pp2;
+                    if constexpr (GDN) Am[s2 * kLT + t] = pa2;
+                    put_pm(t, s2, pp2);
                 }
             }
             if (tid >= 256 && tid < 256 + 4 * kC) {  // diagonal of P: q_t . k_t, four lanes per token
@@ -544,7 +611,7 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
                 pp += dpp_move<0xB1>(pp);  // lane ^ 1
                 pp += dpp_move<0x4E>(pp);  // lane ^ 2
-                if (part == 0) Pm[td * kLT + td] = pp;
+                if (part == 0) put_pm(td, td, pp);
             }
             __syncthreads();
         }
@@ -624,6 +691,34 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
             else
                 return rows_dot(X, KB, Full{}, 0, f32x16{});
         };
+        // the factored P (lower, inclusive) into Pm.  With bf16 data it is formed
+        // transposed, C[s][t] = P[t][s], so that a lane holds row t = l32 of P with
+        // four consecutive s per element group: 8-byte plane stores.
+        auto store_p = [&]() {
+            if constexpr (PL) {
+                const f32x16 c = dot_pp(KB, QA, std::integral_constant<int, DK / 16>{}, 0, f32x16{});
+                uint16_t* P = reinterpret_cast<uint16_t*>(Pm) + l32 * LT2 + 4 * kg;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    bf16x4 hi, lo;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = 8 * b + 4 * kg + r <= l32 ? c[4 * b + r] : 0.f;
+                        hi[r] = static_cast<__bf16>(x);
+                        lo[r] = static_cast<__bf16>(x - static_cast<float>(hi[r]));
+                    }
+                    *reinterpret_cast<bf16x4*>(P + 8 * b) = hi;
+                    *reinterpret_cast<bf16x4*>(P + kC + 8 * b) = lo;
+                }
+            } else {
+                const f32x16 c = gram(QA);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = row(e);
+                    Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
+                }
+            }
+        };
         auto store_o = [&](int I, const f32x16& c) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -695,8 +790,7 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const int ru = 32 * I + l32;
 #pragma unroll
                 for (int i = 0; i < kC / 16; ++i) {
-                    bf16x8 ah, al;
-                    split_bf16(lds_f32x8(&Pm[l32 * kLT + 16 * i + 8 * kg]), ah, al);
+                    const bf16x8 ah = tplane(Pm, l32, i, 0), al = tplane(Pm, l32, i, 1);
                     const bf16x8 bh = tplane(UT, ru, i, 0), bl = tplane(UT, ru, i, 1);
                     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
                     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
@@ -716,24 +810,21 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
             // them reads another's result.
             if (w == 0) {
                 if (!wide) {
+                    // c[e] = A[t][s] for t = row(e), s = l32: row s of A^T, tokens
+                    // 8 b + 4 kg .. + 3 in elements 4 b .. 4 b + 3 (16-byte stores)
                     const f32x16 c = gram(KA);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int t = row(e);
-                        Am[t * kC + l32] = l32 < t ? c[e] : 0.f;
+                    for (int b = 0; b < 4; ++b) {
+                        f32x4 a;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) a[r] = 8 * b + 4 * kg + r > l32 ? c[4 * b + r] : 0.f;
+                        *reinterpret_cast<f32x4*>(&Am[l32 * kLT + 8 * b + 4 * kg]) = a;
                     }
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 }
-                solve_unit_lower<kC, kLT>(Am, bet, Tm, lane);
+                solve_unit_lower_t<kLT, kLT>(Am, bet, Tm, lane);
             } else if (w == 1) {
-                if (!wide) {
-                    const f32x16 c = gram(QA);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int t = row(e);
-                        Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
-                    }
-                }
+                if (!wide) store_p();
             } else if (w < 4) {
                 const int I = w - 2;
                 const float sg = wide ? 1.f : -1.f;
@@ -785,14 +876,7 @@ __global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2, 2)
             // P (wave 0) beside O = (Q gamma) S^T on value columns 32 (w - 2) ..
             // (waves 2, 3; waves 1, 5 the last key quarter of tiles 0, 1)
             if (w == 0) {
-                if (!wide) {
-                    const f32x16 c = gram(QA);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int t = row(e);
-                        Pm[t * kLT + l32] = l32 <= t ? c[e] : 0.f;
-                    }
-                }
+                if (!wide) store_p();
             } else if (w == 2 || w == 3) {
                 oacc = op_dot_s(wide ? Qg : QA, Ss + 32 * (w - 2) * L4, OHead{}, 0, oacc);
             } else if (kSplitO && (w == 1 || w == 5)) {
