@@ -55,6 +55,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kThreadsR = 512;  // the reverse chunk pass: 8 waves, two per SIMD
+// the states pass: 8 waves (two per SIMD) with bf16 data, 4 with float32 data
+// (whose wider prefetch registers would spill at two waves per SIMD)
+template <typename E>
+constexpr int states_waves() { return std::is_same<E, uint16_t>::value ? 8 : 4; }
 constexpr int kC = 32;       // tokens per chunk
 constexpr int kSL = 64;      // value rows per workgroup
 constexpr int LV = kSL + 1;  // row stride of [32][64] value-row arrays
@@ -146,28 +150,33 @@ __device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, float w_ra
 //
 // Only X = beta V - beta gamma K S^T, U = T X and the update of S depend on the
 // state, so they alone make the serial chain; the rest runs ahead of it on the
-// waves the chain leaves idle.  In the loop over chunks n (three barriers):
-//   1: waves 1, 2 form X(n); wave 0 solves T(n + 1) from its k-Gram and (two
-//      value slices) zeroes the outputs the reverse pass adds into; wave 3
-//      moves k(n + 2) and v(n + 1) from its registers into LDS, forms the gates
-//      of chunk n + 2 and fetches k(n + 3) and v(n + 2) from HBM;
+// waves the chain leaves idle.  Eight waves (two per SIMD) with bf16 data, four
+// with float32 data.  In the loop over chunks n (three barriers):
+//   1: waves 1, 2 form X(n); wave 0 solves T(n + 1) from its k-Gram; wave 4 (wave
+//      0 with four waves; two value slices) zeroes the outputs the reverse pass
+//      adds into; wave 3 moves k(n + 2) and v(n + 1) from its registers into LDS,
+//      forms the gates of chunk n + 2 and fetches k(n + 3) and v(n + 2) from HBM;
 //   2: waves 1, 2 form U(n) = T(n) X(n); wave 3 forms the k-Gram of chunk n + 2;
-//      waves 0 (half), 1 and 2 (a quarter each) store S entering chunk n;
+//      waves 4 .. 7 store S entering chunk n, a quarter each (four waves: wave 0
+//      half, waves 1, 2 a quarter each);
 //   3: all waves update S, each on the tiles it keeps in registers.
 // k and the gates are held three chunks deep, v/U, T and the k-Gram two.
-// GLA (U = V, nothing to solve): wave 3 moves k(n + 1) and v(n + 1) and wave 0
-// stores the state; a barrier; the update.
+// GLA (U = V, nothing to solve): wave 3 moves k(n + 1) and v(n + 1), wave 0
+// zeroes the outputs (wave 3 with four waves) and waves 4 .. 7 store the state
+// (wave 0 with four waves); a barrier; the update.
 struct ChunkGatesLds {
     float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
 };
 
 template <int MODE, int DK, typename E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_states_kernel(
+__global__ __launch_bounds__(64 * states_waves<E>())
+__attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4))) void bwd_states_kernel(
     BwdJob J) {
     constexpr bool GDN = MODE == 0;
     // bf16 data: the products in split bf16 (about 16 significant bits each)
     constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
     constexpr int NJ = DK / 32;
+    constexpr int NW = states_waves<E>(), NTH = 64 * NW;
     // Row strides: 16-byte rows (vector reads and writes along a row), and
     // k-operands read down a column as rows r and r + 8 (the two lane halves)
     // land 32 banks apart.
@@ -295,9 +304,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     };
 
     // Prologue: S0; k, v and gates of the first chunks; T(0) and B(1).
-    for (int x = tid; x < kSL * DK; x += kThreads) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
+    for (int x = tid; x < kSL * DK; x += NTH) Ss[x / DK * L1 + x % DK] = J.S0 ? J.S0[s_base + x] : 0.f;
     if constexpr (GDN)
-        for (int x = tid; x < 2 * kC * LT; x += kThreads) Tm[x / (kC * LT)][x % (kC * LT)] = 0.f;  // T's upper right block stays zero
+        for (int x = tid; x < 2 * kC * LT; x += NTH) Tm[x / (kC * LT)][x % (kC * LT)] = 0.f;  // T's upper right block stays zero
     if (w == 3) {
         fetch_k(0);
         fetch_v(0);
@@ -332,13 +341,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         constexpr int W = decltype(wc)::value;
         constexpr int MS = kSL * DK / 4 / 64;  // 16-byte pieces of the state per lane
         // The state's tiles stay in the registers of the wave that updates them
-        // (tile W + 4 it: value rows 32 (tile / NJ) .., key columns 32 (tile % NJ) ..);
+        // (tile W + NW it: value rows 32 (tile / NJ) .., key columns 32 (tile % NJ) ..);
         // Ss holds a copy for the X products.
-        constexpr int NT = (2 * NJ - W + 3) / 4;
+        constexpr int NT = (2 * NJ - W + NW - 1) / NW;
         f32x16 st[NT > 0 ? NT : 1];
 #pragma unroll
         for (int it = 0; it < NT; ++it) {
-            const int tile = W + 4 * it, I = tile / NJ, Jt = tile - I * NJ;
+            const int tile = W + NW * it, I = tile / NJ, Jt = tile - I * NJ;
 #pragma unroll
             for (int e = 0; e < 16; ++e) st[it][e] = Ss[(32 * I + row(e)) * L1 + 32 * Jt + l32];
         }
@@ -363,8 +372,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     }
                 } else if constexpr (W == 0) {
                     if (n + 1 < NC) solve_unit_lower<LB, LT>(Bm[(n + 1) & 1], gt[(n + 1) % NB].bet, Tm[(n + 1) & 1], lane);
+                    if (NW == 4 && slices == 2) zero_outputs(c0);
+                } else if constexpr (W == 4) {
                     if (slices == 2) zero_outputs(c0);
-                } else {
+                } else if constexpr (W == 3) {
                     if (n + 2 < NC) put_k(n + 2);
                     if (n + 1 < NC) put_v(n + 1);
                     fetch_k(n + 3 < NC ? n + 3 : NC - 1);
@@ -379,11 +390,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         [&](int i) { return lds_col8<LU>(&Un[(16 * i + 8 * kg) * LU + 32 * I + l32]); }, f32x16{});
 #pragma unroll
                     for (int e = 0; e < 16; ++e) Un[row(e) * LU + 32 * I + l32] = gn.Dd[row(e)] * c[e];
-                    // a quarter of the state's store each
-                    stash(n, std::integral_constant<int, MS * (W + 1) / 4>{}, std::integral_constant<int, MS * (W + 2) / 4>{});
+                    // four waves: a quarter of the state's store each
+                    if constexpr (NW == 4)
+                        stash(n, std::integral_constant<int, MS * (W + 1) / 4>{}, std::integral_constant<int, MS * (W + 2) / 4>{});
                 } else if constexpr (W == 3) {
                     if (n + 2 < NC) k_gram(n + 2);
-                } else {  // the first half of the state's store
+                } else if constexpr (W >= 4) {  // eight waves: a quarter of the state's store each
+                    stash(n, std::integral_constant<int, MS * (W - 4) / 4>{}, std::integral_constant<int, MS * (W - 3) / 4>{});
+                } else if constexpr (NW == 4) {  // four waves, wave 0: the first half of the state's store
                     stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS / 2>{});
                 }
                 __syncthreads();
@@ -395,16 +409,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     }
                     fetch_k(n + 2 < NC ? n + 2 : NC - 1);
                     fetch_v(n + 2 < NC ? n + 2 : NC - 1);
-                    if (slices == 2) zero_outputs(c0);
+                    if (NW == 4 && slices == 2) zero_outputs(c0);
                 } else if constexpr (W == 0) {
-                    stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS>{});
+                    if (NW == 8 && slices == 2) zero_outputs(c0);
+                    if constexpr (NW == 4) stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS>{});
+                } else if constexpr (W >= 4) {  // a quarter of the state's store each
+                    stash(n, std::integral_constant<int, MS * (W - 4) / 4>{}, std::integral_constant<int, MS * (W - 3) / 4>{});
                 }
                 __syncthreads();  // the stash reads Ss before the update rewrites it
             }
             // S <- gamma_C S + U^T diag(e^{g_C - g}) K
 #pragma unroll
             for (int it = 0; it < NT; ++it) {
-                const int tile = W + 4 * it, I = tile / NJ, Jt = tile - I * NJ;
+                const int tile = W + NW * it, I = tile / NJ, Jt = tile - I * NJ;
                 f32x16 c = gn.gC[0] * st[it];
                 c = chain8_t<SPLIT, kC / 16, false, true>(
                     [&](int i) { return lds_col8<LU>(&Un[(16 * i + 8 * kg) * LU + 32 * I + l32]); },
@@ -416,14 +433,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             __syncthreads();
         }
     };
-    if (w == 0)
-        run(std::integral_constant<int, 0>{});
-    else if (w == 1)
-        run(std::integral_constant<int, 1>{});
-    else if (w == 2)
-        run(std::integral_constant<int, 2>{});
-    else
-        run(std::integral_constant<int, 3>{});
+    if (w == 0) run(std::integral_constant<int, 0>{});
+    else if (w == 1) run(std::integral_constant<int, 1>{});
+    else if (w == 2) run(std::integral_constant<int, 2>{});
+    else if (w == 3) run(std::integral_constant<int, 3>{});
+    else if constexpr (NW == 8) {
+        if (w == 4) run(std::integral_constant<int, 4>{});
+        else if (w == 5) run(std::integral_constant<int, 5>{});
+        else if (w == 6) run(std::integral_constant<int, 6>{});
+        else run(std::integral_constant<int, 7>{});
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1042,7 +1061,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdJob J) {
 template <int MODE, int DK, typename E>
 hipError_t launch_typed(const BwdJob& J, hipStream_t s) {
     const dim3 grid((unsigned)((size_t)J.BH * (J.dv / kSL)));
-    hipLaunchKernelGGL((bwd_states_kernel<MODE, DK, E>), grid, dim3(kThreads), 0, s, J);
+    hipLaunchKernelGGL((bwd_states_kernel<MODE, DK, E>), grid, dim3(64 * states_waves<E>()), 0, s, J);
     hipLaunchKernelGGL((bwd_chunk_kernel<MODE, DK, E>), grid, dim3(kThreadsR), 0, s, J);
     if (J.dv / kSL > 2) {
         const size_t n4 = (size_t)J.BH * J.T * J.dk / 4;
