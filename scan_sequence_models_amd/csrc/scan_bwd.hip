@@ -84,25 +84,41 @@ __device__ __forceinline__ void unpack16(const uint4& u, float (&f)[EV]) {
 // column l32 (lane = 32 kg + l32)
 __device__ __forceinline__ int acc_row(int e, int kg) { return 8 * (e >> 2) + 4 * kg + (e & 3); }
 
-// Sum over the 32 lanes of each half-wave: quad and row steps on DPP, the
-// lane ^ 16 step on v_permlane16_swap (a VALU exchange of the two 16-lane rows
-// of each 32-lane group), not on the LDS-path swizzle.
-__device__ __forceinline__ float sum32(float x) {
-    x += dpp_move<0xB1>(x);   // lane ^ 1
-    x += dpp_move<0x4E>(x);   // lane ^ 2
-    x += dpp_move<0x141>(x);  // row half mirror
-    x += dpp_move<0x140>(x);  // row mirror
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Row sums of a tile: rows of the lane's half go to out[row] from lane l32 == 0.
+// Row sums of a tile: rows of the lane's half go to out[row].  A transposing
+// butterfly over the 32 lanes of the half: at each step the two lanes of a pair
+// (the two 16-lane rows, then the mirrors within a row, half-row and quad) each
+// keep one half of their remaining elements and add the partner's copy of it,
+// so 16 elements take 8 + 4 + 2 + 1 exchanges (and one more to finish) instead
+// of 5 per element.  Lane l32 ends with element (l32 >> 1) of its row group.
 __device__ __forceinline__ void store_row_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
+    // lane ^ 16: the lanes of 16-lane row 0 keep elements 0 .. 7, those of row 1
+    // elements 8 .. 15 (v_permlane16_swap exchanges row 1 of its first operand with
+    // row 0 of its second)
+    float u[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const float s = sum32(x[e]);
-        if (l32 == 0) out[acc_row(e, kg)] = sign * s;
+    for (int j = 0; j < 8; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + 8]), false, false);
+        u[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
+    const bool b3 = (l32 & 8) != 0, b2 = (l32 & 4) != 0, b1 = (l32 & 2) != 0;
+    float t4[4], t2[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // row mirror: lanes 0 .. 7 with 8 .. 15
+        const float keep = b3 ? u[j + 4] : u[j], send = b3 ? u[j] : u[j + 4];
+        t4[j] = keep + dpp_move<0x140>(send);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // half-row mirror: lanes 0 .. 3 with 4 .. 7
+        const float keep = b2 ? t4[j + 2] : t4[j], send = b2 ? t4[j] : t4[j + 2];
+        t2[j] = keep + dpp_move<0x141>(send);
+    }
+    float t1;
+    {  // lane ^ 2
+        const float keep = b1 ? t2[1] : t2[0], send = b1 ? t2[0] : t2[1];
+        t1 = keep + dpp_move<0x4E>(send);
+    }
+    t1 += dpp_move<0xB1>(t1);  // lane ^ 1
+    if ((l32 & 1) == 0) out[acc_row((l32 >> 1) & 15, kg)] = sign * t1;
 }
 // Column sums of a tile: out[column] from the lanes of half 0.
 __device__ __forceinline__ void store_col_sums(const f32x16& x, float* out, int l32, int kg, float sign) {
@@ -477,7 +493,9 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
     __shared__ __align__(16) float Tm[GDN ? kC * LP : 1];
     __shared__ __align__(16) float dQKm[kC * LP];  // dP o Gamma
     __shared__ __align__(16) float dKKm[GDN ? kC * LP : 1];
-    __shared__ float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
+    __shared__ __align__(16) float G2[kC];
+    __shared__ __align__(16) float bet[kC];
+    __shared__ float gam[kC], Dd[kC], bw[kC], bg[kC], gC[1];
     __shared__ float dgp[16 * kC];   // per-product contributions to dg (fixed slots)
     __shared__ float dbp[8 * kC];    // ... to dbeta
     __shared__ float dgc[16];        // ... to dg_C
@@ -665,11 +683,14 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int jq = w - 4, jk = w;  // the owned tiles
         f32x16 acc = {};   // dq tile jq (qown) or dk tile jk (kown)
         f32x16 ksT = {};   // waves 2, 3 (delta rule): (K S^T)^T on value columns 32 (w - 2) .., kept to phase 5
-        // waves 4 + h2 (h2 < 4): dS tiles 2 h2, 2 h2 + 1 from phase 2 to phase 5
+        // dS tiles, from phase 2 to phase 5: waves 4, 5, 7 two each (0, 1; 2, 3;
+        // 6, 7), waves 0, 1 one each (4; 5); wave 6 forms dA in phase 5 instead
         f32x16 dsc[2];
         float dss[2] = {0.f, 0.f};
-        const int h2 = w - 4;
-        auto ds_tile = [&](int h) { return 2 * h2 + h; };
+        auto ds_tile = [&](int h) {
+            return w == 4 ? h : w == 5 ? 2 + h : w == 7 ? 6 + h : (w < 2 && h == 0) ? 4 + w : 2 * NJ;
+        };
+        const bool ds_wave = w < 2 || w == 4 || w == 5 || w == 7;
         constexpr int G1 = kC / 16;
         // Phase 1: B and then T (wave 0, delta rule), P (wave 1), X (waves 2, 3,
         // delta rule) or dU = Kd dS'^T (waves 2, 3, linear attention), and the dq
@@ -729,7 +750,7 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         __syncthreads();
         // Phase 2: U = T X (waves 2, 3) and dU = Kd dS'^T (waves 0, 1) with the
         // delta rule; the first part of the dS tiles, gamma_C dS' + dO^T diag(gamma) Q,
-        // and <dS', S> (waves 4 .. 7, held in registers until phase 5: dS' is read
+        // and <dS', S> (the dS waves, held in registers until phase 5: dS' is read
         // until then)
         if (GDN && (w == 2 || w == 3)) {
             const int I = w - 2;
@@ -745,7 +766,8 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
                 [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
 #pragma unroll
             for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
-        } else if (w >= 4) {
+        }
+        if (ds_wave) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int tile = ds_tile(h);
@@ -857,9 +879,8 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         __syncthreads();
         // the next chunk's inputs are in flight through phases 5 and 6
         if (n > 0) fetch(n - 1);
-        // Phase 5: dRw (dk owners), dA (waves 6 and 7 both form it: wave 6 writes
-        // dKK, wave 7 the sums), <dRw, K> (waves 2, 3), the rest of the dS tiles
-        // (waves 4 .. 7)
+        // Phase 5: dRw (dk owners), dA with dKK and its sums (wave 6), <dRw, K>
+        // (waves 2, 3), the rest of the dS tiles (the dS waves)
         if constexpr (GDN) {
             if (kown) {  // dRw = -dX S
                 const f32x16 c = chain8_t<SPLIT, kSL / 16>(
@@ -868,29 +889,29 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[e] += bg[row(e)] * c[e];
             }
-            if (w == 6 || w == 7) {
+            if (w == 6) {  // dA = strict_lower(-dX U^T): dKK, then the row and column sums of dA o B
                 const f32x16 c = chain8_t<SPLIT, kSL / 16>([&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
                                                   [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
                                                   f32x16{});
-                if (w == 6) {
+                f32x16 xb, xa;
+                const float gs = G2[l32];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int t = row(e);
-                        dKKm[t * LP + l32] = l32 < t ? bet[t] * c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
-                    }
-                } else {
-                    f32x16 xb, xa;
+                for (int b4 = 0; b4 < 4; ++b4) {  // rows 8 b4 + 4 kg .. + 3: the gates as 16-byte reads
+                    const f32x4 g = *reinterpret_cast<const f32x4*>(&G2[8 * b4 + 4 * kg]);
+                    const f32x4 bt = *reinterpret_cast<const f32x4*>(&bet[8 * b4 + 4 * kg]);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int t = row(e);
+                    for (int r = 0; r < 4; ++r) {
+                        const int e = 4 * b4 + r, t = row(e);
                         const float da = l32 < t ? c[e] : 0.f;
+                        // (a select: above the diagonal the exponent is not bounded)
+                        dKKm[t * LP + l32] = l32 < t ? bt[r] * c[e] * __builtin_amdgcn_exp2f(g[r] - gs) : 0.f;
                         const float b = Bm[t * LB + l32];
                         xb[e] = da * b;
-                        xa[e] = da * bet[t] * b;
+                        xa[e] = da * bt[r] * b;
                     }
-                    store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6 (dg: beta_t times it)
-                    store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
                 }
+                store_row_sums(xb, dbp + 6 * kC, l32, kg, 1.f);    // dbeta slot 6 (dg: beta_t times it)
+                store_col_sums(xa, dgp + 15 * kC, l32, kg, -1.f);  // dg slot 15
             }
             if (w == 2 || w == 3) {  // <dRw_t, K_t> = -<dX_t, (K S^T)_t> over this wave's value columns
                 const int I = w - 2;
@@ -912,7 +933,7 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         // dS = gamma_C dS' + dO^T diag(gamma) Q - dX^T diag(beta gamma) K: the last
         // term (delta rule; k exact in bf16, beta gamma on the dX side), then dS into LDS
-        if (w >= 4) {
+        if (ds_wave) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int tile = ds_tile(h);
