@@ -959,7 +959,8 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         __syncthreads();
         if (SWZ && n > 0) load_state(n - 1);
-        // Phase 6: dK += (dKK + dKK^T) K (dk owners); dq, dk; dg -> d ln alpha, dbeta (wave 7)
+        // Phase 6: dK += (dKK + dKK^T) K (dk owners); dq, dk; dg -> d ln alpha (wave 7),
+        // dbeta (wave 6)
         if (GDN && kown)
             acc = chain8_t<SPLIT, kC / 16, false, true>(
                 [&](int i) {
@@ -1003,14 +1004,21 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const float y = __shfl_down(dg, off, 32);
                 if (t + off < 32) dg += y;
             }
-            // dbeta slots 0, 1 belong to the write strength (they come from V), the rest to the erase one
+            if (kg == 0 && c0 + t < T) {
+                if (slices > 2) pdl[part_tok + c0 + t] = dg;
+                else put(J.dalpha + tok0 + c0 + t, dg);  // d ln alpha until bwd_finish_kernel
+            }
+        }
+        if (w == 6) {
+            // dbeta: slots 0, 1 belong to the write strength (they come from V), the
+            // rest to the erase one
+            const int t = l32;
             const float dbw = dbp[t] + dbp[kC + t];
             float dbe = 0.f;
 #pragma unroll
             for (int s = 2; s < 8; ++s) dbe += dbp[s * kC + t];
             if (kg == 0 && c0 + t < T) {
                 if (slices > 2) {
-                    pdl[part_tok + c0 + t] = dg;
                     if (J.dbeta_w) {
                         pdb[part_tok + c0 + t] = dbe;
                         pdbw[part_tok + c0 + t] = dbw;
@@ -1019,7 +1027,6 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
                     }
                 } else {
                     const size_t tk = tok0 + c0 + t;
-                    put(J.dalpha + tk, dg);  // d ln alpha until bwd_finish_kernel
                     if (J.dbeta_w) {
                         put(J.dbeta + tk, dbe);
                         put(J.dbeta_w + tk, dbw);
