@@ -83,6 +83,18 @@ __device__ __forceinline__ void unpack16(const uint4& u, float (&f)[EV]) {
 // accumulator element e of a 32x32 tile sits at row 8 (e / 4) + 4 kg + e % 4,
 // column l32 (lane = 32 kg + l32)
 __device__ __forceinline__ int acc_row(int e, int kg) { return 8 * (e >> 2) + 4 * kg + (e & 3); }
+// p[acc_row(e, kg)] for e = 0 .. 15 from a 16-byte aligned per-token array: the
+// rows of a lane come in four runs of four consecutive tokens, one 16-byte read each
+__device__ __forceinline__ f32x16 acc_rows16(const float* p, int kg) {
+    f32x16 r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&p[8 * b + 4 * kg]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[4 * b + i] = v[i];
+    }
+    return r;
+}
 
 // Row sums of a tile: rows of the lane's half go to out[row].  A transposing
 // butterfly over the 32 lanes of the half: at each step the two lanes of a pair
@@ -180,7 +192,7 @@ __device__ __forceinline__ void chunk_gates(float a_raw, float b_raw, float w_ra
 // GLA (U = V, nothing to solve): wave 3 moves k(n + 1) and v(n + 1), wave 0
 // zeroes the outputs (wave 3 with four waves) and waves 4 .. 7 store the state
 // (wave 0 with four waves); a barrier; the update.
-struct ChunkGatesLds {
+struct alignas(16) ChunkGatesLds {  // every array 16-byte aligned (kC floats each)
     float G2[kC], gam[kC], Dd[kC], bet[kC], bw[kC], bg[kC], gC[1];
 };
 
@@ -288,10 +300,12 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
         auto kr = [&](int i) { return lds_f32x8(&Kb[l32 * L1 + 16 * i + 8 * kg]); };
         const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(kr, kr, f32x16{});
         float* B = Bm[cn & 1];
+        const f32x16 gt16 = acc_rows16(G2, kg);
+        const float gs = G2[l32];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int t = row(e);
-            B[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+            B[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(gt16[e] - gs) * c[e] : 0.f;
         }
     };
     // the state entering chunk cn, from Ss: 16-byte pieces m0, m0 + 1, .. < m1
@@ -381,10 +395,11 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
                     const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
                         [&](int i) { return lds_f32x8(&Kn[l32 * L1 + 16 * i + 8 * kg]); },
                         [&](int i) { return lds_f32x8(&Ss[(32 * I + l32) * L1 + 16 * i + 8 * kg]); }, f32x16{});
+                    const f32x16 bw16 = acc_rows16(gn.bw, kg), bg16 = acc_rows16(gn.bg, kg);
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int t = row(e), y = t * LU + 32 * I + l32;
-                        Un[y] = gn.bw[t] * Un[y] - gn.bg[t] * c[e];
+                        Un[y] = bw16[e] * Un[y] - bg16[e] * c[e];
                     }
                 } else if constexpr (W == 0) {
                     if (n + 1 < NC) solve_unit_lower<LB, LT>(Bm[(n + 1) & 1], gt[(n + 1) % NB].bet, Tm[(n + 1) & 1], lane);
@@ -404,8 +419,9 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
                     const f32x16 c = chain8_t<SPLIT, kC / 16>(
                         [&](int i) { return lds_f32x8(&Tn[l32 * LT + 16 * i + 8 * kg]); },
                         [&](int i) { return lds_col8<LU>(&Un[(16 * i + 8 * kg) * LU + 32 * I + l32]); }, f32x16{});
+                    const f32x16 dd16 = acc_rows16(gn.Dd, kg);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) Un[row(e) * LU + 32 * I + l32] = gn.Dd[row(e)] * c[e];
+                    for (int e = 0; e < 16; ++e) Un[row(e) * LU + 32 * I + l32] = dd16[e] * c[e];
                     // four waves: a quarter of the state's store each
                     if constexpr (NW == 4)
                         stash(n, std::integral_constant<int, MS * (W + 1) / 4>{}, std::integral_constant<int, MS * (W + 2) / 4>{});
@@ -495,7 +511,11 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
     __shared__ __align__(16) float dKKm[GDN ? kC * LP : 1];
     __shared__ __align__(16) float G2[kC];
     __shared__ __align__(16) float bet[kC];
-    __shared__ float gam[kC], Dd[kC], bw[kC], bg[kC], gC[1];
+    __shared__ __align__(16) float gam[kC];
+    __shared__ __align__(16) float Dd[kC];
+    __shared__ __align__(16) float bw[kC];
+    __shared__ __align__(16) float bg[kC];
+    __shared__ float gC[1];
     __shared__ float dgp[16 * kC];   // per-product contributions to dg (fixed slots)
     __shared__ float dbp[8 * kC];    // ... to dbeta
     __shared__ float dgc[16];        // ... to dg_C
@@ -698,10 +718,11 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (GDN && w == 0) {
             auto kr = [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); };
             const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(kr, kr, f32x16{});
+            const f32x16 g16 = acc_rows16(G2, kg); const float gs = G2[l32];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
-                Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+                Bm[t * LB + l32] = l32 < t ? __builtin_amdgcn_exp2f(g16[e] - gs) * c[e] : 0.f;
             }
             // the same wave solves right away: its own B rows are complete once
             // its LDS writes are
@@ -711,10 +732,11 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
             const f32x16 c = chain8_t<SPLIT, DK / 16, true, true>(
                 [&](int i) { return lds_f32x8(&Qs[l32 * L1 + 16 * i + k8]); },
                 [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); }, f32x16{});
+            const f32x16 g16 = acc_rows16(G2, kg); const float gs = G2[l32];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = row(e);
-                Pm[t * LP + l32] = l32 <= t ? __builtin_amdgcn_exp2f(G2[t] - G2[l32]) * c[e] : 0.f;
+                Pm[t * LP + l32] = l32 <= t ? __builtin_amdgcn_exp2f(g16[e] - gs) * c[e] : 0.f;
             }
         } else if (GDN && (w == 2 || w == 3)) {
             const int I = w - 2;
@@ -734,14 +756,16 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
             const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
                 [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
                 [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
+            const f32x16 dd16 = acc_rows16(Dd, kg);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
+            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = dd16[e] * c[e];
         } else if (qown) {
             // dO exact in bf16, gamma applied to the rows after
             acc = chain8_t<SPLIT, kSL / 16, true>([&](int i) { return rowv8(&dOs[l32 * LV + 16 * i + k8]); },
                                          [&](int i) { return s_col8(16 * i + k8, 32 * jq + l32); }, acc);
+            const f32x16 gam16 = acc_rows16(gam, kg);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] *= gam[row(e)];
+            for (int e = 0; e < 16; ++e) acc[e] *= gam16[e];
             f32x16 x;
 #pragma unroll
             for (int e = 0; e < 16; ++e) x[e] = acc[e] * Qs[row(e) * L1 + 32 * jq + l32];
@@ -764,8 +788,9 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
             const f32x16 c = chain8_t<SPLIT, DK / 16, true>(
                 [&](int i) { return lds_f32x8(&Ks[l32 * L1 + 16 * i + k8]); },
                 [&](int i) { return lds_f32x8(&dSs[(32 * I + l32) * L1 + 16 * i + k8]); }, f32x16{});
+            const f32x16 dd16 = acc_rows16(Dd, kg);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = Dd[row(e)] * c[e];
+            for (int e = 0; e < 16; ++e) dUs[row(e) * LV + 32 * I + l32] = dd16[e] * c[e];
         }
         if (ds_wave) {
 #pragma unroll
@@ -804,10 +829,11 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
                                                     [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
                                                     f32x16{});
             if (w == 4) {
+                const f32x16 g16 = acc_rows16(G2, kg); const float gs = G2[l32];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = row(e);
-                    dQKm[t * LP + l32] = l32 <= t ? c[e] * __builtin_amdgcn_exp2f(G2[t] - G2[l32]) : 0.f;
+                    dQKm[t * LP + l32] = l32 <= t ? c[e] * __builtin_amdgcn_exp2f(g16[e] - gs) : 0.f;
                 }
             } else {
                 f32x16 L;
@@ -846,8 +872,9 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
             const f32x16 c = chain8_t<SPLIT, kSL / 16>(
                 [&](int i) { return rowv8(&Us[l32 * LV + 16 * i + k8]); },
                 [&](int i) { return lds_col8<L1>(&dSs[(16 * i + k8) * L1 + 32 * jk + l32]); }, f32x16{});
+            const f32x16 dd16 = acc_rows16(Dd, kg);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] += Dd[row(e)] * c[e];
+            for (int e = 0; e < 16; ++e) acc[e] += dd16[e] * c[e];
         }
         __syncthreads();
         // Phase 4: dX = T^T dU (delta rule, waves 0, 1; computed as dX^T = dU^T T, the token
@@ -886,8 +913,9 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const f32x16 c = chain8_t<SPLIT, kSL / 16>(
                     [&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
                     [&](int i) { return s_col8(16 * i + k8, 32 * jk + l32); }, f32x16{});
+                const f32x16 bg16 = acc_rows16(bg, kg);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[e] += bg[row(e)] * c[e];
+                for (int e = 0; e < 16; ++e) acc[e] += bg16[e] * c[e];
             }
             if (w == 6) {  // dA = strict_lower(-dX U^T): dKK, then the row and column sums of dA o B
                 const f32x16 c = chain8_t<SPLIT, kSL / 16>([&](int i) { return -rowv8(&Vs[l32 * LV + 16 * i + k8]); },
