@@ -703,14 +703,17 @@ __global__ __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int jq = w - 4, jk = w;  // the owned tiles
         f32x16 acc = {};   // dq tile jq (qown) or dk tile jk (kown)
         f32x16 ksT = {};   // waves 2, 3 (delta rule): (K S^T)^T on value columns 32 (w - 2) .., kept to phase 5
-        // dS tiles, from phase 2 to phase 5: waves 4, 5, 7 two each (0, 1; 2, 3;
-        // 6, 7), waves 0, 1 one each (4; 5); wave 6 forms dA in phase 5 instead
+        // dS tiles, from phase 2 to phase 5: wave 7 two (6, 7), waves 4, 2, 5, 3
+        // one each (0, 1, 2, 3), waves 0, 1 one each (4, 5); wave 6 forms dA in
+        // phase 5 instead
         f32x16 dsc[2];
         float dss[2] = {0.f, 0.f};
         auto ds_tile = [&](int h) {
-            return w == 4 ? h : w == 5 ? 2 + h : w == 7 ? 6 + h : (w < 2 && h == 0) ? 4 + w : 2 * NJ;
+            if (w == 7) return 6 + h;
+            if (h == 1) return 2 * NJ;
+            return w == 4 ? 0 : w == 2 ? 1 : w == 5 ? 2 : w == 3 ? 3 : w < 2 ? 4 + w : 2 * NJ;
         };
-        const bool ds_wave = w < 2 || w == 4 || w == 5 || w == 7;
+        const bool ds_wave = w != 6;
         constexpr int G1 = kC / 16;
         // Phase 1: B and then T (wave 0, delta rule), P (wave 1), X (waves 2, 3,
         // delta rule) or dU = Kd dS'^T (waves 2, 3, linear attention), and the dq
