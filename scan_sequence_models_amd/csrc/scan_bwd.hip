@@ -404,13 +404,11 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
                 } else if constexpr (W == 0) {
                     if (n + 1 < NC) solve_unit_lower<LB, LT>(Bm[(n + 1) & 1], gt[(n + 1) % NB].bet, Tm[(n + 1) & 1], lane);
                     if (NW == 4 && slices == 2) zero_outputs(c0);
-                } else if constexpr (W == 4) {
-                    if (slices == 2) zero_outputs(c0);
+                } else if constexpr (W >= 4) {  // eight waves: a quarter of the state's store each, beside X
+                    stash(n, std::integral_constant<int, MS * (W - 4) / 4>{}, std::integral_constant<int, MS * (W - 3) / 4>{});
                 } else if constexpr (W == 3) {
                     if (n + 2 < NC) put_k(n + 2);
-                    if (n + 1 < NC) put_v(n + 1);
                     fetch_k(n + 3 < NC ? n + 3 : NC - 1);
-                    fetch_v(n + 2 < NC ? n + 2 : NC - 1);
                 }
                 __syncthreads();
                 if constexpr (W == 1 || W == 2) {  // diag(e^{g_C - g}) U, U = T X in place, on this wave's X columns
@@ -427,8 +425,11 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
                         stash(n, std::integral_constant<int, MS * (W + 1) / 4>{}, std::integral_constant<int, MS * (W + 2) / 4>{});
                 } else if constexpr (W == 3) {
                     if (n + 2 < NC) k_gram(n + 2);
-                } else if constexpr (W >= 4) {  // eight waves: a quarter of the state's store each
-                    stash(n, std::integral_constant<int, MS * (W - 4) / 4>{}, std::integral_constant<int, MS * (W - 3) / 4>{});
+                    // v of the next chunk into its U buffer, which no wave reads before the next X
+                    if (n + 1 < NC) put_v(n + 1);
+                    fetch_v(n + 2 < NC ? n + 2 : NC - 1);
+                } else if constexpr (W == 4) {
+                    if (slices == 2) zero_outputs(c0);
                 } else if constexpr (NW == 4) {  // four waves, wave 0: the first half of the state's store
                     stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS / 2>{});
                 }
