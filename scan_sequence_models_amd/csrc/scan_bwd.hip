@@ -205,6 +205,8 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
     constexpr bool SPLIT = std::is_same<E, uint16_t>::value;
     constexpr int NJ = DK / 32;
     constexpr int NW = states_waves<E>(), NTH = 64 * NW;
+    // the wave that stages v: with eight waves and the delta rule, one whose X phase is short
+    constexpr int VW = (GDN && NW == 8) ? 5 : 3;
     // Row strides: 16-byte rows (vector reads and writes along a row), and
     // k-operands read down a column as rows r and r + 8 (the two lane halves)
     // land 32 banks apart.
@@ -339,9 +341,9 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
         for (int x = tid; x < 2 * kC * LT; x += NTH) Tm[x / (kC * LT)][x % (kC * LT)] = 0.f;  // T's upper right block stays zero
     if (w == 3) {
         fetch_k(0);
-        fetch_v(0);
+        if (VW == 3) fetch_v(0);
         put_k(0);
-        put_v(0);
+        if (VW == 3) put_v(0);
         if constexpr (GDN) {
             if (NC > 1) {
                 fetch_k(1);
@@ -351,6 +353,10 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
         } else {
             fetch_k(1);
         }
+        if (VW == 3) fetch_v(1);
+    } else if (w == VW) {  // (the delta rule's put_v needs no gates)
+        fetch_v(0);
+        put_v(0);
         fetch_v(1);
     }
     __syncthreads();
@@ -425,12 +431,14 @@ __attribute__((amdgpu_waves_per_eu(states_waves<E>() / 4, states_waves<E>() / 4)
                         stash(n, std::integral_constant<int, MS * (W + 1) / 4>{}, std::integral_constant<int, MS * (W + 2) / 4>{});
                 } else if constexpr (W == 3) {
                     if (n + 2 < NC) k_gram(n + 2);
-                    // v of the next chunk into its U buffer, which no wave reads before the next X
+                }
+                if constexpr (W == VW) {  // v of the next chunk into its U buffer, which no wave reads before the next X
                     if (n + 1 < NC) put_v(n + 1);
                     fetch_v(n + 2 < NC ? n + 2 : NC - 1);
-                } else if constexpr (W == 4) {
+                }
+                if constexpr (W == 4) {
                     if (slices == 2) zero_outputs(c0);
-                } else if constexpr (NW == 4) {  // four waves, wave 0: the first half of the state's store
+                } else if constexpr (NW == 4 && W == 0) {  // four waves, wave 0: the first half of the state's store
                     stash(n, std::integral_constant<int, 0>{}, std::integral_constant<int, MS / 2>{});
                 }
                 __syncthreads();
